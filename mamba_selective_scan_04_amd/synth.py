@@ -1,0 +1,130 @@
+"""Seeded synthetic inputs for the block-restricted bidirectional scan.
+
+This module only draws random numbers and lays them out; it holds none of the
+scan's arithmetic.  Both the GPU path and the CPU oracle are fed from here.
+
+The pages give no input distributions, shapes or precisions for the scan
+(they report model-level throughput at 65K and 262K tokens of context and
+models of 87M and 350M parameters).  The recipe used everywhere:
+
+* x, B, C ~ N(0, 1)
+* dt = softplus(z) with z ~ N(-1, 0.5), drawn and transformed in fp32 and then
+  cast, i.e. dt is handed to the scan already positive (no bias, no softplus
+  inside the scan)
+* A[d, n] = -(n + 1)   (the "default" kind; kernels never rely on this
+  structure: "random", "long" and "zero" kinds exist for parity tests)
+* Dskip ~ N(0, 1)
+* x, dt, B, C are cast to the stream dtype (bf16 or fp32); A, Dskip and all
+  states stay fp32.
+
+Seeds: tensor k of workload s uses generator seed 1000*s + k with
+k = 0 x, 1 dt, 2 B, 3 C, 4 Dskip, 5 A (random kind); the j-th denoising
+step's block streams use k = 10+4j .. 13+4j and the i-th committed block's
+clean streams k = 90+4i .. 93+4i (x, dt, B, C in that order).
+"""
+import math
+
+import torch
+
+# name -> (workload id, dict of shape parameters)
+WORKLOADS = {
+    # fp32 parity workload: 240 context tokens + one 16-token block
+    "tiny_fp32": dict(sid=1, batch=1, d_inner=64, d_state=16, seq=256, block=16,
+                      ctx=240, dtype="f32"),
+    # all-block training scans shaped like the 87M / 350M models
+    "train_87m": dict(sid=2, batch=8, d_inner=1536, d_state=16, seq=4096, block=16,
+                      dtype="bf16"),
+    "train_350m": dict(sid=3, batch=4, d_inner=2048, d_state=16, seq=8192, block=16,
+                       dtype="bf16"),
+    # long-context inference: prefill the context, then denoise / commit blocks
+    "infer_65k_b1": dict(sid=4, batch=1, d_inner=1536, d_state=16, ctx=65536, block=16,
+                         steps=16, n_blocks=1, dtype="bf16"),
+    "infer_65k_b8": dict(sid=4, batch=8, d_inner=1536, d_state=16, ctx=65536, block=16,
+                         steps=16, n_blocks=1, dtype="bf16"),
+    "infer_262k_b1": dict(sid=5, batch=1, d_inner=2048, d_state=16, ctx=262144, block=16,
+                          steps=16, n_blocks=8, dtype="bf16"),
+    "infer_262k_b4": dict(sid=5, batch=4, d_inner=2048, d_state=16, ctx=262144, block=16,
+                          steps=16, n_blocks=8, dtype="bf16"),
+    "infer_262k_b16": dict(sid=5, batch=16, d_inner=2048, d_state=16, ctx=262144, block=16,
+                           steps=16, n_blocks=8, dtype="bf16"),
+}
+
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _gen(seed, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def normal(shape, seed, device="cpu", dtype=torch.float32, mean=0.0, std=1.0):
+    g = _gen(seed, device)
+    t = torch.empty(shape, dtype=torch.float32, device=device)
+    t.normal_(mean, std, generator=g)
+    return t.to(dtype)
+
+
+def positive_step(shape, seed, device="cpu", dtype=torch.float32):
+    """dt = softplus(N(-1, 0.5)), drawn and transformed in fp32, then cast."""
+    z = normal(shape, seed, device, torch.float32, mean=-1.0, std=0.5)
+    return torch.nn.functional.softplus(z).to(dtype)
+
+
+def a_matrix(d_inner, d_state, kind="default", seed=5, device="cpu"):
+    """A [D, N] fp32.  kinds: default -(n+1); random -exp(U(ln .01, ln 16));
+    long -1e-3 (n+1); zero."""
+    n = torch.arange(1, d_state + 1, dtype=torch.float32, device=device)
+    if kind == "default":
+        return (-n).expand(d_inner, d_state).contiguous()
+    if kind == "long":
+        return (-1e-3 * n).expand(d_inner, d_state).contiguous()
+    if kind == "zero":
+        return torch.zeros(d_inner, d_state, dtype=torch.float32, device=device)
+    if kind == "random":
+        g = _gen(seed, device)
+        u = torch.empty(d_inner, d_state, dtype=torch.float32, device=device)
+        u.uniform_(math.log(0.01), math.log(16.0), generator=g)
+        return -torch.exp(u)
+    raise ValueError("unknown A kind %r" % kind)
+
+
+def stream(batch, T, d_inner, d_state, sid, k0, dtype, device="cpu"):
+    """The four per-token streams (x, dt, B, C) of one segment.
+
+    Seeds 1000*sid + k0 + {0,1,2,3}."""
+    base = 1000 * sid + k0
+    x = normal((batch, T, d_inner), base + 0, device, dtype)
+    dt = positive_step((batch, T, d_inner), base + 1, device, dtype)
+    B = normal((batch, T, d_state), base + 2, device, dtype)
+    C = normal((batch, T, d_state), base + 3, device, dtype)
+    return x, dt, B, C
+
+
+def params(d_inner, d_state, sid, a_kind="default", device="cpu"):
+    """(A [D,N] fp32, Dskip [D] fp32) for workload sid."""
+    A = a_matrix(d_inner, d_state, a_kind, seed=1000 * sid + 5, device=device)
+    Dskip = normal((d_inner,), 1000 * sid + 4, device, torch.float32)
+    return A, Dskip
+
+
+def step_inputs(batch, L, d_inner, d_state, sid, j, dtype, device="cpu"):
+    """Block inputs of the j-th denoising step (seed offset 10+j, 4 seeds each)."""
+    return stream(batch, L, d_inner, d_state, sid, 10 + 4 * j, dtype, device)
+
+
+def commit_inputs(batch, L, d_inner, d_state, sid, i, dtype, device="cpu"):
+    """Clean inputs of the i-th committed block (seed offset 90+i, 4 seeds each)."""
+    return stream(batch, L, d_inner, d_state, sid, 90 + 4 * i, dtype, device)
+
+
+def to_oracle(t):
+    """Marshal a torch tensor for the oracle: fp32 -> float32 array, bf16 ->
+    raw uint16 bit patterns, exactly, on the host."""
+    import numpy as np
+    t = t.detach().to("cpu").contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.numpy()
+    raise TypeError("unsupported dtype %s" % t.dtype)

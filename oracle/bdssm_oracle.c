@@ -1,0 +1,225 @@
+/*
+ * bdssm_oracle.c -- plain, slow, fp64 CPU oracle of the block-restricted
+ * bidirectional selective scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
+ * the benchmark's CPU-baseline leg may load this library.  The GPU library
+ * shares no code, header, table or helper with it, and neither calls the other.
+ *
+ * Pages cited (all describe arXiv 2607.02805, "Training Hybrid Block Diffusion
+ * Language Models with Partial Bidirectionality"):
+ *   [ABS]  the paper's abstract, as printed on the newx.sg page (section
+ *          "Abstract") and on the gptget.net page (section "原文摘要").
+ *   [SUM]  the newx.sg page, section "AI Summary".
+ *   [DE-M] the gist.science German page, "Technische Zusammenfassung",
+ *          subsection "Methodik" (the same text is in "Sintesi Tecnica /
+ *          Metodologia" on the Italian page and "Resumo Técnico /
+ *          Metodologia" on the Portuguese page).
+ *   [DE-P] same page, subsection "Problemstellung".
+ *
+ * What is computed.  The pages name Mamba's linear-time selective state-space
+ * mixer [ABS] but print no formula, no shapes and no precision.  The reading
+ * taken here is the standard Mamba-1 selective scan with a diagonal real A:
+ * for every (batch b, channel d) row and every state n,
+ *     forward:  hf_t[n] = exp(dt_t * A[d,n]) * hf_{t-1}[n] + dt_t * B_t[n] * x_t
+ * (zero-order hold for A, Euler step for B), starting from hf_{-1} = h0
+ * (zero, a supplied initial state, or the prefix cache).
+ * The reverse scan is confined to the active block [ABS], [SUM], [DE-M]: for
+ * each block of L tokens aligned at multiples of L from token 0, a state that
+ * starts at zero after the block's last token runs toward the block's first
+ * token with the same per-token coefficients:
+ *     reverse:  hr_t[n] = exp(dt_t * A[d,n]) * hr_{t+1}[n] + dt_t * B_t[n] * x_t
+ * (so token t is counted in both directions).  The output is
+ *     y_t = sum_n C_t[n] * (hf_t[n] + hr_t[n]) + Dskip[d] * x_t.
+ * The cache is the forward state after the last committed token: it depends
+ * on the clean prefix alone [DE-M]; the reverse state is never cached because
+ * it depends on later tokens of the block [ABS], [DE-P].
+ * Setting L = T reproduces the full-sequence reverse scan of the earlier
+ * bidirectional hybrids the pages contrast with [ABS], [DE-P].
+ *
+ * Everything is fp64; inputs (fp32 or bf16) are widened exactly per element.
+ * Rows are independent, so an OpenMP loop over (b,d) is the only parallelism;
+ * every row is a plain sequential loop over tokens with exp() from libm.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <string.h>
+#include <stdlib.h>
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* exact widening of one input element */
+static double ld(const void *p, size_t i, int dtype)
+{
+    if (dtype == ORACLE_BF16) {
+        uint32_t bits = ((uint32_t)((const uint16_t *)p)[i]) << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float *)p)[i];
+}
+
+int oracle_version(void) { return 1; }
+
+/*
+ * Core routine.  Shapes (row-major, contiguous):
+ *   x, dt: [batch, T, D]     Bm, Cm: [batch, T, N]     A: [D, N]    Dskip: [D]
+ *   h0:    [batch, D, N] or NULL (zero)
+ * Outputs (any may be NULL):
+ *   y, yf, yr: [batch, T, D]  (yf = sum_n C*hf, yr = sum_n C*hr, y = yf+yr+Dskip*x)
+ *   hT:        [batch, D, N]  forward state after token T-1
+ *   bounds:    [batch, T/L+1, D, N]  forward state before token 0 and after
+ *              every L-th token (bounds[:,0] = h0)
+ * L must divide T (L >= 1).  Cm may be NULL only when y, yf and yr are NULL.
+ * Returns 0, or -1 on bad arguments / allocation failure.
+ */
+int oracle_scan(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int dtype,
+                const void *x, const void *dt, const void *Bm, const void *Cm,
+                const float *A, const float *Dskip, const double *h0,
+                double *y, double *yf, double *yr, double *hT, double *bounds)
+{
+    const int want_y = (y != NULL) || (yf != NULL) || (yr != NULL);
+    if (batch < 0 || T < 0 || D < 0 || N < 1 || L < 1) return -1;
+    if (T % L != 0) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    if (T > 0 && (x == NULL || dt == NULL || Bm == NULL)) return -1;
+    if (A == NULL) return -1;
+    if (want_y && T > 0 && (Cm == NULL || Dskip == NULL)) return -1;
+    const int64_t nb = T / L;
+    int fail = 0;
+
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < D; ++d) {
+            double *h = (double *)malloc((size_t)N * sizeof(double));
+            double *r = (double *)malloc((size_t)N * sizeof(double));
+            double *fwd = want_y ? (double *)malloc((size_t)(T > 0 ? T : 1) * sizeof(double)) : NULL;
+            if (!h || !r || (want_y && !fwd)) {
+                free(h); free(r); free(fwd);
+#pragma omp atomic write
+                fail = 1;
+                continue;
+            }
+            for (int64_t n = 0; n < N; ++n)
+                h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
+            if (bounds)
+                for (int64_t n = 0; n < N; ++n)
+                    bounds[((b * (nb + 1) + 0) * D + d) * N + n] = h[n];
+
+            /* forward, causal, over the whole row */
+            for (int64_t t = 0; t < T; ++t) {
+                const size_t ix = (size_t)((b * T + t) * D + d);
+                const size_t ib = (size_t)((b * T + t) * N);
+                const double dtv = ld(dt, ix, dtype);
+                const double xv = ld(x, ix, dtype);
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double decay = exp(dtv * (double)A[d * N + n]);
+                    const double inject = dtv * ld(Bm, ib + n, dtype) * xv;
+                    h[n] = decay * h[n] + inject;
+                    if (want_y) acc += ld(Cm, ib + n, dtype) * h[n];
+                }
+                if (want_y) fwd[t] = acc;
+                if (bounds && (t + 1) % L == 0)
+                    for (int64_t n = 0; n < N; ++n)
+                        bounds[((b * (nb + 1) + (t + 1) / L) * D + d) * N + n] = h[n];
+            }
+            if (hT)
+                for (int64_t n = 0; n < N; ++n) hT[(b * D + d) * N + n] = h[n];
+
+            /* reverse, restricted to each L-token block, from zero at its end */
+            if (want_y) {
+                for (int64_t k = 0; k < nb; ++k) {
+                    for (int64_t n = 0; n < N; ++n) r[n] = 0.0;
+                    for (int64_t t = k * L + L - 1; t >= k * L; --t) {
+                        const size_t ix = (size_t)((b * T + t) * D + d);
+                        const size_t ib = (size_t)((b * T + t) * N);
+                        const double dtv = ld(dt, ix, dtype);
+                        const double xv = ld(x, ix, dtype);
+                        double acc = 0.0;
+                        for (int64_t n = 0; n < N; ++n) {
+                            const double decay = exp(dtv * (double)A[d * N + n]);
+                            const double inject = dtv * ld(Bm, ib + n, dtype) * xv;
+                            r[n] = decay * r[n] + inject;
+                            acc += ld(Cm, ib + n, dtype) * r[n];
+                        }
+                        if (yf) yf[ix] = fwd[t];
+                        if (yr) yr[ix] = acc;
+                        if (y) y[ix] = fwd[t] + acc + (double)Dskip[d] * xv;
+                    }
+                }
+            }
+            free(h); free(r); free(fwd);
+        }
+    }
+    return fail ? -1 : 0;
+}
+
+/* ---- the five entry points, each a composition of the core routine ---- */
+
+/* Clean-context prefill: forward over t_ctx tokens from h_init (NULL = 0);
+ * h_cache <- forward state after the last context token.  When y is given it
+ * also receives the clean-stream output (forward + in-block reverse per
+ * committed block), i.e. what committing the blocks one by one would emit. */
+int oracle_prefill(int64_t batch, int64_t D, int64_t N, int64_t L, int dtype, int64_t t_ctx,
+                   const void *x, const void *dt, const void *Bm, const void *Cm,
+                   const float *A, const float *Dskip, const double *h_init,
+                   double *h_cache, double *y)
+{
+    return oracle_scan(batch, t_ctx, D, N, L, dtype, x, dt, Bm, Cm, A, Dskip, h_init,
+                       y, NULL, NULL, h_cache, NULL);
+}
+
+/* One denoising step on the active block of exactly L tokens: forward from the
+ * cache (not modified) plus the in-block reverse from zero; y: [batch, L, D]. */
+int oracle_block_step(int64_t batch, int64_t D, int64_t N, int64_t L, int dtype,
+                      const double *h_cache, const void *x, const void *dt, const void *Bm,
+                      const void *Cm, const float *A, const float *Dskip, double *y)
+{
+    if (h_cache == NULL || y == NULL) return -1;
+    return oracle_scan(batch, L, D, N, L, dtype, x, dt, Bm, Cm, A, Dskip, h_cache,
+                       y, NULL, NULL, NULL, NULL);
+}
+
+/* Commit a finished block (L clean tokens): h_cache <- forward state after it.
+ * The update is computed into a temporary so that input and output may be the
+ * same buffer.  y (optional) equals block_step on the same inputs. */
+int oracle_commit(int64_t batch, int64_t D, int64_t N, int64_t L, int dtype,
+                  double *h_cache, const void *x, const void *dt, const void *Bm,
+                  const void *Cm, const float *A, const float *Dskip, double *y)
+{
+    if (h_cache == NULL) return -1;
+    const size_t ns = (size_t)(batch * D * N);
+    double *tmp = (double *)malloc((ns ? ns : 1) * sizeof(double));
+    if (!tmp) return -1;
+    int rc = oracle_scan(batch, L, D, N, L, dtype, x, dt, Bm, Cm, A, Dskip, h_cache,
+                         y, NULL, NULL, tmp, NULL);
+    if (rc == 0) memcpy(h_cache, tmp, ns * sizeof(double));
+    free(tmp);
+    return rc;
+}
+
+/* All-block training form: continuous forward over T tokens from h_init
+ * (NULL = 0) plus the reverse segmented into L-token blocks. */
+int oracle_train_scan(int64_t batch, int64_t D, int64_t N, int64_t L, int dtype, int64_t T,
+                      const void *x, const void *dt, const void *Bm, const void *Cm,
+                      const float *A, const float *Dskip, const double *h_init,
+                      double *y, double *h_bounds)
+{
+    return oracle_scan(batch, T, D, N, L, dtype, x, dt, Bm, Cm, A, Dskip, h_init,
+                       y, NULL, NULL, NULL, h_bounds);
+}
+
+/* Full-sequence bidirectional baseline: the reverse runs over the whole
+ * sequence (one segment of length T), forward from zero. */
+int oracle_full_scan(int64_t batch, int64_t D, int64_t N, int dtype, int64_t T,
+                     const void *x, const void *dt, const void *Bm, const void *Cm,
+                     const float *A, const float *Dskip, double *y)
+{
+    if (T == 0) return 0;
+    return oracle_scan(batch, T, D, N, T, dtype, x, dt, Bm, Cm, A, Dskip, NULL,
+                       y, NULL, NULL, NULL, NULL);
+}

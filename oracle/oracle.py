@@ -1,0 +1,136 @@
+"""ctypes marshalling for the fp64 oracle (TEST INFRASTRUCTURE ONLY).
+
+Inputs are numpy arrays: float32, or bfloat16 passed as their raw uint16 bit
+patterns (``dtype=np.uint16``).  A and Dskip are float32.  States and every
+output are float64.  Shapes follow the library: x, dt, y: [batch, T, D];
+B, C: [batch, T, N]; A: [D, N]; Dskip: [D]; states: [batch, D, N].
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+F32 = 0
+BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "bdssm_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force=True):
+    """Compile the C oracle into oracle/liboracle.so with gcc + OpenMP."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int64
+        lib.oracle_scan.argtypes = [I, I, I, I, I, ctypes.c_int] + [P] * 12
+        lib.oracle_scan.restype = ctypes.c_int
+        lib.oracle_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(a):
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError("oracle inputs must be float32 or bf16 bits (uint16), got %s" % a.dtype)
+
+
+def _c(a, dt=None):
+    if a is None:
+        return None
+    a = np.asarray(a)
+    if dt is not None:
+        a = a.astype(dt, copy=False)
+    return np.ascontiguousarray(a)
+
+
+def scan(x, dt, B, C, A, Dskip, L, h0=None, want_y=True, want_parts=False, want_bounds=False):
+    """Core oracle: continuous forward from h0, reverse segmented into L-token
+    blocks.  Returns a dict with 'y' (and 'yf', 'yr' if want_parts), 'hT',
+    and 'bounds' ([batch, T/L+1, D, N]) if want_bounds."""
+    x, dt, B = _c(x), _c(dt), _c(B)
+    C = _c(C)
+    A = _c(A, np.float32)
+    Dskip = _c(Dskip, np.float32)
+    h0 = _c(h0, np.float64)
+    code = _dtype_code(x)
+    for a in (dt, B) + ((C,) if C is not None else ()):
+        if a.dtype != x.dtype:
+            raise TypeError("x, dt, B, C must share one dtype")
+    batch, T, D = x.shape
+    N = A.shape[1]
+    assert dt.shape == (batch, T, D) and B.shape == (batch, T, N) and A.shape == (D, N)
+    if C is not None:
+        assert C.shape == (batch, T, N)
+    if h0 is not None:
+        assert h0.shape == (batch, D, N)
+    out = {"hT": np.empty((batch, D, N), np.float64)}
+    y = yf = yr = bounds = None
+    if want_y:
+        y = out["y"] = np.empty((batch, T, D), np.float64)
+        if want_parts:
+            yf = out["yf"] = np.empty((batch, T, D), np.float64)
+            yr = out["yr"] = np.empty((batch, T, D), np.float64)
+    if want_bounds:
+        bounds = out["bounds"] = np.empty((batch, T // L + 1, D, N), np.float64)
+    rc = load().oracle_scan(batch, T, D, N, L, code, _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
+                            _ptr(A), _ptr(Dskip), _ptr(h0), _ptr(y), _ptr(yf), _ptr(yr),
+                            _ptr(out["hT"]), _ptr(bounds))
+    if rc != 0:
+        raise ValueError("oracle_scan rejected its arguments (rc=%d)" % rc)
+    return out
+
+
+def prefill(x, dt, B, C, A, Dskip, L, h_init=None, want_y=False):
+    """Clean-context prefill -> (h_cache, y or None)."""
+    r = scan(x, dt, B, C, A, Dskip, L, h0=h_init, want_y=want_y)
+    return r["hT"], r.get("y")
+
+
+def block_step(h_cache, x, dt, B, C, A, Dskip):
+    """One denoising step on an L-token block (L = x.shape[1]) -> y."""
+    L = x.shape[1]
+    return scan(x, dt, B, C, A, Dskip, L, h0=h_cache, want_y=True)["y"]
+
+
+def commit(h_cache, x, dt, B, C, A, Dskip, want_y=False):
+    """Finalise an L-token block -> (new h_cache, y or None)."""
+    L = x.shape[1]
+    r = scan(x, dt, B, C, A, Dskip, L, h0=h_cache, want_y=want_y)
+    return r["hT"], r.get("y")
+
+
+def train_scan(x, dt, B, C, A, Dskip, L, h_init=None, want_bounds=False):
+    """All-block training form -> (y, h_bounds or None)."""
+    r = scan(x, dt, B, C, A, Dskip, L, h0=h_init, want_y=True, want_bounds=want_bounds)
+    return r["y"], r.get("bounds")
+
+
+def full_scan(x, dt, B, C, A, Dskip):
+    """Full-sequence bidirectional baseline (reverse over the whole row) -> y."""
+    T = x.shape[1]
+    return scan(x, dt, B, C, A, Dskip, max(T, 1), h0=None, want_y=True)["y"]
