@@ -1,0 +1,170 @@
+/*
+ * bdssm.h -- C ABI of the block-restricted bidirectional selective scan for
+ * MI355X (gfx950).
+ *
+ * Pages cited (all describe arXiv 2607.02805, "Training Hybrid Block Diffusion
+ * Language Models with Partial Bidirectionality"):
+ *   [ABS]  the paper's abstract (newx.sg page, section "Abstract"; identical on
+ *          the gptget.net page, section "原文摘要").
+ *   [SUM]  newx.sg page, section "AI Summary".
+ *   [DE-M] gist.science German page, "Technische Zusammenfassung" >
+ *          "Methodik" (same text: Italian "Sintesi Tecnica" > "Metodologia",
+ *          Portuguese "Resumo Técnico" > "Metodologia").
+ *   [DE-P] same page, "Problemstellung".
+ *
+ * The operation.  Mamba's selective state-space mixer [ABS] with a diagonal
+ * real A; the pages print no formula, so the standard Mamba-1 discretisation
+ * is used (zero-order hold for A, Euler step for B).  For each (batch b,
+ * channel d) row and state n (0 <= n < 16):
+ *   forward:  hf_t = exp(dt_t A[d,n]) hf_{t-1} + dt_t B_t[n] x_t   (causal,
+ *             over the whole sequence, starting from h0)
+ *   reverse:  hr_t = exp(dt_t A[d,n]) hr_{t+1} + dt_t B_t[n] x_t   confined to
+ *             the active L-token block and starting from zero after the
+ *             block's last token [ABS], [SUM], [DE-M]
+ *   output:   y_t  = sum_n C_t[n] (hf_t + hr_t) + Dskip[d] x_t
+ * The prefix cache is the forward state after the last committed token; it is
+ * a function of the clean prefix alone and takes no diffusion timestep
+ * [DE-M].  The reverse state is never cached: it depends on later tokens of
+ * the block [ABS], [DE-P].  Blocks are aligned at multiples of L from token 0.
+ *
+ * Layouts (row-major, contiguous, token-major):
+ *   x, dt, y : [batch, T, d_inner]   dtype = shape->dtype (fp32 or bf16)
+ *   B, C     : [batch, T, d_state]   same dtype (shared by all channels)
+ *   A        : [d_inner, d_state]    fp32 (any values; not assumed structured)
+ *   Dskip    : [d_inner]             fp32
+ *   states   : [batch, d_inner, d_state] fp32
+ *   h_bounds : [batch, T/L + 1, d_inner, d_state] fp32
+ * dt is the positive step size, already passed through softplus by the
+ * caller.  bf16 outputs are rounded to nearest even from fp32.
+ *
+ * Ownership and execution.  Every pointer is caller-owned device memory on the
+ * current HIP device with a 16-byte aligned base.  The library allocates
+ * nothing; entry points that need scratch take a caller-supplied workspace
+ * sized by bdssm_workspace_bytes().  There is no global mutable state, so
+ * calls on different streams are independent as long as they do not share
+ * output or workspace buffers.  Work is enqueued on `stream` (a hipStream_t;
+ * NULL = the null stream) and returns without waiting.
+ *
+ * Errors.  Every entry point returns an int status (bdssm_status).  Argument
+ * checks run on the host before any HIP call, so a rejected call enqueues
+ * nothing.  BDSSM_ERR_HIP reports a failed launch; faults inside a kernel
+ * surface at the caller's next synchronisation.  No C++ exception crosses
+ * this interface.  Outputs must not overlap inputs (only h_cache of
+ * bdssm_commit is read and written in place).
+ *
+ * Limits of this version: d_state == 16; block_len in {1, 2, 4, 8, 16};
+ * T % block_len == 0; x, dt, B, C and y share one dtype.
+ */
+#ifndef BDSSM_H
+#define BDSSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BDSSM_OK = 0,
+    BDSSM_ERR_NULL = -1,      /* a required pointer is NULL */
+    BDSSM_ERR_SHAPE = -2,     /* unsupported or inconsistent sizes */
+    BDSSM_ERR_DTYPE = -3,     /* unknown dtype code */
+    BDSSM_ERR_ALIGN = -4,     /* a base pointer is not 16-byte aligned */
+    BDSSM_ERR_WORKSPACE = -5, /* workspace missing or smaller than required */
+    BDSSM_ERR_HIP = -6,       /* a HIP launch or runtime call failed */
+    BDSSM_ERR_ALIAS = -7      /* an output overlaps an input */
+} bdssm_status;
+
+typedef enum { BDSSM_F32 = 0, BDSSM_BF16 = 1 } bdssm_dtype;
+
+/* Which entry point a workspace is sized for. */
+typedef enum { BDSSM_OP_PREFILL = 0, BDSSM_OP_TRAIN = 1, BDSSM_OP_FULL = 2 } bdssm_op;
+
+typedef struct {
+    int64_t batch;     /* >= 0 */
+    int64_t d_inner;   /* channels D, >= 0 */
+    int64_t d_state;   /* states N, must be 16 */
+    int64_t block_len; /* L, the denoising block length */
+    int32_t dtype;     /* bdssm_dtype of x, dt, B, C, y */
+} bdssm_shape;
+
+/*
+ * Prefill a clean context of t_ctx tokens (a multiple of L) [DE-M]: the
+ * prefix cache is built by scanning the clean prefix forward.
+ *   h_init  [batch,D,N] forward state before the first token, or NULL (zero).
+ *   h_cache [batch,D,N] out: forward state after the last token.  May equal
+ *           h_init (in place).
+ *   y       NULL (state only), or [batch,t_ctx,D] out: the clean-stream output,
+ *           forward plus reverse within each L-block, i.e. what committing the
+ *           blocks one at a time with y would emit.  C may be NULL iff y is.
+ *   ws      workspace of ws_bytes >= bdssm_workspace_bytes(shape, t_ctx,
+ *           BDSSM_OP_PREFILL).
+ */
+int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const void *dt,
+                  const void *B, const void *C, const float *A, const float *Dskip,
+                  const float *h_init, float *h_cache, void *y, void *ws, size_t ws_bytes,
+                  void *stream);
+
+/*
+ * One denoising step on the active block (exactly L tokens) [ABS], [DE-M]:
+ * forward from the cache plus the reverse confined to the block.
+ *   h_cache [batch,D,N] in, read only.
+ *   x, dt   [batch,L,D];  B, C [batch,L,N];  y [batch,L,D] out.
+ */
+int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void *x,
+                     const void *dt, const void *B, const void *C, const float *A,
+                     const float *Dskip, void *y, void *stream);
+
+/*
+ * Commit a finished block (its final clean inputs, L tokens) [DE-M]: the
+ * forward boundary state advances over the block, in place.
+ *   h_cache [batch,D,N] in/out.
+ *   y       NULL, or [batch,L,D] out, equal to block_step on the same inputs
+ *           and the cache as it was before the call.  C may be NULL iff y is.
+ */
+int bdssm_commit(const bdssm_shape *shape, float *h_cache, const void *x, const void *dt,
+                 const void *B, const void *C, const float *A, const float *Dskip, void *y,
+                 void *stream);
+
+/*
+ * All-block training form over T tokens [DE-M]: the forward scan runs over
+ * the whole sequence from h_init (NULL = zero) and the reverse is segmented
+ * into L-token blocks.
+ *   y        [batch,T,D] out.
+ *   h_bounds NULL, or [batch,T/L+1,D,N] out: the forward state before token 0
+ *            and after every L-th token (the per-block prefix caches).
+ *   ws       ws_bytes >= bdssm_workspace_bytes(shape, T, BDSSM_OP_TRAIN).
+ */
+int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
+                     const void *B, const void *C, const float *A, const float *Dskip,
+                     const float *h_init, void *y, float *h_bounds, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/*
+ * Baseline: the full-sequence bidirectional scan of the earlier diffusion
+ * hybrids the pages contrast with [ABS], [DE-P], i.e. the training form with a
+ * single block of length T (reverse over the whole sequence), forward from
+ * zero.  block_len is ignored.
+ *   y   [batch,T,D] out.
+ *   ws  ws_bytes >= bdssm_workspace_bytes(shape, T, BDSSM_OP_FULL).
+ */
+int bdssm_full_scan(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
+                    const void *B, const void *C, const float *A, const float *Dskip, void *y,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes the given entry point needs at sequence length T (0 if none;
+ * (size_t)-1 if the shape is invalid). */
+size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T, int op);
+
+/* Static, human-readable text for a status code. */
+const char *bdssm_status_str(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int bdssm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BDSSM_H */

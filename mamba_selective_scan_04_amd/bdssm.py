@@ -1,0 +1,237 @@
+"""ctypes binding of libbdssm.so.  Argument marshalling only.
+
+Names and semantics follow include/bdssm.h:
+  prefill(x, dt, B, C, A, Dskip, block_len, h_init=None, h_cache=None, y=None, want_y=False)
+  block_step(h_cache, x, dt, B, C, A, Dskip, y=None)
+  commit(h_cache, x, dt, B, C, A, Dskip, want_y=False, y=None)
+  train_scan(x, dt, B, C, A, Dskip, block_len, h_init=None, want_bounds=False, y=None, h_bounds=None)
+  full_scan(x, dt, B, C, A, Dskip, y=None)
+Shapes: x, dt, y [batch, T, D]; B, C [batch, T, 16]; A [D, 16] fp32;
+Dskip [D] fp32; states [batch, D, 16] fp32.  x/dt/B/C/y share fp32 or bf16.
+All tensors must be contiguous, on the current CUDA (HIP) device.  Work is
+enqueued on torch's current stream; nothing synchronises.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbdssm.so")
+
+F32 = 0
+BF16 = 1
+OP_PREFILL, OP_TRAIN, OP_FULL = 0, 1, 2
+EXPORTS = ("bdssm_prefill", "bdssm_block_step", "bdssm_commit", "bdssm_train_scan",
+           "bdssm_full_scan", "bdssm_workspace_bytes", "bdssm_status_str", "bdssm_version")
+
+
+class BdssmError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__("%s failed: %s (status %d)" % (fn, msg, status))
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("d_inner", ctypes.c_int64),
+                ("d_state", ctypes.c_int64), ("block_len", ctypes.c_int64),
+                ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load():
+    """Load libbdssm.so (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libbdssm.so not built: run `python -m mamba_selective_scan_04_amd.build` "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, S = ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(Shape)
+    Z = ctypes.c_size_t
+    lib.bdssm_prefill.argtypes = [S, I, P, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.bdssm_block_step.argtypes = [S, P, P, P, P, P, P, P, P, P]
+    lib.bdssm_commit.argtypes = [S, P, P, P, P, P, P, P, P, P]
+    lib.bdssm_train_scan.argtypes = [S, I, P, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.bdssm_full_scan.argtypes = [S, I, P, P, P, P, P, P, P, P, Z, P]
+    for f in ("bdssm_prefill", "bdssm_block_step", "bdssm_commit", "bdssm_train_scan",
+              "bdssm_full_scan", "bdssm_version"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.bdssm_workspace_bytes.argtypes = [S, I, ctypes.c_int]
+    lib.bdssm_workspace_bytes.restype = ctypes.c_size_t
+    lib.bdssm_status_str.argtypes = [ctypes.c_int]
+    lib.bdssm_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def version():
+    return load().bdssm_version()
+
+
+def status_str(status):
+    return load().bdssm_status_str(int(status)).decode()
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("x/dt/B/C must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype=None, shape=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU (got %s)" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _shape(batch, D, N, L, code):
+    return Shape(batch, D, N, L, code)
+
+
+def _raise(fn, rc):
+    if rc != 0:
+        raise BdssmError(fn, rc, status_str(rc))
+
+
+def _streams(x, dt, B, C, A, Dskip, need_c=True):
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, T, D]")
+    batch, T, D = x.shape
+    _check(x, "x")
+    code = _dtype_code(x)
+    _check(dt, "dt", x.dtype, (batch, T, D))
+    _check(B, "B", x.dtype)
+    if B.dim() != 3 or B.shape[0] != batch or B.shape[1] != T:
+        raise ValueError("B must be [batch, T, d_state]")
+    N = B.shape[2]
+    if need_c or C is not None:
+        _check(C, "C", x.dtype, (batch, T, N))
+    _check(A, "A", torch.float32, (D, N))
+    if Dskip is not None:
+        _check(Dskip, "Dskip", torch.float32, (D,))
+    return batch, T, D, N, code
+
+
+def workspace_bytes(batch, d_inner, T, op, block_len=16, d_state=16, dtype=torch.bfloat16):
+    s = _shape(batch, d_inner, d_state, block_len, BF16 if dtype == torch.bfloat16 else F32)
+    n = load().bdssm_workspace_bytes(ctypes.byref(s), T, op)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid shape for workspace query")
+    return n
+
+
+def _workspace(nbytes, device):
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def prefill(x, dt, B, C, A, Dskip, block_len, h_init=None, h_cache=None, y=None, want_y=False,
+            ws=None):
+    """Build the prefix cache over a clean context -> (h_cache, y or None)."""
+    batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip, need_c=want_y or y is not None)
+    want_y = want_y or y is not None
+    _check(h_init, "h_init", torch.float32, (batch, D, N))
+    if h_cache is None:
+        h_cache = torch.empty(batch, D, N, dtype=torch.float32, device=x.device)
+    _check(h_cache, "h_cache", torch.float32, (batch, D, N))
+    if want_y and y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", x.dtype, (batch, T, D))
+    s = _shape(batch, D, N, block_len, code)
+    if ws is None:
+        ws = _workspace(workspace_bytes(batch, D, T, OP_PREFILL, block_len, N, x.dtype), x.device)
+    rc = load().bdssm_prefill(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A), _p(Dskip),
+                              _p(h_init), _p(h_cache), _p(y), _p(ws),
+                              0 if ws is None else ws.numel(), _stream())
+    _raise("bdssm_prefill", rc)
+    return h_cache, y
+
+
+def block_step(h_cache, x, dt, B, C, A, Dskip, y=None):
+    """One denoising step on the active block (T == block_len) -> y."""
+    batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip)
+    _check(h_cache, "h_cache", torch.float32, (batch, D, N))
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", x.dtype, (batch, T, D))
+    s = _shape(batch, D, N, T, code)
+    rc = load().bdssm_block_step(ctypes.byref(s), _p(h_cache), _p(x), _p(dt), _p(B), _p(C), _p(A),
+                                 _p(Dskip), _p(y), _stream())
+    _raise("bdssm_block_step", rc)
+    return y
+
+
+def commit(h_cache, x, dt, B, C, A, Dskip, want_y=False, y=None):
+    """Advance the cache over a finished block, in place -> (h_cache, y or None)."""
+    want_y = want_y or y is not None
+    batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip, need_c=want_y)
+    _check(h_cache, "h_cache", torch.float32, (batch, D, N))
+    if want_y and y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", x.dtype, (batch, T, D))
+    s = _shape(batch, D, N, T, code)
+    rc = load().bdssm_commit(ctypes.byref(s), _p(h_cache), _p(x), _p(dt), _p(B), _p(C), _p(A),
+                             _p(Dskip), _p(y), _stream())
+    _raise("bdssm_commit", rc)
+    return h_cache, y
+
+
+def train_scan(x, dt, B, C, A, Dskip, block_len, h_init=None, want_bounds=False, y=None,
+               h_bounds=None, ws=None):
+    """All-block training form -> (y, h_bounds or None)."""
+    batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip)
+    _check(h_init, "h_init", torch.float32, (batch, D, N))
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", x.dtype, (batch, T, D))
+    if want_bounds and h_bounds is None:
+        h_bounds = torch.empty(batch, T // block_len + 1, D, N, dtype=torch.float32, device=x.device)
+    if h_bounds is not None:
+        _check(h_bounds, "h_bounds", torch.float32, (batch, T // block_len + 1, D, N))
+    s = _shape(batch, D, N, block_len, code)
+    if ws is None:
+        ws = _workspace(workspace_bytes(batch, D, T, OP_TRAIN, block_len, N, x.dtype), x.device)
+    rc = load().bdssm_train_scan(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A),
+                                 _p(Dskip), _p(h_init), _p(y), _p(h_bounds), _p(ws),
+                                 0 if ws is None else ws.numel(), _stream())
+    _raise("bdssm_train_scan", rc)
+    return y, h_bounds
+
+
+def full_scan(x, dt, B, C, A, Dskip, y=None, ws=None):
+    """Full-sequence bidirectional baseline (reverse over the whole sequence) -> y."""
+    batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", x.dtype, (batch, T, D))
+    s = _shape(batch, D, N, 1, code)
+    if ws is None:
+        ws = _workspace(workspace_bytes(batch, D, T, OP_FULL, 1, N, x.dtype), x.device)
+    rc = load().bdssm_full_scan(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A), _p(Dskip),
+                                _p(y), _p(ws), 0 if ws is None else ws.numel(), _stream())
+    _raise("bdssm_full_scan", rc)
+    return y

@@ -1,0 +1,533 @@
+// bdssm.hip -- C ABI, argument checks and launch policy of the
+// block-restricted bidirectional selective scan on MI355X (gfx950).
+//
+// Pages cited (arXiv 2607.02805, "Training Hybrid Block Diffusion Language
+// Models with Partial Bidirectionality"):
+//   [ABS]  the paper's abstract (newx.sg page, "Abstract").
+//   [DE-M] gist.science German page, "Technische Zusammenfassung" > "Methodik".
+//   [DE-P] same page, "Problemstellung".
+//
+// Each entry point validates every argument on the host before the first HIP
+// call, then enqueues a fixed sequence of kernels on the caller's stream:
+//   prefill (state only): chunk aggregates + carry            [DE-M] cache built
+//                                                             from the clean prefix
+//   prefill (with y), train_scan: chunk aggregates + carry + bidirectional pass
+//   block_step: one bidirectional pass over one block from the cache [ABS]
+//   commit: one forward pass over one block, cache updated in place [DE-M]
+//   full_scan (baseline): forward and reverse aggregates + both carries +
+//                         a forward output sweep + a reverse output sweep [DE-P]
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <initializer_list>
+
+#include "bdssm.h"
+#include "bdssm_kernels.hpp"
+
+using namespace bdssm_dev;
+
+namespace {
+
+constexpr int kVersion = 10000;   // 1.0.0
+
+// ------------------------------------------------------------ launch policy
+//
+// Chunking of the time axis.  The per-token loop is sequential per channel,
+// so a launch has batch * ceil(D/64) waves per chunk; long sequences are cut
+// into chunks until the chip is full.
+//   fine chunks  (one wave per 64 channels, 16 states per lane): aim for
+//                kFineWaves waves in flight, ~8 per SIMD on 256 CUs.
+//   coarse chunks (bidirectional pass, 4 waves per 64 channels): aim for
+//                kCoarseGroups workgroups, 2 per CU, each a whole number of
+//                fine chunks so its incoming state is a fine-chunk boundary.
+// Every chunk is a multiple of 16 tokens, so blocks of L | 16 never straddle.
+// BDSSM_FINE_WAVES / BDSSM_COARSE_GROUPS / BDSSM_CHUNK (fine chunk length in
+// tokens) override the targets; they exist for tuning sweeps and for the
+// chunk-invariance tests.
+struct Plan {
+    int64_t fine_len;    // tokens per fine chunk (multiple of 16)
+    int n_fine;          // number of fine chunks
+    int per_coarse;      // fine chunks per coarse chunk
+    int n_coarse;        // number of coarse chunks
+};
+
+int64_t env_int(const char *name, int64_t dflt) {
+    const char *s = getenv(name);
+    if (s == nullptr || *s == 0) return dflt;
+    char *end = nullptr;
+    long long v = strtoll(s, &end, 10);
+    return (end != s && v > 0) ? (int64_t)v : dflt;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+Plan make_plan(int64_t batch, int64_t D, int64_t T) {
+    Plan p{};
+    const int64_t groups = batch * ceil_div(D, kWave);
+    const int64_t ngroups16 = ceil_div(T, kGroup);
+    if (T == 0 || groups == 0) {
+        p.fine_len = kGroup; p.n_fine = 1; p.per_coarse = 1; p.n_coarse = 1;
+        return p;
+    }
+    const int64_t fine_waves = env_int("BDSSM_FINE_WAVES", 8192);
+    const int64_t coarse_groups = env_int("BDSSM_COARSE_GROUPS", 512);
+    int64_t nf = ceil_div(fine_waves, groups);
+    if (nf > ngroups16) nf = ngroups16;
+    if (nf < 1) nf = 1;
+    int64_t fl = ceil_div(ngroups16, nf) * kGroup;
+    const int64_t forced = env_int("BDSSM_CHUNK", 0);
+    if (forced > 0) fl = ceil_div(forced, kGroup) * kGroup;
+    if (ceil_div(T, fl) > 65535) fl = ceil_div(ceil_div(T, 65535), kGroup) * kGroup;
+    nf = ceil_div(T, fl);
+    int64_t nc = ceil_div(coarse_groups, groups);
+    if (nc > nf) nc = nf;
+    if (nc < 1) nc = 1;
+    const int64_t per = ceil_div(nf, nc);
+    nc = ceil_div(nf, per);
+    p.fine_len = fl;
+    p.n_fine = (int)nf;
+    p.per_coarse = (int)per;
+    p.n_coarse = (int)nc;
+    return p;
+}
+
+// Workspace layout (fp32 arrays, each 256-byte aligned):
+//   agg_h [batch, n_fine, D, 16], agg_s [batch, n_fine, D], h_in [batch, n_fine, D, 16]
+//   full scan adds ragg_h, ragg_s, hr_in (same sizes) and yf [batch, T, D].
+struct Workspace {
+    float *agg_h, *agg_s, *h_in, *ragg_h, *ragg_s, *hr_in, *yf;
+    size_t bytes;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Workspace layout_ws(void *base, int64_t batch, int64_t D, int64_t T, const Plan &p, int op) {
+    Workspace w{};
+    const size_t nh = (size_t)batch * p.n_fine * D * kStates * sizeof(float);
+    const size_t ns = (size_t)batch * p.n_fine * D * sizeof(float);
+    size_t off = 0;
+    auto take = [&](size_t n) -> float * {
+        float *r = base ? reinterpret_cast<float *>(static_cast<char *>(base) + off) : nullptr;
+        off += align256(n);
+        return r;
+    };
+    const bool chunked = p.n_fine > 1;
+    if (op == BDSSM_OP_PREFILL || op == BDSSM_OP_TRAIN) {
+        if (chunked) { w.agg_h = take(nh); w.agg_s = take(ns); w.h_in = take(nh); }
+    } else if (op == BDSSM_OP_FULL) {
+        w.agg_h = take(nh); w.agg_s = take(ns); w.h_in = take(nh);
+        w.ragg_h = take(nh); w.ragg_s = take(ns); w.hr_in = take(nh);
+        w.yf = take((size_t)batch * T * D * sizeof(float));
+    }
+    w.bytes = off;
+    return w;
+}
+
+// ---------------------------------------------------------------- checking
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range { const void *p; size_t n; };
+
+bool overlaps(Range a, Range b) {
+    if (a.p == nullptr || b.p == nullptr || a.n == 0 || b.n == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+int check_shape(const bdssm_shape *s) {
+    if (s == nullptr) return BDSSM_ERR_NULL;
+    if (s->dtype != BDSSM_F32 && s->dtype != BDSSM_BF16) return BDSSM_ERR_DTYPE;
+    if (s->batch < 0 || s->d_inner < 0) return BDSSM_ERR_SHAPE;
+    if (s->d_state != kStates) return BDSSM_ERR_SHAPE;
+    const int64_t L = s->block_len;
+    if (!(L == 1 || L == 2 || L == 4 || L == 8 || L == 16)) return BDSSM_ERR_SHAPE;
+    if (s->d_inner > (int64_t)1 << 30 || s->batch > 65535) return BDSSM_ERR_SHAPE;
+    return BDSSM_OK;
+}
+
+size_t esize(const bdssm_shape *s) { return s->dtype == BDSSM_BF16 ? 2 : 4; }
+
+// Shared checks of the per-token streams of one call covering T tokens.
+int check_streams(const bdssm_shape *s, int64_t T, const void *x, const void *dt, const void *B,
+                  const void *C, bool need_c, const float *A, const float *Dskip, bool need_dskip) {
+    const bool nonempty = s->batch > 0 && s->d_inner > 0 && T > 0;
+    if (!nonempty) return BDSSM_OK;
+    if (!x || !dt || !B || !A || (need_c && !C) || (need_dskip && !Dskip)) return BDSSM_ERR_NULL;
+    const void *ps[] = {x, dt, B, C, A, Dskip};
+    for (const void *p : ps)
+        if (p && !aligned16(p)) return BDSSM_ERR_ALIGN;
+    if (T > ((int64_t)1 << 40) / (s->batch * s->d_inner)) return BDSSM_ERR_SHAPE;
+    if (s->d_inner * ceil_div(T, kGroup) > ((int64_t)1 << 40)) return BDSSM_ERR_SHAPE;
+    return BDSSM_OK;
+}
+
+// Outputs must not overlap any input.
+int check_alias(const bdssm_shape *s, int64_t T, const void *x, const void *dt, const void *B,
+                const void *C, const float *A, const float *Dskip, const float *h_src,
+                std::initializer_list<Range> outs) {
+    const size_t e = esize(s);
+    const size_t nx = (size_t)s->batch * T * s->d_inner * e;
+    const size_t nb = (size_t)s->batch * T * kStates * e;
+    const Range ins[] = {{x, nx}, {dt, nx}, {B, nb}, {C, nb},
+                         {A, (size_t)s->d_inner * kStates * 4}, {Dskip, (size_t)s->d_inner * 4},
+                         {h_src, (size_t)s->batch * s->d_inner * kStates * 4}};
+    for (const Range &o : outs) {
+        for (const Range &i : ins)
+            if (overlaps(o, i)) return BDSSM_ERR_ALIAS;
+    }
+    // outputs among themselves
+    const Range *ob = outs.begin();
+    for (size_t i = 0; i < outs.size(); ++i)
+        for (size_t j = i + 1; j < outs.size(); ++j)
+            if (overlaps(ob[i], ob[j])) return BDSSM_ERR_ALIAS;
+    return BDSSM_OK;
+}
+
+int launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? BDSSM_OK : BDSSM_ERR_HIP;
+}
+
+// dst <- src (or zeros); src may equal dst.
+int copy_or_zero(const float *src, float *dst, int64_t n, hipStream_t st) {
+    (void)hipGetLastError();
+    if (src == dst || n == 0) return BDSSM_OK;
+    hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, src,
+                       dst, n);
+    return launch_status();
+}
+
+dim3 grid3(int64_t D, int64_t chunks, int64_t batch) {
+    return dim3((unsigned)ceil_div(D, kWave), (unsigned)chunks, (unsigned)batch);
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <typename Tin>
+void launch_chunk_state(bool rev, const void *x, const void *dt, const void *B, const float *A,
+                        const float *h0, float *hout, float *sout, int64_t batch, int64_t T,
+                        int64_t D, int64_t Tc, int n_chunks, int c_first, int n_launch,
+                        hipStream_t st) {
+    if (n_launch <= 0) return;
+    const dim3 g = grid3(D, n_launch, batch);
+    if (rev)
+        hipLaunchKernelGGL((chunk_state_kernel<Tin, true>), g, dim3(kWave), 0, st,
+                           (const Tin *)x, (const Tin *)dt, (const Tin *)B, A, h0, hout, sout, T,
+                           (int)D, Tc, n_chunks, c_first);
+    else
+        hipLaunchKernelGGL((chunk_state_kernel<Tin, false>), g, dim3(kWave), 0, st,
+                           (const Tin *)x, (const Tin *)dt, (const Tin *)B, A, h0, hout, sout, T,
+                           (int)D, Tc, n_chunks, c_first);
+}
+
+void launch_carry(bool rev, const float *agg_h, const float *agg_s, const float *A,
+                  const float *h_init, float *h_in, float *h_final, int64_t batch, int64_t D,
+                  int n_chunks, int n_agg, hipStream_t st) {
+    const int64_t total = batch * D * kStates;
+    const dim3 g((unsigned)ceil_div(total, 256));
+    if (rev)
+        hipLaunchKernelGGL((carry_kernel<true>), g, dim3(256), 0, st, agg_h, agg_s, A, h_init, h_in,
+                           h_final, (int)batch, (int)D, n_chunks, n_agg);
+    else
+        hipLaunchKernelGGL((carry_kernel<false>), g, dim3(256), 0, st, agg_h, agg_s, A, h_init, h_in,
+                           h_final, (int)batch, (int)D, n_chunks, n_agg);
+}
+
+template <typename Tin, int L>
+void launch_bidir_L(const void *x, const void *dt, const void *B, const void *C, const float *A,
+                    const float *Dskip, const float *hin, int64_t hin_bs, int64_t hin_cs, void *y,
+                    float *bounds, float *hout, int64_t batch, int64_t T, int64_t D, int64_t Tc,
+                    int n_chunks, hipStream_t st) {
+    hipLaunchKernelGGL((bidir_kernel<Tin, L>), grid3(D, n_chunks, batch), dim3(kWave * kWavesBidir),
+                       0, st, (const Tin *)x, (const Tin *)dt, (const Tin *)B, (const Tin *)C, A,
+                       Dskip, hin, hin_bs, hin_cs, (Tin *)y, bounds, hout, T, (int)D, Tc);
+}
+
+template <typename Tin>
+void launch_bidir(int64_t L, const void *x, const void *dt, const void *B, const void *C,
+                  const float *A, const float *Dskip, const float *hin, int64_t hin_bs,
+                  int64_t hin_cs, void *y, float *bounds, float *hout, int64_t batch, int64_t T,
+                  int64_t D, int64_t Tc, int n_chunks, hipStream_t st) {
+    switch (L) {
+    case 1: launch_bidir_L<Tin, 1>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, st); break;
+    case 2: launch_bidir_L<Tin, 2>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, st); break;
+    case 4: launch_bidir_L<Tin, 4>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, st); break;
+    case 8: launch_bidir_L<Tin, 8>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, st); break;
+    default: launch_bidir_L<Tin, 16>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, st); break;
+    }
+}
+
+template <typename Tin>
+void launch_sweep(bool rev, const void *x, const void *dt, const void *B, const void *C,
+                  const float *A, const float *Dskip, const float *hin, float *yf, void *y,
+                  int64_t batch, int64_t T, int64_t D, int64_t Tc, int n_chunks, hipStream_t st) {
+    const dim3 g = grid3(D, n_chunks, batch);
+    if (rev)
+        hipLaunchKernelGGL((sweep_output_kernel<Tin, true>), g, dim3(kWave), 0, st, (const Tin *)x,
+                           (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip, hin, yf,
+                           (Tin *)y, T, (int)D, Tc, n_chunks);
+    else
+        hipLaunchKernelGGL((sweep_output_kernel<Tin, false>), g, dim3(kWave), 0, st, (const Tin *)x,
+                           (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip, hin, yf,
+                           (Tin *)y, T, (int)D, Tc, n_chunks);
+}
+
+// Forward state only over T tokens from h_init: h_final <- state after T.
+template <typename Tin>
+void run_state_only(const bdssm_shape *s, int64_t T, const void *x, const void *dt, const void *B,
+                    const float *A, const float *h_init, float *h_final, const Workspace &w,
+                    const Plan &p, hipStream_t st) {
+    const int64_t batch = s->batch, D = s->d_inner;
+    if (p.n_fine == 1) {
+        // one chunk: scan directly from h_init into h_final (same-lane read then write)
+        launch_chunk_state<Tin>(false, x, dt, B, A, h_init, h_final, nullptr, batch, T, D,
+                                p.fine_len, 1, 0, 1, st);
+        return;
+    }
+    launch_chunk_state<Tin>(false, x, dt, B, A, nullptr, w.agg_h, w.agg_s, batch, T, D,
+                            p.fine_len, p.n_fine, 0, p.n_fine, st);
+    launch_carry(false, w.agg_h, w.agg_s, A, h_init, nullptr, h_final, batch, D, p.n_fine,
+                 p.n_fine, st);
+}
+
+// Forward over T tokens from h_init with the in-block reverse and the output.
+template <typename Tin>
+void run_bidirectional(const bdssm_shape *s, int64_t T, const void *x, const void *dt,
+                       const void *B, const void *C, const float *A, const float *Dskip,
+                       const float *h_init, void *y, float *bounds, float *h_final,
+                       const Workspace &w, const Plan &p, hipStream_t st) {
+    const int64_t batch = s->batch, D = s->d_inner;
+    const int64_t hs = D * kStates;
+    if (p.n_coarse == 1) {
+        launch_bidir<Tin>(s->block_len, x, dt, B, C, A, Dskip, h_init, hs, 0, y, bounds, h_final,
+                          batch, T, D, p.fine_len * p.n_fine, 1, st);
+        return;
+    }
+    // aggregates of every fine chunk before the last coarse chunk, then the carry
+    const int n_agg = (p.n_coarse - 1) * p.per_coarse;
+    launch_chunk_state<Tin>(false, x, dt, B, A, nullptr, w.agg_h, w.agg_s, batch, T, D,
+                            p.fine_len, p.n_fine, 0, n_agg, st);
+    launch_carry(false, w.agg_h, w.agg_s, A, h_init, w.h_in, nullptr, batch, D, p.n_fine, n_agg,
+                 st);
+    launch_bidir<Tin>(s->block_len, x, dt, B, C, A, Dskip, w.h_in, (int64_t)p.n_fine * hs,
+                      (int64_t)p.per_coarse * hs, y, bounds, h_final, batch, T, D,
+                      p.fine_len * p.per_coarse, p.n_coarse, st);
+}
+
+template <typename Tin>
+void run_full(const bdssm_shape *s, int64_t T, const void *x, const void *dt, const void *B,
+              const void *C, const float *A, const float *Dskip, void *y, const Workspace &w,
+              const Plan &p, hipStream_t st) {
+    const int64_t batch = s->batch, D = s->d_inner;
+    const int nf = p.n_fine;
+    // forward: aggregates of chunks 0..nf-2, incoming states of all chunks
+    launch_chunk_state<Tin>(false, x, dt, B, A, nullptr, w.agg_h, w.agg_s, batch, T, D,
+                            p.fine_len, nf, 0, nf - 1, st);
+    launch_carry(false, w.agg_h, w.agg_s, A, nullptr, w.h_in, nullptr, batch, D, nf, nf - 1, st);
+    // reverse: aggregates of chunks 1..nf-1 (scanned right to left), incoming states
+    launch_chunk_state<Tin>(true, x, dt, B, A, nullptr, w.ragg_h, w.ragg_s, batch, T, D,
+                            p.fine_len, nf, 1, nf - 1, st);
+    launch_carry(true, w.ragg_h, w.ragg_s, A, nullptr, w.hr_in, nullptr, batch, D, nf, nf, st);
+    launch_sweep<Tin>(false, x, dt, B, C, A, Dskip, w.h_in, w.yf, y, batch, T, D, p.fine_len, nf, st);
+    launch_sweep<Tin>(true, x, dt, B, C, A, Dskip, w.hr_in, w.yf, y, batch, T, D, p.fine_len, nf, st);
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+
+extern "C" {
+
+int bdssm_version(void) { return kVersion; }
+
+const char *bdssm_status_str(int status) {
+    switch (status) {
+    case BDSSM_OK: return "ok";
+    case BDSSM_ERR_NULL: return "a required pointer is NULL";
+    case BDSSM_ERR_SHAPE: return "unsupported or inconsistent sizes";
+    case BDSSM_ERR_DTYPE: return "unknown dtype";
+    case BDSSM_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
+    case BDSSM_ERR_WORKSPACE: return "workspace missing or too small";
+    case BDSSM_ERR_HIP: return "HIP launch or runtime error";
+    case BDSSM_ERR_ALIAS: return "an output overlaps an input";
+    default: return "unknown status";
+    }
+}
+
+size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T, int op) {
+    if (check_shape(shape) != BDSSM_OK || T < 0 || T % shape->block_len != 0) return (size_t)-1;
+    if (op != BDSSM_OP_PREFILL && op != BDSSM_OP_TRAIN && op != BDSSM_OP_FULL) return (size_t)-1;
+    if (shape->batch == 0 || shape->d_inner == 0 || T == 0) return 0;
+    const Plan p = make_plan(shape->batch, shape->d_inner, T);
+    return layout_ws(nullptr, shape->batch, shape->d_inner, T, p, op).bytes;
+}
+
+int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const void *dt,
+                  const void *B, const void *C, const float *A, const float *Dskip,
+                  const float *h_init, float *h_cache, void *y, void *ws, size_t ws_bytes,
+                  void *stream) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (t_ctx < 0 || t_ctx % shape->block_len != 0) return BDSSM_ERR_SHAPE;
+    const bool with_y = y != nullptr;
+    rc = check_streams(shape, t_ctx, x, dt, B, C, with_y, A, Dskip, with_y);
+    if (rc) return rc;
+    const int64_t batch = shape->batch, D = shape->d_inner;
+    if (batch == 0 || D == 0) return BDSSM_OK;
+    if (h_cache == nullptr) return BDSSM_ERR_NULL;
+    if (!aligned16(h_cache) || !aligned16(h_init) || !aligned16(y) || !aligned16(ws))
+        return BDSSM_ERR_ALIGN;
+    const size_t nstate = (size_t)batch * D * kStates * 4;
+    const size_t ny = (size_t)batch * t_ctx * D * esize(shape);
+    rc = check_alias(shape, t_ctx, x, dt, B, C, A, Dskip, nullptr,
+                     {Range{h_cache, nstate}, Range{y, ny}});
+    if (rc) return rc;
+    if (h_init && h_init != h_cache && overlaps({h_init, nstate}, {h_cache, nstate}))
+        return BDSSM_ERR_ALIAS;
+    if (h_init && overlaps({h_init, nstate}, {y, ny})) return BDSSM_ERR_ALIAS;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (t_ctx == 0) return copy_or_zero(h_init, h_cache, batch * D * kStates, st);
+    const Plan p = make_plan(batch, D, t_ctx);
+    const Workspace probe = layout_ws(nullptr, batch, D, t_ctx, p, BDSSM_OP_PREFILL);
+    if (probe.bytes > 0 && (ws == nullptr || ws_bytes < probe.bytes)) return BDSSM_ERR_WORKSPACE;
+    if (probe.bytes > 0) {
+        rc = check_alias(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, {Range{ws, probe.bytes}});
+        if (rc) return rc;
+        if (overlaps({ws, probe.bytes}, {y, ny}) || overlaps({ws, probe.bytes}, {h_cache, nstate}))
+            return BDSSM_ERR_ALIAS;
+    }
+    const Workspace w = layout_ws(ws, batch, D, t_ctx, p, BDSSM_OP_PREFILL);
+    (void)hipGetLastError();
+    if (shape->dtype == BDSSM_BF16) {
+        if (with_y) run_bidirectional<uint16_t>(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, y, nullptr, h_cache, w, p, st);
+        else run_state_only<uint16_t>(shape, t_ctx, x, dt, B, A, h_init, h_cache, w, p, st);
+    } else {
+        if (with_y) run_bidirectional<float>(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, y, nullptr, h_cache, w, p, st);
+        else run_state_only<float>(shape, t_ctx, x, dt, B, A, h_init, h_cache, w, p, st);
+    }
+    return launch_status();
+}
+
+int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void *x,
+                     const void *dt, const void *B, const void *C, const float *A,
+                     const float *Dskip, void *y, void *stream) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    const int64_t L = shape->block_len;
+    rc = check_streams(shape, L, x, dt, B, C, true, A, Dskip, true);
+    if (rc) return rc;
+    const int64_t batch = shape->batch, D = shape->d_inner;
+    if (batch == 0 || D == 0) return BDSSM_OK;
+    if (h_cache == nullptr || y == nullptr) return BDSSM_ERR_NULL;
+    if (!aligned16(h_cache) || !aligned16(y)) return BDSSM_ERR_ALIGN;
+    rc = check_alias(shape, L, x, dt, B, C, A, Dskip, h_cache,
+                     {Range{y, (size_t)batch * L * D * esize(shape)}});
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (shape->dtype == BDSSM_BF16)
+        launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, nullptr, batch, L, D, kGroup, 1, st);
+    else
+        launch_bidir<float>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, nullptr, batch, L, D, kGroup, 1, st);
+    return launch_status();
+}
+
+int bdssm_commit(const bdssm_shape *shape, float *h_cache, const void *x, const void *dt,
+                 const void *B, const void *C, const float *A, const float *Dskip, void *y,
+                 void *stream) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    const int64_t L = shape->block_len;
+    const bool with_y = y != nullptr;
+    rc = check_streams(shape, L, x, dt, B, C, with_y, A, Dskip, with_y);
+    if (rc) return rc;
+    const int64_t batch = shape->batch, D = shape->d_inner;
+    if (batch == 0 || D == 0) return BDSSM_OK;
+    if (h_cache == nullptr) return BDSSM_ERR_NULL;
+    if (!aligned16(h_cache) || !aligned16(y)) return BDSSM_ERR_ALIGN;
+    rc = check_alias(shape, L, x, dt, B, C, A, Dskip, nullptr,
+                     {Range{h_cache, (size_t)batch * D * kStates * 4},
+                      Range{y, (size_t)batch * L * D * esize(shape)}});
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (shape->dtype == BDSSM_BF16) {
+        if (with_y) launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, h_cache, batch, L, D, kGroup, 1, st);
+        else launch_chunk_state<uint16_t>(false, x, dt, B, A, h_cache, h_cache, nullptr, batch, L, D, kGroup, 1, 0, 1, st);
+    } else {
+        if (with_y) launch_bidir<float>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, h_cache, batch, L, D, kGroup, 1, st);
+        else launch_chunk_state<float>(false, x, dt, B, A, h_cache, h_cache, nullptr, batch, L, D, kGroup, 1, 0, 1, st);
+    }
+    return launch_status();
+}
+
+int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
+                     const void *B, const void *C, const float *A, const float *Dskip,
+                     const float *h_init, void *y, float *h_bounds, void *ws, size_t ws_bytes,
+                     void *stream) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (T < 0 || T % shape->block_len != 0) return BDSSM_ERR_SHAPE;
+    rc = check_streams(shape, T, x, dt, B, C, true, A, Dskip, true);
+    if (rc) return rc;
+    const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len;
+    if (batch == 0 || D == 0) return BDSSM_OK;
+    if (T > 0 && y == nullptr) return BDSSM_ERR_NULL;
+    if (!aligned16(h_init) || !aligned16(y) || !aligned16(h_bounds) || !aligned16(ws))
+        return BDSSM_ERR_ALIGN;
+    const size_t nbnd = (size_t)batch * (T / L + 1) * D * kStates * 4;
+    const Plan p = make_plan(batch, D, T);
+    const Workspace probe = layout_ws(nullptr, batch, D, T, p, BDSSM_OP_TRAIN);
+    rc = check_alias(shape, T, x, dt, B, C, A, Dskip, h_init,
+                     {Range{y, (size_t)batch * T * D * esize(shape)}, Range{h_bounds, nbnd},
+                      Range{T > 0 ? ws : nullptr, probe.bytes}});
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (T == 0) {
+        if (h_bounds == nullptr) return BDSSM_OK;
+        return copy_or_zero(h_init, h_bounds, batch * D * kStates, st);
+    }
+    if (probe.bytes > 0 && (ws == nullptr || ws_bytes < probe.bytes)) return BDSSM_ERR_WORKSPACE;
+    const Workspace w = layout_ws(ws, batch, D, T, p, BDSSM_OP_TRAIN);
+    (void)hipGetLastError();
+    if (shape->dtype == BDSSM_BF16)
+        run_bidirectional<uint16_t>(shape, T, x, dt, B, C, A, Dskip, h_init, y, h_bounds, nullptr, w, p, st);
+    else
+        run_bidirectional<float>(shape, T, x, dt, B, C, A, Dskip, h_init, y, h_bounds, nullptr, w, p, st);
+    return launch_status();
+}
+
+int bdssm_full_scan(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
+                    const void *B, const void *C, const float *A, const float *Dskip, void *y,
+                    void *ws, size_t ws_bytes, void *stream) {
+    if (shape == nullptr) return BDSSM_ERR_NULL;
+    // the block length does not apply; validate the rest with L = 1
+    bdssm_shape s1 = *shape;
+    s1.block_len = 1;
+    int rc = check_shape(&s1);
+    if (rc) return rc;
+    if (T < 0) return BDSSM_ERR_SHAPE;
+    rc = check_streams(&s1, T, x, dt, B, C, true, A, Dskip, true);
+    if (rc) return rc;
+    const int64_t batch = s1.batch, D = s1.d_inner;
+    if (batch == 0 || D == 0 || T == 0) return BDSSM_OK;
+    if (y == nullptr) return BDSSM_ERR_NULL;
+    if (!aligned16(y) || !aligned16(ws)) return BDSSM_ERR_ALIGN;
+    const Plan p = make_plan(batch, D, T);
+    const Workspace probe = layout_ws(nullptr, batch, D, T, p, BDSSM_OP_FULL);
+    if (ws == nullptr || ws_bytes < probe.bytes) return BDSSM_ERR_WORKSPACE;
+    rc = check_alias(&s1, T, x, dt, B, C, A, Dskip, nullptr,
+                     {Range{y, (size_t)batch * T * D * esize(&s1)}, Range{ws, probe.bytes}});
+    if (rc) return rc;
+    const Workspace w = layout_ws(ws, batch, D, T, p, BDSSM_OP_FULL);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (s1.dtype == BDSSM_BF16) run_full<uint16_t>(&s1, T, x, dt, B, C, A, Dskip, y, w, p, st);
+    else run_full<float>(&s1, T, x, dt, B, C, A, Dskip, y, w, p, st);
+    return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,145 @@
+"""Host-side checks of the C ABI, no GPU needed: the library loads, exports
+every symbol include/bdssm.h declares, sizes workspaces, and rejects bad
+arguments before any HIP call (so rejected calls are safe without a device).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba_selective_scan_04_amd as m
+from mamba_selective_scan_04_amd import bdssm as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "bdssm.h")).read()
+    return sorted(set(re.findall(r"\b(bdssm_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_match_header():
+    lib = m.load()
+    names = header_functions()
+    assert set(names) == set(m.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert m.version() == 10000
+    for code in range(-7, 1):
+        assert m.status_str(code) not in ("", "unknown status")
+    assert m.status_str(-99) == "unknown status"
+
+
+FAKE = 0x10000            # 16-byte aligned, never dereferenced: rejected calls return first
+MIS = 0x10002             # misaligned
+
+
+def shape(batch=1, D=64, N=16, L=16, dtype=B.BF16):
+    return B.Shape(batch, D, N, L, dtype)
+
+
+def lib():
+    return m.load()
+
+
+def P(v):
+    return ctypes.c_void_p(v)
+
+
+def prefill(s, T, x=FAKE, dt=FAKE + 0x1000, Bm=FAKE + 0x2000, C=FAKE + 0x3000, A=FAKE + 0x4000,
+            Ds=FAKE + 0x5000, h_init=None, h_cache=FAKE + 0x6000, y=None, ws=None, ws_bytes=0):
+    return lib().bdssm_prefill(ctypes.byref(s), T, P(x), P(dt), P(Bm), P(C), P(A), P(Ds),
+                               P(h_init), P(h_cache), P(y), P(ws), ws_bytes, None)
+
+
+def test_shape_errors():
+    assert prefill(shape(N=8), 16) == -2
+    assert prefill(shape(L=3), 15) == -2
+    assert prefill(shape(L=32), 32) == -2
+    assert prefill(shape(), 24) == -2            # T % L != 0
+    assert prefill(shape(), -16) == -2
+    assert prefill(shape(batch=-1), 16) == -2
+
+
+def test_dtype_error():
+    assert prefill(shape(dtype=7), 16) == -3
+
+
+def test_null_errors():
+    assert lib().bdssm_prefill(None, 16, *([None] * 10), 0, None) == -1
+    assert prefill(shape(), 16, x=None) == -1
+    assert prefill(shape(), 16, h_cache=None) == -1
+    # y requested without C
+    assert prefill(shape(), 16, C=None, y=FAKE + 0x7000) == -1
+
+
+def test_alignment_error():
+    assert prefill(shape(), 16, x=MIS) == -4
+    assert prefill(shape(), 16, h_cache=MIS) == -4
+
+
+def test_workspace_error():
+    s = shape(batch=1, D=1536)
+    need = m.workspace_bytes(1, 1536, 65536, m.OP_PREFILL)
+    assert need > 0
+    big = 0x100000000
+    # no workspace / too small
+    assert prefill(s, 65536, x=big, dt=big * 2, Bm=big * 3, C=big * 4, A=big * 5, Ds=big * 6,
+                   h_cache=big * 7) == -5
+    assert prefill(s, 65536, x=big, dt=big * 2, Bm=big * 3, C=big * 4, A=big * 5, Ds=big * 6,
+                   h_cache=big * 7, ws=big * 8, ws_bytes=need - 1) == -5
+
+
+def test_alias_error():
+    # y overlapping x
+    assert prefill(shape(), 16, y=FAKE) == -7
+    # block step output on top of the cache
+    s = shape()
+    rc = lib().bdssm_block_step(ctypes.byref(s), P(FAKE), P(FAKE + 0x1000), P(FAKE + 0x2000),
+                                P(FAKE + 0x3000), P(FAKE + 0x4000), P(FAKE + 0x5000),
+                                P(FAKE + 0x6000), P(FAKE), None)
+    assert rc == -7
+
+
+def test_empty_calls_are_noops():
+    # batch 0 / D 0: nothing to do, no pointer needed, no HIP call
+    assert prefill(shape(batch=0), 16, x=None, dt=None, Bm=None, C=None, h_cache=None) == 0
+    assert prefill(shape(D=0), 16, x=None, dt=None, Bm=None, C=None, h_cache=None) == 0
+    s = shape(batch=0)
+    assert lib().bdssm_full_scan(ctypes.byref(s), 0, *([None] * 8), 0, None) == 0
+
+
+def test_workspace_sizes():
+    assert m.workspace_bytes(1, 64, 0, m.OP_TRAIN) == 0
+    # short sequences need no chunking and therefore no workspace
+    assert m.workspace_bytes(1, 64, 16, m.OP_PREFILL) == 0
+    # the baseline always needs its fp32 output staging buffer
+    assert m.workspace_bytes(1, 64, 16, m.OP_FULL) >= 64 * 16 * 4
+    with pytest.raises(ValueError):
+        m.workspace_bytes(1, 64, 24, m.OP_TRAIN, block_len=16)
+    # monotone in T
+    a = m.workspace_bytes(8, 1536, 4096, m.OP_TRAIN)
+    b = m.workspace_bytes(8, 1536, 8192, m.OP_TRAIN)
+    assert 0 < a <= b
+
+
+def test_timestep_free_prefix_operators():
+    """The prefix operator takes no diffusion timestep: prefill and commit
+    have no timestep parameter at the ABI."""
+    txt = open(os.path.join(ROOT, "include", "bdssm.h")).read()
+    for fn in ("bdssm_prefill", "bdssm_commit"):
+        decl = txt[txt.index("int " + fn + "("):]
+        decl = decl[:decl.index(");")]
+        assert "timestep" not in decl and "int64_t t," not in decl
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 16, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        m.block_step(torch.zeros(1, 64, 16), x, x, torch.zeros(1, 16, 16, dtype=torch.bfloat16),
+                     torch.zeros(1, 16, 16, dtype=torch.bfloat16), torch.zeros(64, 16), torch.zeros(64))

@@ -1,0 +1,243 @@
+"""GPU parity: every entry point of the HIP library against the fp64 oracle,
+element by element, on seeded inputs.  Sizes span several 64-channel tiles,
+several time chunks and ragged tails (channels not a multiple of 64, the last
+16-token group partly filled).  Full-size workloads are checked on sampled
+channels in test_parity_fullsize.py.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import mamba_selective_scan_04_amd as m
+import oracle
+from parity_util import Case, N, STATE_TOL, TOL, rel_err, to_np, worst
+
+pytestmark = pytest.mark.gpu
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+@pytest.fixture(autouse=True)
+def _announce(request, dev):
+    print("\n[parity] %s" % request.node.name, flush=True)
+    yield
+
+
+# ------------------------------------------------------------- tiny fp32 workload
+
+def test_tiny_fp32_workload(dev):
+    """batch 1, d_inner 64, d_state 16, 256 tokens, block 16, fp32: prefill of
+    240 tokens, one block step, commit, and the training / baseline forms."""
+    c = Case(1, 256, 64, torch.float32, sid=1)
+    L, P = 16, 240
+    seg = c.segment(0, P)
+    h, _ = m.prefill(*seg, L)
+    blk = c.segment(P, P + L)
+    y = m.block_step(h, *blk)
+    h_before = h.clone()
+    _, yc = m.commit(h, *blk, want_y=True)
+    yt, bnd = m.train_scan(*c.args(), L, want_bounds=True)
+    yfull = m.full_scan(*c.args())
+    _sync()
+    oa = c.oracle_args(0, P)
+    ho, _ = oracle.prefill(*oa, L)
+    ob = c.oracle_args(P, P + L)
+    yo = oracle.block_step(ho, *ob)
+    ho2, yco = oracle.commit(ho, *ob, want_y=True)
+    full = c.oracle_args()
+    yto, bo = oracle.train_scan(*full, L, want_bounds=True)
+    yfo = oracle.full_scan(*full)
+    assert rel_err(to_np(h_before), ho) < STATE_TOL
+    assert rel_err(to_np(y), yo) < TOL[torch.float32]
+    assert rel_err(to_np(yc), yco) < TOL[torch.float32]
+    assert rel_err(to_np(h), ho2) < STATE_TOL
+    assert rel_err(to_np(yt), yto) < TOL[torch.float32]
+    assert rel_err(to_np(bnd), bo) < STATE_TOL
+    assert rel_err(to_np(yfull), yfo) < TOL[torch.float32]
+    # the block step equals the last block of the training form (exact caching)
+    assert rel_err(to_np(y), yto[:, P:]) < TOL[torch.float32]
+
+
+# ----------------------------------------------------- medium bf16, ragged, chunked
+
+@pytest.mark.parametrize("a_kind", ["default", "random", "long"])
+def test_bf16_medium_all_forms(dev, a_kind, monkeypatch):
+    """batch 2, 200 channels (three full 64-lane tiles and a ragged one),
+    2048 tokens; chunk length forced to 128 so every chunked path runs."""
+    monkeypatch.setenv("BDSSM_CHUNK", "128")
+    c = Case(2, 2048, 200, torch.bfloat16, sid=8, a_kind=a_kind)
+    L = 16
+    tol = TOL[torch.bfloat16]
+    h, yp = m.prefill(*c.args(), L, want_y=True)
+    h2, _ = m.prefill(*c.args(), L)
+    yt, bnd = m.train_scan(*c.args(), L, want_bounds=True)
+    yf = m.full_scan(*c.args())
+    _sync()
+    oa = c.oracle_args()
+    r = oracle.scan(*oa, L, want_y=True, want_bounds=True)
+    yfo = oracle.full_scan(*oa)
+    assert rel_err(to_np(h), r["hT"]) < STATE_TOL
+    assert rel_err(to_np(h2), r["hT"]) < STATE_TOL
+    assert rel_err(to_np(yp), r["y"]) < tol
+    assert rel_err(to_np(yt), r["y"]) < tol
+    assert rel_err(to_np(bnd), r["bounds"]) < STATE_TOL, worst(to_np(bnd), r["bounds"])
+    assert rel_err(to_np(yf), yfo) < tol
+    # bf16 outputs within one bf16 rounding of the oracle's value
+    ref = torch.from_numpy(r["y"]).float().to(torch.bfloat16).float().numpy()
+    diff = np.abs(to_np(yt) - ref)
+    ulp = np.abs(ref) * 2.0 ** -7 + 1e-30
+    assert np.mean(diff <= ulp) > 0.999
+
+
+def test_fp32_zero_A_and_initial_state(dev, monkeypatch):
+    """A = 0 (no decay, long cumulative sums) with a nonzero initial state."""
+    monkeypatch.setenv("BDSSM_CHUNK", "64")
+    c = Case(2, 512, 96, torch.float32, sid=9, a_kind="zero")
+    h0 = torch.randn(2, 96, N, generator=torch.Generator().manual_seed(3)).to(dev)
+    L = 16
+    h, yp = m.prefill(*c.args(), L, h_init=h0, want_y=True)
+    yt, _ = m.train_scan(*c.args(), L, h_init=h0)
+    _sync()
+    r = oracle.scan(*c.oracle_args(), L, h0=to_np(h0), want_y=True)
+    assert rel_err(to_np(h), r["hT"]) < STATE_TOL
+    assert rel_err(to_np(yp), r["y"]) < TOL[torch.float32]
+    assert rel_err(to_np(yt), r["y"]) < TOL[torch.float32]
+
+
+@pytest.mark.parametrize("L,T", [(1, 37), (2, 50), (4, 36), (8, 40), (8, 8), (16, 48)])
+def test_block_lengths_and_ragged_groups(dev, L, T):
+    """Every supported block length, with sequence lengths that leave the last
+    16-token group partly filled."""
+    c = Case(1, T, 70, torch.float32, sid=10, a_kind="random")
+    yt, bnd = m.train_scan(*c.args(), L, want_bounds=True)
+    blk = c.segment(T - L, T)
+    hpre, _ = m.prefill(*c.segment(0, T - L), L)
+    yb = m.block_step(hpre, *blk)
+    _sync()
+    r = oracle.scan(*c.oracle_args(), L, want_y=True, want_bounds=True)
+    assert rel_err(to_np(yt), r["y"]) < TOL[torch.float32]
+    assert rel_err(to_np(bnd), r["bounds"]) < STATE_TOL
+    assert rel_err(to_np(yb), r["y"][:, T - L:]) < TOL[torch.float32]
+
+
+def test_chunk_length_invariance(dev, monkeypatch):
+    c = Case(1, 1024, 128, torch.float32, sid=11, a_kind="long")
+    outs = []
+    for ch in ("16", "48", "256", "100000"):
+        monkeypatch.setenv("BDSSM_CHUNK", ch)
+        yt, _ = m.train_scan(*c.args(), 16)
+        h, _ = m.prefill(*c.args(), 16)
+        outs.append((to_np(yt), to_np(h)))
+    _sync()
+    r = oracle.scan(*c.oracle_args(), 16, want_y=True)
+    for yt, h in outs:
+        assert rel_err(yt, r["y"]) < TOL[torch.float32]
+        assert rel_err(h, r["hT"]) < STATE_TOL
+        assert rel_err(yt, outs[0][0]) < 1e-4
+
+
+# ------------------------------------------------------------------ invariants
+
+def test_exact_caching_on_gpu(dev):
+    """The cache after prefill(P) and commits of b1..b3 matches prefill over
+    P|b1|b2|b3; block steps never modify the cache; a cache saved to the host
+    and restored gives bit-identical block outputs."""
+    L = 16
+    for a_kind in ("default", "long"):
+        c = Case(2, 64 * L, 130, torch.bfloat16, sid=12, a_kind=a_kind)
+        P = 60 * L
+        h, _ = m.prefill(*c.segment(0, P), L)
+        for k in range(3):
+            blk = c.segment(P + k * L, P + (k + 1) * L)
+            before = h.clone()
+            y1 = m.block_step(h, *blk)
+            y2 = m.block_step(h, *blk)
+            _sync()
+            assert torch.equal(before, h)
+            assert torch.equal(y1, y2)
+            saved = h.cpu()
+            restored = saved.to(dev)
+            y3 = m.block_step(restored, *blk)
+            _sync()
+            assert torch.equal(y1, y3)
+            m.commit(h, *blk)
+        hall, _ = m.prefill(*c.segment(0, P + 3 * L), L)
+        _sync()
+        ho, _ = oracle.prefill(*c.oracle_args(0, P + 3 * L), L)
+        assert rel_err(to_np(h), ho) < STATE_TOL
+        assert rel_err(to_np(hall), ho) < STATE_TOL
+
+
+def test_block_locality_on_gpu(dev, monkeypatch):
+    """Perturbing tokens after block k leaves block k's training-form outputs
+    bitwise unchanged (the reverse is confined to the block); the full-sequence
+    baseline is not prefix-only."""
+    monkeypatch.setenv("BDSSM_CHUNK", "64")
+    L = 16
+    c = Case(1, 512, 100, torch.float32, sid=13, a_kind="long")
+    y0, _ = m.train_scan(*c.args(), L)
+    f0 = m.full_scan(*c.args())
+    k = 20
+    x2 = c.dev["x"].clone()
+    x2[:, (k + 1) * L:] += 1.0
+    args2 = (x2,) + c.args()[1:]
+    y2, _ = m.train_scan(*args2, L)
+    f2 = m.full_scan(*args2)
+    _sync()
+    assert torch.equal(y0[:, :(k + 1) * L], y2[:, :(k + 1) * L])
+    assert not torch.equal(y0[:, (k + 1) * L:], y2[:, (k + 1) * L:])
+    assert not torch.equal(f0[:, :L], f2[:, :L])
+
+
+def test_determinism(dev, monkeypatch):
+    monkeypatch.setenv("BDSSM_CHUNK", "128")
+    c = Case(2, 1024, 192, torch.bfloat16, sid=14, a_kind="random")
+    a = [m.train_scan(*c.args(), 16)[0], m.prefill(*c.args(), 16)[0], m.full_scan(*c.args())]
+    b = [m.train_scan(*c.args(), 16)[0], m.prefill(*c.args(), 16)[0], m.full_scan(*c.args())]
+    _sync()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+# ------------------------------------------------------------------ edge cases
+
+@pytest.mark.parametrize("D", [1, 63, 65])
+def test_small_and_ragged_channel_counts(dev, D):
+    c = Case(3, 64, D, torch.float32, sid=15, a_kind="random")
+    yt, _ = m.train_scan(*c.args(), 16)
+    h, _ = m.prefill(*c.args(), 16)
+    yf = m.full_scan(*c.args())
+    _sync()
+    r = oracle.scan(*c.oracle_args(), 16, want_y=True)
+    assert rel_err(to_np(yt), r["y"]) < TOL[torch.float32]
+    assert rel_err(to_np(h), r["hT"]) < STATE_TOL
+    assert rel_err(to_np(yf), oracle.full_scan(*c.oracle_args())) < TOL[torch.float32]
+
+
+def test_empty_inputs(dev):
+    x = torch.zeros(2, 0, 64, device=dev)
+    Bm = torch.zeros(2, 0, N, device=dev)
+    A = -torch.ones(64, N, device=dev)
+    Ds = torch.zeros(64, device=dev)
+    h0 = torch.randn(2, 64, N, device=dev)
+    h, _ = m.prefill(x, x, Bm, Bm, A, Ds, 16, h_init=h0)
+    _, bnd = m.train_scan(x, x, Bm, Bm, A, Ds, 16, h_init=h0, want_bounds=True)
+    y = m.full_scan(x, x, Bm, Bm, A, Ds)
+    _sync()
+    assert torch.equal(h, h0)
+    assert torch.equal(bnd[:, 0], h0)
+    assert y.shape == (2, 0, 64)
+
+
+def test_in_place_prefill_continuation(dev):
+    """prefill may take its initial state from the buffer it writes."""
+    c = Case(1, 512, 64, torch.bfloat16, sid=16)
+    h, _ = m.prefill(*c.segment(0, 256), 16)
+    m.prefill(*c.segment(256, 512), 16, h_init=h, h_cache=h)
+    _sync()
+    ho, _ = oracle.prefill(*c.oracle_args(), 16)
+    assert rel_err(to_np(h), ho) < STATE_TOL
