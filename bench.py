@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-restricted bidirectional selective scan on one MI355X.
+
+One step = one pass of the inference hot path over one batch of synthetic,
+device-resident input of the chosen workload:
+    prefill of the clean context (forward scan, cache written)
+    then, for each of n_blocks blocks: 16 denoising block steps (forward from
+    the cache + in-block reverse + output) and one commit (cache advanced).
+The prefill is launched eagerly; each block's 16 block steps + commit are
+replayed from a captured HIP graph (one graph per block: the launches are
+identical every step, so capture removes only host launch overhead).
+
+Printed: one JSON line on stdout (progress goes to stderr).
+  value   whole-step algorithmic HBM throughput (GB/s): bytes every call in the
+          step must move (inputs read once, outputs written once, states read
+          or written once) / measured step time
+  roofline  for the dominant kernel (the prefill's chunk-local forward scan +
+          its carry), which is VALU-bound: achieved fp32 VALU issue slots per
+          second against the chip's slot rate, plus the HBM view
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same step
+Also measured outside the timed region: the full-sequence bidirectional
+baseline (reverse over the whole sequence, rescanned every denoising step).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+# fp32 VALU issue slots per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
+EXP_SLOTS = 2            # v_exp_f32 issues at half rate on gfx950
+NS = 16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ algorithmic cost
+
+def bytes_prefill(batch, T, D, e, h_init=False):
+    return batch * T * D * 2 * e + batch * T * NS * e + 4 * D * NS + 4 * batch * D * NS * (2 if h_init else 1)
+
+
+def bytes_block_step(batch, L, D, e):
+    return batch * L * D * 3 * e + batch * L * NS * 2 * e + 4 * D * NS + 4 * D + 4 * batch * D * NS
+
+
+def bytes_commit(batch, L, D, e):
+    return batch * L * D * 2 * e + batch * L * NS * e + 4 * D * NS + 2 * 4 * batch * D * NS
+
+
+def bytes_full(batch, T, D, e):
+    return batch * T * D * 3 * e + batch * T * NS * 2 * e + 4 * D * NS + 4 * D
+
+
+def slots_forward(batch, T, D):
+    """exp2 (2 slots) + dt*A' mul + (dt*x)*B mul + state FMA per (b,t,d,n),
+    plus the dt*x multiply per (b,t,d)."""
+    return batch * T * D * (NS * (EXP_SLOTS + 3) + 1)
+
+
+def slots_bidirectional(batch, T, D):
+    """forward + in-block reverse + output: exp2 + 2 mul + 4 FMA per
+    (b,t,d,n), plus dt*x and the Dskip*x FMA per (b,t,d)."""
+    return batch * T * D * (NS * (EXP_SLOTS + 6) + 2)
+
+
+# ------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="infer_65k_b8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-baseline-scan", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch block steps eagerly (no graph)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    import mamba_selective_scan_04_amd as m
+    from mamba_selective_scan_04_amd import synth
+
+    m.load()   # fails loudly if the HIP library is missing
+    wl = dict(synth.WORKLOADS[args.workload])
+    if "ctx" not in wl or "steps" not in wl:
+        raise SystemExit("workload %s is not an inference workload" % args.workload)
+    batch, D, ctx, L = wl["batch"], wl["d_inner"], wl["ctx"], wl["block"]
+    S, nblk, sid = wl["steps"], wl["n_blocks"], wl["sid"]
+    dtype = synth.TORCH_DTYPE[wl["dtype"]]
+    e = 2 if dtype == torch.bfloat16 else 4
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    st = torch.cuda.current_stream()
+
+    log("[bench] workload %s: batch %d, d_inner %d, ctx %d, block %d, %d steps x %d blocks"
+        % (args.workload, batch, D, ctx, L, S, nblk))
+    t_gen = time.time()
+    x, dt, Bm, Cm = synth.stream(batch, ctx, D, NS, sid, 0, dtype, dev)
+    A, Dskip = synth.params(D, NS, sid, "default", dev)
+    steps_in = [synth.step_inputs(batch, L, D, NS, sid, j, dtype, dev) for j in range(S)]
+    commit_in = [synth.commit_inputs(batch, L, D, NS, sid, k, dtype, dev) for k in range(nblk)]
+    h = torch.empty(batch, D, NS, dtype=torch.float32, device=dev)
+    y_blk = torch.empty(batch, L, D, dtype=dtype, device=dev)
+    ws = torch.empty(max(1, m.workspace_bytes(batch, D, ctx, m.OP_PREFILL, L, NS, dtype)),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log("[bench] inputs generated on device in %.1f s" % (time.time() - t_gen))
+
+    def prefill():
+        m.prefill(x, dt, Bm, Cm, A, Dskip, L, h_cache=h, ws=ws)
+
+    def block(k):
+        for j in range(S):
+            m.block_step(h, *steps_in[j], A, Dskip, y=y_blk)
+        m.commit(h, *commit_in[k], A, Dskip)
+
+    launch = "eager"
+    graphs = None
+    if not args.eager:
+        try:
+            prefill()
+            torch.cuda.synchronize()
+            graphs = []
+            for k in range(nblk):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    block(k)
+                graphs.append(g)
+            torch.cuda.synchronize()
+            launch = "graph"
+        except Exception as exc:       # capture unsupported: fall back to eager launches
+            log("[bench] graph capture failed (%s); launching eagerly" % exc)
+            graphs = None
+
+    def run_block(k):
+        if graphs is not None:
+            graphs[k].replay()
+        else:
+            block(k)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(st)
+        prefill()
+        if ev is not None:
+            ev[1].record(st)
+        for k in range(nblk):
+            run_block(k)
+        if ev is not None:
+            ev[2].record(st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("[bench] warmup done (%d steps, %s block launches)" % (args.warmup, launch))
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pf_ms = sum(ev[0].elapsed_time(ev[1]) for ev in evs) / args.steps
+    blk_ms = sum(ev[1].elapsed_time(ev[2]) for ev in evs) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    log("[bench] timed %d steps: %.3f ms/step (prefill %.3f ms, blocks %.3f ms)"
+        % (args.steps, ms_per_step, pf_ms, blk_ms))
+
+    # ---- per-call breakdown of the block phase (events around R replays)
+    R = 50
+    bs_x = [steps_in[0][i] for i in range(4)]
+    def time_calls(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        a.record(st)
+        for _ in range(reps):
+            fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+    g_bs = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_bs):
+        for _ in range(R):
+            m.block_step(h, *bs_x, A, Dskip, y=y_blk)
+    g_cm = torch.cuda.CUDAGraph()
+    hc = h.clone()
+    with torch.cuda.graph(g_cm):
+        for _ in range(R):
+            m.commit(hc, *commit_in[0], A, Dskip)
+    bs_ms = time_calls(g_bs.replay, 4) / R
+    cm_ms = time_calls(g_cm.replay, 4) / R
+    bs_eager_ms = time_calls(lambda: m.block_step(h, *bs_x, A, Dskip, y=y_blk), 200)
+
+    step_bytes = (bytes_prefill(batch, ctx, D, e)
+                  + nblk * (S * bytes_block_step(batch, L, D, e) + bytes_commit(batch, L, D, e)))
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    pf_bytes = bytes_prefill(batch, ctx, D, e)
+    pf_slots = slots_forward(batch, ctx, D)
+    achieved_slots = pf_slots / (pf_ms * 1e-3)
+    roofline = {
+        "kernel": "prefill: chunk_state_kernel (chunk-local forward scan) + carry_kernel",
+        "bound": "alu",
+        "achieved": achieved_slots / 1e12,
+        "peak": VALU_SLOTS_PER_S / 1e12,
+        "unit": "TFLOP/s",
+        "op": "fp32 VALU issue slot (mul/FMA 1, v_exp_f32 %d); per (token, channel): "
+              "16 x (exp2 + 2 mul + FMA) + 1 mul" % EXP_SLOTS,
+        "frac": achieved_slots / VALU_SLOTS_PER_S,
+        "traffic": None,
+        "hbm_achieved_GBs": pf_bytes / (pf_ms * 1e-3) / 1e9,
+        "hbm_frac": pf_bytes / (pf_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "launch_ms": pf_ms,
+    }
+
+    gen_tok = batch * L * nblk
+    gen_ms = nblk * (S * bs_ms + cm_ms)
+    calls = {
+        "prefill": {"ms": pf_ms, "tokens_per_s": batch * ctx / (pf_ms * 1e-3),
+                    "GBs": pf_bytes / (pf_ms * 1e-3) / 1e9, "bytes": pf_bytes},
+        "block_step": {"us_graph": bs_ms * 1e3, "us_eager": bs_eager_ms * 1e3,
+                       "GBs": bytes_block_step(batch, L, D, e) / (bs_ms * 1e-3) / 1e9,
+                       "bytes": bytes_block_step(batch, L, D, e)},
+        "commit": {"us_graph": cm_ms * 1e3,
+                   "GBs": bytes_commit(batch, L, D, e) / (cm_ms * 1e-3) / 1e9,
+                   "bytes": bytes_commit(batch, L, D, e)},
+        "generation_tokens_per_s": gen_tok / (gen_ms * 1e-3),
+    }
+
+    # ---- contrast: full-sequence bidirectional baseline, rescanned every step
+    baseline = None
+    if not args.no_baseline_scan:
+        Tf = ctx + L
+        del ws
+        xf, dtf, Bf, Cf = synth.stream(batch, Tf, D, NS, sid, 200, dtype, dev)
+        yf = torch.empty_like(xf)
+        wsf = torch.empty(max(1, m.workspace_bytes(batch, D, Tf, m.OP_FULL, 1, NS, dtype)),
+                          dtype=torch.uint8, device=dev)
+        f_ms = time_calls(lambda: m.full_scan(xf, dtf, Bf, Cf, A, Dskip, y=yf, ws=wsf), 3)
+        base_gen = batch * L / (S * f_ms * 1e-3)
+        baseline = {"full_scan_ms": f_ms, "T": Tf,
+                    "GBs": bytes_full(batch, Tf, D, e) / (f_ms * 1e-3) / 1e9,
+                    "generation_tokens_per_s": base_gen,
+                    "speedup_block_restricted": calls["generation_tokens_per_s"] / base_gen}
+        del xf, dtf, Bf, Cf, yf, wsf
+        log("[bench] baseline full scan over %d tokens: %.3f ms" % (Tf, f_ms))
+
+    # ---- CPU baseline: the fp64 oracle on a bounded sample of the same step
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(x, dt, Bm, Cm, A, Dskip, steps_in, commit_in, L, args.cpu_seconds, e)
+
+    line = {
+        "metric": "block-step scan GB/s & % HBM peak at 65K/262K ctx; prefill tokens/s",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": batch, "d_inner": D, "d_state": NS,
+                   "ctx": ctx, "block": L, "denoising_steps": S, "n_blocks": nblk,
+                   "launch": launch},
+        "hbm_frac_step": value / HBM_PEAK_GBS,
+        "prefill_tokens_per_s": calls["prefill"]["tokens_per_s"],
+        "block_step_GBs": calls["block_step"]["GBs"],
+        "calls": calls,
+        "baseline_full_scan": baseline,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(x, dt, Bm, Cm, A, Dskip, steps_in, commit_in, L, target_s, e):
+    """Time the oracle (as it stands) on batch rows 0..k-1 of the step:
+    prefill of the whole context, the block steps and the commits, all
+    channels.  k grows until about target_s seconds of wall time."""
+    import oracle
+    from mamba_selective_scan_04_amd import synth
+
+    oracle.load()
+    batch, ctx, D = x.shape
+    to = synth.to_oracle
+    Ah, Dh = to(A), to(Dskip)
+    spent = 0.0
+    rows = 0
+    sample_bytes = 0
+    for b in range(batch):
+        xb, dtb, Bb, Cb = (to(t[b:b + 1]) for t in (x, dt, Bm, Cm))
+        sb = [tuple(to(t[b:b + 1]) for t in s) for s in steps_in]
+        cb = [tuple(to(t[b:b + 1]) for t in c) for c in commit_in]
+        t0 = time.perf_counter()
+        hcache, _ = oracle.prefill(xb, dtb, Bb, Cb, Ah, Dh, L)
+        for k in range(len(cb)):
+            for s in sb:
+                oracle.block_step(hcache, *s, Ah, Dh)
+            hcache, _ = oracle.commit(hcache, *cb[k], Ah, Dh)
+        spent += time.perf_counter() - t0
+        rows += 1
+        sample_bytes += (bytes_prefill(1, ctx, D, e)
+                         + len(cb) * (len(sb) * bytes_block_step(1, L, D, e) + bytes_commit(1, L, D, e)))
+        log("[bench] cpu oracle: batch row %d done, %.1f s so far" % (b, spent))
+        if spent >= target_s:
+            break
+    return {"value": sample_bytes / spent / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "batch rows 0..%d of %d (all %d channels): prefill of %d tokens + the "
+                      "block steps and commits; %.1f s wall" % (rows - 1, batch, D, ctx, spent),
+            "seconds": spent}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -32,13 +32,19 @@ namespace {
 
 constexpr int kVersion = 10000;   // 1.0.0
 
+// 256 CUs x 4 SIMDs x 8 resident waves (the chunk kernel fits in 64 VGPRs)
+constexpr int64_t kFineWaves = 256 * 4 * 8;
+// 2 workgroups of the bidirectional kernel per CU
+constexpr int64_t kCoarseGroups = 512;
+
 // ------------------------------------------------------------ launch policy
 //
 // Chunking of the time axis.  The per-token loop is sequential per channel,
 // so a launch has batch * ceil(D/64) waves per chunk; long sequences are cut
 // into chunks until the chip is full.
-//   fine chunks  (one wave per 64 channels, 16 states per lane): aim for
-//                kFineWaves waves in flight, ~8 per SIMD on 256 CUs.
+//   fine chunks  (one wave per 64 channels, 16 states per lane): at most
+//                kFineWaves waves, the number resident at once (8 per SIMD),
+//                so the launch runs in a single round with no tail.
 //   coarse chunks (bidirectional pass, 4 waves per 64 channels): aim for
 //                kCoarseGroups workgroups, 2 per CU, each a whole number of
 //                fine chunks so its incoming state is a fine-chunk boundary.
@@ -71,9 +77,10 @@ Plan make_plan(int64_t batch, int64_t D, int64_t T) {
         p.fine_len = kGroup; p.n_fine = 1; p.per_coarse = 1; p.n_coarse = 1;
         return p;
     }
-    const int64_t fine_waves = env_int("BDSSM_FINE_WAVES", 8192);
-    const int64_t coarse_groups = env_int("BDSSM_COARSE_GROUPS", 512);
-    int64_t nf = ceil_div(fine_waves, groups);
+    const int64_t fine_waves = env_int("BDSSM_FINE_WAVES", kFineWaves);
+    const int64_t coarse_groups = env_int("BDSSM_COARSE_GROUPS", kCoarseGroups);
+    // one round of resident waves: never more chunks than fit at once
+    int64_t nf = fine_waves / groups;
     if (nf > ngroups16) nf = ngroups16;
     if (nf < 1) nf = 1;
     int64_t fl = ceil_div(ngroups16, nf) * kGroup;
@@ -213,14 +220,16 @@ void launch_chunk_state(bool rev, const void *x, const void *dt, const void *B, 
                         hipStream_t st) {
     if (n_launch <= 0) return;
     const dim3 g = grid3(D, n_launch, batch);
-    if (rev)
-        hipLaunchKernelGGL((chunk_state_kernel<Tin, true>), g, dim3(kWave), 0, st,
-                           (const Tin *)x, (const Tin *)dt, (const Tin *)B, A, h0, hout, sout, T,
-                           (int)D, Tc, n_chunks, c_first);
+    const Tin *xp = (const Tin *)x, *dp = (const Tin *)dt, *bp = (const Tin *)B;
+    if (sout == nullptr)   // direct pass from h0 into hout (one chunk)
+        hipLaunchKernelGGL((chunk_state_kernel<Tin, false, true>), g, dim3(kWave), 0, st, xp, dp, bp,
+                           A, h0, hout, sout, T, (int)D, Tc, n_chunks, c_first);
+    else if (rev)
+        hipLaunchKernelGGL((chunk_state_kernel<Tin, true, false>), g, dim3(kWave), 0, st, xp, dp, bp,
+                           A, h0, hout, sout, T, (int)D, Tc, n_chunks, c_first);
     else
-        hipLaunchKernelGGL((chunk_state_kernel<Tin, false>), g, dim3(kWave), 0, st,
-                           (const Tin *)x, (const Tin *)dt, (const Tin *)B, A, h0, hout, sout, T,
-                           (int)D, Tc, n_chunks, c_first);
+        hipLaunchKernelGGL((chunk_state_kernel<Tin, false, false>), g, dim3(kWave), 0, st, xp, dp, bp,
+                           A, h0, hout, sout, T, (int)D, Tc, n_chunks, c_first);
 }
 
 void launch_carry(bool rev, const float *agg_h, const float *agg_s, const float *A,

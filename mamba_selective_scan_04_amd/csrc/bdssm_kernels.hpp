@@ -60,6 +60,19 @@ template <> __device__ __forceinline__ uint16_t narrow<uint16_t>(float v) {
 
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 
+// States 2q and 2q+1 of a B or C row.  The row is read as 32-bit words: with a
+// wave-uniform address that lets the compiler use scalar loads (s_load_dwordxN)
+// and unpack bf16 pairs on the scalar unit instead of spending VALU slots.
+__device__ __forceinline__ void load_pair(const uint16_t *row, int q, float &lo, float &hi) {
+    const uint32_t w = reinterpret_cast<const uint32_t *>(row)[q];
+    lo = __uint_as_float(w << 16);
+    hi = __uint_as_float(w & 0xffff0000u);
+}
+__device__ __forceinline__ void load_pair(const float *row, int q, float &lo, float &hi) {
+    lo = row[2 * q];
+    hi = row[2 * q + 1];
+}
+
 // Wave-uniform value kept in a scalar register.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -69,18 +82,23 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 //   * aggregates (h0 == nullptr): the state reached from zero over the chunk
 //     and S = sum of dt over the chunk, so the chunk acts on an incoming
 //     state h as  h -> exp2(A' S) h + h_local;
-//   * a direct forward pass over one chunk from h0 (commit without output,
-//     prefill of a short context), writing the final state.
+//   * kDirect: a forward pass over one chunk from h0 (commit without output,
+//     prefill of a short context), writing the final state (a separate
+//     instantiation so profiles tell the two uses apart).
+// Tokens stream through a 6-deep register pipeline: the loads of the next 6
+// tokens are issued before the arithmetic of the current 6 (6 keeps the bf16
+// kernel at <= 64 VGPRs, i.e. 8 waves per SIMD).
 // kRev scans the chunk from its last token to its first (the reverse
 // direction of the full-sequence baseline).
 // grid = (ceil(D/64), chunks launched, batch), block = 64.
 // hout / sout are indexed by chunk id c = c_first + blockIdx.y over n_chunks.
-template <typename Tin, bool kRev>
+template <typename Tin, bool kRev, bool kDirect>
 __global__ __launch_bounds__(kWave) void chunk_state_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const float *__restrict__ A, const float *h0, float *hout, float *__restrict__ sout,
     int64_t T, int D, int64_t Tc, int n_chunks, int c_first)
 {
+    constexpr int U = 6;                      // tokens per pipeline stage
     const int lane = threadIdx.x;
     const int d_raw = blockIdx.x * kWave + lane;
     const bool live = d_raw < D;
@@ -89,6 +107,7 @@ __global__ __launch_bounds__(kWave) void chunk_state_kernel(
     const int b = blockIdx.z;
     const int64_t t_begin = (int64_t)c * Tc;
     const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
+    const int64_t len = t_end - t_begin;      // >= 1
 
     float a2[kStates], h[kStates];
     {
@@ -100,7 +119,7 @@ __global__ __launch_bounds__(kWave) void chunk_state_kernel(
             a2[4 * q + 2] = v.z * kLog2e; a2[4 * q + 3] = v.w * kLog2e;
         }
     }
-    if (h0 != nullptr) {
+    if (kDirect && h0 != nullptr) {
         const float4 *hr = reinterpret_cast<const float4 *>(h0 + ((int64_t)b * D + d) * kStates);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -112,29 +131,76 @@ __global__ __launch_bounds__(kWave) void chunk_state_kernel(
         for (int n = 0; n < kStates; ++n) h[n] = 0.f;
     }
     float S = 0.f;
-    const int64_t row = (int64_t)b * T;
-    const int64_t len = t_end - t_begin;
+    // Step k of the sweep is token t_first + k * step.  Row pointers are
+    // wave-uniform (scalar registers); lanes index them by channel, so the
+    // loads need no per-lane address arithmetic.
+    const int64_t step = kRev ? -(int64_t)D : (int64_t)D;
+    const int64_t t_first = kRev ? t_end - 1 : t_begin;
+    const Tin *xs = x + ((int64_t)b * T + t_first) * D;
+    const Tin *ds = dt + ((int64_t)b * T + t_first) * D;
+    const Tin *bs = Bm + ((int64_t)b * T + t_first) * kStates;
+    const int64_t bstep = kRev ? -kStates : kStates;
 
-#pragma unroll 4
-    for (int64_t k = 0; k < len; ++k) {
-        const int64_t t = kRev ? (t_end - 1 - k) : (t_begin + k);
-        const int64_t ix = (row + t) * D + d;
-        const float dl = widen(dt[ix]);
-        const float dx = dl * widen(x[ix]);
-        S += dl;
-        const Tin *brow = Bm + (row + t) * kStates;
+    auto consume = [&](const Tin *xr, const Tin *dr, int64_t k0, int count) {
 #pragma unroll
-        for (int n = 0; n < kStates; ++n) {
-            const float e = fast_exp2(dl * a2[n]);
-            h[n] = __builtin_fmaf(e, h[n], dx * widen(brow[n]));
+        for (int i = 0; i < U; ++i) {
+            if (i < count) {
+                const float dl = widen(dr[i]);
+                const float dx = dl * widen(xr[i]);
+                S += dl;
+                const Tin *brow = bs + (k0 + i) * bstep;
+#pragma unroll
+                for (int q = 0; q < kStates / 2; ++q) {
+                    float b0, b1;
+                    load_pair(brow, q, b0, b1);
+                    h[2 * q] = __builtin_fmaf(fast_exp2(dl * a2[2 * q]), h[2 * q], dx * b0);
+                    h[2 * q + 1] = __builtin_fmaf(fast_exp2(dl * a2[2 * q + 1]), h[2 * q + 1], dx * b1);
+                }
+            }
         }
+    };
+
+    const int64_t n_full = len / U;
+    const int rem = (int)(len - n_full * U);
+    Tin xr[U], dr[U];
+    if (n_full > 0) {
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            xr[i] = xs[i * step + d];
+            dr[i] = ds[i * step + d];
+        }
+    }
+    for (int64_t g = 0; g < n_full; ++g) {
+        // issue the next stage's loads before this stage's arithmetic
+        Tin xn[U], dn[U];
+        const int64_t kn = (g + 1) * U;
+        if (g + 1 < n_full) {
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                xn[i] = xs[(kn + i) * step + d];
+                dn[i] = ds[(kn + i) * step + d];
+            }
+        }
+        consume(xr, dr, g * U, U);
+#pragma unroll
+        for (int i = 0; i < U; ++i) { xr[i] = xn[i]; dr[i] = dn[i]; }
+    }
+    if (rem > 0) {
+        const int64_t k0 = n_full * U;
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int64_t k = k0 + (i < rem ? i : rem - 1);
+            xr[i] = xs[k * step + d];
+            dr[i] = ds[k * step + d];
+        }
+        consume(xr, dr, k0, rem);
     }
     if (live) {
         float4 *o = reinterpret_cast<float4 *>(hout + (((int64_t)b * n_chunks + c) * D + d) * kStates);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             o[q] = make_float4(h[4 * q + 0], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
-        if (sout != nullptr) sout[((int64_t)b * n_chunks + c) * D + d] = S;
+        if (!kDirect && sout != nullptr) sout[((int64_t)b * n_chunks + c) * D + d] = S;
     }
 }
 
@@ -260,10 +326,13 @@ __global__ __launch_bounds__(kWave * kWavesBidir) void bidir_kernel(
             const int ii = i < nvalid ? i : nvalid - 1;
             const Tin *brow = Bm + (row + t0 + ii) * kStates + s0;
             const float dx = dl[i] * xv[i];
+            float bv[4];
+            load_pair(brow, 0, bv[0], bv[1]);
+            load_pair(brow, 1, bv[2], bv[3]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 dA[i][j] = fast_exp2(dl[i] * a2[j]);
-                u[i][j] = dx * widen(brow[j]);
+                u[i][j] = dx * bv[j];
             }
         }
         // forward, ascending
@@ -271,11 +340,14 @@ __global__ __launch_bounds__(kWave * kWavesBidir) void bidir_kernel(
         for (int i = 0; i < kGroup; ++i) {
             const int ii = i < nvalid ? i : nvalid - 1;
             const Tin *crow = Cm + (row + t0 + ii) * kStates + s0;
+            float cv[4];
+            load_pair(crow, 0, cv[0], cv[1]);
+            load_pair(crow, 1, cv[2], cv[3]);
             float acc = 0.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 hf[j] = __builtin_fmaf(dA[i][j], hf[j], u[i][j]);
-                acc = __builtin_fmaf(widen(crow[j]), hf[j], acc);
+                acc = __builtin_fmaf(cv[j], hf[j], acc);
             }
             ya[i] = acc;
             if ((i + 1) % L == 0 && bounds != nullptr && i < nvalid && live) {
@@ -290,12 +362,15 @@ __global__ __launch_bounds__(kWave * kWavesBidir) void bidir_kernel(
         for (int i = kGroup - 1; i >= 0; --i) {
             const int ii = i < nvalid ? i : nvalid - 1;
             const Tin *crow = Cm + (row + t0 + ii) * kStates + s0;
+            float cv[4];
+            load_pair(crow, 0, cv[0], cv[1]);
+            load_pair(crow, 1, cv[2], cv[3]);
             if ((i + 1) % L == 0) { hr[0] = hr[1] = hr[2] = hr[3] = 0.f; }
             float acc = ya[i];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 hr[j] = __builtin_fmaf(dA[i][j], hr[j], u[i][j]);
-                acc = __builtin_fmaf(widen(crow[j]), hr[j], acc);
+                acc = __builtin_fmaf(cv[j], hr[j], acc);
             }
             ya[i] = acc;
         }
@@ -335,6 +410,7 @@ __global__ __launch_bounds__(kWave) void sweep_output_kernel(
     const float *__restrict__ hin, float *__restrict__ yf, Tin *__restrict__ y,
     int64_t T, int D, int64_t Tc, int n_chunks)
 {
+    constexpr int U = 4;                      // tokens per pipeline stage
     const int lane = threadIdx.x;
     const int d_raw = blockIdx.x * kWave + lane;
     const bool live = d_raw < D;
@@ -343,6 +419,7 @@ __global__ __launch_bounds__(kWave) void sweep_output_kernel(
     const int b = blockIdx.z;
     const int64_t t_begin = (int64_t)c * Tc;
     const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
+    const int64_t len = t_end - t_begin;
 
     float a2[kStates], h[kStates];
     {
@@ -358,30 +435,73 @@ __global__ __launch_bounds__(kWave) void sweep_output_kernel(
         }
     }
     const float dsk = Dskip[d];
-    const int64_t row = (int64_t)b * T;
-    const int64_t len = t_end - t_begin;
-#pragma unroll 2
-    for (int64_t k = 0; k < len; ++k) {
-        const int64_t t = kRev ? (t_end - 1 - k) : (t_begin + k);
-        const int64_t ix = (row + t) * D + d;
-        const float dl = widen(dt[ix]);
-        const float xr = widen(x[ix]);
-        const float dx = dl * xr;
-        const Tin *brow = Bm + (row + t) * kStates;
-        const Tin *crow = Cm + (row + t) * kStates;
-        float acc = 0.f;
+    const int64_t step = kRev ? -(int64_t)D : (int64_t)D;
+    const int64_t t_first = kRev ? t_end - 1 : t_begin;
+    const int64_t o_first = ((int64_t)b * T + t_first) * D;
+    const Tin *xs = x + o_first;
+    const Tin *ds = dt + o_first;
+    float *yfs = yf + o_first;
+    Tin *ys = y + o_first;
+    const Tin *bs = Bm + ((int64_t)b * T + t_first) * kStates;
+    const Tin *cs = Cm + ((int64_t)b * T + t_first) * kStates;
+    const int64_t bstep = kRev ? -kStates : kStates;
+
+    auto consume = [&](const Tin *xr, const Tin *dr, const float *yr, int64_t k0, int count) {
 #pragma unroll
-        for (int n = 0; n < kStates; ++n) {
-            const float e = fast_exp2(dl * a2[n]);
-            h[n] = __builtin_fmaf(e, h[n], dx * widen(brow[n]));
-            acc = __builtin_fmaf(widen(crow[n]), h[n], acc);
+        for (int i = 0; i < U; ++i) {
+            if (i < count) {
+                const float xv = widen(xr[i]);
+                const float dl = widen(dr[i]);
+                const float dx = dl * xv;
+                const Tin *brow = bs + (k0 + i) * bstep;
+                const Tin *crow = cs + (k0 + i) * bstep;
+                float acc = 0.f;
+#pragma unroll
+                for (int q = 0; q < kStates / 2; ++q) {
+                    float b0, b1, c0, c1;
+                    load_pair(brow, q, b0, b1);
+                    load_pair(crow, q, c0, c1);
+                    h[2 * q] = __builtin_fmaf(fast_exp2(dl * a2[2 * q]), h[2 * q], dx * b0);
+                    h[2 * q + 1] = __builtin_fmaf(fast_exp2(dl * a2[2 * q + 1]), h[2 * q + 1], dx * b1);
+                    acc = __builtin_fmaf(c0, h[2 * q], acc);
+                    acc = __builtin_fmaf(c1, h[2 * q + 1], acc);
+                }
+                const int64_t o = (k0 + i) * step + d;
+                if (!kRev) {
+                    if (live) yfs[o] = acc;
+                } else {
+                    const float tot = yr[i] + acc + dsk * xv;
+                    if (live) ys[o] = narrow<Tin>(tot);
+                }
+            }
         }
-        if (!kRev) {
-            if (live) yf[ix] = acc;
-        } else {
-            const float tot = yf[ix] + acc + dsk * xr;
-            if (live) y[ix] = narrow<Tin>(tot);
+    };
+
+    const int64_t n_full = len / U;
+    const int rem = (int)(len - n_full * U);
+    Tin xr[U], dr[U];
+    float yr[U];
+    auto load_stage = [&](int64_t k0, int count, Tin *xo, Tin *dout, float *yo) {
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int64_t k = k0 + (i < count ? i : count - 1);
+            xo[i] = xs[k * step + d];
+            dout[i] = ds[k * step + d];
+            if (kRev) yo[i] = yfs[k * step + d];
         }
+    };
+    if (n_full > 0) load_stage(0, U, xr, dr, yr);
+    for (int64_t g = 0; g < n_full; ++g) {
+        Tin xn[U], dn[U];
+        float yn[U];
+        if (g + 1 < n_full) load_stage((g + 1) * U, U, xn, dn, yn);
+        consume(xr, dr, yr, g * U, U);
+#pragma unroll
+        for (int i = 0; i < U; ++i) { xr[i] = xn[i]; dr[i] = dn[i]; yr[i] = yn[i]; }
+    }
+    if (rem > 0) {
+        load_stage(n_full * U, rem, xr, dr, yr);
+        consume(xr, dr, yr, n_full * U, rem);
     }
 }
 

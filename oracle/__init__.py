@@ -12,5 +12,5 @@ C file's header.
 """
 from .oracle import (  # noqa: F401
     build, load, scan, prefill, block_step, commit, train_scan, full_scan,
-    F32, BF16,
+    F32, BF16, num_threads,
 )

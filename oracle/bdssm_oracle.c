@@ -46,6 +46,9 @@
 #include <stddef.h>
 #include <string.h>
 #include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
@@ -63,6 +66,16 @@ static double ld(const void *p, size_t i, int dtype)
 }
 
 int oracle_version(void) { return 1; }
+
+/* Threads the OpenMP loop over rows will use (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /*
  * Core routine.  Shapes (row-major, contiguous):

@@ -43,8 +43,14 @@ def load():
         lib.oracle_scan.argtypes = [I, I, I, I, I, ctypes.c_int] + [P] * 12
         lib.oracle_scan.restype = ctypes.c_int
         lib.oracle_version.restype = ctypes.c_int
+        lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
+
+
+def num_threads():
+    """Threads the oracle's row loop uses."""
+    return load().oracle_num_threads()
 
 
 def _ptr(a):

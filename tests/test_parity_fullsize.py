@@ -1,0 +1,109 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (same shapes, same chunk plan, same kernels), checked on
+sampled channels: the oracle recomputes those channels' rows from the same
+device-resident inputs (rows are independent, so a subset of channels is an
+exact sub-problem).  Expected values come from the oracle alone: its cache
+for the block step is its own prefill over the sampled channels.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mamba_selective_scan_04_amd as m
+import oracle
+from mamba_selective_scan_04_amd import synth
+from parity_util import N, STATE_TOL, TOL, rel_err, to_np, worst
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = TOL[torch.bfloat16]
+
+
+def sample_channels(D, k, seed):
+    g = np.random.default_rng(seed)
+    ch = np.sort(g.choice(D, size=k, replace=False))
+    ch[0] = 0
+    ch[-1] = D - 1            # include both ends of the channel range
+    return ch
+
+
+def gather(t, ch):
+    return t.index_select(2, torch.as_tensor(ch, device=t.device))
+
+
+def ora(t):
+    return synth.to_oracle(t)
+
+
+@pytest.mark.parametrize("name", ["infer_65k_b1", "infer_65k_b8", "infer_262k_b1", "infer_262k_b16"])
+def test_inference_workload_sampled(dev, name):
+    wl = synth.WORKLOADS[name]
+    batch, D, ctx, L, sid = wl["batch"], wl["d_inner"], wl["ctx"], wl["block"], wl["sid"]
+    print("[fullsize] %s: batch %d, D %d, ctx %d" % (name, batch, D, ctx), flush=True)
+    dtype = synth.TORCH_DTYPE[wl["dtype"]]
+    x, dt, Bm, Cm = synth.stream(batch, ctx, D, N, sid, 0, dtype, dev)
+    A, Dskip = synth.params(D, N, sid, "default", dev)
+    h, _ = m.prefill(x, dt, Bm, Cm, A, Dskip, L)
+    s0 = synth.step_inputs(batch, L, D, N, sid, 0, dtype, dev)
+    s15 = synth.step_inputs(batch, L, D, N, sid, 15, dtype, dev)
+    y0 = m.block_step(h, *s0, A, Dskip)
+    y15 = m.block_step(h, *s15, A, Dskip)
+    c0 = synth.commit_inputs(batch, L, D, N, sid, 0, dtype, dev)
+    h_pre = h.clone()
+    m.commit(h, *c0, A, Dskip)
+    torch.cuda.synchronize()
+
+    ch = sample_channels(D, 8, 17)
+    Ah, Dh = ora(A[torch.as_tensor(ch, device=dev)]), ora(Dskip[torch.as_tensor(ch, device=dev)])
+    ho, _ = oracle.prefill(ora(gather(x, ch)), ora(gather(dt, ch)), ora(Bm), ora(Cm), Ah, Dh, L)
+    del x, dt
+    got_h = to_np(h_pre[:, torch.as_tensor(ch, device=dev)])
+    assert rel_err(got_h, ho) < STATE_TOL, worst(got_h, ho)
+    for s, yg in ((s0, y0), (s15, y15)):
+        yo = oracle.block_step(ho, ora(gather(s[0], ch)), ora(gather(s[1], ch)), ora(s[2]), ora(s[3]), Ah, Dh)
+        got = to_np(gather(yg, ch))
+        assert rel_err(got, yo) < TOL_BF16, worst(got, yo)
+    ho2, _ = oracle.commit(ho, ora(gather(c0[0], ch)), ora(gather(c0[1], ch)), ora(c0[2]), ora(c0[3]), Ah, Dh)
+    got_h2 = to_np(h[:, torch.as_tensor(ch, device=dev)])
+    assert rel_err(got_h2, ho2) < STATE_TOL, worst(got_h2, ho2)
+
+
+@pytest.mark.parametrize("name", ["train_87m", "train_350m"])
+def test_training_workload_sampled(dev, name):
+    wl = synth.WORKLOADS[name]
+    batch, D, T, L, sid = wl["batch"], wl["d_inner"], wl["seq"], wl["block"], wl["sid"]
+    print("[fullsize] %s: batch %d, D %d, T %d" % (name, batch, D, T), flush=True)
+    dtype = synth.TORCH_DTYPE[wl["dtype"]]
+    x, dt, Bm, Cm = synth.stream(batch, T, D, N, sid, 0, dtype, dev)
+    A, Dskip = synth.params(D, N, sid, "default", dev)
+    y, bnd = m.train_scan(x, dt, Bm, Cm, A, Dskip, L, want_bounds=True)
+    yfull = m.full_scan(x, dt, Bm, Cm, A, Dskip)
+    torch.cuda.synchronize()
+    ch = sample_channels(D, 8, 23)
+    idx = torch.as_tensor(ch, device=dev)
+    args = (ora(gather(x, ch)), ora(gather(dt, ch)), ora(Bm), ora(Cm), ora(A[idx]), ora(Dskip[idx]))
+    r = oracle.scan(*args, L, want_y=True, want_bounds=True)
+    got = to_np(gather(y, ch))
+    assert rel_err(got, r["y"]) < TOL_BF16, worst(got, r["y"])
+    gb = to_np(bnd[:, :, idx])
+    assert rel_err(gb, r["bounds"]) < STATE_TOL, worst(gb, r["bounds"])
+    yfo = oracle.full_scan(*args)
+    gf = to_np(gather(yfull, ch))
+    assert rel_err(gf, yfo) < TOL_BF16, worst(gf, yfo)
+
+
+def test_baseline_full_scan_65k_sampled(dev):
+    """The contrast baseline at the size the benchmark times it: the 65,536
+    token context plus one 16-token block, batch 8."""
+    wl = synth.WORKLOADS["infer_65k_b8"]
+    batch, D, T, sid = wl["batch"], wl["d_inner"], wl["ctx"] + wl["block"], wl["sid"]
+    x, dt, Bm, Cm = synth.stream(batch, T, D, N, sid, 200, torch.bfloat16, dev)
+    A, Dskip = synth.params(D, N, sid, "default", dev)
+    y = m.full_scan(x, dt, Bm, Cm, A, Dskip)
+    torch.cuda.synchronize()
+    ch = sample_channels(D, 4, 29)
+    idx = torch.as_tensor(ch, device=dev)
+    yo = oracle.full_scan(ora(gather(x, ch)), ora(gather(dt, ch)), ora(Bm), ora(Cm),
+                          ora(A[idx]), ora(Dskip[idx]))
+    got = to_np(gather(y, ch))
+    assert rel_err(got, yo) < TOL_BF16, worst(got, yo)
