@@ -62,6 +62,37 @@ def bytes_full(batch, T, D, e):
     return batch * T * D * 3 * e + batch * T * NS * 2 * e + 4 * D * NS + 4 * D
 
 
+def committed_traffic(workload, batch, D):
+    """HBM bytes per prefill (chunk scan + carry) from the committed counter
+    summary for this workload, or None if there is none or the kernels have
+    changed since it was taken (source hash mismatch)."""
+    from mamba_selective_scan_04_amd import profile_summary
+    path = os.path.join(ROOT, "profiles", "prefill_%s_hbm_traffic.md" % workload.replace("infer_", ""))
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    if "kernel source hash: %s" % profile_summary.source_hash() not in txt:
+        return None
+    chunk, carry = None, None
+    carry_grid = (batch * D * NS + 255) // 256 * 256
+    for line in txt.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) != 7:
+            continue
+        try:
+            grid, rd, wr = int(cells[1]), float(cells[5]), float(cells[6])
+        except ValueError:
+            continue
+        if cells[0].startswith("chunk_state_kernel<") and cells[0].endswith("false, false>"):
+            if chunk is None or grid > chunk[0]:
+                chunk = (grid, rd + wr)
+        if cells[0] == "carry_kernel<false>" and grid == carry_grid:
+            carry = rd + wr
+    if chunk is None or carry is None:
+        return None
+    return chunk[1] + carry
+
+
 def slots_forward(batch, T, D):
     """exp2 (2 slots) + dt*A' mul + (dt*x)*B mul + state FMA per (b,t,d,n),
     plus the dt*x multiply per (b,t,d)."""
@@ -86,6 +117,8 @@ def main():
     ap.add_argument("--no-baseline-scan", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch block steps eagerly (no graph)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (scale for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -122,6 +155,15 @@ def main():
                      dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log("[bench] inputs generated on device in %.1f s" % (time.time() - t_gen))
+    if args.copy_calibration:
+        # a plain copy of known size: 1 GiB read + 1 GiB written per launch
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] copy calibration: 3 x 1 GiB device copies")
 
     def prefill():
         m.prefill(x, dt, Bm, Cm, A, Dskip, L, h_cache=h, ws=ws)
@@ -226,7 +268,7 @@ def main():
         "op": "fp32 VALU issue slot (mul/FMA 1, v_exp_f32 %d); per (token, channel): "
               "16 x (exp2 + 2 mul + FMA) + 1 mul" % EXP_SLOTS,
         "frac": achieved_slots / VALU_SLOTS_PER_S,
-        "traffic": None,
+        "traffic": committed_traffic(args.workload, batch, D),
         "hbm_achieved_GBs": pf_bytes / (pf_ms * 1e-3) / 1e9,
         "hbm_frac": pf_bytes / (pf_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "launch_ms": pf_ms,

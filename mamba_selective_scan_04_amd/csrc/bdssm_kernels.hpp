@@ -230,7 +230,23 @@ __global__ __launch_bounds__(256) void carry_kernel(
     const int64_t base_s = b * n_chunks * (int64_t)D + d;
     float h = (h_init != nullptr && !kRev) ? h_init[i] : 0.f;
     if (!kRev) {
-        for (int c = 0; c < n_agg; ++c) {
+        // Groups of 8 chunks: the 16 loads and 8 decays of a group do not
+        // depend on h, so only the 8 FMAs form the serial chain.
+        int c = 0;
+        for (; c + 8 <= n_agg; c += 8) {
+            float g[8], l[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                g[k] = fast_exp2(a2 * agg_s[base_s + (int64_t)(c + k) * D]);
+                l[k] = agg_h[base_h + (c + k) * cs];
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                if (h_in) h_in[base_h + (c + k) * cs] = h;
+                h = __builtin_fmaf(g[k], h, l[k]);
+            }
+        }
+        for (; c < n_agg; ++c) {
             if (h_in) h_in[base_h + c * cs] = h;
             const float s = agg_s[base_s + (int64_t)c * D];
             h = __builtin_fmaf(fast_exp2(a2 * s), h, agg_h[base_h + c * cs]);

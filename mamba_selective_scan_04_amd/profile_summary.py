@@ -1,0 +1,114 @@
+"""Condense rocprofv3 CSV output into the short text summaries kept under
+profiles/.
+
+  python -m mamba_selective_scan_04_amd.profile_summary trace <kernel_trace.csv>
+      per (kernel, grid) launch group: calls, average / min / max duration
+  python -m mamba_selective_scan_04_amd.profile_summary pmc <FETCH counter_collection.csv> \
+      <WRITE counter_collection.csv>
+      per (kernel, grid): FETCH_SIZE and WRITE_SIZE per dispatch, raw (KiB) and
+      scaled to bytes by what the same counter reads for a plain device copy of
+      known size (the 1 GiB copyBuffer launches of bench.py --copy-calibration)
+
+Only this library's kernels (bdssm_dev::) and the calibration copy are listed.
+The summary starts with the source hash of the kernels so a stale profile can
+be recognised.
+"""
+import collections
+import csv
+import hashlib
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = [os.path.join(HERE, "csrc", "bdssm_kernels.hpp"), os.path.join(HERE, "csrc", "bdssm.hip")]
+COPY_BYTES = 1 << 30
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short(name):
+    n = name.split("(")[0]
+    return n.replace("void ", "").replace("bdssm_dev::", "").replace("unsigned short", "bf16")
+
+
+def keep(name):
+    return "bdssm_dev::" in name or "copyBuffer" in name
+
+
+def trace(path):
+    groups = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if not keep(r["Kernel_Name"]):
+            continue
+        grid = (int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]))
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups[(short(r["Kernel_Name"]), grid)].append(dur)
+    out = ["kernel source hash: %s" % source_hash(), "",
+           "| kernel | grid (threads x,y,z) | calls | avg us | min us | max us |",
+           "|---|---|---:|---:|---:|---:|"]
+    for (k, g), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        out.append("| %s | %s | %d | %.2f | %.2f | %.2f |" % (k, "x".join(map(str, g)), len(v),
+                                                           sum(v) / len(v), min(v), max(v)))
+    return "\n".join(out)
+
+
+def _counters(path):
+    groups = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if not keep(r["Kernel_Name"]):
+            continue
+        groups[(short(r["Kernel_Name"]), int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+    return groups
+
+
+def pmc(fetch_path, write_path):
+    f = _counters(fetch_path)
+    w = _counters(write_path)
+    # the calibration copies are the copyBuffer launch group that writes the most
+    copies = [key for key in w if "copyBuffer" in key[0]]
+    if not copies:
+        raise SystemExit("no calibration copy in the counter files (run bench.py --copy-calibration)")
+    ckey = max(copies, key=lambda k: sum(w[k]) / len(w[k]))
+    cf, cw = f.get(ckey, []), w[ckey]
+    if not cf or not cw:
+        raise SystemExit("no calibration copy in the counter files (run bench.py --copy-calibration)")
+    sf = COPY_BYTES / (sum(cf) / len(cf) * 1024)
+    sw = COPY_BYTES / (sum(cw) / len(cw) * 1024)
+    out = ["kernel source hash: %s" % source_hash(), "",
+           "calibration: a 1 GiB device copy reads FETCH_SIZE %.0f KiB and WRITE_SIZE %.0f KiB per "
+           "dispatch, so bytes = FETCH_SIZE x 1024 x %.4f and WRITE_SIZE x 1024 x %.4f"
+           % (sum(cf) / len(cf), sum(cw) / len(cw), sf, sw), "",
+           "| kernel | grid (threads) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes | write bytes |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
+    for key in sorted(set(f) | set(w), key=lambda k: -sum(f.get(k, [0]))):
+        if "copyBuffer" in key[0]:
+            continue
+        fv, wv = f.get(key, []), w.get(key, [])
+        fa = sum(fv) / len(fv) if fv else float("nan")
+        wa = sum(wv) / len(wv) if wv else float("nan")
+        out.append("| %s | %d | %d | %.1f | %.1f | %.4g | %.4g |" % (
+            key[0], key[1], max(len(fv), len(wv)), fa, wa, fa * 1024 * sf, wa * 1024 * sw))
+    return "\n".join(out)
+
+
+def main(argv):
+    if len(argv) >= 2 and argv[0] == "trace":
+        print(trace(argv[1]))
+    elif len(argv) >= 3 and argv[0] == "pmc":
+        print(pmc(argv[1], argv[2]))
+    elif len(argv) >= 1 and argv[0] == "hash":
+        print(source_hash())
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))

@@ -241,3 +241,40 @@ def test_in_place_prefill_continuation(dev):
     _sync()
     ho, _ = oracle.prefill(*c.oracle_args(), 16)
     assert rel_err(to_np(h), ho) < STATE_TOL
+
+
+def test_graph_replay_matches_eager(dev):
+    """The inference calls can be captured in a HIP graph (no memset or
+    allocation inside): replays, with eager work and synchronisations in
+    between, reproduce the eager results bit for bit every time."""
+    c = Case(2, 16 * 40, 130, torch.bfloat16, sid=17, a_kind="random")
+    L, P = 16, 16 * 36
+    h, _ = m.prefill(*c.segment(0, P), L)
+    blocks = [c.segment(P + k * L, P + (k + 1) * L) for k in range(4)]
+    # eager reference: 3 block steps on block 0, commit block 0, 1 step on block 1
+    h_ref = h.clone()
+    ys_ref = [m.block_step(h_ref, *blocks[0]) for _ in range(3)]
+    m.commit(h_ref, *blocks[0])
+    y_next_ref = m.block_step(h_ref, *blocks[1])
+    torch.cuda.synchronize()
+    hg = torch.empty_like(h)
+    ys = [torch.empty_like(ys_ref[0]) for _ in range(3)]
+    y_next = torch.empty_like(y_next_ref)
+    g = torch.cuda.CUDAGraph()
+    hg.copy_(h)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(3):
+            m.block_step(hg, *blocks[0], y=ys[i])
+        m.commit(hg, *blocks[0])
+        m.block_step(hg, *blocks[1], y=y_next)
+    for rep in range(4):
+        hg.copy_(h)                               # eager work between replays
+        _ = m.block_step(h, *blocks[2])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert torch.equal(ys[i], ys_ref[i]), rep
+        assert torch.equal(hg, h_ref), rep
+        assert torch.equal(y_next, y_next_ref), rep
