@@ -132,8 +132,8 @@ def main():
 
     m.load()   # fails loudly if the HIP library is missing
     wl = dict(synth.WORKLOADS[args.workload])
-    if "ctx" not in wl or "steps" not in wl:
-        raise SystemExit("workload %s is not an inference workload" % args.workload)
+    if "seq" in wl:
+        return train_main(args, wl, m, synth, torch)
     batch, D, ctx, L = wl["batch"], wl["d_inner"], wl["ctx"], wl["block"]
     S, nblk, sid = wl["steps"], wl["n_blocks"], wl["sid"]
     dtype = synth.TORCH_DTYPE[wl["dtype"]]
@@ -334,6 +334,71 @@ def main():
         "baseline_full_scan": baseline,
         "roofline": roofline,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def train_main(args, wl, m, synth, torch):
+    """Training workloads: one step = one all-block training scan (continuous
+    forward + reverse segmented per block) over the batch.  The full-sequence
+    bidirectional scan over the same tokens is timed beside it."""
+    batch, D, T, L, sid = wl["batch"], wl["d_inner"], wl["seq"], wl["block"], wl["sid"]
+    dtype = synth.TORCH_DTYPE[wl["dtype"]]
+    e = 2 if dtype == torch.bfloat16 else 4
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    st = torch.cuda.current_stream()
+    log("[bench] workload %s: batch %d, d_inner %d, T %d, block %d" % (args.workload, batch, D, T, L))
+    x, dt, Bm, Cm = synth.stream(batch, T, D, NS, sid, 0, dtype, dev)
+    A, Dskip = synth.params(D, NS, sid, "default", dev)
+    y = torch.empty_like(x)
+    ws = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_TRAIN, L, NS, dtype)),
+                     dtype=torch.uint8, device=dev)
+    wsf = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_FULL, 1, NS, dtype)),
+                      dtype=torch.uint8, device=dev)
+
+    def step():
+        m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(st)
+        step()
+        evs[i][1].record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    nbytes = bytes_full(batch, T, D, e)
+    slots = slots_bidirectional(batch, T, D)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m.full_scan(x, dt, Bm, Cm, A, Dskip, y=y, ws=wsf)
+    a.record(st)
+    for _ in range(args.steps):
+        m.full_scan(x, dt, Bm, Cm, A, Dskip, y=y, ws=wsf)
+    b.record(st)
+    torch.cuda.synchronize()
+    full_ms = a.elapsed_time(b) / args.steps
+    line = {
+        "metric": "all-block training scan GB/s (forward over T + reverse per block)",
+        "value": nbytes / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if dtype == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": batch, "d_inner": D, "d_state": NS,
+                   "seq": T, "block": L},
+        "train_scan": {"ms": ev_ms, "tokens_per_s": batch * T / (ev_ms * 1e-3),
+                       "GBs": nbytes / (ev_ms * 1e-3) / 1e9,
+                       "valu_slot_frac": slots / (ev_ms * 1e-3) / VALU_SLOTS_PER_S,
+                       "hbm_frac": nbytes / (ev_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "full_scan": {"ms": full_ms, "tokens_per_s": batch * T / (full_ms * 1e-3),
+                      "train_scan_over_full_scan_time": ev_ms / full_ms},
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -26,6 +26,10 @@
 #include "bdssm.h"
 #include "bdssm_kernels.hpp"
 
+#ifndef BDSSM_BIDIR_WAVES
+#define BDSSM_BIDIR_WAVES 8
+#endif
+
 using namespace bdssm_dev;
 
 namespace {
@@ -34,8 +38,11 @@ constexpr int kVersion = 10000;   // 1.0.0
 
 // 256 CUs x 4 SIMDs x 8 resident waves (the chunk kernel fits in 64 VGPRs)
 constexpr int64_t kFineWaves = 256 * 4 * 8;
-// 2 workgroups of the bidirectional kernel per CU
-constexpr int64_t kCoarseGroups = 512;
+// waves per workgroup of the bidirectional kernel (16 / kWavesBidir states per wave)
+constexpr int kWavesBidir = BDSSM_BIDIR_WAVES;
+// workgroups of the bidirectional kernel resident at once (one 8-wave
+// workgroup per CU at its register use)
+constexpr int64_t kCoarseGroups = 256;
 
 // ------------------------------------------------------------ launch policy
 //
@@ -45,13 +52,14 @@ constexpr int64_t kCoarseGroups = 512;
 //   fine chunks  (one wave per 64 channels, 16 states per lane): at most
 //                kFineWaves waves, the number resident at once (8 per SIMD),
 //                so the launch runs in a single round with no tail.
-//   coarse chunks (bidirectional pass, 4 waves per 64 channels): aim for
-//                kCoarseGroups workgroups, 2 per CU, each a whole number of
+//   coarse chunks (bidirectional pass, one 8-wave workgroup per 64
+//                channels): count chosen by a small cost model (below) against
+//                kCoarseGroups resident workgroups; each is a whole number of
 //                fine chunks so its incoming state is a fine-chunk boundary.
 // Every chunk is a multiple of 16 tokens, so blocks of L | 16 never straddle.
 // BDSSM_FINE_WAVES / BDSSM_COARSE_GROUPS / BDSSM_CHUNK (fine chunk length in
-// tokens) override the targets; they exist for tuning sweeps and for the
-// chunk-invariance tests.
+// tokens) / BDSSM_COARSE_CHUNKS override the targets; they exist for tuning
+// sweeps and for the chunk-invariance tests.
 struct Plan {
     int64_t fine_len;    // tokens per fine chunk (multiple of 16)
     int n_fine;          // number of fine chunks
@@ -87,11 +95,28 @@ Plan make_plan(int64_t batch, int64_t D, int64_t T) {
     const int64_t forced = env_int("BDSSM_CHUNK", 0);
     if (forced > 0) fl = ceil_div(forced, kGroup) * kGroup;
     if (ceil_div(T, fl) > 65535) fl = ceil_div(ceil_div(T, 65535), kGroup) * kGroup;
+    // every chunk's rows of one stream must stay below 2^31 bytes (32-bit
+    // buffer offsets); 4 bytes per element covers both dtypes
+    const int64_t max_tok = ((((int64_t)1 << 31) - 1) / (D * 4)) / kGroup * kGroup;
+    if (fl > max_tok) fl = max_tok;
     nf = ceil_div(T, fl);
-    int64_t nc = ceil_div(coarse_groups, groups);
-    if (nc > nf) nc = nf;
-    if (nc < 1) nc = 1;
-    const int64_t per = ceil_div(nf, nc);
+    // Coarse chunk count: each extra chunk adds parallelism to the
+    // bidirectional pass but costs a forward pre-pass over its tokens.
+    // Estimated time, in units of "one resident wave of workgroups scanning
+    // the whole sequence": ceil(groups * nc / capacity) / nc for the pass
+    // itself, plus the pre-pass over (nc - 1) / nc of the tokens at full
+    // occupancy, weighted by its share of issue slots (~0.45).
+    int64_t nc = 1;
+    double best = 1e30;
+    for (int64_t cand = 1; cand <= 32 && cand <= nf; ++cand) {
+        const double rounds = (double)ceil_div(groups * cand, coarse_groups);
+        const double est = rounds / cand + 0.45 * (double)(cand - 1) / cand * (double)groups / coarse_groups;
+        if (est < best - 1e-9) { best = est; nc = cand; }
+    }
+    const int64_t forced_nc = env_int("BDSSM_COARSE_CHUNKS", 0);
+    if (forced_nc > 0) nc = forced_nc < nf ? forced_nc : nf;
+    int64_t per = ceil_div(nf, nc);
+    if (per * fl > max_tok) per = max_tok / fl;
     nc = ceil_div(nf, per);
     p.fine_len = fl;
     p.n_fine = (int)nf;
@@ -151,7 +176,8 @@ int check_shape(const bdssm_shape *s) {
     if (s->d_state != kStates) return BDSSM_ERR_SHAPE;
     const int64_t L = s->block_len;
     if (!(L == 1 || L == 2 || L == 4 || L == 8 || L == 16)) return BDSSM_ERR_SHAPE;
-    if (s->d_inner > (int64_t)1 << 30 || s->batch > 65535) return BDSSM_ERR_SHAPE;
+    // d_inner bound keeps a 16-token group of one stream within 32-bit buffer offsets
+    if (s->d_inner > (int64_t)1 << 24 || s->batch > 65535) return BDSSM_ERR_SHAPE;
     return BDSSM_OK;
 }
 
@@ -250,9 +276,10 @@ void launch_bidir_L(const void *x, const void *dt, const void *B, const void *C,
                     const float *Dskip, const float *hin, int64_t hin_bs, int64_t hin_cs, void *y,
                     float *bounds, float *hout, int64_t batch, int64_t T, int64_t D, int64_t Tc,
                     int n_chunks, hipStream_t st) {
-    hipLaunchKernelGGL((bidir_kernel<Tin, L>), grid3(D, n_chunks, batch), dim3(kWave * kWavesBidir),
-                       0, st, (const Tin *)x, (const Tin *)dt, (const Tin *)B, (const Tin *)C, A,
-                       Dskip, hin, hin_bs, hin_cs, (Tin *)y, bounds, hout, T, (int)D, Tc);
+    hipLaunchKernelGGL((bidir_kernel<Tin, L, kWavesBidir>), grid3(D, n_chunks, batch),
+                       dim3(kWave * kWavesBidir), 0, st, (const Tin *)x, (const Tin *)dt,
+                       (const Tin *)B, (const Tin *)C, A, Dskip, hin, hin_bs, hin_cs, (Tin *)y,
+                       bounds, hout, T, (int)D, Tc);
 }
 
 template <typename Tin>

@@ -41,7 +41,6 @@ namespace bdssm_dev {
 constexpr int kStates = 16;      // d_state handled by this build
 constexpr int kWave = 64;        // gfx950 wavefront
 constexpr int kGroup = 16;       // tokens per register-resident group in the bidirectional kernel
-constexpr int kWavesBidir = 4;   // waves per workgroup of the bidirectional kernel (4 states each)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------- element io
@@ -76,6 +75,66 @@ __device__ __forceinline__ void load_pair(const float *row, int q, float &lo, fl
 // Wave-uniform value kept in a scalar register.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// A wave-uniform pointer, asserted as such so that loads through it become
+// scalar loads even when the compiler cannot prove uniformity by itself.
+template <typename T> __device__ __forceinline__ T *uniform_ptr(T *p) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = (uint32_t)uniform((int)(uint32_t)a);
+    const uint64_t hi = (uint32_t)uniform((int)(uint32_t)(a >> 32));
+    return reinterpret_cast<T *>(lo | (hi << 32));
+}
+
+// ---------------------------------------------------------- token-row streams
+//
+// x, dt and y are [batch, T, D] with lanes on channels.  A chunk's rows are
+// read and written through a raw buffer resource based at the chunk's first
+// row: the lane's byte offset (channel * element size) sits in one VGPR for
+// the whole kernel and the row offset (k * D * element size) in a scalar
+// register, so streaming a row costs no VALU address arithmetic.  The launch
+// plan keeps every chunk below 2^31 bytes per stream.
+constexpr int32_t kRawBufferWord3 = 0x00020000;   // gfx9-family raw buffer descriptor
+
+// One row of 64 elements from a raw buffer straight into LDS (lane i's element
+// lands zero-extended in dword i of the destination).
+typedef __attribute__((address_space(3))) void lds_void;
+template <int kBytes>
+__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t rsrc, void *lds_dst, int voffset, int soffset) {
+    static_assert(kBytes == 2 || kBytes == 4, "16- or 32-bit elements");
+    if constexpr (kBytes == 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)lds_dst, 2, voffset, soffset, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)lds_dst, 4, voffset, soffset, 0, 0);
+}
+
+template <typename Tin> struct Rows {
+    __amdgpu_buffer_rsrc_t rsrc;
+    int32_t lane_off;    // channel * sizeof(Tin)
+    int32_t pitch;       // D * sizeof(Tin)
+
+    __device__ __forceinline__ Rows(const Tin *first_row, int64_t nrows, int D, int d) {
+        pitch = uniform(D * (int32_t)sizeof(Tin));
+        lane_off = d * (int32_t)sizeof(Tin);
+        // the base and size are wave-uniform; say so, so that the descriptor
+        // is built in scalar registers (no per-lane waterfall)
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(const_cast<Tin *>(first_row)), 0,
+                                                 uniform((int)(nrows * pitch)), kRawBufferWord3);
+    }
+    __device__ __forceinline__ Tin load(int k) const;
+    __device__ __forceinline__ void store(int k, Tin v) const;
+};
+template <> __device__ __forceinline__ uint16_t Rows<uint16_t>::load(int k) const {
+    return __builtin_amdgcn_raw_buffer_load_b16(rsrc, lane_off, k * pitch, 0);
+}
+template <> __device__ __forceinline__ float Rows<float>::load(int k) const {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, lane_off, k * pitch, 0));
+}
+template <> __device__ __forceinline__ void Rows<uint16_t>::store(int k, uint16_t v) const {
+    __builtin_amdgcn_raw_buffer_store_b16(v, rsrc, lane_off, k * pitch, 0);
+}
+template <> __device__ __forceinline__ void Rows<float>::store(int k, float v) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsrc, lane_off, k * pitch, 0);
+}
+
 // ------------------------------------------------------------------------
 // Chunk-local directional scan, one lane per channel, all 16 states in
 // registers.  Used for
@@ -85,11 +144,10 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 //   * kDirect: a forward pass over one chunk from h0 (commit without output,
 //     prefill of a short context), writing the final state (a separate
 //     instantiation so profiles tell the two uses apart).
-// Tokens stream through a 6-deep register pipeline: the loads of the next 6
-// tokens are issued before the arithmetic of the current 6 (6 keeps the bf16
-// kernel at <= 64 VGPRs, i.e. 8 waves per SIMD).
 // kRev scans the chunk from its last token to its first (the reverse
 // direction of the full-sequence baseline).
+// Tokens stream through an 8-deep register pipeline: the loads of the next 8
+// tokens are issued before the arithmetic of the current 8.
 // grid = (ceil(D/64), chunks launched, batch), block = 64.
 // hout / sout are indexed by chunk id c = c_first + blockIdx.y over n_chunks.
 template <typename Tin, bool kRev, bool kDirect>
@@ -98,7 +156,7 @@ __global__ __launch_bounds__(kWave) void chunk_state_kernel(
     const float *__restrict__ A, const float *h0, float *hout, float *__restrict__ sout,
     int64_t T, int D, int64_t Tc, int n_chunks, int c_first)
 {
-    constexpr int U = 6;                      // tokens per pipeline stage
+    constexpr int U = 8;                      // tokens per pipeline stage
     const int lane = threadIdx.x;
     const int d_raw = blockIdx.x * kWave + lane;
     const bool live = d_raw < D;
@@ -107,7 +165,7 @@ __global__ __launch_bounds__(kWave) void chunk_state_kernel(
     const int b = blockIdx.z;
     const int64_t t_begin = (int64_t)c * Tc;
     const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
-    const int64_t len = t_end - t_begin;      // >= 1
+    const int len = (int)(t_end - t_begin);   // >= 1
 
     float a2[kStates], h[kStates];
     {
@@ -131,24 +189,21 @@ __global__ __launch_bounds__(kWave) void chunk_state_kernel(
         for (int n = 0; n < kStates; ++n) h[n] = 0.f;
     }
     float S = 0.f;
-    // Step k of the sweep is token t_first + k * step.  Row pointers are
-    // wave-uniform (scalar registers); lanes index them by channel, so the
-    // loads need no per-lane address arithmetic.
-    const int64_t step = kRev ? -(int64_t)D : (int64_t)D;
-    const int64_t t_first = kRev ? t_end - 1 : t_begin;
-    const Tin *xs = x + ((int64_t)b * T + t_first) * D;
-    const Tin *ds = dt + ((int64_t)b * T + t_first) * D;
-    const Tin *bs = Bm + ((int64_t)b * T + t_first) * kStates;
-    const int64_t bstep = kRev ? -kStates : kStates;
+    const int64_t first = (int64_t)b * T + t_begin;           // first row of the chunk
+    const Rows<Tin> xs(x + first * D, len, D, d);
+    const Rows<Tin> ds(dt + first * D, len, D, d);
+    const Tin *bs = Bm + first * kStates;
+    // step k of the sweep visits row pos(k) of the chunk
+    auto pos = [&](int k) -> int { return kRev ? len - 1 - k : k; };
 
-    auto consume = [&](const Tin *xr, const Tin *dr, int64_t k0, int count) {
+    auto consume = [&](const Tin *xr, const Tin *dr, int k0, int count) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             if (i < count) {
                 const float dl = widen(dr[i]);
                 const float dx = dl * widen(xr[i]);
                 S += dl;
-                const Tin *brow = bs + (k0 + i) * bstep;
+                const Tin *brow = bs + (int64_t)pos(k0 + i) * kStates;
 #pragma unroll
                 for (int q = 0; q < kStates / 2; ++q) {
                     float b0, b1;
@@ -159,41 +214,30 @@ __global__ __launch_bounds__(kWave) void chunk_state_kernel(
             }
         }
     };
-
-    const int64_t n_full = len / U;
-    const int rem = (int)(len - n_full * U);
-    Tin xr[U], dr[U];
-    if (n_full > 0) {
+    auto load_stage = [&](int k0, int count, Tin *xo, Tin *dout) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-            xr[i] = xs[i * step + d];
-            dr[i] = ds[i * step + d];
+            const int k = pos(k0 + (i < count ? i : count - 1));
+            xo[i] = xs.load(k);
+            dout[i] = ds.load(k);
         }
-    }
-    for (int64_t g = 0; g < n_full; ++g) {
+    };
+
+    const int n_full = len / U;
+    const int rem = len - n_full * U;
+    Tin xr[U], dr[U];
+    if (n_full > 0) load_stage(0, U, xr, dr);
+    for (int g = 0; g < n_full; ++g) {
         // issue the next stage's loads before this stage's arithmetic
         Tin xn[U], dn[U];
-        const int64_t kn = (g + 1) * U;
-        if (g + 1 < n_full) {
-#pragma unroll
-            for (int i = 0; i < U; ++i) {
-                xn[i] = xs[(kn + i) * step + d];
-                dn[i] = ds[(kn + i) * step + d];
-            }
-        }
+        if (g + 1 < n_full) load_stage((g + 1) * U, U, xn, dn);
         consume(xr, dr, g * U, U);
 #pragma unroll
         for (int i = 0; i < U; ++i) { xr[i] = xn[i]; dr[i] = dn[i]; }
     }
     if (rem > 0) {
-        const int64_t k0 = n_full * U;
-#pragma unroll
-        for (int i = 0; i < U; ++i) {
-            const int64_t k = k0 + (i < rem ? i : rem - 1);
-            xr[i] = xs[k * step + d];
-            dr[i] = ds[k * step + d];
-        }
-        consume(xr, dr, k0, rem);
+        load_stage(n_full * U, rem, xr, dr);
+        consume(xr, dr, n_full * U, rem);
     }
     if (live) {
         float4 *o = reinterpret_cast<float4 *>(hout + (((int64_t)b * n_chunks + c) * D + d) * kStates);
@@ -204,7 +248,6 @@ __global__ __launch_bounds__(kWave) void chunk_state_kernel(
     }
 }
 
-// ------------------------------------------------------------------------
 // Carry across chunks: one thread per (b, d, n), sequential over chunks.
 // Forward: h starts at h_init (or 0); for chunk c < n_agg, h_in[c] = h, then
 // h <- exp2(A' S_c) h + h_local_c.  Writes h_in[n_agg] too when requested,
@@ -267,32 +310,57 @@ __global__ __launch_bounds__(256) void carry_kernel(
 // Bidirectional block kernel: forward scan from the chunk's incoming state,
 // reverse scan restricted to each L-token block, fused output.
 //
-// Workgroup = 4 waves x 64 lanes; lane = channel, wave w = states 4w..4w+3.
-// Tokens are processed in register-resident groups of 16: the discretisation
-// (decay and injection for 16 tokens x 4 states) is computed once, kept in
-// VGPRs, and consumed by the forward pass (ascending) and then the in-block
-// reverse pass (descending).  Each wave's partial output sums over its 4
-// states go through LDS (double-buffered, one barrier per group) and each
-// wave finishes 4 of the 16 tokens.  Dskip * x is folded into wave 0's
-// partial.  Tokens past the chunk end inside the last group are neutral
-// (dt = 0 gives decay 1 and injection 0) and are not stored.
+// Workgroup = W waves x 64 lanes; lane = channel, wave w = states
+// [w*P, (w+1)*P) with P = 16 / W states per wave.  Tokens are processed in
+// groups of 16:
+//   * the group's x / dt rows (16 tokens x 64 channels) and its B / C rows
+//     (16 tokens x 16 states) arrive by buffer loads that write straight into
+//     LDS (no VGPRs, no VALU), issued one group ahead so their latency
+//     overlaps the current group's arithmetic.  Each lane's 16-bit element
+//     lands zero-extended in its own dword (the hardware writes lane i at
+//     dword i).  Buffers are double-buffered in *distinct* LDS arrays and the
+//     loop is unrolled by two, so the compiler can tell the group being read
+//     from the group being loaded and inserts no early wait;
+//   * each wave widens the B / C elements it loaded itself into fp32 LDS rows
+//     (one element per lane per piece), read later by all waves as broadcast
+//     LDS reads of their P states;
+//   * the decays of 16 tokens x P states are computed once (one exp2 per
+//     element), kept in VGPRs and used by the forward pass (ascending) and then
+//     the in-block reverse pass (descending); dt * x is kept per token and the
+//     injections are formed again in the reverse pass;
+//   * each wave's partial output sums over its P states go through LDS and
+//     each wave finishes 16 / W of the 16 tokens; Dskip * x is folded into
+//     wave 0's partial.  One barrier per group publishes the partials, the
+//     next group's x / dt rows and its widened B / C at once.
+// Tokens past the chunk end inside the last group re-read the last valid row
+// and are neutralised with dt = 0 (decay 1, injection 0); they are not stored.
 //
 // hin: incoming state of chunk c at hin[b*hin_bs + c*hin_cs + d*16 + n].
 // bounds (optional): forward state at every multiple of L, [batch,T/L+1,D,16].
 // hout (optional): forward state after token T-1 (written by the last chunk;
 // may alias hin when there is a single chunk: each thread reads its own
 // states before it writes them).
-// grid = (ceil(D/64), chunks, batch), block = 256.
-template <typename Tin, int L>
-__global__ __launch_bounds__(kWave * kWavesBidir) void bidir_kernel(
+// grid = (ceil(D/64), chunks, batch), block = 64 * W.
+template <typename Tin, int L, int W>
+__global__ __launch_bounds__(kWave * W) void bidir_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const Tin *__restrict__ Cm, const float *__restrict__ A, const float *__restrict__ Dskip,
     const float *hin, int64_t hin_bs, int64_t hin_cs,
     Tin *__restrict__ y, float *__restrict__ bounds, float *hout,
     int64_t T, int D, int64_t Tc)
 {
+    constexpr int P = kStates / W;           // states per wave
+    constexpr int Q = kGroup / W;            // tokens each wave finishes per group
+    constexpr int NPIECE = 2 * kGroup * kStates / kWave;   // 64-element pieces of B and C (8)
+    constexpr int ES = sizeof(Tin);
     static_assert(kGroup % L == 0, "block length must divide the token group");
-    __shared__ float red[2][kWavesBidir][kGroup][kWave];
+    static_assert(P * W == kStates && Q * W == kGroup && (P == 2 || P == 4), "wave split");
+    static_assert(NPIECE % W == 0, "B / C pieces per wave");
+    // double buffers, each half its own object (see above)
+    __shared__ uint32_t xdA[2][kGroup][kWave], xdB[2][kGroup][kWave];   // [x|dt][token][lane]
+    __shared__ uint32_t bcrA[NPIECE][kWave], bcrB[NPIECE][kWave];       // raw B / C pieces
+    __shared__ float bcfA[kGroup][2][kStates], bcfB[kGroup][2][kStates];  // widened B / C
+    __shared__ float redA[W][kGroup][kWave], redB[W][kGroup][kWave];    // output partials
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform(threadIdx.x >> 6);
@@ -303,113 +371,170 @@ __global__ __launch_bounds__(kWave * kWavesBidir) void bidir_kernel(
     const int b = blockIdx.z;
     const int64_t t_begin = (int64_t)c * Tc;
     const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
-    const int64_t row = (int64_t)b * T;
-    const int s0 = 4 * w;                  // first state of this wave
+    const int len = (int)(t_end - t_begin);
+    const int s0 = P * w;                    // first state of this wave
 
-    float a2[4], hf[4];
-    {
-        const float4 av = *reinterpret_cast<const float4 *>(A + (int64_t)d * kStates + s0);
-        a2[0] = av.x * kLog2e; a2[1] = av.y * kLog2e; a2[2] = av.z * kLog2e; a2[3] = av.w * kLog2e;
-        if (hin != nullptr) {
-            const float4 hv = *reinterpret_cast<const float4 *>(
-                hin + (int64_t)b * hin_bs + (int64_t)c * hin_cs + (int64_t)d * kStates + s0);
-            hf[0] = hv.x; hf[1] = hv.y; hf[2] = hv.z; hf[3] = hv.w;
-        } else {
-            hf[0] = hf[1] = hf[2] = hf[3] = 0.f;
-        }
+    float a2[P], hf[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        a2[j] = A[(int64_t)d * kStates + s0 + j] * kLog2e;
+        hf[j] = hin != nullptr ? hin[(int64_t)b * hin_bs + (int64_t)c * hin_cs + (int64_t)d * kStates + s0 + j]
+                               : 0.f;
     }
     const float dsk = Dskip[d];
     const int64_t nbl = T / L;             // number of L-blocks (T % L == 0)
-    if (bounds != nullptr && c == 0 && live) {
-        *reinterpret_cast<float4 *>(bounds + ((int64_t)b * (nbl + 1) * D + d) * kStates + s0) =
-            make_float4(hf[0], hf[1], hf[2], hf[3]);
-    }
+    auto store_state = [&](float *dst) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) dst[s0 + j] = hf[j];
+    };
+    if (bounds != nullptr && c == 0 && live)
+        store_state(bounds + ((int64_t)b * (nbl + 1) * D + d) * kStates);
+    const int64_t first = (int64_t)b * T + t_begin;
+    const Rows<Tin> xs(x + first * D, len, D, d);
+    const Rows<Tin> ds(dt + first * D, len, D, d);
+    __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(const_cast<Tin *>(Bm + first * kStates)), 0, uniform(len * kStates * (int)sizeof(Tin)),
+        kRawBufferWord3);
+    __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(const_cast<Tin *>(Cm + first * kStates)), 0, uniform(len * kStates * (int)sizeof(Tin)),
+        kRawBufferWord3);
+    // y goes out through ordinary global stores (per-lane base pointer)
+    Tin *ylane = y + first * D + d;
 
-    int buf = 0;
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += kGroup) {
-        const int nvalid = (int)((t_end - t0 < kGroup) ? (t_end - t0) : kGroup);   // uniform
-        float xv[kGroup], dl[kGroup];
+    // issue the LDS loads of group k0: rows r = w, w+W, ... of the 32 x / dt
+    // rows, and pieces p = w, w+W, ... of the 8 B / C pieces
+    auto issue = [&](auto &xd, auto &bcr, int k0) {
+        const int nv = (len - k0 < kGroup) ? len - k0 : kGroup;
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i) {
-            const int ii = i < nvalid ? i : nvalid - 1;
-            const int64_t ix = (row + t0 + ii) * D + d;
-            xv[i] = widen(x[ix]);
-            dl[i] = i < nvalid ? widen(dt[ix]) : 0.f;
+        for (int r = w; r < 2 * kGroup; r += W) {
+            const int which = r / kGroup, i = r % kGroup;
+            const int k = k0 + (i < nv ? i : nv - 1);
+            const Rows<Tin> &src = which == 0 ? xs : ds;
+            load_to_lds<ES>(src.rsrc, &xd[which][i][0], src.lane_off, k * src.pitch);
         }
-        float dA[kGroup][4], u[kGroup][4], ya[kGroup];
+#pragma unroll
+        for (int p = w; p < NPIECE; p += W) {
+            const int which = p / (NPIECE / 2);
+            const int e = (p % (NPIECE / 2)) * kWave + lane;       // element within the tensor's group rows
+            const int tok = e / kStates, n = e % kStates;
+            const int k = k0 + (tok < nv ? tok : nv - 1);
+            load_to_lds<ES>(which == 0 ? brs : crs, &bcr[p][0], (k * kStates + n) * ES, 0);
+        }
+    };
+    // widen this wave's own B / C pieces of a group into fp32 rows.  The
+    // pieces were written by this wave's own LDS loads; the compiler does not
+    // track that dependency through the loop, so wait for them explicitly
+    // (vmcnt = 0; expcnt and lgkmcnt fields left at their maxima).
+    auto widen_bc = [&](auto &bcr, auto &bcf) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+#pragma unroll
+        for (int p = w; p < NPIECE; p += W) {
+            const int which = p / (NPIECE / 2);
+            const int e = (p % (NPIECE / 2)) * kWave + lane;
+            const uint32_t v = bcr[p][lane];
+            bcf[e / kStates][which][e % kStates] =
+                sizeof(Tin) == 2 ? __uint_as_float(v << 16) : __uint_as_float(v);
+        }
+    };
+    auto elem = [&](uint32_t v) -> float {
+        return sizeof(Tin) == 2 ? __uint_as_float(v << 16) : __uint_as_float(v);
+    };
+    // Dskip * x enters wave 0's partial sums only
+    const float skip = (w == 0) ? dsk : 0.f;
+
+    // one group: xd / bcf / red hold group k0; the next group goes to the
+    // other half (xdn / bcrn / bcfn)
+    auto group = [&](auto &xd, auto &bcf, auto &red, auto &xdn, auto &bcrn, auto &bcfn, int k0) {
+        const int nvalid = (len - k0 < kGroup) ? len - k0 : kGroup;   // uniform
+        const bool more = k0 + kGroup < len;
+        if (more) issue(xdn, bcrn, k0 + kGroup);
+        float dx[kGroup], dl[kGroup], ya[kGroup];
 #pragma unroll
         for (int i = 0; i < kGroup; ++i) {
-            const int ii = i < nvalid ? i : nvalid - 1;
-            const Tin *brow = Bm + (row + t0 + ii) * kStates + s0;
-            const float dx = dl[i] * xv[i];
-            float bv[4];
-            load_pair(brow, 0, bv[0], bv[1]);
-            load_pair(brow, 1, bv[2], bv[3]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                dA[i][j] = fast_exp2(dl[i] * a2[j]);
-                u[i][j] = dx * bv[j];
+            const float xv = elem(xd[0][i][lane]);
+            const float dv = elem(xd[1][i][lane]);
+            dl[i] = i < nvalid ? dv : 0.f;
+            dx[i] = dl[i] * xv;
+            ya[i] = skip * xv;
+        }
+        auto read_bc = [&](int i, int which, float *v) {
+            if constexpr (P == 4) {
+                const float4 q = *reinterpret_cast<const float4 *>(&bcf[i][which][s0]);
+                v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+            } else {
+                const float2 q = *reinterpret_cast<const float2 *>(&bcf[i][which][s0]);
+                v[0] = q.x; v[1] = q.y;
             }
-        }
-        // forward, ascending
+        };
+        // forward, ascending: decays are kept for the reverse pass
+        float dA[kGroup][P];
 #pragma unroll
         for (int i = 0; i < kGroup; ++i) {
-            const int ii = i < nvalid ? i : nvalid - 1;
-            const Tin *crow = Cm + (row + t0 + ii) * kStates + s0;
-            float cv[4];
-            load_pair(crow, 0, cv[0], cv[1]);
-            load_pair(crow, 1, cv[2], cv[3]);
-            float acc = 0.f;
+            float bv[P], cv[P];
+            read_bc(i, 0, bv);
+            read_bc(i, 1, cv);
+            float acc = ya[i];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                hf[j] = __builtin_fmaf(dA[i][j], hf[j], u[i][j]);
+            for (int j = 0; j < P; ++j) {
+                dA[i][j] = fast_exp2(dl[i] * a2[j]);
+                hf[j] = __builtin_fmaf(dA[i][j], hf[j], dx[i] * bv[j]);
                 acc = __builtin_fmaf(cv[j], hf[j], acc);
             }
             ya[i] = acc;
+            // the empty asm statements (memory clobbers) bound how far the
+            // compiler hoists LDS reads: B / C at most four tokens ahead, and
+            // no forward value is kept live for the reverse pass
+            if ((i & 3) == 3) asm volatile("" ::: "memory");
             if ((i + 1) % L == 0 && bounds != nullptr && i < nvalid && live) {
-                const int64_t k = (t0 + i + 1) / L;
-                *reinterpret_cast<float4 *>(bounds + (((int64_t)b * (nbl + 1) + k) * D + d) * kStates + s0) =
-                    make_float4(hf[0], hf[1], hf[2], hf[3]);
+                const int64_t kb = (t_begin + k0 + i + 1) / L;
+                store_state(bounds + (((int64_t)b * (nbl + 1) + kb) * D + d) * kStates);
             }
         }
         // reverse inside each L-block, descending, from zero at the block end
-        float hr[4] = {0.f, 0.f, 0.f, 0.f};
+        asm volatile("" ::: "memory");
+        float hr[P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) hr[j] = 0.f;
 #pragma unroll
         for (int i = kGroup - 1; i >= 0; --i) {
-            const int ii = i < nvalid ? i : nvalid - 1;
-            const Tin *crow = Cm + (row + t0 + ii) * kStates + s0;
-            float cv[4];
-            load_pair(crow, 0, cv[0], cv[1]);
-            load_pair(crow, 1, cv[2], cv[3]);
-            if ((i + 1) % L == 0) { hr[0] = hr[1] = hr[2] = hr[3] = 0.f; }
+            float bv[P], cv[P];
+            read_bc(i, 0, bv);
+            read_bc(i, 1, cv);
+            if ((i + 1) % L == 0) {
+#pragma unroll
+                for (int j = 0; j < P; ++j) hr[j] = 0.f;
+            }
             float acc = ya[i];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                hr[j] = __builtin_fmaf(dA[i][j], hr[j], u[i][j]);
+            for (int j = 0; j < P; ++j) {
+                hr[j] = __builtin_fmaf(dA[i][j], hr[j], dx[i] * bv[j]);
                 acc = __builtin_fmaf(cv[j], hr[j], acc);
             }
             ya[i] = acc;
-        }
-        if (w == 0) {
-#pragma unroll
-            for (int i = 0; i < kGroup; ++i) ya[i] = __builtin_fmaf(dsk, xv[i], ya[i]);
+            if ((i & 3) == 0) asm volatile("" ::: "memory");
         }
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i) red[buf][w][i][lane] = ya[i];
+        for (int i = 0; i < kGroup; ++i) red[w][i][lane] = ya[i];
+        if (more) widen_bc(bcrn, bcfn);
         __syncthreads();
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int i = 4 * w + q;
-            const float s = red[buf][0][i][lane] + red[buf][1][i][lane] + red[buf][2][i][lane] +
-                            red[buf][3][i][lane];
-            if (live && i < nvalid) y[(row + t0 + i) * D + d] = narrow<Tin>(s);
+        for (int q = 0; q < Q; ++q) {
+            const int i = Q * w + q;
+            float sum = 0.f;
+#pragma unroll
+            for (int v = 0; v < W; ++v) sum += red[v][i][lane];
+            if (live && i < nvalid) ylane[(int64_t)(k0 + i) * D] = narrow<Tin>(sum);
         }
-        buf ^= 1;
+    };
+
+    issue(xdA, bcrA, 0);
+    widen_bc(bcrA, bcfA);
+    __syncthreads();
+    for (int k0 = 0; k0 < len; k0 += 2 * kGroup) {
+        group(xdA, bcfA, redA, xdB, bcrB, bcfB, k0);
+        if (k0 + kGroup < len) group(xdB, bcfB, redB, xdA, bcrA, bcfA, k0 + kGroup);
     }
-    if (hout != nullptr && t_end == T && live) {
-        *reinterpret_cast<float4 *>(hout + ((int64_t)b * D + d) * kStates + s0) =
-            make_float4(hf[0], hf[1], hf[2], hf[3]);
-    }
+    if (hout != nullptr && t_end == T && live) store_state(hout + ((int64_t)b * D + d) * kStates);
 }
 
 // ------------------------------------------------------------------------
@@ -435,7 +560,7 @@ __global__ __launch_bounds__(kWave) void sweep_output_kernel(
     const int b = blockIdx.z;
     const int64_t t_begin = (int64_t)c * Tc;
     const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
-    const int64_t len = t_end - t_begin;
+    const int len = (int)(t_end - t_begin);
 
     float a2[kStates], h[kStates];
     {
@@ -451,26 +576,25 @@ __global__ __launch_bounds__(kWave) void sweep_output_kernel(
         }
     }
     const float dsk = Dskip[d];
-    const int64_t step = kRev ? -(int64_t)D : (int64_t)D;
-    const int64_t t_first = kRev ? t_end - 1 : t_begin;
-    const int64_t o_first = ((int64_t)b * T + t_first) * D;
-    const Tin *xs = x + o_first;
-    const Tin *ds = dt + o_first;
-    float *yfs = yf + o_first;
-    Tin *ys = y + o_first;
-    const Tin *bs = Bm + ((int64_t)b * T + t_first) * kStates;
-    const Tin *cs = Cm + ((int64_t)b * T + t_first) * kStates;
-    const int64_t bstep = kRev ? -kStates : kStates;
+    const int64_t first = (int64_t)b * T + t_begin;
+    const Rows<Tin> xs(x + first * D, len, D, d);
+    const Rows<Tin> ds(dt + first * D, len, D, d);
+    const Rows<Tin> ys(y + first * D, len, D, d);
+    const Rows<float> fs(yf + first * D, len, D, d);
+    const Tin *bs = Bm + first * kStates;
+    const Tin *cs = Cm + first * kStates;
+    auto pos = [&](int k) -> int { return kRev ? len - 1 - k : k; };
 
-    auto consume = [&](const Tin *xr, const Tin *dr, const float *yr, int64_t k0, int count) {
+    auto consume = [&](const Tin *xr, const Tin *dr, const float *yr, int k0, int count) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             if (i < count) {
+                const int p = pos(k0 + i);
                 const float xv = widen(xr[i]);
                 const float dl = widen(dr[i]);
                 const float dx = dl * xv;
-                const Tin *brow = bs + (k0 + i) * bstep;
-                const Tin *crow = cs + (k0 + i) * bstep;
+                const Tin *brow = bs + (int64_t)p * kStates;
+                const Tin *crow = cs + (int64_t)p * kStates;
                 float acc = 0.f;
 #pragma unroll
                 for (int q = 0; q < kStates / 2; ++q) {
@@ -482,32 +606,31 @@ __global__ __launch_bounds__(kWave) void sweep_output_kernel(
                     acc = __builtin_fmaf(c0, h[2 * q], acc);
                     acc = __builtin_fmaf(c1, h[2 * q + 1], acc);
                 }
-                const int64_t o = (k0 + i) * step + d;
                 if (!kRev) {
-                    if (live) yfs[o] = acc;
+                    if (live) fs.store(p, acc);
                 } else {
                     const float tot = yr[i] + acc + dsk * xv;
-                    if (live) ys[o] = narrow<Tin>(tot);
+                    if (live) ys.store(p, narrow<Tin>(tot));
                 }
             }
         }
     };
 
-    const int64_t n_full = len / U;
-    const int rem = (int)(len - n_full * U);
+    const int n_full = len / U;
+    const int rem = len - n_full * U;
     Tin xr[U], dr[U];
     float yr[U];
-    auto load_stage = [&](int64_t k0, int count, Tin *xo, Tin *dout, float *yo) {
+    auto load_stage = [&](int k0, int count, Tin *xo, Tin *dout, float *yo) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-            const int64_t k = k0 + (i < count ? i : count - 1);
-            xo[i] = xs[k * step + d];
-            dout[i] = ds[k * step + d];
-            if (kRev) yo[i] = yfs[k * step + d];
+            const int p = pos(k0 + (i < count ? i : count - 1));
+            xo[i] = xs.load(p);
+            dout[i] = ds.load(p);
+            if (kRev) yo[i] = fs.load(p);
         }
     };
     if (n_full > 0) load_stage(0, U, xr, dr, yr);
-    for (int64_t g = 0; g < n_full; ++g) {
+    for (int g = 0; g < n_full; ++g) {
         Tin xn[U], dn[U];
         float yn[U];
         if (g + 1 < n_full) load_stage((g + 1) * U, U, xn, dn, yn);
