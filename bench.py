@@ -385,6 +385,15 @@ def train_main(args, wl, m, synth, torch):
     b.record(st)
     torch.cuda.synchronize()
     full_ms = a.elapsed_time(b) / args.steps
+    # two-stream form: the noisy stream scanned from the clean stream's bounds
+    bnd = torch.empty(batch, T // L + 1, D, NS, dtype=torch.float32, device=dev)
+    m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, h_bounds=bnd, ws=ws)
+    a.record(st)
+    for _ in range(args.steps):
+        m.train_scan_blocks(x, dt, Bm, Cm, A, Dskip, L, bnd, y=y)
+    b.record(st)
+    torch.cuda.synchronize()
+    blocks_ms = a.elapsed_time(b) / args.steps
     line = {
         "metric": "all-block training scan GB/s (forward over T + reverse per block)",
         "value": nbytes / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
@@ -397,6 +406,8 @@ def train_main(args, wl, m, synth, torch):
                        "GBs": nbytes / (ev_ms * 1e-3) / 1e9,
                        "valu_slot_frac": slots / (ev_ms * 1e-3) / VALU_SLOTS_PER_S,
                        "hbm_frac": nbytes / (ev_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "train_scan_blocks": {"ms": blocks_ms, "tokens_per_s": batch * T / (blocks_ms * 1e-3),
+                              "valu_slot_frac": slots / (blocks_ms * 1e-3) / VALU_SLOTS_PER_S},
         "full_scan": {"ms": full_ms, "tokens_per_s": batch * T / (full_ms * 1e-3),
                       "train_scan_over_full_scan_time": ev_ms / full_ms},
     }

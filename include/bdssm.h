@@ -142,6 +142,24 @@ int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const v
                      void *stream);
 
 /*
+ * Two-stream all-block training form, noisy stream [DE-M]: downstream block
+ * losses train the prefix states, so each noisy L-block k is scanned from the
+ * clean stream's forward state before block k, exactly as the sampler does at
+ * inference from its cache.  Every block k runs its forward scan from
+ * h0_blocks[:, k] and the reverse inside the block; no state crosses a block
+ * boundary.
+ *   h0_blocks [batch, T/L + 1, D, N] fp32, the layout of h_bounds from
+ *             bdssm_train_scan (entry k is the state before block k; the last
+ *             entry is not read), so the clean stream's h_bounds can be passed
+ *             as is.  Passing the same stream's own h_bounds reproduces
+ *             bdssm_train_scan's output.
+ *   y         [batch, T, D] out.  No workspace.
+ */
+int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
+                            const void *B, const void *C, const float *A, const float *Dskip,
+                            const float *h0_blocks, void *y, void *stream);
+
+/*
  * Baseline: the full-sequence bidirectional scan of the earlier diffusion
  * hybrids the pages contrast with [ABS], [DE-P], i.e. the training form with a
  * single block of length T (reverse over the whole sequence), forward from

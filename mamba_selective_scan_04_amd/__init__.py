@@ -8,6 +8,6 @@ missing, importing the binding functions raises.
 """
 from .bdssm import (  # noqa: F401
     BdssmError, load, version, status_str, workspace_bytes,
-    prefill, block_step, commit, train_scan, full_scan,
+    prefill, block_step, commit, train_scan, train_scan_blocks, full_scan,
     OP_PREFILL, OP_TRAIN, OP_FULL, F32, BF16, LIB_PATH, EXPORTS,
 )

@@ -5,6 +5,7 @@ Names and semantics follow include/bdssm.h:
   block_step(h_cache, x, dt, B, C, A, Dskip, y=None)
   commit(h_cache, x, dt, B, C, A, Dskip, want_y=False, y=None)
   train_scan(x, dt, B, C, A, Dskip, block_len, h_init=None, want_bounds=False, y=None, h_bounds=None)
+  train_scan_blocks(x, dt, B, C, A, Dskip, block_len, h0_blocks, y=None)
   full_scan(x, dt, B, C, A, Dskip, y=None)
 Shapes: x, dt, y [batch, T, D]; B, C [batch, T, 16]; A [D, 16] fp32;
 Dskip [D] fp32; states [batch, D, 16] fp32.  x/dt/B/C/y share fp32 or bf16.
@@ -23,7 +24,8 @@ F32 = 0
 BF16 = 1
 OP_PREFILL, OP_TRAIN, OP_FULL = 0, 1, 2
 EXPORTS = ("bdssm_prefill", "bdssm_block_step", "bdssm_commit", "bdssm_train_scan",
-           "bdssm_full_scan", "bdssm_workspace_bytes", "bdssm_status_str", "bdssm_version")
+           "bdssm_train_scan_blocks", "bdssm_full_scan", "bdssm_workspace_bytes",
+           "bdssm_status_str", "bdssm_version")
 
 
 class BdssmError(RuntimeError):
@@ -57,8 +59,9 @@ def load():
     lib.bdssm_commit.argtypes = [S, P, P, P, P, P, P, P, P, P]
     lib.bdssm_train_scan.argtypes = [S, I, P, P, P, P, P, P, P, P, P, P, Z, P]
     lib.bdssm_full_scan.argtypes = [S, I, P, P, P, P, P, P, P, P, Z, P]
+    lib.bdssm_train_scan_blocks.argtypes = [S, I, P, P, P, P, P, P, P, P, P]
     for f in ("bdssm_prefill", "bdssm_block_step", "bdssm_commit", "bdssm_train_scan",
-              "bdssm_full_scan", "bdssm_version"):
+              "bdssm_train_scan_blocks", "bdssm_full_scan", "bdssm_version"):
         getattr(lib, f).restype = ctypes.c_int
     lib.bdssm_workspace_bytes.argtypes = [S, I, ctypes.c_int]
     lib.bdssm_workspace_bytes.restype = ctypes.c_size_t
@@ -220,6 +223,21 @@ def train_scan(x, dt, B, C, A, Dskip, block_len, h_init=None, want_bounds=False,
                                  0 if ws is None else ws.numel(), _stream())
     _raise("bdssm_train_scan", rc)
     return y, h_bounds
+
+
+def train_scan_blocks(x, dt, B, C, A, Dskip, block_len, h0_blocks, y=None):
+    """Two-stream training form, noisy stream: every block k starts from
+    h0_blocks[:, k] ([batch, T/L + 1, D, 16], the h_bounds layout) -> y."""
+    batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip)
+    _check(h0_blocks, "h0_blocks", torch.float32, (batch, T // block_len + 1, D, N))
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", x.dtype, (batch, T, D))
+    s = _shape(batch, D, N, block_len, code)
+    rc = load().bdssm_train_scan_blocks(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A),
+                                        _p(Dskip), _p(h0_blocks), _p(y), _stream())
+    _raise("bdssm_train_scan_blocks", rc)
+    return y
 
 
 def full_scan(x, dt, B, C, A, Dskip, y=None, ws=None):

@@ -275,24 +275,31 @@ template <typename Tin, int L>
 void launch_bidir_L(const void *x, const void *dt, const void *B, const void *C, const float *A,
                     const float *Dskip, const float *hin, int64_t hin_bs, int64_t hin_cs, void *y,
                     float *bounds, float *hout, int64_t batch, int64_t T, int64_t D, int64_t Tc,
-                    int n_chunks, hipStream_t st) {
-    hipLaunchKernelGGL((bidir_kernel<Tin, L, kWavesBidir>), grid3(D, n_chunks, batch),
-                       dim3(kWave * kWavesBidir), 0, st, (const Tin *)x, (const Tin *)dt,
-                       (const Tin *)B, (const Tin *)C, A, Dskip, hin, hin_bs, hin_cs, (Tin *)y,
-                       bounds, hout, T, (int)D, Tc);
+                    int n_chunks, const float *h0_blocks, hipStream_t st) {
+    if (h0_blocks != nullptr)
+        hipLaunchKernelGGL((bidir_kernel<Tin, L, kWavesBidir, true>), grid3(D, n_chunks, batch),
+                           dim3(kWave * kWavesBidir), 0, st, (const Tin *)x, (const Tin *)dt,
+                           (const Tin *)B, (const Tin *)C, A, Dskip, hin, hin_bs, hin_cs, (Tin *)y,
+                           bounds, hout, T, (int)D, Tc, h0_blocks);
+    else
+        hipLaunchKernelGGL((bidir_kernel<Tin, L, kWavesBidir, false>), grid3(D, n_chunks, batch),
+                           dim3(kWave * kWavesBidir), 0, st, (const Tin *)x, (const Tin *)dt,
+                           (const Tin *)B, (const Tin *)C, A, Dskip, hin, hin_bs, hin_cs, (Tin *)y,
+                           bounds, hout, T, (int)D, Tc, h0_blocks);
 }
 
 template <typename Tin>
 void launch_bidir(int64_t L, const void *x, const void *dt, const void *B, const void *C,
                   const float *A, const float *Dskip, const float *hin, int64_t hin_bs,
                   int64_t hin_cs, void *y, float *bounds, float *hout, int64_t batch, int64_t T,
-                  int64_t D, int64_t Tc, int n_chunks, hipStream_t st) {
+                  int64_t D, int64_t Tc, int n_chunks, hipStream_t st,
+                  const float *h0_blocks = nullptr) {
     switch (L) {
-    case 1: launch_bidir_L<Tin, 1>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, st); break;
-    case 2: launch_bidir_L<Tin, 2>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, st); break;
-    case 4: launch_bidir_L<Tin, 4>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, st); break;
-    case 8: launch_bidir_L<Tin, 8>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, st); break;
-    default: launch_bidir_L<Tin, 16>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, st); break;
+    case 1: launch_bidir_L<Tin, 1>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, st); break;
+    case 2: launch_bidir_L<Tin, 2>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, st); break;
+    case 4: launch_bidir_L<Tin, 4>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, st); break;
+    case 8: launch_bidir_L<Tin, 8>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, st); break;
+    default: launch_bidir_L<Tin, 16>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, st); break;
     }
 }
 
@@ -533,6 +540,44 @@ int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const v
         run_bidirectional<uint16_t>(shape, T, x, dt, B, C, A, Dskip, h_init, y, h_bounds, nullptr, w, p, st);
     else
         run_bidirectional<float>(shape, T, x, dt, B, C, A, Dskip, h_init, y, h_bounds, nullptr, w, p, st);
+    return launch_status();
+}
+
+int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
+                            const void *B, const void *C, const float *A, const float *Dskip,
+                            const float *h0_blocks, void *y, void *stream) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (T < 0 || T % shape->block_len != 0) return BDSSM_ERR_SHAPE;
+    rc = check_streams(shape, T, x, dt, B, C, true, A, Dskip, true);
+    if (rc) return rc;
+    const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len;
+    if (batch == 0 || D == 0 || T == 0) return BDSSM_OK;
+    if (y == nullptr || h0_blocks == nullptr) return BDSSM_ERR_NULL;
+    if (!aligned16(y) || !aligned16(h0_blocks)) return BDSSM_ERR_ALIGN;
+    const size_t nb0 = (size_t)batch * (T / L + 1) * D * kStates * 4;
+    rc = check_alias(shape, T, x, dt, B, C, A, Dskip, nullptr,
+                     {Range{y, (size_t)batch * T * D * esize(shape)}});
+    if (rc) return rc;
+    if (overlaps({y, (size_t)batch * T * D * esize(shape)}, {h0_blocks, nb0})) return BDSSM_ERR_ALIAS;
+    // blocks are independent: chunks only add parallelism (no carry), so aim
+    // for about four rounds of resident workgroups
+    const int64_t groups = batch * ceil_div(D, kWave);
+    const int64_t ngroups16 = ceil_div(T, kGroup);
+    int64_t nc = ceil_div(4 * kCoarseGroups, groups);
+    if (nc > ngroups16) nc = ngroups16;
+    if (nc < 1) nc = 1;
+    int64_t tc = ceil_div(ngroups16, nc) * kGroup;
+    const int64_t max_tok = ((((int64_t)1 << 31) - 1) / (D * 4)) / kGroup * kGroup;
+    if (tc > max_tok) tc = max_tok;
+    nc = ceil_div(T, tc);
+    if (nc > 65535) return BDSSM_ERR_SHAPE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (shape->dtype == BDSSM_BF16)
+        launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, nullptr, 0, 0, y, nullptr, nullptr, batch, T, D, tc, (int)nc, st, h0_blocks);
+    else
+        launch_bidir<float>(L, x, dt, B, C, A, Dskip, nullptr, 0, 0, y, nullptr, nullptr, batch, T, D, tc, (int)nc, st, h0_blocks);
     return launch_status();
 }
 

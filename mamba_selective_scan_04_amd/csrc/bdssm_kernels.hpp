@@ -146,17 +146,18 @@ template <> __device__ __forceinline__ void Rows<float>::store(int k, float v) c
 //     instantiation so profiles tell the two uses apart).
 // kRev scans the chunk from its last token to its first (the reverse
 // direction of the full-sequence baseline).
-// Tokens stream through an 8-deep register pipeline: the loads of the next 8
-// tokens are issued before the arithmetic of the current 8.
+// Tokens stream through a 6-deep register pipeline: the loads of the next 6
+// tokens are issued before the arithmetic of the current 6 (6 keeps the bf16
+// kernel within 64 VGPRs, i.e. 8 waves per SIMD).
 // grid = (ceil(D/64), chunks launched, batch), block = 64.
 // hout / sout are indexed by chunk id c = c_first + blockIdx.y over n_chunks.
 template <typename Tin, bool kRev, bool kDirect>
-__global__ __launch_bounds__(kWave) void chunk_state_kernel(
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(8))) void chunk_state_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const float *__restrict__ A, const float *h0, float *hout, float *__restrict__ sout,
     int64_t T, int D, int64_t Tc, int n_chunks, int c_first)
 {
-    constexpr int U = 8;                      // tokens per pipeline stage
+    constexpr int U = 6;                      // tokens per pipeline stage
     const int lane = threadIdx.x;
     const int d_raw = blockIdx.x * kWave + lane;
     const bool live = d_raw < D;
@@ -336,18 +337,21 @@ __global__ __launch_bounds__(256) void carry_kernel(
 // and are neutralised with dt = 0 (decay 1, injection 0); they are not stored.
 //
 // hin: incoming state of chunk c at hin[b*hin_bs + c*hin_cs + d*16 + n].
+// kBlockInit (two-stream training form): instead of carrying the forward
+// state across blocks, every L-block k starts from h0_blocks[b, k, d, :]
+// ([batch, T/L+1, D, 16], the layout of bounds); hin is then unused.
 // bounds (optional): forward state at every multiple of L, [batch,T/L+1,D,16].
 // hout (optional): forward state after token T-1 (written by the last chunk;
 // may alias hin when there is a single chunk: each thread reads its own
 // states before it writes them).
 // grid = (ceil(D/64), chunks, batch), block = 64 * W.
-template <typename Tin, int L, int W>
+template <typename Tin, int L, int W, bool kBlockInit>
 __global__ __launch_bounds__(kWave * W) void bidir_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const Tin *__restrict__ Cm, const float *__restrict__ A, const float *__restrict__ Dskip,
     const float *hin, int64_t hin_bs, int64_t hin_cs,
     Tin *__restrict__ y, float *__restrict__ bounds, float *hout,
-    int64_t T, int D, int64_t Tc)
+    int64_t T, int D, int64_t Tc, const float *__restrict__ h0_blocks)
 {
     constexpr int P = kStates / W;           // states per wave
     constexpr int Q = kGroup / W;            // tokens each wave finishes per group
@@ -466,10 +470,28 @@ __global__ __launch_bounds__(kWave * W) void bidir_kernel(
                 v[0] = q.x; v[1] = q.y;
             }
         };
+        // block-start states of the blocks in this group (two-stream form)
+        float hb[kBlockInit ? kGroup / L : 1][P];
+        if constexpr (kBlockInit) {
+#pragma unroll
+            for (int q = 0; q < kGroup / L; ++q) {
+                const int i = q * L < nvalid ? q * L : 0;
+                const int64_t blk = (t_begin + k0 + i) / L;
+#pragma unroll
+                for (int j = 0; j < P; ++j)
+                    hb[q][j] = h0_blocks[(((int64_t)b * (nbl + 1) + blk) * D + d) * kStates + s0 + j];
+            }
+        }
         // forward, ascending: decays are kept for the reverse pass
         float dA[kGroup][P];
 #pragma unroll
         for (int i = 0; i < kGroup; ++i) {
+            if constexpr (kBlockInit) {
+                if (i % L == 0) {
+#pragma unroll
+                    for (int j = 0; j < P; ++j) hf[j] = hb[i / L][j];
+                }
+            }
             float bv[P], cv[P];
             read_bc(i, 0, bv);
             read_bc(i, 1, cv);

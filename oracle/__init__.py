@@ -11,6 +11,6 @@ through ctypes.  Which passage of the pages each step follows is stated in the
 C file's header.
 """
 from .oracle import (  # noqa: F401
-    build, load, scan, prefill, block_step, commit, train_scan, full_scan,
+    build, load, scan, prefill, block_step, commit, train_scan, full_scan, train_blocks,
     F32, BF16, num_threads,
 )

@@ -36,6 +36,10 @@
  * it depends on later tokens of the block [ABS], [DE-P].
  * Setting L = T reproduces the full-sequence reverse scan of the earlier
  * bidirectional hybrids the pages contrast with [ABS], [DE-P].
+ * The two-stream all-block training form [DE-M] (prefix caches built by
+ * scanning the clean prefix; downstream block losses train them) runs every
+ * noisy L-block from the clean stream's forward state before that block:
+ * oracle_train_blocks below.
  *
  * Everything is fp64; inputs (fp32 or bf16) are widened exactly per element.
  * Rows are independent, so an OpenMP loop over (b,d) is the only parallelism;
@@ -224,6 +228,70 @@ int oracle_train_scan(int64_t batch, int64_t D, int64_t N, int64_t L, int dtype,
 {
     return oracle_scan(batch, T, D, N, L, dtype, x, dt, Bm, Cm, A, Dskip, h_init,
                        y, NULL, NULL, NULL, h_bounds);
+}
+
+/* Two-stream training form, noisy stream: every L-block k runs its forward
+ * scan from h0_blocks[b, k] (layout [batch, T/L + 1, D, N], the layout of the
+ * bounds output; entry T/L is not read) and the reverse inside the block.
+ * No state crosses a block boundary.  y: [batch, T, D]. */
+int oracle_train_blocks(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int dtype,
+                        const void *x, const void *dt, const void *Bm, const void *Cm,
+                        const float *A, const float *Dskip, const double *h0_blocks, double *y)
+{
+    if (batch < 0 || T < 0 || D < 0 || N < 1 || L < 1 || T % L != 0) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    if (T > 0 && (!x || !dt || !Bm || !Cm || !A || !Dskip || !h0_blocks || !y)) return -1;
+    const int64_t nb = T / L;
+    int fail = 0;
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < D; ++d) {
+            double *h = (double *)malloc((size_t)N * sizeof(double));
+            double *r = (double *)malloc((size_t)N * sizeof(double));
+            double *fwd = (double *)malloc((size_t)L * sizeof(double));
+            if (!h || !r || !fwd) {
+                free(h); free(r); free(fwd);
+#pragma omp atomic write
+                fail = 1;
+                continue;
+            }
+            for (int64_t k = 0; k < nb; ++k) {
+                for (int64_t n = 0; n < N; ++n)
+                    h[n] = h0_blocks[((b * (nb + 1) + k) * D + d) * N + n];
+                /* forward through the block from its clean start state */
+                for (int64_t t = k * L; t < k * L + L; ++t) {
+                    const size_t ix = (size_t)((b * T + t) * D + d);
+                    const size_t ib = (size_t)((b * T + t) * N);
+                    const double dtv = ld(dt, ix, dtype);
+                    const double xv = ld(x, ix, dtype);
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        const double decay = exp(dtv * (double)A[d * N + n]);
+                        h[n] = decay * h[n] + dtv * ld(Bm, ib + n, dtype) * xv;
+                        acc += ld(Cm, ib + n, dtype) * h[n];
+                    }
+                    fwd[t - k * L] = acc;
+                }
+                /* reverse inside the block from zero */
+                for (int64_t n = 0; n < N; ++n) r[n] = 0.0;
+                for (int64_t t = k * L + L - 1; t >= k * L; --t) {
+                    const size_t ix = (size_t)((b * T + t) * D + d);
+                    const size_t ib = (size_t)((b * T + t) * N);
+                    const double dtv = ld(dt, ix, dtype);
+                    const double xv = ld(x, ix, dtype);
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        const double decay = exp(dtv * (double)A[d * N + n]);
+                        r[n] = decay * r[n] + dtv * ld(Bm, ib + n, dtype) * xv;
+                        acc += ld(Cm, ib + n, dtype) * r[n];
+                    }
+                    y[ix] = fwd[t - k * L] + acc + (double)Dskip[d] * xv;
+                }
+            }
+            free(h); free(r); free(fwd);
+        }
+    }
+    return fail ? -1 : 0;
 }
 
 /* Full-sequence bidirectional baseline: the reverse runs over the whole

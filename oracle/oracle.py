@@ -44,6 +44,8 @@ def load():
         lib.oracle_scan.restype = ctypes.c_int
         lib.oracle_version.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_train_blocks.argtypes = [I, I, I, I, I, ctypes.c_int] + [P] * 8
+        lib.oracle_train_blocks.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -140,3 +142,22 @@ def full_scan(x, dt, B, C, A, Dskip):
     """Full-sequence bidirectional baseline (reverse over the whole row) -> y."""
     T = x.shape[1]
     return scan(x, dt, B, C, A, Dskip, max(T, 1), h0=None, want_y=True)["y"]
+
+
+def train_blocks(x, dt, B, C, A, Dskip, L, h0_blocks):
+    """Two-stream training form, noisy stream: every L-block k scanned from
+    h0_blocks[:, k] ([batch, T/L + 1, D, N]) plus the in-block reverse -> y."""
+    x, dt, B, C = _c(x), _c(dt), _c(B), _c(C)
+    A = _c(A, np.float32)
+    Dskip = _c(Dskip, np.float32)
+    h0 = _c(h0_blocks, np.float64)
+    code = _dtype_code(x)
+    batch, T, D = x.shape
+    N = A.shape[1]
+    assert h0.shape == (batch, T // L + 1, D, N)
+    y = np.empty((batch, T, D), np.float64)
+    rc = load().oracle_train_blocks(batch, T, D, N, L, code, _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
+                                    _ptr(A), _ptr(Dskip), _ptr(h0), _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_train_blocks rejected its arguments (rc=%d)" % rc)
+    return y

@@ -330,3 +330,43 @@ def test_empty_sequence():
     r = oracle.scan(x, x, B, B, A, np.zeros(3, np.float32), 8, h0=h0)
     assert r["y"].shape == (1, 0, 3)
     assert np.array_equal(r["hT"], h0)
+
+
+# ---------------------------------------------------- two-stream training form
+
+def test_train_blocks_with_own_bounds_is_continuous_scan():
+    """Starting every block from the stream's own boundary states reproduces
+    the continuous forward scan, bit for bit."""
+    for kind in ("random", "long"):
+        rng = np.random.default_rng(30)
+        x, dt, B, C, A, Dskip = rand_inputs(rng, 2, 48, 3, 5, a_kind=kind)
+        h0 = rng.standard_normal((2, 3, 5))
+        for L in (1, 4, 8, 16):
+            r = oracle.scan(x, dt, B, C, A, Dskip, L, h0=h0, want_bounds=True)
+            yb = oracle.train_blocks(x, dt, B, C, A, Dskip, L, r["bounds"])
+            assert np.array_equal(yb, r["y"])
+
+
+def test_train_blocks_independent_blocks_brute_force():
+    """With arbitrary block start states every block is its own problem: the
+    materialised form of each block from its own start state."""
+    rng = np.random.default_rng(31)
+    L = 8
+    x, dt, B, C, A, Dskip = rand_inputs(rng, 2, 24, 3, 5)
+    h0b = rng.standard_normal((2, 24 // L + 1, 3, 5))
+    yb = oracle.train_blocks(x, dt, B, C, A, Dskip, L, h0b)
+    for k in range(24 // L):
+        seg = lambda a: a[:, k * L:(k + 1) * L]
+        want, _ = brute_force(seg(x), seg(dt), seg(B), seg(C), A, Dskip, L, h0b[:, k])
+        assert rel(yb[:, k * L:(k + 1) * L], want) < 1e-12
+
+
+def test_train_blocks_zero_starts_is_block_step_from_zero():
+    rng = np.random.default_rng(32)
+    L = 8
+    x, dt, B, C, A, Dskip = rand_inputs(rng, 1, 32, 3, 4)
+    yb = oracle.train_blocks(x, dt, B, C, A, Dskip, L, np.zeros((1, 32 // L + 1, 3, 4)))
+    for k in range(32 // L):
+        seg = lambda a: np.ascontiguousarray(a[:, k * L:(k + 1) * L])
+        ys = oracle.block_step(np.zeros((1, 3, 4)), seg(x), seg(dt), seg(B), seg(C), A, Dskip)
+        assert np.array_equal(yb[:, k * L:(k + 1) * L], ys)

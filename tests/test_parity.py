@@ -278,3 +278,29 @@ def test_graph_replay_matches_eager(dev):
             assert torch.equal(ys[i], ys_ref[i]), rep
         assert torch.equal(hg, h_ref), rep
         assert torch.equal(y_next, y_next_ref), rep
+
+
+# ---------------------------------------------------- two-stream training form
+
+@pytest.mark.parametrize("L,T,D,dtype", [(16, 512, 130, torch.bfloat16), (8, 200, 70, torch.float32),
+                                         (4, 36, 64, torch.float32), (1, 37, 65, torch.float32)])
+def test_train_blocks_against_oracle(dev, L, T, D, dtype):
+    """Every block from its own (seeded, synthetic) start state."""
+    from mamba_selective_scan_04_amd import synth
+    c = Case(2, T, D, dtype, sid=18, a_kind="random")
+    h0b = synth.normal((2, T // L + 1, D, N), 1000 * 18 + 7).to(dev)
+    y = m.train_scan_blocks(*c.args(), L, h0b)
+    _sync()
+    yo = oracle.train_blocks(*c.oracle_args(), L, to_np(h0b))
+    assert rel_err(to_np(y), yo) < TOL[dtype], worst(to_np(y), yo)
+
+
+def test_train_blocks_with_clean_bounds_matches_continuous(dev):
+    """Passing the stream's own boundary states (from train_scan) reproduces
+    train_scan's output: the noisy-stream form equals the clean form when the
+    noisy tokens are the clean ones."""
+    c = Case(4, 2048, 192, torch.bfloat16, sid=19, a_kind="long")
+    y, bnd = m.train_scan(*c.args(), 16, want_bounds=True)
+    yb = m.train_scan_blocks(*c.args(), 16, bnd)
+    _sync()
+    assert rel_err(to_np(yb), to_np(y)) < TOL[torch.bfloat16]

@@ -107,3 +107,20 @@ def test_baseline_full_scan_65k_sampled(dev):
                           ora(A[idx]), ora(Dskip[idx]))
     got = to_np(gather(y, ch))
     assert rel_err(got, yo) < TOL_BF16, worst(got, yo)
+
+
+def test_train_blocks_87m_sampled(dev):
+    """Two-stream form at the 87M training shape with seeded block start states."""
+    wl = synth.WORKLOADS["train_87m"]
+    batch, D, T, L, sid = wl["batch"], wl["d_inner"], wl["seq"], wl["block"], wl["sid"]
+    x, dt, Bm, Cm = synth.stream(batch, T, D, N, sid, 0, torch.bfloat16, dev)
+    A, Dskip = synth.params(D, N, sid, "default", dev)
+    h0b = synth.normal((batch, T // L + 1, D, N), 1000 * sid + 7, dev)
+    y = m.train_scan_blocks(x, dt, Bm, Cm, A, Dskip, L, h0b)
+    torch.cuda.synchronize()
+    ch = sample_channels(D, 8, 31)
+    idx = torch.as_tensor(ch, device=dev)
+    yo = oracle.train_blocks(ora(gather(x, ch)), ora(gather(dt, ch)), ora(Bm), ora(Cm), ora(A[idx]),
+                             ora(Dskip[idx]), L, to_np(h0b[:, :, idx]))
+    got = to_np(gather(y, ch))
+    assert rel_err(got, yo) < TOL_BF16, worst(got, yo)
