@@ -26,9 +26,7 @@
 #include "bdssm.h"
 #include "bdssm_kernels.hpp"
 
-#ifndef BDSSM_BIDIR_WAVES
-#define BDSSM_BIDIR_WAVES 8
-#endif
+
 
 using namespace bdssm_dev;
 
@@ -38,11 +36,9 @@ constexpr int kVersion = 10000;   // 1.0.0
 
 // 256 CUs x 4 SIMDs x 8 resident waves (the chunk kernel fits in 64 VGPRs)
 constexpr int64_t kFineWaves = 256 * 4 * 8;
-// waves per workgroup of the bidirectional kernel (16 / kWavesBidir states per wave)
-constexpr int kWavesBidir = BDSSM_BIDIR_WAVES;
-// workgroups of the bidirectional kernel resident at once (one 8-wave
-// workgroup per CU at its register use)
-constexpr int64_t kCoarseGroups = 256;
+// workgroups of the bidirectional kernel resident at once (two 4-wave
+// workgroups per CU at its register use)
+constexpr int64_t kCoarseGroups = 512;
 
 // ------------------------------------------------------------ launch policy
 //
@@ -52,7 +48,7 @@ constexpr int64_t kCoarseGroups = 256;
 //   fine chunks  (one wave per 64 channels, 16 states per lane): at most
 //                kFineWaves waves, the number resident at once (8 per SIMD),
 //                so the launch runs in a single round with no tail.
-//   coarse chunks (bidirectional pass, one 8-wave workgroup per 64
+//   coarse chunks (bidirectional pass, 4 independent waves per 64
 //                channels): count chosen by a small cost model (below) against
 //                kCoarseGroups resident workgroups; each is a whole number of
 //                fine chunks so its incoming state is a fine-chunk boundary.
@@ -276,16 +272,15 @@ void launch_bidir_L(const void *x, const void *dt, const void *B, const void *C,
                     const float *Dskip, const float *hin, int64_t hin_bs, int64_t hin_cs, void *y,
                     float *bounds, float *hout, int64_t batch, int64_t T, int64_t D, int64_t Tc,
                     int n_chunks, const float *h0_blocks, hipStream_t st) {
+    const dim3 g = grid3(D, n_chunks, batch), blk(4 * kWave);
     if (h0_blocks != nullptr)
-        hipLaunchKernelGGL((bidir_kernel<Tin, L, kWavesBidir, true>), grid3(D, n_chunks, batch),
-                           dim3(kWave * kWavesBidir), 0, st, (const Tin *)x, (const Tin *)dt,
-                           (const Tin *)B, (const Tin *)C, A, Dskip, hin, hin_bs, hin_cs, (Tin *)y,
-                           bounds, hout, T, (int)D, Tc, h0_blocks);
+        hipLaunchKernelGGL((bidir_wave_kernel<Tin, L, true>), g, blk, 0, st, (const Tin *)x,
+                           (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip, hin, hin_bs,
+                           hin_cs, (Tin *)y, bounds, hout, T, (int)D, Tc, h0_blocks);
     else
-        hipLaunchKernelGGL((bidir_kernel<Tin, L, kWavesBidir, false>), grid3(D, n_chunks, batch),
-                           dim3(kWave * kWavesBidir), 0, st, (const Tin *)x, (const Tin *)dt,
-                           (const Tin *)B, (const Tin *)C, A, Dskip, hin, hin_bs, hin_cs, (Tin *)y,
-                           bounds, hout, T, (int)D, Tc, h0_blocks);
+        hipLaunchKernelGGL((bidir_wave_kernel<Tin, L, false>), g, blk, 0, st, (const Tin *)x,
+                           (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip, hin, hin_bs,
+                           hin_cs, (Tin *)y, bounds, hout, T, (int)D, Tc, h0_blocks);
 }
 
 template <typename Tin>

@@ -308,33 +308,27 @@ __global__ __launch_bounds__(256) void carry_kernel(
 }
 
 // ------------------------------------------------------------------------
-// Bidirectional block kernel: forward scan from the chunk's incoming state,
-// reverse scan restricted to each L-token block, fused output.
+// Bidirectional kernel: forward scan from the chunk's incoming state, reverse
+// scan restricted to each L-token block, fused output.
 //
-// Workgroup = W waves x 64 lanes; lane = channel, wave w = states
-// [w*P, (w+1)*P) with P = 16 / W states per wave.  Tokens are processed in
-// groups of 16:
-//   * the group's x / dt rows (16 tokens x 64 channels) and its B / C rows
-//     (16 tokens x 16 states) arrive by buffer loads that write straight into
-//     LDS (no VGPRs, no VALU), issued one group ahead so their latency
-//     overlaps the current group's arithmetic.  Each lane's 16-bit element
-//     lands zero-extended in its own dword (the hardware writes lane i at
-//     dword i).  Buffers are double-buffered in *distinct* LDS arrays and the
-//     loop is unrolled by two, so the compiler can tell the group being read
-//     from the group being loaded and inserts no early wait;
-//   * each wave widens the B / C elements it loaded itself into fp32 LDS rows
-//     (one element per lane per piece), read later by all waves as broadcast
-//     LDS reads of their P states;
-//   * the decays of 16 tokens x P states are computed once (one exp2 per
-//     element), kept in VGPRs and used by the forward pass (ascending) and then
-//     the in-block reverse pass (descending); dt * x is kept per token and the
-//     injections are formed again in the reverse pass;
-//   * each wave's partial output sums over its P states go through LDS and
-//     each wave finishes 16 / W of the 16 tokens; Dskip * x is folded into
-//     wave 0's partial.  One barrier per group publishes the partials, the
-//     next group's x / dt rows and its widened B / C at once.
-// Tokens past the chunk end inside the last group re-read the last valid row
-// and are neutralised with dt = 0 (decay 1, injection 0); they are not stored.
+// One wave owns 16 channels completely: lane l handles channel l / 4 and
+// states 4 (l % 4) .. 4 (l % 4) + 3, so the four lanes of a DPP quad hold the
+// 16 states of one channel.  Nothing is shared between waves, so there is no
+// barrier at all:
+//   * each wave loads its own 16 channels' x / dt rows and the group's B / C
+//     rows straight into its own LDS region (lane-varying buffer offsets pack
+//     4 tokens x 16 channels, or 4 tokens x 16 states, into one 64-lane load),
+//     one group ahead, double-buffered in distinct arrays;
+//   * after waiting for its own loads it widens B / C to fp32 in LDS; lanes
+//     read x, dt and their 4 states of B / C back as LDS broadcasts;
+//   * the output sum over a channel's 16 states is a reduce-scatter inside the
+//     quad (two DPP exchange steps), after which each lane owns 4 tokens of
+//     its channel.
+// The decays of 16 tokens x 4 states stay in VGPRs between the forward pass
+// and the in-block reverse pass; dt * x is kept per token and the injections
+// are formed again in the reverse pass.  Tokens past the chunk end inside the
+// last group re-read the last valid row and are neutralised with dt = 0
+// (decay 1, injection 0); they are not stored.
 //
 // hin: incoming state of chunk c at hin[b*hin_bs + c*hin_cs + d*16 + n].
 // kBlockInit (two-stream training form): instead of carrying the forward
@@ -342,33 +336,32 @@ __global__ __launch_bounds__(256) void carry_kernel(
 // ([batch, T/L+1, D, 16], the layout of bounds); hin is then unused.
 // bounds (optional): forward state at every multiple of L, [batch,T/L+1,D,16].
 // hout (optional): forward state after token T-1 (written by the last chunk;
-// may alias hin when there is a single chunk: each thread reads its own
-// states before it writes them).
-// grid = (ceil(D/64), chunks, batch), block = 64 * W.
-template <typename Tin, int L, int W, bool kBlockInit>
-__global__ __launch_bounds__(kWave * W) void bidir_kernel(
+// may alias hin when there is a single chunk: each lane reads its own states
+// before it writes them).
+// grid = (ceil(D/64), chunks, batch), block = 256 (4 independent waves).
+template <typename Tin, int L, bool kBlockInit>
+__global__ __launch_bounds__(4 * kWave) void bidir_wave_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const Tin *__restrict__ Cm, const float *__restrict__ A, const float *__restrict__ Dskip,
     const float *hin, int64_t hin_bs, int64_t hin_cs,
     Tin *__restrict__ y, float *__restrict__ bounds, float *hout,
     int64_t T, int D, int64_t Tc, const float *__restrict__ h0_blocks)
 {
-    constexpr int P = kStates / W;           // states per wave
-    constexpr int Q = kGroup / W;            // tokens each wave finishes per group
-    constexpr int NPIECE = 2 * kGroup * kStates / kWave;   // 64-element pieces of B and C (8)
+    constexpr int P = 4;                      // states per lane
+    constexpr int CW = kWave / P;             // channels per wave (16)
     constexpr int ES = sizeof(Tin);
     static_assert(kGroup % L == 0, "block length must divide the token group");
-    static_assert(P * W == kStates && Q * W == kGroup && (P == 2 || P == 4), "wave split");
-    static_assert(NPIECE % W == 0, "B / C pieces per wave");
-    // double buffers, each half its own object (see above)
-    __shared__ uint32_t xdA[2][kGroup][kWave], xdB[2][kGroup][kWave];   // [x|dt][token][lane]
-    __shared__ uint32_t bcrA[NPIECE][kWave], bcrB[NPIECE][kWave];       // raw B / C pieces
-    __shared__ float bcfA[kGroup][2][kStates], bcfB[kGroup][2][kStates];  // widened B / C
-    __shared__ float redA[W][kGroup][kWave], redB[W][kGroup][kWave];    // output partials
+    // per wave: [x|dt][4 loads][64]  and  [B|C][4 loads][64]  and  fp32 B/C rows
+    __shared__ uint32_t xdA[4][2][4][kWave], xdB[4][2][4][kWave];
+    __shared__ uint32_t bcrA[4][2][4][kWave], bcrB[4][2][4][kWave];
+    __shared__ float bcfA[4][kGroup][2][kStates], bcfB[4][kGroup][2][kStates];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform(threadIdx.x >> 6);
-    const int d_raw = blockIdx.x * kWave + lane;
+    const int cl = lane >> 2;                 // channel within the wave
+    const int g = lane & 3;                   // state group
+    const int s0 = P * g;
+    const int d_raw = blockIdx.x * kWave + w * CW + cl;
     const bool live = d_raw < D;
     const int d = live ? d_raw : D - 1;
     const int c = blockIdx.y;
@@ -376,113 +369,98 @@ __global__ __launch_bounds__(kWave * W) void bidir_kernel(
     const int64_t t_begin = (int64_t)c * Tc;
     const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
     const int len = (int)(t_end - t_begin);
-    const int s0 = P * w;                    // first state of this wave
 
     float a2[P], hf[P];
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-        a2[j] = A[(int64_t)d * kStates + s0 + j] * kLog2e;
-        hf[j] = hin != nullptr ? hin[(int64_t)b * hin_bs + (int64_t)c * hin_cs + (int64_t)d * kStates + s0 + j]
-                               : 0.f;
+    {
+        const float4 av = *reinterpret_cast<const float4 *>(A + (int64_t)d * kStates + s0);
+        a2[0] = av.x * kLog2e; a2[1] = av.y * kLog2e; a2[2] = av.z * kLog2e; a2[3] = av.w * kLog2e;
+        if (hin != nullptr) {
+            const float4 hv = *reinterpret_cast<const float4 *>(
+                hin + (int64_t)b * hin_bs + (int64_t)c * hin_cs + (int64_t)d * kStates + s0);
+            hf[0] = hv.x; hf[1] = hv.y; hf[2] = hv.z; hf[3] = hv.w;
+        } else {
+            hf[0] = hf[1] = hf[2] = hf[3] = 0.f;
+        }
     }
     const float dsk = Dskip[d];
-    const int64_t nbl = T / L;             // number of L-blocks (T % L == 0)
+    const int64_t nbl = T / L;
     auto store_state = [&](float *dst) {
-#pragma unroll
-        for (int j = 0; j < P; ++j) dst[s0 + j] = hf[j];
+        *reinterpret_cast<float4 *>(dst + s0) = make_float4(hf[0], hf[1], hf[2], hf[3]);
     };
     if (bounds != nullptr && c == 0 && live)
         store_state(bounds + ((int64_t)b * (nbl + 1) * D + d) * kStates);
-    const int64_t first = (int64_t)b * T + t_begin;
-    const Rows<Tin> xs(x + first * D, len, D, d);
-    const Rows<Tin> ds(dt + first * D, len, D, d);
-    __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(const_cast<Tin *>(Bm + first * kStates)), 0, uniform(len * kStates * (int)sizeof(Tin)),
-        kRawBufferWord3);
-    __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(const_cast<Tin *>(Cm + first * kStates)), 0, uniform(len * kStates * (int)sizeof(Tin)),
-        kRawBufferWord3);
-    // y goes out through ordinary global stores (per-lane base pointer)
-    Tin *ylane = y + first * D + d;
 
-    // issue the LDS loads of group k0: rows r = w, w+W, ... of the 32 x / dt
-    // rows, and pieces p = w, w+W, ... of the 8 B / C pieces
+    const int64_t first = (int64_t)b * T + t_begin;
+    // the wave's 16 channels start at channel d_w0 (clamped lanes re-read D-1)
+    const int d_w0 = blockIdx.x * kWave + w * CW;
+    const Rows<Tin> xs(x + first * D, len, D, 0);
+    const Rows<Tin> ds(dt + first * D, len, D, 0);
+    __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(const_cast<Tin *>(Bm + first * kStates)), 0, uniform(len * kStates * ES), kRawBufferWord3);
+    __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(const_cast<Tin *>(Cm + first * kStates)), 0, uniform(len * kStates * ES), kRawBufferWord3);
+    // load j of a group covers tokens 4j .. 4j+3: lane l takes token 4j + l/16
+    // and channel (or state) l % 16
+    const int ld_tok = lane >> 4, ld_col = lane & 15;
+    const int ld_ch = (d_w0 + ld_col < D) ? d_w0 + ld_col : D - 1;
+
     auto issue = [&](auto &xd, auto &bcr, int k0) {
-        const int nv = (len - k0 < kGroup) ? len - k0 : kGroup;
 #pragma unroll
-        for (int r = w; r < 2 * kGroup; r += W) {
-            const int which = r / kGroup, i = r % kGroup;
-            const int k = k0 + (i < nv ? i : nv - 1);
-            const Rows<Tin> &src = which == 0 ? xs : ds;
-            load_to_lds<ES>(src.rsrc, &xd[which][i][0], src.lane_off, k * src.pitch);
-        }
-#pragma unroll
-        for (int p = w; p < NPIECE; p += W) {
-            const int which = p / (NPIECE / 2);
-            const int e = (p % (NPIECE / 2)) * kWave + lane;       // element within the tensor's group rows
-            const int tok = e / kStates, n = e % kStates;
-            const int k = k0 + (tok < nv ? tok : nv - 1);
-            load_to_lds<ES>(which == 0 ? brs : crs, &bcr[p][0], (k * kStates + n) * ES, 0);
-        }
-    };
-    // widen this wave's own B / C pieces of a group into fp32 rows.  The
-    // pieces were written by this wave's own LDS loads; the compiler does not
-    // track that dependency through the loop, so wait for them explicitly
-    // (vmcnt = 0; expcnt and lgkmcnt fields left at their maxima).
-    auto widen_bc = [&](auto &bcr, auto &bcf) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-#pragma unroll
-        for (int p = w; p < NPIECE; p += W) {
-            const int which = p / (NPIECE / 2);
-            const int e = (p % (NPIECE / 2)) * kWave + lane;
-            const uint32_t v = bcr[p][lane];
-            bcf[e / kStates][which][e % kStates] =
-                sizeof(Tin) == 2 ? __uint_as_float(v << 16) : __uint_as_float(v);
+        for (int j = 0; j < 4; ++j) {
+            int k = k0 + 4 * j + ld_tok;
+            k = k < len ? k : len - 1;
+            load_to_lds<ES>(xs.rsrc, &xd[w][0][j][0], ld_ch * ES + k * xs.pitch, 0);
+            load_to_lds<ES>(ds.rsrc, &xd[w][1][j][0], ld_ch * ES + k * ds.pitch, 0);
+            load_to_lds<ES>(brs, &bcr[w][0][j][0], (k * kStates + ld_col) * ES, 0);
+            load_to_lds<ES>(crs, &bcr[w][1][j][0], (k * kStates + ld_col) * ES, 0);
         }
     };
     auto elem = [&](uint32_t v) -> float {
-        return sizeof(Tin) == 2 ? __uint_as_float(v << 16) : __uint_as_float(v);
+        return ES == 2 ? __uint_as_float(v << 16) : __uint_as_float(v);
     };
-    // Dskip * x enters wave 0's partial sums only
-    const float skip = (w == 0) ? dsk : 0.f;
+    // wait for this wave's own LDS loads (vmcnt = 0), then widen B / C
+    auto widen_bc = [&](auto &bcr, auto &bcf) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+#pragma unroll
+        for (int which = 0; which < 2; ++which)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bcf[w][4 * j + ld_tok][which][ld_col] = elem(bcr[w][which][j][lane]);
+    };
+    // quad reduce-scatter helpers (DPP within groups of 4 lanes)
+    auto xor2 = [](float v) {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+    };
+    auto xor1 = [](float v) {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    };
+    Tin *ylane = y + first * D + d;
+    const bool hi2 = (g & 2) != 0, hi1 = (g & 1) != 0;
 
-    // one group: xd / bcf / red hold group k0; the next group goes to the
-    // other half (xdn / bcrn / bcfn)
-    auto group = [&](auto &xd, auto &bcf, auto &red, auto &xdn, auto &bcrn, auto &bcfn, int k0) {
+    auto group = [&](auto &xd, auto &bcf, auto &xdn, auto &bcrn, auto &bcfn, int k0) {
         const int nvalid = (len - k0 < kGroup) ? len - k0 : kGroup;   // uniform
         const bool more = k0 + kGroup < len;
         if (more) issue(xdn, bcrn, k0 + kGroup);
         float dx[kGroup], dl[kGroup], ya[kGroup];
 #pragma unroll
         for (int i = 0; i < kGroup; ++i) {
-            const float xv = elem(xd[0][i][lane]);
-            const float dv = elem(xd[1][i][lane]);
+            const float xv = elem(xd[w][0][i >> 2][(i & 3) * CW + cl]);
+            const float dv = elem(xd[w][1][i >> 2][(i & 3) * CW + cl]);
             dl[i] = i < nvalid ? dv : 0.f;
             dx[i] = dl[i] * xv;
-            ya[i] = skip * xv;
+            ya[i] = 0.f;
         }
-        auto read_bc = [&](int i, int which, float *v) {
-            if constexpr (P == 4) {
-                const float4 q = *reinterpret_cast<const float4 *>(&bcf[i][which][s0]);
-                v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-            } else {
-                const float2 q = *reinterpret_cast<const float2 *>(&bcf[i][which][s0]);
-                v[0] = q.x; v[1] = q.y;
-            }
-        };
-        // block-start states of the blocks in this group (two-stream form)
         float hb[kBlockInit ? kGroup / L : 1][P];
         if constexpr (kBlockInit) {
 #pragma unroll
             for (int q = 0; q < kGroup / L; ++q) {
                 const int i = q * L < nvalid ? q * L : 0;
                 const int64_t blk = (t_begin + k0 + i) / L;
-#pragma unroll
-                for (int j = 0; j < P; ++j)
-                    hb[q][j] = h0_blocks[(((int64_t)b * (nbl + 1) + blk) * D + d) * kStates + s0 + j];
+                const float4 v = *reinterpret_cast<const float4 *>(
+                    h0_blocks + (((int64_t)b * (nbl + 1) + blk) * D + d) * kStates + s0);
+                hb[q][0] = v.x; hb[q][1] = v.y; hb[q][2] = v.z; hb[q][3] = v.w;
             }
         }
-        // forward, ascending: decays are kept for the reverse pass
         float dA[kGroup][P];
 #pragma unroll
         for (int i = 0; i < kGroup; ++i) {
@@ -492,9 +470,10 @@ __global__ __launch_bounds__(kWave * W) void bidir_kernel(
                     for (int j = 0; j < P; ++j) hf[j] = hb[i / L][j];
                 }
             }
-            float bv[P], cv[P];
-            read_bc(i, 0, bv);
-            read_bc(i, 1, cv);
+            const float4 b4 = *reinterpret_cast<const float4 *>(&bcf[w][i][0][s0]);
+            const float4 c4 = *reinterpret_cast<const float4 *>(&bcf[w][i][1][s0]);
+            const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+            const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
             float acc = ya[i];
 #pragma unroll
             for (int j = 0; j < P; ++j) {
@@ -503,29 +482,21 @@ __global__ __launch_bounds__(kWave * W) void bidir_kernel(
                 acc = __builtin_fmaf(cv[j], hf[j], acc);
             }
             ya[i] = acc;
-            // the empty asm statements (memory clobbers) bound how far the
-            // compiler hoists LDS reads: B / C at most four tokens ahead, and
-            // no forward value is kept live for the reverse pass
             if ((i & 3) == 3) asm volatile("" ::: "memory");
             if ((i + 1) % L == 0 && bounds != nullptr && i < nvalid && live) {
                 const int64_t kb = (t_begin + k0 + i + 1) / L;
                 store_state(bounds + (((int64_t)b * (nbl + 1) + kb) * D + d) * kStates);
             }
         }
-        // reverse inside each L-block, descending, from zero at the block end
         asm volatile("" ::: "memory");
-        float hr[P];
-#pragma unroll
-        for (int j = 0; j < P; ++j) hr[j] = 0.f;
+        float hr[P] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = kGroup - 1; i >= 0; --i) {
-            float bv[P], cv[P];
-            read_bc(i, 0, bv);
-            read_bc(i, 1, cv);
-            if ((i + 1) % L == 0) {
-#pragma unroll
-                for (int j = 0; j < P; ++j) hr[j] = 0.f;
-            }
+            const float4 b4 = *reinterpret_cast<const float4 *>(&bcf[w][i][0][s0]);
+            const float4 c4 = *reinterpret_cast<const float4 *>(&bcf[w][i][1][s0]);
+            const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+            const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+            if ((i + 1) % L == 0) { hr[0] = hr[1] = hr[2] = hr[3] = 0.f; }
             float acc = ya[i];
 #pragma unroll
             for (int j = 0; j < P; ++j) {
@@ -535,26 +506,38 @@ __global__ __launch_bounds__(kWave * W) void bidir_kernel(
             ya[i] = acc;
             if ((i & 3) == 0) asm volatile("" ::: "memory");
         }
+        // reduce-scatter over the quad: after step 1 the lanes with g & 2
+        // hold tokens 8..15, the others 0..7; after step 2 lane g holds
+        // tokens 4g .. 4g+3 summed over the channel's 16 states
+        float r8[8];
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i) red[w][i][lane] = ya[i];
-        if (more) widen_bc(bcrn, bcfn);
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int i = Q * w + q;
-            float sum = 0.f;
-#pragma unroll
-            for (int v = 0; v < W; ++v) sum += red[v][i][lane];
-            if (live && i < nvalid) ylane[(int64_t)(k0 + i) * D] = narrow<Tin>(sum);
+        for (int k = 0; k < 8; ++k) {
+            const float keep = hi2 ? ya[k + 8] : ya[k];
+            const float send = hi2 ? ya[k] : ya[k + 8];
+            r8[k] = keep + xor2(send);
         }
+        float r4[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float keep = hi1 ? r8[k + 4] : r8[k];
+            const float send = hi1 ? r8[k] : r8[k + 4];
+            r4[k] = keep + xor1(send);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = 4 * g + q;
+            const float xv = elem(xd[w][0][g][q * CW + cl]);
+            const float tot = __builtin_fmaf(dsk, xv, r4[q]);
+            if (live && i < nvalid) ylane[(int64_t)(k0 + i) * D] = narrow<Tin>(tot);
+        }
+        if (more) widen_bc(bcrn, bcfn);
     };
 
     issue(xdA, bcrA, 0);
     widen_bc(bcrA, bcfA);
-    __syncthreads();
     for (int k0 = 0; k0 < len; k0 += 2 * kGroup) {
-        group(xdA, bcfA, redA, xdB, bcrB, bcfB, k0);
-        if (k0 + kGroup < len) group(xdB, bcfB, redB, xdA, bcrA, bcfA, k0 + kGroup);
+        group(xdA, bcfA, xdB, bcrB, bcfB, k0);
+        if (k0 + kGroup < len) group(xdB, bcfB, xdA, bcrA, bcfA, k0 + kGroup);
     }
     if (hout != nullptr && t_end == T && live) store_state(hout + ((int64_t)b * D + d) * kStates);
 }
