@@ -16,12 +16,18 @@ Printed: one JSON line on stdout (progress goes to stderr).
           or written once) / measured step time
   roofline  for the dominant kernel (the prefill's chunk-local forward scan +
           its carry), which is VALU-bound: achieved fp32 VALU issue slots per
-          second against the chip's slot rate, plus the HBM view
+          second against the chip's slot rate (256 CUs x 4 SIMDs x 16 lanes x
+          2.4 GHz; v_exp_f32 takes two slots), plus the HBM view
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same step
 Also measured outside the timed region: the full-sequence bidirectional
 baseline (reverse over the whole sequence, rescanned every denoising step).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Training workloads (train_87m, train_350m) time the all-block training scan,
+the two-stream form and the full-sequence scan instead.  --crossover sweeps the
+context length from 8K to 64K tokens and prints generation rates of the
+block-restricted and the full-sequence schemes.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--crossover]
 """
 import argparse
 import json
@@ -119,6 +125,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (scale for HBM byte counters)")
+    ap.add_argument("--crossover", action="store_true",
+                    help="sweep the context length (8K..64K, batch 8, d_inner 1536) and report "
+                         "block-restricted against full-sequence generation rates")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -131,6 +140,8 @@ def main():
     from mamba_selective_scan_04_amd import synth
 
     m.load()   # fails loudly if the HIP library is missing
+    if args.crossover:
+        return crossover_main(args, m, synth, torch)
     wl = dict(synth.WORKLOADS[args.workload])
     if "seq" in wl:
         return train_main(args, wl, m, synth, torch)
@@ -394,6 +405,15 @@ def train_main(args, wl, m, synth, torch):
     b.record(st)
     torch.cuda.synchronize()
     blocks_ms = a.elapsed_time(b) / args.steps
+    # the all-block objective's two streams: the clean stream with its block
+    # bounds, then the noisy stream scanned block by block from those bounds
+    a.record(st)
+    for _ in range(args.steps):
+        m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, h_bounds=bnd, ws=ws)
+        m.train_scan_blocks(x, dt, Bm, Cm, A, Dskip, L, bnd, y=y)
+    b.record(st)
+    torch.cuda.synchronize()
+    two_ms = a.elapsed_time(b) / args.steps
     line = {
         "metric": "all-block training scan GB/s (forward over T + reverse per block)",
         "value": nbytes / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
@@ -410,6 +430,83 @@ def train_main(args, wl, m, synth, torch):
                               "valu_slot_frac": slots / (blocks_ms * 1e-3) / VALU_SLOTS_PER_S},
         "full_scan": {"ms": full_ms, "tokens_per_s": batch * T / (full_ms * 1e-3),
                       "train_scan_over_full_scan_time": ev_ms / full_ms},
+        "two_stream": {"ms": two_ms, "over_full_scan_time": two_ms / full_ms,
+                       "note": "clean train_scan with h_bounds + noisy train_scan_blocks, "
+                               "against one full-sequence scan of the noisy stream"},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def crossover_main(args, m, synth, torch):
+    """Context-length sweep at batch 8, d_inner 1536: per context, the cost of
+    generating one 16-token block (16 denoising block steps + the commit, from
+    the cache) against the full-sequence scheme, which rescans context + block
+    in both directions at each of the 16 steps.  Also reported: the prefill,
+    and the break-even number of generated blocks after which the prefill has
+    paid for itself against rescanning (the kernel-level crossover)."""
+    batch, D, L, S, sid = 8, 1536, 16, 16, 6
+    dtype = torch.bfloat16
+    e = 2
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    st = torch.cuda.current_stream()
+    A, Dskip = synth.params(D, NS, sid, "default", dev)
+    steps_in = [synth.step_inputs(batch, L, D, NS, sid, j, dtype, dev) for j in range(S)]
+    commit_in = synth.commit_inputs(batch, L, D, NS, sid, 0, dtype, dev)
+    y_blk = torch.empty(batch, L, D, dtype=dtype, device=dev)
+
+    def time_calls(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        a.record(st)
+        for _ in range(reps):
+            fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    rows = []
+    for ctx in (8192, 16384, 32768, 65536):
+        log("[bench] crossover: ctx %d" % ctx)
+        Tf = ctx + L
+        x, dt, Bm, Cm = synth.stream(batch, Tf, D, NS, sid, 0, dtype, dev)
+        h = torch.empty(batch, D, NS, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, m.workspace_bytes(batch, D, Tf, m.OP_FULL, 1, NS, dtype)),
+                         dtype=torch.uint8, device=dev)
+        xc, dtc, Bc, Cc = x[:, :ctx], dt[:, :ctx], Bm[:, :ctx], Cm[:, :ctx]
+        xc, dtc, Bc, Cc = xc.contiguous(), dtc.contiguous(), Bc.contiguous(), Cc.contiguous()
+        pf_ms = time_calls(lambda: m.prefill(xc, dtc, Bc, Cc, A, Dskip, L, h_cache=h, ws=ws), 10)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for j in range(S):
+                m.block_step(h, *steps_in[j], A, Dskip, y=y_blk)
+            m.commit(h, *commit_in, A, Dskip)
+        blk_ms = time_calls(g.replay, 20)
+        yf = torch.empty_like(x)
+        f_ms = time_calls(lambda: m.full_scan(x, dt, Bm, Cm, A, Dskip, y=yf, ws=ws), 5)
+        full_blk_ms = S * f_ms
+        rows.append({
+            "ctx": ctx, "prefill_ms": pf_ms, "block_restricted_block_ms": blk_ms,
+            "full_sequence_block_ms": full_blk_ms,
+            "generation_tokens_per_s": batch * L / (blk_ms * 1e-3),
+            "full_sequence_generation_tokens_per_s": batch * L / (full_blk_ms * 1e-3),
+            "ratio": full_blk_ms / blk_ms,
+            "break_even_blocks": pf_ms / max(full_blk_ms - blk_ms, 1e-9),
+        })
+        del x, dt, Bm, Cm, xc, dtc, Bc, Cc, yf, ws, g
+        torch.cuda.empty_cache()
+    r8 = rows[0]
+    line = {
+        "metric": "kernel-level generation tokens/s, block-restricted vs full-sequence, by context",
+        "value": r8["generation_tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": len(rows), "warmup": 1, "ms_per_step": r8["block_restricted_block_ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "crossover sweep, contexts 8192..65536", "batch": batch,
+                   "d_inner": D, "d_state": NS, "block": L, "denoising_steps": S},
+        "rows": rows,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -41,6 +41,9 @@ WORKLOADS = {
                          steps=16, n_blocks=1, dtype="bf16"),
     "infer_65k_b8": dict(sid=4, batch=8, d_inner=1536, d_state=16, ctx=65536, block=16,
                          steps=16, n_blocks=1, dtype="bf16"),
+    # short context, where the pages report full-sequence models as faster
+    "infer_8k_b8": dict(sid=6, batch=8, d_inner=1536, d_state=16, ctx=8192, block=16,
+                        steps=16, n_blocks=1, dtype="bf16"),
     "infer_262k_b1": dict(sid=5, batch=1, d_inner=2048, d_state=16, ctx=262144, block=16,
                           steps=16, n_blocks=8, dtype="bf16"),
     "infer_262k_b4": dict(sid=5, batch=4, d_inner=2048, d_state=16, ctx=262144, block=16,

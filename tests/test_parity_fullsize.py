@@ -35,7 +35,8 @@ def ora(t):
     return synth.to_oracle(t)
 
 
-@pytest.mark.parametrize("name", ["infer_65k_b1", "infer_65k_b8", "infer_262k_b1", "infer_262k_b16"])
+@pytest.mark.parametrize("name", ["infer_8k_b8", "infer_65k_b1", "infer_65k_b8", "infer_262k_b1",
+                                  "infer_262k_b16"])
 def test_inference_workload_sampled(dev, name):
     wl = synth.WORKLOADS[name]
     batch, D, ctx, L, sid = wl["batch"], wl["d_inner"], wl["ctx"], wl["block"], wl["sid"]
