@@ -12,5 +12,5 @@ C file's header.
 """
 from .oracle import (  # noqa: F401
     build, load, scan, prefill, block_step, commit, train_scan, full_scan, train_blocks,
-    F32, BF16, num_threads,
+    scan_bwd, F32, BF16, F64, num_threads,
 )

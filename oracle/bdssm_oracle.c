@@ -41,7 +41,8 @@
  * noisy L-block from the clean stream's forward state before that block:
  * oracle_train_blocks below.
  *
- * Everything is fp64; inputs (fp32 or bf16) are widened exactly per element.
+ * Everything is fp64; stream inputs (fp32, bf16 or fp64) are widened exactly
+ * per element; A, Dskip and states are fp64 (fp32 values convert exactly).
  * Rows are independent, so an OpenMP loop over (b,d) is the only parallelism;
  * every row is a plain sequential loop over tokens with exp() from libm.
  */
@@ -56,10 +57,12 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_F64 2
 
 /* exact widening of one input element */
 static double ld(const void *p, size_t i, int dtype)
 {
+    if (dtype == ORACLE_F64) return ((const double *)p)[i];
     if (dtype == ORACLE_BF16) {
         uint32_t bits = ((uint32_t)((const uint16_t *)p)[i]) << 16;
         float f;
@@ -69,7 +72,7 @@ static double ld(const void *p, size_t i, int dtype)
     return (double)((const float *)p)[i];
 }
 
-int oracle_version(void) { return 1; }
+int oracle_version(void) { return 2; }
 
 /* Threads the OpenMP loop over rows will use (1 without OpenMP). */
 int oracle_num_threads(void)
@@ -83,7 +86,8 @@ int oracle_num_threads(void)
 
 /*
  * Core routine.  Shapes (row-major, contiguous):
- *   x, dt: [batch, T, D]     Bm, Cm: [batch, T, N]     A: [D, N]    Dskip: [D]
+ *   x, dt: [batch, T, D]     Bm, Cm: [batch, T, N]     (dtype: fp32, bf16 or fp64)
+ *   A: [D, N] fp64     Dskip: [D] fp64
  *   h0:    [batch, D, N] or NULL (zero)
  * Outputs (any may be NULL):
  *   y, yf, yr: [batch, T, D]  (yf = sum_n C*hf, yr = sum_n C*hr, y = yf+yr+Dskip*x)
@@ -95,13 +99,13 @@ int oracle_num_threads(void)
  */
 int oracle_scan(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int dtype,
                 const void *x, const void *dt, const void *Bm, const void *Cm,
-                const float *A, const float *Dskip, const double *h0,
+                const double *A, const double *Dskip, const double *h0,
                 double *y, double *yf, double *yr, double *hT, double *bounds)
 {
     const int want_y = (y != NULL) || (yf != NULL) || (yr != NULL);
     if (batch < 0 || T < 0 || D < 0 || N < 1 || L < 1) return -1;
     if (T % L != 0) return -1;
-    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) return -1;
     if (T > 0 && (x == NULL || dt == NULL || Bm == NULL)) return -1;
     if (A == NULL) return -1;
     if (want_y && T > 0 && (Cm == NULL || Dskip == NULL)) return -1;
@@ -134,7 +138,7 @@ int oracle_scan(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int d
                 const double xv = ld(x, ix, dtype);
                 double acc = 0.0;
                 for (int64_t n = 0; n < N; ++n) {
-                    const double decay = exp(dtv * (double)A[d * N + n]);
+                    const double decay = exp(dtv * A[d * N + n]);
                     const double inject = dtv * ld(Bm, ib + n, dtype) * xv;
                     h[n] = decay * h[n] + inject;
                     if (want_y) acc += ld(Cm, ib + n, dtype) * h[n];
@@ -158,14 +162,14 @@ int oracle_scan(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int d
                         const double xv = ld(x, ix, dtype);
                         double acc = 0.0;
                         for (int64_t n = 0; n < N; ++n) {
-                            const double decay = exp(dtv * (double)A[d * N + n]);
+                            const double decay = exp(dtv * A[d * N + n]);
                             const double inject = dtv * ld(Bm, ib + n, dtype) * xv;
                             r[n] = decay * r[n] + inject;
                             acc += ld(Cm, ib + n, dtype) * r[n];
                         }
                         if (yf) yf[ix] = fwd[t];
                         if (yr) yr[ix] = acc;
-                        if (y) y[ix] = fwd[t] + acc + (double)Dskip[d] * xv;
+                        if (y) y[ix] = fwd[t] + acc + Dskip[d] * xv;
                     }
                 }
             }
@@ -183,7 +187,7 @@ int oracle_scan(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int d
  * committed block), i.e. what committing the blocks one by one would emit. */
 int oracle_prefill(int64_t batch, int64_t D, int64_t N, int64_t L, int dtype, int64_t t_ctx,
                    const void *x, const void *dt, const void *Bm, const void *Cm,
-                   const float *A, const float *Dskip, const double *h_init,
+                   const double *A, const double *Dskip, const double *h_init,
                    double *h_cache, double *y)
 {
     return oracle_scan(batch, t_ctx, D, N, L, dtype, x, dt, Bm, Cm, A, Dskip, h_init,
@@ -194,7 +198,7 @@ int oracle_prefill(int64_t batch, int64_t D, int64_t N, int64_t L, int dtype, in
  * cache (not modified) plus the in-block reverse from zero; y: [batch, L, D]. */
 int oracle_block_step(int64_t batch, int64_t D, int64_t N, int64_t L, int dtype,
                       const double *h_cache, const void *x, const void *dt, const void *Bm,
-                      const void *Cm, const float *A, const float *Dskip, double *y)
+                      const void *Cm, const double *A, const double *Dskip, double *y)
 {
     if (h_cache == NULL || y == NULL) return -1;
     return oracle_scan(batch, L, D, N, L, dtype, x, dt, Bm, Cm, A, Dskip, h_cache,
@@ -206,7 +210,7 @@ int oracle_block_step(int64_t batch, int64_t D, int64_t N, int64_t L, int dtype,
  * same buffer.  y (optional) equals block_step on the same inputs. */
 int oracle_commit(int64_t batch, int64_t D, int64_t N, int64_t L, int dtype,
                   double *h_cache, const void *x, const void *dt, const void *Bm,
-                  const void *Cm, const float *A, const float *Dskip, double *y)
+                  const void *Cm, const double *A, const double *Dskip, double *y)
 {
     if (h_cache == NULL) return -1;
     const size_t ns = (size_t)(batch * D * N);
@@ -223,7 +227,7 @@ int oracle_commit(int64_t batch, int64_t D, int64_t N, int64_t L, int dtype,
  * (NULL = 0) plus the reverse segmented into L-token blocks. */
 int oracle_train_scan(int64_t batch, int64_t D, int64_t N, int64_t L, int dtype, int64_t T,
                       const void *x, const void *dt, const void *Bm, const void *Cm,
-                      const float *A, const float *Dskip, const double *h_init,
+                      const double *A, const double *Dskip, const double *h_init,
                       double *y, double *h_bounds)
 {
     return oracle_scan(batch, T, D, N, L, dtype, x, dt, Bm, Cm, A, Dskip, h_init,
@@ -236,10 +240,10 @@ int oracle_train_scan(int64_t batch, int64_t D, int64_t N, int64_t L, int dtype,
  * No state crosses a block boundary.  y: [batch, T, D]. */
 int oracle_train_blocks(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int dtype,
                         const void *x, const void *dt, const void *Bm, const void *Cm,
-                        const float *A, const float *Dskip, const double *h0_blocks, double *y)
+                        const double *A, const double *Dskip, const double *h0_blocks, double *y)
 {
     if (batch < 0 || T < 0 || D < 0 || N < 1 || L < 1 || T % L != 0) return -1;
-    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) return -1;
     if (T > 0 && (!x || !dt || !Bm || !Cm || !A || !Dskip || !h0_blocks || !y)) return -1;
     const int64_t nb = T / L;
     int fail = 0;
@@ -266,7 +270,7 @@ int oracle_train_blocks(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t 
                     const double xv = ld(x, ix, dtype);
                     double acc = 0.0;
                     for (int64_t n = 0; n < N; ++n) {
-                        const double decay = exp(dtv * (double)A[d * N + n]);
+                        const double decay = exp(dtv * A[d * N + n]);
                         h[n] = decay * h[n] + dtv * ld(Bm, ib + n, dtype) * xv;
                         acc += ld(Cm, ib + n, dtype) * h[n];
                     }
@@ -281,11 +285,11 @@ int oracle_train_blocks(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t 
                     const double xv = ld(x, ix, dtype);
                     double acc = 0.0;
                     for (int64_t n = 0; n < N; ++n) {
-                        const double decay = exp(dtv * (double)A[d * N + n]);
+                        const double decay = exp(dtv * A[d * N + n]);
                         r[n] = decay * r[n] + dtv * ld(Bm, ib + n, dtype) * xv;
                         acc += ld(Cm, ib + n, dtype) * r[n];
                     }
-                    y[ix] = fwd[t - k * L] + acc + (double)Dskip[d] * xv;
+                    y[ix] = fwd[t - k * L] + acc + Dskip[d] * xv;
                 }
             }
             free(h); free(r); free(fwd);
@@ -298,9 +302,206 @@ int oracle_train_blocks(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t 
  * sequence (one segment of length T), forward from zero. */
 int oracle_full_scan(int64_t batch, int64_t D, int64_t N, int dtype, int64_t T,
                      const void *x, const void *dt, const void *Bm, const void *Cm,
-                     const float *A, const float *Dskip, double *y)
+                     const double *A, const double *Dskip, double *y)
 {
     if (T == 0) return 0;
     return oracle_scan(batch, T, D, N, T, dtype, x, dt, Bm, Cm, A, Dskip, NULL,
                        y, NULL, NULL, NULL, NULL);
+}
+
+/* ------------------------------------------------------------------------
+ * Reverse-mode gradients of the scan (the backward pass of the training
+ * forms).  The pages say the all-block objective lets downstream block losses
+ * train the prefix scan [DE-M]; this is the derivative that does it, written
+ * out from the two recurrences above for one (b, d) row and state n, with
+ * a_t = exp(dt_t A[d,n]) and u_t = dt_t B_t[n] x_t:
+ *   hf_t = a_t hf_{t-1} + u_t          (hf_{-1} = h0, or the block's start
+ *                                       state in the two-stream form)
+ *   hr_t = a_t hr_{t+1} + u_t          (hr = 0 after each block's last token)
+ *   y_t  = sum_n C_t[n] (hf_t + hr_t) + Dskip x_t
+ * Adjoints, given dy_t = dJ/dy_t (and dbounds = dJ/dbounds if the bounds feed
+ * a later computation, as the clean stream's do in the two-stream form):
+ *   gf_t = dy_t C_t[n] + a_{t+1} gf_{t+1} (+ dbounds[(t+1)/L] at block ends)
+ *          -- right to left over the whole row (continuous form), or inside
+ *             each block only (two-stream form)
+ *   gr_t = dy_t C_t[n] + a_{t-1} gr_{t-1}
+ *          -- left to right inside each block (the reverse scan's adjoint)
+ *   du_t = gf_t + gr_t,   da_t = gf_t hf_{t-1} + gr_t hr_{t+1}
+ * and then, by the chain rule through a_t and u_t:
+ *   ddt_t    += sum_n du_t B_t[n] x_t + da_t a_t A[d,n]
+ *   dx_t     += sum_n du_t dt_t B_t[n]   + dy_t Dskip
+ *   dB_t[n]  += du_t dt_t x_t            (summed over channels d)
+ *   dC_t[n]  += dy_t (hf_t + hr_t)       (summed over channels d)
+ *   dA[d,n]  += da_t a_t dt_t            (summed over batch and tokens)
+ *   dDskip   += dy_t x_t
+ *   dh0[n]    = a_0 gf_0 (+ dbounds[0])  continuous form
+ *   dh0_blocks[k][n] = a_{kL} gf_{kL}    two-stream form (entry T/L: zero)
+ *
+ * Arguments: the forward inputs (stream dtype as in oracle_scan), exactly one
+ * of h0 (continuous form; NULL = zero start) or h0_blocks (two-stream form,
+ * [batch, T/L+1, D, N]) as selected by `blocks`, dy [batch, T, D] fp64, dbounds
+ * (continuous form only, [batch, T/L+1, D, N] fp64, or NULL).  Outputs (fp64,
+ * any may be NULL, all overwritten): dx, ddt [batch, T, D]; dB, dC
+ * [batch, T, N]; dA [D, N]; dDskip [D]; dh0 [batch, D, N] (continuous);
+ * dh0_blocks [batch, T/L+1, D, N] (two-stream).
+ * Rows run in parallel; the cross-row sums (dB, dC over channels, dA and
+ * dDskip over batch and tokens) are accumulated per thread and added in
+ * thread order afterwards.
+ */
+int oracle_scan_bwd(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int dtype,
+                    const void *x, const void *dt, const void *Bm, const void *Cm,
+                    const double *A, const double *Dskip, int blocks, const double *h0,
+                    const double *h0_blocks, const double *dy, const double *dbounds,
+                    double *dx, double *ddt, double *dB, double *dC, double *dA,
+                    double *dDskip, double *dh0, double *dh0_blocks)
+{
+    if (batch < 0 || T < 0 || D < 0 || N < 1 || L < 1 || T % L != 0) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) return -1;
+    if (!A || !Dskip) return -1;
+    if (T > 0 && (!x || !dt || !Bm || !Cm || !dy)) return -1;
+    if (blocks && (h0 || dbounds || (T > 0 && !h0_blocks))) return -1;
+    if (!blocks && (h0_blocks || dh0_blocks)) return -1;
+    const int64_t nb = T / L;
+    const size_t n_tok = (size_t)(batch * T * D), n_bc = (size_t)(batch * T * N);
+    if (dx) memset(dx, 0, n_tok * sizeof(double));
+    if (ddt) memset(ddt, 0, n_tok * sizeof(double));
+    if (dB) memset(dB, 0, n_bc * sizeof(double));
+    if (dC) memset(dC, 0, n_bc * sizeof(double));
+    if (dA) memset(dA, 0, (size_t)(D * N) * sizeof(double));
+    if (dDskip) memset(dDskip, 0, (size_t)D * sizeof(double));
+    if (dh0) memset(dh0, 0, (size_t)(batch * D * N) * sizeof(double));
+    if (dh0_blocks) memset(dh0_blocks, 0, (size_t)(batch * (nb + 1) * D * N) * sizeof(double));
+    if (batch == 0 || D == 0) return 0;
+
+    int nthr = 1;
+#ifdef _OPENMP
+    nthr = omp_get_max_threads();
+#endif
+    /* per-thread partial sums of the cross-row gradients */
+    const size_t part = 2 * n_bc + (size_t)(D * N) + (size_t)D;
+    double *parts = (double *)calloc((size_t)nthr * part, sizeof(double));
+    if (!parts) return -1;
+    int fail = 0;
+
+#pragma omp parallel num_threads(nthr)
+    {
+        int tid = 0;
+#ifdef _OPENMP
+        tid = omp_get_thread_num();
+#endif
+        double *my_dB = parts + (size_t)tid * part;
+        double *my_dC = my_dB + n_bc;
+        double *my_dA = my_dC + n_bc;
+        double *my_dD = my_dA + D * N;
+        const size_t tn = (size_t)(T > 0 ? T : 1) * (size_t)N;
+        double *a = (double *)malloc(tn * sizeof(double));      /* a_t[n]       */
+        double *hp = (double *)malloc(tn * sizeof(double));     /* hf_{t-1}[n]  */
+        double *rn = (double *)malloc(tn * sizeof(double));     /* hr_{t+1}[n]  */
+        double *gr = (double *)malloc(tn * sizeof(double));     /* gr_t[n]      */
+        double *h = (double *)malloc((size_t)N * sizeof(double));
+        double *q = (double *)malloc((size_t)N * sizeof(double));
+        if (!a || !hp || !rn || !gr || !h || !q) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(static) collapse(2)
+        for (int64_t b = 0; b < batch; ++b) {
+            for (int64_t d = 0; d < D; ++d) {
+                if (fail) continue;
+                /* forward: decays and the state before every token */
+                for (int64_t t = 0; t < T; ++t) {
+                    if (t == 0 || (blocks && t % L == 0)) {
+                        for (int64_t n = 0; n < N; ++n) {
+                            if (blocks) h[n] = h0_blocks[((b * (nb + 1) + t / L) * D + d) * N + n];
+                            else h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
+                        }
+                    }
+                    const size_t ix = (size_t)((b * T + t) * D + d);
+                    const size_t ib = (size_t)((b * T + t) * N);
+                    const double dtv = ld(dt, ix, dtype), xv = ld(x, ix, dtype);
+                    for (int64_t n = 0; n < N; ++n) {
+                        const double at = exp(dtv * A[d * N + n]);
+                        a[t * N + n] = at;
+                        hp[t * N + n] = h[n];
+                        h[n] = at * h[n] + dtv * ld(Bm, ib + n, dtype) * xv;
+                    }
+                }
+                /* in-block reverse: the state after every token (hr_{t+1}) */
+                for (int64_t k = 0; k < nb; ++k) {
+                    for (int64_t n = 0; n < N; ++n) h[n] = 0.0;
+                    for (int64_t t = k * L + L - 1; t >= k * L; --t) {
+                        const size_t ix = (size_t)((b * T + t) * D + d);
+                        const size_t ib = (size_t)((b * T + t) * N);
+                        const double dtv = ld(dt, ix, dtype), xv = ld(x, ix, dtype);
+                        for (int64_t n = 0; n < N; ++n) {
+                            rn[t * N + n] = h[n];
+                            h[n] = a[t * N + n] * h[n] + dtv * ld(Bm, ib + n, dtype) * xv;
+                        }
+                    }
+                }
+                /* adjoint of the in-block reverse, left to right in each block */
+                for (int64_t k = 0; k < nb; ++k) {
+                    for (int64_t n = 0; n < N; ++n) q[n] = 0.0;
+                    for (int64_t t = k * L; t < k * L + L; ++t) {
+                        const size_t ix = (size_t)((b * T + t) * D + d);
+                        const size_t ib = (size_t)((b * T + t) * N);
+                        for (int64_t n = 0; n < N; ++n) {
+                            const double g = dy[ix] * ld(Cm, ib + n, dtype) + q[n];
+                            gr[t * N + n] = g;
+                            q[n] = a[t * N + n] * g;
+                        }
+                    }
+                }
+                /* adjoint of the forward, right to left, and every gradient */
+                for (int64_t n = 0; n < N; ++n) q[n] = 0.0;
+                for (int64_t t = T - 1; t >= 0; --t) {
+                    const size_t ix = (size_t)((b * T + t) * D + d);
+                    const size_t ib = (size_t)((b * T + t) * N);
+                    const double dtv = ld(dt, ix, dtype), xv = ld(x, ix, dtype);
+                    const int block_end = (t + 1) % L == 0;
+                    if (blocks && block_end)
+                        for (int64_t n = 0; n < N; ++n) q[n] = 0.0;
+                    double sdt = 0.0, sx = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        const double bv = ld(Bm, ib + n, dtype), cv = ld(Cm, ib + n, dtype);
+                        double gf = dy[ix] * cv + q[n];
+                        if (!blocks && block_end && dbounds)
+                            gf += dbounds[((b * (nb + 1) + (t + 1) / L) * D + d) * N + n];
+                        const double at = a[t * N + n];
+                        const double u = dtv * bv * xv;
+                        const double du = gf + gr[t * N + n];
+                        const double da = gf * hp[t * N + n] + gr[t * N + n] * rn[t * N + n];
+                        sdt += du * bv * xv + da * at * A[d * N + n];
+                        sx += du * dtv * bv;
+                        my_dB[ib + n] += du * dtv * xv;
+                        my_dC[ib + n] += dy[ix] * ((at * hp[t * N + n] + u) + (at * rn[t * N + n] + u));
+                        my_dA[d * N + n] += da * at * dtv;
+                        q[n] = at * gf;
+                    }
+                    if (ddt) ddt[ix] = sdt;
+                    if (dx) dx[ix] = sx + dy[ix] * Dskip[d];
+                    my_dD[d] += dy[ix] * xv;
+                    if (blocks && t % L == 0 && dh0_blocks)
+                        for (int64_t n = 0; n < N; ++n)
+                            dh0_blocks[((b * (nb + 1) + t / L) * D + d) * N + n] = q[n];
+                }
+                if (!blocks && dh0)
+                    for (int64_t n = 0; n < N; ++n)
+                        dh0[(b * D + d) * N + n] =
+                            q[n] + (dbounds ? dbounds[((b * (nb + 1)) * D + d) * N + n] : 0.0);
+            }
+        }
+        free(a); free(hp); free(rn); free(gr); free(h); free(q);
+    }
+    if (!fail) {
+        for (int th = 0; th < nthr; ++th) {
+            const double *p = parts + (size_t)th * part;
+            if (dB) for (size_t i = 0; i < n_bc; ++i) dB[i] += p[i];
+            if (dC) for (size_t i = 0; i < n_bc; ++i) dC[i] += p[n_bc + i];
+            if (dA) for (int64_t i = 0; i < D * N; ++i) dA[i] += p[2 * n_bc + i];
+            if (dDskip) for (int64_t i = 0; i < D; ++i) dDskip[i] += p[2 * n_bc + D * N + i];
+        }
+    }
+    free(parts);
+    return fail ? -1 : 0;
 }

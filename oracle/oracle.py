@@ -1,8 +1,9 @@
 """ctypes marshalling for the fp64 oracle (TEST INFRASTRUCTURE ONLY).
 
-Inputs are numpy arrays: float32, or bfloat16 passed as their raw uint16 bit
-patterns (``dtype=np.uint16``).  A and Dskip are float32.  States and every
-output are float64.  Shapes follow the library: x, dt, y: [batch, T, D];
+Stream inputs (x, dt, B, C) are numpy arrays: float32, float64, or bfloat16
+passed as their raw uint16 bit patterns (``dtype=np.uint16``).  A and Dskip
+are passed to the C code as float64 (float32 values convert exactly).  States
+and every output are float64.  Shapes follow the library: x, dt, y: [batch, T, D];
 B, C: [batch, T, N]; A: [D, N]; Dskip: [D]; states: [batch, D, N].
 """
 import ctypes
@@ -13,6 +14,7 @@ import numpy as np
 
 F32 = 0
 BF16 = 1
+F64 = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "bdssm_oracle.c")
@@ -32,21 +34,28 @@ def build(force=True):
     return _LIB
 
 
+def bind(lib):
+    """Declare the C signatures on a loaded oracle library."""
+    P = ctypes.c_void_p
+    I = ctypes.c_int64
+    lib.oracle_scan.argtypes = [I, I, I, I, I, ctypes.c_int] + [P] * 12
+    lib.oracle_scan.restype = ctypes.c_int
+    lib.oracle_version.restype = ctypes.c_int
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_train_blocks.argtypes = [I, I, I, I, I, ctypes.c_int] + [P] * 8
+    lib.oracle_train_blocks.restype = ctypes.c_int
+    lib.oracle_scan_bwd.argtypes = ([I, I, I, I, I, ctypes.c_int] + [P] * 6 + [ctypes.c_int]
+                                    + [P] * 12)
+    lib.oracle_scan_bwd.restype = ctypes.c_int
+    return lib
+
+
 def load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build()
-        lib = ctypes.CDLL(_LIB)
-        P = ctypes.c_void_p
-        I = ctypes.c_int64
-        lib.oracle_scan.argtypes = [I, I, I, I, I, ctypes.c_int] + [P] * 12
-        lib.oracle_scan.restype = ctypes.c_int
-        lib.oracle_version.restype = ctypes.c_int
-        lib.oracle_num_threads.restype = ctypes.c_int
-        lib.oracle_train_blocks.argtypes = [I, I, I, I, I, ctypes.c_int] + [P] * 8
-        lib.oracle_train_blocks.restype = ctypes.c_int
-        _lib = lib
+        _lib = bind(ctypes.CDLL(_LIB))
     return _lib
 
 
@@ -64,7 +73,9 @@ def _dtype_code(a):
         return F32
     if a.dtype == np.uint16:
         return BF16
-    raise TypeError("oracle inputs must be float32 or bf16 bits (uint16), got %s" % a.dtype)
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError("oracle inputs must be float32, float64 or bf16 bits (uint16), got %s" % a.dtype)
 
 
 def _c(a, dt=None):
@@ -82,8 +93,8 @@ def scan(x, dt, B, C, A, Dskip, L, h0=None, want_y=True, want_parts=False, want_
     and 'bounds' ([batch, T/L+1, D, N]) if want_bounds."""
     x, dt, B = _c(x), _c(dt), _c(B)
     C = _c(C)
-    A = _c(A, np.float32)
-    Dskip = _c(Dskip, np.float32)
+    A = _c(A, np.float64)
+    Dskip = _c(Dskip, np.float64)
     h0 = _c(h0, np.float64)
     code = _dtype_code(x)
     for a in (dt, B) + ((C,) if C is not None else ()):
@@ -148,8 +159,8 @@ def train_blocks(x, dt, B, C, A, Dskip, L, h0_blocks):
     """Two-stream training form, noisy stream: every L-block k scanned from
     h0_blocks[:, k] ([batch, T/L + 1, D, N]) plus the in-block reverse -> y."""
     x, dt, B, C = _c(x), _c(dt), _c(B), _c(C)
-    A = _c(A, np.float32)
-    Dskip = _c(Dskip, np.float32)
+    A = _c(A, np.float64)
+    Dskip = _c(Dskip, np.float64)
     h0 = _c(h0_blocks, np.float64)
     code = _dtype_code(x)
     batch, T, D = x.shape
@@ -161,3 +172,47 @@ def train_blocks(x, dt, B, C, A, Dskip, L, h0_blocks):
     if rc != 0:
         raise ValueError("oracle_train_blocks rejected its arguments (rc=%d)" % rc)
     return y
+
+
+def scan_bwd(x, dt, B, C, A, Dskip, L, dy, h0=None, h0_blocks=None, dbounds=None):
+    """Reverse-mode gradients of the training forms.  Continuous form (the
+    gradient of train_scan): forward from h0, optional dbounds = dJ/dh_bounds
+    ([batch, T/L+1, D, N]).  Two-stream form (the gradient of train_blocks):
+    pass h0_blocks.  dy = dJ/dy [batch, T, D].  Returns a dict of float64
+    arrays: dx, ddt [batch, T, D]; dB, dC [batch, T, N]; dA [D, N];
+    dDskip [D]; and dh0 [batch, D, N] or dh0_blocks [batch, T/L+1, D, N]."""
+    x, dt, B, C = _c(x), _c(dt), _c(B), _c(C)
+    A = _c(A, np.float64)
+    Dskip = _c(Dskip, np.float64)
+    h0 = _c(h0, np.float64)
+    h0b = _c(h0_blocks, np.float64)
+    dy = _c(dy, np.float64)
+    dbounds = _c(dbounds, np.float64)
+    code = _dtype_code(x)
+    for a in (dt, B, C):
+        if a.dtype != x.dtype:
+            raise TypeError("x, dt, B, C must share one dtype")
+    batch, T, D = x.shape
+    N = A.shape[1]
+    nb = T // L
+    assert dy.shape == (batch, T, D)
+    blocks = h0b is not None
+    if blocks:
+        assert h0b.shape == (batch, nb + 1, D, N)
+    if dbounds is not None:
+        assert dbounds.shape == (batch, nb + 1, D, N)
+    out = {"dx": np.empty((batch, T, D)), "ddt": np.empty((batch, T, D)),
+           "dB": np.empty((batch, T, N)), "dC": np.empty((batch, T, N)),
+           "dA": np.empty((D, N)), "dDskip": np.empty(D)}
+    if blocks:
+        out["dh0_blocks"] = np.empty((batch, nb + 1, D, N))
+    else:
+        out["dh0"] = np.empty((batch, D, N))
+    rc = load().oracle_scan_bwd(batch, T, D, N, L, code, _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
+                                _ptr(A), _ptr(Dskip), int(blocks), _ptr(h0), _ptr(h0b), _ptr(dy),
+                                _ptr(dbounds), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dB"]),
+                                _ptr(out["dC"]), _ptr(out["dA"]), _ptr(out["dDskip"]),
+                                _ptr(out.get("dh0")), _ptr(out.get("dh0_blocks")))
+    if rc != 0:
+        raise ValueError("oracle_scan_bwd rejected its arguments (rc=%d)" % rc)
+    return out

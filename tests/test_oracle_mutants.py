@@ -2,8 +2,10 @@
 
 Each case copies the oracle's C source to a temporary directory, plants one
 mistake in that copy, builds it, points the oracle wrapper at the mutant and
-runs every pin of tests/test_oracle.py.  At least one pin must fail for every
-mutant.  Nothing here touches the real oracle library or any GPU code.
+runs every pin of tests/test_oracle.py (forward mutants) or of
+tests/test_oracle_bwd.py (mutants of the gradient routine).  At least one pin
+must fail for every mutant.  Nothing here touches the real oracle library or
+any GPU code.
 """
 import ctypes
 import inspect
@@ -15,19 +17,20 @@ import pytest
 import oracle
 from oracle import oracle as _oracle_mod
 import test_oracle as pins
+import test_oracle_bwd as bwd_pins
 
 SRC = os.path.join(os.path.dirname(_oracle_mod.__file__), "bdssm_oracle.c")
 
 MUTANTS = {
-    "drop_skip_term": ("y[ix] = fwd[t] + acc + (double)Dskip[d] * xv;", "y[ix] = fwd[t] + acc;"),
-    "decay_sign": ("const double decay = exp(dtv * (double)A[d * N + n]);\n                    const double inject",
-                   "const double decay = exp(-dtv * (double)A[d * N + n]);\n                    const double inject"),
+    "drop_skip_term": ("y[ix] = fwd[t] + acc + Dskip[d] * xv;", "y[ix] = fwd[t] + acc;"),
+    "decay_sign": ("const double decay = exp(dtv * A[d * N + n]);\n                    const double inject",
+                   "const double decay = exp(-dtv * A[d * N + n]);\n                    const double inject"),
     "reverse_exclusive": ("r[n] = decay * r[n] + inject;\n                            acc += ld(Cm, ib + n, dtype) * r[n];",
                           "acc += ld(Cm, ib + n, dtype) * r[n];\n                            r[n] = decay * r[n] + inject;"),
     "B_C_swapped": ("const double inject = dtv * ld(Bm, ib + n, dtype) * xv;\n                    h[n]",
                     "const double inject = dtv * ld(Cm, ib + n, dtype) * xv;\n                    h[n]"),
-    "A_transposed": ("const double decay = exp(dtv * (double)A[d * N + n]);\n                    const double inject",
-                     "const double decay = exp(dtv * (double)A[n * D + d]);\n                    const double inject"),
+    "A_transposed": ("const double decay = exp(dtv * A[d * N + n]);\n                    const double inject",
+                     "const double decay = exp(dtv * A[n * D + d]);\n                    const double inject"),
     "ignore_initial_state": ("h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;"),
     "reverse_not_reset": ("for (int64_t n = 0; n < N; ++n) r[n] = 0.0;\n", ""),
     "no_reverse": ("if (y) y[ix] = fwd[t] + acc +", "if (y) y[ix] = fwd[t] + 0.0 * acc +"),
@@ -40,47 +43,72 @@ MUTANTS = {
                           "const double inject = ld(Bm, ib + n, dtype) * xv;\n                    h[n]"),
 }
 
+MUTANTS_BWD = {
+    "bwd_reverse_adjoint_no_decay": ("q[n] = a[t * N + n] * g;", "q[n] = g;"),
+    "bwd_da_missing_reverse_term": ("const double da = gf * hp[t * N + n] + gr[t * N + n] * rn[t * N + n];",
+                                    "const double da = gf * hp[t * N + n];"),
+    "bwd_dbounds_ignored": ("if (!blocks && block_end && dbounds)", "if (0)"),
+    "bwd_ddt_missing_decay_term": ("sdt += du * bv * xv + da * at * A[d * N + n];",
+                                   "sdt += du * bv * xv;"),
+    "bwd_dC_forward_only": ("my_dC[ib + n] += dy[ix] * ((at * hp[t * N + n] + u) + (at * rn[t * N + n] + u));",
+                            "my_dC[ib + n] += dy[ix] * (at * hp[t * N + n] + u);"),
+    "bwd_two_stream_adjoint_crosses_blocks": ("if (blocks && block_end)\n                        for (int64_t n = 0; n < N; ++n) q[n] = 0.0;",
+                                              ""),
+    "bwd_forward_adjoint_no_decay": ("q[n] = at * gf;", "q[n] = gf;"),
+    "bwd_dx_missing_skip": ("dx[ix] = sx + dy[ix] * Dskip[d];", "dx[ix] = sx;"),
+    "bwd_dB_missing_dt": ("my_dB[ib + n] += du * dtv * xv;", "my_dB[ib + n] += du * xv;"),
+    "bwd_dA_missing_dt": ("my_dA[d * N + n] += da * at * dtv;", "my_dA[d * N + n] += da * at;"),
+}
 
-def _pin_functions():
+
+def _pin_functions(module=pins):
     out = []
-    for name, fn in inspect.getmembers(pins, inspect.isfunction):
-        if not name.startswith("test_") or name == "test_rejects_bad_arguments":
+    for name, fn in inspect.getmembers(module, inspect.isfunction):
+        if not name.startswith("test_") or name in ("test_rejects_bad_arguments",
+                                                     "test_bwd_rejects_bad_arguments"):
             continue
         params = getattr(fn, "pytestmark", [])
         cases = [()]
         for m in params:
             if m.name == "parametrize":
-                cases = [(v,) for v in m.args[1]]
+                multi = "," in m.args[0]
+                cases = [tuple(v) if multi else (v,) for v in m.args[1]]
         for c in cases:
             out.append((name, fn, c))
     return out
 
 
-@pytest.mark.parametrize("mutant", sorted(MUTANTS))
-def test_some_pin_catches_mutant(mutant, tmp_path):
-    old, new = MUTANTS[mutant]
+def _run_mutant(old, new, tmp_path, module):
     src = open(SRC).read()
-    assert src.count(old) >= 1, "mutation anchor not found: %s" % mutant
+    assert src.count(old) >= 1, "mutation anchor not found"
     mutated = src.replace(old, new, 1)
     cpath = tmp_path / "mut.c"
     cpath.write_text(mutated)
     so = tmp_path / "libmut.so"
     subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-o", str(so), str(cpath), "-lm"],
                    check=True)
-    lib = ctypes.CDLL(str(so))
-    P = ctypes.c_void_p
-    I = ctypes.c_int64
-    lib.oracle_scan.argtypes = [I, I, I, I, I, ctypes.c_int] + [P] * 12
-    lib.oracle_scan.restype = ctypes.c_int
+    lib = _oracle_mod.bind(ctypes.CDLL(str(so)))
     saved = _oracle_mod._lib
     _oracle_mod._lib = lib
     caught = []
     try:
-        for name, fn, case in _pin_functions():
+        for name, fn, case in _pin_functions(module):
             try:
                 fn(*case)
             except (AssertionError, ValueError, IndexError):
                 caught.append(name)
     finally:
         _oracle_mod._lib = saved
-    assert caught, "no pin noticed mutant %s" % mutant
+    return caught
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_some_pin_catches_mutant(mutant, tmp_path):
+    old, new = MUTANTS[mutant]
+    assert _run_mutant(old, new, tmp_path, pins), "no pin noticed mutant %s" % mutant
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS_BWD))
+def test_some_gradient_pin_catches_mutant(mutant, tmp_path):
+    old, new = MUTANTS_BWD[mutant]
+    assert _run_mutant(old, new, tmp_path, bwd_pins), "no gradient pin noticed mutant %s" % mutant
