@@ -79,7 +79,13 @@ typedef enum {
 typedef enum { BDSSM_F32 = 0, BDSSM_BF16 = 1 } bdssm_dtype;
 
 /* Which entry point a workspace is sized for. */
-typedef enum { BDSSM_OP_PREFILL = 0, BDSSM_OP_TRAIN = 1, BDSSM_OP_FULL = 2 } bdssm_op;
+typedef enum {
+    BDSSM_OP_PREFILL = 0,     /* bdssm_prefill */
+    BDSSM_OP_TRAIN = 1,       /* bdssm_train_scan */
+    BDSSM_OP_FULL = 2,        /* bdssm_full_scan */
+    BDSSM_OP_TRAIN_BWD = 3,   /* bdssm_train_scan_bwd */
+    BDSSM_OP_BLOCKS_BWD = 4   /* bdssm_train_scan_blocks_bwd */
+} bdssm_op;
 
 typedef struct {
     int64_t batch;     /* >= 0 */
@@ -158,6 +164,52 @@ int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const v
 int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
                             const void *B, const void *C, const float *A, const float *Dskip,
                             const float *h0_blocks, void *y, void *stream);
+
+/*
+ * Backward of bdssm_train_scan (reverse-mode gradients).  The all-block
+ * objective trains the prefix scan through the downstream block losses
+ * [DE-M]: the gradient runs back through the forward recurrence over the whole
+ * sequence and, via d_bounds, from later computations that read the block
+ * states (the noisy stream of the two-stream form).
+ * With a_t = exp(dt_t A), the adjoints are gf_t = dy_t C_t + a_{t+1} gf_{t+1}
+ * (+ d_bounds at block ends) over the whole sequence and gr_t = dy_t C_t +
+ * a_{t-1} gr_{t-1} inside each block; every gradient follows by the chain rule
+ * through a_t and u_t = dt_t B_t x_t.
+ *   h_bounds [batch, T/L+1, D, N] fp32, required: the block states that
+ *            bdssm_train_scan returned for the same inputs (entry 0 = h_init).
+ *   dy       [batch, T, D] stream dtype: dJ/dy.
+ *   d_bounds NULL, or [batch, T/L+1, D, N] fp32: dJ/dh_bounds (for the
+ *            two-stream form, the noisy stream's dh0_blocks).
+ * Outputs, all overwritten:
+ *   dx, ddt  [batch, T, D] stream dtype;   dB, dC [batch, T, N] stream dtype;
+ *   dA [D, N] fp32 (summed over batch and tokens);  dDskip [D] fp32;
+ *   dh_init  NULL, or [batch, D, N] fp32: dJ/dh_init.
+ *   ws       ws_bytes >= bdssm_workspace_bytes(shape, T, BDSSM_OP_TRAIN_BWD).
+ * Sums over channels (dB, dC), batch and tokens (dA, dDskip) are taken in a
+ * fixed order: results are bitwise reproducible for a given shape.
+ */
+int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
+                         const void *B, const void *C, const float *A, const float *Dskip,
+                         const float *h_bounds, const void *dy, const float *d_bounds, void *dx,
+                         void *ddt, void *dB, void *dC, float *dA, float *dDskip, float *dh_init,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward of bdssm_train_scan_blocks (the noisy stream of the two-stream
+ * form [DE-M]): every block's forward adjoint starts from zero at its end, and
+ * dh0_blocks[:, k] = dJ/dh0_blocks[:, k] is what flows back into the clean
+ * stream's block states (pass it as d_bounds to bdssm_train_scan_bwd).
+ *   h0_blocks [batch, T/L+1, D, N] fp32: the same block start states as the
+ *             forward call.
+ *   dy, dx, ddt, dB, dC, dA, dDskip as in bdssm_train_scan_bwd.
+ *   dh0_blocks NULL, or [batch, T/L+1, D, N] fp32 out (entry T/L is zero).
+ *   ws        ws_bytes >= bdssm_workspace_bytes(shape, T, BDSSM_OP_BLOCKS_BWD).
+ */
+int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
+                                const void *B, const void *C, const float *A, const float *Dskip,
+                                const float *h0_blocks, const void *dy, void *dx, void *ddt,
+                                void *dB, void *dC, float *dA, float *dDskip, float *dh0_blocks,
+                                void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Baseline: the full-sequence bidirectional scan of the earlier diffusion

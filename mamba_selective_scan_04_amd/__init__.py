@@ -9,5 +9,6 @@ missing, importing the binding functions raises.
 from .bdssm import (  # noqa: F401
     BdssmError, load, version, status_str, workspace_bytes,
     prefill, block_step, commit, train_scan, train_scan_blocks, full_scan,
-    OP_PREFILL, OP_TRAIN, OP_FULL, F32, BF16, LIB_PATH, EXPORTS,
+    train_scan_bwd, train_scan_blocks_bwd,
+    OP_PREFILL, OP_TRAIN, OP_FULL, OP_TRAIN_BWD, OP_BLOCKS_BWD, F32, BF16, LIB_PATH, EXPORTS,
 )

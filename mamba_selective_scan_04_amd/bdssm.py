@@ -7,6 +7,8 @@ Names and semantics follow include/bdssm.h:
   train_scan(x, dt, B, C, A, Dskip, block_len, h_init=None, want_bounds=False, y=None, h_bounds=None)
   train_scan_blocks(x, dt, B, C, A, Dskip, block_len, h0_blocks, y=None)
   full_scan(x, dt, B, C, A, Dskip, y=None)
+  train_scan_bwd(x, dt, B, C, A, Dskip, block_len, h_bounds, dy, d_bounds=None, want_dh_init=False)
+  train_scan_blocks_bwd(x, dt, B, C, A, Dskip, block_len, h0_blocks, dy, want_dh0_blocks=False)
 Shapes: x, dt, y [batch, T, D]; B, C [batch, T, 16]; A [D, 16] fp32;
 Dskip [D] fp32; states [batch, D, 16] fp32.  x/dt/B/C/y share fp32 or bf16.
 All tensors must be contiguous, on the current CUDA (HIP) device.  Work is
@@ -22,10 +24,11 @@ LIB_PATH = os.path.join(HERE, "libbdssm.so")
 
 F32 = 0
 BF16 = 1
-OP_PREFILL, OP_TRAIN, OP_FULL = 0, 1, 2
+OP_PREFILL, OP_TRAIN, OP_FULL, OP_TRAIN_BWD, OP_BLOCKS_BWD = 0, 1, 2, 3, 4
 EXPORTS = ("bdssm_prefill", "bdssm_block_step", "bdssm_commit", "bdssm_train_scan",
-           "bdssm_train_scan_blocks", "bdssm_full_scan", "bdssm_workspace_bytes",
-           "bdssm_status_str", "bdssm_version")
+           "bdssm_train_scan_blocks", "bdssm_full_scan", "bdssm_train_scan_bwd",
+           "bdssm_train_scan_blocks_bwd", "bdssm_workspace_bytes", "bdssm_status_str",
+           "bdssm_version")
 
 
 class BdssmError(RuntimeError):
@@ -60,8 +63,11 @@ def load():
     lib.bdssm_train_scan.argtypes = [S, I, P, P, P, P, P, P, P, P, P, P, Z, P]
     lib.bdssm_full_scan.argtypes = [S, I, P, P, P, P, P, P, P, P, Z, P]
     lib.bdssm_train_scan_blocks.argtypes = [S, I, P, P, P, P, P, P, P, P, P]
+    lib.bdssm_train_scan_bwd.argtypes = [S, I] + [P] * 17 + [Z, P]
+    lib.bdssm_train_scan_blocks_bwd.argtypes = [S, I] + [P] * 16 + [Z, P]
     for f in ("bdssm_prefill", "bdssm_block_step", "bdssm_commit", "bdssm_train_scan",
-              "bdssm_train_scan_blocks", "bdssm_full_scan", "bdssm_version"):
+              "bdssm_train_scan_blocks", "bdssm_full_scan", "bdssm_train_scan_bwd",
+              "bdssm_train_scan_blocks_bwd", "bdssm_version"):
         getattr(lib, f).restype = ctypes.c_int
     lib.bdssm_workspace_bytes.argtypes = [S, I, ctypes.c_int]
     lib.bdssm_workspace_bytes.restype = ctypes.c_size_t
@@ -253,3 +259,58 @@ def full_scan(x, dt, B, C, A, Dskip, y=None, ws=None):
                                 _p(y), _p(ws), 0 if ws is None else ws.numel(), _stream())
     _raise("bdssm_full_scan", rc)
     return y
+
+
+def _grad_outputs(x, D, N):
+    batch, T = x.shape[0], x.shape[1]
+    dev = x.device
+    return (torch.empty_like(x), torch.empty_like(x),
+            torch.empty(batch, T, N, dtype=x.dtype, device=dev),
+            torch.empty(batch, T, N, dtype=x.dtype, device=dev),
+            torch.empty(D, N, dtype=torch.float32, device=dev),
+            torch.empty(D, dtype=torch.float32, device=dev))
+
+
+def train_scan_bwd(x, dt, B, C, A, Dskip, block_len, h_bounds, dy, d_bounds=None,
+                   want_dh_init=False, ws=None):
+    """Gradients of train_scan given dy (and dJ/dh_bounds) -> dict with dx, ddt,
+    dB, dC (stream dtype), dA, dDskip (fp32) and dh_init (fp32 or None).
+    h_bounds: the block states train_scan returned for the same inputs."""
+    batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip)
+    nb = T // block_len + 1
+    _check(h_bounds, "h_bounds", torch.float32, (batch, nb, D, N))
+    _check(dy, "dy", x.dtype, (batch, T, D))
+    _check(d_bounds, "d_bounds", torch.float32, (batch, nb, D, N))
+    dx, ddt, dB, dC, dA, dDs = _grad_outputs(x, D, N)
+    dh = torch.empty(batch, D, N, dtype=torch.float32, device=x.device) if want_dh_init else None
+    s = _shape(batch, D, N, block_len, code)
+    if ws is None:
+        ws = _workspace(workspace_bytes(batch, D, T, OP_TRAIN_BWD, block_len, N, x.dtype), x.device)
+    rc = load().bdssm_train_scan_bwd(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A),
+                                     _p(Dskip), _p(h_bounds), _p(dy), _p(d_bounds), _p(dx),
+                                     _p(ddt), _p(dB), _p(dC), _p(dA), _p(dDs), _p(dh), _p(ws),
+                                     0 if ws is None else ws.numel(), _stream())
+    _raise("bdssm_train_scan_bwd", rc)
+    return {"dx": dx, "ddt": ddt, "dB": dB, "dC": dC, "dA": dA, "dDskip": dDs, "dh_init": dh}
+
+
+def train_scan_blocks_bwd(x, dt, B, C, A, Dskip, block_len, h0_blocks, dy, want_dh0_blocks=False,
+                          ws=None):
+    """Gradients of train_scan_blocks -> dict with dx, ddt, dB, dC, dA, dDskip
+    and dh0_blocks ([batch, T/L+1, D, 16] fp32, or None)."""
+    batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip)
+    nb = T // block_len + 1
+    _check(h0_blocks, "h0_blocks", torch.float32, (batch, nb, D, N))
+    _check(dy, "dy", x.dtype, (batch, T, D))
+    dx, ddt, dB, dC, dA, dDs = _grad_outputs(x, D, N)
+    dh = (torch.empty(batch, nb, D, N, dtype=torch.float32, device=x.device)
+          if want_dh0_blocks else None)
+    s = _shape(batch, D, N, block_len, code)
+    if ws is None:
+        ws = _workspace(workspace_bytes(batch, D, T, OP_BLOCKS_BWD, block_len, N, x.dtype), x.device)
+    rc = load().bdssm_train_scan_blocks_bwd(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A),
+                                            _p(Dskip), _p(h0_blocks), _p(dy), _p(dx), _p(ddt),
+                                            _p(dB), _p(dC), _p(dA), _p(dDs), _p(dh), _p(ws),
+                                            0 if ws is None else ws.numel(), _stream())
+    _raise("bdssm_train_scan_blocks_bwd", rc)
+    return {"dx": dx, "ddt": ddt, "dB": dB, "dC": dC, "dA": dA, "dDskip": dDs, "dh0_blocks": dh}

@@ -24,6 +24,7 @@
 #include <initializer_list>
 
 #include "bdssm.h"
+#include "bdssm_bwd_kernels.hpp"
 #include "bdssm_kernels.hpp"
 
 
@@ -32,13 +33,15 @@ using namespace bdssm_dev;
 
 namespace {
 
-constexpr int kVersion = 10000;   // 1.0.0
+constexpr int kVersion = 10100;   // 1.1.0
 
 // 256 CUs x 4 SIMDs x 8 resident waves (the chunk kernel fits in 64 VGPRs)
 constexpr int64_t kFineWaves = 256 * 4 * 8;
 // workgroups of the bidirectional kernel resident at once (two 4-wave
 // workgroups per CU at its register use)
 constexpr int64_t kCoarseGroups = 512;
+// issue slots of the adjoint pre-pass per token relative to the backward pass
+constexpr double kBwdPrepassWeight = 0.2;
 
 // ------------------------------------------------------------ launch policy
 //
@@ -73,7 +76,10 @@ int64_t env_int(const char *name, int64_t dflt) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-Plan make_plan(int64_t batch, int64_t D, int64_t T) {
+// prepass_weight: issue slots of the chunk pre-pass per token relative to
+// the main pass (forward aggregates vs the bidirectional pass ~0.45; adjoint
+// aggregates vs the backward pass ~0.2).
+Plan make_plan(int64_t batch, int64_t D, int64_t T, double prepass_weight = 0.45) {
     Plan p{};
     const int64_t groups = batch * ceil_div(D, kWave);
     const int64_t ngroups16 = ceil_div(T, kGroup);
@@ -106,7 +112,7 @@ Plan make_plan(int64_t batch, int64_t D, int64_t T) {
     double best = 1e30;
     for (int64_t cand = 1; cand <= 32 && cand <= nf; ++cand) {
         const double rounds = (double)ceil_div(groups * cand, coarse_groups);
-        const double est = rounds / cand + 0.45 * (double)(cand - 1) / cand * (double)groups / coarse_groups;
+        const double est = rounds / cand + prepass_weight * (double)(cand - 1) / cand * (double)groups / coarse_groups;
         if (est < best - 1e-9) { best = est; nc = cand; }
     }
     const int64_t forced_nc = env_int("BDSSM_COARSE_CHUNKS", 0);
@@ -121,6 +127,24 @@ Plan make_plan(int64_t batch, int64_t D, int64_t T) {
     return p;
 }
 
+// Chunking of the two-stream forms: blocks are independent, so chunks only
+// add parallelism (no carry); aim for about four rounds of resident
+// workgroups.  Returns false if the chunk count exceeds the grid limit.
+bool blocks_plan(int64_t batch, int64_t D, int64_t T, int64_t *tc_out, int64_t *nc_out) {
+    const int64_t groups = batch * ceil_div(D, kWave);
+    const int64_t ngroups16 = ceil_div(T, kGroup);
+    int64_t nc = ceil_div(4 * kCoarseGroups, groups);
+    if (nc > ngroups16) nc = ngroups16;
+    if (nc < 1) nc = 1;
+    int64_t tc = ceil_div(ngroups16, nc) * kGroup;
+    const int64_t max_tok = ((((int64_t)1 << 31) - 1) / (D * 4)) / kGroup * kGroup;
+    if (tc > max_tok) tc = max_tok;
+    nc = ceil_div(T, tc);
+    *tc_out = tc;
+    *nc_out = nc;
+    return nc <= 65535;
+}
+
 // Workspace layout (fp32 arrays, each 256-byte aligned):
 //   agg_h [batch, n_fine, D, 16], agg_s [batch, n_fine, D], h_in [batch, n_fine, D, 16]
 //   full scan adds ragg_h, ragg_s, hr_in (same sizes) and yf [batch, T, D].
@@ -130,6 +154,38 @@ struct Workspace {
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Backward workspace (fp32, 256-byte aligned):
+//   continuous form with several coarse chunks: agg_q [batch, n_fine, D, 16],
+//     agg_s [batch, n_fine, D], q_in [batch, n_fine, D, 16];
+//   both forms: part_bc [batch, ceil(D/64), T, 32], part_a [batch, nc, D, 16],
+//     part_d [batch, nc, D]   (nc = coarse chunks of the backward pass).
+struct BwdWorkspace {
+    float *agg_q, *agg_s, *q_in, *part_bc, *part_a, *part_d;
+    size_t bytes;
+};
+
+BwdWorkspace layout_bwd(void *base, int64_t batch, int64_t D, int64_t T, int64_t n_fine,
+                        int64_t nc, bool carry) {
+    BwdWorkspace w{};
+    size_t off = 0;
+    auto take = [&](size_t n) -> float * {
+        float *r = base ? reinterpret_cast<float *>(static_cast<char *>(base) + off) : nullptr;
+        off += align256(n);
+        return r;
+    };
+    if (carry) {
+        const size_t nh = (size_t)batch * n_fine * D * kStates * sizeof(float);
+        w.agg_q = take(nh);
+        w.agg_s = take((size_t)batch * n_fine * D * sizeof(float));
+        w.q_in = take(nh);
+    }
+    w.part_bc = take((size_t)batch * ceil_div(D, kWave) * T * 32 * sizeof(float));
+    w.part_a = take((size_t)batch * nc * D * kStates * sizeof(float));
+    w.part_d = take((size_t)batch * nc * D * sizeof(float));
+    w.bytes = off;
+    return w;
+}
 
 Workspace layout_ws(void *base, int64_t batch, int64_t D, int64_t T, const Plan &p, int op) {
     Workspace w{};
@@ -256,15 +312,15 @@ void launch_chunk_state(bool rev, const void *x, const void *dt, const void *B, 
 
 void launch_carry(bool rev, const float *agg_h, const float *agg_s, const float *A,
                   const float *h_init, float *h_in, float *h_final, int64_t batch, int64_t D,
-                  int n_chunks, int n_agg, hipStream_t st) {
+                  int n_chunks, int n_agg, hipStream_t st, int c_low = 0) {
     const int64_t total = batch * D * kStates;
     const dim3 g((unsigned)ceil_div(total, 256));
     if (rev)
         hipLaunchKernelGGL((carry_kernel<true>), g, dim3(256), 0, st, agg_h, agg_s, A, h_init, h_in,
-                           h_final, (int)batch, (int)D, n_chunks, n_agg);
+                           h_final, (int)batch, (int)D, n_chunks, n_agg, c_low);
     else
         hipLaunchKernelGGL((carry_kernel<false>), g, dim3(256), 0, st, agg_h, agg_s, A, h_init, h_in,
-                           h_final, (int)batch, (int)D, n_chunks, n_agg);
+                           h_final, (int)batch, (int)D, n_chunks, n_agg, c_low);
 }
 
 template <typename Tin, int L>
@@ -311,6 +367,57 @@ void launch_sweep(bool rev, const void *x, const void *dt, const void *B, const 
         hipLaunchKernelGGL((sweep_output_kernel<Tin, false>), g, dim3(kWave), 0, st, (const Tin *)x,
                            (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip, hin, yf,
                            (Tin *)y, T, (int)D, Tc, n_chunks);
+}
+
+template <typename Tin>
+void launch_adjoint_chunk(const void *dt, const void *dy, const void *C, const float *A,
+                          const float *dbounds, float *qout, float *sout, int64_t batch, int64_t T,
+                          int64_t D, int64_t L, int64_t Tc, int n_chunks, int c_first, int n_launch,
+                          hipStream_t st) {
+    if (n_launch <= 0) return;
+    hipLaunchKernelGGL((adjoint_chunk_kernel<Tin>), grid3(D, n_launch, batch), dim3(kWave), 0, st,
+                       (const Tin *)dt, (const Tin *)dy, (const Tin *)C, A, dbounds, qout, sout, T,
+                       (int)D, (int)L, Tc, n_chunks, c_first);
+}
+
+struct BwdArgs {
+    const void *x, *dt, *B, *C, *dy;
+    const float *A, *Dskip, *h_start, *qin, *dbounds;
+    int64_t qin_bs, qin_cs;
+    void *dx, *ddt;
+    float *part_bc, *part_a, *part_d, *dh0;
+};
+
+template <typename Tin, int L, bool kBlockInit>
+void launch_bwd_L(const BwdArgs &a, int64_t batch, int64_t T, int64_t D, int64_t Tc, int nc,
+                  hipStream_t st) {
+    hipLaunchKernelGGL((bwd_wave_kernel<Tin, L, kBlockInit>), grid3(D, nc, batch), dim3(4 * kWave), 0,
+                       st, (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
+                       (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
+                       a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0, T,
+                       (int)D, Tc);
+}
+
+template <typename Tin, bool kBlockInit>
+void launch_bwd(int64_t L, const BwdArgs &a, int64_t batch, int64_t T, int64_t D, int64_t Tc,
+                int nc, hipStream_t st) {
+    switch (L) {
+    case 1: launch_bwd_L<Tin, 1, kBlockInit>(a, batch, T, D, Tc, nc, st); break;
+    case 2: launch_bwd_L<Tin, 2, kBlockInit>(a, batch, T, D, Tc, nc, st); break;
+    case 4: launch_bwd_L<Tin, 4, kBlockInit>(a, batch, T, D, Tc, nc, st); break;
+    case 8: launch_bwd_L<Tin, 8, kBlockInit>(a, batch, T, D, Tc, nc, st); break;
+    default: launch_bwd_L<Tin, 16, kBlockInit>(a, batch, T, D, Tc, nc, st); break;
+    }
+}
+
+template <typename Tin>
+void launch_bwd_reduce(const BwdWorkspace &w, void *dB, void *dC, float *dA, float *dDskip,
+                       int64_t batch, int64_t T, int64_t D, int64_t nc, hipStream_t st) {
+    const int64_t nbc = batch * T * 32;
+    hipLaunchKernelGGL((bc_reduce_kernel<Tin>), dim3((unsigned)ceil_div(nbc, 256)), dim3(256), 0, st,
+                       w.part_bc, (Tin *)dB, (Tin *)dC, (int)batch, T, (int)ceil_div(D, kWave));
+    hipLaunchKernelGGL(param_reduce_kernel, dim3((unsigned)ceil_div(D * (kStates + 1), 256)), dim3(256),
+                       0, st, w.part_a, w.part_d, dA, dDskip, (int)D, (int)(batch * nc));
 }
 
 // Forward state only over T tokens from h_init: h_final <- state after T.
@@ -397,10 +504,20 @@ const char *bdssm_status_str(int status) {
 
 size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T, int op) {
     if (check_shape(shape) != BDSSM_OK || T < 0 || T % shape->block_len != 0) return (size_t)-1;
-    if (op != BDSSM_OP_PREFILL && op != BDSSM_OP_TRAIN && op != BDSSM_OP_FULL) return (size_t)-1;
-    if (shape->batch == 0 || shape->d_inner == 0 || T == 0) return 0;
-    const Plan p = make_plan(shape->batch, shape->d_inner, T);
-    return layout_ws(nullptr, shape->batch, shape->d_inner, T, p, op).bytes;
+    if (op < BDSSM_OP_PREFILL || op > BDSSM_OP_BLOCKS_BWD) return (size_t)-1;
+    const int64_t batch = shape->batch, D = shape->d_inner;
+    if (batch == 0 || D == 0 || T == 0) return 0;
+    if (op == BDSSM_OP_TRAIN_BWD) {
+        const Plan p = make_plan(batch, D, T, kBwdPrepassWeight);
+        return layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, p.n_coarse > 1).bytes;
+    }
+    if (op == BDSSM_OP_BLOCKS_BWD) {
+        int64_t tc, nc;
+        if (!blocks_plan(batch, D, T, &tc, &nc)) return (size_t)-1;
+        return layout_bwd(nullptr, batch, D, T, 1, nc, false).bytes;
+    }
+    const Plan p = make_plan(batch, D, T);
+    return layout_ws(nullptr, batch, D, T, p, op).bytes;
 }
 
 int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const void *dt,
@@ -555,18 +672,8 @@ int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, 
                      {Range{y, (size_t)batch * T * D * esize(shape)}});
     if (rc) return rc;
     if (overlaps({y, (size_t)batch * T * D * esize(shape)}, {h0_blocks, nb0})) return BDSSM_ERR_ALIAS;
-    // blocks are independent: chunks only add parallelism (no carry), so aim
-    // for about four rounds of resident workgroups
-    const int64_t groups = batch * ceil_div(D, kWave);
-    const int64_t ngroups16 = ceil_div(T, kGroup);
-    int64_t nc = ceil_div(4 * kCoarseGroups, groups);
-    if (nc > ngroups16) nc = ngroups16;
-    if (nc < 1) nc = 1;
-    int64_t tc = ceil_div(ngroups16, nc) * kGroup;
-    const int64_t max_tok = ((((int64_t)1 << 31) - 1) / (D * 4)) / kGroup * kGroup;
-    if (tc > max_tok) tc = max_tok;
-    nc = ceil_div(T, tc);
-    if (nc > 65535) return BDSSM_ERR_SHAPE;
+    int64_t tc, nc;
+    if (!blocks_plan(batch, D, T, &tc, &nc)) return BDSSM_ERR_SHAPE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (shape->dtype == BDSSM_BF16)
@@ -603,6 +710,170 @@ int bdssm_full_scan(const bdssm_shape *shape, int64_t T, const void *x, const vo
     (void)hipGetLastError();
     if (s1.dtype == BDSSM_BF16) run_full<uint16_t>(&s1, T, x, dt, B, C, A, Dskip, y, w, p, st);
     else run_full<float>(&s1, T, x, dt, B, C, A, Dskip, y, w, p, st);
+    return launch_status();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- backward
+
+namespace {
+
+// Argument checks shared by the two backward entry points; on success fills
+// the byte sizes used by the caller.
+int check_bwd(const bdssm_shape *shape, int64_t T, const void *x, const void *dt, const void *B,
+              const void *C, const float *A, const float *Dskip, const float *h_states,
+              const void *dy, const float *dbounds, void *dx, void *ddt, void *dB, void *dC,
+              float *dA, float *dDskip, float *dh, size_t dh_bytes) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (T < 0 || T % shape->block_len != 0) return BDSSM_ERR_SHAPE;
+    rc = check_streams(shape, T, x, dt, B, C, true, A, Dskip, true);
+    if (rc) return rc;
+    const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len;
+    if (D > 0 && (dA == nullptr || dDskip == nullptr)) return BDSSM_ERR_NULL;
+    const bool work = batch > 0 && D > 0 && T > 0;
+    if (work && (!h_states || !dy || !dx || !ddt || !dB || !dC)) return BDSSM_ERR_NULL;
+    const void *ps[] = {h_states, dy, dbounds, dx, ddt, dB, dC, dA, dDskip, dh};
+    for (const void *p : ps)
+        if (p && !aligned16(p)) return BDSSM_ERR_ALIGN;
+    const size_t e = esize(shape);
+    const size_t ntok = (size_t)batch * T * D * e, nbc = (size_t)batch * T * kStates * e;
+    const size_t nbnd = (size_t)batch * (T / L + 1) * D * kStates * 4;
+    const Range outs[] = {{dx, ntok}, {ddt, ntok}, {dB, nbc}, {dC, nbc},
+                          {dA, (size_t)D * kStates * 4}, {dDskip, (size_t)D * 4}, {dh, dh_bytes}};
+    const Range ins[] = {{x, ntok}, {dt, ntok}, {B, nbc}, {C, nbc}, {A, (size_t)D * kStates * 4},
+                         {Dskip, (size_t)D * 4}, {h_states, nbnd}, {dy, ntok}, {dbounds, nbnd}};
+    for (const Range &o : outs) {
+        for (const Range &i : ins)
+            if (overlaps(o, i)) return BDSSM_ERR_ALIAS;
+        for (const Range &o2 : outs)
+            if (&o2 != &o && overlaps(o, o2)) return BDSSM_ERR_ALIAS;
+    }
+    return BDSSM_OK;
+}
+
+// Zero the parameter gradients (and the start-state gradient) of an empty call.
+int zero_bwd(int64_t D, float *dA, float *dDskip, float *dh, int64_t dh_n, hipStream_t st) {
+    int rc = D > 0 ? copy_or_zero(nullptr, dA, D * kStates, st) : BDSSM_OK;
+    if (!rc && D > 0) rc = copy_or_zero(nullptr, dDskip, D, st);
+    if (!rc && dh && dh_n > 0) rc = copy_or_zero(nullptr, dh, dh_n, st);
+    return rc;
+}
+
+bool ws_clear(void *ws, size_t bytes, std::initializer_list<Range> others) {
+    for (const Range &o : others)
+        if (overlaps({ws, bytes}, o)) return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
+                         const void *B, const void *C, const float *A, const float *Dskip,
+                         const float *h_bounds, const void *dy, const float *d_bounds, void *dx,
+                         void *ddt, void *dB, void *dC, float *dA, float *dDskip, float *dh_init,
+                         void *ws, size_t ws_bytes, void *stream) {
+    const size_t nstate = shape ? (size_t)(shape->batch > 0 ? shape->batch : 0) *
+                                      (shape->d_inner > 0 ? shape->d_inner : 0) * kStates * 4 : 0;
+    int rc = check_bwd(shape, T, x, dt, B, C, A, Dskip, h_bounds, dy, d_bounds, dx, ddt, dB, dC, dA,
+                       dDskip, dh_init, nstate);
+    if (rc) return rc;
+    const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (batch == 0 || D == 0 || T == 0) {
+        rc = zero_bwd(D, dA, dDskip, dh_init, batch * D * kStates, st);
+        if (rc || dh_init == nullptr || d_bounds == nullptr || batch == 0 || D == 0) return rc;
+        // T == 0: the only gradient of the start state is its own bound
+        return copy_or_zero(d_bounds, dh_init, batch * D * kStates, st);
+    }
+    if (!aligned16(ws)) return BDSSM_ERR_ALIGN;
+    const Plan p = make_plan(batch, D, T, kBwdPrepassWeight);
+    const bool carry = p.n_coarse > 1;
+    const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, carry);
+    if (ws == nullptr || ws_bytes < probe.bytes) return BDSSM_ERR_WORKSPACE;
+    const size_t e = esize(shape);
+    const size_t ntok = (size_t)batch * T * D * e, nbc = (size_t)batch * T * kStates * e;
+    const size_t nbnd = (size_t)batch * (T / L + 1) * D * kStates * 4;
+    if (!ws_clear(ws, probe.bytes, {{x, ntok}, {dt, ntok}, {B, nbc}, {C, nbc}, {dy, ntok},
+                                    {h_bounds, nbnd}, {d_bounds, nbnd}, {dx, ntok}, {ddt, ntok},
+                                    {dB, nbc}, {dC, nbc}, {dA, (size_t)D * kStates * 4},
+                                    {dDskip, (size_t)D * 4}, {dh_init, nstate},
+                                    {A, (size_t)D * kStates * 4}, {Dskip, (size_t)D * 4}}))
+        return BDSSM_ERR_ALIAS;
+    const BwdWorkspace w = layout_bwd(ws, batch, D, T, p.n_fine, p.n_coarse, carry);
+    const int64_t hs = D * kStates;
+    BwdArgs a{x, dt, B, C, dy, A, Dskip, h_bounds, nullptr, d_bounds, 0, 0, dx, ddt,
+              w.part_bc, w.part_a, w.part_d, dh_init};
+    const int64_t Tc = carry ? p.fine_len * p.per_coarse : p.fine_len * p.n_fine;
+    if (carry) {
+        // adjoint aggregates of the fine chunks right of the first coarse chunk,
+        // then the adjoint entering each fine chunk from its right end
+        if (shape->dtype == BDSSM_BF16)
+            launch_adjoint_chunk<uint16_t>(dt, dy, C, A, d_bounds, w.agg_q, w.agg_s, batch, T, D, L,
+                                           p.fine_len, p.n_fine, p.per_coarse, p.n_fine - p.per_coarse, st);
+        else
+            launch_adjoint_chunk<float>(dt, dy, C, A, d_bounds, w.agg_q, w.agg_s, batch, T, D, L,
+                                        p.fine_len, p.n_fine, p.per_coarse, p.n_fine - p.per_coarse, st);
+        launch_carry(true, w.agg_q, w.agg_s, A, nullptr, w.q_in, nullptr, batch, D, p.n_fine,
+                     p.n_fine, st, p.per_coarse - 1);
+        a.qin = w.q_in + (int64_t)(p.per_coarse - 1) * hs;
+        a.qin_bs = (int64_t)p.n_fine * hs;
+        a.qin_cs = (int64_t)p.per_coarse * hs;
+    }
+    const int nc = carry ? p.n_coarse : 1;
+    if (shape->dtype == BDSSM_BF16) {
+        launch_bwd<uint16_t, false>(L, a, batch, T, D, Tc, nc, st);
+        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, nc, st);
+    } else {
+        launch_bwd<float, false>(L, a, batch, T, D, Tc, nc, st);
+        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, nc, st);
+    }
+    return launch_status();
+}
+
+int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
+                                const void *B, const void *C, const float *A, const float *Dskip,
+                                const float *h0_blocks, const void *dy, void *dx, void *ddt,
+                                void *dB, void *dC, float *dA, float *dDskip, float *dh0_blocks,
+                                void *ws, size_t ws_bytes, void *stream) {
+    size_t nbnd = 0;
+    if (shape && shape->block_len > 0 && T >= 0 && shape->batch > 0 && shape->d_inner > 0)
+        nbnd = (size_t)shape->batch * (T / shape->block_len + 1) * shape->d_inner * kStates * 4;
+    int rc = check_bwd(shape, T, x, dt, B, C, A, Dskip, h0_blocks, dy, nullptr, dx, ddt, dB, dC, dA,
+                       dDskip, dh0_blocks, nbnd);
+    if (rc) return rc;
+    const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (batch == 0 || D == 0 || T == 0)
+        return zero_bwd(D, dA, dDskip, dh0_blocks, batch * D * kStates, st);
+    if (!aligned16(ws)) return BDSSM_ERR_ALIGN;
+    int64_t tc, nc;
+    if (!blocks_plan(batch, D, T, &tc, &nc)) return BDSSM_ERR_SHAPE;
+    const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, 1, nc, false);
+    if (ws == nullptr || ws_bytes < probe.bytes) return BDSSM_ERR_WORKSPACE;
+    const size_t e = esize(shape);
+    const size_t ntok = (size_t)batch * T * D * e, nbc = (size_t)batch * T * kStates * e;
+    if (!ws_clear(ws, probe.bytes, {{x, ntok}, {dt, ntok}, {B, nbc}, {C, nbc}, {dy, ntok},
+                                    {h0_blocks, nbnd}, {dx, ntok}, {ddt, ntok}, {dB, nbc},
+                                    {dC, nbc}, {dA, (size_t)D * kStates * 4},
+                                    {dDskip, (size_t)D * 4}, {dh0_blocks, nbnd},
+                                    {A, (size_t)D * kStates * 4}, {Dskip, (size_t)D * 4}}))
+        return BDSSM_ERR_ALIAS;
+    const BwdWorkspace w = layout_bwd(ws, batch, D, T, 1, nc, false);
+    const BwdArgs a{x, dt, B, C, dy, A, Dskip, h0_blocks, nullptr, nullptr, 0, 0, dx, ddt,
+                    w.part_bc, w.part_a, w.part_d, dh0_blocks};
+    if (shape->dtype == BDSSM_BF16) {
+        launch_bwd<uint16_t, true>(L, a, batch, T, D, tc, (int)nc, st);
+        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, nc, st);
+    } else {
+        launch_bwd<float, true>(L, a, batch, T, D, tc, (int)nc, st);
+        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, nc, st);
+    }
     return launch_status();
 }
 

@@ -93,6 +93,10 @@ template <typename T> __device__ __forceinline__ T *uniform_ptr(T *p) {
 // register, so streaming a row costs no VALU address arithmetic.  The launch
 // plan keeps every chunk below 2^31 bytes per stream.
 constexpr int32_t kRawBufferWord3 = 0x00020000;   // gfx9-family raw buffer descriptor
+// A byte offset (0xFFFFFF00 as the unsigned 32-bit buffer offset) past any
+// buffer range the launch plan creates (every range is below 2^31 bytes): a
+// buffer load there is out of range and returns zero.
+constexpr int32_t kOutOfRange = (int32_t)0xFFFFFF00u;
 
 // One row of 64 elements from a raw buffer straight into LDS (lane i's element
 // lands zero-extended in dword i of the destination).
@@ -253,13 +257,13 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(8))) void
 // Forward: h starts at h_init (or 0); for chunk c < n_agg, h_in[c] = h, then
 // h <- exp2(A' S_c) h + h_local_c.  Writes h_in[n_agg] too when requested,
 // and the final state.  Reverse (kRev): h starts at 0 on the right, walks
-// chunks n_chunks-1 .. 0, h_in[c] = h (the state entering chunk c from its
-// right end), then folds chunk c (aggregates exist for c >= 1).
+// chunks n_chunks-1 .. c_low, h_in[c] = h (the state entering chunk c from its
+// right end), then folds chunk c (aggregates exist for c > c_low).
 template <bool kRev>
 __global__ __launch_bounds__(256) void carry_kernel(
     const float *__restrict__ agg_h, const float *__restrict__ agg_s, const float *__restrict__ A,
     const float *h_init, float *__restrict__ h_in, float *h_final,
-    int batch, int D, int n_chunks, int n_agg)
+    int batch, int D, int n_chunks, int n_agg, int c_low)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t total = (int64_t)batch * D * kStates;
@@ -298,9 +302,9 @@ __global__ __launch_bounds__(256) void carry_kernel(
         if (h_in && n_agg < n_chunks) h_in[base_h + (int64_t)n_agg * cs] = h;
         if (h_final) h_final[i] = h;
     } else {
-        for (int c = n_chunks - 1; c >= 0; --c) {
+        for (int c = n_chunks - 1; c >= c_low; --c) {
             h_in[base_h + c * cs] = h;
-            if (c == 0) break;
+            if (c == c_low) break;
             const float s = agg_s[base_s + (int64_t)c * D];
             h = __builtin_fmaf(fast_exp2(a2 * s), h, agg_h[base_h + c * cs]);
         }

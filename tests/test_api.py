@@ -28,7 +28,7 @@ def test_exports_match_header():
 
 
 def test_version_and_status_strings():
-    assert m.version() == 10000
+    assert m.version() == 10100
     for code in range(-7, 1):
         assert m.status_str(code) not in ("", "unknown status")
     assert m.status_str(-99) == "unknown status"
@@ -143,3 +143,43 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         m.block_step(torch.zeros(1, 64, 16), x, x, torch.zeros(1, 16, 16, dtype=torch.bfloat16),
                      torch.zeros(1, 16, 16, dtype=torch.bfloat16), torch.zeros(64, 16), torch.zeros(64))
+
+
+def train_bwd(s, T, x=FAKE, dt=FAKE + 0x1000, Bm=FAKE + 0x2000, C=FAKE + 0x3000, A=FAKE + 0x4000,
+              Ds=FAKE + 0x5000, hb=FAKE + 0x6000, dy=FAKE + 0x7000, dbnd=None, dx=FAKE + 0x8000,
+              ddt=FAKE + 0x9000, dB=FAKE + 0xA000, dC=FAKE + 0xB000, dA=FAKE + 0xC000,
+              dD=FAKE + 0xD000, dh=None, ws=None, ws_bytes=0):
+    return lib().bdssm_train_scan_bwd(ctypes.byref(s), T, P(x), P(dt), P(Bm), P(C), P(A), P(Ds),
+                                      P(hb), P(dy), P(dbnd), P(dx), P(ddt), P(dB), P(dC), P(dA),
+                                      P(dD), P(dh), P(ws), ws_bytes, None)
+
+
+def test_backward_argument_errors():
+    s = shape(D=8)
+    assert train_bwd(shape(N=8), 16) == -2
+    assert train_bwd(s, 24) == -2                      # T % L != 0
+    assert train_bwd(s, 16, hb=None) == -1             # saved block states required
+    assert train_bwd(s, 16, dy=None) == -1
+    assert train_bwd(s, 16, dA=None) == -1
+    assert train_bwd(s, 16, dx=MIS) == -4
+    assert train_bwd(s, 16, dx=FAKE) == -7             # dx on top of x
+    assert train_bwd(s, 16, dB=FAKE + 0x8000) == -7    # two outputs overlap
+    assert train_bwd(s, 16, dC=FAKE + 0x7000) == -7    # output on top of dy
+    # with a valid argument set the missing workspace is reported
+    need = m.workspace_bytes(1, 8, 16, m.OP_TRAIN_BWD)
+    assert need > 0
+    assert train_bwd(s, 16) == -5
+    assert train_bwd(s, 16, ws=FAKE + 0x100000, ws_bytes=need - 1) == -5
+    rc = lib().bdssm_train_scan_blocks_bwd(ctypes.byref(s), 16, *[P(FAKE + k * 0x1000) for k in range(6)],
+                                           P(None), P(FAKE + 0x7000), *[P(FAKE + k * 0x1000) for k in range(8, 14)],
+                                           P(None), P(None), 0, None)
+    assert rc == -1                                    # h0_blocks required
+
+
+def test_backward_workspace_sizes():
+    # the dB / dC channel partials dominate: batch * ceil(D/64) * T * 32 fp32
+    n = m.workspace_bytes(8, 1536, 4096, m.OP_TRAIN_BWD)
+    assert n >= 8 * 24 * 4096 * 32 * 4
+    n2 = m.workspace_bytes(8, 1536, 4096, m.OP_BLOCKS_BWD)
+    assert 8 * 24 * 4096 * 32 * 4 <= n2 <= n
+    assert m.workspace_bytes(1, 64, 0, m.OP_TRAIN_BWD) == 0

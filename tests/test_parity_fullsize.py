@@ -125,3 +125,63 @@ def test_train_blocks_87m_sampled(dev):
                              ora(Dskip[idx]), L, to_np(h0b[:, :, idx]))
     got = to_np(gather(y, ch))
     assert rel_err(got, yo) < TOL_BF16, worst(got, yo)
+
+
+@pytest.mark.parametrize("name", ["train_87m", "train_350m"])
+def test_training_backward_sampled(dev, name):
+    """Backward of the all-block training scan at full size.  Per-channel
+    gradients (dx, ddt, dA, dDskip, dh_init) on sampled channels over every
+    batch row; the channel-summed dB, dC on batch row 0 over every channel."""
+    wl = synth.WORKLOADS[name]
+    batch, D, T, L, sid = wl["batch"], wl["d_inner"], wl["seq"], wl["block"], wl["sid"]
+    print("[fullsize] %s backward: batch %d, D %d, T %d" % (name, batch, D, T), flush=True)
+    x, dt, Bm, Cm = synth.stream(batch, T, D, N, sid, 0, torch.bfloat16, dev)
+    A, Dskip = synth.params(D, N, sid, "default", dev)
+    dy = synth.normal((batch, T, D), 1000 * sid + 8, dev, torch.bfloat16)
+    db = synth.normal((batch, T // L + 1, D, N), 1000 * sid + 9, dev)
+    _, bnd = m.train_scan(x, dt, Bm, Cm, A, Dskip, L, want_bounds=True)
+    g = m.train_scan_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, d_bounds=db, want_dh_init=True)
+    torch.cuda.synchronize()
+    del bnd
+    ch = sample_channels(D, 8, 41)
+    idx = torch.as_tensor(ch, device=dev)
+    r = oracle.scan_bwd(ora(gather(x, ch)), ora(gather(dt, ch)), ora(Bm), ora(Cm), ora(A[idx]),
+                        ora(Dskip[idx]), L, to_np(gather(dy, ch)), dbounds=to_np(db[:, :, idx]))
+    for k in ("dx", "ddt"):
+        got = to_np(gather(g[k], ch))
+        assert rel_err(got, r[k]) < TOL_BF16, (k, worst(got, r[k]))
+    for k, got in (("dA", to_np(g["dA"][idx])), ("dDskip", to_np(g["dDskip"][idx])),
+                   ("dh0", to_np(g["dh_init"][:, idx]))):
+        assert rel_err(got, r[k]) < STATE_TOL, (k, worst(got, r[k]))
+    r0 = oracle.scan_bwd(ora(x[:1]), ora(dt[:1]), ora(Bm[:1]), ora(Cm[:1]), ora(A), ora(Dskip), L,
+                         to_np(dy[:1]), dbounds=to_np(db[:1]))
+    for k in ("dB", "dC"):
+        got = to_np(g[k][:1])
+        assert rel_err(got, r0[k]) < TOL_BF16, (k, worst(got, r0[k]))
+
+
+def test_two_stream_backward_87m_sampled(dev):
+    """Backward of the two-stream form at the 87M training shape."""
+    wl = synth.WORKLOADS["train_87m"]
+    batch, D, T, L, sid = wl["batch"], wl["d_inner"], wl["seq"], wl["block"], wl["sid"]
+    x, dt, Bm, Cm = synth.stream(batch, T, D, N, sid, 0, torch.bfloat16, dev)
+    A, Dskip = synth.params(D, N, sid, "default", dev)
+    h0b = synth.normal((batch, T // L + 1, D, N), 1000 * sid + 7, dev)
+    dy = synth.normal((batch, T, D), 1000 * sid + 8, dev, torch.bfloat16)
+    g = m.train_scan_blocks_bwd(x, dt, Bm, Cm, A, Dskip, L, h0b, dy, want_dh0_blocks=True)
+    torch.cuda.synchronize()
+    ch = sample_channels(D, 8, 43)
+    idx = torch.as_tensor(ch, device=dev)
+    r = oracle.scan_bwd(ora(gather(x, ch)), ora(gather(dt, ch)), ora(Bm), ora(Cm), ora(A[idx]),
+                        ora(Dskip[idx]), L, to_np(gather(dy, ch)), h0_blocks=to_np(h0b[:, :, idx]))
+    for k in ("dx", "ddt"):
+        got = to_np(gather(g[k], ch))
+        assert rel_err(got, r[k]) < TOL_BF16, (k, worst(got, r[k]))
+    for k, got in (("dA", to_np(g["dA"][idx])), ("dDskip", to_np(g["dDskip"][idx])),
+                   ("dh0_blocks", to_np(g["dh0_blocks"][:, :, idx]))):
+        assert rel_err(got, r[k]) < STATE_TOL, (k, worst(got, r[k]))
+    r0 = oracle.scan_bwd(ora(x[:1]), ora(dt[:1]), ora(Bm[:1]), ora(Cm[:1]), ora(A), ora(Dskip), L,
+                         to_np(dy[:1]), h0_blocks=to_np(h0b[:1]))
+    for k in ("dB", "dC"):
+        got = to_np(g[k][:1])
+        assert rel_err(got, r0[k]) < TOL_BF16, (k, worst(got, r0[k]))
