@@ -105,6 +105,15 @@ def slots_forward(batch, T, D):
     return batch * T * D * (NS * (EXP_SLOTS + 3) + 1)
 
 
+def slots_backward(batch, T, D):
+    """Algorithmic issue slots of the backward pass per (b,t,d,n): one exp2 (2)
+    and dt*A' (1); the forward state (u, FMA), the reverse state (FMA), the
+    forward adjoint (FMA, mul), the reverse adjoint (FMA, mul); du (add), da
+    (FMA, mul), the dt / x / A sums (FMA, mul, FMA, FMA), dB (mul), dC (FMA,
+    add, mul): 22; plus 4 per (b,t,d) for the dt and x gradients."""
+    return batch * T * D * (NS * 22 + 4)
+
+
 def slots_bidirectional(batch, T, D):
     """forward + in-block reverse + output: exp2 + 2 mul + 4 FMA per
     (b,t,d,n), plus dt*x and the Dskip*x FMA per (b,t,d)."""
@@ -414,6 +423,46 @@ def train_main(args, wl, m, synth, torch):
     b.record(st)
     torch.cuda.synchronize()
     two_ms = a.elapsed_time(b) / args.steps
+    # backward passes: continuous form (from the saved block states) and the
+    # two-stream form; then one whole all-block training step, forward and
+    # backward over both streams
+    dy = synth.normal((batch, T, D), 1000 * sid + 8, dev, dtype)
+    wsb = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_TRAIN_BWD, L, NS, dtype)),
+                      dtype=torch.uint8, device=dev)
+    wsbb = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_BLOCKS_BWD, L, NS, dtype)),
+                       dtype=torch.uint8, device=dev)
+    m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, h_bounds=bnd, ws=ws)
+    m.train_scan_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, ws=wsb)
+    torch.cuda.synchronize()
+    a.record(st)
+    for _ in range(args.steps):
+        m.train_scan_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, ws=wsb)
+    b.record(st)
+    torch.cuda.synchronize()
+    bwd_ms = a.elapsed_time(b) / args.steps
+    a.record(st)
+    for _ in range(args.steps):
+        m.train_scan_blocks_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, want_dh0_blocks=True, ws=wsbb)
+    b.record(st)
+    torch.cuda.synchronize()
+    bbwd_ms = a.elapsed_time(b) / args.steps
+
+    def all_block_step():
+        m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, h_bounds=bnd, ws=ws)
+        m.train_scan_blocks(x, dt, Bm, Cm, A, Dskip, L, bnd, y=y)
+        gn = m.train_scan_blocks_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, want_dh0_blocks=True,
+                                     ws=wsbb)
+        m.train_scan_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, d_bounds=gn["dh0_blocks"], ws=wsb)
+
+    all_block_step()
+    torch.cuda.synchronize()
+    a.record(st)
+    for _ in range(args.steps):
+        all_block_step()
+    b.record(st)
+    torch.cuda.synchronize()
+    step_ms = a.elapsed_time(b) / args.steps
+    bslots = slots_backward(batch, T, D)
     line = {
         "metric": "all-block training scan GB/s (forward over T + reverse per block)",
         "value": nbytes / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
@@ -433,6 +482,16 @@ def train_main(args, wl, m, synth, torch):
         "two_stream": {"ms": two_ms, "over_full_scan_time": two_ms / full_ms,
                        "note": "clean train_scan with h_bounds + noisy train_scan_blocks, "
                                "against one full-sequence scan of the noisy stream"},
+        "backward": {"train_scan_bwd_ms": bwd_ms,
+                     "train_scan_bwd_valu_slot_frac": bslots / (bwd_ms * 1e-3) / VALU_SLOTS_PER_S,
+                     "train_scan_blocks_bwd_ms": bbwd_ms,
+                     "train_scan_blocks_bwd_valu_slot_frac": bslots / (bbwd_ms * 1e-3) / VALU_SLOTS_PER_S,
+                     "bwd_over_fwd_time": bwd_ms / ev_ms},
+        "all_block_training_step": {
+            "ms": step_ms, "tokens_per_s": batch * T / (step_ms * 1e-3),
+            "note": "forward and backward of both streams: clean train_scan (block states), "
+                    "noisy train_scan_blocks, noisy backward, clean backward fed the noisy "
+                    "block-start gradients"},
     }
     print(json.dumps(line), flush=True)
     return 0
