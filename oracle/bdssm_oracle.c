@@ -72,7 +72,22 @@ static double ld(const void *p, size_t i, int dtype)
     return (double)((const float *)p)[i];
 }
 
-int oracle_version(void) { return 2; }
+/*
+ * Optional fusions of a Mamba-1 layer around the scan (the pages are silent on
+ * them; they follow the Mamba-1 layer): the raw step size plus a per-channel
+ * bias, passed through softplus, gives dt; the output is gated by silu(z).
+ */
+static double step_size(double raw, double bias, int softplus)
+{
+    const double v = raw + bias;
+    if (!softplus) return v;
+    /* softplus(v) = log(1 + e^v), written so that neither branch overflows */
+    return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));
+}
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+int oracle_version(void) { return 3; }
 
 /* Threads the OpenMP loop over rows will use (1 without OpenMP). */
 int oracle_num_threads(void)
@@ -97,10 +112,11 @@ int oracle_num_threads(void)
  * L must divide T (L >= 1).  Cm may be NULL only when y, yf and yr are NULL.
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
-int oracle_scan(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int dtype,
-                const void *x, const void *dt, const void *Bm, const void *Cm,
-                const double *A, const double *Dskip, const double *h0,
-                double *y, double *yf, double *yr, double *hT, double *bounds)
+int oracle_scan_ex(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int dtype,
+                   const void *x, const void *dt, const void *Bm, const void *Cm,
+                   const double *A, const double *Dskip, const double *h0,
+                   const double *dt_bias, int dt_softplus, const void *z,
+                   double *y, double *yf, double *yr, double *hT, double *bounds)
 {
     const int want_y = (y != NULL) || (yf != NULL) || (yr != NULL);
     if (batch < 0 || T < 0 || D < 0 || N < 1 || L < 1) return -1;
@@ -134,7 +150,7 @@ int oracle_scan(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int d
             for (int64_t t = 0; t < T; ++t) {
                 const size_t ix = (size_t)((b * T + t) * D + d);
                 const size_t ib = (size_t)((b * T + t) * N);
-                const double dtv = ld(dt, ix, dtype);
+                const double dtv = step_size(ld(dt, ix, dtype), dt_bias ? dt_bias[d] : 0.0, dt_softplus);
                 const double xv = ld(x, ix, dtype);
                 double acc = 0.0;
                 for (int64_t n = 0; n < N; ++n) {
@@ -158,7 +174,7 @@ int oracle_scan(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int d
                     for (int64_t t = k * L + L - 1; t >= k * L; --t) {
                         const size_t ix = (size_t)((b * T + t) * D + d);
                         const size_t ib = (size_t)((b * T + t) * N);
-                        const double dtv = ld(dt, ix, dtype);
+                        const double dtv = step_size(ld(dt, ix, dtype), dt_bias ? dt_bias[d] : 0.0, dt_softplus);
                         const double xv = ld(x, ix, dtype);
                         double acc = 0.0;
                         for (int64_t n = 0; n < N; ++n) {
@@ -169,7 +185,7 @@ int oracle_scan(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int d
                         }
                         if (yf) yf[ix] = fwd[t];
                         if (yr) yr[ix] = acc;
-                        if (y) y[ix] = fwd[t] + acc + Dskip[d] * xv;
+                        if (y) y[ix] = (fwd[t] + acc + Dskip[d] * xv) * (z ? silu(ld(z, ix, dtype)) : 1.0);
                     }
                 }
             }
@@ -177,6 +193,16 @@ int oracle_scan(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int d
         }
     }
     return fail ? -1 : 0;
+}
+
+/* The core routine without the fusions. */
+int oracle_scan(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int dtype,
+                const void *x, const void *dt, const void *Bm, const void *Cm,
+                const double *A, const double *Dskip, const double *h0,
+                double *y, double *yf, double *yr, double *hT, double *bounds)
+{
+    return oracle_scan_ex(batch, T, D, N, L, dtype, x, dt, Bm, Cm, A, Dskip, h0, NULL, 0, NULL,
+                          y, yf, yr, hT, bounds);
 }
 
 /* ---- the five entry points, each a composition of the core routine ---- */
@@ -238,9 +264,10 @@ int oracle_train_scan(int64_t batch, int64_t D, int64_t N, int64_t L, int dtype,
  * scan from h0_blocks[b, k] (layout [batch, T/L + 1, D, N], the layout of the
  * bounds output; entry T/L is not read) and the reverse inside the block.
  * No state crosses a block boundary.  y: [batch, T, D]. */
-int oracle_train_blocks(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int dtype,
-                        const void *x, const void *dt, const void *Bm, const void *Cm,
-                        const double *A, const double *Dskip, const double *h0_blocks, double *y)
+int oracle_train_blocks_ex(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int dtype,
+                           const void *x, const void *dt, const void *Bm, const void *Cm,
+                           const double *A, const double *Dskip, const double *h0_blocks,
+                           const double *dt_bias, int dt_softplus, const void *z, double *y)
 {
     if (batch < 0 || T < 0 || D < 0 || N < 1 || L < 1 || T % L != 0) return -1;
     if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) return -1;
@@ -266,7 +293,7 @@ int oracle_train_blocks(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t 
                 for (int64_t t = k * L; t < k * L + L; ++t) {
                     const size_t ix = (size_t)((b * T + t) * D + d);
                     const size_t ib = (size_t)((b * T + t) * N);
-                    const double dtv = ld(dt, ix, dtype);
+                    const double dtv = step_size(ld(dt, ix, dtype), dt_bias ? dt_bias[d] : 0.0, dt_softplus);
                     const double xv = ld(x, ix, dtype);
                     double acc = 0.0;
                     for (int64_t n = 0; n < N; ++n) {
@@ -281,7 +308,7 @@ int oracle_train_blocks(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t 
                 for (int64_t t = k * L + L - 1; t >= k * L; --t) {
                     const size_t ix = (size_t)((b * T + t) * D + d);
                     const size_t ib = (size_t)((b * T + t) * N);
-                    const double dtv = ld(dt, ix, dtype);
+                    const double dtv = step_size(ld(dt, ix, dtype), dt_bias ? dt_bias[d] : 0.0, dt_softplus);
                     const double xv = ld(x, ix, dtype);
                     double acc = 0.0;
                     for (int64_t n = 0; n < N; ++n) {
@@ -289,13 +316,21 @@ int oracle_train_blocks(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t 
                         r[n] = decay * r[n] + dtv * ld(Bm, ib + n, dtype) * xv;
                         acc += ld(Cm, ib + n, dtype) * r[n];
                     }
-                    y[ix] = fwd[t - k * L] + acc + Dskip[d] * xv;
+                    y[ix] = (fwd[t - k * L] + acc + Dskip[d] * xv) * (z ? silu(ld(z, ix, dtype)) : 1.0);
                 }
             }
             free(h); free(r); free(fwd);
         }
     }
     return fail ? -1 : 0;
+}
+
+int oracle_train_blocks(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int dtype,
+                        const void *x, const void *dt, const void *Bm, const void *Cm,
+                        const double *A, const double *Dskip, const double *h0_blocks, double *y)
+{
+    return oracle_train_blocks_ex(batch, T, D, N, L, dtype, x, dt, Bm, Cm, A, Dskip, h0_blocks,
+                                  NULL, 0, NULL, y);
 }
 
 /* Full-sequence bidirectional baseline: the reverse runs over the whole

@@ -40,6 +40,12 @@ def bind(lib):
     I = ctypes.c_int64
     lib.oracle_scan.argtypes = [I, I, I, I, I, ctypes.c_int] + [P] * 12
     lib.oracle_scan.restype = ctypes.c_int
+    lib.oracle_scan_ex.argtypes = ([I, I, I, I, I, ctypes.c_int] + [P] * 8 + [ctypes.c_int]
+                                   + [P] * 6)
+    lib.oracle_scan_ex.restype = ctypes.c_int
+    lib.oracle_train_blocks_ex.argtypes = ([I, I, I, I, I, ctypes.c_int] + [P] * 8 + [ctypes.c_int]
+                                           + [P] * 2)
+    lib.oracle_train_blocks_ex.restype = ctypes.c_int
     lib.oracle_version.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_train_blocks.argtypes = [I, I, I, I, I, ctypes.c_int] + [P] * 8
@@ -87,10 +93,24 @@ def _c(a, dt=None):
     return np.ascontiguousarray(a)
 
 
-def scan(x, dt, B, C, A, Dskip, L, h0=None, want_y=True, want_parts=False, want_bounds=False):
+def _fusion(x, D, dt_bias, z):
+    """Marshal the optional fusions: dt_bias [D] (float64), z (x's dtype)."""
+    bias = _c(dt_bias, np.float64)
+    if bias is not None:
+        assert bias.shape == (D,)
+    zz = _c(z)
+    if zz is not None:
+        if zz.dtype != x.dtype or zz.shape != x.shape:
+            raise TypeError("z must match x in dtype and shape")
+    return bias, zz
+
+
+def scan(x, dt, B, C, A, Dskip, L, h0=None, want_y=True, want_parts=False, want_bounds=False,
+         dt_bias=None, dt_softplus=False, z=None):
     """Core oracle: continuous forward from h0, reverse segmented into L-token
     blocks.  Returns a dict with 'y' (and 'yf', 'yr' if want_parts), 'hT',
-    and 'bounds' ([batch, T/L+1, D, N]) if want_bounds."""
+    and 'bounds' ([batch, T/L+1, D, N]) if want_bounds.  Optional fusions:
+    dt <- dt + dt_bias, then softplus if dt_softplus; y <- y * silu(z)."""
     x, dt, B = _c(x), _c(dt), _c(B)
     C = _c(C)
     A = _c(A, np.float64)
@@ -116,46 +136,48 @@ def scan(x, dt, B, C, A, Dskip, L, h0=None, want_y=True, want_parts=False, want_
             yr = out["yr"] = np.empty((batch, T, D), np.float64)
     if want_bounds:
         bounds = out["bounds"] = np.empty((batch, T // L + 1, D, N), np.float64)
-    rc = load().oracle_scan(batch, T, D, N, L, code, _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
-                            _ptr(A), _ptr(Dskip), _ptr(h0), _ptr(y), _ptr(yf), _ptr(yr),
-                            _ptr(out["hT"]), _ptr(bounds))
+    bias, zz = _fusion(x, D, dt_bias, z)
+    rc = load().oracle_scan_ex(batch, T, D, N, L, code, _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
+                               _ptr(A), _ptr(Dskip), _ptr(h0), _ptr(bias), int(bool(dt_softplus)),
+                               _ptr(zz), _ptr(y), _ptr(yf), _ptr(yr), _ptr(out["hT"]),
+                               _ptr(bounds))
     if rc != 0:
         raise ValueError("oracle_scan rejected its arguments (rc=%d)" % rc)
     return out
 
 
-def prefill(x, dt, B, C, A, Dskip, L, h_init=None, want_y=False):
+def prefill(x, dt, B, C, A, Dskip, L, h_init=None, want_y=False, **fusion):
     """Clean-context prefill -> (h_cache, y or None)."""
-    r = scan(x, dt, B, C, A, Dskip, L, h0=h_init, want_y=want_y)
+    r = scan(x, dt, B, C, A, Dskip, L, h0=h_init, want_y=want_y, **fusion)
     return r["hT"], r.get("y")
 
 
-def block_step(h_cache, x, dt, B, C, A, Dskip):
+def block_step(h_cache, x, dt, B, C, A, Dskip, **fusion):
     """One denoising step on an L-token block (L = x.shape[1]) -> y."""
     L = x.shape[1]
-    return scan(x, dt, B, C, A, Dskip, L, h0=h_cache, want_y=True)["y"]
+    return scan(x, dt, B, C, A, Dskip, L, h0=h_cache, want_y=True, **fusion)["y"]
 
 
-def commit(h_cache, x, dt, B, C, A, Dskip, want_y=False):
+def commit(h_cache, x, dt, B, C, A, Dskip, want_y=False, **fusion):
     """Finalise an L-token block -> (new h_cache, y or None)."""
     L = x.shape[1]
-    r = scan(x, dt, B, C, A, Dskip, L, h0=h_cache, want_y=want_y)
+    r = scan(x, dt, B, C, A, Dskip, L, h0=h_cache, want_y=want_y, **fusion)
     return r["hT"], r.get("y")
 
 
-def train_scan(x, dt, B, C, A, Dskip, L, h_init=None, want_bounds=False):
+def train_scan(x, dt, B, C, A, Dskip, L, h_init=None, want_bounds=False, **fusion):
     """All-block training form -> (y, h_bounds or None)."""
-    r = scan(x, dt, B, C, A, Dskip, L, h0=h_init, want_y=True, want_bounds=want_bounds)
+    r = scan(x, dt, B, C, A, Dskip, L, h0=h_init, want_y=True, want_bounds=want_bounds, **fusion)
     return r["y"], r.get("bounds")
 
 
-def full_scan(x, dt, B, C, A, Dskip):
+def full_scan(x, dt, B, C, A, Dskip, **fusion):
     """Full-sequence bidirectional baseline (reverse over the whole row) -> y."""
     T = x.shape[1]
-    return scan(x, dt, B, C, A, Dskip, max(T, 1), h0=None, want_y=True)["y"]
+    return scan(x, dt, B, C, A, Dskip, max(T, 1), h0=None, want_y=True, **fusion)["y"]
 
 
-def train_blocks(x, dt, B, C, A, Dskip, L, h0_blocks):
+def train_blocks(x, dt, B, C, A, Dskip, L, h0_blocks, dt_bias=None, dt_softplus=False, z=None):
     """Two-stream training form, noisy stream: every L-block k scanned from
     h0_blocks[:, k] ([batch, T/L + 1, D, N]) plus the in-block reverse -> y."""
     x, dt, B, C = _c(x), _c(dt), _c(B), _c(C)
@@ -167,8 +189,10 @@ def train_blocks(x, dt, B, C, A, Dskip, L, h0_blocks):
     N = A.shape[1]
     assert h0.shape == (batch, T // L + 1, D, N)
     y = np.empty((batch, T, D), np.float64)
-    rc = load().oracle_train_blocks(batch, T, D, N, L, code, _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
-                                    _ptr(A), _ptr(Dskip), _ptr(h0), _ptr(y))
+    bias, zz = _fusion(x, D, dt_bias, z)
+    rc = load().oracle_train_blocks_ex(batch, T, D, N, L, code, _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
+                                       _ptr(A), _ptr(Dskip), _ptr(h0), _ptr(bias),
+                                       int(bool(dt_softplus)), _ptr(zz), _ptr(y))
     if rc != 0:
         raise ValueError("oracle_train_blocks rejected its arguments (rc=%d)" % rc)
     return y

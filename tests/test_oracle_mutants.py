@@ -18,11 +18,12 @@ import oracle
 from oracle import oracle as _oracle_mod
 import test_oracle as pins
 import test_oracle_bwd as bwd_pins
+import test_oracle_fused as fused_pins
 
 SRC = os.path.join(os.path.dirname(_oracle_mod.__file__), "bdssm_oracle.c")
 
 MUTANTS = {
-    "drop_skip_term": ("y[ix] = fwd[t] + acc + Dskip[d] * xv;", "y[ix] = fwd[t] + acc;"),
+    "drop_skip_term": ("if (y) y[ix] = (fwd[t] + acc + Dskip[d] * xv) *", "if (y) y[ix] = (fwd[t] + acc) *"),
     "decay_sign": ("const double decay = exp(dtv * A[d * N + n]);\n                    const double inject",
                    "const double decay = exp(-dtv * A[d * N + n]);\n                    const double inject"),
     "reverse_exclusive": ("r[n] = decay * r[n] + inject;\n                            acc += ld(Cm, ib + n, dtype) * r[n];",
@@ -33,7 +34,7 @@ MUTANTS = {
                      "const double decay = exp(dtv * A[n * D + d]);\n                    const double inject"),
     "ignore_initial_state": ("h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;"),
     "reverse_not_reset": ("for (int64_t n = 0; n < N; ++n) r[n] = 0.0;\n", ""),
-    "no_reverse": ("if (y) y[ix] = fwd[t] + acc +", "if (y) y[ix] = fwd[t] + 0.0 * acc +"),
+    "no_reverse": ("if (y) y[ix] = (fwd[t] + acc +", "if (y) y[ix] = (fwd[t] + 0.0 * acc +"),
     "forward_reset_per_block": ("if (bounds && (t + 1) % L == 0)",
                                 "if ((t + 1) % L == 0) for (int64_t n = 0; n < N; ++n) h[n] = 0.0;\n"
                                 "                if (bounds && (t + 1) % L == 0)"),
@@ -58,6 +59,16 @@ MUTANTS_BWD = {
     "bwd_dx_missing_skip": ("dx[ix] = sx + dy[ix] * Dskip[d];", "dx[ix] = sx;"),
     "bwd_dB_missing_dt": ("my_dB[ib + n] += du * dtv * xv;", "my_dB[ib + n] += du * xv;"),
     "bwd_dA_missing_dt": ("my_dA[d * N + n] += da * at * dtv;", "my_dA[d * N + n] += da * at;"),
+}
+
+MUTANTS_FUSED = {
+    "softplus_wrong_branch": ("return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));",
+                              "return v > 0.0 ? v + log1p(exp(v)) : log1p(exp(v));"),
+    "bias_ignored": ("const double v = raw + bias;", "const double v = raw;"),
+    "gate_is_sigmoid": ("static double silu(double z) { return z / (1.0 + exp(-z)); }",
+                        "static double silu(double z) { return 1.0 / (1.0 + exp(-z)); }"),
+    "gate_missing": ("if (y) y[ix] = (fwd[t] + acc + Dskip[d] * xv) * (z ? silu(ld(z, ix, dtype)) : 1.0);",
+                     "if (y) y[ix] = (fwd[t] + acc + Dskip[d] * xv);"),
 }
 
 
@@ -112,3 +123,9 @@ def test_some_pin_catches_mutant(mutant, tmp_path):
 def test_some_gradient_pin_catches_mutant(mutant, tmp_path):
     old, new = MUTANTS_BWD[mutant]
     assert _run_mutant(old, new, tmp_path, bwd_pins), "no gradient pin noticed mutant %s" % mutant
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS_FUSED))
+def test_some_fusion_pin_catches_mutant(mutant, tmp_path):
+    old, new = MUTANTS_FUSED[mutant]
+    assert _run_mutant(old, new, tmp_path, fused_pins), "no fusion pin noticed mutant %s" % mutant
