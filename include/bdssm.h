@@ -35,7 +35,8 @@
  *   states   : [batch, d_inner, d_state] fp32
  *   h_bounds : [batch, T/L + 1, d_inner, d_state] fp32
  * dt is the positive step size, already passed through softplus by the
- * caller.  bf16 outputs are rounded to nearest even from fp32.
+ * caller, unless a bdssm_fusion asks the scan to form it (below).  bf16
+ * outputs are rounded to nearest even from fp32.
  *
  * Ownership and execution.  Every pointer is caller-owned device memory on the
  * current HIP device with a 16-byte aligned base.  The library allocates
@@ -53,7 +54,7 @@
  * bdssm_commit is read and written in place).
  *
  * Limits of this version: d_state == 16; block_len in {1, 2, 4, 8, 16};
- * T % block_len == 0; x, dt, B, C and y share one dtype.
+ * T % block_len == 0; x, dt, B, C, z and y share one dtype.
  */
 #ifndef BDSSM_H
 #define BDSSM_H
@@ -87,6 +88,26 @@ typedef enum {
     BDSSM_OP_BLOCKS_BWD = 4   /* bdssm_train_scan_blocks_bwd */
 } bdssm_op;
 
+/*
+ * Optional fusions of a Mamba-1 layer around the scan (the pages are silent on
+ * them; they follow the Mamba-1 layer).  Pass NULL for none.
+ *   dt_bias     NULL, or [d_inner] fp32: added to the dt stream per channel.
+ *   dt_softplus nonzero: dt = softplus(dt_stream + dt_bias) = log(1 + e^v);
+ *               the dt stream then holds the raw pre-activation.
+ *   z           NULL, or the gate, with the layout and dtype of y ([batch,
+ *               T, d_inner] of the call): y = (sum_n C (hf + hr) + Dskip x) *
+ *               silu(z), silu(v) = v / (1 + e^-v).  Read only by calls that
+ *               write y.
+ * With dt_bias = NULL, dt_softplus = 0 and z = NULL every result is the same
+ * as with no fusion.  The backward entry points take no fusion: they
+ * differentiate the unfused scan.
+ */
+typedef struct {
+    const float *dt_bias;
+    int32_t dt_softplus;
+    const void *z;
+} bdssm_fusion;
+
 typedef struct {
     int64_t batch;     /* >= 0 */
     int64_t d_inner;   /* channels D, >= 0 */
@@ -110,7 +131,7 @@ typedef struct {
 int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const void *dt,
                   const void *B, const void *C, const float *A, const float *Dskip,
                   const float *h_init, float *h_cache, void *y, void *ws, size_t ws_bytes,
-                  void *stream);
+                  const bdssm_fusion *fusion, void *stream);
 
 /*
  * One denoising step on the active block (exactly L tokens) [ABS], [DE-M]:
@@ -120,7 +141,7 @@ int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const 
  */
 int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void *x,
                      const void *dt, const void *B, const void *C, const float *A,
-                     const float *Dskip, void *y, void *stream);
+                     const float *Dskip, void *y, const bdssm_fusion *fusion, void *stream);
 
 /*
  * Commit a finished block (its final clean inputs, L tokens) [DE-M]: the
@@ -131,7 +152,7 @@ int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void 
  */
 int bdssm_commit(const bdssm_shape *shape, float *h_cache, const void *x, const void *dt,
                  const void *B, const void *C, const float *A, const float *Dskip, void *y,
-                 void *stream);
+                 const bdssm_fusion *fusion, void *stream);
 
 /*
  * All-block training form over T tokens [DE-M]: the forward scan runs over
@@ -145,7 +166,7 @@ int bdssm_commit(const bdssm_shape *shape, float *h_cache, const void *x, const 
 int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
                      const void *B, const void *C, const float *A, const float *Dskip,
                      const float *h_init, void *y, float *h_bounds, void *ws, size_t ws_bytes,
-                     void *stream);
+                     const bdssm_fusion *fusion, void *stream);
 
 /*
  * Two-stream all-block training form, noisy stream [DE-M]: downstream block
@@ -163,7 +184,8 @@ int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const v
  */
 int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
                             const void *B, const void *C, const float *A, const float *Dskip,
-                            const float *h0_blocks, void *y, void *stream);
+                            const float *h0_blocks, void *y, const bdssm_fusion *fusion,
+                            void *stream);
 
 /*
  * Backward of bdssm_train_scan (reverse-mode gradients).  The all-block
@@ -221,7 +243,7 @@ int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void 
  */
 int bdssm_full_scan(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
                     const void *B, const void *C, const float *A, const float *Dskip, void *y,
-                    void *ws, size_t ws_bytes, void *stream);
+                    void *ws, size_t ws_bytes, const bdssm_fusion *fusion, void *stream);
 
 /* Workspace bytes the given entry point needs at sequence length T (0 if none;
  * (size_t)-1 if the shape is invalid). */

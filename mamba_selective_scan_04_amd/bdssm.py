@@ -9,6 +9,8 @@ Names and semantics follow include/bdssm.h:
   full_scan(x, dt, B, C, A, Dskip, y=None)
   train_scan_bwd(x, dt, B, C, A, Dskip, block_len, h_bounds, dy, d_bounds=None, want_dh_init=False)
   train_scan_blocks_bwd(x, dt, B, C, A, Dskip, block_len, h0_blocks, dy, want_dh0_blocks=False)
+The six forward functions also take the optional Mamba-1 fusions as keyword
+arguments: dt_bias ([D] fp32), dt_softplus (bool), z (gate, like y).
 Shapes: x, dt, y [batch, T, D]; B, C [batch, T, 16]; A [D, 16] fp32;
 Dskip [D] fp32; states [batch, D, 16] fp32.  x/dt/B/C/y share fp32 or bf16.
 All tensors must be contiguous, on the current CUDA (HIP) device.  Work is
@@ -43,6 +45,11 @@ class Shape(ctypes.Structure):
                 ("dtype", ctypes.c_int32)]
 
 
+class Fusion(ctypes.Structure):
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int32),
+                ("z", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -57,12 +64,13 @@ def load():
     lib = ctypes.CDLL(LIB_PATH)
     P, I, S = ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(Shape)
     Z = ctypes.c_size_t
-    lib.bdssm_prefill.argtypes = [S, I, P, P, P, P, P, P, P, P, P, P, Z, P]
-    lib.bdssm_block_step.argtypes = [S, P, P, P, P, P, P, P, P, P]
-    lib.bdssm_commit.argtypes = [S, P, P, P, P, P, P, P, P, P]
-    lib.bdssm_train_scan.argtypes = [S, I, P, P, P, P, P, P, P, P, P, P, Z, P]
-    lib.bdssm_full_scan.argtypes = [S, I, P, P, P, P, P, P, P, P, Z, P]
-    lib.bdssm_train_scan_blocks.argtypes = [S, I, P, P, P, P, P, P, P, P, P]
+    F = ctypes.POINTER(Fusion)
+    lib.bdssm_prefill.argtypes = [S, I, P, P, P, P, P, P, P, P, P, P, Z, F, P]
+    lib.bdssm_block_step.argtypes = [S, P, P, P, P, P, P, P, P, F, P]
+    lib.bdssm_commit.argtypes = [S, P, P, P, P, P, P, P, P, F, P]
+    lib.bdssm_train_scan.argtypes = [S, I, P, P, P, P, P, P, P, P, P, P, Z, F, P]
+    lib.bdssm_full_scan.argtypes = [S, I, P, P, P, P, P, P, P, P, Z, F, P]
+    lib.bdssm_train_scan_blocks.argtypes = [S, I, P, P, P, P, P, P, P, P, F, P]
     lib.bdssm_train_scan_bwd.argtypes = [S, I] + [P] * 17 + [Z, P]
     lib.bdssm_train_scan_blocks_bwd.argtypes = [S, I] + [P] * 16 + [Z, P]
     for f in ("bdssm_prefill", "bdssm_block_step", "bdssm_commit", "bdssm_train_scan",
@@ -144,6 +152,17 @@ def _streams(x, dt, B, C, A, Dskip, need_c=True):
     return batch, T, D, N, code
 
 
+def _fusion(x, D, dt_bias=None, dt_softplus=False, z=None):
+    """Marshal the optional fusions -> (ctypes pointer or None, keep-alive refs)."""
+    if dt_bias is None and not dt_softplus and z is None:
+        return None
+    _check(dt_bias, "dt_bias", torch.float32, (D,))
+    _check(z, "z", x.dtype, tuple(x.shape))
+    f = Fusion(None if dt_bias is None else dt_bias.data_ptr(), 1 if dt_softplus else 0,
+               None if z is None else z.data_ptr())
+    return ctypes.pointer(f)
+
+
 def workspace_bytes(batch, d_inner, T, op, block_len=16, d_state=16, dtype=torch.bfloat16):
     s = _shape(batch, d_inner, d_state, block_len, BF16 if dtype == torch.bfloat16 else F32)
     n = load().bdssm_workspace_bytes(ctypes.byref(s), T, op)
@@ -159,7 +178,7 @@ def _workspace(nbytes, device):
 
 
 def prefill(x, dt, B, C, A, Dskip, block_len, h_init=None, h_cache=None, y=None, want_y=False,
-            ws=None):
+            ws=None, **fusion):
     """Build the prefix cache over a clean context -> (h_cache, y or None)."""
     batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip, need_c=want_y or y is not None)
     want_y = want_y or y is not None
@@ -173,14 +192,15 @@ def prefill(x, dt, B, C, A, Dskip, block_len, h_init=None, h_cache=None, y=None,
     s = _shape(batch, D, N, block_len, code)
     if ws is None:
         ws = _workspace(workspace_bytes(batch, D, T, OP_PREFILL, block_len, N, x.dtype), x.device)
+    fz = _fusion(x, D, **fusion)
     rc = load().bdssm_prefill(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A), _p(Dskip),
                               _p(h_init), _p(h_cache), _p(y), _p(ws),
-                              0 if ws is None else ws.numel(), _stream())
+                              0 if ws is None else ws.numel(), fz, _stream())
     _raise("bdssm_prefill", rc)
     return h_cache, y
 
 
-def block_step(h_cache, x, dt, B, C, A, Dskip, y=None):
+def block_step(h_cache, x, dt, B, C, A, Dskip, y=None, **fusion):
     """One denoising step on the active block (T == block_len) -> y."""
     batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip)
     _check(h_cache, "h_cache", torch.float32, (batch, D, N))
@@ -188,13 +208,14 @@ def block_step(h_cache, x, dt, B, C, A, Dskip, y=None):
         y = torch.empty_like(x)
     _check(y, "y", x.dtype, (batch, T, D))
     s = _shape(batch, D, N, T, code)
+    fz = _fusion(x, D, **fusion)
     rc = load().bdssm_block_step(ctypes.byref(s), _p(h_cache), _p(x), _p(dt), _p(B), _p(C), _p(A),
-                                 _p(Dskip), _p(y), _stream())
+                                 _p(Dskip), _p(y), fz, _stream())
     _raise("bdssm_block_step", rc)
     return y
 
 
-def commit(h_cache, x, dt, B, C, A, Dskip, want_y=False, y=None):
+def commit(h_cache, x, dt, B, C, A, Dskip, want_y=False, y=None, **fusion):
     """Advance the cache over a finished block, in place -> (h_cache, y or None)."""
     want_y = want_y or y is not None
     batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip, need_c=want_y)
@@ -203,14 +224,15 @@ def commit(h_cache, x, dt, B, C, A, Dskip, want_y=False, y=None):
         y = torch.empty_like(x)
     _check(y, "y", x.dtype, (batch, T, D))
     s = _shape(batch, D, N, T, code)
+    fz = _fusion(x, D, **fusion)
     rc = load().bdssm_commit(ctypes.byref(s), _p(h_cache), _p(x), _p(dt), _p(B), _p(C), _p(A),
-                             _p(Dskip), _p(y), _stream())
+                             _p(Dskip), _p(y), fz, _stream())
     _raise("bdssm_commit", rc)
     return h_cache, y
 
 
 def train_scan(x, dt, B, C, A, Dskip, block_len, h_init=None, want_bounds=False, y=None,
-               h_bounds=None, ws=None):
+               h_bounds=None, ws=None, **fusion):
     """All-block training form -> (y, h_bounds or None)."""
     batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip)
     _check(h_init, "h_init", torch.float32, (batch, D, N))
@@ -224,14 +246,15 @@ def train_scan(x, dt, B, C, A, Dskip, block_len, h_init=None, want_bounds=False,
     s = _shape(batch, D, N, block_len, code)
     if ws is None:
         ws = _workspace(workspace_bytes(batch, D, T, OP_TRAIN, block_len, N, x.dtype), x.device)
+    fz = _fusion(x, D, **fusion)
     rc = load().bdssm_train_scan(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A),
                                  _p(Dskip), _p(h_init), _p(y), _p(h_bounds), _p(ws),
-                                 0 if ws is None else ws.numel(), _stream())
+                                 0 if ws is None else ws.numel(), fz, _stream())
     _raise("bdssm_train_scan", rc)
     return y, h_bounds
 
 
-def train_scan_blocks(x, dt, B, C, A, Dskip, block_len, h0_blocks, y=None):
+def train_scan_blocks(x, dt, B, C, A, Dskip, block_len, h0_blocks, y=None, **fusion):
     """Two-stream training form, noisy stream: every block k starts from
     h0_blocks[:, k] ([batch, T/L + 1, D, 16], the h_bounds layout) -> y."""
     batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip)
@@ -240,13 +263,14 @@ def train_scan_blocks(x, dt, B, C, A, Dskip, block_len, h0_blocks, y=None):
         y = torch.empty_like(x)
     _check(y, "y", x.dtype, (batch, T, D))
     s = _shape(batch, D, N, block_len, code)
+    fz = _fusion(x, D, **fusion)
     rc = load().bdssm_train_scan_blocks(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A),
-                                        _p(Dskip), _p(h0_blocks), _p(y), _stream())
+                                        _p(Dskip), _p(h0_blocks), _p(y), fz, _stream())
     _raise("bdssm_train_scan_blocks", rc)
     return y
 
 
-def full_scan(x, dt, B, C, A, Dskip, y=None, ws=None):
+def full_scan(x, dt, B, C, A, Dskip, y=None, ws=None, **fusion):
     """Full-sequence bidirectional baseline (reverse over the whole sequence) -> y."""
     batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip)
     if y is None:
@@ -255,8 +279,9 @@ def full_scan(x, dt, B, C, A, Dskip, y=None, ws=None):
     s = _shape(batch, D, N, 1, code)
     if ws is None:
         ws = _workspace(workspace_bytes(batch, D, T, OP_FULL, 1, N, x.dtype), x.device)
+    fz = _fusion(x, D, **fusion)
     rc = load().bdssm_full_scan(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A), _p(Dskip),
-                                _p(y), _p(ws), 0 if ws is None else ws.numel(), _stream())
+                                _p(y), _p(ws), 0 if ws is None else ws.numel(), fz, _stream())
     _raise("bdssm_full_scan", rc)
     return y
 

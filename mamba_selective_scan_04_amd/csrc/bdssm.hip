@@ -33,7 +33,7 @@ using namespace bdssm_dev;
 
 namespace {
 
-constexpr int kVersion = 10100;   // 1.1.0
+constexpr int kVersion = 10200;   // 1.2.0
 
 // 256 CUs x 4 SIMDs x 8 resident waves (the chunk kernel fits in 64 VGPRs)
 constexpr int64_t kFineWaves = 256 * 4 * 8;
@@ -271,6 +271,20 @@ int check_alias(const bdssm_shape *s, int64_t T, const void *x, const void *dt, 
     return BDSSM_OK;
 }
 
+// Checks of the optional fusion arguments: 16-byte alignment, and no output
+// may overlap dt_bias or z (z is read only when the call produces y).
+int check_fusion(const bdssm_fusion *f, const bdssm_shape *s, int64_t T, bool with_y,
+                 std::initializer_list<Range> outs) {
+    if (f == nullptr) return BDSSM_OK;
+    if (!aligned16(f->dt_bias) || (with_y && !aligned16(f->z))) return BDSSM_ERR_ALIGN;
+    const Range ins[] = {{f->dt_bias, (size_t)s->d_inner * 4},
+                         {with_y ? f->z : nullptr, (size_t)s->batch * T * s->d_inner * esize(s)}};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlaps(o, i)) return BDSSM_ERR_ALIAS;
+    return BDSSM_OK;
+}
+
 int launch_status() {
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? BDSSM_OK : BDSSM_ERR_HIP;
@@ -291,23 +305,61 @@ dim3 grid3(int64_t D, int64_t chunks, int64_t batch) {
 
 // ---------------------------------------------------------------- launchers
 
+// The optional Mamba-1 fusions of one call, resolved from bdssm_fusion.
+struct Fuse {
+    const float *dt_bias = nullptr;
+    int dt_mode = kDtPlain;
+    const void *z = nullptr;
+    bool any() const { return dt_mode != kDtPlain || z != nullptr; }
+};
+
+Fuse resolve_fusion(const bdssm_fusion *f, bool with_y) {
+    Fuse r;
+    if (f == nullptr) return r;
+    r.dt_bias = f->dt_bias;
+    r.dt_mode = f->dt_softplus ? kDtSoftplus : (f->dt_bias != nullptr ? kDtBias : kDtPlain);
+    r.z = with_y ? f->z : nullptr;
+    return r;
+}
+
+template <typename Tin, bool kRev, bool kDirect>
+void launch_chunk_state_k(int dt_mode, dim3 g, const Tin *xp, const Tin *dp, const Tin *bp,
+                          const float *A, const float *h0, float *hout, float *sout, int64_t T,
+                          int64_t D, int64_t Tc, int n_chunks, int c_first, const float *bias,
+                          hipStream_t st) {
+    switch (dt_mode) {
+    case kDtSoftplus:
+        hipLaunchKernelGGL((chunk_state_kernel<Tin, kRev, kDirect, kDtSoftplus>), g, dim3(kWave), 0, st,
+                           xp, dp, bp, A, h0, hout, sout, T, (int)D, Tc, n_chunks, c_first, bias);
+        break;
+    case kDtBias:
+        hipLaunchKernelGGL((chunk_state_kernel<Tin, kRev, kDirect, kDtBias>), g, dim3(kWave), 0, st,
+                           xp, dp, bp, A, h0, hout, sout, T, (int)D, Tc, n_chunks, c_first, bias);
+        break;
+    default:
+        hipLaunchKernelGGL((chunk_state_kernel<Tin, kRev, kDirect, kDtPlain>), g, dim3(kWave), 0, st,
+                           xp, dp, bp, A, h0, hout, sout, T, (int)D, Tc, n_chunks, c_first, bias);
+        break;
+    }
+}
+
 template <typename Tin>
 void launch_chunk_state(bool rev, const void *x, const void *dt, const void *B, const float *A,
                         const float *h0, float *hout, float *sout, int64_t batch, int64_t T,
                         int64_t D, int64_t Tc, int n_chunks, int c_first, int n_launch,
-                        hipStream_t st) {
+                        hipStream_t st, const Fuse &f = Fuse()) {
     if (n_launch <= 0) return;
     const dim3 g = grid3(D, n_launch, batch);
     const Tin *xp = (const Tin *)x, *dp = (const Tin *)dt, *bp = (const Tin *)B;
     if (sout == nullptr)   // direct pass from h0 into hout (one chunk)
-        hipLaunchKernelGGL((chunk_state_kernel<Tin, false, true>), g, dim3(kWave), 0, st, xp, dp, bp,
-                           A, h0, hout, sout, T, (int)D, Tc, n_chunks, c_first);
+        launch_chunk_state_k<Tin, false, true>(f.dt_mode, g, xp, dp, bp, A, h0, hout, sout, T, D, Tc,
+                                               n_chunks, c_first, f.dt_bias, st);
     else if (rev)
-        hipLaunchKernelGGL((chunk_state_kernel<Tin, true, false>), g, dim3(kWave), 0, st, xp, dp, bp,
-                           A, h0, hout, sout, T, (int)D, Tc, n_chunks, c_first);
+        launch_chunk_state_k<Tin, true, false>(f.dt_mode, g, xp, dp, bp, A, h0, hout, sout, T, D, Tc,
+                                               n_chunks, c_first, f.dt_bias, st);
     else
-        hipLaunchKernelGGL((chunk_state_kernel<Tin, false, false>), g, dim3(kWave), 0, st, xp, dp, bp,
-                           A, h0, hout, sout, T, (int)D, Tc, n_chunks, c_first);
+        launch_chunk_state_k<Tin, false, false>(f.dt_mode, g, xp, dp, bp, A, h0, hout, sout, T, D,
+                                                Tc, n_chunks, c_first, f.dt_bias, st);
 }
 
 void launch_carry(bool rev, const float *agg_h, const float *agg_s, const float *A,
@@ -323,20 +375,34 @@ void launch_carry(bool rev, const float *agg_h, const float *agg_s, const float 
                            h_final, (int)batch, (int)D, n_chunks, n_agg, c_low);
 }
 
+template <typename Tin, int L, bool kInit, bool kFuse>
+void launch_bidir_k(dim3 g, const void *x, const void *dt, const void *B, const void *C,
+                    const float *A, const float *Dskip, const float *hin, int64_t hin_bs,
+                    int64_t hin_cs, void *y, float *bounds, float *hout, int64_t T, int64_t D,
+                    int64_t Tc, const float *h0_blocks, const Fuse &f, hipStream_t st) {
+    hipLaunchKernelGGL((bidir_wave_kernel<Tin, L, kInit, kFuse>), g, dim3(4 * kWave), 0, st,
+                       (const Tin *)x, (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip,
+                       hin, hin_bs, hin_cs, (Tin *)y, bounds, hout, T, (int)D, Tc, h0_blocks,
+                       f.dt_bias, f.dt_mode, (const Tin *)f.z);
+}
+
 template <typename Tin, int L>
 void launch_bidir_L(const void *x, const void *dt, const void *B, const void *C, const float *A,
                     const float *Dskip, const float *hin, int64_t hin_bs, int64_t hin_cs, void *y,
                     float *bounds, float *hout, int64_t batch, int64_t T, int64_t D, int64_t Tc,
-                    int n_chunks, const float *h0_blocks, hipStream_t st) {
-    const dim3 g = grid3(D, n_chunks, batch), blk(4 * kWave);
-    if (h0_blocks != nullptr)
-        hipLaunchKernelGGL((bidir_wave_kernel<Tin, L, true>), g, blk, 0, st, (const Tin *)x,
-                           (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip, hin, hin_bs,
-                           hin_cs, (Tin *)y, bounds, hout, T, (int)D, Tc, h0_blocks);
-    else
-        hipLaunchKernelGGL((bidir_wave_kernel<Tin, L, false>), g, blk, 0, st, (const Tin *)x,
-                           (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip, hin, hin_bs,
-                           hin_cs, (Tin *)y, bounds, hout, T, (int)D, Tc, h0_blocks);
+                    int n_chunks, const float *h0_blocks, const Fuse &f, hipStream_t st) {
+    const dim3 g = grid3(D, n_chunks, batch);
+    if (h0_blocks != nullptr) {
+        if (f.any())
+            launch_bidir_k<Tin, L, true, true>(g, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, T, D, Tc, h0_blocks, f, st);
+        else
+            launch_bidir_k<Tin, L, true, false>(g, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, T, D, Tc, h0_blocks, f, st);
+    } else {
+        if (f.any())
+            launch_bidir_k<Tin, L, false, true>(g, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, T, D, Tc, h0_blocks, f, st);
+        else
+            launch_bidir_k<Tin, L, false, false>(g, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, T, D, Tc, h0_blocks, f, st);
+    }
 }
 
 template <typename Tin>
@@ -344,29 +410,41 @@ void launch_bidir(int64_t L, const void *x, const void *dt, const void *B, const
                   const float *A, const float *Dskip, const float *hin, int64_t hin_bs,
                   int64_t hin_cs, void *y, float *bounds, float *hout, int64_t batch, int64_t T,
                   int64_t D, int64_t Tc, int n_chunks, hipStream_t st,
-                  const float *h0_blocks = nullptr) {
+                  const float *h0_blocks = nullptr, const Fuse &f = Fuse()) {
     switch (L) {
-    case 1: launch_bidir_L<Tin, 1>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, st); break;
-    case 2: launch_bidir_L<Tin, 2>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, st); break;
-    case 4: launch_bidir_L<Tin, 4>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, st); break;
-    case 8: launch_bidir_L<Tin, 8>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, st); break;
-    default: launch_bidir_L<Tin, 16>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, st); break;
+    case 1: launch_bidir_L<Tin, 1>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
+    case 2: launch_bidir_L<Tin, 2>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
+    case 4: launch_bidir_L<Tin, 4>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
+    case 8: launch_bidir_L<Tin, 8>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
+    default: launch_bidir_L<Tin, 16>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
     }
+}
+
+template <typename Tin, bool kRev>
+void launch_sweep_k(dim3 g, const void *x, const void *dt, const void *B, const void *C,
+                    const float *A, const float *Dskip, const float *hin, float *yf, void *y,
+                    int64_t T, int64_t D, int64_t Tc, int n_chunks, const Fuse &f, hipStream_t st) {
+    const Tin *zp = (const Tin *)f.z;
+#define BDSSM_SWEEP(KDT)                                                                          \
+    hipLaunchKernelGGL((sweep_output_kernel<Tin, kRev, KDT>), g, dim3(kWave), 0, st, (const Tin *)x, \
+                       (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip, hin, yf, (Tin *)y, \
+                       T, (int)D, Tc, n_chunks, f.dt_bias, zp)
+    switch (f.dt_mode) {
+    case kDtSoftplus: BDSSM_SWEEP(kDtSoftplus); break;
+    case kDtBias: BDSSM_SWEEP(kDtBias); break;
+    default: BDSSM_SWEEP(kDtPlain); break;
+    }
+#undef BDSSM_SWEEP
 }
 
 template <typename Tin>
 void launch_sweep(bool rev, const void *x, const void *dt, const void *B, const void *C,
                   const float *A, const float *Dskip, const float *hin, float *yf, void *y,
-                  int64_t batch, int64_t T, int64_t D, int64_t Tc, int n_chunks, hipStream_t st) {
+                  int64_t batch, int64_t T, int64_t D, int64_t Tc, int n_chunks, hipStream_t st,
+                  const Fuse &f = Fuse()) {
     const dim3 g = grid3(D, n_chunks, batch);
-    if (rev)
-        hipLaunchKernelGGL((sweep_output_kernel<Tin, true>), g, dim3(kWave), 0, st, (const Tin *)x,
-                           (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip, hin, yf,
-                           (Tin *)y, T, (int)D, Tc, n_chunks);
-    else
-        hipLaunchKernelGGL((sweep_output_kernel<Tin, false>), g, dim3(kWave), 0, st, (const Tin *)x,
-                           (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip, hin, yf,
-                           (Tin *)y, T, (int)D, Tc, n_chunks);
+    if (rev) launch_sweep_k<Tin, true>(g, x, dt, B, C, A, Dskip, hin, yf, y, T, D, Tc, n_chunks, f, st);
+    else launch_sweep_k<Tin, false>(g, x, dt, B, C, A, Dskip, hin, yf, y, T, D, Tc, n_chunks, f, st);
 }
 
 template <typename Tin>
@@ -424,16 +502,16 @@ void launch_bwd_reduce(const BwdWorkspace &w, void *dB, void *dC, float *dA, flo
 template <typename Tin>
 void run_state_only(const bdssm_shape *s, int64_t T, const void *x, const void *dt, const void *B,
                     const float *A, const float *h_init, float *h_final, const Workspace &w,
-                    const Plan &p, hipStream_t st) {
+                    const Plan &p, hipStream_t st, const Fuse &f = Fuse()) {
     const int64_t batch = s->batch, D = s->d_inner;
     if (p.n_fine == 1) {
         // one chunk: scan directly from h_init into h_final (same-lane read then write)
         launch_chunk_state<Tin>(false, x, dt, B, A, h_init, h_final, nullptr, batch, T, D,
-                                p.fine_len, 1, 0, 1, st);
+                                p.fine_len, 1, 0, 1, st, f);
         return;
     }
     launch_chunk_state<Tin>(false, x, dt, B, A, nullptr, w.agg_h, w.agg_s, batch, T, D,
-                            p.fine_len, p.n_fine, 0, p.n_fine, st);
+                            p.fine_len, p.n_fine, 0, p.n_fine, st, f);
     launch_carry(false, w.agg_h, w.agg_s, A, h_init, nullptr, h_final, batch, D, p.n_fine,
                  p.n_fine, st);
 }
@@ -443,41 +521,41 @@ template <typename Tin>
 void run_bidirectional(const bdssm_shape *s, int64_t T, const void *x, const void *dt,
                        const void *B, const void *C, const float *A, const float *Dskip,
                        const float *h_init, void *y, float *bounds, float *h_final,
-                       const Workspace &w, const Plan &p, hipStream_t st) {
+                       const Workspace &w, const Plan &p, hipStream_t st, const Fuse &f = Fuse()) {
     const int64_t batch = s->batch, D = s->d_inner;
     const int64_t hs = D * kStates;
     if (p.n_coarse == 1) {
         launch_bidir<Tin>(s->block_len, x, dt, B, C, A, Dskip, h_init, hs, 0, y, bounds, h_final,
-                          batch, T, D, p.fine_len * p.n_fine, 1, st);
+                          batch, T, D, p.fine_len * p.n_fine, 1, st, nullptr, f);
         return;
     }
     // aggregates of every fine chunk before the last coarse chunk, then the carry
     const int n_agg = (p.n_coarse - 1) * p.per_coarse;
     launch_chunk_state<Tin>(false, x, dt, B, A, nullptr, w.agg_h, w.agg_s, batch, T, D,
-                            p.fine_len, p.n_fine, 0, n_agg, st);
+                            p.fine_len, p.n_fine, 0, n_agg, st, f);
     launch_carry(false, w.agg_h, w.agg_s, A, h_init, w.h_in, nullptr, batch, D, p.n_fine, n_agg,
                  st);
     launch_bidir<Tin>(s->block_len, x, dt, B, C, A, Dskip, w.h_in, (int64_t)p.n_fine * hs,
                       (int64_t)p.per_coarse * hs, y, bounds, h_final, batch, T, D,
-                      p.fine_len * p.per_coarse, p.n_coarse, st);
+                      p.fine_len * p.per_coarse, p.n_coarse, st, nullptr, f);
 }
 
 template <typename Tin>
 void run_full(const bdssm_shape *s, int64_t T, const void *x, const void *dt, const void *B,
               const void *C, const float *A, const float *Dskip, void *y, const Workspace &w,
-              const Plan &p, hipStream_t st) {
+              const Plan &p, hipStream_t st, const Fuse &f = Fuse()) {
     const int64_t batch = s->batch, D = s->d_inner;
     const int nf = p.n_fine;
     // forward: aggregates of chunks 0..nf-2, incoming states of all chunks
     launch_chunk_state<Tin>(false, x, dt, B, A, nullptr, w.agg_h, w.agg_s, batch, T, D,
-                            p.fine_len, nf, 0, nf - 1, st);
+                            p.fine_len, nf, 0, nf - 1, st, f);
     launch_carry(false, w.agg_h, w.agg_s, A, nullptr, w.h_in, nullptr, batch, D, nf, nf - 1, st);
     // reverse: aggregates of chunks 1..nf-1 (scanned right to left), incoming states
     launch_chunk_state<Tin>(true, x, dt, B, A, nullptr, w.ragg_h, w.ragg_s, batch, T, D,
-                            p.fine_len, nf, 1, nf - 1, st);
+                            p.fine_len, nf, 1, nf - 1, st, f);
     launch_carry(true, w.ragg_h, w.ragg_s, A, nullptr, w.hr_in, nullptr, batch, D, nf, nf, st);
-    launch_sweep<Tin>(false, x, dt, B, C, A, Dskip, w.h_in, w.yf, y, batch, T, D, p.fine_len, nf, st);
-    launch_sweep<Tin>(true, x, dt, B, C, A, Dskip, w.hr_in, w.yf, y, batch, T, D, p.fine_len, nf, st);
+    launch_sweep<Tin>(false, x, dt, B, C, A, Dskip, w.h_in, w.yf, y, batch, T, D, p.fine_len, nf, st, f);
+    launch_sweep<Tin>(true, x, dt, B, C, A, Dskip, w.hr_in, w.yf, y, batch, T, D, p.fine_len, nf, st, f);
 }
 
 }  // namespace
@@ -523,7 +601,7 @@ size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T, int op) {
 int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const void *dt,
                   const void *B, const void *C, const float *A, const float *Dskip,
                   const float *h_init, float *h_cache, void *y, void *ws, size_t ws_bytes,
-                  void *stream) {
+                  const bdssm_fusion *fusion, void *stream) {
     int rc = check_shape(shape);
     if (rc) return rc;
     if (t_ctx < 0 || t_ctx % shape->block_len != 0) return BDSSM_ERR_SHAPE;
@@ -543,6 +621,9 @@ int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const 
     if (h_init && h_init != h_cache && overlaps({h_init, nstate}, {h_cache, nstate}))
         return BDSSM_ERR_ALIAS;
     if (h_init && overlaps({h_init, nstate}, {y, ny})) return BDSSM_ERR_ALIAS;
+    rc = check_fusion(fusion, shape, t_ctx, with_y, {Range{h_cache, nstate}, Range{y, ny}, Range{ws, ws_bytes}});
+    if (rc) return rc;
+    const Fuse f = resolve_fusion(fusion, with_y);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (t_ctx == 0) return copy_or_zero(h_init, h_cache, batch * D * kStates, st);
     const Plan p = make_plan(batch, D, t_ctx);
@@ -557,18 +638,18 @@ int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const 
     const Workspace w = layout_ws(ws, batch, D, t_ctx, p, BDSSM_OP_PREFILL);
     (void)hipGetLastError();
     if (shape->dtype == BDSSM_BF16) {
-        if (with_y) run_bidirectional<uint16_t>(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, y, nullptr, h_cache, w, p, st);
-        else run_state_only<uint16_t>(shape, t_ctx, x, dt, B, A, h_init, h_cache, w, p, st);
+        if (with_y) run_bidirectional<uint16_t>(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, y, nullptr, h_cache, w, p, st, f);
+        else run_state_only<uint16_t>(shape, t_ctx, x, dt, B, A, h_init, h_cache, w, p, st, f);
     } else {
-        if (with_y) run_bidirectional<float>(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, y, nullptr, h_cache, w, p, st);
-        else run_state_only<float>(shape, t_ctx, x, dt, B, A, h_init, h_cache, w, p, st);
+        if (with_y) run_bidirectional<float>(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, y, nullptr, h_cache, w, p, st, f);
+        else run_state_only<float>(shape, t_ctx, x, dt, B, A, h_init, h_cache, w, p, st, f);
     }
     return launch_status();
 }
 
 int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void *x,
                      const void *dt, const void *B, const void *C, const float *A,
-                     const float *Dskip, void *y, void *stream) {
+                     const float *Dskip, void *y, const bdssm_fusion *fusion, void *stream) {
     int rc = check_shape(shape);
     if (rc) return rc;
     const int64_t L = shape->block_len;
@@ -581,18 +662,21 @@ int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void 
     rc = check_alias(shape, L, x, dt, B, C, A, Dskip, h_cache,
                      {Range{y, (size_t)batch * L * D * esize(shape)}});
     if (rc) return rc;
+    rc = check_fusion(fusion, shape, L, true, {Range{y, (size_t)batch * L * D * esize(shape)}});
+    if (rc) return rc;
+    const Fuse f = resolve_fusion(fusion, true);
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (shape->dtype == BDSSM_BF16)
-        launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, nullptr, batch, L, D, kGroup, 1, st);
+        launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, nullptr, batch, L, D, kGroup, 1, st, nullptr, f);
     else
-        launch_bidir<float>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, nullptr, batch, L, D, kGroup, 1, st);
+        launch_bidir<float>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, nullptr, batch, L, D, kGroup, 1, st, nullptr, f);
     return launch_status();
 }
 
 int bdssm_commit(const bdssm_shape *shape, float *h_cache, const void *x, const void *dt,
                  const void *B, const void *C, const float *A, const float *Dskip, void *y,
-                 void *stream) {
+                 const bdssm_fusion *fusion, void *stream) {
     int rc = check_shape(shape);
     if (rc) return rc;
     const int64_t L = shape->block_len;
@@ -607,14 +691,18 @@ int bdssm_commit(const bdssm_shape *shape, float *h_cache, const void *x, const 
                      {Range{h_cache, (size_t)batch * D * kStates * 4},
                       Range{y, (size_t)batch * L * D * esize(shape)}});
     if (rc) return rc;
+    rc = check_fusion(fusion, shape, L, with_y, {Range{h_cache, (size_t)batch * D * kStates * 4},
+                                                 Range{y, (size_t)batch * L * D * esize(shape)}});
+    if (rc) return rc;
+    const Fuse f = resolve_fusion(fusion, with_y);
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (shape->dtype == BDSSM_BF16) {
-        if (with_y) launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, h_cache, batch, L, D, kGroup, 1, st);
-        else launch_chunk_state<uint16_t>(false, x, dt, B, A, h_cache, h_cache, nullptr, batch, L, D, kGroup, 1, 0, 1, st);
+        if (with_y) launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, h_cache, batch, L, D, kGroup, 1, st, nullptr, f);
+        else launch_chunk_state<uint16_t>(false, x, dt, B, A, h_cache, h_cache, nullptr, batch, L, D, kGroup, 1, 0, 1, st, f);
     } else {
-        if (with_y) launch_bidir<float>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, h_cache, batch, L, D, kGroup, 1, st);
-        else launch_chunk_state<float>(false, x, dt, B, A, h_cache, h_cache, nullptr, batch, L, D, kGroup, 1, 0, 1, st);
+        if (with_y) launch_bidir<float>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, h_cache, batch, L, D, kGroup, 1, st, nullptr, f);
+        else launch_chunk_state<float>(false, x, dt, B, A, h_cache, h_cache, nullptr, batch, L, D, kGroup, 1, 0, 1, st, f);
     }
     return launch_status();
 }
@@ -622,7 +710,7 @@ int bdssm_commit(const bdssm_shape *shape, float *h_cache, const void *x, const 
 int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
                      const void *B, const void *C, const float *A, const float *Dskip,
                      const float *h_init, void *y, float *h_bounds, void *ws, size_t ws_bytes,
-                     void *stream) {
+                     const bdssm_fusion *fusion, void *stream) {
     int rc = check_shape(shape);
     if (rc) return rc;
     if (T < 0 || T % shape->block_len != 0) return BDSSM_ERR_SHAPE;
@@ -640,6 +728,10 @@ int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const v
                      {Range{y, (size_t)batch * T * D * esize(shape)}, Range{h_bounds, nbnd},
                       Range{T > 0 ? ws : nullptr, probe.bytes}});
     if (rc) return rc;
+    rc = check_fusion(fusion, shape, T, true, {Range{y, (size_t)batch * T * D * esize(shape)},
+                                               Range{h_bounds, nbnd}, Range{T > 0 ? ws : nullptr, probe.bytes}});
+    if (rc) return rc;
+    const Fuse f = resolve_fusion(fusion, true);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (T == 0) {
         if (h_bounds == nullptr) return BDSSM_OK;
@@ -649,15 +741,16 @@ int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const v
     const Workspace w = layout_ws(ws, batch, D, T, p, BDSSM_OP_TRAIN);
     (void)hipGetLastError();
     if (shape->dtype == BDSSM_BF16)
-        run_bidirectional<uint16_t>(shape, T, x, dt, B, C, A, Dskip, h_init, y, h_bounds, nullptr, w, p, st);
+        run_bidirectional<uint16_t>(shape, T, x, dt, B, C, A, Dskip, h_init, y, h_bounds, nullptr, w, p, st, f);
     else
-        run_bidirectional<float>(shape, T, x, dt, B, C, A, Dskip, h_init, y, h_bounds, nullptr, w, p, st);
+        run_bidirectional<float>(shape, T, x, dt, B, C, A, Dskip, h_init, y, h_bounds, nullptr, w, p, st, f);
     return launch_status();
 }
 
 int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
                             const void *B, const void *C, const float *A, const float *Dskip,
-                            const float *h0_blocks, void *y, void *stream) {
+                            const float *h0_blocks, void *y, const bdssm_fusion *fusion,
+                            void *stream) {
     int rc = check_shape(shape);
     if (rc) return rc;
     if (T < 0 || T % shape->block_len != 0) return BDSSM_ERR_SHAPE;
@@ -672,20 +765,23 @@ int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, 
                      {Range{y, (size_t)batch * T * D * esize(shape)}});
     if (rc) return rc;
     if (overlaps({y, (size_t)batch * T * D * esize(shape)}, {h0_blocks, nb0})) return BDSSM_ERR_ALIAS;
+    rc = check_fusion(fusion, shape, T, true, {Range{y, (size_t)batch * T * D * esize(shape)}});
+    if (rc) return rc;
+    const Fuse f = resolve_fusion(fusion, true);
     int64_t tc, nc;
     if (!blocks_plan(batch, D, T, &tc, &nc)) return BDSSM_ERR_SHAPE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (shape->dtype == BDSSM_BF16)
-        launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, nullptr, 0, 0, y, nullptr, nullptr, batch, T, D, tc, (int)nc, st, h0_blocks);
+        launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, nullptr, 0, 0, y, nullptr, nullptr, batch, T, D, tc, (int)nc, st, h0_blocks, f);
     else
-        launch_bidir<float>(L, x, dt, B, C, A, Dskip, nullptr, 0, 0, y, nullptr, nullptr, batch, T, D, tc, (int)nc, st, h0_blocks);
+        launch_bidir<float>(L, x, dt, B, C, A, Dskip, nullptr, 0, 0, y, nullptr, nullptr, batch, T, D, tc, (int)nc, st, h0_blocks, f);
     return launch_status();
 }
 
 int bdssm_full_scan(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
                     const void *B, const void *C, const float *A, const float *Dskip, void *y,
-                    void *ws, size_t ws_bytes, void *stream) {
+                    void *ws, size_t ws_bytes, const bdssm_fusion *fusion, void *stream) {
     if (shape == nullptr) return BDSSM_ERR_NULL;
     // the block length does not apply; validate the rest with L = 1
     bdssm_shape s1 = *shape;
@@ -705,11 +801,14 @@ int bdssm_full_scan(const bdssm_shape *shape, int64_t T, const void *x, const vo
     rc = check_alias(&s1, T, x, dt, B, C, A, Dskip, nullptr,
                      {Range{y, (size_t)batch * T * D * esize(&s1)}, Range{ws, probe.bytes}});
     if (rc) return rc;
+    rc = check_fusion(fusion, &s1, T, true, {Range{y, (size_t)batch * T * D * esize(&s1)}, Range{ws, probe.bytes}});
+    if (rc) return rc;
+    const Fuse f = resolve_fusion(fusion, true);
     const Workspace w = layout_ws(ws, batch, D, T, p, BDSSM_OP_FULL);
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    if (s1.dtype == BDSSM_BF16) run_full<uint16_t>(&s1, T, x, dt, B, C, A, Dskip, y, w, p, st);
-    else run_full<float>(&s1, T, x, dt, B, C, A, Dskip, y, w, p, st);
+    if (s1.dtype == BDSSM_BF16) run_full<uint16_t>(&s1, T, x, dt, B, C, A, Dskip, y, w, p, st, f);
+    else run_full<float>(&s1, T, x, dt, B, C, A, Dskip, y, w, p, st, f);
     return launch_status();
 }
 

@@ -59,6 +59,34 @@ template <> __device__ __forceinline__ uint16_t narrow<uint16_t>(float v) {
 
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 
+// ------------------------------------------------- optional Mamba-1 fusions
+// The step size may arrive raw: dt = dt_raw + bias (kDtBias), optionally
+// through softplus (kDtSoftplus); the output may be gated by silu(z).
+constexpr int kDtPlain = 0, kDtBias = 1, kDtSoftplus = 2;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|).  log1p(w) uses the
+// hardware log2 with Goldberg's correction (1991, Theorem 4):
+// u = fl(1 + w), log1p(w) = log(u) * w / (u - 1), and = w when u == 1; this
+// keeps the relative accuracy for small w that log(1 + w) alone would lose.
+__device__ __forceinline__ float softplus_f(float v) {
+    const float w = fast_exp2(-__builtin_fabsf(v) * kLog2e);
+    const float u = 1.f + w;
+    const float l1p = (u == 1.f) ? w : __builtin_amdgcn_logf(u) * kLn2 * (w * __builtin_amdgcn_rcpf(u - 1.f));
+    return __builtin_fmaxf(v, 0.f) + l1p;
+}
+
+template <int kDt> __device__ __forceinline__ float step_size(float raw, float bias) {
+    if constexpr (kDt == kDtPlain) return raw;
+    else if constexpr (kDt == kDtBias) return raw + bias;
+    else return softplus_f(raw + bias);
+}
+
+// silu(z) = z / (1 + e^-z)
+__device__ __forceinline__ float silu_f(float z) {
+    return z * __builtin_amdgcn_rcpf(1.f + fast_exp2(-z * kLog2e));
+}
+
 // States 2q and 2q+1 of a B or C row.  The row is read as 32-bit words: with a
 // wave-uniform address that lets the compiler use scalar loads (s_load_dwordxN)
 // and unpack bf16 pairs on the scalar unit instead of spending VALU slots.
@@ -155,11 +183,13 @@ template <> __device__ __forceinline__ void Rows<float>::store(int k, float v) c
 // kernel within 64 VGPRs, i.e. 8 waves per SIMD).
 // grid = (ceil(D/64), chunks launched, batch), block = 64.
 // hout / sout are indexed by chunk id c = c_first + blockIdx.y over n_chunks.
-template <typename Tin, bool kRev, bool kDirect>
+// kDt: how dt is formed from the dt stream (kDtPlain / kDtBias / kDtSoftplus,
+// with the per-channel dt_bias, which may be null).
+template <typename Tin, bool kRev, bool kDirect, int kDt = kDtPlain>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(8))) void chunk_state_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const float *__restrict__ A, const float *h0, float *hout, float *__restrict__ sout,
-    int64_t T, int D, int64_t Tc, int n_chunks, int c_first)
+    int64_t T, int D, int64_t Tc, int n_chunks, int c_first, const float *__restrict__ dt_bias)
 {
     constexpr int U = 6;                      // tokens per pipeline stage
     const int lane = threadIdx.x;
@@ -194,6 +224,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(8))) void
         for (int n = 0; n < kStates; ++n) h[n] = 0.f;
     }
     float S = 0.f;
+    const float bias = (kDt != kDtPlain && dt_bias != nullptr) ? dt_bias[d] : 0.f;
     const int64_t first = (int64_t)b * T + t_begin;           // first row of the chunk
     const Rows<Tin> xs(x + first * D, len, D, d);
     const Rows<Tin> ds(dt + first * D, len, D, d);
@@ -205,7 +236,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(8))) void
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             if (i < count) {
-                const float dl = widen(dr[i]);
+                const float dl = step_size<kDt>(widen(dr[i]), bias);
                 const float dx = dl * widen(xr[i]);
                 S += dl;
                 const Tin *brow = bs + (int64_t)pos(k0 + i) * kStates;
@@ -342,21 +373,27 @@ __global__ __launch_bounds__(256) void carry_kernel(
 // hout (optional): forward state after token T-1 (written by the last chunk;
 // may alias hin when there is a single chunk: each lane reads its own states
 // before it writes them).
+// kFuse (Mamba-1 fusions): dt is formed from the dt stream as step_size<dt_mode>
+// with dt_bias (each lane transforms the 4 dt values it loaded, in LDS, once
+// per token and channel), and when z is given the output is multiplied by
+// silu(z) (z rows are loaded with x and dt).
 // grid = (ceil(D/64), chunks, batch), block = 256 (4 independent waves).
-template <typename Tin, int L, bool kBlockInit>
+template <typename Tin, int L, bool kBlockInit, bool kFuse = false>
 __global__ __launch_bounds__(4 * kWave) void bidir_wave_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const Tin *__restrict__ Cm, const float *__restrict__ A, const float *__restrict__ Dskip,
     const float *hin, int64_t hin_bs, int64_t hin_cs,
     Tin *__restrict__ y, float *__restrict__ bounds, float *hout,
-    int64_t T, int D, int64_t Tc, const float *__restrict__ h0_blocks)
+    int64_t T, int D, int64_t Tc, const float *__restrict__ h0_blocks,
+    const float *__restrict__ dt_bias, int dt_mode, const Tin *__restrict__ z)
 {
     constexpr int P = 4;                      // states per lane
     constexpr int CW = kWave / P;             // channels per wave (16)
     constexpr int ES = sizeof(Tin);
+    constexpr int NS = kFuse ? 3 : 2;         // token-row streams staged per group
     static_assert(kGroup % L == 0, "block length must divide the token group");
-    // per wave: [x|dt][4 loads][64]  and  [B|C][4 loads][64]  and  fp32 B/C rows
-    __shared__ uint32_t xdA[4][2][4][kWave], xdB[4][2][4][kWave];
+    // per wave: [x|dt(|z)][4 loads][64]  and  [B|C][4 loads][64]  and  fp32 B/C rows
+    __shared__ uint32_t xdA[4][NS][4][kWave], xdB[4][NS][4][kWave];
     __shared__ uint32_t bcrA[4][2][4][kWave], bcrB[4][2][4][kWave];
     __shared__ float bcfA[4][kGroup][2][kStates], bcfB[4][kGroup][2][kStates];
 
@@ -407,6 +444,9 @@ __global__ __launch_bounds__(4 * kWave) void bidir_wave_kernel(
     // and channel (or state) l % 16
     const int ld_tok = lane >> 4, ld_col = lane & 15;
     const int ld_ch = (d_w0 + ld_col < D) ? d_w0 + ld_col : D - 1;
+    const bool gate = kFuse && z != nullptr;
+    const Rows<Tin> zs((gate ? z : x) + first * D, len, D, 0);
+    const float ld_bias = (kFuse && dt_bias != nullptr) ? dt_bias[ld_ch] : 0.f;
 
     auto issue = [&](auto &xd, auto &bcr, int k0) {
 #pragma unroll
@@ -415,6 +455,9 @@ __global__ __launch_bounds__(4 * kWave) void bidir_wave_kernel(
             k = k < len ? k : len - 1;
             load_to_lds<ES>(xs.rsrc, &xd[w][0][j][0], ld_ch * ES + k * xs.pitch, 0);
             load_to_lds<ES>(ds.rsrc, &xd[w][1][j][0], ld_ch * ES + k * ds.pitch, 0);
+            if constexpr (kFuse) {
+                if (gate) load_to_lds<ES>(zs.rsrc, &xd[w][NS - 1][j][0], ld_ch * ES + k * zs.pitch, 0);
+            }
             load_to_lds<ES>(brs, &bcr[w][0][j][0], (k * kStates + ld_col) * ES, 0);
             load_to_lds<ES>(crs, &bcr[w][1][j][0], (k * kStates + ld_col) * ES, 0);
         }
@@ -422,15 +465,29 @@ __global__ __launch_bounds__(4 * kWave) void bidir_wave_kernel(
     auto elem = [&](uint32_t v) -> float {
         return ES == 2 ? __uint_as_float(v << 16) : __uint_as_float(v);
     };
-    // wait for this wave's own LDS loads (vmcnt = 0), then widen B / C
-    auto widen_bc = [&](auto &bcr, auto &bcf) {
+    // wait for this wave's own LDS loads (vmcnt = 0), then widen B / C (and,
+    // with the fusions, turn the lane's own 4 raw dt values into fp32 dt)
+    auto widen_bc = [&](auto &bcr, auto &bcf, auto &xd) {
         __builtin_amdgcn_s_waitcnt(0x0F70);
 #pragma unroll
         for (int which = 0; which < 2; ++which)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 bcf[w][4 * j + ld_tok][which][ld_col] = elem(bcr[w][which][j][lane]);
+        if constexpr (kFuse) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float raw = elem(xd[w][1][j][lane]);
+                float v;
+                if (dt_mode == kDtSoftplus) v = step_size<kDtSoftplus>(raw, ld_bias);
+                else if (dt_mode == kDtBias) v = step_size<kDtBias>(raw, ld_bias);
+                else v = raw;
+                xd[w][1][j][lane] = __float_as_uint(v);
+            }
+        }
     };
+    // dt as stored in LDS: raw stream bits, or fp32 after the fusion transform
+    auto dt_elem = [&](uint32_t v) -> float { return kFuse ? __uint_as_float(v) : elem(v); };
     // quad reduce-scatter helpers (DPP within groups of 4 lanes)
     auto xor2 = [](float v) {
         return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
@@ -449,7 +506,7 @@ __global__ __launch_bounds__(4 * kWave) void bidir_wave_kernel(
 #pragma unroll
         for (int i = 0; i < kGroup; ++i) {
             const float xv = elem(xd[w][0][i >> 2][(i & 3) * CW + cl]);
-            const float dv = elem(xd[w][1][i >> 2][(i & 3) * CW + cl]);
+            const float dv = dt_elem(xd[w][1][i >> 2][(i & 3) * CW + cl]);
             dl[i] = i < nvalid ? dv : 0.f;
             dx[i] = dl[i] * xv;
             ya[i] = 0.f;
@@ -531,14 +588,17 @@ __global__ __launch_bounds__(4 * kWave) void bidir_wave_kernel(
         for (int q = 0; q < 4; ++q) {
             const int i = 4 * g + q;
             const float xv = elem(xd[w][0][g][q * CW + cl]);
-            const float tot = __builtin_fmaf(dsk, xv, r4[q]);
+            float tot = __builtin_fmaf(dsk, xv, r4[q]);
+            if constexpr (kFuse) {
+                if (gate) tot *= silu_f(elem(xd[w][NS - 1][g][q * CW + cl]));
+            }
             if (live && i < nvalid) ylane[(int64_t)(k0 + i) * D] = narrow<Tin>(tot);
         }
-        if (more) widen_bc(bcrn, bcfn);
+        if (more) widen_bc(bcrn, bcfn, xdn);
     };
 
     issue(xdA, bcrA, 0);
-    widen_bc(bcrA, bcfA);
+    widen_bc(bcrA, bcfA, xdA);
     for (int k0 = 0; k0 < len; k0 += 2 * kGroup) {
         group(xdA, bcfA, xdB, bcrB, bcfB, k0);
         if (k0 + kGroup < len) group(xdB, bcfB, xdA, bcrA, bcfA, k0 + kGroup);
@@ -551,14 +611,16 @@ __global__ __launch_bounds__(4 * kWave) void bidir_wave_kernel(
 // channel, 16 states.  Forward (kRev = false): from the chunk's incoming
 // forward state, writes yf_t = sum_n C_t h_t to an fp32 buffer.  Reverse:
 // from the state entering the chunk from its right end, walks the chunk
-// backwards and writes y_t = yf_t + sum_n C_t h_t + Dskip x_t.
+// backwards and writes y_t = yf_t + sum_n C_t h_t + Dskip x_t (times silu(z_t)
+// when the gate z is given).  kDt / dt_bias form dt as in chunk_state_kernel.
 // grid = (ceil(D/64), chunks, batch), block = 64.
-template <typename Tin, bool kRev>
+template <typename Tin, bool kRev, int kDt = kDtPlain>
 __global__ __launch_bounds__(kWave) void sweep_output_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const Tin *__restrict__ Cm, const float *__restrict__ A, const float *__restrict__ Dskip,
     const float *__restrict__ hin, float *__restrict__ yf, Tin *__restrict__ y,
-    int64_t T, int D, int64_t Tc, int n_chunks)
+    int64_t T, int D, int64_t Tc, int n_chunks, const float *__restrict__ dt_bias,
+    const Tin *__restrict__ z)
 {
     constexpr int U = 4;                      // tokens per pipeline stage
     const int lane = threadIdx.x;
@@ -585,10 +647,13 @@ __global__ __launch_bounds__(kWave) void sweep_output_kernel(
         }
     }
     const float dsk = Dskip[d];
+    const float bias = (kDt != kDtPlain && dt_bias != nullptr) ? dt_bias[d] : 0.f;
+    const bool gate = kRev && z != nullptr;
     const int64_t first = (int64_t)b * T + t_begin;
     const Rows<Tin> xs(x + first * D, len, D, d);
     const Rows<Tin> ds(dt + first * D, len, D, d);
     const Rows<Tin> ys(y + first * D, len, D, d);
+    const Rows<Tin> zs((gate ? z : x) + first * D, len, D, d);
     const Rows<float> fs(yf + first * D, len, D, d);
     const Tin *bs = Bm + first * kStates;
     const Tin *cs = Cm + first * kStates;
@@ -600,7 +665,7 @@ __global__ __launch_bounds__(kWave) void sweep_output_kernel(
             if (i < count) {
                 const int p = pos(k0 + i);
                 const float xv = widen(xr[i]);
-                const float dl = widen(dr[i]);
+                const float dl = step_size<kDt>(widen(dr[i]), bias);
                 const float dx = dl * xv;
                 const Tin *brow = bs + (int64_t)p * kStates;
                 const Tin *crow = cs + (int64_t)p * kStates;
@@ -618,7 +683,8 @@ __global__ __launch_bounds__(kWave) void sweep_output_kernel(
                 if (!kRev) {
                     if (live) fs.store(p, acc);
                 } else {
-                    const float tot = yr[i] + acc + dsk * xv;
+                    float tot = yr[i] + acc + dsk * xv;
+                    if (gate) tot *= silu_f(widen(zs.load(p)));
                     if (live) ys.store(p, narrow<Tin>(tot));
                 }
             }

@@ -28,7 +28,7 @@ def test_exports_match_header():
 
 
 def test_version_and_status_strings():
-    assert m.version() == 10100
+    assert m.version() == 10200
     for code in range(-7, 1):
         assert m.status_str(code) not in ("", "unknown status")
     assert m.status_str(-99) == "unknown status"
@@ -53,7 +53,7 @@ def P(v):
 def prefill(s, T, x=FAKE, dt=FAKE + 0x1000, Bm=FAKE + 0x2000, C=FAKE + 0x3000, A=FAKE + 0x4000,
             Ds=FAKE + 0x5000, h_init=None, h_cache=FAKE + 0x6000, y=None, ws=None, ws_bytes=0):
     return lib().bdssm_prefill(ctypes.byref(s), T, P(x), P(dt), P(Bm), P(C), P(A), P(Ds),
-                               P(h_init), P(h_cache), P(y), P(ws), ws_bytes, None)
+                               P(h_init), P(h_cache), P(y), P(ws), ws_bytes, None, None)
 
 
 def test_shape_errors():
@@ -70,7 +70,7 @@ def test_dtype_error():
 
 
 def test_null_errors():
-    assert lib().bdssm_prefill(None, 16, *([None] * 10), 0, None) == -1
+    assert lib().bdssm_prefill(None, 16, *([None] * 10), 0, None, None) == -1
     assert prefill(shape(), 16, x=None) == -1
     assert prefill(shape(), 16, h_cache=None) == -1
     # y requested without C
@@ -101,7 +101,7 @@ def test_alias_error():
     s = shape()
     rc = lib().bdssm_block_step(ctypes.byref(s), P(FAKE), P(FAKE + 0x1000), P(FAKE + 0x2000),
                                 P(FAKE + 0x3000), P(FAKE + 0x4000), P(FAKE + 0x5000),
-                                P(FAKE + 0x6000), P(FAKE), None)
+                                P(FAKE + 0x6000), P(FAKE), None, None)
     assert rc == -7
 
 
@@ -110,7 +110,7 @@ def test_empty_calls_are_noops():
     assert prefill(shape(batch=0), 16, x=None, dt=None, Bm=None, C=None, h_cache=None) == 0
     assert prefill(shape(D=0), 16, x=None, dt=None, Bm=None, C=None, h_cache=None) == 0
     s = shape(batch=0)
-    assert lib().bdssm_full_scan(ctypes.byref(s), 0, *([None] * 8), 0, None) == 0
+    assert lib().bdssm_full_scan(ctypes.byref(s), 0, *([None] * 8), 0, None, None) == 0
 
 
 def test_workspace_sizes():
@@ -183,3 +183,17 @@ def test_backward_workspace_sizes():
     n2 = m.workspace_bytes(8, 1536, 4096, m.OP_BLOCKS_BWD)
     assert 8 * 24 * 4096 * 32 * 4 <= n2 <= n
     assert m.workspace_bytes(1, 64, 0, m.OP_TRAIN_BWD) == 0
+
+
+def test_fusion_argument_errors():
+    f = B.Fusion(MIS, 1, None)                         # misaligned bias
+    s = shape()
+    rc = lib().bdssm_block_step(ctypes.byref(s), P(FAKE), P(FAKE + 0x1000), P(FAKE + 0x2000),
+                                P(FAKE + 0x3000), P(FAKE + 0x4000), P(FAKE + 0x5000),
+                                P(FAKE + 0x6000), P(FAKE + 0x7000), ctypes.byref(f), None)
+    assert rc == -4
+    f = B.Fusion(None, 1, FAKE + 0x7000)               # gate on top of y
+    rc = lib().bdssm_block_step(ctypes.byref(s), P(FAKE), P(FAKE + 0x1000), P(FAKE + 0x2000),
+                                P(FAKE + 0x3000), P(FAKE + 0x4000), P(FAKE + 0x5000),
+                                P(FAKE + 0x6000), P(FAKE + 0x7000), ctypes.byref(f), None)
+    assert rc == -7
