@@ -33,6 +33,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -43,6 +44,10 @@ HBM_PEAK_GBS = 8000.0
 # fp32 VALU issue slots per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
 EXP_SLOTS = 2            # v_exp_f32 issues at half rate on gfx950
+# dt = softplus(dt_raw + bias) per (token, channel): bias add, |v| scale, exp2
+# (2), 1 + w, log2 (2), ln 2 scale, u - 1, rcp (2), two muls, compare, select,
+# max, add
+SOFTPLUS_SLOTS = 17
 NS = 16
 
 
@@ -89,7 +94,7 @@ def committed_traffic(workload, batch, D):
             grid, rd, wr = int(cells[1]), float(cells[5]), float(cells[6])
         except ValueError:
             continue
-        if cells[0].startswith("chunk_state_kernel<") and cells[0].endswith("false, false>"):
+        if re.fullmatch(r"chunk_state_kernel<\w+, false, false(, 0)?>", cells[0]):
             if chunk is None or grid > chunk[0]:
                 chunk = (grid, rd + wr)
         if cells[0] == "carry_kernel<false>" and grid == carry_grid:
@@ -134,6 +139,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (scale for HBM byte counters)")
+    ap.add_argument("--fused", action="store_true",
+                    help="use the Mamba-1 fusions: the dt stream holds the raw step size, "
+                         "dt = softplus(dt_raw + bias) inside the scan, block-step outputs gated by silu(z)")
     ap.add_argument("--crossover", action="store_true",
                     help="sweep the context length (8K..64K, batch 8, d_inner 1536) and report "
                          "block-restricted against full-sequence generation rates")
@@ -169,6 +177,16 @@ def main():
     A, Dskip = synth.params(D, NS, sid, "default", dev)
     steps_in = [synth.step_inputs(batch, L, D, NS, sid, j, dtype, dev) for j in range(S)]
     commit_in = [synth.commit_inputs(batch, L, D, NS, sid, k, dtype, dev) for k in range(nblk)]
+    fz_pf, fz_bs = {}, {}
+    if args.fused:
+        # raw step sizes in place of dt, a per-channel bias, and the gates
+        raw = lambda shape, seed: synth.normal(shape, seed, dev, dtype, mean=-1.0, std=0.5)
+        dt = raw((batch, ctx, D), 1000 * sid + 70)
+        steps_in = [(sx, raw((batch, L, D), 1000 * sid + 71 + j), sb, sc) for j, (sx, _, sb, sc) in enumerate(steps_in)]
+        commit_in = [(cx, raw((batch, L, D), 1000 * sid + 91 + k), cb, cc) for k, (cx, _, cb, cc) in enumerate(commit_in)]
+        bias = synth.normal((D,), 1000 * sid + 72, dev, torch.float32, std=0.3)
+        fz_pf = dict(dt_bias=bias, dt_softplus=True)
+        fz_bs = dict(fz_pf, z=synth.normal((batch, L, D), 1000 * sid + 73, dev, dtype))
     h = torch.empty(batch, D, NS, dtype=torch.float32, device=dev)
     y_blk = torch.empty(batch, L, D, dtype=dtype, device=dev)
     ws = torch.empty(max(1, m.workspace_bytes(batch, D, ctx, m.OP_PREFILL, L, NS, dtype)),
@@ -186,12 +204,12 @@ def main():
         log("[bench] copy calibration: 3 x 1 GiB device copies")
 
     def prefill():
-        m.prefill(x, dt, Bm, Cm, A, Dskip, L, h_cache=h, ws=ws)
+        m.prefill(x, dt, Bm, Cm, A, Dskip, L, h_cache=h, ws=ws, **fz_pf)
 
     def block(k):
         for j in range(S):
-            m.block_step(h, *steps_in[j], A, Dskip, y=y_blk)
-        m.commit(h, *commit_in[k], A, Dskip)
+            m.block_step(h, *steps_in[j], A, Dskip, y=y_blk, **fz_bs)
+        m.commit(h, *commit_in[k], A, Dskip, **fz_pf)
 
     launch = "eager"
     graphs = None
@@ -262,22 +280,27 @@ def main():
     g_bs = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_bs):
         for _ in range(R):
-            m.block_step(h, *bs_x, A, Dskip, y=y_blk)
+            m.block_step(h, *bs_x, A, Dskip, y=y_blk, **fz_bs)
     g_cm = torch.cuda.CUDAGraph()
     hc = h.clone()
     with torch.cuda.graph(g_cm):
         for _ in range(R):
-            m.commit(hc, *commit_in[0], A, Dskip)
+            m.commit(hc, *commit_in[0], A, Dskip, **fz_pf)
     bs_ms = time_calls(g_bs.replay, 4) / R
     cm_ms = time_calls(g_cm.replay, 4) / R
-    bs_eager_ms = time_calls(lambda: m.block_step(h, *bs_x, A, Dskip, y=y_blk), 200)
+    bs_eager_ms = time_calls(lambda: m.block_step(h, *bs_x, A, Dskip, y=y_blk, **fz_bs), 200)
 
-    step_bytes = (bytes_prefill(batch, ctx, D, e)
-                  + nblk * (S * bytes_block_step(batch, L, D, e) + bytes_commit(batch, L, D, e)))
+    # the fused path also reads the bias (4 D bytes per call) and the block
+    # steps' gates (one element per (token, channel))
+    fz_bytes_bs = (batch * L * D * e + 4 * D) if args.fused else 0
+    fz_bytes_pf = 4 * D if args.fused else 0
+    step_bytes = (bytes_prefill(batch, ctx, D, e) + fz_bytes_pf
+                  + nblk * (S * (bytes_block_step(batch, L, D, e) + fz_bytes_bs)
+                            + bytes_commit(batch, L, D, e) + fz_bytes_pf))
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    pf_bytes = bytes_prefill(batch, ctx, D, e)
-    pf_slots = slots_forward(batch, ctx, D)
+    pf_bytes = bytes_prefill(batch, ctx, D, e) + fz_bytes_pf
+    pf_slots = slots_forward(batch, ctx, D) + (batch * ctx * D * SOFTPLUS_SLOTS if args.fused else 0)
     achieved_slots = pf_slots / (pf_ms * 1e-3)
     roofline = {
         "kernel": "prefill: chunk_state_kernel (chunk-local forward scan) + carry_kernel",
@@ -286,9 +309,10 @@ def main():
         "peak": VALU_SLOTS_PER_S / 1e12,
         "unit": "TFLOP/s",
         "op": "fp32 VALU issue slot (mul/FMA 1, v_exp_f32 %d); per (token, channel): "
-              "16 x (exp2 + 2 mul + FMA) + 1 mul" % EXP_SLOTS,
+              "16 x (exp2 + 2 mul + FMA) + 1 mul%s" % (
+                  EXP_SLOTS, " + %d for dt = softplus(dt_raw + bias)" % SOFTPLUS_SLOTS if args.fused else ""),
         "frac": achieved_slots / VALU_SLOTS_PER_S,
-        "traffic": committed_traffic(args.workload, batch, D),
+        "traffic": None if args.fused else committed_traffic(args.workload, batch, D),
         "hbm_achieved_GBs": pf_bytes / (pf_ms * 1e-3) / 1e9,
         "hbm_frac": pf_bytes / (pf_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "launch_ms": pf_ms,
@@ -300,8 +324,8 @@ def main():
         "prefill": {"ms": pf_ms, "tokens_per_s": batch * ctx / (pf_ms * 1e-3),
                     "GBs": pf_bytes / (pf_ms * 1e-3) / 1e9, "bytes": pf_bytes},
         "block_step": {"us_graph": bs_ms * 1e3, "us_eager": bs_eager_ms * 1e3,
-                       "GBs": bytes_block_step(batch, L, D, e) / (bs_ms * 1e-3) / 1e9,
-                       "bytes": bytes_block_step(batch, L, D, e)},
+                       "GBs": (bytes_block_step(batch, L, D, e) + fz_bytes_bs) / (bs_ms * 1e-3) / 1e9,
+                       "bytes": bytes_block_step(batch, L, D, e) + fz_bytes_bs},
         "commit": {"us_graph": cm_ms * 1e3,
                    "GBs": bytes_commit(batch, L, D, e) / (cm_ms * 1e-3) / 1e9,
                    "bytes": bytes_commit(batch, L, D, e)},
@@ -310,7 +334,7 @@ def main():
 
     # ---- contrast: full-sequence bidirectional baseline, rescanned every step
     baseline = None
-    if not args.no_baseline_scan:
+    if not args.no_baseline_scan and not args.fused:
         Tf = ctx + L
         del ws
         xf, dtf, Bf, Cf = synth.stream(batch, Tf, D, NS, sid, 200, dtype, dev)
@@ -328,7 +352,7 @@ def main():
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample of the same step
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.fused:
         cpu = cpu_baseline(x, dt, Bm, Cm, A, Dskip, steps_in, commit_in, L, args.cpu_seconds, e)
 
     line = {
@@ -346,7 +370,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": batch, "d_inner": D, "d_state": NS,
                    "ctx": ctx, "block": L, "denoising_steps": S, "n_blocks": nblk,
-                   "launch": launch},
+                   "launch": launch, "fused": bool(args.fused)},
         "hbm_frac_step": value / HBM_PEAK_GBS,
         "prefill_tokens_per_s": calls["prefill"]["tokens_per_s"],
         "block_step_GBs": calls["block_step"]["GBs"],
@@ -373,13 +397,18 @@ def train_main(args, wl, m, synth, torch):
     x, dt, Bm, Cm = synth.stream(batch, T, D, NS, sid, 0, dtype, dev)
     A, Dskip = synth.params(D, NS, sid, "default", dev)
     y = torch.empty_like(x)
+    fz = {}
+    if args.fused:
+        dt = synth.normal((batch, T, D), 1000 * sid + 70, dev, dtype, mean=-1.0, std=0.5)
+        fz = dict(dt_bias=synth.normal((D,), 1000 * sid + 72, dev, torch.float32, std=0.3),
+                  dt_softplus=True, z=synth.normal((batch, T, D), 1000 * sid + 73, dev, dtype))
     ws = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_TRAIN, L, NS, dtype)),
                      dtype=torch.uint8, device=dev)
     wsf = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_FULL, 1, NS, dtype)),
                       dtype=torch.uint8, device=dev)
 
     def step():
-        m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, ws=ws)
+        m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, ws=ws, **fz)
 
     for _ in range(args.warmup):
         step()
@@ -398,19 +427,19 @@ def train_main(args, wl, m, synth, torch):
     nbytes = bytes_full(batch, T, D, e)
     slots = slots_bidirectional(batch, T, D)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    m.full_scan(x, dt, Bm, Cm, A, Dskip, y=y, ws=wsf)
+    m.full_scan(x, dt, Bm, Cm, A, Dskip, y=y, ws=wsf, **fz)
     a.record(st)
     for _ in range(args.steps):
-        m.full_scan(x, dt, Bm, Cm, A, Dskip, y=y, ws=wsf)
+        m.full_scan(x, dt, Bm, Cm, A, Dskip, y=y, ws=wsf, **fz)
     b.record(st)
     torch.cuda.synchronize()
     full_ms = a.elapsed_time(b) / args.steps
     # two-stream form: the noisy stream scanned from the clean stream's bounds
     bnd = torch.empty(batch, T // L + 1, D, NS, dtype=torch.float32, device=dev)
-    m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, h_bounds=bnd, ws=ws)
+    m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, h_bounds=bnd, ws=ws, **fz)
     a.record(st)
     for _ in range(args.steps):
-        m.train_scan_blocks(x, dt, Bm, Cm, A, Dskip, L, bnd, y=y)
+        m.train_scan_blocks(x, dt, Bm, Cm, A, Dskip, L, bnd, y=y, **fz)
     b.record(st)
     torch.cuda.synchronize()
     blocks_ms = a.elapsed_time(b) / args.steps
@@ -418,11 +447,16 @@ def train_main(args, wl, m, synth, torch):
     # bounds, then the noisy stream scanned block by block from those bounds
     a.record(st)
     for _ in range(args.steps):
-        m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, h_bounds=bnd, ws=ws)
-        m.train_scan_blocks(x, dt, Bm, Cm, A, Dskip, L, bnd, y=y)
+        m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, h_bounds=bnd, ws=ws, **fz)
+        m.train_scan_blocks(x, dt, Bm, Cm, A, Dskip, L, bnd, y=y, **fz)
     b.record(st)
     torch.cuda.synchronize()
     two_ms = a.elapsed_time(b) / args.steps
+    if args.fused:      # the backward entry points differentiate the unfused scan
+        line = train_line(args, batch, D, T, L, dtype, nbytes, slots, ms_per_step, ev_ms,
+                          blocks_ms, full_ms, two_ms, None, None, None, torch)
+        print(json.dumps(line), flush=True)
+        return 0
     # backward passes: continuous form (from the saved block states) and the
     # two-stream form; then one whole all-block training step, forward and
     # backward over both streams
@@ -462,6 +496,16 @@ def train_main(args, wl, m, synth, torch):
     b.record(st)
     torch.cuda.synchronize()
     step_ms = a.elapsed_time(b) / args.steps
+    line = train_line(args, batch, D, T, L, dtype, nbytes, slots, ms_per_step, ev_ms, blocks_ms,
+                      full_ms, two_ms, bwd_ms, bbwd_ms, step_ms, torch)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def train_line(args, batch, D, T, L, dtype, nbytes, slots, ms_per_step, ev_ms, blocks_ms, full_ms,
+               two_ms, bwd_ms, bbwd_ms, step_ms, torch):
+    """The JSON line of a training workload (bwd_ms / bbwd_ms / step_ms are
+    None when the backward was not run)."""
     bslots = slots_backward(batch, T, D)
     line = {
         "metric": "all-block training scan GB/s (forward over T + reverse per block)",
@@ -470,7 +514,7 @@ def train_main(args, wl, m, synth, torch):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if dtype == torch.bfloat16 else "f32", "data": "synthetic",
         "config": {"workload": args.workload, "batch": batch, "d_inner": D, "d_state": NS,
-                   "seq": T, "block": L},
+                   "seq": T, "block": L, "fused": bool(args.fused)},
         "train_scan": {"ms": ev_ms, "tokens_per_s": batch * T / (ev_ms * 1e-3),
                        "GBs": nbytes / (ev_ms * 1e-3) / 1e9,
                        "valu_slot_frac": slots / (ev_ms * 1e-3) / VALU_SLOTS_PER_S,
@@ -482,19 +526,18 @@ def train_main(args, wl, m, synth, torch):
         "two_stream": {"ms": two_ms, "over_full_scan_time": two_ms / full_ms,
                        "note": "clean train_scan with h_bounds + noisy train_scan_blocks, "
                                "against one full-sequence scan of the noisy stream"},
-        "backward": {"train_scan_bwd_ms": bwd_ms,
+        "backward": None if bwd_ms is None else {"train_scan_bwd_ms": bwd_ms,
                      "train_scan_bwd_valu_slot_frac": bslots / (bwd_ms * 1e-3) / VALU_SLOTS_PER_S,
                      "train_scan_blocks_bwd_ms": bbwd_ms,
                      "train_scan_blocks_bwd_valu_slot_frac": bslots / (bbwd_ms * 1e-3) / VALU_SLOTS_PER_S,
                      "bwd_over_fwd_time": bwd_ms / ev_ms},
-        "all_block_training_step": {
+        "all_block_training_step": None if step_ms is None else {
             "ms": step_ms, "tokens_per_s": batch * T / (step_ms * 1e-3),
             "note": "forward and backward of both streams: clean train_scan (block states), "
                     "noisy train_scan_blocks, noisy backward, clean backward fed the noisy "
                     "block-start gradients"},
     }
-    print(json.dumps(line), flush=True)
-    return 0
+    return line
 
 
 def crossover_main(args, m, synth, torch):
