@@ -87,6 +87,32 @@ static double step_size(double raw, double bias, int softplus)
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
+/*
+ * Optionally the reverse scan has operands of its own (a bidirectional Mamba
+ * layer whose reverse direction has its own projections and A): step size
+ * dt_r (with its own bias, same softplus setting), B_r, C_r and A_r.  The
+ * forward scan, and so the cache, never sees them.  With dt_r == NULL the
+ * reverse shares the forward's operands.
+ */
+typedef struct {
+    const void *dt, *Bm, *Cm;
+    const double *A, *dt_bias;
+} rev_operands;
+
+static int pick_reverse(rev_operands *r, const void *dt, const void *Bm, const void *Cm,
+                        const double *A, const double *dt_bias, const void *dt_r,
+                        const void *B_r, const void *C_r, const double *A_r,
+                        const double *dt_bias_r)
+{
+    if (dt_r == NULL) {
+        r->dt = dt; r->Bm = Bm; r->Cm = Cm; r->A = A; r->dt_bias = dt_bias;
+        return 0;
+    }
+    if (B_r == NULL || C_r == NULL || A_r == NULL) return -1;
+    r->dt = dt_r; r->Bm = B_r; r->Cm = C_r; r->A = A_r; r->dt_bias = dt_bias_r;
+    return 0;
+}
+
 int oracle_version(void) { return 3; }
 
 /* Threads the OpenMP loop over rows will use (1 without OpenMP). */
@@ -116,9 +142,13 @@ int oracle_scan_ex(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, in
                    const void *x, const void *dt, const void *Bm, const void *Cm,
                    const double *A, const double *Dskip, const double *h0,
                    const double *dt_bias, int dt_softplus, const void *z,
+                   const void *dt_r, const void *B_r, const void *C_r, const double *A_r,
+                   const double *dt_bias_r,
                    double *y, double *yf, double *yr, double *hT, double *bounds)
 {
     const int want_y = (y != NULL) || (yf != NULL) || (yr != NULL);
+    rev_operands rv;
+    if (pick_reverse(&rv, dt, Bm, Cm, A, dt_bias, dt_r, B_r, C_r, A_r, dt_bias_r)) return -1;
     if (batch < 0 || T < 0 || D < 0 || N < 1 || L < 1) return -1;
     if (T % L != 0) return -1;
     if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) return -1;
@@ -174,14 +204,14 @@ int oracle_scan_ex(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, in
                     for (int64_t t = k * L + L - 1; t >= k * L; --t) {
                         const size_t ix = (size_t)((b * T + t) * D + d);
                         const size_t ib = (size_t)((b * T + t) * N);
-                        const double dtv = step_size(ld(dt, ix, dtype), dt_bias ? dt_bias[d] : 0.0, dt_softplus);
+                        const double dtv = step_size(ld(rv.dt, ix, dtype), rv.dt_bias ? rv.dt_bias[d] : 0.0, dt_softplus);
                         const double xv = ld(x, ix, dtype);
                         double acc = 0.0;
                         for (int64_t n = 0; n < N; ++n) {
-                            const double decay = exp(dtv * A[d * N + n]);
-                            const double inject = dtv * ld(Bm, ib + n, dtype) * xv;
+                            const double decay = exp(dtv * rv.A[d * N + n]);
+                            const double inject = dtv * ld(rv.Bm, ib + n, dtype) * xv;
                             r[n] = decay * r[n] + inject;
-                            acc += ld(Cm, ib + n, dtype) * r[n];
+                            acc += ld(rv.Cm, ib + n, dtype) * r[n];
                         }
                         if (yf) yf[ix] = fwd[t];
                         if (yr) yr[ix] = acc;
@@ -202,7 +232,7 @@ int oracle_scan(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int d
                 double *y, double *yf, double *yr, double *hT, double *bounds)
 {
     return oracle_scan_ex(batch, T, D, N, L, dtype, x, dt, Bm, Cm, A, Dskip, h0, NULL, 0, NULL,
-                          y, yf, yr, hT, bounds);
+                          NULL, NULL, NULL, NULL, NULL, y, yf, yr, hT, bounds);
 }
 
 /* ---- the five entry points, each a composition of the core routine ---- */
@@ -267,8 +297,12 @@ int oracle_train_scan(int64_t batch, int64_t D, int64_t N, int64_t L, int dtype,
 int oracle_train_blocks_ex(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int dtype,
                            const void *x, const void *dt, const void *Bm, const void *Cm,
                            const double *A, const double *Dskip, const double *h0_blocks,
-                           const double *dt_bias, int dt_softplus, const void *z, double *y)
+                           const double *dt_bias, int dt_softplus, const void *z,
+                           const void *dt_r, const void *B_r, const void *C_r, const double *A_r,
+                           const double *dt_bias_r, double *y)
 {
+    rev_operands rv;
+    if (pick_reverse(&rv, dt, Bm, Cm, A, dt_bias, dt_r, B_r, C_r, A_r, dt_bias_r)) return -1;
     if (batch < 0 || T < 0 || D < 0 || N < 1 || L < 1 || T % L != 0) return -1;
     if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) return -1;
     if (T > 0 && (!x || !dt || !Bm || !Cm || !A || !Dskip || !h0_blocks || !y)) return -1;
@@ -308,13 +342,13 @@ int oracle_train_blocks_ex(int64_t batch, int64_t T, int64_t D, int64_t N, int64
                 for (int64_t t = k * L + L - 1; t >= k * L; --t) {
                     const size_t ix = (size_t)((b * T + t) * D + d);
                     const size_t ib = (size_t)((b * T + t) * N);
-                    const double dtv = step_size(ld(dt, ix, dtype), dt_bias ? dt_bias[d] : 0.0, dt_softplus);
+                    const double dtv = step_size(ld(rv.dt, ix, dtype), rv.dt_bias ? rv.dt_bias[d] : 0.0, dt_softplus);
                     const double xv = ld(x, ix, dtype);
                     double acc = 0.0;
                     for (int64_t n = 0; n < N; ++n) {
-                        const double decay = exp(dtv * A[d * N + n]);
-                        r[n] = decay * r[n] + dtv * ld(Bm, ib + n, dtype) * xv;
-                        acc += ld(Cm, ib + n, dtype) * r[n];
+                        const double decay = exp(dtv * rv.A[d * N + n]);
+                        r[n] = decay * r[n] + dtv * ld(rv.Bm, ib + n, dtype) * xv;
+                        acc += ld(rv.Cm, ib + n, dtype) * r[n];
                     }
                     y[ix] = (fwd[t - k * L] + acc + Dskip[d] * xv) * (z ? silu(ld(z, ix, dtype)) : 1.0);
                 }
@@ -330,7 +364,7 @@ int oracle_train_blocks(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t 
                         const double *A, const double *Dskip, const double *h0_blocks, double *y)
 {
     return oracle_train_blocks_ex(batch, T, D, N, L, dtype, x, dt, Bm, Cm, A, Dskip, h0_blocks,
-                                  NULL, 0, NULL, y);
+                                  NULL, 0, NULL, NULL, NULL, NULL, NULL, NULL, y);
 }
 
 /* Full-sequence bidirectional baseline: the reverse runs over the whole

@@ -41,10 +41,10 @@ def bind(lib):
     lib.oracle_scan.argtypes = [I, I, I, I, I, ctypes.c_int] + [P] * 12
     lib.oracle_scan.restype = ctypes.c_int
     lib.oracle_scan_ex.argtypes = ([I, I, I, I, I, ctypes.c_int] + [P] * 8 + [ctypes.c_int]
-                                   + [P] * 6)
+                                   + [P] * 11)
     lib.oracle_scan_ex.restype = ctypes.c_int
     lib.oracle_train_blocks_ex.argtypes = ([I, I, I, I, I, ctypes.c_int] + [P] * 8 + [ctypes.c_int]
-                                           + [P] * 2)
+                                           + [P] * 7)
     lib.oracle_train_blocks_ex.restype = ctypes.c_int
     lib.oracle_version.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -93,6 +93,22 @@ def _c(a, dt=None):
     return np.ascontiguousarray(a)
 
 
+def _reverse(x, B, A, rev):
+    """Marshal separate reverse-direction operands: dict with dt, B, C, A and
+    optionally dt_bias, or None (the reverse shares the forward's)."""
+    if rev is None:
+        return (None,) * 5
+    dt_r, B_r, C_r = _c(rev["dt"]), _c(rev["B"]), _c(rev["C"])
+    A_r = _c(rev["A"], np.float64)
+    bias_r = _c(rev.get("dt_bias"), np.float64)
+    for a in (dt_r, B_r, C_r):
+        if a.dtype != x.dtype:
+            raise TypeError("reverse operands must share x's dtype")
+    assert dt_r.shape == x.shape and B_r.shape == B.shape and C_r.shape == B.shape
+    assert A_r.shape == A.shape
+    return dt_r, B_r, C_r, A_r, bias_r
+
+
 def _fusion(x, D, dt_bias, z):
     """Marshal the optional fusions: dt_bias [D] (float64), z (x's dtype)."""
     bias = _c(dt_bias, np.float64)
@@ -106,11 +122,12 @@ def _fusion(x, D, dt_bias, z):
 
 
 def scan(x, dt, B, C, A, Dskip, L, h0=None, want_y=True, want_parts=False, want_bounds=False,
-         dt_bias=None, dt_softplus=False, z=None):
+         dt_bias=None, dt_softplus=False, z=None, rev=None):
     """Core oracle: continuous forward from h0, reverse segmented into L-token
     blocks.  Returns a dict with 'y' (and 'yf', 'yr' if want_parts), 'hT',
     and 'bounds' ([batch, T/L+1, D, N]) if want_bounds.  Optional fusions:
-    dt <- dt + dt_bias, then softplus if dt_softplus; y <- y * silu(z)."""
+    dt <- dt + dt_bias, then softplus if dt_softplus; y <- y * silu(z).
+    rev: separate reverse-direction operands {dt, B, C, A[, dt_bias]}."""
     x, dt, B = _c(x), _c(dt), _c(B)
     C = _c(C)
     A = _c(A, np.float64)
@@ -137,10 +154,11 @@ def scan(x, dt, B, C, A, Dskip, L, h0=None, want_y=True, want_parts=False, want_
     if want_bounds:
         bounds = out["bounds"] = np.empty((batch, T // L + 1, D, N), np.float64)
     bias, zz = _fusion(x, D, dt_bias, z)
+    rv = _reverse(x, B, A, rev)
     rc = load().oracle_scan_ex(batch, T, D, N, L, code, _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
                                _ptr(A), _ptr(Dskip), _ptr(h0), _ptr(bias), int(bool(dt_softplus)),
-                               _ptr(zz), _ptr(y), _ptr(yf), _ptr(yr), _ptr(out["hT"]),
-                               _ptr(bounds))
+                               _ptr(zz), *[_ptr(a) for a in rv], _ptr(y), _ptr(yf), _ptr(yr),
+                               _ptr(out["hT"]), _ptr(bounds))
     if rc != 0:
         raise ValueError("oracle_scan rejected its arguments (rc=%d)" % rc)
     return out
@@ -177,7 +195,8 @@ def full_scan(x, dt, B, C, A, Dskip, **fusion):
     return scan(x, dt, B, C, A, Dskip, max(T, 1), h0=None, want_y=True, **fusion)["y"]
 
 
-def train_blocks(x, dt, B, C, A, Dskip, L, h0_blocks, dt_bias=None, dt_softplus=False, z=None):
+def train_blocks(x, dt, B, C, A, Dskip, L, h0_blocks, dt_bias=None, dt_softplus=False, z=None,
+                 rev=None):
     """Two-stream training form, noisy stream: every L-block k scanned from
     h0_blocks[:, k] ([batch, T/L + 1, D, N]) plus the in-block reverse -> y."""
     x, dt, B, C = _c(x), _c(dt), _c(B), _c(C)
@@ -190,9 +209,11 @@ def train_blocks(x, dt, B, C, A, Dskip, L, h0_blocks, dt_bias=None, dt_softplus=
     assert h0.shape == (batch, T // L + 1, D, N)
     y = np.empty((batch, T, D), np.float64)
     bias, zz = _fusion(x, D, dt_bias, z)
+    rv = _reverse(x, B, A, rev)
     rc = load().oracle_train_blocks_ex(batch, T, D, N, L, code, _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
                                        _ptr(A), _ptr(Dskip), _ptr(h0), _ptr(bias),
-                                       int(bool(dt_softplus)), _ptr(zz), _ptr(y))
+                                       int(bool(dt_softplus)), _ptr(zz), *[_ptr(a) for a in rv],
+                                       _ptr(y))
     if rc != 0:
         raise ValueError("oracle_train_blocks rejected its arguments (rc=%d)" % rc)
     return y

@@ -94,3 +94,63 @@ def test_fusions_of_bf16_inputs_widen_exactly():
     a = oracle.scan(xb, rb, Bb, Cb, A, Ds, 16, dt_bias=bias, dt_softplus=True, z=zb)
     b = oracle.scan(xw, rw, Bw, Cw, A, Ds, 16, dt_bias=bias, dt_softplus=True, z=zw)
     assert np.array_equal(a["y"], b["y"])
+
+
+# ---- separate reverse-direction operands
+
+def rev_operands(rng, batch, T, D, N):
+    return dict(dt=np.log1p(np.exp(rng.normal(-0.5, 0.5, (batch, T, D)))),
+                B=rng.standard_normal((batch, T, N)), C=rng.standard_normal((batch, T, N)),
+                A=-np.exp(rng.uniform(np.log(0.05), np.log(4.0), (D, N))))
+
+
+def test_reverse_operands_equal_to_forward_are_the_shared_scan():
+    rng = np.random.default_rng(760)
+    x, raw, B, C, A, Ds, bias, z = inputs(rng, 2, 32, 3, 4)
+    dt = np.log1p(np.exp(raw))
+    shared = oracle.scan(x, dt, B, C, A, Ds, 8, want_parts=True)
+    same = oracle.scan(x, dt, B, C, A, Ds, 8, want_parts=True, rev=dict(dt=dt, B=B, C=C, A=A))
+    for k in ("y", "yf", "yr", "hT"):
+        assert np.array_equal(shared[k], same[k]), k
+
+
+def test_reverse_operands_leave_the_forward_and_the_cache_alone():
+    rng = np.random.default_rng(770)
+    x, raw, B, C, A, Ds, bias, z = inputs(rng, 2, 32, 3, 4)
+    dt = np.log1p(np.exp(raw))
+    rev = rev_operands(rng, 2, 32, 3, 4)
+    a = oracle.scan(x, dt, B, C, A, Ds, 8, want_parts=True, want_bounds=True)
+    b = oracle.scan(x, dt, B, C, A, Ds, 8, want_parts=True, want_bounds=True, rev=rev)
+    for k in ("yf", "hT", "bounds"):
+        assert np.array_equal(a[k], b[k]), k
+    assert not np.allclose(a["yr"], b["yr"])
+
+
+@pytest.mark.parametrize("softplus", [False, True])
+def test_reverse_with_own_operands_is_the_flipped_forward_of_them(softplus):
+    """With one block covering the row, the reverse part equals the forward
+    scan (from zero) of the time-flipped inputs taken with the reverse
+    operands, flipped back."""
+    rng = np.random.default_rng(780 + softplus)
+    T = 24
+    x, raw, B, C, A, Ds, bias, z = inputs(rng, 2, T, 3, 4)
+    rev = rev_operands(rng, 2, T, 3, 4)
+    rev["dt_bias"] = rng.normal(0.0, 0.3, 3)
+    dt = raw if softplus else np.log1p(np.exp(raw))
+    got = oracle.scan(x, dt, B, C, A, Ds, T, want_parts=True, rev=rev, dt_softplus=softplus,
+                      dt_bias=bias)["yr"]
+    f = lambda a: np.ascontiguousarray(a[:, ::-1])
+    ref = oracle.scan(f(x), f(rev["dt"]), f(rev["B"]), f(rev["C"]), rev["A"], Ds, T, want_parts=True,
+                      dt_softplus=softplus, dt_bias=rev["dt_bias"])["yf"]
+    assert rel(got, f(ref)) < 1e-12
+
+
+def test_two_stream_form_with_reverse_operands():
+    rng = np.random.default_rng(790)
+    L, T = 4, 16
+    x, raw, B, C, A, Ds, bias, z = inputs(rng, 2, T, 3, 4)
+    dt = np.log1p(np.exp(raw))
+    rev = rev_operands(rng, 2, T, 3, 4)
+    r = oracle.scan(x, dt, B, C, A, Ds, L, want_bounds=True, rev=rev, z=z)
+    yb = oracle.train_blocks(x, dt, B, C, A, Ds, L, r["bounds"], rev=rev, z=z)
+    assert rel(yb, r["y"]) < 1e-13

@@ -26,8 +26,8 @@ MUTANTS = {
     "drop_skip_term": ("if (y) y[ix] = (fwd[t] + acc + Dskip[d] * xv) *", "if (y) y[ix] = (fwd[t] + acc) *"),
     "decay_sign": ("const double decay = exp(dtv * A[d * N + n]);\n                    const double inject",
                    "const double decay = exp(-dtv * A[d * N + n]);\n                    const double inject"),
-    "reverse_exclusive": ("r[n] = decay * r[n] + inject;\n                            acc += ld(Cm, ib + n, dtype) * r[n];",
-                          "acc += ld(Cm, ib + n, dtype) * r[n];\n                            r[n] = decay * r[n] + inject;"),
+    "reverse_exclusive": ("r[n] = decay * r[n] + inject;\n                            acc += ld(rv.Cm, ib + n, dtype) * r[n];",
+                          "acc += ld(rv.Cm, ib + n, dtype) * r[n];\n                            r[n] = decay * r[n] + inject;"),
     "B_C_swapped": ("const double inject = dtv * ld(Bm, ib + n, dtype) * xv;\n                    h[n]",
                     "const double inject = dtv * ld(Cm, ib + n, dtype) * xv;\n                    h[n]"),
     "A_transposed": ("const double decay = exp(dtv * A[d * N + n]);\n                    const double inject",
@@ -67,6 +67,12 @@ MUTANTS_FUSED = {
     "bias_ignored": ("const double v = raw + bias;", "const double v = raw;"),
     "gate_is_sigmoid": ("static double silu(double z) { return z / (1.0 + exp(-z)); }",
                         "static double silu(double z) { return 1.0 / (1.0 + exp(-z)); }"),
+    "reverse_uses_forward_A": ("const double decay = exp(dtv * rv.A[d * N + n]);\n                            const double inject = dtv * ld(rv.Bm",
+                               "const double decay = exp(dtv * A[d * N + n]);\n                            const double inject = dtv * ld(rv.Bm"),
+    "reverse_uses_forward_C": ("acc += ld(rv.Cm, ib + n, dtype) * r[n];\n                        }\n                        if (yf)",
+                               "acc += ld(Cm, ib + n, dtype) * r[n];\n                        }\n                        if (yf)"),
+    "reverse_uses_forward_bias": ("const double dtv = step_size(ld(rv.dt, ix, dtype), rv.dt_bias ? rv.dt_bias[d] : 0.0, dt_softplus);\n                        const double xv",
+                                  "const double dtv = step_size(ld(rv.dt, ix, dtype), dt_bias ? dt_bias[d] : 0.0, dt_softplus);\n                        const double xv"),
     "gate_missing": ("if (y) y[ix] = (fwd[t] + acc + Dskip[d] * xv) * (z ? silu(ld(z, ix, dtype)) : 1.0);",
                      "if (y) y[ix] = (fwd[t] + acc + Dskip[d] * xv);"),
 }
