@@ -54,7 +54,8 @@
  * bdssm_commit is read and written in place).
  *
  * Limits of this version: d_state == 16; block_len in {1, 2, 4, 8, 16};
- * T % block_len == 0; x, dt, B, C, z and y share one dtype.
+ * T % block_len == 0; x, dt, B, C, z, the reverse operands and y share one
+ * dtype.
  */
 #ifndef BDSSM_H
 #define BDSSM_H
@@ -106,6 +107,20 @@ typedef struct {
     const float *dt_bias;
     int32_t dt_softplus;
     const void *z;
+    /* Separate reverse-direction operands (a bidirectional Mamba layer whose
+     * reverse direction has its own projections and A; the pages are silent):
+     * dt_rev NULL = the reverse shares dt, B, C, A and dt_bias.  Otherwise
+     * B_rev and C_rev ([batch, T, d_state], stream dtype) and A_rev ([d_inner,
+     * d_state] fp32) are required and dt_bias_rev ([d_inner] fp32) optional;
+     * dt_rev ([batch, T, d_inner], stream dtype) goes through the same
+     * transform as dt (dt_softplus) with dt_bias_rev.  Only the in-block
+     * reverse scan reads them: the forward scan and the cache never do.  A
+     * separate reverse skip term is folded into Dskip by the caller. */
+    const void *dt_rev;
+    const void *B_rev;
+    const void *C_rev;
+    const float *A_rev;
+    const float *dt_bias_rev;
 } bdssm_fusion;
 
 typedef struct {

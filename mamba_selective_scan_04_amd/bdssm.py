@@ -9,8 +9,9 @@ Names and semantics follow include/bdssm.h:
   full_scan(x, dt, B, C, A, Dskip, y=None)
   train_scan_bwd(x, dt, B, C, A, Dskip, block_len, h_bounds, dy, d_bounds=None, want_dh_init=False)
   train_scan_blocks_bwd(x, dt, B, C, A, Dskip, block_len, h0_blocks, dy, want_dh0_blocks=False)
-The six forward functions also take the optional Mamba-1 fusions as keyword
-arguments: dt_bias ([D] fp32), dt_softplus (bool), z (gate, like y).
+The six forward functions also take the optional layer features as keyword
+arguments: dt_bias ([D] fp32), dt_softplus (bool), z (gate, like y), and rev
+(separate reverse-direction operands: dict with dt, B, C, A, optional dt_bias).
 Shapes: x, dt, y [batch, T, D]; B, C [batch, T, 16]; A [D, 16] fp32;
 Dskip [D] fp32; states [batch, D, 16] fp32.  x/dt/B/C/y share fp32 or bf16.
 All tensors must be contiguous, on the current CUDA (HIP) device.  Work is
@@ -47,7 +48,9 @@ class Shape(ctypes.Structure):
 
 class Fusion(ctypes.Structure):
     _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int32),
-                ("z", ctypes.c_void_p)]
+                ("z", ctypes.c_void_p), ("dt_rev", ctypes.c_void_p), ("B_rev", ctypes.c_void_p),
+                ("C_rev", ctypes.c_void_p), ("A_rev", ctypes.c_void_p),
+                ("dt_bias_rev", ctypes.c_void_p)]
 
 
 _lib = None
@@ -152,14 +155,27 @@ def _streams(x, dt, B, C, A, Dskip, need_c=True):
     return batch, T, D, N, code
 
 
-def _fusion(x, D, dt_bias=None, dt_softplus=False, z=None):
-    """Marshal the optional fusions -> (ctypes pointer or None, keep-alive refs)."""
-    if dt_bias is None and not dt_softplus and z is None:
+def _fusion(x, D, dt_bias=None, dt_softplus=False, z=None, rev=None):
+    """Marshal the optional layer features -> ctypes pointer to a Fusion, or
+    None.  rev: separate reverse-direction operands, a dict with dt, B, C
+    (stream dtype), A ([D, 16] fp32) and optionally dt_bias ([D] fp32)."""
+    if dt_bias is None and not dt_softplus and z is None and rev is None:
         return None
     _check(dt_bias, "dt_bias", torch.float32, (D,))
     _check(z, "z", x.dtype, tuple(x.shape))
-    f = Fusion(None if dt_bias is None else dt_bias.data_ptr(), 1 if dt_softplus else 0,
-               None if z is None else z.data_ptr())
+    ptr = lambda t: None if t is None else t.data_ptr()
+    r = {} if rev is None else rev
+    if rev is not None:
+        batch, T = x.shape[0], x.shape[1]
+        _check(r["dt"], "rev['dt']", x.dtype, tuple(x.shape))
+        _check(r["B"], "rev['B']", x.dtype)
+        _check(r["C"], "rev['C']", x.dtype, tuple(r["B"].shape))
+        if r["B"].dim() != 3 or tuple(r["B"].shape[:2]) != (batch, T):
+            raise ValueError("rev['B'] must be [batch, T, d_state]")
+        _check(r["A"], "rev['A']", torch.float32, (D, r["B"].shape[2]))
+        _check(r.get("dt_bias"), "rev['dt_bias']", torch.float32, (D,))
+    f = Fusion(ptr(dt_bias), 1 if dt_softplus else 0, ptr(z), ptr(r.get("dt")), ptr(r.get("B")),
+               ptr(r.get("C")), ptr(r.get("A")), ptr(r.get("dt_bias")))
     return ctypes.pointer(f)
 
 

@@ -276,9 +276,22 @@ int check_alias(const bdssm_shape *s, int64_t T, const void *x, const void *dt, 
 int check_fusion(const bdssm_fusion *f, const bdssm_shape *s, int64_t T, bool with_y,
                  std::initializer_list<Range> outs) {
     if (f == nullptr) return BDSSM_OK;
-    if (!aligned16(f->dt_bias) || (with_y && !aligned16(f->z))) return BDSSM_ERR_ALIGN;
+    const bool rev = with_y && f->dt_rev != nullptr;
+    if (rev && (f->B_rev == nullptr || f->C_rev == nullptr || f->A_rev == nullptr))
+        return BDSSM_ERR_NULL;
+    const void *ps[] = {f->dt_bias, with_y ? f->z : nullptr, rev ? f->dt_rev : nullptr,
+                        rev ? f->B_rev : nullptr, rev ? f->C_rev : nullptr,
+                        rev ? f->A_rev : nullptr, rev ? f->dt_bias_rev : nullptr};
+    for (const void *p : ps)
+        if (!aligned16(p)) return BDSSM_ERR_ALIGN;
+    const size_t ntok = (size_t)s->batch * T * s->d_inner * esize(s);
+    const size_t nbc = (size_t)s->batch * T * kStates * esize(s);
     const Range ins[] = {{f->dt_bias, (size_t)s->d_inner * 4},
-                         {with_y ? f->z : nullptr, (size_t)s->batch * T * s->d_inner * esize(s)}};
+                         {with_y ? f->z : nullptr, ntok},
+                         {rev ? f->dt_rev : nullptr, ntok}, {rev ? f->B_rev : nullptr, nbc},
+                         {rev ? f->C_rev : nullptr, nbc},
+                         {rev ? f->A_rev : nullptr, (size_t)s->d_inner * kStates * 4},
+                         {rev ? f->dt_bias_rev : nullptr, (size_t)s->d_inner * 4}};
     for (const Range &o : outs)
         for (const Range &i : ins)
             if (overlaps(o, i)) return BDSSM_ERR_ALIAS;
@@ -310,7 +323,26 @@ struct Fuse {
     const float *dt_bias = nullptr;
     int dt_mode = kDtPlain;
     const void *z = nullptr;
-    bool any() const { return dt_mode != kDtPlain || z != nullptr; }
+    // separate reverse-direction operands (dt_r == nullptr: shared)
+    const void *dt_r = nullptr, *B_r = nullptr, *C_r = nullptr;
+    const float *A_r = nullptr, *dt_bias_r = nullptr;
+    bool any() const { return dt_mode != kDtPlain || z != nullptr || dt_r != nullptr; }
+    template <typename Tin> FuseArgs<Tin> args() const {
+        return FuseArgs<Tin>{dt_bias, dt_mode, (const Tin *)z, (const Tin *)dt_r,
+                             (const Tin *)B_r, (const Tin *)C_r, A_r, dt_bias_r};
+    }
+    // the operands of the reverse direction, as a plain (unfused-reverse) Fuse
+    // for the baseline's reverse passes: its own bias, the same transform
+    Fuse reverse() const {
+        Fuse r = *this;
+        if (dt_r != nullptr) {
+            r.dt_bias = dt_bias_r;
+            r.dt_mode = dt_mode == kDtSoftplus ? kDtSoftplus : (dt_bias_r != nullptr ? kDtBias : kDtPlain);
+        }
+        r.dt_r = r.B_r = r.C_r = nullptr;
+        r.A_r = r.dt_bias_r = nullptr;
+        return r;
+    }
 };
 
 Fuse resolve_fusion(const bdssm_fusion *f, bool with_y) {
@@ -319,6 +351,10 @@ Fuse resolve_fusion(const bdssm_fusion *f, bool with_y) {
     r.dt_bias = f->dt_bias;
     r.dt_mode = f->dt_softplus ? kDtSoftplus : (f->dt_bias != nullptr ? kDtBias : kDtPlain);
     r.z = with_y ? f->z : nullptr;
+    if (with_y && f->dt_rev != nullptr) {
+        r.dt_r = f->dt_rev; r.B_r = f->B_rev; r.C_r = f->C_rev;
+        r.A_r = f->A_rev; r.dt_bias_r = f->dt_bias_rev;
+    }
     return r;
 }
 
@@ -383,7 +419,7 @@ void launch_bidir_k(dim3 g, const void *x, const void *dt, const void *B, const 
     hipLaunchKernelGGL((bidir_wave_kernel<Tin, L, kInit, kFuse>), g, dim3(4 * kWave), 0, st,
                        (const Tin *)x, (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip,
                        hin, hin_bs, hin_cs, (Tin *)y, bounds, hout, T, (int)D, Tc, h0_blocks,
-                       f.dt_bias, f.dt_mode, (const Tin *)f.z);
+                       f.args<Tin>());
 }
 
 template <typename Tin, int L>
@@ -550,12 +586,19 @@ void run_full(const bdssm_shape *s, int64_t T, const void *x, const void *dt, co
     launch_chunk_state<Tin>(false, x, dt, B, A, nullptr, w.agg_h, w.agg_s, batch, T, D,
                             p.fine_len, nf, 0, nf - 1, st, f);
     launch_carry(false, w.agg_h, w.agg_s, A, nullptr, w.h_in, nullptr, batch, D, nf, nf - 1, st);
-    // reverse: aggregates of chunks 1..nf-1 (scanned right to left), incoming states
-    launch_chunk_state<Tin>(true, x, dt, B, A, nullptr, w.ragg_h, w.ragg_s, batch, T, D,
-                            p.fine_len, nf, 1, nf - 1, st, f);
-    launch_carry(true, w.ragg_h, w.ragg_s, A, nullptr, w.hr_in, nullptr, batch, D, nf, nf, st);
-    launch_sweep<Tin>(false, x, dt, B, C, A, Dskip, w.h_in, w.yf, y, batch, T, D, p.fine_len, nf, st, f);
-    launch_sweep<Tin>(true, x, dt, B, C, A, Dskip, w.hr_in, w.yf, y, batch, T, D, p.fine_len, nf, st, f);
+    // reverse (with its own operands when given): aggregates of chunks
+    // 1..nf-1 (scanned right to left), incoming states
+    const bool sep = f.dt_r != nullptr;
+    const void *rdt = sep ? f.dt_r : dt, *rB = sep ? f.B_r : B, *rC = sep ? f.C_r : C;
+    const float *rA = sep ? f.A_r : A;
+    const Fuse fr = f.reverse();
+    launch_chunk_state<Tin>(true, x, rdt, rB, rA, nullptr, w.ragg_h, w.ragg_s, batch, T, D,
+                            p.fine_len, nf, 1, nf - 1, st, fr);
+    launch_carry(true, w.ragg_h, w.ragg_s, rA, nullptr, w.hr_in, nullptr, batch, D, nf, nf, st);
+    Fuse ff = f;
+    ff.z = nullptr;             // the gate multiplies the final output only
+    launch_sweep<Tin>(false, x, dt, B, C, A, Dskip, w.h_in, w.yf, y, batch, T, D, p.fine_len, nf, st, ff);
+    launch_sweep<Tin>(true, x, rdt, rB, rC, rA, Dskip, w.hr_in, w.yf, y, batch, T, D, p.fine_len, nf, st, fr);
 }
 
 }  // namespace

@@ -87,6 +87,18 @@ __device__ __forceinline__ float silu_f(float z) {
     return z * __builtin_amdgcn_rcpf(1.f + fast_exp2(-z * kLog2e));
 }
 
+// Optional per-call features of the bidirectional pass (all may be null):
+// the step-size transform (dt_mode, dt_bias), the output gate z, and separate
+// reverse-direction operands (dt_r with its own bias dt_bias_r, B_r, C_r,
+// A_r), which only the in-block reverse scan reads.
+template <typename Tin> struct FuseArgs {
+    const float *dt_bias;
+    int dt_mode;
+    const Tin *z;
+    const Tin *dt_r, *B_r, *C_r;
+    const float *A_r, *dt_bias_r;
+};
+
 // States 2q and 2q+1 of a B or C row.  The row is read as 32-bit words: with a
 // wave-uniform address that lets the compiler use scalar loads (s_load_dwordxN)
 // and unpack bf16 pairs on the scalar unit instead of spending VALU slots.
@@ -373,10 +385,12 @@ __global__ __launch_bounds__(256) void carry_kernel(
 // hout (optional): forward state after token T-1 (written by the last chunk;
 // may alias hin when there is a single chunk: each lane reads its own states
 // before it writes them).
-// kFuse (Mamba-1 fusions): dt is formed from the dt stream as step_size<dt_mode>
-// with dt_bias (each lane transforms the 4 dt values it loaded, in LDS, once
-// per token and channel), and when z is given the output is multiplied by
-// silu(z) (z rows are loaded with x and dt).
+// kFuse (optional layer features, FuseArgs): dt is formed from the dt stream as
+// step_size<dt_mode> with dt_bias (each lane transforms the 4 dt values it
+// loaded, in LDS, once per token and channel); when z is given the output is
+// multiplied by silu(z) (z rows are loaded with x and dt); when dt_r is given
+// the reverse scan takes its own operands (dt_r, B_r, C_r rows staged beside
+// the forward ones, decays exp2(dt_r A_r') computed in the reverse pass).
 // grid = (ceil(D/64), chunks, batch), block = 256 (4 independent waves).
 template <typename Tin, int L, bool kBlockInit, bool kFuse = false>
 __global__ __launch_bounds__(4 * kWave) void bidir_wave_kernel(
@@ -384,18 +398,21 @@ __global__ __launch_bounds__(4 * kWave) void bidir_wave_kernel(
     const Tin *__restrict__ Cm, const float *__restrict__ A, const float *__restrict__ Dskip,
     const float *hin, int64_t hin_bs, int64_t hin_cs,
     Tin *__restrict__ y, float *__restrict__ bounds, float *hout,
-    int64_t T, int D, int64_t Tc, const float *__restrict__ h0_blocks,
-    const float *__restrict__ dt_bias, int dt_mode, const Tin *__restrict__ z)
+    int64_t T, int D, int64_t Tc, const float *__restrict__ h0_blocks, FuseArgs<Tin> fz)
 {
     constexpr int P = 4;                      // states per lane
     constexpr int CW = kWave / P;             // channels per wave (16)
     constexpr int ES = sizeof(Tin);
-    constexpr int NS = kFuse ? 3 : 2;         // token-row streams staged per group
+    constexpr int NS = kFuse ? 4 : 2;         // token-row streams: x, dt (, z, dt_r)
+    constexpr int NR = kFuse ? 4 : 2;         // per-token rows: B, C (, B_r, C_r)
     static_assert(kGroup % L == 0, "block length must divide the token group");
-    // per wave: [x|dt(|z)][4 loads][64]  and  [B|C][4 loads][64]  and  fp32 B/C rows
+    // per wave: token rows [stream][4 loads][64], raw B/C rows [row][4 loads][64]
+    // (both double buffered: the next group's loads are in flight), and fp32
+    // B/C rows [token][row][16] (single buffer: written after this wave's last
+    // read of the previous group, in program order)
     __shared__ uint32_t xdA[4][NS][4][kWave], xdB[4][NS][4][kWave];
-    __shared__ uint32_t bcrA[4][2][4][kWave], bcrB[4][2][4][kWave];
-    __shared__ float bcfA[4][kGroup][2][kStates], bcfB[4][kGroup][2][kStates];
+    __shared__ uint32_t bcrA[4][NR][4][kWave], bcrB[4][NR][4][kWave];
+    __shared__ float bcf[4][kGroup][NR][kStates];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform(threadIdx.x >> 6);
@@ -444,9 +461,21 @@ __global__ __launch_bounds__(4 * kWave) void bidir_wave_kernel(
     // and channel (or state) l % 16
     const int ld_tok = lane >> 4, ld_col = lane & 15;
     const int ld_ch = (d_w0 + ld_col < D) ? d_w0 + ld_col : D - 1;
-    const bool gate = kFuse && z != nullptr;
-    const Rows<Tin> zs((gate ? z : x) + first * D, len, D, 0);
-    const float ld_bias = (kFuse && dt_bias != nullptr) ? dt_bias[ld_ch] : 0.f;
+    const bool gate = kFuse && fz.z != nullptr;
+    const bool sep = kFuse && fz.dt_r != nullptr;
+    const Rows<Tin> zs((gate ? fz.z : x) + first * D, len, D, 0);
+    const Rows<Tin> rds((sep ? fz.dt_r : x) + first * D, len, D, 0);
+    __amdgpu_buffer_rsrc_t rbrs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(const_cast<Tin *>((sep ? fz.B_r : Bm) + first * kStates)), 0, uniform(len * kStates * ES), kRawBufferWord3);
+    __amdgpu_buffer_rsrc_t rcrs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(const_cast<Tin *>((sep ? fz.C_r : Cm) + first * kStates)), 0, uniform(len * kStates * ES), kRawBufferWord3);
+    const float ld_bias = (kFuse && fz.dt_bias != nullptr) ? fz.dt_bias[ld_ch] : 0.f;
+    const float ld_bias_r = (kFuse && sep && fz.dt_bias_r != nullptr) ? fz.dt_bias_r[ld_ch] : 0.f;
+    float a2r[P] = {0.f, 0.f, 0.f, 0.f};
+    if (sep) {
+        const float4 av = *reinterpret_cast<const float4 *>(fz.A_r + (int64_t)d * kStates + s0);
+        a2r[0] = av.x * kLog2e; a2r[1] = av.y * kLog2e; a2r[2] = av.z * kLog2e; a2r[3] = av.w * kLog2e;
+    }
 
     auto issue = [&](auto &xd, auto &bcr, int k0) {
 #pragma unroll
@@ -455,19 +484,29 @@ __global__ __launch_bounds__(4 * kWave) void bidir_wave_kernel(
             k = k < len ? k : len - 1;
             load_to_lds<ES>(xs.rsrc, &xd[w][0][j][0], ld_ch * ES + k * xs.pitch, 0);
             load_to_lds<ES>(ds.rsrc, &xd[w][1][j][0], ld_ch * ES + k * ds.pitch, 0);
-            if constexpr (kFuse) {
-                if (gate) load_to_lds<ES>(zs.rsrc, &xd[w][NS - 1][j][0], ld_ch * ES + k * zs.pitch, 0);
-            }
             load_to_lds<ES>(brs, &bcr[w][0][j][0], (k * kStates + ld_col) * ES, 0);
             load_to_lds<ES>(crs, &bcr[w][1][j][0], (k * kStates + ld_col) * ES, 0);
+            if constexpr (kFuse) {
+                if (gate) load_to_lds<ES>(zs.rsrc, &xd[w][2][j][0], ld_ch * ES + k * zs.pitch, 0);
+                if (sep) {
+                    load_to_lds<ES>(rds.rsrc, &xd[w][3][j][0], ld_ch * ES + k * rds.pitch, 0);
+                    load_to_lds<ES>(rbrs, &bcr[w][2][j][0], (k * kStates + ld_col) * ES, 0);
+                    load_to_lds<ES>(rcrs, &bcr[w][3][j][0], (k * kStates + ld_col) * ES, 0);
+                }
+            }
         }
     };
     auto elem = [&](uint32_t v) -> float {
         return ES == 2 ? __uint_as_float(v << 16) : __uint_as_float(v);
     };
     // wait for this wave's own LDS loads (vmcnt = 0), then widen B / C (and,
-    // with the fusions, turn the lane's own 4 raw dt values into fp32 dt)
-    auto widen_bc = [&](auto &bcr, auto &bcf, auto &xd) {
+    // with kFuse, turn the lane's own 4 raw dt (and dt_r) values into fp32 dt)
+    auto form_dt = [&](float raw, float bias) -> float {
+        if (fz.dt_mode == kDtSoftplus) return step_size<kDtSoftplus>(raw, bias);
+        if (fz.dt_mode == kDtBias) return step_size<kDtBias>(raw, bias);
+        return raw;
+    };
+    auto widen_bc = [&](auto &bcr, auto &xd) {
         __builtin_amdgcn_s_waitcnt(0x0F70);
 #pragma unroll
         for (int which = 0; which < 2; ++which)
@@ -476,13 +515,17 @@ __global__ __launch_bounds__(4 * kWave) void bidir_wave_kernel(
                 bcf[w][4 * j + ld_tok][which][ld_col] = elem(bcr[w][which][j][lane]);
         if constexpr (kFuse) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float raw = elem(xd[w][1][j][lane]);
-                float v;
-                if (dt_mode == kDtSoftplus) v = step_size<kDtSoftplus>(raw, ld_bias);
-                else if (dt_mode == kDtBias) v = step_size<kDtBias>(raw, ld_bias);
-                else v = raw;
-                xd[w][1][j][lane] = __float_as_uint(v);
+            for (int j = 0; j < 4; ++j)
+                xd[w][1][j][lane] = __float_as_uint(form_dt(elem(xd[w][1][j][lane]), ld_bias));
+            if (sep) {
+#pragma unroll
+                for (int which = 2; which < 4; ++which)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        bcf[w][4 * j + ld_tok][which][ld_col] = elem(bcr[w][which][j][lane]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    xd[w][3][j][lane] = __float_as_uint(form_dt(elem(xd[w][3][j][lane]), ld_bias_r));
             }
         }
     };
@@ -498,7 +541,7 @@ __global__ __launch_bounds__(4 * kWave) void bidir_wave_kernel(
     Tin *ylane = y + first * D + d;
     const bool hi2 = (g & 2) != 0, hi1 = (g & 1) != 0;
 
-    auto group = [&](auto &xd, auto &bcf, auto &xdn, auto &bcrn, auto &bcfn, int k0) {
+    auto group = [&](auto &xd, auto &xdn, auto &bcrn, int k0) {
         const int nvalid = (len - k0 < kGroup) ? len - k0 : kGroup;   // uniform
         const bool more = k0 + kGroup < len;
         if (more) issue(xdn, bcrn, k0 + kGroup);
@@ -551,21 +594,44 @@ __global__ __launch_bounds__(4 * kWave) void bidir_wave_kernel(
         }
         asm volatile("" ::: "memory");
         float hr[P] = {0.f, 0.f, 0.f, 0.f};
+        if (!sep) {
+            // shared operands: the forward's decays and injections
 #pragma unroll
-        for (int i = kGroup - 1; i >= 0; --i) {
-            const float4 b4 = *reinterpret_cast<const float4 *>(&bcf[w][i][0][s0]);
-            const float4 c4 = *reinterpret_cast<const float4 *>(&bcf[w][i][1][s0]);
-            const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
-            const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
-            if ((i + 1) % L == 0) { hr[0] = hr[1] = hr[2] = hr[3] = 0.f; }
-            float acc = ya[i];
+            for (int i = kGroup - 1; i >= 0; --i) {
+                const float4 b4 = *reinterpret_cast<const float4 *>(&bcf[w][i][0][s0]);
+                const float4 c4 = *reinterpret_cast<const float4 *>(&bcf[w][i][1][s0]);
+                const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+                const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+                if ((i + 1) % L == 0) { hr[0] = hr[1] = hr[2] = hr[3] = 0.f; }
+                float acc = ya[i];
 #pragma unroll
-            for (int j = 0; j < P; ++j) {
-                hr[j] = __builtin_fmaf(dA[i][j], hr[j], dx[i] * bv[j]);
-                acc = __builtin_fmaf(cv[j], hr[j], acc);
+                for (int j = 0; j < P; ++j) {
+                    hr[j] = __builtin_fmaf(dA[i][j], hr[j], dx[i] * bv[j]);
+                    acc = __builtin_fmaf(cv[j], hr[j], acc);
+                }
+                ya[i] = acc;
+                if ((i & 3) == 0) asm volatile("" ::: "memory");
             }
-            ya[i] = acc;
-            if ((i & 3) == 0) asm volatile("" ::: "memory");
+        } else if constexpr (kFuse) {
+            // the reverse scan's own operands: dt_r, B_r, C_r, A_r
+#pragma unroll
+            for (int i = kGroup - 1; i >= 0; --i) {
+                const float4 b4 = *reinterpret_cast<const float4 *>(&bcf[w][i][2][s0]);
+                const float4 c4 = *reinterpret_cast<const float4 *>(&bcf[w][i][3][s0]);
+                const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+                const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+                if ((i + 1) % L == 0) { hr[0] = hr[1] = hr[2] = hr[3] = 0.f; }
+                const float dlr = i < nvalid ? dt_elem(xd[w][3][i >> 2][(i & 3) * CW + cl]) : 0.f;
+                const float dxr = dlr * elem(xd[w][0][i >> 2][(i & 3) * CW + cl]);
+                float acc = ya[i];
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    hr[j] = __builtin_fmaf(fast_exp2(dlr * a2r[j]), hr[j], dxr * bv[j]);
+                    acc = __builtin_fmaf(cv[j], hr[j], acc);
+                }
+                ya[i] = acc;
+                if ((i & 3) == 0) asm volatile("" ::: "memory");
+            }
         }
         // reduce-scatter over the quad: after step 1 the lanes with g & 2
         // hold tokens 8..15, the others 0..7; after step 2 lane g holds
@@ -590,18 +656,18 @@ __global__ __launch_bounds__(4 * kWave) void bidir_wave_kernel(
             const float xv = elem(xd[w][0][g][q * CW + cl]);
             float tot = __builtin_fmaf(dsk, xv, r4[q]);
             if constexpr (kFuse) {
-                if (gate) tot *= silu_f(elem(xd[w][NS - 1][g][q * CW + cl]));
+                if (gate) tot *= silu_f(elem(xd[w][2][g][q * CW + cl]));
             }
             if (live && i < nvalid) ylane[(int64_t)(k0 + i) * D] = narrow<Tin>(tot);
         }
-        if (more) widen_bc(bcrn, bcfn, xdn);
+        if (more) widen_bc(bcrn, xdn);
     };
 
     issue(xdA, bcrA, 0);
-    widen_bc(bcrA, bcfA, xdA);
+    widen_bc(bcrA, xdA);
     for (int k0 = 0; k0 < len; k0 += 2 * kGroup) {
-        group(xdA, bcfA, xdB, bcrB, bcfB, k0);
-        if (k0 + kGroup < len) group(xdB, bcfB, xdA, bcrA, bcfA, k0 + kGroup);
+        group(xdA, xdB, bcrB, k0);
+        if (k0 + kGroup < len) group(xdB, xdA, bcrA, k0 + kGroup);
     }
     if (hout != nullptr && t_end == T && live) store_state(hout + ((int64_t)b * D + d) * kStates);
 }

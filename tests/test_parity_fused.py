@@ -144,3 +144,87 @@ def test_no_fusion_arguments_is_bitwise_unfused(dev):
     y2, _ = m.train_scan(*c.args(), 16, dt_bias=None, dt_softplus=False, z=None)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+# ---- separate reverse-direction operands
+
+def rev_case(c, batch, T, D, dtype, sid, with_bias):
+    dt_r = synth.positive_step((batch, T, D), 1000 * sid + 80, "cpu", dtype)
+    B_r = synth.normal((batch, T, N), 1000 * sid + 81, "cpu", dtype)
+    C_r = synth.normal((batch, T, N), 1000 * sid + 82, "cpu", dtype)
+    A_r = synth.a_matrix(D, N, "random", seed=1000 * sid + 83)
+    rev = {k: v.to("cuda").contiguous() for k, v in dict(dt=dt_r, B=B_r, C=C_r, A=A_r).items()}
+    if with_bias:
+        rev["dt_bias"] = synth.normal((D,), 1000 * sid + 84, "cuda", torch.float32, std=0.05)
+    return rev
+
+
+def rev_oracle(rev, t0=None, t1=None):
+    sl = (lambda t: t) if t0 is None else (lambda t: t[:, t0:t1])
+    out = dict(dt=synth.to_oracle(sl(rev["dt"])), B=synth.to_oracle(sl(rev["B"])),
+               C=synth.to_oracle(sl(rev["C"])), A=synth.to_oracle(rev["A"]))
+    if "dt_bias" in rev:
+        out["dt_bias"] = to_np(rev["dt_bias"])
+    return out
+
+
+def rev_sub(rev, t0, t1):
+    out = dict(rev)
+    for k in ("dt", "B", "C"):
+        out[k] = rev[k][:, t0:t1].contiguous()
+    return out
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("fused", [False, True])
+def test_reverse_operands_training_and_baseline(dev, dtype, fused, monkeypatch):
+    monkeypatch.setenv("BDSSM_CHUNK", "64")
+    batch, T, D, L = 2, 512, 130, 16
+    c = Case(batch, T, D, dtype, sid=55, a_kind="random")
+    rev = rev_case(c, batch, T, D, dtype, 55, with_bias=fused)
+    kw = dict(rev=rev)
+    ok = dict(rev=rev_oracle(rev))
+    if fused:
+        # both dt streams go through softplus with their own bias (positive
+        # inputs: the steps stay positive), and the output is gated
+        z = synth.normal((batch, T, D), 5590, "cuda", dtype)
+        bias = synth.normal((D,), 5591, "cuda", torch.float32, std=0.3)
+        kw.update(dt_bias=bias, dt_softplus=True, z=z)
+        ok.update(dt_bias=to_np(bias), dt_softplus=True, z=synth.to_oracle(z))
+    y, bnd = m.train_scan(*c.args(), L, want_bounds=True, **kw)
+    h0b = synth.normal((batch, T // L + 1, D, N), 5592, "cuda")
+    yb = m.train_scan_blocks(*c.args(), L, h0b, **kw)
+    yfull = m.full_scan(*c.args(), **kw)
+    torch.cuda.synchronize()
+    oa = c.oracle_args()
+    yo, bo = oracle.train_scan(*oa, L, want_bounds=True, **ok)
+    ybo = oracle.train_blocks(*oa, L, to_np(h0b), **ok)
+    yfo = oracle.full_scan(*oa, **ok)
+    tol = TOL[dtype]
+    assert rel_err(to_np(y), yo) < tol, worst(to_np(y), yo)
+    assert rel_err(to_np(bnd), bo) < STATE_TOL
+    assert rel_err(to_np(yb), ybo) < tol, worst(to_np(yb), ybo)
+    assert rel_err(to_np(yfull), yfo) < tol, worst(to_np(yfull), yfo)
+
+
+@pytest.mark.parametrize("L", [4, 16])
+def test_reverse_operands_inference_cycle(dev, L, monkeypatch):
+    monkeypatch.setenv("BDSSM_CHUNK", "64")
+    batch, D, P = 2, 96, 256
+    T = P + L
+    dtype = torch.bfloat16
+    c = Case(batch, T, D, dtype, sid=56, a_kind="random")
+    rev = rev_case(c, batch, T, D, dtype, 56, with_bias=False)
+    h, yp = m.prefill(*c.segment(0, P), L, want_y=True, rev=rev_sub(rev, 0, P))
+    ys = m.block_step(h, *c.segment(P, T), rev=rev_sub(rev, P, T))
+    hc = h.clone()
+    _, yc = m.commit(hc, *c.segment(P, T), want_y=True, rev=rev_sub(rev, P, T))
+    torch.cuda.synchronize()
+    ho, ypo = oracle.prefill(*c.oracle_args(0, P), L, want_y=True, rev=rev_oracle(rev, 0, P))
+    assert rel_err(to_np(h), ho) < STATE_TOL
+    assert rel_err(to_np(yp), ypo) < TOL[dtype], worst(to_np(yp), ypo)
+    yso = oracle.block_step(ho, *c.oracle_args(P, T), rev=rev_oracle(rev, P, T))
+    assert rel_err(to_np(ys), yso) < TOL[dtype], worst(to_np(ys), yso)
+    hco, yco = oracle.commit(ho, *c.oracle_args(P, T), want_y=True, rev=rev_oracle(rev, P, T))
+    assert rel_err(to_np(yc), yco) < TOL[dtype]
+    assert rel_err(to_np(hc), hco) < STATE_TOL
