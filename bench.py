@@ -142,6 +142,9 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="use the Mamba-1 fusions: the dt stream holds the raw step size, "
                          "dt = softplus(dt_raw + bias) inside the scan, block-step outputs gated by silu(z)")
+    ap.add_argument("--reverse-operands", action="store_true",
+                    help="give the in-block reverse scan its own dt, B, C and A (block steps, "
+                         "training forms and the baseline)")
     ap.add_argument("--crossover", action="store_true",
                     help="sweep the context length (8K..64K, batch 8, d_inner 1536) and report "
                          "block-restricted against full-sequence generation rates")
@@ -187,6 +190,8 @@ def main():
         bias = synth.normal((D,), 1000 * sid + 72, dev, torch.float32, std=0.3)
         fz_pf = dict(dt_bias=bias, dt_softplus=True)
         fz_bs = dict(fz_pf, z=synth.normal((batch, L, D), 1000 * sid + 73, dev, dtype))
+    if args.reverse_operands:
+        fz_bs = dict(fz_bs, rev=reverse_operands(synth, batch, L, D, sid, dtype, dev, torch))
     h = torch.empty(batch, D, NS, dtype=torch.float32, device=dev)
     y_blk = torch.empty(batch, L, D, dtype=dtype, device=dev)
     ws = torch.empty(max(1, m.workspace_bytes(batch, D, ctx, m.OP_PREFILL, L, NS, dtype)),
@@ -293,6 +298,8 @@ def main():
     # the fused path also reads the bias (4 D bytes per call) and the block
     # steps' gates (one element per (token, channel))
     fz_bytes_bs = (batch * L * D * e + 4 * D) if args.fused else 0
+    if args.reverse_operands:   # dt_r per (token, channel), B_r and C_r per token, A_r
+        fz_bytes_bs += batch * L * D * e + 2 * batch * L * NS * e + 4 * D * NS
     fz_bytes_pf = 4 * D if args.fused else 0
     step_bytes = (bytes_prefill(batch, ctx, D, e) + fz_bytes_pf
                   + nblk * (S * (bytes_block_step(batch, L, D, e) + fz_bytes_bs)
@@ -334,7 +341,7 @@ def main():
 
     # ---- contrast: full-sequence bidirectional baseline, rescanned every step
     baseline = None
-    if not args.no_baseline_scan and not args.fused:
+    if not args.no_baseline_scan and not args.fused and not args.reverse_operands:
         Tf = ctx + L
         del ws
         xf, dtf, Bf, Cf = synth.stream(batch, Tf, D, NS, sid, 200, dtype, dev)
@@ -352,7 +359,7 @@ def main():
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample of the same step
     cpu = None
-    if not args.no_cpu_baseline and not args.fused:
+    if not args.no_cpu_baseline and not args.fused and not args.reverse_operands:
         cpu = cpu_baseline(x, dt, Bm, Cm, A, Dskip, steps_in, commit_in, L, args.cpu_seconds, e)
 
     line = {
@@ -370,7 +377,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": batch, "d_inner": D, "d_state": NS,
                    "ctx": ctx, "block": L, "denoising_steps": S, "n_blocks": nblk,
-                   "launch": launch, "fused": bool(args.fused)},
+                   "launch": launch, "fused": bool(args.fused),
+                   "reverse_operands": bool(args.reverse_operands)},
         "hbm_frac_step": value / HBM_PEAK_GBS,
         "prefill_tokens_per_s": calls["prefill"]["tokens_per_s"],
         "block_step_GBs": calls["block_step"]["GBs"],
@@ -402,6 +410,8 @@ def train_main(args, wl, m, synth, torch):
         dt = synth.normal((batch, T, D), 1000 * sid + 70, dev, dtype, mean=-1.0, std=0.5)
         fz = dict(dt_bias=synth.normal((D,), 1000 * sid + 72, dev, torch.float32, std=0.3),
                   dt_softplus=True, z=synth.normal((batch, T, D), 1000 * sid + 73, dev, dtype))
+    if args.reverse_operands:
+        fz = dict(fz, rev=reverse_operands(synth, batch, T, D, sid, dtype, dev, torch))
     ws = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_TRAIN, L, NS, dtype)),
                      dtype=torch.uint8, device=dev)
     wsf = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_FULL, 1, NS, dtype)),
@@ -452,7 +462,7 @@ def train_main(args, wl, m, synth, torch):
     b.record(st)
     torch.cuda.synchronize()
     two_ms = a.elapsed_time(b) / args.steps
-    if args.fused:      # the backward entry points differentiate the unfused scan
+    if args.fused or args.reverse_operands:   # the backward differentiates the plain scan
         line = train_line(args, batch, D, T, L, dtype, nbytes, slots, ms_per_step, ev_ms,
                           blocks_ms, full_ms, two_ms, None, None, None, torch)
         print(json.dumps(line), flush=True)
@@ -502,6 +512,14 @@ def train_main(args, wl, m, synth, torch):
     return 0
 
 
+def reverse_operands(synth, batch, T, D, sid, dtype, dev, torch):
+    """Seeded operands of the reverse direction: dt_r, B_r, C_r, A_r."""
+    return dict(dt=synth.positive_step((batch, T, D), 1000 * sid + 80, dev, dtype),
+                B=synth.normal((batch, T, NS), 1000 * sid + 81, dev, dtype),
+                C=synth.normal((batch, T, NS), 1000 * sid + 82, dev, dtype),
+                A=synth.a_matrix(D, NS, "default", device=dev))
+
+
 def train_line(args, batch, D, T, L, dtype, nbytes, slots, ms_per_step, ev_ms, blocks_ms, full_ms,
                two_ms, bwd_ms, bbwd_ms, step_ms, torch):
     """The JSON line of a training workload (bwd_ms / bbwd_ms / step_ms are
@@ -514,7 +532,8 @@ def train_line(args, batch, D, T, L, dtype, nbytes, slots, ms_per_step, ev_ms, b
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if dtype == torch.bfloat16 else "f32", "data": "synthetic",
         "config": {"workload": args.workload, "batch": batch, "d_inner": D, "d_state": NS,
-                   "seq": T, "block": L, "fused": bool(args.fused)},
+                   "seq": T, "block": L, "fused": bool(args.fused),
+                   "reverse_operands": bool(args.reverse_operands)},
         "train_scan": {"ms": ev_ms, "tokens_per_s": batch * T / (ev_ms * 1e-3),
                        "GBs": nbytes / (ev_ms * 1e-3) / 1e9,
                        "valu_slot_frac": slots / (ev_ms * 1e-3) / VALU_SLOTS_PER_S,

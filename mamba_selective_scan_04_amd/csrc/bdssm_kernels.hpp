@@ -393,7 +393,7 @@ __global__ __launch_bounds__(256) void carry_kernel(
 // the forward ones, decays exp2(dt_r A_r') computed in the reverse pass).
 // grid = (ceil(D/64), chunks, batch), block = 256 (4 independent waves).
 template <typename Tin, int L, bool kBlockInit, bool kFuse = false>
-__global__ __launch_bounds__(4 * kWave) void bidir_wave_kernel(
+__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) void bidir_wave_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const Tin *__restrict__ Cm, const float *__restrict__ A, const float *__restrict__ Dskip,
     const float *hin, int64_t hin_bs, int64_t hin_cs,
