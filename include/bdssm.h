@@ -11,6 +11,7 @@
  *          "Methodik" (same text: Italian "Sintesi Tecnica" > "Metodologia",
  *          Portuguese "Resumo Técnico" > "Metodologia").
  *   [DE-P] same page, "Problemstellung".
+ *   [ZH]   gptget.net Chinese page, section "未来方向" (future directions).
  *
  * The operation.  Mamba's selective state-space mixer [ABS] with a diagonal
  * real A; the pages print no formula, so the standard Mamba-1 discretisation
@@ -53,9 +54,13 @@
  * this interface.  Outputs must not overlap inputs (only h_cache of
  * bdssm_commit is read and written in place).
  *
- * Limits of this version: d_state == 16; block_len in {1, 2, 4, 8, 16};
- * T % block_len == 0; x, dt, B, C, z, the reverse operands and y share one
- * dtype.
+ * Limits of this version: d_state == 16; T % block_len == 0; block_len is
+ * any value from 1 to 256 for the forward entry points (1, 2, 4, 8 and 16
+ * run the register-resident kernels, other lengths a kernel that stages one
+ * block's forward output in LDS, 256 * block_len bytes), and one of 1, 2, 4,
+ * 8, 16 for the backward entry points; x, dt, B, C, z, the reverse operands
+ * and y share one dtype.  The pages leave the block length open and name a
+ * dynamic block size as future work ([ZH] "未来方向").
  */
 #ifndef BDSSM_H
 #define BDSSM_H

@@ -10,7 +10,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "bdssm.hip")
-DEPS = [SRC, os.path.join(HERE, "csrc", "bdssm_kernels.hpp"), os.path.join(ROOT, "include", "bdssm.h")]
+DEPS = [SRC, os.path.join(HERE, "csrc", "bdssm_kernels.hpp"), os.path.join(HERE, "csrc", "bdssm_bwd_kernels.hpp"),
+        os.path.join(ROOT, "include", "bdssm.h")]
 LIB = os.path.join(HERE, "libbdssm.so")
 ARCH = os.environ.get("BDSSM_ARCH", "gfx950")
 

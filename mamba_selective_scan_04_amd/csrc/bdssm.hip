@@ -33,7 +33,7 @@ using namespace bdssm_dev;
 
 namespace {
 
-constexpr int kVersion = 10200;   // 1.2.0
+constexpr int kVersion = 10300;   // 1.3.0
 
 // 256 CUs x 4 SIMDs x 8 resident waves (the chunk kernel fits in 64 VGPRs)
 constexpr int64_t kFineWaves = 256 * 4 * 8;
@@ -127,22 +127,56 @@ Plan make_plan(int64_t batch, int64_t D, int64_t T, double prepass_weight = 0.45
     return p;
 }
 
+// Block lengths the register-resident wave kernels take (L divides their
+// 16-token group); every other L up to kMaxLdsBlock goes to block_bidir_kernel.
+bool wave_block(int64_t L) { return L == 1 || L == 2 || L == 4 || L == 8 || L == 16; }
+
 // Chunking of the two-stream forms: blocks are independent, so chunks only
 // add parallelism (no carry); aim for about four rounds of resident
 // workgroups.  Returns false if the chunk count exceeds the grid limit.
-bool blocks_plan(int64_t batch, int64_t D, int64_t T, int64_t *tc_out, int64_t *nc_out) {
+// Block lengths outside the wave kernels' set round the chunk up to whole
+// blocks (one wave per 64 channels there, so four times the chunks).
+bool blocks_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t *tc_out, int64_t *nc_out) {
+    const bool wave = wave_block(L);
+    const int64_t unit = wave ? kGroup : L;
     const int64_t groups = batch * ceil_div(D, kWave);
-    const int64_t ngroups16 = ceil_div(T, kGroup);
-    int64_t nc = ceil_div(4 * kCoarseGroups, groups);
-    if (nc > ngroups16) nc = ngroups16;
+    const int64_t nunits = ceil_div(T, unit);
+    int64_t nc = ceil_div((wave ? 4 : 16) * kCoarseGroups, groups);
+    if (nc > nunits) nc = nunits;
     if (nc < 1) nc = 1;
-    int64_t tc = ceil_div(ngroups16, nc) * kGroup;
-    const int64_t max_tok = ((((int64_t)1 << 31) - 1) / (D * 4)) / kGroup * kGroup;
+    int64_t tc = ceil_div(nunits, nc) * unit;
+    const int64_t max_tok = ((((int64_t)1 << 31) - 1) / (D * 4)) / unit * unit;
+    if (max_tok < unit) return false;
     if (tc > max_tok) tc = max_tok;
     nc = ceil_div(T, tc);
     *tc_out = tc;
     *nc_out = nc;
     return nc <= 65535;
+}
+
+// Chunking for the other block lengths: chunks are whole numbers of blocks,
+// about as long as make_plan's fine chunks, all aggregated by the forward
+// pre-pass and each scanned by one block_bidir_kernel workgroup column.
+// Returns false if no such chunking fits the grid or the 32-bit offsets.
+bool plan_general(int64_t batch, int64_t D, int64_t T, int64_t L, Plan *out) {
+    const Plan base = make_plan(batch, D, T);
+    int64_t tc = ceil_div(base.fine_len, L) * L;
+    const int64_t max_tok = (((int64_t)1 << 31) - 1) / (D * 4);
+    if (tc > max_tok) tc = (max_tok / L) * L;
+    if (tc < L || T == 0) { if (T != 0) return false; tc = L; }
+    const int64_t n = T == 0 ? 1 : ceil_div(T, tc);
+    if (n > 65535) return false;
+    out->fine_len = tc;
+    out->n_fine = (int)n;
+    out->per_coarse = 1;
+    out->n_coarse = (int)n;
+    return true;
+}
+
+// The plan of the forward entry points for block length L.
+bool plan_for(int64_t batch, int64_t D, int64_t T, int64_t L, Plan *out) {
+    if (wave_block(L)) { *out = make_plan(batch, D, T); return true; }
+    return plan_general(batch, D, T, L, out);
 }
 
 // Workspace layout (fp32 arrays, each 256-byte aligned):
@@ -227,7 +261,7 @@ int check_shape(const bdssm_shape *s) {
     if (s->batch < 0 || s->d_inner < 0) return BDSSM_ERR_SHAPE;
     if (s->d_state != kStates) return BDSSM_ERR_SHAPE;
     const int64_t L = s->block_len;
-    if (!(L == 1 || L == 2 || L == 4 || L == 8 || L == 16)) return BDSSM_ERR_SHAPE;
+    if (L < 1 || (!wave_block(L) && L > kMaxLdsBlock)) return BDSSM_ERR_SHAPE;
     // d_inner bound keeps a 16-token group of one stream within 32-bit buffer offsets
     if (s->d_inner > (int64_t)1 << 24 || s->batch > 65535) return BDSSM_ERR_SHAPE;
     return BDSSM_OK;
@@ -354,6 +388,9 @@ Fuse resolve_fusion(const bdssm_fusion *f, bool with_y) {
     if (with_y && f->dt_rev != nullptr) {
         r.dt_r = f->dt_rev; r.B_r = f->B_rev; r.C_r = f->C_rev;
         r.A_r = f->A_rev; r.dt_bias_r = f->dt_bias_rev;
+        // a reverse bias needs the biased transform even when the forward
+        // direction has none (its bias then reads as zero)
+        if (r.dt_mode == kDtPlain && r.dt_bias_r != nullptr) r.dt_mode = kDtBias;
     }
     return r;
 }
@@ -441,12 +478,58 @@ void launch_bidir_L(const void *x, const void *dt, const void *B, const void *C,
     }
 }
 
+template <typename Tin, int kN, bool kInit, int kDt>
+void launch_block_bidir_k(dim3 g, int64_t L, const void *x, const void *dt, const void *B,
+                          const void *C, const float *A, const float *Dskip, const float *hin,
+                          int64_t hin_bs, int64_t hin_cs, void *y, float *bounds, float *hout,
+                          int64_t T, int64_t D, int64_t Tc, const float *h0_blocks, const Fuse &f,
+                          hipStream_t st) {
+    const size_t lds = (size_t)L * kWave * sizeof(float);
+    hipLaunchKernelGGL((block_bidir_kernel<Tin, kN, kInit, kDt>), g, dim3(kWave), lds, st,
+                       (const Tin *)x, (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip,
+                       hin, hin_bs, hin_cs, (Tin *)y, bounds, hout, T, (int)D, (int)L, Tc,
+                       h0_blocks, f.args<Tin>());
+}
+
+// Bidirectional pass with block_bidir_kernel (any L <= kMaxLdsBlock; Tc a
+// multiple of L).
+template <typename Tin, int kN>
+void launch_block_bidir(int64_t L, const void *x, const void *dt, const void *B, const void *C,
+                        const float *A, const float *Dskip, const float *hin, int64_t hin_bs,
+                        int64_t hin_cs, void *y, float *bounds, float *hout, int64_t batch,
+                        int64_t T, int64_t D, int64_t Tc, int n_chunks, const float *h0_blocks,
+                        const Fuse &f, hipStream_t st) {
+    const dim3 g = grid3(D, n_chunks, batch);
+#define BDSSM_BLOCK(INIT, KDT)                                                                       \
+    launch_block_bidir_k<Tin, kN, INIT, KDT>(g, L, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, \
+                                             hout, T, D, Tc, h0_blocks, f, st)
+    if (h0_blocks != nullptr) {
+        switch (f.dt_mode) {
+        case kDtSoftplus: BDSSM_BLOCK(true, kDtSoftplus); break;
+        case kDtBias: BDSSM_BLOCK(true, kDtBias); break;
+        default: BDSSM_BLOCK(true, kDtPlain); break;
+        }
+    } else {
+        switch (f.dt_mode) {
+        case kDtSoftplus: BDSSM_BLOCK(false, kDtSoftplus); break;
+        case kDtBias: BDSSM_BLOCK(false, kDtBias); break;
+        default: BDSSM_BLOCK(false, kDtPlain); break;
+        }
+    }
+#undef BDSSM_BLOCK
+}
+
 template <typename Tin>
 void launch_bidir(int64_t L, const void *x, const void *dt, const void *B, const void *C,
                   const float *A, const float *Dskip, const float *hin, int64_t hin_bs,
                   int64_t hin_cs, void *y, float *bounds, float *hout, int64_t batch, int64_t T,
                   int64_t D, int64_t Tc, int n_chunks, hipStream_t st,
                   const float *h0_blocks = nullptr, const Fuse &f = Fuse()) {
+    if (!wave_block(L)) {
+        launch_block_bidir<Tin, kStates>(L, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds,
+                                         hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st);
+        return;
+    }
     switch (L) {
     case 1: launch_bidir_L<Tin, 1>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
     case 2: launch_bidir_L<Tin, 2>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
@@ -634,10 +717,12 @@ size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T, int op) {
     }
     if (op == BDSSM_OP_BLOCKS_BWD) {
         int64_t tc, nc;
-        if (!blocks_plan(batch, D, T, &tc, &nc)) return (size_t)-1;
+        if (!blocks_plan(batch, D, T, shape->block_len, &tc, &nc)) return (size_t)-1;
         return layout_bwd(nullptr, batch, D, T, 1, nc, false).bytes;
     }
-    const Plan p = make_plan(batch, D, T);
+    Plan p;
+    if (op == BDSSM_OP_FULL) p = make_plan(batch, D, T);
+    else if (!plan_for(batch, D, T, shape->block_len, &p)) return (size_t)-1;
     return layout_ws(nullptr, batch, D, T, p, op).bytes;
 }
 
@@ -669,7 +754,8 @@ int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const 
     const Fuse f = resolve_fusion(fusion, with_y);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (t_ctx == 0) return copy_or_zero(h_init, h_cache, batch * D * kStates, st);
-    const Plan p = make_plan(batch, D, t_ctx);
+    Plan p;
+    if (!plan_for(batch, D, t_ctx, shape->block_len, &p)) return BDSSM_ERR_SHAPE;
     const Workspace probe = layout_ws(nullptr, batch, D, t_ctx, p, BDSSM_OP_PREFILL);
     if (probe.bytes > 0 && (ws == nullptr || ws_bytes < probe.bytes)) return BDSSM_ERR_WORKSPACE;
     if (probe.bytes > 0) {
@@ -711,9 +797,9 @@ int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void 
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (shape->dtype == BDSSM_BF16)
-        launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, nullptr, batch, L, D, kGroup, 1, st, nullptr, f);
+        launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, nullptr, batch, L, D, L, 1, st, nullptr, f);
     else
-        launch_bidir<float>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, nullptr, batch, L, D, kGroup, 1, st, nullptr, f);
+        launch_bidir<float>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, nullptr, batch, L, D, L, 1, st, nullptr, f);
     return launch_status();
 }
 
@@ -741,11 +827,11 @@ int bdssm_commit(const bdssm_shape *shape, float *h_cache, const void *x, const 
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (shape->dtype == BDSSM_BF16) {
-        if (with_y) launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, h_cache, batch, L, D, kGroup, 1, st, nullptr, f);
-        else launch_chunk_state<uint16_t>(false, x, dt, B, A, h_cache, h_cache, nullptr, batch, L, D, kGroup, 1, 0, 1, st, f);
+        if (with_y) launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, h_cache, batch, L, D, L, 1, st, nullptr, f);
+        else launch_chunk_state<uint16_t>(false, x, dt, B, A, h_cache, h_cache, nullptr, batch, L, D, L, 1, 0, 1, st, f);
     } else {
-        if (with_y) launch_bidir<float>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, h_cache, batch, L, D, kGroup, 1, st, nullptr, f);
-        else launch_chunk_state<float>(false, x, dt, B, A, h_cache, h_cache, nullptr, batch, L, D, kGroup, 1, 0, 1, st, f);
+        if (with_y) launch_bidir<float>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, h_cache, batch, L, D, L, 1, st, nullptr, f);
+        else launch_chunk_state<float>(false, x, dt, B, A, h_cache, h_cache, nullptr, batch, L, D, L, 1, 0, 1, st, f);
     }
     return launch_status();
 }
@@ -765,7 +851,8 @@ int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const v
     if (!aligned16(h_init) || !aligned16(y) || !aligned16(h_bounds) || !aligned16(ws))
         return BDSSM_ERR_ALIGN;
     const size_t nbnd = (size_t)batch * (T / L + 1) * D * kStates * 4;
-    const Plan p = make_plan(batch, D, T);
+    Plan p;
+    if (!plan_for(batch, D, T, L, &p)) return BDSSM_ERR_SHAPE;
     const Workspace probe = layout_ws(nullptr, batch, D, T, p, BDSSM_OP_TRAIN);
     rc = check_alias(shape, T, x, dt, B, C, A, Dskip, h_init,
                      {Range{y, (size_t)batch * T * D * esize(shape)}, Range{h_bounds, nbnd},
@@ -812,7 +899,7 @@ int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, 
     if (rc) return rc;
     const Fuse f = resolve_fusion(fusion, true);
     int64_t tc, nc;
-    if (!blocks_plan(batch, D, T, &tc, &nc)) return BDSSM_ERR_SHAPE;
+    if (!blocks_plan(batch, D, T, L, &tc, &nc)) return BDSSM_ERR_SHAPE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (shape->dtype == BDSSM_BF16)
@@ -870,6 +957,8 @@ int check_bwd(const bdssm_shape *shape, int64_t T, const void *x, const void *dt
     int rc = check_shape(shape);
     if (rc) return rc;
     if (T < 0 || T % shape->block_len != 0) return BDSSM_ERR_SHAPE;
+    // the backward kernels keep a block inside one 16-token group
+    if (!wave_block(shape->block_len)) return BDSSM_ERR_SHAPE;
     rc = check_streams(shape, T, x, dt, B, C, true, A, Dskip, true);
     if (rc) return rc;
     const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len;
@@ -995,7 +1084,7 @@ int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void 
         return zero_bwd(D, dA, dDskip, dh0_blocks, batch * D * kStates, st);
     if (!aligned16(ws)) return BDSSM_ERR_ALIGN;
     int64_t tc, nc;
-    if (!blocks_plan(batch, D, T, &tc, &nc)) return BDSSM_ERR_SHAPE;
+    if (!blocks_plan(batch, D, T, L, &tc, &nc)) return BDSSM_ERR_SHAPE;
     const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, 1, nc, false);
     if (ws == nullptr || ws_bytes < probe.bytes) return BDSSM_ERR_WORKSPACE;
     const size_t e = esize(shape);

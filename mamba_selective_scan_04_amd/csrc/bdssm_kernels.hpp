@@ -29,12 +29,14 @@
 // * Parallelism over time comes from chunking: chunk-local forward aggregates
 //   (decay exponent sum S = sum dt and the local end state), a tiny carry
 //   kernel that chains them, then a final pass that starts every chunk from
-//   its exact incoming state.  Chunks are multiples of 16 tokens, so an
-//   L-block (L | 16) never straddles two chunks.
+//   its exact incoming state.  Chunks are multiples of 16 tokens (of L for
+//   other block lengths), so an L-block never straddles two chunks.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace bdssm_dev {
 
@@ -782,6 +784,193 @@ __global__ __launch_bounds__(kWave) void sweep_output_kernel(
     if (rem > 0) {
         load_stage(n_full * U, rem, xr, dr, yr);
         consume(xr, dr, yr, n_full * U, rem);
+    }
+}
+
+// ------------------------------------------------------------------------
+// Rows of kN fp32 values (A rows, states): float4 accesses when kN % 4 == 0.
+template <int kN> __device__ __forceinline__ void load_row(const float *p, float *v) {
+    if constexpr (kN % 4 == 0) {
+#pragma unroll
+        for (int q = 0; q < kN / 4; ++q) {
+            const float4 t = reinterpret_cast<const float4 *>(p)[q];
+            v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) v[n] = p[n];
+    }
+}
+template <int kN> __device__ __forceinline__ void store_row(float *p, const float *v) {
+    if constexpr (kN % 4 == 0) {
+#pragma unroll
+        for (int q = 0; q < kN / 4; ++q)
+            reinterpret_cast<float4 *>(p)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    } else {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) p[n] = v[n];
+    }
+}
+
+// ------------------------------------------------------------------------
+// Bidirectional pass for any block length up to kMaxLdsBlock (T % L == 0)
+// and any even state count kN: one lane per channel, the kN states of the
+// forward and of the reverse scan in registers, one wave per workgroup.
+// Every L-block of the chunk is walked twice:
+//   * left to right with the forward state (carried across the chunk's
+//     blocks; kBlockInit: restarted from h0_blocks at every block), the
+//     per-token forward output yf_t = sum_n C_t hf_t going to LDS;
+//   * right to left with the reverse state from zero, adding yr_t + Dskip x_t
+//     to yf_t and storing y (times silu(z_t) when the gate is given).
+// The second walk forms its decays again: a block may be longer than the
+// registers can hold, and the rows it re-reads are the block's own, still in
+// L2.  LDS holds one fp32 value per token and channel of a block: 256 * L
+// bytes of dynamic shared memory.
+// Chunks are whole numbers of blocks (Tc % L == 0).  hin, bounds, hout and the
+// fusions as in bidir_wave_kernel (states are [.., kN] instead of [.., 16]);
+// with separate reverse operands the reverse walk reads dt_r (with dt_bias_r,
+// same transform), B_r, C_r and A_r.
+// grid = (ceil(D/64), chunks, batch), block = 64.
+constexpr int kMaxLdsBlock = 256;
+
+template <typename Tin, int kN, bool kBlockInit, int kDt>
+__global__ __launch_bounds__(kWave) void block_bidir_kernel(
+    const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
+    const Tin *__restrict__ Cm, const float *__restrict__ A, const float *__restrict__ Dskip,
+    const float *hin, int64_t hin_bs, int64_t hin_cs, Tin *__restrict__ y,
+    float *__restrict__ bounds, float *hout, int64_t T, int D, int L, int64_t Tc,
+    const float *__restrict__ h0_blocks, FuseArgs<Tin> fz)
+{
+    static_assert(kN % 2 == 0, "B and C rows are read in pairs");
+    extern __shared__ float yf_lds[];             // [L][64]
+    constexpr int U = 4;                          // tokens per pipeline stage
+    const int lane = threadIdx.x;
+    const int d_raw = blockIdx.x * kWave + lane;
+    const bool live = d_raw < D;
+    const int d = live ? d_raw : D - 1;
+    const int c = blockIdx.y;
+    const int b = blockIdx.z;
+    const int64_t t_begin = (int64_t)c * Tc;
+    const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
+    const int len = (int)(t_end - t_begin);      // a multiple of L
+    const int64_t nbl = T / L;
+    const bool gate = fz.z != nullptr;
+    const bool sep = fz.dt_r != nullptr;
+
+    float a2[kN], a2r[kN], h[kN], hr[kN];
+    load_row<kN>(A + (int64_t)d * kN, a2);
+    load_row<kN>((sep ? fz.A_r : A) + (int64_t)d * kN, a2r);
+#pragma unroll
+    for (int n = 0; n < kN; ++n) { a2[n] *= kLog2e; a2r[n] *= kLog2e; }
+    if (!kBlockInit && hin != nullptr) {
+        load_row<kN>(hin + (int64_t)b * hin_bs + (int64_t)c * hin_cs + (int64_t)d * kN, h);
+    } else {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) h[n] = 0.f;
+    }
+    const float dsk = Dskip[d];
+    const float bias = (kDt != kDtPlain && fz.dt_bias != nullptr) ? fz.dt_bias[d] : 0.f;
+    const float bias_r = sep ? ((kDt != kDtPlain && fz.dt_bias_r != nullptr) ? fz.dt_bias_r[d] : 0.f) : bias;
+
+    const int64_t first = (int64_t)b * T + t_begin;
+    const Rows<Tin> xs(x + first * D, len, D, d);
+    const Rows<Tin> ds(dt + first * D, len, D, d);
+    const Rows<Tin> rds((sep ? fz.dt_r : dt) + first * D, len, D, d);
+    const Rows<Tin> zs((gate ? fz.z : x) + first * D, len, D, d);
+    const Rows<Tin> ys(y + first * D, len, D, d);
+    const Tin *bs = Bm + first * kN, *cs = Cm + first * kN;
+    const Tin *rbs = (sep ? fz.B_r : Bm) + first * kN, *rcs = (sep ? fz.C_r : Cm) + first * kN;
+
+    // one token of the forward walk (row p of the chunk, row r of the block)
+    auto fwd_tok = [&](int p, int r, float xv, float dl) {
+        const float dx = dl * xv;
+        const Tin *brow = bs + (int64_t)p * kN, *crow = cs + (int64_t)p * kN;
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int q = 0; q < kN / 2; ++q) {
+            float b0, b1, c0, c1;
+            load_pair(brow, q, b0, b1);
+            load_pair(crow, q, c0, c1);
+            h[2 * q] = __builtin_fmaf(fast_exp2(dl * a2[2 * q]), h[2 * q], dx * b0);
+            h[2 * q + 1] = __builtin_fmaf(fast_exp2(dl * a2[2 * q + 1]), h[2 * q + 1], dx * b1);
+            acc0 = __builtin_fmaf(c0, h[2 * q], acc0);
+            acc1 = __builtin_fmaf(c1, h[2 * q + 1], acc1);
+        }
+        yf_lds[r * kWave + lane] = acc0 + acc1;
+    };
+    // one token of the reverse walk
+    auto rev_tok = [&](int p, int r, float xv, float dl, float zv) {
+        const float dx = dl * xv;
+        const Tin *brow = rbs + (int64_t)p * kN, *crow = rcs + (int64_t)p * kN;
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int q = 0; q < kN / 2; ++q) {
+            float b0, b1, c0, c1;
+            load_pair(brow, q, b0, b1);
+            load_pair(crow, q, c0, c1);
+            hr[2 * q] = __builtin_fmaf(fast_exp2(dl * a2r[2 * q]), hr[2 * q], dx * b0);
+            hr[2 * q + 1] = __builtin_fmaf(fast_exp2(dl * a2r[2 * q + 1]), hr[2 * q + 1], dx * b1);
+            acc0 = __builtin_fmaf(c0, hr[2 * q], acc0);
+            acc1 = __builtin_fmaf(c1, hr[2 * q + 1], acc1);
+        }
+        float tot = __builtin_fmaf(dsk, xv, yf_lds[r * kWave + lane] + (acc0 + acc1));
+        if (gate) tot *= silu_f(zv);
+        if (live) ys.store(p, narrow<Tin>(tot));
+    };
+    // walk the block starting at chunk row k0, forward or reverse; the rows of
+    // the next U tokens are loaded before the arithmetic of the current U
+    auto walk = [&](auto rev_tag, int k0) {
+        constexpr bool R = decltype(rev_tag)::value;
+        const Rows<Tin> &dsrc = R ? rds : ds;
+        const int nst = (L + U - 1) / U;
+        auto pos = [&](int k) { return R ? k0 + L - 1 - k : k0 + k; };
+        auto stage = [&](int s, Tin *xo, Tin *dout, Tin *zo) {
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const int k = (s * U + i < L) ? s * U + i : L - 1;
+                const int p = pos(k);
+                xo[i] = xs.load(p);
+                dout[i] = dsrc.load(p);
+                zo[i] = (R && gate) ? zs.load(p) : xo[i];
+            }
+        };
+        Tin xr[U], dr[U], zr[U];
+        stage(0, xr, dr, zr);
+        for (int s = 0; s < nst; ++s) {
+            Tin xn[U], dn[U], zn[U];
+            if (s + 1 < nst) stage(s + 1, xn, dn, zn);
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const int k = s * U + i;
+                if (k < L) {
+                    const int p = pos(k);
+                    if constexpr (R)
+                        rev_tok(p, p - k0, widen(xr[i]), step_size<kDt>(widen(dr[i]), bias_r), widen(zr[i]));
+                    else
+                        fwd_tok(p, p - k0, widen(xr[i]), step_size<kDt>(widen(dr[i]), bias));
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < U; ++i) { xr[i] = xn[i]; dr[i] = dn[i]; zr[i] = zn[i]; }
+        }
+    };
+
+    for (int k0 = 0; k0 < len; k0 += L) {
+        const int64_t blk = (t_begin + k0) / L;
+        if constexpr (kBlockInit) {
+            load_row<kN>(h0_blocks + (((int64_t)b * (nbl + 1) + blk) * D + d) * kN, h);
+        } else if (bounds != nullptr && live) {
+            store_row<kN>(bounds + (((int64_t)b * (nbl + 1) + blk) * D + d) * kN, h);
+        }
+        walk(std::false_type{}, k0);
+#pragma unroll
+        for (int n = 0; n < kN; ++n) hr[n] = 0.f;
+        walk(std::true_type{}, k0);
+    }
+    if (t_end == T && live) {
+        if (!kBlockInit && bounds != nullptr)
+            store_row<kN>(bounds + (((int64_t)b * (nbl + 1) + nbl) * D + d) * kN, h);
+        if (hout != nullptr) store_row<kN>(hout + ((int64_t)b * D + d) * kN, h);
     }
 }
 

@@ -28,7 +28,7 @@ def test_exports_match_header():
 
 
 def test_version_and_status_strings():
-    assert m.version() == 10200
+    assert m.version() == 10300
     for code in range(-7, 1):
         assert m.status_str(code) not in ("", "unknown status")
     assert m.status_str(-99) == "unknown status"
@@ -58,8 +58,10 @@ def prefill(s, T, x=FAKE, dt=FAKE + 0x1000, Bm=FAKE + 0x2000, C=FAKE + 0x3000, A
 
 def test_shape_errors():
     assert prefill(shape(N=8), 16) == -2
-    assert prefill(shape(L=3), 15) == -2
-    assert prefill(shape(L=32), 32) == -2
+    assert prefill(shape(L=0), 16) == -2
+    assert prefill(shape(L=-4), 16) == -2
+    assert prefill(shape(L=3), 16) == -2         # T % L != 0 for a block length off the wave set
+    assert prefill(shape(L=257), 257) == -2      # beyond the LDS-staged block kernel
     assert prefill(shape(), 24) == -2            # T % L != 0
     assert prefill(shape(), -16) == -2
     assert prefill(shape(batch=-1), 16) == -2
@@ -121,6 +123,11 @@ def test_workspace_sizes():
     assert m.workspace_bytes(1, 64, 16, m.OP_FULL) >= 64 * 16 * 4
     with pytest.raises(ValueError):
         m.workspace_bytes(1, 64, 24, m.OP_TRAIN, block_len=16)
+    # other block lengths chunk by whole blocks; short sequences need none
+    assert m.workspace_bytes(1, 64, 32, m.OP_TRAIN, block_len=32) == 0
+    assert m.workspace_bytes(8, 1536, 4800, m.OP_TRAIN, block_len=48) > 0
+    with pytest.raises(ValueError):
+        m.workspace_bytes(1, 64, 512, m.OP_TRAIN, block_len=512)
     # monotone in T
     a = m.workspace_bytes(8, 1536, 4096, m.OP_TRAIN)
     b = m.workspace_bytes(8, 1536, 8192, m.OP_TRAIN)
@@ -158,6 +165,8 @@ def test_backward_argument_errors():
     s = shape(D=8)
     assert train_bwd(shape(N=8), 16) == -2
     assert train_bwd(s, 24) == -2                      # T % L != 0
+    assert train_bwd(shape(D=8, L=32), 32) == -2       # the backward takes L | 16 only
+    assert train_bwd(shape(D=8, L=3), 48) == -2
     assert train_bwd(s, 16, hb=None) == -1             # saved block states required
     assert train_bwd(s, 16, dy=None) == -1
     assert train_bwd(s, 16, dA=None) == -1

@@ -1,0 +1,208 @@
+"""GPU parity of the block lengths outside {1, 2, 4, 8, 16} (block_bidir_kernel:
+one lane per channel, each block's forward output staged in LDS) on every
+forward entry point, against the fp64 oracle, element by element: lengths
+that are not powers of two, multiples of 16, the largest supported (256),
+ragged channel counts, forced multi-chunk plans (chunks rounded up to whole
+blocks, so the forward carry runs), the two-stream form, the fusions and
+separate reverse operands.  Also the regression case of a reverse step-size
+bias given without a forward one, on both bidirectional kernels.
+"""
+import pytest
+import torch
+
+import mamba_selective_scan_04_amd as m
+import oracle
+from mamba_selective_scan_04_amd import synth
+from parity_util import Case, N, STATE_TOL, TOL, rel_err, to_np, worst
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request, dev):
+    print("\n[parity-blocklen] %s" % request.node.name, flush=True)
+    yield
+
+
+def close(got, ref, tol, what):
+    g = to_np(got)
+    assert g.shape == ref.shape, (what, g.shape, ref.shape)
+    e = rel_err(g, ref)
+    assert e < tol, (what, e, worst(g, ref))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("L,T,D", [(3, 96, 70), (5, 200, 64), (12, 240, 130), (24, 480, 96),
+                                   (32, 512, 200), (48, 480, 64), (100, 400, 65), (256, 768, 96)])
+def test_training_forms(dev, dtype, L, T, D, monkeypatch):
+    """train_scan (with block states) and the two-stream form, several chunks."""
+    monkeypatch.setenv("BDSSM_CHUNK", "64")
+    batch = 2
+    c = Case(batch, T, D, dtype, sid=61, a_kind="random")
+    y, bnd = m.train_scan(*c.args(), L, want_bounds=True)
+    h0b = synth.normal((batch, T // L + 1, D, N), 6101, "cuda")
+    yb = m.train_scan_blocks(*c.args(), L, h0b)
+    torch.cuda.synchronize()
+    oa = c.oracle_args()
+    yo, bo = oracle.train_scan(*oa, L, want_bounds=True)
+    ybo = oracle.train_blocks(*oa, L, to_np(h0b))
+    close(y, yo, TOL[dtype], "train_scan y")
+    close(bnd, bo, STATE_TOL, "h_bounds")
+    close(yb, ybo, TOL[dtype], "train_scan_blocks y")
+
+
+@pytest.mark.parametrize("a_kind", ["default", "long"])
+def test_training_single_chunk_with_h_init(dev, a_kind):
+    """One chunk (no carry), a given start state, long-memory A."""
+    batch, T, D, L = 2, 192, 128, 32
+    c = Case(batch, T, D, torch.float32, sid=62, a_kind=a_kind)
+    h0 = synth.normal((batch, D, N), 6201, "cuda")
+    y, bnd = m.train_scan(*c.args(), L, h_init=h0, want_bounds=True)
+    torch.cuda.synchronize()
+    yo, bo = oracle.train_scan(*c.oracle_args(), L, h_init=to_np(h0), want_bounds=True)
+    close(y, yo, TOL[torch.float32], "y")
+    close(bnd, bo, STATE_TOL, "h_bounds")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("L", [6, 32, 64, 256])
+def test_inference_cycle(dev, dtype, L, monkeypatch):
+    """prefill (state only and with y) over a multi-chunk context, block step,
+    commit with and without y; the block step equals the training form's
+    last block (exact caching)."""
+    monkeypatch.setenv("BDSSM_CHUNK", "64")
+    batch, D = 2, 130
+    P = 6 * L if L <= 64 else 2 * L
+    T = P + 2 * L
+    c = Case(batch, T, D, dtype, sid=63, a_kind="random")
+    h, yp = m.prefill(*c.segment(0, P), L, want_y=True)
+    h2, _ = m.prefill(*c.segment(0, P), L)
+    ys = m.block_step(h, *c.segment(P, P + L))
+    hc = h.clone()
+    _, yc = m.commit(hc, *c.segment(P, P + L), want_y=True)
+    hc2 = hc.clone()
+    m.commit(hc2, *c.segment(P + L, T))
+    yt, _ = m.train_scan(*c.segment(0, P + L), L)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    ho, ypo = oracle.prefill(*c.oracle_args(0, P), L, want_y=True)
+    close(h, ho, STATE_TOL, "prefill state")
+    close(h2, ho, STATE_TOL, "prefill state (state only)")
+    close(yp, ypo, tol, "prefill y")
+    yso = oracle.block_step(ho, *c.oracle_args(P, P + L))
+    close(ys, yso, tol, "block_step y")
+    hco, yco = oracle.commit(ho, *c.oracle_args(P, P + L), want_y=True)
+    close(yc, yco, tol, "commit y")
+    close(hc, hco, STATE_TOL, "commit state")
+    hco2, _ = oracle.commit(hco, *c.oracle_args(P + L, T))
+    close(hc2, hco2, STATE_TOL, "commit state (no y)")
+    close(ys, to_np(yt)[:, P:], tol, "block_step vs train_scan's last block")
+
+
+@pytest.mark.parametrize("D", [1, 63, 64, 65])
+def test_ragged_channels(dev, D):
+    batch, T, L = 3, 96, 24
+    c = Case(batch, T, D, torch.float32, sid=64, a_kind="random")
+    y, bnd = m.train_scan(*c.args(), L, want_bounds=True)
+    torch.cuda.synchronize()
+    yo, bo = oracle.train_scan(*c.oracle_args(), L, want_bounds=True)
+    close(y, yo, TOL[torch.float32], "y")
+    close(bnd, bo, STATE_TOL, "h_bounds")
+
+
+def test_block_equal_to_sequence_is_the_full_scan(dev):
+    """L = T: the in-block reverse covers the whole sequence, as the baseline."""
+    batch, T, D = 2, 192, 96
+    c = Case(batch, T, D, torch.float32, sid=65, a_kind="random")
+    y, _ = m.train_scan(*c.args(), T)
+    yf = m.full_scan(*c.args())
+    torch.cuda.synchronize()
+    yo = oracle.full_scan(*c.oracle_args())
+    close(y, yo, TOL[torch.float32], "train_scan L = T")
+    close(yf, yo, TOL[torch.float32], "full_scan")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("mode", ["softplus_bias", "bias"])
+def test_fusions(dev, dtype, mode, monkeypatch):
+    """dt = softplus(dt_raw + bias) or dt_raw + bias, gate silu(z), L = 40."""
+    monkeypatch.setenv("BDSSM_CHUNK", "64")
+    batch, T, D, L = 2, 400, 100, 40
+    c = Case(batch, T, D, dtype, sid=66, a_kind="random")
+    mean = -1.0 if mode == "softplus_bias" else 1.0
+    std = 0.5 if mode == "softplus_bias" else 0.1
+    c.dev["dt"] = synth.normal((batch, T, D), 6601, "cpu", torch.float32, mean=mean,
+                               std=std).to(dtype).to("cuda").contiguous()
+    bias = synth.normal((D,), 6602, "cuda", torch.float32, std=0.3 if mode == "softplus_bias" else 0.05)
+    z = synth.normal((batch, T, D), 6603, "cuda", dtype, std=2.0)
+    kw = dict(dt_bias=bias, dt_softplus=mode == "softplus_bias", z=z)
+    ok = dict(dt_bias=to_np(bias), dt_softplus=kw["dt_softplus"], z=synth.to_oracle(z))
+    y, bnd = m.train_scan(*c.args(), L, want_bounds=True, **kw)
+    h0b = synth.normal((batch, T // L + 1, D, N), 6604, "cuda")
+    yb = m.train_scan_blocks(*c.args(), L, h0b, **kw)
+    torch.cuda.synchronize()
+    oa = c.oracle_args()
+    yo, bo = oracle.train_scan(*oa, L, want_bounds=True, **ok)
+    ybo = oracle.train_blocks(*oa, L, to_np(h0b), **ok)
+    close(y, yo, TOL[dtype], "y")
+    close(bnd, bo, STATE_TOL, "h_bounds")
+    close(yb, ybo, TOL[dtype], "two-stream y")
+
+
+def _rev_operands(batch, T, D, dtype, sid, with_bias):
+    rev = dict(dt=synth.positive_step((batch, T, D), 1000 * sid + 80, "cpu", dtype),
+               B=synth.normal((batch, T, N), 1000 * sid + 81, "cpu", dtype),
+               C=synth.normal((batch, T, N), 1000 * sid + 82, "cpu", dtype),
+               A=synth.a_matrix(D, N, "random", seed=1000 * sid + 83))
+    rev = {k: v.to("cuda").contiguous() for k, v in rev.items()}
+    if with_bias:
+        rev["dt_bias"] = synth.normal((D,), 1000 * sid + 84, "cuda", torch.float32, std=0.05)
+    return rev
+
+
+def _rev_oracle(rev):
+    out = dict(dt=synth.to_oracle(rev["dt"]), B=synth.to_oracle(rev["B"]),
+               C=synth.to_oracle(rev["C"]), A=synth.to_oracle(rev["A"]))
+    if "dt_bias" in rev:
+        out["dt_bias"] = to_np(rev["dt_bias"])
+    return out
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_reverse_operands(dev, dtype, monkeypatch):
+    monkeypatch.setenv("BDSSM_CHUNK", "64")
+    batch, T, D, L = 2, 384, 96, 48
+    c = Case(batch, T, D, dtype, sid=67, a_kind="random")
+    rev = _rev_operands(batch, T, D, dtype, 67, with_bias=False)
+    y, bnd = m.train_scan(*c.args(), L, want_bounds=True, rev=rev)
+    h0b = synth.normal((batch, T // L + 1, D, N), 6701, "cuda")
+    yb = m.train_scan_blocks(*c.args(), L, h0b, rev=rev)
+    torch.cuda.synchronize()
+    oa = c.oracle_args()
+    ro = _rev_oracle(rev)
+    yo, bo = oracle.train_scan(*oa, L, want_bounds=True, rev=ro)
+    ybo = oracle.train_blocks(*oa, L, to_np(h0b), rev=ro)
+    close(y, yo, TOL[dtype], "y")
+    close(bnd, bo, STATE_TOL, "h_bounds")
+    close(yb, ybo, TOL[dtype], "two-stream y")
+
+
+@pytest.mark.parametrize("L", [16, 4, 20])
+def test_reverse_bias_without_forward_bias(dev, L, monkeypatch):
+    """Separate reverse operands with a reverse step-size bias and no forward
+    bias (no softplus): the reverse bias must still be added."""
+    monkeypatch.setenv("BDSSM_CHUNK", "64")
+    batch, T, D = 2, 320, 80
+    dtype = torch.float32
+    c = Case(batch, T, D, dtype, sid=68, a_kind="random")
+    rev = _rev_operands(batch, T, D, dtype, 68, with_bias=True)
+    y, _ = m.train_scan(*c.args(), L, rev=rev)
+    h0b = synth.normal((batch, T // L + 1, D, N), 6801, "cuda")
+    yb = m.train_scan_blocks(*c.args(), L, h0b, rev=rev)
+    yf = m.full_scan(*c.args(), rev=rev)
+    torch.cuda.synchronize()
+    oa = c.oracle_args()
+    ro = _rev_oracle(rev)
+    close(y, oracle.train_scan(*oa, L, rev=ro)[0], TOL[dtype], "train_scan y")
+    close(yb, oracle.train_blocks(*oa, L, to_np(h0b), rev=ro), TOL[dtype], "two-stream y")
+    close(yf, oracle.full_scan(*oa, rev=ro), TOL[dtype], "full_scan y")
