@@ -110,19 +110,19 @@ def slots_forward(batch, T, D):
     return batch * T * D * (NS * (EXP_SLOTS + 3) + 1)
 
 
-def slots_backward(batch, T, D):
+def slots_backward(batch, T, D, ns=NS):
     """Algorithmic issue slots of the backward pass per (b,t,d,n): one exp2 (2)
     and dt*A' (1); the forward state (u, FMA), the reverse state (FMA), the
     forward adjoint (FMA, mul), the reverse adjoint (FMA, mul); du (add), da
     (FMA, mul), the dt / x / A sums (FMA, mul, FMA, FMA), dB (mul), dC (FMA,
     add, mul): 22; plus 4 per (b,t,d) for the dt and x gradients."""
-    return batch * T * D * (NS * 22 + 4)
+    return batch * T * D * (ns * 22 + 4)
 
 
-def slots_bidirectional(batch, T, D):
+def slots_bidirectional(batch, T, D, ns=NS):
     """forward + in-block reverse + output: exp2 + 2 mul + 4 FMA per
     (b,t,d,n), plus dt*x and the Dskip*x FMA per (b,t,d)."""
-    return batch * T * D * (NS * (EXP_SLOTS + 6) + 2)
+    return batch * T * D * (ns * (EXP_SLOTS + 6) + 2)
 
 
 # ------------------------------------------------------------------- main
@@ -145,6 +145,10 @@ def main():
     ap.add_argument("--reverse-operands", action="store_true",
                     help="give the in-block reverse scan its own dt, B, C and A (block steps, "
                          "training forms and the baseline)")
+    ap.add_argument("--block-len", type=int, default=0,
+                    help="training workloads: block length other than the workload's (1..256)")
+    ap.add_argument("--d-state", type=int, default=0,
+                    help="training workloads: state count other than 16 (4, 8 or 32)")
     ap.add_argument("--crossover", action="store_true",
                     help="sweep the context length (8K..64K, batch 8, d_inner 1536) and report "
                          "block-restricted against full-sequence generation rates")
@@ -165,6 +169,9 @@ def main():
     wl = dict(synth.WORKLOADS[args.workload])
     if "seq" in wl:
         return train_main(args, wl, m, synth, torch)
+    if args.block_len or args.d_state:
+        print("--block-len / --d-state apply to the training workloads", file=sys.stderr)
+        return 2
     batch, D, ctx, L = wl["batch"], wl["d_inner"], wl["ctx"], wl["block"]
     S, nblk, sid = wl["steps"], wl["n_blocks"], wl["sid"]
     dtype = synth.TORCH_DTYPE[wl["dtype"]]
@@ -396,14 +403,19 @@ def train_main(args, wl, m, synth, torch):
     forward + reverse segmented per block) over the batch.  The full-sequence
     bidirectional scan over the same tokens is timed beside it."""
     batch, D, T, L, sid = wl["batch"], wl["d_inner"], wl["seq"], wl["block"], wl["sid"]
+    L = args.block_len or L
+    ns = args.d_state or NS
+    if T % L != 0:
+        raise SystemExit("block length %d does not divide the sequence length %d" % (L, T))
     dtype = synth.TORCH_DTYPE[wl["dtype"]]
     e = 2 if dtype == torch.bfloat16 else 4
     dev = "cuda:0"
     torch.cuda.set_device(0)
     st = torch.cuda.current_stream()
-    log("[bench] workload %s: batch %d, d_inner %d, T %d, block %d" % (args.workload, batch, D, T, L))
-    x, dt, Bm, Cm = synth.stream(batch, T, D, NS, sid, 0, dtype, dev)
-    A, Dskip = synth.params(D, NS, sid, "default", dev)
+    log("[bench] workload %s: batch %d, d_inner %d, d_state %d, T %d, block %d"
+        % (args.workload, batch, D, ns, T, L))
+    x, dt, Bm, Cm = synth.stream(batch, T, D, ns, sid, 0, dtype, dev)
+    A, Dskip = synth.params(D, ns, sid, "default", dev)
     y = torch.empty_like(x)
     fz = {}
     if args.fused:
@@ -411,10 +423,10 @@ def train_main(args, wl, m, synth, torch):
         fz = dict(dt_bias=synth.normal((D,), 1000 * sid + 72, dev, torch.float32, std=0.3),
                   dt_softplus=True, z=synth.normal((batch, T, D), 1000 * sid + 73, dev, dtype))
     if args.reverse_operands:
-        fz = dict(fz, rev=reverse_operands(synth, batch, T, D, sid, dtype, dev, torch))
-    ws = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_TRAIN, L, NS, dtype)),
+        fz = dict(fz, rev=reverse_operands(synth, batch, T, D, sid, dtype, dev, torch, ns))
+    ws = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_TRAIN, L, ns, dtype)),
                      dtype=torch.uint8, device=dev)
-    wsf = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_FULL, 1, NS, dtype)),
+    wsf = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_FULL, 1, ns, dtype)),
                       dtype=torch.uint8, device=dev)
 
     def step():
@@ -435,7 +447,7 @@ def train_main(args, wl, m, synth, torch):
     ev_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     nbytes = bytes_full(batch, T, D, e)
-    slots = slots_bidirectional(batch, T, D)
+    slots = slots_bidirectional(batch, T, D, ns)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     m.full_scan(x, dt, Bm, Cm, A, Dskip, y=y, ws=wsf, **fz)
     a.record(st)
@@ -445,7 +457,7 @@ def train_main(args, wl, m, synth, torch):
     torch.cuda.synchronize()
     full_ms = a.elapsed_time(b) / args.steps
     # two-stream form: the noisy stream scanned from the clean stream's bounds
-    bnd = torch.empty(batch, T // L + 1, D, NS, dtype=torch.float32, device=dev)
+    bnd = torch.empty(batch, T // L + 1, D, ns, dtype=torch.float32, device=dev)
     m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, h_bounds=bnd, ws=ws, **fz)
     a.record(st)
     for _ in range(args.steps):
@@ -462,18 +474,19 @@ def train_main(args, wl, m, synth, torch):
     b.record(st)
     torch.cuda.synchronize()
     two_ms = a.elapsed_time(b) / args.steps
-    if args.fused or args.reverse_operands:   # the backward differentiates the plain scan
+    # the backward differentiates the plain scan with 16 states and L | 16
+    if args.fused or args.reverse_operands or ns != NS or L not in (1, 2, 4, 8, 16):
         line = train_line(args, batch, D, T, L, dtype, nbytes, slots, ms_per_step, ev_ms,
-                          blocks_ms, full_ms, two_ms, None, None, None, torch)
+                          blocks_ms, full_ms, two_ms, None, None, None, torch, ns)
         print(json.dumps(line), flush=True)
         return 0
     # backward passes: continuous form (from the saved block states) and the
     # two-stream form; then one whole all-block training step, forward and
     # backward over both streams
     dy = synth.normal((batch, T, D), 1000 * sid + 8, dev, dtype)
-    wsb = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_TRAIN_BWD, L, NS, dtype)),
+    wsb = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_TRAIN_BWD, L, ns, dtype)),
                       dtype=torch.uint8, device=dev)
-    wsbb = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_BLOCKS_BWD, L, NS, dtype)),
+    wsbb = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_BLOCKS_BWD, L, ns, dtype)),
                        dtype=torch.uint8, device=dev)
     m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, h_bounds=bnd, ws=ws)
     m.train_scan_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, ws=wsb)
@@ -507,31 +520,31 @@ def train_main(args, wl, m, synth, torch):
     torch.cuda.synchronize()
     step_ms = a.elapsed_time(b) / args.steps
     line = train_line(args, batch, D, T, L, dtype, nbytes, slots, ms_per_step, ev_ms, blocks_ms,
-                      full_ms, two_ms, bwd_ms, bbwd_ms, step_ms, torch)
+                      full_ms, two_ms, bwd_ms, bbwd_ms, step_ms, torch, ns)
     print(json.dumps(line), flush=True)
     return 0
 
 
-def reverse_operands(synth, batch, T, D, sid, dtype, dev, torch):
+def reverse_operands(synth, batch, T, D, sid, dtype, dev, torch, ns=NS):
     """Seeded operands of the reverse direction: dt_r, B_r, C_r, A_r."""
     return dict(dt=synth.positive_step((batch, T, D), 1000 * sid + 80, dev, dtype),
-                B=synth.normal((batch, T, NS), 1000 * sid + 81, dev, dtype),
-                C=synth.normal((batch, T, NS), 1000 * sid + 82, dev, dtype),
-                A=synth.a_matrix(D, NS, "default", device=dev))
+                B=synth.normal((batch, T, ns), 1000 * sid + 81, dev, dtype),
+                C=synth.normal((batch, T, ns), 1000 * sid + 82, dev, dtype),
+                A=synth.a_matrix(D, ns, "default", device=dev))
 
 
 def train_line(args, batch, D, T, L, dtype, nbytes, slots, ms_per_step, ev_ms, blocks_ms, full_ms,
-               two_ms, bwd_ms, bbwd_ms, step_ms, torch):
+               two_ms, bwd_ms, bbwd_ms, step_ms, torch, ns=NS):
     """The JSON line of a training workload (bwd_ms / bbwd_ms / step_ms are
     None when the backward was not run)."""
-    bslots = slots_backward(batch, T, D)
+    bslots = slots_backward(batch, T, D, ns)
     line = {
         "metric": "all-block training scan GB/s (forward over T + reverse per block)",
         "value": nbytes / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if dtype == torch.bfloat16 else "f32", "data": "synthetic",
-        "config": {"workload": args.workload, "batch": batch, "d_inner": D, "d_state": NS,
+        "config": {"workload": args.workload, "batch": batch, "d_inner": D, "d_state": ns,
                    "seq": T, "block": L, "fused": bool(args.fused),
                    "reverse_operands": bool(args.reverse_operands)},
         "train_scan": {"ms": ev_ms, "tokens_per_s": batch * T / (ev_ms * 1e-3),

@@ -16,7 +16,7 @@
  * The operation.  Mamba's selective state-space mixer [ABS] with a diagonal
  * real A; the pages print no formula, so the standard Mamba-1 discretisation
  * is used (zero-order hold for A, Euler step for B).  For each (batch b,
- * channel d) row and state n (0 <= n < 16):
+ * channel d) row and state n (0 <= n < d_state):
  *   forward:  hf_t = exp(dt_t A[d,n]) hf_{t-1} + dt_t B_t[n] x_t   (causal,
  *             over the whole sequence, starting from h0)
  *   reverse:  hr_t = exp(dt_t A[d,n]) hr_{t+1} + dt_t B_t[n] x_t   confined to
@@ -54,13 +54,15 @@
  * this interface.  Outputs must not overlap inputs (only h_cache of
  * bdssm_commit is read and written in place).
  *
- * Limits of this version: d_state == 16; T % block_len == 0; block_len is
- * any value from 1 to 256 for the forward entry points (1, 2, 4, 8 and 16
- * run the register-resident kernels, other lengths a kernel that stages one
- * block's forward output in LDS, 256 * block_len bytes), and one of 1, 2, 4,
- * 8, 16 for the backward entry points; x, dt, B, C, z, the reverse operands
- * and y share one dtype.  The pages leave the block length open and name a
- * dynamic block size as future work ([ZH] "未来方向").
+ * Limits of this version: T % block_len == 0; x, dt, B, C, z, the reverse
+ * operands and y share one dtype.
+ *   forward entry points: d_state 4, 8, 16 or 32 and block_len 1 to 256.
+ *     d_state 16 with block_len 1, 2, 4, 8 or 16 runs the register-resident
+ *     kernels; every other combination runs a kernel with one lane per
+ *     channel that stages one block's forward output in LDS (256 * block_len
+ *     bytes).  The pages fix neither size (the workloads here use 16 and 16)
+ *     and name a dynamic block size as future work ([ZH] "未来方向").
+ *   backward entry points: d_state 16, block_len 1, 2, 4, 8 or 16.
  */
 #ifndef BDSSM_H
 #define BDSSM_H
@@ -131,7 +133,7 @@ typedef struct {
 typedef struct {
     int64_t batch;     /* >= 0 */
     int64_t d_inner;   /* channels D, >= 0 */
-    int64_t d_state;   /* states N, must be 16 */
+    int64_t d_state;   /* states N: 4, 8, 16 or 32 (16 for the backward) */
     int64_t block_len; /* L, the denoising block length */
     int32_t dtype;     /* bdssm_dtype of x, dt, B, C, y */
 } bdssm_shape;

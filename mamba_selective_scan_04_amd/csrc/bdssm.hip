@@ -22,6 +22,7 @@
 #include <stdlib.h>
 
 #include <initializer_list>
+#include <type_traits>
 
 #include "bdssm.h"
 #include "bdssm_bwd_kernels.hpp"
@@ -131,13 +132,32 @@ Plan make_plan(int64_t batch, int64_t D, int64_t T, double prepass_weight = 0.45
 // 16-token group); every other L up to kMaxLdsBlock goes to block_bidir_kernel.
 bool wave_block(int64_t L) { return L == 1 || L == 2 || L == 4 || L == 8 || L == 16; }
 
+// State counts the library is built for.  16 runs everything; the others run
+// the one-lane-per-channel kernels (chunk scan, carry, block_bidir_kernel,
+// the baseline's sweeps), whose templates are instantiated for each.
+bool supported_states(int64_t N) { return N == 4 || N == 8 || N == 16 || N == 32; }
+
+// Whether a bidirectional pass runs the register-resident wave kernels.
+bool wave_path(int64_t L, int64_t N) { return N == kStates && wave_block(L); }
+
+// f(std::integral_constant<int, N>) for a supported state count N.
+template <typename F> void with_states(int64_t N, F &&f) {
+    switch (N) {
+    case 4: f(std::integral_constant<int, 4>()); break;
+    case 8: f(std::integral_constant<int, 8>()); break;
+    case 32: f(std::integral_constant<int, 32>()); break;
+    default: f(std::integral_constant<int, 16>()); break;
+    }
+}
+
 // Chunking of the two-stream forms: blocks are independent, so chunks only
 // add parallelism (no carry); aim for about four rounds of resident
 // workgroups.  Returns false if the chunk count exceeds the grid limit.
 // Block lengths outside the wave kernels' set round the chunk up to whole
 // blocks (one wave per 64 channels there, so four times the chunks).
-bool blocks_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t *tc_out, int64_t *nc_out) {
-    const bool wave = wave_block(L);
+bool blocks_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, int64_t *tc_out,
+                 int64_t *nc_out) {
+    const bool wave = wave_path(L, N);
     const int64_t unit = wave ? kGroup : L;
     const int64_t groups = batch * ceil_div(D, kWave);
     const int64_t nunits = ceil_div(T, unit);
@@ -173,14 +193,14 @@ bool plan_general(int64_t batch, int64_t D, int64_t T, int64_t L, Plan *out) {
     return true;
 }
 
-// The plan of the forward entry points for block length L.
-bool plan_for(int64_t batch, int64_t D, int64_t T, int64_t L, Plan *out) {
-    if (wave_block(L)) { *out = make_plan(batch, D, T); return true; }
+// The plan of the forward entry points for block length L, N states.
+bool plan_for(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, Plan *out) {
+    if (wave_path(L, N)) { *out = make_plan(batch, D, T); return true; }
     return plan_general(batch, D, T, L, out);
 }
 
 // Workspace layout (fp32 arrays, each 256-byte aligned):
-//   agg_h [batch, n_fine, D, 16], agg_s [batch, n_fine, D], h_in [batch, n_fine, D, 16]
+//   agg_h [batch, n_fine, D, N], agg_s [batch, n_fine, D], h_in [batch, n_fine, D, N]
 //   full scan adds ragg_h, ragg_s, hr_in (same sizes) and yf [batch, T, D].
 struct Workspace {
     float *agg_h, *agg_s, *h_in, *ragg_h, *ragg_s, *hr_in, *yf;
@@ -221,9 +241,10 @@ BwdWorkspace layout_bwd(void *base, int64_t batch, int64_t D, int64_t T, int64_t
     return w;
 }
 
-Workspace layout_ws(void *base, int64_t batch, int64_t D, int64_t T, const Plan &p, int op) {
+Workspace layout_ws(void *base, int64_t batch, int64_t D, int64_t N, int64_t T, const Plan &p,
+                    int op) {
     Workspace w{};
-    const size_t nh = (size_t)batch * p.n_fine * D * kStates * sizeof(float);
+    const size_t nh = (size_t)batch * p.n_fine * D * N * sizeof(float);
     const size_t ns = (size_t)batch * p.n_fine * D * sizeof(float);
     size_t off = 0;
     auto take = [&](size_t n) -> float * {
@@ -259,7 +280,7 @@ int check_shape(const bdssm_shape *s) {
     if (s == nullptr) return BDSSM_ERR_NULL;
     if (s->dtype != BDSSM_F32 && s->dtype != BDSSM_BF16) return BDSSM_ERR_DTYPE;
     if (s->batch < 0 || s->d_inner < 0) return BDSSM_ERR_SHAPE;
-    if (s->d_state != kStates) return BDSSM_ERR_SHAPE;
+    if (!supported_states(s->d_state)) return BDSSM_ERR_SHAPE;
     const int64_t L = s->block_len;
     if (L < 1 || (!wave_block(L) && L > kMaxLdsBlock)) return BDSSM_ERR_SHAPE;
     // d_inner bound keeps a 16-token group of one stream within 32-bit buffer offsets
@@ -289,10 +310,11 @@ int check_alias(const bdssm_shape *s, int64_t T, const void *x, const void *dt, 
                 std::initializer_list<Range> outs) {
     const size_t e = esize(s);
     const size_t nx = (size_t)s->batch * T * s->d_inner * e;
-    const size_t nb = (size_t)s->batch * T * kStates * e;
+    const size_t N = (size_t)s->d_state;
+    const size_t nb = (size_t)s->batch * T * N * e;
     const Range ins[] = {{x, nx}, {dt, nx}, {B, nb}, {C, nb},
-                         {A, (size_t)s->d_inner * kStates * 4}, {Dskip, (size_t)s->d_inner * 4},
-                         {h_src, (size_t)s->batch * s->d_inner * kStates * 4}};
+                         {A, (size_t)s->d_inner * N * 4}, {Dskip, (size_t)s->d_inner * 4},
+                         {h_src, (size_t)s->batch * s->d_inner * N * 4}};
     for (const Range &o : outs) {
         for (const Range &i : ins)
             if (overlaps(o, i)) return BDSSM_ERR_ALIAS;
@@ -319,12 +341,12 @@ int check_fusion(const bdssm_fusion *f, const bdssm_shape *s, int64_t T, bool wi
     for (const void *p : ps)
         if (!aligned16(p)) return BDSSM_ERR_ALIGN;
     const size_t ntok = (size_t)s->batch * T * s->d_inner * esize(s);
-    const size_t nbc = (size_t)s->batch * T * kStates * esize(s);
+    const size_t nbc = (size_t)s->batch * T * s->d_state * esize(s);
     const Range ins[] = {{f->dt_bias, (size_t)s->d_inner * 4},
                          {with_y ? f->z : nullptr, ntok},
                          {rev ? f->dt_rev : nullptr, ntok}, {rev ? f->B_rev : nullptr, nbc},
                          {rev ? f->C_rev : nullptr, nbc},
-                         {rev ? f->A_rev : nullptr, (size_t)s->d_inner * kStates * 4},
+                         {rev ? f->A_rev : nullptr, (size_t)s->d_inner * s->d_state * 4},
                          {rev ? f->dt_bias_rev : nullptr, (size_t)s->d_inner * 4}};
     for (const Range &o : outs)
         for (const Range &i : ins)
@@ -395,57 +417,61 @@ Fuse resolve_fusion(const bdssm_fusion *f, bool with_y) {
     return r;
 }
 
-template <typename Tin, bool kRev, bool kDirect>
+template <typename Tin, bool kRev, bool kDirect, int kN>
 void launch_chunk_state_k(int dt_mode, dim3 g, const Tin *xp, const Tin *dp, const Tin *bp,
                           const float *A, const float *h0, float *hout, float *sout, int64_t T,
                           int64_t D, int64_t Tc, int n_chunks, int c_first, const float *bias,
                           hipStream_t st) {
     switch (dt_mode) {
     case kDtSoftplus:
-        hipLaunchKernelGGL((chunk_state_kernel<Tin, kRev, kDirect, kDtSoftplus>), g, dim3(kWave), 0, st,
+        hipLaunchKernelGGL((chunk_state_kernel<Tin, kRev, kDirect, kDtSoftplus, kN>), g, dim3(kWave), 0, st,
                            xp, dp, bp, A, h0, hout, sout, T, (int)D, Tc, n_chunks, c_first, bias);
         break;
     case kDtBias:
-        hipLaunchKernelGGL((chunk_state_kernel<Tin, kRev, kDirect, kDtBias>), g, dim3(kWave), 0, st,
+        hipLaunchKernelGGL((chunk_state_kernel<Tin, kRev, kDirect, kDtBias, kN>), g, dim3(kWave), 0, st,
                            xp, dp, bp, A, h0, hout, sout, T, (int)D, Tc, n_chunks, c_first, bias);
         break;
     default:
-        hipLaunchKernelGGL((chunk_state_kernel<Tin, kRev, kDirect, kDtPlain>), g, dim3(kWave), 0, st,
+        hipLaunchKernelGGL((chunk_state_kernel<Tin, kRev, kDirect, kDtPlain, kN>), g, dim3(kWave), 0, st,
                            xp, dp, bp, A, h0, hout, sout, T, (int)D, Tc, n_chunks, c_first, bias);
         break;
     }
 }
 
+// Chunk-local scans of n_launch chunks (N states per channel).
 template <typename Tin>
 void launch_chunk_state(bool rev, const void *x, const void *dt, const void *B, const float *A,
                         const float *h0, float *hout, float *sout, int64_t batch, int64_t T,
-                        int64_t D, int64_t Tc, int n_chunks, int c_first, int n_launch,
+                        int64_t D, int64_t N, int64_t Tc, int n_chunks, int c_first, int n_launch,
                         hipStream_t st, const Fuse &f = Fuse()) {
     if (n_launch <= 0) return;
     const dim3 g = grid3(D, n_launch, batch);
     const Tin *xp = (const Tin *)x, *dp = (const Tin *)dt, *bp = (const Tin *)B;
-    if (sout == nullptr)   // direct pass from h0 into hout (one chunk)
-        launch_chunk_state_k<Tin, false, true>(f.dt_mode, g, xp, dp, bp, A, h0, hout, sout, T, D, Tc,
-                                               n_chunks, c_first, f.dt_bias, st);
-    else if (rev)
-        launch_chunk_state_k<Tin, true, false>(f.dt_mode, g, xp, dp, bp, A, h0, hout, sout, T, D, Tc,
-                                               n_chunks, c_first, f.dt_bias, st);
-    else
-        launch_chunk_state_k<Tin, false, false>(f.dt_mode, g, xp, dp, bp, A, h0, hout, sout, T, D,
-                                                Tc, n_chunks, c_first, f.dt_bias, st);
+    with_states(N, [&](auto kn) {
+        constexpr int kN = decltype(kn)::value;
+        if (sout == nullptr)   // direct pass from h0 into hout (one chunk)
+            launch_chunk_state_k<Tin, false, true, kN>(f.dt_mode, g, xp, dp, bp, A, h0, hout, sout, T, D,
+                                                       Tc, n_chunks, c_first, f.dt_bias, st);
+        else if (rev)
+            launch_chunk_state_k<Tin, true, false, kN>(f.dt_mode, g, xp, dp, bp, A, h0, hout, sout, T, D,
+                                                       Tc, n_chunks, c_first, f.dt_bias, st);
+        else
+            launch_chunk_state_k<Tin, false, false, kN>(f.dt_mode, g, xp, dp, bp, A, h0, hout, sout, T,
+                                                        D, Tc, n_chunks, c_first, f.dt_bias, st);
+    });
 }
 
 void launch_carry(bool rev, const float *agg_h, const float *agg_s, const float *A,
                   const float *h_init, float *h_in, float *h_final, int64_t batch, int64_t D,
-                  int n_chunks, int n_agg, hipStream_t st, int c_low = 0) {
-    const int64_t total = batch * D * kStates;
+                  int64_t N, int n_chunks, int n_agg, hipStream_t st, int c_low = 0) {
+    const int64_t total = batch * D * N;
     const dim3 g((unsigned)ceil_div(total, 256));
     if (rev)
         hipLaunchKernelGGL((carry_kernel<true>), g, dim3(256), 0, st, agg_h, agg_s, A, h_init, h_in,
-                           h_final, (int)batch, (int)D, n_chunks, n_agg, c_low);
+                           h_final, (int)batch, (int)D, (int)N, n_chunks, n_agg, c_low);
     else
         hipLaunchKernelGGL((carry_kernel<false>), g, dim3(256), 0, st, agg_h, agg_s, A, h_init, h_in,
-                           h_final, (int)batch, (int)D, n_chunks, n_agg, c_low);
+                           h_final, (int)batch, (int)D, (int)N, n_chunks, n_agg, c_low);
 }
 
 template <typename Tin, int L, bool kInit, bool kFuse>
@@ -519,15 +545,20 @@ void launch_block_bidir(int64_t L, const void *x, const void *dt, const void *B,
 #undef BDSSM_BLOCK
 }
 
+// The bidirectional pass: the wave kernels for N = 16 and L | 16, else
+// block_bidir_kernel (Tc then a multiple of L).
 template <typename Tin>
 void launch_bidir(int64_t L, const void *x, const void *dt, const void *B, const void *C,
                   const float *A, const float *Dskip, const float *hin, int64_t hin_bs,
                   int64_t hin_cs, void *y, float *bounds, float *hout, int64_t batch, int64_t T,
-                  int64_t D, int64_t Tc, int n_chunks, hipStream_t st,
+                  int64_t D, int64_t N, int64_t Tc, int n_chunks, hipStream_t st,
                   const float *h0_blocks = nullptr, const Fuse &f = Fuse()) {
-    if (!wave_block(L)) {
-        launch_block_bidir<Tin, kStates>(L, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds,
-                                         hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st);
+    if (!wave_path(L, N)) {
+        with_states(N, [&](auto kn) {
+            launch_block_bidir<Tin, decltype(kn)::value>(L, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs,
+                                                         y, bounds, hout, batch, T, D, Tc, n_chunks,
+                                                         h0_blocks, f, st);
+        });
         return;
     }
     switch (L) {
@@ -539,13 +570,13 @@ void launch_bidir(int64_t L, const void *x, const void *dt, const void *B, const
     }
 }
 
-template <typename Tin, bool kRev>
+template <typename Tin, bool kRev, int kN>
 void launch_sweep_k(dim3 g, const void *x, const void *dt, const void *B, const void *C,
                     const float *A, const float *Dskip, const float *hin, float *yf, void *y,
                     int64_t T, int64_t D, int64_t Tc, int n_chunks, const Fuse &f, hipStream_t st) {
     const Tin *zp = (const Tin *)f.z;
 #define BDSSM_SWEEP(KDT)                                                                          \
-    hipLaunchKernelGGL((sweep_output_kernel<Tin, kRev, KDT>), g, dim3(kWave), 0, st, (const Tin *)x, \
+    hipLaunchKernelGGL((sweep_output_kernel<Tin, kRev, KDT, kN>), g, dim3(kWave), 0, st, (const Tin *)x, \
                        (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip, hin, yf, (Tin *)y, \
                        T, (int)D, Tc, n_chunks, f.dt_bias, zp)
     switch (f.dt_mode) {
@@ -559,11 +590,14 @@ void launch_sweep_k(dim3 g, const void *x, const void *dt, const void *B, const 
 template <typename Tin>
 void launch_sweep(bool rev, const void *x, const void *dt, const void *B, const void *C,
                   const float *A, const float *Dskip, const float *hin, float *yf, void *y,
-                  int64_t batch, int64_t T, int64_t D, int64_t Tc, int n_chunks, hipStream_t st,
-                  const Fuse &f = Fuse()) {
+                  int64_t batch, int64_t T, int64_t D, int64_t N, int64_t Tc, int n_chunks,
+                  hipStream_t st, const Fuse &f = Fuse()) {
     const dim3 g = grid3(D, n_chunks, batch);
-    if (rev) launch_sweep_k<Tin, true>(g, x, dt, B, C, A, Dskip, hin, yf, y, T, D, Tc, n_chunks, f, st);
-    else launch_sweep_k<Tin, false>(g, x, dt, B, C, A, Dskip, hin, yf, y, T, D, Tc, n_chunks, f, st);
+    with_states(N, [&](auto kn) {
+        constexpr int kN = decltype(kn)::value;
+        if (rev) launch_sweep_k<Tin, true, kN>(g, x, dt, B, C, A, Dskip, hin, yf, y, T, D, Tc, n_chunks, f, st);
+        else launch_sweep_k<Tin, false, kN>(g, x, dt, B, C, A, Dskip, hin, yf, y, T, D, Tc, n_chunks, f, st);
+    });
 }
 
 template <typename Tin>
@@ -622,16 +656,16 @@ template <typename Tin>
 void run_state_only(const bdssm_shape *s, int64_t T, const void *x, const void *dt, const void *B,
                     const float *A, const float *h_init, float *h_final, const Workspace &w,
                     const Plan &p, hipStream_t st, const Fuse &f = Fuse()) {
-    const int64_t batch = s->batch, D = s->d_inner;
+    const int64_t batch = s->batch, D = s->d_inner, N = s->d_state;
     if (p.n_fine == 1) {
         // one chunk: scan directly from h_init into h_final (same-lane read then write)
-        launch_chunk_state<Tin>(false, x, dt, B, A, h_init, h_final, nullptr, batch, T, D,
+        launch_chunk_state<Tin>(false, x, dt, B, A, h_init, h_final, nullptr, batch, T, D, N,
                                 p.fine_len, 1, 0, 1, st, f);
         return;
     }
-    launch_chunk_state<Tin>(false, x, dt, B, A, nullptr, w.agg_h, w.agg_s, batch, T, D,
+    launch_chunk_state<Tin>(false, x, dt, B, A, nullptr, w.agg_h, w.agg_s, batch, T, D, N,
                             p.fine_len, p.n_fine, 0, p.n_fine, st, f);
-    launch_carry(false, w.agg_h, w.agg_s, A, h_init, nullptr, h_final, batch, D, p.n_fine,
+    launch_carry(false, w.agg_h, w.agg_s, A, h_init, nullptr, h_final, batch, D, N, p.n_fine,
                  p.n_fine, st);
 }
 
@@ -641,21 +675,21 @@ void run_bidirectional(const bdssm_shape *s, int64_t T, const void *x, const voi
                        const void *B, const void *C, const float *A, const float *Dskip,
                        const float *h_init, void *y, float *bounds, float *h_final,
                        const Workspace &w, const Plan &p, hipStream_t st, const Fuse &f = Fuse()) {
-    const int64_t batch = s->batch, D = s->d_inner;
-    const int64_t hs = D * kStates;
+    const int64_t batch = s->batch, D = s->d_inner, N = s->d_state;
+    const int64_t hs = D * N;
     if (p.n_coarse == 1) {
         launch_bidir<Tin>(s->block_len, x, dt, B, C, A, Dskip, h_init, hs, 0, y, bounds, h_final,
-                          batch, T, D, p.fine_len * p.n_fine, 1, st, nullptr, f);
+                          batch, T, D, N, p.fine_len * p.n_fine, 1, st, nullptr, f);
         return;
     }
     // aggregates of every fine chunk before the last coarse chunk, then the carry
     const int n_agg = (p.n_coarse - 1) * p.per_coarse;
-    launch_chunk_state<Tin>(false, x, dt, B, A, nullptr, w.agg_h, w.agg_s, batch, T, D,
+    launch_chunk_state<Tin>(false, x, dt, B, A, nullptr, w.agg_h, w.agg_s, batch, T, D, N,
                             p.fine_len, p.n_fine, 0, n_agg, st, f);
-    launch_carry(false, w.agg_h, w.agg_s, A, h_init, w.h_in, nullptr, batch, D, p.n_fine, n_agg,
+    launch_carry(false, w.agg_h, w.agg_s, A, h_init, w.h_in, nullptr, batch, D, N, p.n_fine, n_agg,
                  st);
     launch_bidir<Tin>(s->block_len, x, dt, B, C, A, Dskip, w.h_in, (int64_t)p.n_fine * hs,
-                      (int64_t)p.per_coarse * hs, y, bounds, h_final, batch, T, D,
+                      (int64_t)p.per_coarse * hs, y, bounds, h_final, batch, T, D, N,
                       p.fine_len * p.per_coarse, p.n_coarse, st, nullptr, f);
 }
 
@@ -663,25 +697,25 @@ template <typename Tin>
 void run_full(const bdssm_shape *s, int64_t T, const void *x, const void *dt, const void *B,
               const void *C, const float *A, const float *Dskip, void *y, const Workspace &w,
               const Plan &p, hipStream_t st, const Fuse &f = Fuse()) {
-    const int64_t batch = s->batch, D = s->d_inner;
+    const int64_t batch = s->batch, D = s->d_inner, N = s->d_state;
     const int nf = p.n_fine;
     // forward: aggregates of chunks 0..nf-2, incoming states of all chunks
-    launch_chunk_state<Tin>(false, x, dt, B, A, nullptr, w.agg_h, w.agg_s, batch, T, D,
+    launch_chunk_state<Tin>(false, x, dt, B, A, nullptr, w.agg_h, w.agg_s, batch, T, D, N,
                             p.fine_len, nf, 0, nf - 1, st, f);
-    launch_carry(false, w.agg_h, w.agg_s, A, nullptr, w.h_in, nullptr, batch, D, nf, nf - 1, st);
+    launch_carry(false, w.agg_h, w.agg_s, A, nullptr, w.h_in, nullptr, batch, D, N, nf, nf - 1, st);
     // reverse (with its own operands when given): aggregates of chunks
     // 1..nf-1 (scanned right to left), incoming states
     const bool sep = f.dt_r != nullptr;
     const void *rdt = sep ? f.dt_r : dt, *rB = sep ? f.B_r : B, *rC = sep ? f.C_r : C;
     const float *rA = sep ? f.A_r : A;
     const Fuse fr = f.reverse();
-    launch_chunk_state<Tin>(true, x, rdt, rB, rA, nullptr, w.ragg_h, w.ragg_s, batch, T, D,
+    launch_chunk_state<Tin>(true, x, rdt, rB, rA, nullptr, w.ragg_h, w.ragg_s, batch, T, D, N,
                             p.fine_len, nf, 1, nf - 1, st, fr);
-    launch_carry(true, w.ragg_h, w.ragg_s, rA, nullptr, w.hr_in, nullptr, batch, D, nf, nf, st);
+    launch_carry(true, w.ragg_h, w.ragg_s, rA, nullptr, w.hr_in, nullptr, batch, D, N, nf, nf, st);
     Fuse ff = f;
     ff.z = nullptr;             // the gate multiplies the final output only
-    launch_sweep<Tin>(false, x, dt, B, C, A, Dskip, w.h_in, w.yf, y, batch, T, D, p.fine_len, nf, st, ff);
-    launch_sweep<Tin>(true, x, rdt, rB, rC, rA, Dskip, w.hr_in, w.yf, y, batch, T, D, p.fine_len, nf, st, fr);
+    launch_sweep<Tin>(false, x, dt, B, C, A, Dskip, w.h_in, w.yf, y, batch, T, D, N, p.fine_len, nf, st, ff);
+    launch_sweep<Tin>(true, x, rdt, rB, rC, rA, Dskip, w.hr_in, w.yf, y, batch, T, D, N, p.fine_len, nf, st, fr);
 }
 
 }  // namespace
@@ -709,21 +743,24 @@ const char *bdssm_status_str(int status) {
 size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T, int op) {
     if (check_shape(shape) != BDSSM_OK || T < 0 || T % shape->block_len != 0) return (size_t)-1;
     if (op < BDSSM_OP_PREFILL || op > BDSSM_OP_BLOCKS_BWD) return (size_t)-1;
-    const int64_t batch = shape->batch, D = shape->d_inner;
+    const int64_t batch = shape->batch, D = shape->d_inner, N = shape->d_state;
     if (batch == 0 || D == 0 || T == 0) return 0;
+    if ((op == BDSSM_OP_TRAIN_BWD || op == BDSSM_OP_BLOCKS_BWD) &&
+        (!wave_block(shape->block_len) || shape->d_state != kStates))
+        return (size_t)-1;
     if (op == BDSSM_OP_TRAIN_BWD) {
         const Plan p = make_plan(batch, D, T, kBwdPrepassWeight);
         return layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, p.n_coarse > 1).bytes;
     }
     if (op == BDSSM_OP_BLOCKS_BWD) {
         int64_t tc, nc;
-        if (!blocks_plan(batch, D, T, shape->block_len, &tc, &nc)) return (size_t)-1;
+        if (!blocks_plan(batch, D, T, shape->block_len, shape->d_state, &tc, &nc)) return (size_t)-1;
         return layout_bwd(nullptr, batch, D, T, 1, nc, false).bytes;
     }
     Plan p;
     if (op == BDSSM_OP_FULL) p = make_plan(batch, D, T);
-    else if (!plan_for(batch, D, T, shape->block_len, &p)) return (size_t)-1;
-    return layout_ws(nullptr, batch, D, T, p, op).bytes;
+    else if (!plan_for(batch, D, T, shape->block_len, shape->d_state, &p)) return (size_t)-1;
+    return layout_ws(nullptr, batch, D, shape->d_state, T, p, op).bytes;
 }
 
 int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const void *dt,
@@ -736,12 +773,12 @@ int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const 
     const bool with_y = y != nullptr;
     rc = check_streams(shape, t_ctx, x, dt, B, C, with_y, A, Dskip, with_y);
     if (rc) return rc;
-    const int64_t batch = shape->batch, D = shape->d_inner;
+    const int64_t batch = shape->batch, D = shape->d_inner, N = shape->d_state;
     if (batch == 0 || D == 0) return BDSSM_OK;
     if (h_cache == nullptr) return BDSSM_ERR_NULL;
     if (!aligned16(h_cache) || !aligned16(h_init) || !aligned16(y) || !aligned16(ws))
         return BDSSM_ERR_ALIGN;
-    const size_t nstate = (size_t)batch * D * kStates * 4;
+    const size_t nstate = (size_t)batch * D * N * 4;
     const size_t ny = (size_t)batch * t_ctx * D * esize(shape);
     rc = check_alias(shape, t_ctx, x, dt, B, C, A, Dskip, nullptr,
                      {Range{h_cache, nstate}, Range{y, ny}});
@@ -753,10 +790,10 @@ int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const 
     if (rc) return rc;
     const Fuse f = resolve_fusion(fusion, with_y);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (t_ctx == 0) return copy_or_zero(h_init, h_cache, batch * D * kStates, st);
+    if (t_ctx == 0) return copy_or_zero(h_init, h_cache, batch * D * N, st);
     Plan p;
-    if (!plan_for(batch, D, t_ctx, shape->block_len, &p)) return BDSSM_ERR_SHAPE;
-    const Workspace probe = layout_ws(nullptr, batch, D, t_ctx, p, BDSSM_OP_PREFILL);
+    if (!plan_for(batch, D, t_ctx, shape->block_len, N, &p)) return BDSSM_ERR_SHAPE;
+    const Workspace probe = layout_ws(nullptr, batch, D, N, t_ctx, p, BDSSM_OP_PREFILL);
     if (probe.bytes > 0 && (ws == nullptr || ws_bytes < probe.bytes)) return BDSSM_ERR_WORKSPACE;
     if (probe.bytes > 0) {
         rc = check_alias(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, {Range{ws, probe.bytes}});
@@ -764,7 +801,7 @@ int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const 
         if (overlaps({ws, probe.bytes}, {y, ny}) || overlaps({ws, probe.bytes}, {h_cache, nstate}))
             return BDSSM_ERR_ALIAS;
     }
-    const Workspace w = layout_ws(ws, batch, D, t_ctx, p, BDSSM_OP_PREFILL);
+    const Workspace w = layout_ws(ws, batch, D, N, t_ctx, p, BDSSM_OP_PREFILL);
     (void)hipGetLastError();
     if (shape->dtype == BDSSM_BF16) {
         if (with_y) run_bidirectional<uint16_t>(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, y, nullptr, h_cache, w, p, st, f);
@@ -784,7 +821,7 @@ int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void 
     const int64_t L = shape->block_len;
     rc = check_streams(shape, L, x, dt, B, C, true, A, Dskip, true);
     if (rc) return rc;
-    const int64_t batch = shape->batch, D = shape->d_inner;
+    const int64_t batch = shape->batch, D = shape->d_inner, N = shape->d_state;
     if (batch == 0 || D == 0) return BDSSM_OK;
     if (h_cache == nullptr || y == nullptr) return BDSSM_ERR_NULL;
     if (!aligned16(h_cache) || !aligned16(y)) return BDSSM_ERR_ALIGN;
@@ -797,9 +834,9 @@ int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void 
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (shape->dtype == BDSSM_BF16)
-        launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, nullptr, batch, L, D, L, 1, st, nullptr, f);
+        launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, h_cache, D * N, 0, y, nullptr, nullptr, batch, L, D, N, L, 1, st, nullptr, f);
     else
-        launch_bidir<float>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, nullptr, batch, L, D, L, 1, st, nullptr, f);
+        launch_bidir<float>(L, x, dt, B, C, A, Dskip, h_cache, D * N, 0, y, nullptr, nullptr, batch, L, D, N, L, 1, st, nullptr, f);
     return launch_status();
 }
 
@@ -812,26 +849,26 @@ int bdssm_commit(const bdssm_shape *shape, float *h_cache, const void *x, const 
     const bool with_y = y != nullptr;
     rc = check_streams(shape, L, x, dt, B, C, with_y, A, Dskip, with_y);
     if (rc) return rc;
-    const int64_t batch = shape->batch, D = shape->d_inner;
+    const int64_t batch = shape->batch, D = shape->d_inner, N = shape->d_state;
     if (batch == 0 || D == 0) return BDSSM_OK;
     if (h_cache == nullptr) return BDSSM_ERR_NULL;
     if (!aligned16(h_cache) || !aligned16(y)) return BDSSM_ERR_ALIGN;
     rc = check_alias(shape, L, x, dt, B, C, A, Dskip, nullptr,
-                     {Range{h_cache, (size_t)batch * D * kStates * 4},
+                     {Range{h_cache, (size_t)batch * D * N * 4},
                       Range{y, (size_t)batch * L * D * esize(shape)}});
     if (rc) return rc;
-    rc = check_fusion(fusion, shape, L, with_y, {Range{h_cache, (size_t)batch * D * kStates * 4},
+    rc = check_fusion(fusion, shape, L, with_y, {Range{h_cache, (size_t)batch * D * N * 4},
                                                  Range{y, (size_t)batch * L * D * esize(shape)}});
     if (rc) return rc;
     const Fuse f = resolve_fusion(fusion, with_y);
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (shape->dtype == BDSSM_BF16) {
-        if (with_y) launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, h_cache, batch, L, D, L, 1, st, nullptr, f);
-        else launch_chunk_state<uint16_t>(false, x, dt, B, A, h_cache, h_cache, nullptr, batch, L, D, L, 1, 0, 1, st, f);
+        if (with_y) launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, h_cache, D * N, 0, y, nullptr, h_cache, batch, L, D, N, L, 1, st, nullptr, f);
+        else launch_chunk_state<uint16_t>(false, x, dt, B, A, h_cache, h_cache, nullptr, batch, L, D, N, L, 1, 0, 1, st, f);
     } else {
-        if (with_y) launch_bidir<float>(L, x, dt, B, C, A, Dskip, h_cache, D * kStates, 0, y, nullptr, h_cache, batch, L, D, L, 1, st, nullptr, f);
-        else launch_chunk_state<float>(false, x, dt, B, A, h_cache, h_cache, nullptr, batch, L, D, L, 1, 0, 1, st, f);
+        if (with_y) launch_bidir<float>(L, x, dt, B, C, A, Dskip, h_cache, D * N, 0, y, nullptr, h_cache, batch, L, D, N, L, 1, st, nullptr, f);
+        else launch_chunk_state<float>(false, x, dt, B, A, h_cache, h_cache, nullptr, batch, L, D, N, L, 1, 0, 1, st, f);
     }
     return launch_status();
 }
@@ -845,15 +882,15 @@ int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const v
     if (T < 0 || T % shape->block_len != 0) return BDSSM_ERR_SHAPE;
     rc = check_streams(shape, T, x, dt, B, C, true, A, Dskip, true);
     if (rc) return rc;
-    const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len;
+    const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len, N = shape->d_state;
     if (batch == 0 || D == 0) return BDSSM_OK;
     if (T > 0 && y == nullptr) return BDSSM_ERR_NULL;
     if (!aligned16(h_init) || !aligned16(y) || !aligned16(h_bounds) || !aligned16(ws))
         return BDSSM_ERR_ALIGN;
-    const size_t nbnd = (size_t)batch * (T / L + 1) * D * kStates * 4;
+    const size_t nbnd = (size_t)batch * (T / L + 1) * D * N * 4;
     Plan p;
-    if (!plan_for(batch, D, T, L, &p)) return BDSSM_ERR_SHAPE;
-    const Workspace probe = layout_ws(nullptr, batch, D, T, p, BDSSM_OP_TRAIN);
+    if (!plan_for(batch, D, T, L, N, &p)) return BDSSM_ERR_SHAPE;
+    const Workspace probe = layout_ws(nullptr, batch, D, N, T, p, BDSSM_OP_TRAIN);
     rc = check_alias(shape, T, x, dt, B, C, A, Dskip, h_init,
                      {Range{y, (size_t)batch * T * D * esize(shape)}, Range{h_bounds, nbnd},
                       Range{T > 0 ? ws : nullptr, probe.bytes}});
@@ -865,10 +902,10 @@ int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const v
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (T == 0) {
         if (h_bounds == nullptr) return BDSSM_OK;
-        return copy_or_zero(h_init, h_bounds, batch * D * kStates, st);
+        return copy_or_zero(h_init, h_bounds, batch * D * N, st);
     }
     if (probe.bytes > 0 && (ws == nullptr || ws_bytes < probe.bytes)) return BDSSM_ERR_WORKSPACE;
-    const Workspace w = layout_ws(ws, batch, D, T, p, BDSSM_OP_TRAIN);
+    const Workspace w = layout_ws(ws, batch, D, N, T, p, BDSSM_OP_TRAIN);
     (void)hipGetLastError();
     if (shape->dtype == BDSSM_BF16)
         run_bidirectional<uint16_t>(shape, T, x, dt, B, C, A, Dskip, h_init, y, h_bounds, nullptr, w, p, st, f);
@@ -886,11 +923,11 @@ int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, 
     if (T < 0 || T % shape->block_len != 0) return BDSSM_ERR_SHAPE;
     rc = check_streams(shape, T, x, dt, B, C, true, A, Dskip, true);
     if (rc) return rc;
-    const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len;
+    const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len, N = shape->d_state;
     if (batch == 0 || D == 0 || T == 0) return BDSSM_OK;
     if (y == nullptr || h0_blocks == nullptr) return BDSSM_ERR_NULL;
     if (!aligned16(y) || !aligned16(h0_blocks)) return BDSSM_ERR_ALIGN;
-    const size_t nb0 = (size_t)batch * (T / L + 1) * D * kStates * 4;
+    const size_t nb0 = (size_t)batch * (T / L + 1) * D * N * 4;
     rc = check_alias(shape, T, x, dt, B, C, A, Dskip, nullptr,
                      {Range{y, (size_t)batch * T * D * esize(shape)}});
     if (rc) return rc;
@@ -899,13 +936,13 @@ int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, 
     if (rc) return rc;
     const Fuse f = resolve_fusion(fusion, true);
     int64_t tc, nc;
-    if (!blocks_plan(batch, D, T, L, &tc, &nc)) return BDSSM_ERR_SHAPE;
+    if (!blocks_plan(batch, D, T, L, N, &tc, &nc)) return BDSSM_ERR_SHAPE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (shape->dtype == BDSSM_BF16)
-        launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, nullptr, 0, 0, y, nullptr, nullptr, batch, T, D, tc, (int)nc, st, h0_blocks, f);
+        launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, nullptr, 0, 0, y, nullptr, nullptr, batch, T, D, N, tc, (int)nc, st, h0_blocks, f);
     else
-        launch_bidir<float>(L, x, dt, B, C, A, Dskip, nullptr, 0, 0, y, nullptr, nullptr, batch, T, D, tc, (int)nc, st, h0_blocks, f);
+        launch_bidir<float>(L, x, dt, B, C, A, Dskip, nullptr, 0, 0, y, nullptr, nullptr, batch, T, D, N, tc, (int)nc, st, h0_blocks, f);
     return launch_status();
 }
 
@@ -926,7 +963,7 @@ int bdssm_full_scan(const bdssm_shape *shape, int64_t T, const void *x, const vo
     if (y == nullptr) return BDSSM_ERR_NULL;
     if (!aligned16(y) || !aligned16(ws)) return BDSSM_ERR_ALIGN;
     const Plan p = make_plan(batch, D, T);
-    const Workspace probe = layout_ws(nullptr, batch, D, T, p, BDSSM_OP_FULL);
+    const Workspace probe = layout_ws(nullptr, batch, D, s1.d_state, T, p, BDSSM_OP_FULL);
     if (ws == nullptr || ws_bytes < probe.bytes) return BDSSM_ERR_WORKSPACE;
     rc = check_alias(&s1, T, x, dt, B, C, A, Dskip, nullptr,
                      {Range{y, (size_t)batch * T * D * esize(&s1)}, Range{ws, probe.bytes}});
@@ -934,7 +971,7 @@ int bdssm_full_scan(const bdssm_shape *shape, int64_t T, const void *x, const vo
     rc = check_fusion(fusion, &s1, T, true, {Range{y, (size_t)batch * T * D * esize(&s1)}, Range{ws, probe.bytes}});
     if (rc) return rc;
     const Fuse f = resolve_fusion(fusion, true);
-    const Workspace w = layout_ws(ws, batch, D, T, p, BDSSM_OP_FULL);
+    const Workspace w = layout_ws(ws, batch, D, s1.d_state, T, p, BDSSM_OP_FULL);
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (s1.dtype == BDSSM_BF16) run_full<uint16_t>(&s1, T, x, dt, B, C, A, Dskip, y, w, p, st, f);
@@ -957,8 +994,8 @@ int check_bwd(const bdssm_shape *shape, int64_t T, const void *x, const void *dt
     int rc = check_shape(shape);
     if (rc) return rc;
     if (T < 0 || T % shape->block_len != 0) return BDSSM_ERR_SHAPE;
-    // the backward kernels keep a block inside one 16-token group
-    if (!wave_block(shape->block_len)) return BDSSM_ERR_SHAPE;
+    // the backward kernels keep a block inside one 16-token group and run 16 states
+    if (!wave_block(shape->block_len) || shape->d_state != kStates) return BDSSM_ERR_SHAPE;
     rc = check_streams(shape, T, x, dt, B, C, true, A, Dskip, true);
     if (rc) return rc;
     const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len;
@@ -1049,7 +1086,7 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
         else
             launch_adjoint_chunk<float>(dt, dy, C, A, d_bounds, w.agg_q, w.agg_s, batch, T, D, L,
                                         p.fine_len, p.n_fine, p.per_coarse, p.n_fine - p.per_coarse, st);
-        launch_carry(true, w.agg_q, w.agg_s, A, nullptr, w.q_in, nullptr, batch, D, p.n_fine,
+        launch_carry(true, w.agg_q, w.agg_s, A, nullptr, w.q_in, nullptr, batch, D, kStates, p.n_fine,
                      p.n_fine, st, p.per_coarse - 1);
         a.qin = w.q_in + (int64_t)(p.per_coarse - 1) * hs;
         a.qin_bs = (int64_t)p.n_fine * hs;
@@ -1084,7 +1121,7 @@ int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void 
         return zero_bwd(D, dA, dDskip, dh0_blocks, batch * D * kStates, st);
     if (!aligned16(ws)) return BDSSM_ERR_ALIGN;
     int64_t tc, nc;
-    if (!blocks_plan(batch, D, T, L, &tc, &nc)) return BDSSM_ERR_SHAPE;
+    if (!blocks_plan(batch, D, T, L, kStates, &tc, &nc)) return BDSSM_ERR_SHAPE;
     const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, 1, nc, false);
     if (ws == nullptr || ws_bytes < probe.bytes) return BDSSM_ERR_WORKSPACE;
     const size_t e = esize(shape);

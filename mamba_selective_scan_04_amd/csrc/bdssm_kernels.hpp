@@ -40,7 +40,7 @@
 
 namespace bdssm_dev {
 
-constexpr int kStates = 16;      // d_state handled by this build
+constexpr int kStates = 16;      // d_state of the register-resident wave kernels
 constexpr int kWave = 64;        // gfx950 wavefront
 constexpr int kGroup = 16;       // tokens per register-resident group in the bidirectional kernel
 constexpr float kLog2e = 1.4426950408889634f;
@@ -126,6 +126,30 @@ template <typename T> __device__ __forceinline__ T *uniform_ptr(T *p) {
     return reinterpret_cast<T *>(lo | (hi << 32));
 }
 
+// Rows of kN fp32 values (A rows, states): float4 accesses when kN % 4 == 0.
+template <int kN> __device__ __forceinline__ void load_row(const float *p, float *v) {
+    if constexpr (kN % 4 == 0) {
+#pragma unroll
+        for (int q = 0; q < kN / 4; ++q) {
+            const float4 t = reinterpret_cast<const float4 *>(p)[q];
+            v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) v[n] = p[n];
+    }
+}
+template <int kN> __device__ __forceinline__ void store_row(float *p, const float *v) {
+    if constexpr (kN % 4 == 0) {
+#pragma unroll
+        for (int q = 0; q < kN / 4; ++q)
+            reinterpret_cast<float4 *>(p)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    } else {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) p[n] = v[n];
+    }
+}
+
 // ---------------------------------------------------------- token-row streams
 //
 // x, dt and y are [batch, T, D] with lanes on channels.  A chunk's rows are
@@ -199,8 +223,8 @@ template <> __device__ __forceinline__ void Rows<float>::store(int k, float v) c
 // hout / sout are indexed by chunk id c = c_first + blockIdx.y over n_chunks.
 // kDt: how dt is formed from the dt stream (kDtPlain / kDtBias / kDtSoftplus,
 // with the per-channel dt_bias, which may be null).
-template <typename Tin, bool kRev, bool kDirect, int kDt = kDtPlain>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(8))) void chunk_state_kernel(
+template <typename Tin, bool kRev, bool kDirect, int kDt = kDtPlain, int kN = kStates>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kN > 16 ? 4 : 8))) void chunk_state_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const float *__restrict__ A, const float *h0, float *hout, float *__restrict__ sout,
     int64_t T, int D, int64_t Tc, int n_chunks, int c_first, const float *__restrict__ dt_bias)
@@ -216,33 +240,22 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(8))) void
     const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
     const int len = (int)(t_end - t_begin);   // >= 1
 
-    float a2[kStates], h[kStates];
-    {
-        const float4 *ar = reinterpret_cast<const float4 *>(A + (int64_t)d * kStates);
+    float a2[kN], h[kN];
+    load_row<kN>(A + (int64_t)d * kN, a2);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            float4 v = ar[q];
-            a2[4 * q + 0] = v.x * kLog2e; a2[4 * q + 1] = v.y * kLog2e;
-            a2[4 * q + 2] = v.z * kLog2e; a2[4 * q + 3] = v.w * kLog2e;
-        }
-    }
+    for (int n = 0; n < kN; ++n) a2[n] *= kLog2e;
     if (kDirect && h0 != nullptr) {
-        const float4 *hr = reinterpret_cast<const float4 *>(h0 + ((int64_t)b * D + d) * kStates);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            float4 v = hr[q];
-            h[4 * q + 0] = v.x; h[4 * q + 1] = v.y; h[4 * q + 2] = v.z; h[4 * q + 3] = v.w;
-        }
+        load_row<kN>(h0 + ((int64_t)b * D + d) * kN, h);
     } else {
 #pragma unroll
-        for (int n = 0; n < kStates; ++n) h[n] = 0.f;
+        for (int n = 0; n < kN; ++n) h[n] = 0.f;
     }
     float S = 0.f;
     const float bias = (kDt != kDtPlain && dt_bias != nullptr) ? dt_bias[d] : 0.f;
     const int64_t first = (int64_t)b * T + t_begin;           // first row of the chunk
     const Rows<Tin> xs(x + first * D, len, D, d);
     const Rows<Tin> ds(dt + first * D, len, D, d);
-    const Tin *bs = Bm + first * kStates;
+    const Tin *bs = Bm + first * kN;
     // step k of the sweep visits row pos(k) of the chunk
     auto pos = [&](int k) -> int { return kRev ? len - 1 - k : k; };
 
@@ -253,9 +266,9 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(8))) void
                 const float dl = step_size<kDt>(widen(dr[i]), bias);
                 const float dx = dl * widen(xr[i]);
                 S += dl;
-                const Tin *brow = bs + (int64_t)pos(k0 + i) * kStates;
+                const Tin *brow = bs + (int64_t)pos(k0 + i) * kN;
 #pragma unroll
-                for (int q = 0; q < kStates / 2; ++q) {
+                for (int q = 0; q < kN / 2; ++q) {
                     float b0, b1;
                     load_pair(brow, q, b0, b1);
                     h[2 * q] = __builtin_fmaf(fast_exp2(dl * a2[2 * q]), h[2 * q], dx * b0);
@@ -290,15 +303,13 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(8))) void
         consume(xr, dr, n_full * U, rem);
     }
     if (live) {
-        float4 *o = reinterpret_cast<float4 *>(hout + (((int64_t)b * n_chunks + c) * D + d) * kStates);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            o[q] = make_float4(h[4 * q + 0], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+        store_row<kN>(hout + (((int64_t)b * n_chunks + c) * D + d) * kN, h);
         if (!kDirect && sout != nullptr) sout[((int64_t)b * n_chunks + c) * D + d] = S;
     }
 }
 
-// Carry across chunks: one thread per (b, d, n), sequential over chunks.
+// Carry across chunks: one thread per (b, d, n) (n < n_states), sequential
+// over chunks.
 // Forward: h starts at h_init (or 0); for chunk c < n_agg, h_in[c] = h, then
 // h <- exp2(A' S_c) h + h_local_c.  Writes h_in[n_agg] too when requested,
 // and the final state.  Reverse (kRev): h starts at 0 on the right, walks
@@ -308,18 +319,18 @@ template <bool kRev>
 __global__ __launch_bounds__(256) void carry_kernel(
     const float *__restrict__ agg_h, const float *__restrict__ agg_s, const float *__restrict__ A,
     const float *h_init, float *__restrict__ h_in, float *h_final,
-    int batch, int D, int n_chunks, int n_agg, int c_low)
+    int batch, int D, int n_states, int n_chunks, int n_agg, int c_low)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (int64_t)batch * D * kStates;
+    const int64_t total = (int64_t)batch * D * n_states;
     if (i >= total) return;
-    const int n = (int)(i % kStates);
-    const int64_t bd = i / kStates;
+    const int n = (int)(i % n_states);
+    const int64_t bd = i / n_states;
     const int d = (int)(bd % D);
     const int64_t b = bd / D;
-    const float a2 = A[(int64_t)d * kStates + n] * kLog2e;
-    const int64_t cs = (int64_t)D * kStates;      // chunk stride in agg_h / h_in
-    const int64_t base_h = b * n_chunks * cs + (int64_t)d * kStates + n;
+    const float a2 = A[(int64_t)d * n_states + n] * kLog2e;
+    const int64_t cs = (int64_t)D * n_states;     // chunk stride in agg_h / h_in
+    const int64_t base_h = b * n_chunks * cs + (int64_t)d * n_states + n;
     const int64_t base_s = b * n_chunks * (int64_t)D + d;
     float h = (h_init != nullptr && !kRev) ? h_init[i] : 0.f;
     if (!kRev) {
@@ -682,7 +693,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 // backwards and writes y_t = yf_t + sum_n C_t h_t + Dskip x_t (times silu(z_t)
 // when the gate z is given).  kDt / dt_bias form dt as in chunk_state_kernel.
 // grid = (ceil(D/64), chunks, batch), block = 64.
-template <typename Tin, bool kRev, int kDt = kDtPlain>
+template <typename Tin, bool kRev, int kDt = kDtPlain, int kN = kStates>
 __global__ __launch_bounds__(kWave) void sweep_output_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const Tin *__restrict__ Cm, const float *__restrict__ A, const float *__restrict__ Dskip,
@@ -701,19 +712,11 @@ __global__ __launch_bounds__(kWave) void sweep_output_kernel(
     const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
     const int len = (int)(t_end - t_begin);
 
-    float a2[kStates], h[kStates];
-    {
-        const float4 *ar = reinterpret_cast<const float4 *>(A + (int64_t)d * kStates);
-        const float4 *hr = reinterpret_cast<const float4 *>(hin + (((int64_t)b * n_chunks + c) * D + d) * kStates);
+    float a2[kN], h[kN];
+    load_row<kN>(A + (int64_t)d * kN, a2);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            float4 v = ar[q];
-            a2[4 * q + 0] = v.x * kLog2e; a2[4 * q + 1] = v.y * kLog2e;
-            a2[4 * q + 2] = v.z * kLog2e; a2[4 * q + 3] = v.w * kLog2e;
-            float4 g = hr[q];
-            h[4 * q + 0] = g.x; h[4 * q + 1] = g.y; h[4 * q + 2] = g.z; h[4 * q + 3] = g.w;
-        }
-    }
+    for (int n = 0; n < kN; ++n) a2[n] *= kLog2e;
+    load_row<kN>(hin + (((int64_t)b * n_chunks + c) * D + d) * kN, h);
     const float dsk = Dskip[d];
     const float bias = (kDt != kDtPlain && dt_bias != nullptr) ? dt_bias[d] : 0.f;
     const bool gate = kRev && z != nullptr;
@@ -723,8 +726,8 @@ __global__ __launch_bounds__(kWave) void sweep_output_kernel(
     const Rows<Tin> ys(y + first * D, len, D, d);
     const Rows<Tin> zs((gate ? z : x) + first * D, len, D, d);
     const Rows<float> fs(yf + first * D, len, D, d);
-    const Tin *bs = Bm + first * kStates;
-    const Tin *cs = Cm + first * kStates;
+    const Tin *bs = Bm + first * kN;
+    const Tin *cs = Cm + first * kN;
     auto pos = [&](int k) -> int { return kRev ? len - 1 - k : k; };
 
     auto consume = [&](const Tin *xr, const Tin *dr, const float *yr, int k0, int count) {
@@ -735,11 +738,11 @@ __global__ __launch_bounds__(kWave) void sweep_output_kernel(
                 const float xv = widen(xr[i]);
                 const float dl = step_size<kDt>(widen(dr[i]), bias);
                 const float dx = dl * xv;
-                const Tin *brow = bs + (int64_t)p * kStates;
-                const Tin *crow = cs + (int64_t)p * kStates;
+                const Tin *brow = bs + (int64_t)p * kN;
+                const Tin *crow = cs + (int64_t)p * kN;
                 float acc = 0.f;
 #pragma unroll
-                for (int q = 0; q < kStates / 2; ++q) {
+                for (int q = 0; q < kN / 2; ++q) {
                     float b0, b1, c0, c1;
                     load_pair(brow, q, b0, b1);
                     load_pair(crow, q, c0, c1);
@@ -784,31 +787,6 @@ __global__ __launch_bounds__(kWave) void sweep_output_kernel(
     if (rem > 0) {
         load_stage(n_full * U, rem, xr, dr, yr);
         consume(xr, dr, yr, n_full * U, rem);
-    }
-}
-
-// ------------------------------------------------------------------------
-// Rows of kN fp32 values (A rows, states): float4 accesses when kN % 4 == 0.
-template <int kN> __device__ __forceinline__ void load_row(const float *p, float *v) {
-    if constexpr (kN % 4 == 0) {
-#pragma unroll
-        for (int q = 0; q < kN / 4; ++q) {
-            const float4 t = reinterpret_cast<const float4 *>(p)[q];
-            v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
-        }
-    } else {
-#pragma unroll
-        for (int n = 0; n < kN; ++n) v[n] = p[n];
-    }
-}
-template <int kN> __device__ __forceinline__ void store_row(float *p, const float *v) {
-    if constexpr (kN % 4 == 0) {
-#pragma unroll
-        for (int q = 0; q < kN / 4; ++q)
-            reinterpret_cast<float4 *>(p)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-    } else {
-#pragma unroll
-        for (int n = 0; n < kN; ++n) p[n] = v[n];
     }
 }
 

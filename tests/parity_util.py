@@ -39,10 +39,10 @@ class Case:
     """Seeded inputs for one (batch, T, D) problem, on the host and the GPU."""
 
     def __init__(self, batch, T, D, dtype, sid=7, a_kind="default", k0=0, device="cuda",
-                 gen_device="cpu"):
-        self.batch, self.T, self.D, self.dtype = batch, T, D, dtype
-        x, dt, B, C = synth.stream(batch, T, D, N, sid, k0, dtype, gen_device)
-        A, Dskip = synth.params(D, N, sid, a_kind, gen_device)
+                 gen_device="cpu", n=N):
+        self.batch, self.T, self.D, self.dtype, self.n = batch, T, D, dtype, n
+        x, dt, B, C = synth.stream(batch, T, D, n, sid, k0, dtype, gen_device)
+        A, Dskip = synth.params(D, n, sid, a_kind, gen_device)
         self.host = None
         if gen_device == "cpu":
             self.host = dict(x=x, dt=dt, B=B, C=C, A=A, Dskip=Dskip)

@@ -57,7 +57,8 @@ def prefill(s, T, x=FAKE, dt=FAKE + 0x1000, Bm=FAKE + 0x2000, C=FAKE + 0x3000, A
 
 
 def test_shape_errors():
-    assert prefill(shape(N=8), 16) == -2
+    assert prefill(shape(N=6), 16) == -2           # state counts: 4, 8, 16, 32
+    assert prefill(shape(N=64), 16) == -2
     assert prefill(shape(L=0), 16) == -2
     assert prefill(shape(L=-4), 16) == -2
     assert prefill(shape(L=3), 16) == -2         # T % L != 0 for a block length off the wave set
@@ -128,6 +129,14 @@ def test_workspace_sizes():
     assert m.workspace_bytes(8, 1536, 4800, m.OP_TRAIN, block_len=48) > 0
     with pytest.raises(ValueError):
         m.workspace_bytes(1, 64, 512, m.OP_TRAIN, block_len=512)
+    # other state counts size their chunk states by N
+    assert m.workspace_bytes(8, 1536, 4096, m.OP_TRAIN, d_state=32) > m.workspace_bytes(8, 1536, 4096, m.OP_TRAIN, d_state=8)
+    with pytest.raises(ValueError):
+        m.workspace_bytes(1, 64, 512, m.OP_TRAIN, d_state=6)
+    with pytest.raises(ValueError):
+        m.workspace_bytes(1, 64, 512, m.OP_TRAIN_BWD, d_state=8)
+    with pytest.raises(ValueError):
+        m.workspace_bytes(1, 64, 512, m.OP_TRAIN_BWD, block_len=32)
     # monotone in T
     a = m.workspace_bytes(8, 1536, 4096, m.OP_TRAIN)
     b = m.workspace_bytes(8, 1536, 8192, m.OP_TRAIN)
@@ -163,7 +172,7 @@ def train_bwd(s, T, x=FAKE, dt=FAKE + 0x1000, Bm=FAKE + 0x2000, C=FAKE + 0x3000,
 
 def test_backward_argument_errors():
     s = shape(D=8)
-    assert train_bwd(shape(N=8), 16) == -2
+    assert train_bwd(shape(N=8), 16) == -2             # the backward runs 16 states only
     assert train_bwd(s, 24) == -2                      # T % L != 0
     assert train_bwd(shape(D=8, L=32), 32) == -2       # the backward takes L | 16 only
     assert train_bwd(shape(D=8, L=3), 48) == -2
