@@ -94,7 +94,7 @@ def committed_traffic(workload, batch, D):
             grid, rd, wr = int(cells[1]), float(cells[5]), float(cells[6])
         except ValueError:
             continue
-        if re.fullmatch(r"chunk_state_kernel<\w+, false, false(, 0)?>", cells[0]):
+        if re.fullmatch(r"chunk_state_kernel<\w+, false, false(, 0)?(, 16)?>", cells[0]):
             if chunk is None or grid > chunk[0]:
                 chunk = (grid, rd + wr)
         if cells[0] == "carry_kernel<false>" and grid == carry_grid:
@@ -302,6 +302,39 @@ def main():
     cm_ms = time_calls(g_cm.replay, 4) / R
     bs_eager_ms = time_calls(lambda: m.block_step(h, *bs_x, A, Dskip, y=y_blk, **fz_bs), 200)
 
+    # ---- cold block step: graphs of K x (512 MB scrub write, block step) and
+    # of K x (scrub write) alone; the difference per call is the block step
+    # with the cache, its inputs and A evicted from the 256 MB last-level
+    # cache (the best of 5 replays of each)
+    K = 20
+    scrub = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+    g_cold = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_cold):
+        for i in range(K):
+            scrub.fill_(float(i))
+            m.block_step(h, *bs_x, A, Dskip, y=y_blk, **fz_bs)
+    g_scrub = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_scrub):
+        for i in range(K):
+            scrub.fill_(float(i))
+
+    def best_replay_ms(g, reps=5):
+        best = None
+        for _ in range(reps):
+            v = time_calls(g.replay, 1)
+            best = v if best is None else min(best, v)
+        return best
+
+    bs_cold_ms = (best_replay_ms(g_cold) - best_replay_ms(g_scrub)) / K
+    del g_cold, g_scrub, scrub
+
+    # ---- the practical HBM roof in the same run: a 1 GiB device copy
+    csrc = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    cdst = torch.empty_like(csrc)
+    copy_ms = time_calls(lambda: cdst.copy_(csrc), 5)
+    copy_GBs = 2 * csrc.numel() * 4 / (copy_ms * 1e-3) / 1e9
+    del csrc, cdst
+
     # the fused path also reads the bias (4 D bytes per call) and the block
     # steps' gates (one element per (token, channel))
     fz_bytes_bs = (batch * L * D * e + 4 * D) if args.fused else 0
@@ -330,6 +363,7 @@ def main():
         "hbm_achieved_GBs": pf_bytes / (pf_ms * 1e-3) / 1e9,
         "hbm_frac": pf_bytes / (pf_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "launch_ms": pf_ms,
+        "hbm_frac_of_copy": pf_bytes / (pf_ms * 1e-3) / 1e9 / copy_GBs,
     }
 
     gen_tok = batch * L * nblk
@@ -339,7 +373,12 @@ def main():
                     "GBs": pf_bytes / (pf_ms * 1e-3) / 1e9, "bytes": pf_bytes},
         "block_step": {"us_graph": bs_ms * 1e3, "us_eager": bs_eager_ms * 1e3,
                        "GBs": (bytes_block_step(batch, L, D, e) + fz_bytes_bs) / (bs_ms * 1e-3) / 1e9,
-                       "bytes": bytes_block_step(batch, L, D, e) + fz_bytes_bs},
+                       "bytes": bytes_block_step(batch, L, D, e) + fz_bytes_bs,
+                       "us_graph_cold": bs_cold_ms * 1e3,
+                       "GBs_cold": (bytes_block_step(batch, L, D, e) + fz_bytes_bs) / (bs_cold_ms * 1e-3) / 1e9,
+                       "note": "us_graph: 50 calls in one graph, back to back; us_graph_cold: "
+                               "graph of 20 x (512 MB scrub write + call) minus graph of 20 scrub "
+                               "writes, per call"},
         "commit": {"us_graph": cm_ms * 1e3,
                    "GBs": bytes_commit(batch, L, D, e) / (cm_ms * 1e-3) / 1e9,
                    "bytes": bytes_commit(batch, L, D, e)},
@@ -387,6 +426,8 @@ def main():
                    "launch": launch, "fused": bool(args.fused),
                    "reverse_operands": bool(args.reverse_operands)},
         "hbm_frac_step": value / HBM_PEAK_GBS,
+        "hbm_copy_GBs": copy_GBs,
+        "hbm_frac_step_of_copy": value / copy_GBs,
         "prefill_tokens_per_s": calls["prefill"]["tokens_per_s"],
         "block_step_GBs": calls["block_step"]["GBs"],
         "calls": calls,
