@@ -212,7 +212,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Backward workspace (fp32, 256-byte aligned):
 //   continuous form with several coarse chunks: agg_q [batch, n_fine, D, 16],
 //     agg_s [batch, n_fine, D], q_in [batch, n_fine, D, 16];
-//   both forms: part_bc [batch, ceil(D/64), T, 32], part_a [batch, nc, D, 16],
+//   both forms: part_bc [batch, ceil(D/32), T, 32], part_a [batch, nc, D, 16],
 //     part_d [batch, nc, D]   (nc = coarse chunks of the backward pass).
 struct BwdWorkspace {
     float *agg_q, *agg_s, *q_in, *part_bc, *part_a, *part_d;
@@ -234,7 +234,8 @@ BwdWorkspace layout_bwd(void *base, int64_t batch, int64_t D, int64_t T, int64_t
         w.agg_s = take((size_t)batch * n_fine * D * sizeof(float));
         w.q_in = take(nh);
     }
-    w.part_bc = take((size_t)batch * ceil_div(D, kWave) * T * 32 * sizeof(float));
+    // sized for the smaller channel block of the two backward kernels
+    w.part_bc = take((size_t)batch * ceil_div(D, kPairChannels) * T * 32 * sizeof(float));
     w.part_a = take((size_t)batch * nc * D * kStates * sizeof(float));
     w.part_d = take((size_t)batch * nc * D * sizeof(float));
     w.bytes = off;
@@ -619,11 +620,36 @@ struct BwdArgs {
     float *part_bc, *part_a, *part_d, *dh0;
 };
 
+// The backward's block-local kernel.  bwd_pair_kernel (two states per lane,
+// the whole 16-token group held in registers, 32 channels per workgroup) is
+// the faster for L = 8 and 16; for L <= 4 its per-block loads spill and the
+// four-state bwd_wave_kernel (segment recomputation, 64 channels per
+// workgroup) is faster (measured on MI355X).  BDSSM_BWD_KERNEL=wave / pair
+// forces one of them (tuning and tests).
+bool bwd_use_wave(int64_t L) {
+    const char *v = getenv("BDSSM_BWD_KERNEL");
+    if (v != nullptr && v[0] == 'w') return true;
+    if (v != nullptr && v[0] == 'p') return false;
+    return L < 8;
+}
+
+// channels per workgroup of the chosen kernel (the dB / dC partial blocks)
+int64_t bwd_block_channels(int64_t L) { return bwd_use_wave(L) ? kWave : kPairChannels; }
+
 template <typename Tin, int L, bool kBlockInit>
 void launch_bwd_L(const BwdArgs &a, int64_t batch, int64_t T, int64_t D, int64_t Tc, int nc,
                   hipStream_t st) {
-    hipLaunchKernelGGL((bwd_wave_kernel<Tin, L, kBlockInit>), grid3(D, nc, batch), dim3(4 * kWave), 0,
-                       st, (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
+    if (bwd_use_wave(L)) {
+        hipLaunchKernelGGL((bwd_wave_kernel<Tin, L, kBlockInit>), grid3(D, nc, batch), dim3(4 * kWave), 0,
+                           st, (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
+                           (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
+                           a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0, T,
+                           (int)D, Tc);
+        return;
+    }
+    const dim3 g((unsigned)ceil_div(D, kPairChannels), (unsigned)nc, (unsigned)batch);
+    hipLaunchKernelGGL((bwd_pair_kernel<Tin, L, kBlockInit>), g, dim3(4 * kWave), 0, st,
+                       (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
                        (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
                        a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0, T,
                        (int)D, Tc);
@@ -643,10 +669,10 @@ void launch_bwd(int64_t L, const BwdArgs &a, int64_t batch, int64_t T, int64_t D
 
 template <typename Tin>
 void launch_bwd_reduce(const BwdWorkspace &w, void *dB, void *dC, float *dA, float *dDskip,
-                       int64_t batch, int64_t T, int64_t D, int64_t nc, hipStream_t st) {
+                       int64_t batch, int64_t T, int64_t D, int64_t L, int64_t nc, hipStream_t st) {
     const int64_t nbc = batch * T * 32;
     hipLaunchKernelGGL((bc_reduce_kernel<Tin>), dim3((unsigned)ceil_div(nbc, 256)), dim3(256), 0, st,
-                       w.part_bc, (Tin *)dB, (Tin *)dC, (int)batch, T, (int)ceil_div(D, kWave));
+                       w.part_bc, (Tin *)dB, (Tin *)dC, (int)batch, T, (int)ceil_div(D, bwd_block_channels(L)));
     hipLaunchKernelGGL(param_reduce_kernel, dim3((unsigned)ceil_div(D * (kStates + 1), 256)), dim3(256),
                        0, st, w.part_a, w.part_d, dA, dDskip, (int)D, (int)(batch * nc));
 }
@@ -1095,10 +1121,10 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
     const int nc = carry ? p.n_coarse : 1;
     if (shape->dtype == BDSSM_BF16) {
         launch_bwd<uint16_t, false>(L, a, batch, T, D, Tc, nc, st);
-        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, nc, st);
+        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, nc, st);
     } else {
         launch_bwd<float, false>(L, a, batch, T, D, Tc, nc, st);
-        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, nc, st);
+        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, nc, st);
     }
     return launch_status();
 }
@@ -1137,10 +1163,10 @@ int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void 
                     w.part_bc, w.part_a, w.part_d, dh0_blocks};
     if (shape->dtype == BDSSM_BF16) {
         launch_bwd<uint16_t, true>(L, a, batch, T, D, tc, (int)nc, st);
-        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, nc, st);
+        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, nc, st);
     } else {
         launch_bwd<float, true>(L, a, batch, T, D, tc, (int)nc, st);
-        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, nc, st);
+        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, nc, st);
     }
     return launch_status();
 }

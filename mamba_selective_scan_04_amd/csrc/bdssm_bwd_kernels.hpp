@@ -515,6 +515,346 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
     if (live && g == 0) part_d[((int64_t)b * gridDim.y + c) * D + d] = dD_acc;
 }
 
+// ------------------------------------------------------------------------
+// Backward of the bidirectional pass over one coarse chunk, two states per
+// lane: lane = 8 * channel + state pair (states 2g, 2g+1), 8 channels per
+// wave, 4 waves per workgroup (32 channels).  With two states per lane the
+// decays, the forward states before each token and the reverse adjoints of a
+// whole 16-token group fit in 96 VGPRs, so the forward quantities are formed
+// once per token (no recomputation):
+//   pass A (left to right over the group): hf from the group's block start
+//     state, gr reset at block starts; keeps a_t, hf_{t-1}, gr_t per token;
+//   pass B (right to left): hr (reset at block ends), gf (q carried across
+//     groups; + dbounds or reset at block ends), every gradient term.
+// Reductions go through small per-wave LDS transposes instead of cross-lane
+// butterflies:
+//   * dB / dC: per token the lane's 4 values go to tb[value][channel]; lane
+//     pairs then read one value's 8 channels (one 16-byte read each half) and
+//     add; the wave's sums meet the other waves' in red (one barrier per
+//     group) and are added in a fixed order into part_bc [batch, ceil(D/32),
+//     T, 32], reduced over channel blocks by bc_reduce_kernel;
+//   * dt and x: per token the lane's two partial sums go to td[token][q]
+//     [channel][pair]; every 4 tokens each lane sums one (token, q, channel)
+//     over the 8 state pairs and stores it.
+// Staging: x / dt / dy rows of the wave's 8 channels and the group's B / C
+// rows (shared by the workgroup, each wave loads a quarter) are DMA'd into
+// LDS one group ahead and widened to fp32 in place by the lane that loaded
+// them.  Arguments and the other partial outputs as in bwd_wave_kernel.
+// grid = (ceil(D/32), chunks, batch), block = 256.
+constexpr int kPairChannels = 32;     // channels per bwd_pair_kernel workgroup
+
+template <typename Tin, int L, bool kBlockInit>
+__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) void bwd_pair_kernel(
+    const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
+    const Tin *__restrict__ Cm, const Tin *__restrict__ dy, const float *__restrict__ A,
+    const float *__restrict__ Dskip, const float *__restrict__ h_start, const float *qin,
+    int64_t qin_bs, int64_t qin_cs, const float *__restrict__ dbounds, Tin *__restrict__ dx,
+    Tin *__restrict__ ddt, float *__restrict__ part_bc, float *__restrict__ part_a,
+    float *__restrict__ part_d, float *__restrict__ dh0, int64_t T, int D, int64_t Tc)
+{
+    constexpr int CW = 8;                     // channels per wave
+    constexpr int ES = sizeof(Tin);
+    constexpr int G = kGroup;                 // 16 tokens per group
+    static_assert(G % L == 0, "block length must divide the token group");
+    // Double buffers as distinct arrays (A / B), so that the compiler can tell
+    // the loads in flight into one buffer from the reads of the other and
+    // does not wait for them: [wave][stream x, dt, dy][token][channel] and
+    // [B, C][token][state]
+    __shared__ __attribute__((aligned(16))) uint32_t xdA[4][3][G][CW], xdB[4][3][G][CW];
+    __shared__ __attribute__((aligned(16))) uint32_t bcA[2][G][kStates], bcB[2][G][kStates];
+    __shared__ __attribute__((aligned(16))) float tb[4][2 * kStates][CW];   // dB / dC transpose, one token
+    __shared__ __attribute__((aligned(16))) float td[4][4][2][CW][CW];      // dt / x transpose, 4 tokens
+    __shared__ __attribute__((aligned(16))) float redA[4][G * 2 * kStates], redB[4][G * 2 * kStates];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = uniform(threadIdx.x >> 6);
+    const int cl = lane >> 3;                 // channel within the wave
+    const int g = lane & 7;                   // state pair
+    const int s0 = 2 * g;
+    const int d_w0 = blockIdx.x * kPairChannels + w * CW;
+    const int d_raw = d_w0 + cl;
+    const bool live = d_raw < D;
+    const int d = live ? d_raw : D - 1;
+    const int c = blockIdx.y;
+    const int b = blockIdx.z;
+    const int64_t t_begin = (int64_t)c * Tc;
+    const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
+    const int len = (int)(t_end - t_begin);
+    const int64_t nbl = T / L;
+
+    float a2[2], ar[2], q[2];
+    {
+        const float2 av = *reinterpret_cast<const float2 *>(A + (int64_t)d * kStates + s0);
+        ar[0] = av.x; ar[1] = av.y;
+        a2[0] = av.x * kLog2e; a2[1] = av.y * kLog2e;
+        q[0] = q[1] = 0.f;
+        if (!kBlockInit && qin != nullptr && t_end < T && live) {
+            const float2 v = *reinterpret_cast<const float2 *>(
+                qin + (int64_t)b * qin_bs + (int64_t)c * qin_cs + (int64_t)d * kStates + s0);
+            q[0] = v.x; q[1] = v.y;
+        }
+    }
+    float dA_acc[2] = {0.f, 0.f};
+    float dD_acc = 0.f;
+    auto state_at = [&](const float *base, int64_t blk) -> float2 {
+        return *reinterpret_cast<const float2 *>(base + (((int64_t)b * (nbl + 1) + blk) * D + d) * kStates + s0);
+    };
+    if (kBlockInit && dh0 != nullptr && t_end == T && live)
+        *reinterpret_cast<float2 *>(dh0 + (((int64_t)b * (nbl + 1) + nbl) * D + d) * kStates + s0) =
+            make_float2(0.f, 0.f);
+
+    // output lane of the dt / x transpose: token l / 16 of a 4-token segment,
+    // quantity (l / 8) % 2 (0: dt, 1: x), channel l % 8
+    const int o_tok = lane >> 4, o_q = (lane >> 3) & 1, o_ch = lane & 7;
+    const bool o_live = d_w0 + o_ch < D;
+    const float o_dsk = Dskip[o_live ? d_w0 + o_ch : D - 1];
+
+    const int64_t first = (int64_t)b * T + t_begin;
+    const Rows<Tin> xs(x + first * D, len, D, 0);
+    const Rows<Tin> ds(dt + first * D, len, D, 0);
+    const Rows<Tin> ys(dy + first * D, len, D, 0);
+    __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(const_cast<Tin *>(Bm + first * kStates)), 0, uniform(len * kStates * ES), kRawBufferWord3);
+    __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(const_cast<Tin *>(Cm + first * kStates)), 0, uniform(len * kStates * ES), kRawBufferWord3);
+    // DMA lanes: x / dt / dy load j covers tokens 8j .. 8j+7 (lane: token l / 8,
+    // channel l % 8); B / C: wave w loads tokens 4w .. 4w+3 (lane: token l / 16,
+    // state l % 16)
+    const int ld_tok = lane >> 3, ld_col = lane & 7;
+    const bool ld_live = d_w0 + ld_col < D;
+    const int ld_ch = ld_live ? d_w0 + ld_col : D - 1;
+    const int bc_tok = 4 * w + (lane >> 4), bc_col = lane & 15;
+
+    // dt and dy of tokens past the chunk end and of channels past D are read
+    // at an offset beyond the buffer's range, which returns zero: such tokens
+    // decay by 1 and inject nothing, and dead channels form no gradient terms
+    auto issue = [&](auto &xd, auto &bc, int k0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int kr = k0 + 8 * j + ld_tok;
+            const int k = kr < len ? kr : len - 1;
+            const int zoff = (kr < len && ld_live) ? ld_ch * ES + k * ds.pitch : kOutOfRange;
+            load_to_lds<ES>(xs.rsrc, &xd[w][0][8 * j][0], ld_ch * ES + k * xs.pitch, 0);
+            load_to_lds<ES>(ds.rsrc, &xd[w][1][8 * j][0], zoff, 0);
+            load_to_lds<ES>(ys.rsrc, &xd[w][2][8 * j][0], zoff, 0);
+        }
+        const int kb = (k0 + bc_tok < len) ? k0 + bc_tok : len - 1;
+        load_to_lds<ES>(brs, &bc[0][4 * w][0], (kb * kStates + bc_col) * ES, 0);
+        load_to_lds<ES>(crs, &bc[1][4 * w][0], (kb * kStates + bc_col) * ES, 0);
+    };
+    // after this wave's own loads have landed, widen the dwords this lane
+    // loaded to fp32 in place (bf16 only)
+    auto widen = [&](auto &xd, auto &bc) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        if constexpr (ES == 2) {
+#pragma unroll
+            for (int s = 0; s < 3; ++s)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    uint32_t &v = (&xd[w][s][8 * j][0])[lane];
+                    v <<= 16;
+                }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                uint32_t &v = (&bc[s][4 * w][0])[lane];
+                v <<= 16;
+            }
+        }
+    };
+    auto f32 = [](uint32_t v) { return __uint_as_float(v); };
+
+    float *pbc = part_bc + ((int64_t)b * gridDim.x + blockIdx.x) * T * 32;
+    Tin *dxw = dx + first * D;
+    Tin *dtw = ddt + first * D;
+
+    constexpr int NB = G / L;                 // blocks per group
+    // hst: forward state at the group start (two-stream form: at each block
+    // start of the group); dbd: dbounds at each block end of the group
+    // (continuous form; zero past the chunk end or without dbounds)
+    auto group = [&](auto &xd, auto &bc, auto &red, int k0, const float2 *hst, const float2 *dbd) {
+        const int nvalid = (len - k0 < G) ? len - k0 : G;   // uniform
+        auto xval = [&](int i) { return f32(xd[w][0][i][cl]); };
+        auto dval = [&](int i) { return f32(xd[w][1][i][cl]); };
+        auto yval = [&](int i) { return f32(xd[w][2][i][cl]); };
+        auto bcv = [&](int which, int i) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(&bc[which][i][s0]);
+            return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
+        };
+
+        // pass A: forward state and reverse adjoint, left to right
+        float hp_s[G][2], gr_s[G][2];
+        float hf[2] = {hst[0].x, hst[0].y}, pr[2] = {0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            if (i % L == 0 && i != 0) {
+                if constexpr (kBlockInit) {
+                    hf[0] = hst[i / L].x; hf[1] = hst[i / L].y;
+                }
+                pr[0] = pr[1] = 0.f;
+            }
+            const float dl = dval(i), dxv = dl * xval(i), gy = yval(i);
+            const float2 bv = bcv(0, i), cv = bcv(1, i);
+            const float bb[2] = {bv.x, bv.y}, cc[2] = {cv.x, cv.y};
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float a = fast_exp2(dl * a2[j]);
+                const float gr_j = __builtin_fmaf(gy, cc[j], pr[j]);
+                hp_s[i][j] = hf[j];
+                gr_s[i][j] = gr_j;
+                hf[j] = __builtin_fmaf(a, hf[j], dxv * bb[j]);
+                pr[j] = a * gr_j;
+            }
+            // 4-token batches: keeps the compiler from reading all 16 tokens'
+            // rows ahead (register pressure)
+            if ((i & 3) == 3) asm volatile("" ::: "memory");
+        }
+
+        // read the token rows again in pass B rather than keeping pass A's
+        // values live across the group
+        asm volatile("" ::: "memory");
+        // pass B: reverse state and forward adjoint, right to left
+        float hr[2] = {0.f, 0.f};
+#pragma unroll
+        for (int i = G - 1; i >= 0; --i) {
+            if ((i + 1) % L == 0) {
+                hr[0] = hr[1] = 0.f;
+                if constexpr (kBlockInit) {
+                    q[0] = q[1] = 0.f;
+                } else {
+                    q[0] += dbd[i / L].x; q[1] += dbd[i / L].y;
+                }
+            }
+            const float xv = xval(i), dl = dval(i), gy = yval(i);
+            const float dxv = dl * xv;
+            const float2 bv = bcv(0, i), cv = bcv(1, i);
+            const float bb[2] = {bv.x, bv.y}, cc[2] = {cv.x, cv.y};
+            float s1 = 0.f, s2 = 0.f, vb[2], vc[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float a = fast_exp2(dl * a2[j]);   // formed again: keeps the kernel at 3 waves per SIMD
+                const float u = dxv * bb[j];
+                const float hr1 = hr[j];
+                hr[j] = __builtin_fmaf(a, hr1, u);
+                const float gf = __builtin_fmaf(gy, cc[j], q[j]);
+                const float du = gf + gr_s[i][j];
+                const float da = __builtin_fmaf(gf, hp_s[i][j], gr_s[i][j] * hr1);
+                q[j] = a * gf;
+                s1 = __builtin_fmaf(du, bb[j], s1);
+                const float daa = da * a;
+                s2 = __builtin_fmaf(daa, ar[j], s2);
+                dA_acc[j] = __builtin_fmaf(daa, dl, dA_acc[j]);
+                // forward state after token i: kept as the state before token
+                // i + 1, except where the two-stream form restarts a block
+                const float hf_t = (i == G - 1) ? hf[j]
+                                   : (kBlockInit && (i + 1) % L == 0) ? __builtin_fmaf(a, hp_s[i][j], u)
+                                                                      : hp_s[i + 1][j];
+                vb[j] = du * dxv;                     // dB
+                vc[j] = gy * (hf_t + hr[j]);          // dC
+            }
+            if (g == 0) dD_acc = __builtin_fmaf(gy, xv, dD_acc);
+            if constexpr (kBlockInit) {
+                if (i % L == 0 && dh0 != nullptr && i < nvalid && live)
+                    *reinterpret_cast<float2 *>(dh0 + (((int64_t)b * (nbl + 1) + (t_begin + k0 + i) / L) * D + d) * kStates + s0) =
+                        make_float2(q[0], q[1]);
+            }
+            // dB / dC of the token: sum over the wave's 8 channels
+            tb[w][s0][cl] = vb[0];
+            tb[w][s0 + 1][cl] = vb[1];
+            tb[w][kStates + s0][cl] = vc[0];
+            tb[w][kStates + s0 + 1][cl] = vc[1];
+            {
+                const float4 h4 = *reinterpret_cast<const float4 *>(&tb[w][lane >> 1][4 * (lane & 1)]);
+                float sum = (h4.x + h4.y) + (h4.z + h4.w);
+                sum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sum), 0xB1, 0xF, 0xF, false));
+                if ((lane & 1) == 0) red[w][i * 2 * kStates + (lane >> 1)] = sum;
+            }
+            // dt and x partials of the token: sum over the channel's 8 pairs,
+            // flushed every 4 tokens
+            td[w][i & 3][0][cl][g] = __builtin_fmaf(xv, s1, s2);
+            td[w][i & 3][1][cl][g] = dl * s1;
+            if ((i & 3) == 0) {
+                const float4 p0 = *reinterpret_cast<const float4 *>(&td[w][o_tok][o_q][o_ch][0]);
+                const float4 p1 = *reinterpret_cast<const float4 *>(&td[w][o_tok][o_q][o_ch][4]);
+                float tot = ((p0.x + p0.y) + (p0.z + p0.w)) + ((p1.x + p1.y) + (p1.z + p1.w));
+                const int it = i + o_tok;
+                if (o_live && it < nvalid) {
+                    Tin *dst = (o_q ? dxw : dtw) + (int64_t)(k0 + it) * D + d_w0 + o_ch;
+                    if (o_q) tot = __builtin_fmaf(f32(xd[w][2][it][o_ch]), o_dsk, tot);
+                    *dst = narrow<Tin>(tot);
+                }
+                asm volatile("" ::: "memory");
+            }
+        }
+    };
+
+    // one group: the next group's loads go out first, then this group's
+    // passes; after the barrier the four waves' dB / dC sums of the group are
+    // added in a fixed order
+    auto step = [&](auto &xd, auto &bc, auto &red, auto &xdn, auto &bcn, int k0) {
+        const bool more = k0 > 0;
+        const int nv = (len - k0 < G) ? len - k0 : G;
+        // the group's global loads go out before the next group's DMA: the
+        // vector-memory counter is in order, so waiting for them afterwards
+        // never waits for the DMA too
+        float2 hst[kBlockInit ? NB : 1], dbd[kBlockInit ? 1 : NB];
+        if constexpr (kBlockInit) {
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const int ib = k * L < nv ? k * L : 0;
+                hst[k] = state_at(h_start, (t_begin + k0 + ib) / L);
+            }
+            dbd[0] = make_float2(0.f, 0.f);
+        } else {
+            hst[0] = state_at(h_start, (t_begin + k0) / L);
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const int ie = k * L + L - 1;          // the block's last token
+                dbd[k] = make_float2(0.f, 0.f);
+                if (dbounds != nullptr && ie < nv) {
+                    const float2 v = state_at(dbounds, (t_begin + k0 + ie + 1) / L);
+                    if (live) dbd[k] = v;
+                }
+            }
+        }
+        asm volatile("" ::: "memory");
+        if (more) issue(xdn, bcn, k0 - G);
+        group(xd, bc, red, k0, hst, dbd);
+        if (more) widen(xdn, bcn);
+        __syncthreads();
+        const int nvalid = (len - k0 < G) ? len - k0 : G;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int o = threadIdx.x + h * 256;
+            const float v = ((red[0][o] + red[1][o]) + red[2][o]) + red[3][o];
+            if ((o >> 5) < nvalid) pbc[(t_begin + k0) * 32 + o] = v;
+        }
+    };
+    const int k_last = ((len - 1) / G) * G;
+    issue(xdA, bcA, k_last);
+    widen(xdA, bcA);
+    __syncthreads();
+    for (int k0 = k_last; k0 >= 0; k0 -= 2 * G) {
+        step(xdA, bcA, redA, xdB, bcB, k0);
+        if (k0 - G >= 0) step(xdB, bcB, redB, xdA, bcA, k0 - G);
+    }
+
+    // continuous form: gradient of the start state (chunk 0)
+    if (!kBlockInit && c == 0 && dh0 != nullptr && live) {
+        float v0 = q[0], v1 = q[1];
+        if (dbounds != nullptr) {
+            const float2 e = state_at(dbounds, 0);
+            v0 += e.x; v1 += e.y;
+        }
+        *reinterpret_cast<float2 *>(dh0 + ((int64_t)b * D + d) * kStates + s0) = make_float2(v0, v1);
+    }
+    // dA and dDskip partials of this (batch, chunk)
+    if (live) {
+        const int64_t pc = (int64_t)b * gridDim.y + c;
+        *reinterpret_cast<float2 *>(part_a + (pc * D + d) * kStates + s0) = make_float2(dA_acc[0], dA_acc[1]);
+        if (g == 0) part_d[pc * D + d] = dD_acc;
+    }
+}
+
 // dB and dC: sum the channel-block partials in order.  One thread per
 // (batch, token, j), j < 16 -> dB state j, j >= 16 -> dC state j - 16.
 template <typename Tin>

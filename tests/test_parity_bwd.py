@@ -185,3 +185,30 @@ def test_bwd_empty_sequence(dev):
     torch.cuda.synchronize()
     assert torch.count_nonzero(g["dA"]) == 0 and torch.count_nonzero(g["dDskip"]) == 0
     assert torch.equal(g["dh_init"], db[:, 0])
+
+
+@pytest.mark.parametrize("kernel", ["pair", "wave"])
+@pytest.mark.parametrize("L", [2, 4, 8, 16])
+def test_both_backward_kernels(dev, kernel, L, monkeypatch):
+    """Each block-local backward kernel (two states per lane with the whole
+    group in registers, or four states per lane with segment recomputation),
+    forced whatever the block length would pick, in both training forms with
+    several coarse chunks, ragged channels and a ragged last group."""
+    monkeypatch.setenv("BDSSM_BWD_KERNEL", kernel)
+    monkeypatch.setenv("BDSSM_CHUNK", "64")
+    monkeypatch.setenv("BDSSM_COARSE_CHUNKS", "3")
+    batch, D = 2, 100
+    T = 456 if L < 16 else 464          # a ragged last 16-token group where L allows
+    c = Case(batch, T, D, torch.bfloat16, sid=39, a_kind="random")
+    dy = seeded((batch, T, D), 3950 + L, torch.bfloat16)
+    db = seeded((batch, T // L + 1, D, N), 3960 + L)
+    g = run_continuous(c, L, dy, db)
+    r = oracle_continuous(c, L, dy, db)
+    check(g, r, GRADS, TOL[torch.bfloat16], kernel)
+    check(g, r, PARAM_GRADS + ("dh_init",), STATE_TOL, kernel)
+    h0b = seeded((batch, T // L + 1, D, N), 3970 + L)
+    gb = m.train_scan_blocks_bwd(*c.args(), L, h0b, dy, want_dh0_blocks=True)
+    torch.cuda.synchronize()
+    rb = oracle.scan_bwd(*c.oracle_args(), L, to_np(dy), h0_blocks=to_np(h0b))
+    check(gb, rb, GRADS, TOL[torch.bfloat16], kernel + " blocks")
+    check(gb, rb, PARAM_GRADS + ("dh0_blocks",), STATE_TOL, kernel + " blocks")
