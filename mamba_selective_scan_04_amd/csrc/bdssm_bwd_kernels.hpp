@@ -787,37 +787,48 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
         }
     };
 
+    // The global loads of a group (its start states, its d_bounds entries)
+    // are issued one group ahead, together with that group's rows, so that
+    // the wait for the rows at the end of the previous group covers them (the
+    // vector-memory counter is in order: a wait for them placed after a later
+    // DMA would wait for the DMA as well).
+    float2 hstn[kBlockInit ? NB : 1], dbdn[kBlockInit ? 1 : NB];
+    auto load_group = [&](int k0n) {
+        const int nv = (len - k0n < G) ? len - k0n : G;
+        if constexpr (kBlockInit) {
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const int ib = k * L < nv ? k * L : 0;
+                hstn[k] = state_at(h_start, (t_begin + k0n + ib) / L);
+            }
+            dbdn[0] = make_float2(0.f, 0.f);
+        } else {
+            hstn[0] = state_at(h_start, (t_begin + k0n) / L);
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const int ie = k * L + L - 1;          // the block's last token
+                dbdn[k] = make_float2(0.f, 0.f);
+                if (dbounds != nullptr && ie < nv) {
+                    const float2 v = state_at(dbounds, (t_begin + k0n + ie + 1) / L);
+                    if (live) dbdn[k] = v;
+                }
+            }
+        }
+    };
     // one group: the next group's loads go out first, then this group's
     // passes; after the barrier the four waves' dB / dC sums of the group are
     // added in a fixed order
     auto step = [&](auto &xd, auto &bc, auto &red, auto &xdn, auto &bcn, int k0) {
         const bool more = k0 > 0;
-        const int nv = (len - k0 < G) ? len - k0 : G;
-        // the group's global loads go out before the next group's DMA: the
-        // vector-memory counter is in order, so waiting for them afterwards
-        // never waits for the DMA too
         float2 hst[kBlockInit ? NB : 1], dbd[kBlockInit ? 1 : NB];
-        if constexpr (kBlockInit) {
 #pragma unroll
-            for (int k = 0; k < NB; ++k) {
-                const int ib = k * L < nv ? k * L : 0;
-                hst[k] = state_at(h_start, (t_begin + k0 + ib) / L);
-            }
-            dbd[0] = make_float2(0.f, 0.f);
-        } else {
-            hst[0] = state_at(h_start, (t_begin + k0) / L);
+        for (int k = 0; k < (kBlockInit ? NB : 1); ++k) hst[k] = hstn[k];
 #pragma unroll
-            for (int k = 0; k < NB; ++k) {
-                const int ie = k * L + L - 1;          // the block's last token
-                dbd[k] = make_float2(0.f, 0.f);
-                if (dbounds != nullptr && ie < nv) {
-                    const float2 v = state_at(dbounds, (t_begin + k0 + ie + 1) / L);
-                    if (live) dbd[k] = v;
-                }
-            }
+        for (int k = 0; k < (kBlockInit ? 1 : NB); ++k) dbd[k] = dbdn[k];
+        if (more) {
+            load_group(k0 - G);
+            issue(xdn, bcn, k0 - G);
         }
-        asm volatile("" ::: "memory");
-        if (more) issue(xdn, bcn, k0 - G);
         group(xd, bc, red, k0, hst, dbd);
         if (more) widen(xdn, bcn);
         __syncthreads();
@@ -830,6 +841,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
         }
     };
     const int k_last = ((len - 1) / G) * G;
+    load_group(k_last);
     issue(xdA, bcA, k_last);
     widen(xdA, bcA);
     __syncthreads();

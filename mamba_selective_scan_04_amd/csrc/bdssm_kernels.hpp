@@ -554,10 +554,42 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
     Tin *ylane = y + first * D + d;
     const bool hi2 = (g & 2) != 0, hi1 = (g & 1) != 0;
 
+    // two-stream form: the block start states of a group are loaded one group
+    // ahead, with that group's rows, so that the wait for the rows at the end
+    // of the previous group covers them too (the vector-memory counter is in
+    // order: a wait for them placed after a later DMA would wait for the DMA)
+    // (for L >= 8; with more blocks per group the states would not fit the
+    // registers, and the group loads them itself)
+    constexpr int NBk = kBlockInit ? kGroup / L : 1;
+    constexpr bool kAhead = kBlockInit && L >= 8;
+    float hbn[NBk][P];
+    auto load_hb = [&](int k0n) {
+        if constexpr (kBlockInit) {
+            const int nv = (len - k0n < kGroup) ? len - k0n : kGroup;
+#pragma unroll
+            for (int q = 0; q < NBk; ++q) {
+                const int i = q * L < nv ? q * L : 0;
+                const int64_t blk = (t_begin + k0n + i) / L;
+                const float4 v = *reinterpret_cast<const float4 *>(
+                    h0_blocks + (((int64_t)b * (nbl + 1) + blk) * D + d) * kStates + s0);
+                hbn[q][0] = v.x; hbn[q][1] = v.y; hbn[q][2] = v.z; hbn[q][3] = v.w;
+            }
+        }
+    };
+
     auto group = [&](auto &xd, auto &xdn, auto &bcrn, int k0) {
         const int nvalid = (len - k0 < kGroup) ? len - k0 : kGroup;   // uniform
         const bool more = k0 + kGroup < len;
-        if (more) issue(xdn, bcrn, k0 + kGroup);
+        if constexpr (kBlockInit && !kAhead) load_hb(k0);
+        float hb[NBk][P];
+#pragma unroll
+        for (int q = 0; q < NBk; ++q)
+#pragma unroll
+            for (int j = 0; j < P; ++j) hb[q][j] = hbn[q][j];
+        if (more) {
+            if constexpr (kAhead) load_hb(k0 + kGroup);
+            issue(xdn, bcrn, k0 + kGroup);
+        }
         float dx[kGroup], dl[kGroup], ya[kGroup];
 #pragma unroll
         for (int i = 0; i < kGroup; ++i) {
@@ -566,17 +598,6 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
             dl[i] = i < nvalid ? dv : 0.f;
             dx[i] = dl[i] * xv;
             ya[i] = 0.f;
-        }
-        float hb[kBlockInit ? kGroup / L : 1][P];
-        if constexpr (kBlockInit) {
-#pragma unroll
-            for (int q = 0; q < kGroup / L; ++q) {
-                const int i = q * L < nvalid ? q * L : 0;
-                const int64_t blk = (t_begin + k0 + i) / L;
-                const float4 v = *reinterpret_cast<const float4 *>(
-                    h0_blocks + (((int64_t)b * (nbl + 1) + blk) * D + d) * kStates + s0);
-                hb[q][0] = v.x; hb[q][1] = v.y; hb[q][2] = v.z; hb[q][3] = v.w;
-            }
         }
         float dA[kGroup][P];
 #pragma unroll
@@ -676,6 +697,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
         if (more) widen_bc(bcrn, xdn);
     };
 
+    if constexpr (kAhead) load_hb(0);
     issue(xdA, bcrA, 0);
     widen_bc(bcrA, xdA);
     for (int k0 = 0; k0 < len; k0 += 2 * kGroup) {
