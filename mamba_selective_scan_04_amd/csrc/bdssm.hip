@@ -80,16 +80,21 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // prepass_weight: issue slots of the chunk pre-pass per token relative to
 // the main pass (forward aggregates vs the bidirectional pass ~0.45; adjoint
 // aggregates vs the backward pass ~0.2).
-Plan make_plan(int64_t batch, int64_t D, int64_t T, double prepass_weight = 0.45) {
+// coarse_ch / coarse_cap: channels per workgroup of the coarse pass and how
+// many of its workgroups are resident at once (the forward wave kernel: 64,
+// 512; bwd_pair_kernel: 32, 768).
+Plan make_plan(int64_t batch, int64_t D, int64_t T, double prepass_weight = 0.45,
+               int64_t coarse_ch = kWave, int64_t coarse_cap = kCoarseGroups) {
     Plan p{};
-    const int64_t groups = batch * ceil_div(D, kWave);
+    const int64_t groups = batch * ceil_div(D, kWave);          // fine pass: one wave per 64 channels
+    const int64_t cgroups = batch * ceil_div(D, coarse_ch);     // coarse pass workgroups per chunk
     const int64_t ngroups16 = ceil_div(T, kGroup);
     if (T == 0 || groups == 0) {
         p.fine_len = kGroup; p.n_fine = 1; p.per_coarse = 1; p.n_coarse = 1;
         return p;
     }
     const int64_t fine_waves = env_int("BDSSM_FINE_WAVES", kFineWaves);
-    const int64_t coarse_groups = env_int("BDSSM_COARSE_GROUPS", kCoarseGroups);
+    const int64_t coarse_groups = env_int("BDSSM_COARSE_GROUPS", coarse_cap);
     // one round of resident waves: never more chunks than fit at once
     int64_t nf = fine_waves / groups;
     if (nf > ngroups16) nf = ngroups16;
@@ -112,8 +117,8 @@ Plan make_plan(int64_t batch, int64_t D, int64_t T, double prepass_weight = 0.45
     int64_t nc = 1;
     double best = 1e30;
     for (int64_t cand = 1; cand <= 32 && cand <= nf; ++cand) {
-        const double rounds = (double)ceil_div(groups * cand, coarse_groups);
-        const double est = rounds / cand + prepass_weight * (double)(cand - 1) / cand * (double)groups / coarse_groups;
+        const double rounds = (double)ceil_div(cgroups * cand, coarse_groups);
+        const double est = rounds / cand + prepass_weight * (double)(cand - 1) / cand * (double)cgroups / coarse_groups;
         if (est < best - 1e-9) { best = est; nc = cand; }
     }
     const int64_t forced_nc = env_int("BDSSM_COARSE_CHUNKS", 0);
@@ -156,12 +161,12 @@ template <typename F> void with_states(int64_t N, F &&f) {
 // Block lengths outside the wave kernels' set round the chunk up to whole
 // blocks (one wave per 64 channels there, so four times the chunks).
 bool blocks_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, int64_t *tc_out,
-                 int64_t *nc_out) {
+                 int64_t *nc_out, int64_t coarse_ch = kWave, int64_t coarse_cap = kCoarseGroups) {
     const bool wave = wave_path(L, N);
     const int64_t unit = wave ? kGroup : L;
-    const int64_t groups = batch * ceil_div(D, kWave);
+    const int64_t groups = batch * ceil_div(D, coarse_ch);
     const int64_t nunits = ceil_div(T, unit);
-    int64_t nc = ceil_div((wave ? 4 : 16) * kCoarseGroups, groups);
+    int64_t nc = ceil_div((wave ? 4 : 16) * coarse_cap, groups);
     if (nc > nunits) nc = nunits;
     if (nc < 1) nc = 1;
     int64_t tc = ceil_div(nunits, nc) * unit;
@@ -636,6 +641,18 @@ bool bwd_use_wave(int64_t L) {
 // channels per workgroup of the chosen kernel (the dB / dC partial blocks)
 int64_t bwd_block_channels(int64_t L) { return bwd_use_wave(L) ? kWave : kPairChannels; }
 
+// workgroups of the chosen kernel resident at once: bwd_pair_kernel fits
+// three per CU (168 registers, 44 KB LDS), bwd_wave_kernel two
+int64_t bwd_block_capacity(int64_t L) { return bwd_use_wave(L) ? kCoarseGroups : 3 * 256; }
+
+// chunk plans of the two backward forms, for the chosen kernel's geometry
+Plan bwd_plan(int64_t batch, int64_t D, int64_t T, int64_t L) {
+    return make_plan(batch, D, T, kBwdPrepassWeight, bwd_block_channels(L), bwd_block_capacity(L));
+}
+bool bwd_blocks_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t *tc, int64_t *nc) {
+    return blocks_plan(batch, D, T, L, kStates, tc, nc, bwd_block_channels(L), bwd_block_capacity(L));
+}
+
 template <typename Tin, int L, bool kBlockInit>
 void launch_bwd_L(const BwdArgs &a, int64_t batch, int64_t T, int64_t D, int64_t Tc, int nc,
                   hipStream_t st) {
@@ -775,12 +792,12 @@ size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T, int op) {
         (!wave_block(shape->block_len) || shape->d_state != kStates))
         return (size_t)-1;
     if (op == BDSSM_OP_TRAIN_BWD) {
-        const Plan p = make_plan(batch, D, T, kBwdPrepassWeight);
+        const Plan p = bwd_plan(batch, D, T, shape->block_len);
         return layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, p.n_coarse > 1).bytes;
     }
     if (op == BDSSM_OP_BLOCKS_BWD) {
         int64_t tc, nc;
-        if (!blocks_plan(batch, D, T, shape->block_len, shape->d_state, &tc, &nc)) return (size_t)-1;
+        if (!bwd_blocks_plan(batch, D, T, shape->block_len, &tc, &nc)) return (size_t)-1;
         return layout_bwd(nullptr, batch, D, T, 1, nc, false).bytes;
     }
     Plan p;
@@ -1085,7 +1102,7 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
         return copy_or_zero(d_bounds, dh_init, batch * D * kStates, st);
     }
     if (!aligned16(ws)) return BDSSM_ERR_ALIGN;
-    const Plan p = make_plan(batch, D, T, kBwdPrepassWeight);
+    const Plan p = bwd_plan(batch, D, T, L);
     const bool carry = p.n_coarse > 1;
     const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, carry);
     if (ws == nullptr || ws_bytes < probe.bytes) return BDSSM_ERR_WORKSPACE;
@@ -1147,7 +1164,7 @@ int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void 
         return zero_bwd(D, dA, dDskip, dh0_blocks, batch * D * kStates, st);
     if (!aligned16(ws)) return BDSSM_ERR_ALIGN;
     int64_t tc, nc;
-    if (!blocks_plan(batch, D, T, L, kStates, &tc, &nc)) return BDSSM_ERR_SHAPE;
+    if (!bwd_blocks_plan(batch, D, T, L, &tc, &nc)) return BDSSM_ERR_SHAPE;
     const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, 1, nc, false);
     if (ws == nullptr || ws_bytes < probe.bytes) return BDSSM_ERR_WORKSPACE;
     const size_t e = esize(shape);

@@ -3,6 +3,9 @@ profiles/.
 
   python -m mamba_selective_scan_04_amd.profile_summary trace <kernel_trace.csv>
       per (kernel, grid) launch group: calls, average / min / max duration
+  python -m mamba_selective_scan_04_amd.profile_summary valu <counter_collection.csv>
+      per (kernel, grid): the clock the dies ran at and the VALU issue rate from
+      GRBM_GUI_ACTIVE, SQ_INSTS_VALU, SQ_INSTS_VALU_TRANS_F32, SQ_ACTIVE_INST_VALU
   python -m mamba_selective_scan_04_amd.profile_summary pmc <FETCH counter_collection.csv> \
       <WRITE counter_collection.csv>
       per (kernel, grid): FETCH_SIZE and WRITE_SIZE per dispatch, raw (KiB) and
@@ -97,11 +100,56 @@ def pmc(fetch_path, write_path):
     return "\n".join(out)
 
 
+N_XCC = 8             # MI355X: GRBM_GUI_ACTIVE is summed over its 8 accelerator dies
+N_CU = 256
+VALU_LANES = 1024 * 16   # 256 CUs x 4 SIMDs x 16 lanes: lane issue slots per clock
+NOMINAL_GHZ = 2.4
+
+
+def valu(path):
+    """Per kernel launch group: duration, the clock the dies ran at
+    (GRBM_GUI_ACTIVE / N_XCC / duration), VALU instructions issued (a v_exp
+    counts twice, as it occupies the SIMD for twice the cycles), the lane issue
+    slots per second that makes, and that rate against the nominal 2.4 GHz peak
+    and against the peak at the measured clock; VALUBusy as rocprofv3 defines it."""
+    rows = collections.defaultdict(dict)
+    for r in csv.DictReader(open(path)):
+        if not keep(r["Kernel_Name"]):
+            continue
+        key = (int(r["Dispatch_Id"]), short(r["Kernel_Name"]), int(r["Grid_Size"]),
+               (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        rows[key][r["Counter_Name"]] = float(r["Counter_Value"])
+    groups = collections.defaultdict(list)
+    for (disp, name, grid, us), c in rows.items():
+        groups[(name, grid)].append((us, c))
+    out = ["kernel source hash: %s" % source_hash(), "",
+           "| kernel | grid (threads) | dispatches | avg us | clock GHz | VALU instr (v_exp x2) | "
+           "lane slots / s | of 2.4 GHz peak | of peak at measured clock | VALUBusy % |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(u for u, _ in kv[1])):
+        if "copyBuffer" in name:
+            continue
+        us = sum(u for u, _ in v) / len(v)
+        get = lambda k: sum(c.get(k, 0.0) for _, c in v) / len(v)
+        cyc = get("GRBM_GUI_ACTIVE") / N_XCC
+        ghz = cyc / (us * 1e3) if us > 0 else float("nan")
+        instr = get("SQ_INSTS_VALU") + get("SQ_INSTS_VALU_TRANS_F32")
+        rate = instr * 64 / (us * 1e-6) if us > 0 else float("nan")
+        peak = VALU_LANES * NOMINAL_GHZ * 1e9
+        peak_clk = VALU_LANES * ghz * 1e9
+        busy = 100 * get("SQ_ACTIVE_INST_VALU") / N_CU / cyc if cyc > 0 else float("nan")
+        out.append("| %s | %d | %d | %.2f | %.3f | %.4g | %.4g | %.3f | %.3f | %.1f |" % (
+            name, grid, len(v), us, ghz, instr, rate, rate / peak, rate / peak_clk, busy))
+    return "\n".join(out)
+
+
 def main(argv):
     if len(argv) >= 2 and argv[0] == "trace":
         print(trace(argv[1]))
     elif len(argv) >= 3 and argv[0] == "pmc":
         print(pmc(argv[1], argv[2]))
+    elif len(argv) >= 2 and argv[0] == "valu":
+        print(valu(argv[1]))
     elif len(argv) >= 1 and argv[0] == "hash":
         print(source_hash())
     else:
