@@ -104,6 +104,31 @@ def committed_traffic(workload, batch, D):
     return chunk[1] + carry
 
 
+def committed_clock(workload):
+    """(clock GHz, VALUBusy %) of the prefill's chunk scan from the committed
+    VALU counter summary for this workload, or None if there is none or the
+    kernels have changed since it was taken."""
+    from mamba_selective_scan_04_amd import profile_summary
+    path = os.path.join(ROOT, "profiles", "prefill_%s_valu_counters.md" % workload.replace("infer_", ""))
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    if "kernel source hash: %s" % profile_summary.source_hash() not in txt:
+        return None
+    best = None
+    for line in txt.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) != 10 or not re.fullmatch(r"chunk_state_kernel<\w+, false, false, 0, 16>", cells[0]):
+            continue
+        try:
+            grid, ghz, busy = int(cells[1]), float(cells[4]), float(cells[9])
+        except ValueError:
+            continue
+        if best is None or grid > best[0]:
+            best = (grid, ghz, busy)
+    return None if best is None else best[1:]
+
+
 def slots_forward(batch, T, D):
     """exp2 (2 slots) + dt*A' mul + (dt*x)*B mul + state FMA per (b,t,d,n),
     plus the dt*x multiply per (b,t,d)."""
@@ -365,6 +390,13 @@ def main():
         "launch_ms": pf_ms,
         "hbm_frac_of_copy": pf_bytes / (pf_ms * 1e-3) / 1e9 / copy_GBs,
     }
+    clk = None if args.fused else committed_clock(args.workload)
+    if clk is not None:
+        # the clock the dies sustained under this kernel (rocprofv3 counters,
+        # committed summary): the peak at that clock, and VALUBusy
+        roofline["clock_GHz_measured"] = clk[0]
+        roofline["frac_at_measured_clock"] = achieved_slots / (VALU_SLOTS_PER_S * clk[0] / 2.4)
+        roofline["valu_busy_pct"] = clk[1]
 
     gen_tok = batch * L * nblk
     gen_ms = nblk * (S * bs_ms + cm_ms)
