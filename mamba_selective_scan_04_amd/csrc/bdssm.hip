@@ -612,9 +612,18 @@ void launch_adjoint_chunk(const void *dt, const void *dy, const void *C, const f
                           int64_t D, int64_t L, int64_t Tc, int n_chunks, int c_first, int n_launch,
                           hipStream_t st) {
     if (n_launch <= 0) return;
-    hipLaunchKernelGGL((adjoint_chunk_kernel<Tin>), grid3(D, n_launch, batch), dim3(kWave), 0, st,
-                       (const Tin *)dt, (const Tin *)dy, (const Tin *)C, A, dbounds, qout, sout, T,
-                       (int)D, (int)L, Tc, n_chunks, c_first);
+#define BDSSM_ADJ(LL)                                                                              \
+    hipLaunchKernelGGL((adjoint_chunk_kernel<Tin, LL>), grid3(D, n_launch, batch), dim3(kWave), 0, st, \
+                       (const Tin *)dt, (const Tin *)dy, (const Tin *)C, A, dbounds, qout, sout, T,   \
+                       (int)D, Tc, n_chunks, c_first)
+    switch (L) {
+    case 1: BDSSM_ADJ(1); break;
+    case 2: BDSSM_ADJ(2); break;
+    case 4: BDSSM_ADJ(4); break;
+    case 8: BDSSM_ADJ(8); break;
+    default: BDSSM_ADJ(16); break;
+    }
+#undef BDSSM_ADJ
 }
 
 struct BwdArgs {

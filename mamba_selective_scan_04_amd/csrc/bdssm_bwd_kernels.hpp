@@ -43,13 +43,15 @@ namespace bdssm_dev {
 // end and S = sum dt over the chunk describe the chunk's action on an
 // incoming q:  q_left = exp2(A' S) q_right + q_local.
 // grid = (ceil(D/64), chunks launched, batch), block = 64; chunk c = c_first +
-// blockIdx.y.
-template <typename Tin>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(8))) void adjoint_chunk_kernel(
+// blockIdx.y.  L divides 16 and chunks are whole 16-token groups, so block
+// ends sit at chunk-local rows p with (p + 1) % L == 0 (masks and shifts).
+template <typename Tin, int L>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(6))) void adjoint_chunk_kernel(
     const Tin *__restrict__ dt, const Tin *__restrict__ dy, const Tin *__restrict__ Cm,
     const float *__restrict__ A, const float *__restrict__ dbounds, float *__restrict__ qout,
-    float *__restrict__ sout, int64_t T, int D, int L, int64_t Tc, int n_chunks, int c_first)
+    float *__restrict__ sout, int64_t T, int D, int64_t Tc, int n_chunks, int c_first)
 {
+    static_assert(kGroup % L == 0, "block length must divide the token group");
     constexpr int U = 4;
     const int lane = threadIdx.x;
     const int d_raw = blockIdx.x * kWave + lane;
@@ -61,6 +63,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(8))) void
     const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
     const int len = (int)(t_end - t_begin);
     const int64_t nbl = T / L;
+    const int64_t blk0 = t_begin / L;           // block index of the chunk's first row
 
     float a2[kStates], q[kStates];
     {
@@ -85,10 +88,9 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(8))) void
         for (int i = 0; i < U; ++i) {
             if (i < count) {
                 const int p = len - 1 - (k0 + i);            // row within the chunk
-                const int64_t t = t_begin + p;
-                if (dbounds != nullptr && (t + 1) % L == 0) {
+                if (dbounds != nullptr && (p + 1) % L == 0) {
                     const float4 *r = reinterpret_cast<const float4 *>(
-                        dbounds + (((int64_t)b * (nbl + 1) + (t + 1) / L) * D + d) * kStates);
+                        dbounds + (((int64_t)b * (nbl + 1) + blk0 + (p + 1) / L) * D + d) * kStates);
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         const float4 v = r[k];
