@@ -113,7 +113,7 @@ static int pick_reverse(rev_operands *r, const void *dt, const void *Bm, const v
     return 0;
 }
 
-int oracle_version(void) { return 3; }
+int oracle_version(void) { return 4; }
 
 /* Threads the OpenMP loop over rows will use (1 without OpenMP). */
 int oracle_num_threads(void)
@@ -417,12 +417,31 @@ int oracle_full_scan(int64_t batch, int64_t D, int64_t N, int dtype, int64_t T,
  * dDskip over batch and tokens) are accumulated per thread and added in
  * thread order afterwards.
  */
-int oracle_scan_bwd(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int dtype,
-                    const void *x, const void *dt, const void *Bm, const void *Cm,
-                    const double *A, const double *Dskip, int blocks, const double *h0,
-                    const double *h0_blocks, const double *dy, const double *dbounds,
-                    double *dx, double *ddt, double *dB, double *dC, double *dA,
-                    double *dDskip, double *dh0, double *dh0_blocks)
+/*
+ * With the optional fusions of the forward (oracle_scan_ex: dt = dt_stream +
+ * dt_bias, through softplus when dt_softplus; output multiplied by silu(z)),
+ * the same chain rule runs on the effective step size and on the gradient of
+ * the ungated output:
+ *   v_t = dt_stream_t + dt_bias, dt_t = softplus(v_t) (or v_t); every term
+ *     above uses dt_t;
+ *   g_t = dy_t silu(z_t) takes the place of dy_t in every term above;
+ *   dz_t = dy_t y_pre_t silu'(z_t), y_pre_t = sum_n C_t (hf_t + hr_t) + Dskip x_t,
+ *     silu'(z) = s(z) (1 + z (1 - s(z))), s = the logistic function;
+ *   ddt (the gradient of the dt stream) = ddt_t softplus'(v_t) = ddt_t s(v_t)
+ *     (or ddt_t); d_dt_bias[d] = the sum over batch and tokens of that.
+ * dt_bias, z may be NULL (no bias, no gate); dz [batch, T, D] and d_dt_bias [D]
+ * (fp64) may be NULL.  Separate reverse-direction operands are not taken.
+ */
+static double sigmoid(double v) { return v >= 0.0 ? 1.0 / (1.0 + exp(-v)) : exp(v) / (1.0 + exp(v)); }
+
+int oracle_scan_bwd_ex(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int dtype,
+                       const void *x, const void *dt, const void *Bm, const void *Cm,
+                       const double *A, const double *Dskip, int blocks, const double *h0,
+                       const double *h0_blocks, const double *dy, const double *dbounds,
+                       const double *dt_bias, int dt_softplus, const void *z,
+                       double *dx, double *ddt, double *dB, double *dC, double *dA,
+                       double *dDskip, double *dh0, double *dh0_blocks, double *dz,
+                       double *d_dt_bias)
 {
     if (batch < 0 || T < 0 || D < 0 || N < 1 || L < 1 || T % L != 0) return -1;
     if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) return -1;
@@ -440,6 +459,8 @@ int oracle_scan_bwd(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, i
     if (dDskip) memset(dDskip, 0, (size_t)D * sizeof(double));
     if (dh0) memset(dh0, 0, (size_t)(batch * D * N) * sizeof(double));
     if (dh0_blocks) memset(dh0_blocks, 0, (size_t)(batch * (nb + 1) * D * N) * sizeof(double));
+    if (dz) memset(dz, 0, n_tok * sizeof(double));
+    if (d_dt_bias) memset(d_dt_bias, 0, (size_t)D * sizeof(double));
     if (batch == 0 || D == 0) return 0;
 
     int nthr = 1;
@@ -447,7 +468,7 @@ int oracle_scan_bwd(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, i
     nthr = omp_get_max_threads();
 #endif
     /* per-thread partial sums of the cross-row gradients */
-    const size_t part = 2 * n_bc + (size_t)(D * N) + (size_t)D;
+    const size_t part = 2 * n_bc + (size_t)(D * N) + 2 * (size_t)D;
     double *parts = (double *)calloc((size_t)nthr * part, sizeof(double));
     if (!parts) return -1;
     int fail = 0;
@@ -462,6 +483,7 @@ int oracle_scan_bwd(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, i
         double *my_dC = my_dB + n_bc;
         double *my_dA = my_dC + n_bc;
         double *my_dD = my_dA + D * N;
+        double *my_dbias = my_dD + D;
         const size_t tn = (size_t)(T > 0 ? T : 1) * (size_t)N;
         double *a = (double *)malloc(tn * sizeof(double));      /* a_t[n]       */
         double *hp = (double *)malloc(tn * sizeof(double));     /* hf_{t-1}[n]  */
@@ -487,7 +509,8 @@ int oracle_scan_bwd(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, i
                     }
                     const size_t ix = (size_t)((b * T + t) * D + d);
                     const size_t ib = (size_t)((b * T + t) * N);
-                    const double dtv = ld(dt, ix, dtype), xv = ld(x, ix, dtype);
+                    const double dtv = step_size(ld(dt, ix, dtype), dt_bias ? dt_bias[d] : 0.0, dt_softplus);
+                    const double xv = ld(x, ix, dtype);
                     for (int64_t n = 0; n < N; ++n) {
                         const double at = exp(dtv * A[d * N + n]);
                         a[t * N + n] = at;
@@ -501,7 +524,8 @@ int oracle_scan_bwd(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, i
                     for (int64_t t = k * L + L - 1; t >= k * L; --t) {
                         const size_t ix = (size_t)((b * T + t) * D + d);
                         const size_t ib = (size_t)((b * T + t) * N);
-                        const double dtv = ld(dt, ix, dtype), xv = ld(x, ix, dtype);
+                        const double dtv = step_size(ld(dt, ix, dtype), dt_bias ? dt_bias[d] : 0.0, dt_softplus);
+                        const double xv = ld(x, ix, dtype);
                         for (int64_t n = 0; n < N; ++n) {
                             rn[t * N + n] = h[n];
                             h[n] = a[t * N + n] * h[n] + dtv * ld(Bm, ib + n, dtype) * xv;
@@ -514,8 +538,9 @@ int oracle_scan_bwd(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, i
                     for (int64_t t = k * L; t < k * L + L; ++t) {
                         const size_t ix = (size_t)((b * T + t) * D + d);
                         const size_t ib = (size_t)((b * T + t) * N);
+                        const double gy = z ? dy[ix] * silu(ld(z, ix, dtype)) : dy[ix];
                         for (int64_t n = 0; n < N; ++n) {
-                            const double g = dy[ix] * ld(Cm, ib + n, dtype) + q[n];
+                            const double g = gy * ld(Cm, ib + n, dtype) + q[n];
                             gr[t * N + n] = g;
                             q[n] = a[t * N + n] * g;
                         }
@@ -526,14 +551,18 @@ int oracle_scan_bwd(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, i
                 for (int64_t t = T - 1; t >= 0; --t) {
                     const size_t ix = (size_t)((b * T + t) * D + d);
                     const size_t ib = (size_t)((b * T + t) * N);
-                    const double dtv = ld(dt, ix, dtype), xv = ld(x, ix, dtype);
+                    const double vraw = ld(dt, ix, dtype) + (dt_bias ? dt_bias[d] : 0.0);
+                    const double dtv = step_size(ld(dt, ix, dtype), dt_bias ? dt_bias[d] : 0.0, dt_softplus);
+                    const double xv = ld(x, ix, dtype);
+                    const double zv = z ? ld(z, ix, dtype) : 0.0;
+                    const double gy = z ? dy[ix] * silu(zv) : dy[ix];
                     const int block_end = (t + 1) % L == 0;
                     if (blocks && block_end)
                         for (int64_t n = 0; n < N; ++n) q[n] = 0.0;
-                    double sdt = 0.0, sx = 0.0;
+                    double sdt = 0.0, sx = 0.0, ypre = Dskip[d] * xv;
                     for (int64_t n = 0; n < N; ++n) {
                         const double bv = ld(Bm, ib + n, dtype), cv = ld(Cm, ib + n, dtype);
-                        double gf = dy[ix] * cv + q[n];
+                        double gf = gy * cv + q[n];
                         if (!blocks && block_end && dbounds)
                             gf += dbounds[((b * (nb + 1) + (t + 1) / L) * D + d) * N + n];
                         const double at = a[t * N + n];
@@ -543,13 +572,22 @@ int oracle_scan_bwd(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, i
                         sdt += du * bv * xv + da * at * A[d * N + n];
                         sx += du * dtv * bv;
                         my_dB[ib + n] += du * dtv * xv;
-                        my_dC[ib + n] += dy[ix] * ((at * hp[t * N + n] + u) + (at * rn[t * N + n] + u));
+                        const double hsum = (at * hp[t * N + n] + u) + (at * rn[t * N + n] + u);
+                        my_dC[ib + n] += gy * hsum;
+                        ypre += cv * hsum;
                         my_dA[d * N + n] += da * at * dtv;
                         q[n] = at * gf;
                     }
-                    if (ddt) ddt[ix] = sdt;
-                    if (dx) dx[ix] = sx + dy[ix] * Dskip[d];
-                    my_dD[d] += dy[ix] * xv;
+                    /* the dt stream's gradient: through softplus when it is used */
+                    const double draw = dt_softplus ? sdt * sigmoid(vraw) : sdt;
+                    if (ddt) ddt[ix] = draw;
+                    my_dbias[d] += draw;
+                    if (dx) dx[ix] = sx + gy * Dskip[d];
+                    my_dD[d] += gy * xv;
+                    if (dz && z) {
+                        const double s = sigmoid(zv);
+                        dz[ix] = dy[ix] * ypre * s * (1.0 + zv * (1.0 - s));
+                    }
                     if (blocks && t % L == 0 && dh0_blocks)
                         for (int64_t n = 0; n < N; ++n)
                             dh0_blocks[((b * (nb + 1) + t / L) * D + d) * N + n] = q[n];
@@ -569,8 +607,21 @@ int oracle_scan_bwd(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, i
             if (dC) for (size_t i = 0; i < n_bc; ++i) dC[i] += p[n_bc + i];
             if (dA) for (int64_t i = 0; i < D * N; ++i) dA[i] += p[2 * n_bc + i];
             if (dDskip) for (int64_t i = 0; i < D; ++i) dDskip[i] += p[2 * n_bc + D * N + i];
+            if (d_dt_bias) for (int64_t i = 0; i < D; ++i) d_dt_bias[i] += p[2 * n_bc + D * N + D + i];
         }
     }
     free(parts);
     return fail ? -1 : 0;
+}
+
+int oracle_scan_bwd(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int dtype,
+                    const void *x, const void *dt, const void *Bm, const void *Cm,
+                    const double *A, const double *Dskip, int blocks, const double *h0,
+                    const double *h0_blocks, const double *dy, const double *dbounds,
+                    double *dx, double *ddt, double *dB, double *dC, double *dA,
+                    double *dDskip, double *dh0, double *dh0_blocks)
+{
+    return oracle_scan_bwd_ex(batch, T, D, N, L, dtype, x, dt, Bm, Cm, A, Dskip, blocks, h0,
+                              h0_blocks, dy, dbounds, NULL, 0, NULL, dx, ddt, dB, dC, dA, dDskip,
+                              dh0, dh0_blocks, NULL, NULL);
 }

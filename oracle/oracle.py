@@ -53,6 +53,9 @@ def bind(lib):
     lib.oracle_scan_bwd.argtypes = ([I, I, I, I, I, ctypes.c_int] + [P] * 6 + [ctypes.c_int]
                                     + [P] * 12)
     lib.oracle_scan_bwd.restype = ctypes.c_int
+    lib.oracle_scan_bwd_ex.argtypes = ([I, I, I, I, I, ctypes.c_int] + [P] * 6 + [ctypes.c_int]
+                                       + [P] * 5 + [ctypes.c_int] + [P] * 11)
+    lib.oracle_scan_bwd_ex.restype = ctypes.c_int
     return lib
 
 
@@ -219,13 +222,18 @@ def train_blocks(x, dt, B, C, A, Dskip, L, h0_blocks, dt_bias=None, dt_softplus=
     return y
 
 
-def scan_bwd(x, dt, B, C, A, Dskip, L, dy, h0=None, h0_blocks=None, dbounds=None):
+def scan_bwd(x, dt, B, C, A, Dskip, L, dy, h0=None, h0_blocks=None, dbounds=None, dt_bias=None,
+             dt_softplus=False, z=None):
     """Reverse-mode gradients of the training forms.  Continuous form (the
     gradient of train_scan): forward from h0, optional dbounds = dJ/dh_bounds
     ([batch, T/L+1, D, N]).  Two-stream form (the gradient of train_blocks):
     pass h0_blocks.  dy = dJ/dy [batch, T, D].  Returns a dict of float64
     arrays: dx, ddt [batch, T, D]; dB, dC [batch, T, N]; dA [D, N];
-    dDskip [D]; and dh0 [batch, D, N] or dh0_blocks [batch, T/L+1, D, N]."""
+    dDskip [D]; and dh0 [batch, D, N] or dh0_blocks [batch, T/L+1, D, N].
+    With the forward's fusions (dt_bias, dt_softplus, z as in scan) ddt is the
+    gradient of the dt stream (before bias and softplus), and the dict also
+    holds d_dt_bias [D] (when dt_bias is given) and dz [batch, T, D] (when z
+    is given)."""
     x, dt, B, C = _c(x), _c(dt), _c(B), _c(C)
     A = _c(A, np.float64)
     Dskip = _c(Dskip, np.float64)
@@ -253,11 +261,18 @@ def scan_bwd(x, dt, B, C, A, Dskip, L, dy, h0=None, h0_blocks=None, dbounds=None
         out["dh0_blocks"] = np.empty((batch, nb + 1, D, N))
     else:
         out["dh0"] = np.empty((batch, D, N))
-    rc = load().oracle_scan_bwd(batch, T, D, N, L, code, _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
-                                _ptr(A), _ptr(Dskip), int(blocks), _ptr(h0), _ptr(h0b), _ptr(dy),
-                                _ptr(dbounds), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dB"]),
-                                _ptr(out["dC"]), _ptr(out["dA"]), _ptr(out["dDskip"]),
-                                _ptr(out.get("dh0")), _ptr(out.get("dh0_blocks")))
+    bias, zz = _fusion(x, D, dt_bias, z)
+    if bias is not None:
+        out["d_dt_bias"] = np.empty(D)
+    if zz is not None:
+        out["dz"] = np.empty((batch, T, D))
+    rc = load().oracle_scan_bwd_ex(batch, T, D, N, L, code, _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
+                                   _ptr(A), _ptr(Dskip), int(blocks), _ptr(h0), _ptr(h0b), _ptr(dy),
+                                   _ptr(dbounds), _ptr(bias), int(bool(dt_softplus)), _ptr(zz),
+                                   _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dB"]),
+                                   _ptr(out["dC"]), _ptr(out["dA"]), _ptr(out["dDskip"]),
+                                   _ptr(out.get("dh0")), _ptr(out.get("dh0_blocks")),
+                                   _ptr(out.get("dz")), _ptr(out.get("d_dt_bias")))
     if rc != 0:
         raise ValueError("oracle_scan_bwd rejected its arguments (rc=%d)" % rc)
     return out

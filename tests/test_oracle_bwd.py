@@ -222,3 +222,96 @@ def test_bwd_empty_sequence():
     g = oracle.scan_bwd(p["x"], p["dt"], p["B"], p["C"], p["A"], p["Dskip"], 4,
                         np.zeros((2, 0, 3)), h0=np.ones((2, 3, 4)))
     assert g["dx"].shape == (2, 0, 3) and np.all(g["dA"] == 0) and np.all(g["dh0"] == 0)
+
+
+# ---- gradients of the fusions (dt = softplus(dt_raw + bias) or dt_raw + bias,
+# output times silu(z)), pinned by central differences of the fused forward
+
+def fused_objective_continuous(p, L, dy, dbounds, softplus):
+    r = oracle.scan(p["x"], p["dt"], p["B"], p["C"], p["A"], p["Dskip"], L, h0=p["h0"],
+                    want_y=True, want_bounds=dbounds is not None, dt_bias=p.get("bias"),
+                    dt_softplus=softplus, z=p.get("z"))
+    J = float(np.sum(dy * r["y"]))
+    if dbounds is not None:
+        J += float(np.sum(dbounds * r["bounds"]))
+    return J
+
+
+def fused_objective_blocks(p, L, dy, softplus):
+    y = oracle.train_blocks(p["x"], p["dt"], p["B"], p["C"], p["A"], p["Dskip"], L, p["h0_blocks"],
+                            dt_bias=p.get("bias"), dt_softplus=softplus, z=p.get("z"))
+    return float(np.sum(dy * y))
+
+
+FUSED_MODES = [("softplus_bias_gate", True, True, True), ("softplus_gate", True, False, True),
+               ("softplus_bias", True, True, False), ("bias_gate", False, True, True),
+               ("gate_only", False, False, True)]
+
+
+def fused_inputs(rng, batch, T, D, N, softplus, with_bias, with_gate):
+    p = rand64(rng, batch, T, D, N)
+    if softplus:
+        p["dt"] = rng.normal(-1.0, 0.8, (batch, T, D))       # raw pre-activation, either sign
+    if with_bias:
+        p["bias"] = rng.normal(0.0, 0.3 if softplus else 0.05, D)
+    if with_gate:
+        p["z"] = rng.normal(0.0, 1.5, (batch, T, D))
+    return p
+
+
+@pytest.mark.parametrize("mode,softplus,with_bias,with_gate", FUSED_MODES)
+def test_fused_continuous_gradient_matches_central_differences(mode, softplus, with_bias, with_gate):
+    rng = np.random.default_rng(300 + len(mode))
+    batch, T, D, N, L = 2, 8, 3, 4, 4
+    p = fused_inputs(rng, batch, T, D, N, softplus, with_bias, with_gate)
+    p["h0"] = rng.standard_normal((batch, D, N))
+    dy = rng.standard_normal((batch, T, D))
+    db = rng.standard_normal((batch, T // L + 1, D, N))
+    g = oracle.scan_bwd(p["x"], p["dt"], p["B"], p["C"], p["A"], p["Dskip"], L, dy, h0=p["h0"],
+                        dbounds=db, dt_bias=p.get("bias"), dt_softplus=softplus, z=p.get("z"))
+    names = ["x", "dt", "B", "C", "A", "Dskip", "h0"] + (["bias"] if with_bias else []) + \
+        (["z"] if with_gate else [])
+    fd = central_differences(p, names, lambda q: fused_objective_continuous(q, L, dy, db, softplus))
+    pairs = [("dx", "x"), ("ddt", "dt"), ("dB", "B"), ("dC", "C"), ("dA", "A"), ("dDskip", "Dskip"),
+             ("dh0", "h0")]
+    if with_bias:
+        pairs.append(("d_dt_bias", "bias"))
+    if with_gate:
+        pairs.append(("dz", "z"))
+    for gname, pname in pairs:
+        assert rel(g[gname], fd[pname]) < FD_TOL, (mode, gname, rel(g[gname], fd[pname]))
+
+
+@pytest.mark.parametrize("mode,softplus,with_bias,with_gate", FUSED_MODES[:2] + FUSED_MODES[3:4])
+def test_fused_two_stream_gradient_matches_central_differences(mode, softplus, with_bias, with_gate):
+    rng = np.random.default_rng(400 + len(mode))
+    batch, T, D, N, L = 2, 8, 3, 4, 2
+    p = fused_inputs(rng, batch, T, D, N, softplus, with_bias, with_gate)
+    p["h0_blocks"] = rng.standard_normal((batch, T // L + 1, D, N))
+    dy = rng.standard_normal((batch, T, D))
+    g = oracle.scan_bwd(p["x"], p["dt"], p["B"], p["C"], p["A"], p["Dskip"], L, dy,
+                        h0_blocks=p["h0_blocks"], dt_bias=p.get("bias"), dt_softplus=softplus,
+                        z=p.get("z"))
+    names = ["x", "dt", "B", "C", "A", "Dskip", "h0_blocks"] + (["bias"] if with_bias else []) + \
+        (["z"] if with_gate else [])
+    fd = central_differences(p, names, lambda q: fused_objective_blocks(q, L, dy, softplus))
+    pairs = [("dx", "x"), ("ddt", "dt"), ("dB", "B"), ("dC", "C"), ("dA", "A"), ("dDskip", "Dskip"),
+             ("dh0_blocks", "h0_blocks")]
+    if with_bias:
+        pairs.append(("d_dt_bias", "bias"))
+    if with_gate:
+        pairs.append(("dz", "z"))
+    for gname, pname in pairs:
+        assert rel(g[gname], fd[pname]) < FD_TOL, (mode, gname, rel(g[gname], fd[pname]))
+
+
+def test_fused_gradients_without_fusion_arguments_are_the_plain_ones():
+    rng = np.random.default_rng(500)
+    batch, T, D, N, L = 2, 16, 3, 4, 4
+    p = rand64(rng, batch, T, D, N)
+    dy = rng.standard_normal((batch, T, D))
+    a = oracle.scan_bwd(p["x"], p["dt"], p["B"], p["C"], p["A"], p["Dskip"], L, dy)
+    b = oracle.scan_bwd(p["x"], p["dt"], p["B"], p["C"], p["A"], p["Dskip"], L, dy, dt_bias=None,
+                        dt_softplus=False, z=None)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k

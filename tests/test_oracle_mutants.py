@@ -51,14 +51,24 @@ MUTANTS_BWD = {
     "bwd_dbounds_ignored": ("if (!blocks && block_end && dbounds)", "if (0)"),
     "bwd_ddt_missing_decay_term": ("sdt += du * bv * xv + da * at * A[d * N + n];",
                                    "sdt += du * bv * xv;"),
-    "bwd_dC_forward_only": ("my_dC[ib + n] += dy[ix] * ((at * hp[t * N + n] + u) + (at * rn[t * N + n] + u));",
-                            "my_dC[ib + n] += dy[ix] * (at * hp[t * N + n] + u);"),
+    "bwd_dC_forward_only": ("const double hsum = (at * hp[t * N + n] + u) + (at * rn[t * N + n] + u);",
+                            "const double hsum = (at * hp[t * N + n] + u);"),
     "bwd_two_stream_adjoint_crosses_blocks": ("if (blocks && block_end)\n                        for (int64_t n = 0; n < N; ++n) q[n] = 0.0;",
                                               ""),
     "bwd_forward_adjoint_no_decay": ("q[n] = at * gf;", "q[n] = gf;"),
-    "bwd_dx_missing_skip": ("dx[ix] = sx + dy[ix] * Dskip[d];", "dx[ix] = sx;"),
+    "bwd_dx_missing_skip": ("dx[ix] = sx + gy * Dskip[d];", "dx[ix] = sx;"),
     "bwd_dB_missing_dt": ("my_dB[ib + n] += du * dtv * xv;", "my_dB[ib + n] += du * xv;"),
     "bwd_dA_missing_dt": ("my_dA[d * N + n] += da * at * dtv;", "my_dA[d * N + n] += da * at;"),
+    # gradients of the fusions
+    "bwd_softplus_derivative_missing": ("const double draw = dt_softplus ? sdt * sigmoid(vraw) : sdt;",
+                                        "const double draw = sdt;"),
+    "bwd_gate_not_applied_to_dy": ("const double gy = z ? dy[ix] * silu(zv) : dy[ix];",
+                                   "const double gy = dy[ix];"),
+    "bwd_dz_missing_derivative_term": ("dz[ix] = dy[ix] * ypre * s * (1.0 + zv * (1.0 - s));",
+                                       "dz[ix] = dy[ix] * ypre * s;"),
+    "bwd_ypre_missing_skip": ("double sdt = 0.0, sx = 0.0, ypre = Dskip[d] * xv;",
+                              "double sdt = 0.0, sx = 0.0, ypre = 0.0;"),
+    "bwd_dbias_before_softplus": ("my_dbias[d] += draw;", "my_dbias[d] += sdt;"),
 }
 
 MUTANTS_FUSED = {
