@@ -547,8 +547,8 @@ def train_main(args, wl, m, synth, torch):
     b.record(st)
     torch.cuda.synchronize()
     two_ms = a.elapsed_time(b) / args.steps
-    # the backward differentiates the plain scan with 16 states and L | 16
-    if args.fused or args.reverse_operands or ns != NS or L not in (1, 2, 4, 8, 16):
+    # the backward runs 16 states, L | 16, and no separate reverse operands
+    if args.reverse_operands or ns != NS or L not in (1, 2, 4, 8, 16):
         line = train_line(args, batch, D, T, L, dtype, nbytes, slots, ms_per_step, ev_ms,
                           blocks_ms, full_ms, two_ms, None, None, None, torch, ns)
         print(json.dumps(line), flush=True)
@@ -561,28 +561,30 @@ def train_main(args, wl, m, synth, torch):
                       dtype=torch.uint8, device=dev)
     wsbb = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_BLOCKS_BWD, L, ns, dtype)),
                        dtype=torch.uint8, device=dev)
-    m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, h_bounds=bnd, ws=ws)
-    m.train_scan_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, ws=wsb)
+    m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, h_bounds=bnd, ws=ws, **fz)
+    m.train_scan_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, ws=wsb, **fz)
     torch.cuda.synchronize()
     a.record(st)
     for _ in range(args.steps):
-        m.train_scan_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, ws=wsb)
+        m.train_scan_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, ws=wsb, **fz)
     b.record(st)
     torch.cuda.synchronize()
     bwd_ms = a.elapsed_time(b) / args.steps
     a.record(st)
     for _ in range(args.steps):
-        m.train_scan_blocks_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, want_dh0_blocks=True, ws=wsbb)
+        m.train_scan_blocks_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, want_dh0_blocks=True, ws=wsbb,
+                                **fz)
     b.record(st)
     torch.cuda.synchronize()
     bbwd_ms = a.elapsed_time(b) / args.steps
 
     def all_block_step():
-        m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, h_bounds=bnd, ws=ws)
-        m.train_scan_blocks(x, dt, Bm, Cm, A, Dskip, L, bnd, y=y)
+        m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, h_bounds=bnd, ws=ws, **fz)
+        m.train_scan_blocks(x, dt, Bm, Cm, A, Dskip, L, bnd, y=y, **fz)
         gn = m.train_scan_blocks_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, want_dh0_blocks=True,
-                                     ws=wsbb)
-        m.train_scan_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, d_bounds=gn["dh0_blocks"], ws=wsb)
+                                     ws=wsbb, **fz)
+        m.train_scan_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, d_bounds=gn["dh0_blocks"], ws=wsb,
+                         **fz)
 
     all_block_step()
     torch.cuda.synchronize()

@@ -107,8 +107,9 @@ typedef enum {
  *               silu(z), silu(v) = v / (1 + e^-v).  Read only by calls that
  *               write y.
  * With dt_bias = NULL, dt_softplus = 0 and z = NULL every result is the same
- * as with no fusion.  The backward entry points take no fusion: they
- * differentiate the unfused scan.
+ * as with no fusion.  The backward entry points take dt_bias, dt_softplus and z
+ * (the gradients of the fused forward); they reject separate reverse
+ * operands.
  */
 typedef struct {
     const float *dt_bias;
@@ -231,12 +232,27 @@ int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, 
  *   ws       ws_bytes >= bdssm_workspace_bytes(shape, T, BDSSM_OP_TRAIN_BWD).
  * Sums over channels (dB, dC), batch and tokens (dA, dDskip) are taken in a
  * fixed order: results are bitwise reproducible for a given shape.
+ * fusion: the same bdssm_fusion as the forward call, or NULL.  With dt_bias /
+ *   dt_softplus, ddt is the gradient of the dt stream (before the bias and
+ *   softplus: the step size's gradient times softplus'(v) = 1 / (1 + e^-v)).
+ *   With z, dy is the gradient of the gated output y_pre silu(z); the gate's
+ *   gradient dz = dy y_pre silu'(z) (y_pre recomputed) goes to grads->dz.
+ *   Separate reverse operands (dt_rev) are rejected with BDSSM_ERR_SHAPE.
+ * grads: NULL, or the outputs of the fusion's gradients: dz [batch, T, D]
+ *   stream dtype (required when fusion->z is given); d_dt_bias NULL or [D] fp32,
+ *   the dt stream's gradient summed over batch and tokens (= dJ/d dt_bias).
  */
+typedef struct {
+    void *dz;
+    float *d_dt_bias;
+} bdssm_fusion_grads;
+
 int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
                          const void *B, const void *C, const float *A, const float *Dskip,
                          const float *h_bounds, const void *dy, const float *d_bounds, void *dx,
                          void *ddt, void *dB, void *dC, float *dA, float *dDskip, float *dh_init,
-                         void *ws, size_t ws_bytes, void *stream);
+                         void *ws, size_t ws_bytes, const bdssm_fusion *fusion,
+                         bdssm_fusion_grads *grads, void *stream);
 
 /*
  * Backward of bdssm_train_scan_blocks (the noisy stream of the two-stream
@@ -245,7 +261,7 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
  * stream's block states (pass it as d_bounds to bdssm_train_scan_bwd).
  *   h0_blocks [batch, T/L+1, D, N] fp32: the same block start states as the
  *             forward call.
- *   dy, dx, ddt, dB, dC, dA, dDskip as in bdssm_train_scan_bwd.
+ *   dy, dx, ddt, dB, dC, dA, dDskip, fusion, grads as in bdssm_train_scan_bwd.
  *   dh0_blocks NULL, or [batch, T/L+1, D, N] fp32 out (entry T/L is zero).
  *   ws        ws_bytes >= bdssm_workspace_bytes(shape, T, BDSSM_OP_BLOCKS_BWD).
  */
@@ -253,7 +269,8 @@ int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void 
                                 const void *B, const void *C, const float *A, const float *Dskip,
                                 const float *h0_blocks, const void *dy, void *dx, void *ddt,
                                 void *dB, void *dC, float *dA, float *dDskip, float *dh0_blocks,
-                                void *ws, size_t ws_bytes, void *stream);
+                                void *ws, size_t ws_bytes, const bdssm_fusion *fusion,
+                                bdssm_fusion_grads *grads, void *stream);
 
 /*
  * Baseline: the full-sequence bidirectional scan of the earlier diffusion

@@ -53,6 +53,10 @@ class Fusion(ctypes.Structure):
                 ("dt_bias_rev", ctypes.c_void_p)]
 
 
+class FusionGrads(ctypes.Structure):
+    _fields_ = [("dz", ctypes.c_void_p), ("d_dt_bias", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -74,8 +78,9 @@ def load():
     lib.bdssm_train_scan.argtypes = [S, I, P, P, P, P, P, P, P, P, P, P, Z, F, P]
     lib.bdssm_full_scan.argtypes = [S, I, P, P, P, P, P, P, P, P, Z, F, P]
     lib.bdssm_train_scan_blocks.argtypes = [S, I, P, P, P, P, P, P, P, P, F, P]
-    lib.bdssm_train_scan_bwd.argtypes = [S, I] + [P] * 17 + [Z, P]
-    lib.bdssm_train_scan_blocks_bwd.argtypes = [S, I] + [P] * 16 + [Z, P]
+    G = ctypes.POINTER(FusionGrads)
+    lib.bdssm_train_scan_bwd.argtypes = [S, I] + [P] * 17 + [Z, F, G, P]
+    lib.bdssm_train_scan_blocks_bwd.argtypes = [S, I] + [P] * 16 + [Z, F, G, P]
     for f in ("bdssm_prefill", "bdssm_block_step", "bdssm_commit", "bdssm_train_scan",
               "bdssm_train_scan_blocks", "bdssm_full_scan", "bdssm_train_scan_bwd",
               "bdssm_train_scan_blocks_bwd", "bdssm_version"):
@@ -312,11 +317,29 @@ def _grad_outputs(x, D, N):
             torch.empty(D, dtype=torch.float32, device=dev))
 
 
+def _fusion_grads(x, D, fusion):
+    """Outputs of the fused forward's gradients: dz when z is given, d_dt_bias
+    when dt_bias is -> (ctypes pointer or None, dict of the tensors)."""
+    out = {}
+    if fusion.get("z") is not None:
+        out["dz"] = torch.empty_like(x)
+    if fusion.get("dt_bias") is not None:
+        out["d_dt_bias"] = torch.empty(D, dtype=torch.float32, device=x.device)
+    if not out:
+        return None, out
+    ptr = lambda t: None if t is None else t.data_ptr()
+    g = FusionGrads(ptr(out.get("dz")), ptr(out.get("d_dt_bias")))
+    return ctypes.pointer(g), out
+
+
 def train_scan_bwd(x, dt, B, C, A, Dskip, block_len, h_bounds, dy, d_bounds=None,
-                   want_dh_init=False, ws=None):
+                   want_dh_init=False, ws=None, **fusion):
     """Gradients of train_scan given dy (and dJ/dh_bounds) -> dict with dx, ddt,
     dB, dC (stream dtype), dA, dDskip (fp32) and dh_init (fp32 or None).
-    h_bounds: the block states train_scan returned for the same inputs."""
+    h_bounds: the block states train_scan returned for the same inputs.
+    fusion: the forward's dt_bias / dt_softplus / z; ddt is then the gradient
+    of the raw dt stream, and the dict gains d_dt_bias (fp32 [D], with a bias)
+    and dz (with a gate)."""
     batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip)
     nb = T // block_len + 1
     _check(h_bounds, "h_bounds", torch.float32, (batch, nb, D, N))
@@ -327,18 +350,22 @@ def train_scan_bwd(x, dt, B, C, A, Dskip, block_len, h_bounds, dy, d_bounds=None
     s = _shape(batch, D, N, block_len, code)
     if ws is None:
         ws = _workspace(workspace_bytes(batch, D, T, OP_TRAIN_BWD, block_len, N, x.dtype), x.device)
+    fz = _fusion(x, D, **fusion)
+    gz, extra = _fusion_grads(x, D, fusion)
     rc = load().bdssm_train_scan_bwd(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A),
                                      _p(Dskip), _p(h_bounds), _p(dy), _p(d_bounds), _p(dx),
                                      _p(ddt), _p(dB), _p(dC), _p(dA), _p(dDs), _p(dh), _p(ws),
-                                     0 if ws is None else ws.numel(), _stream())
+                                     0 if ws is None else ws.numel(), fz, gz, _stream())
     _raise("bdssm_train_scan_bwd", rc)
-    return {"dx": dx, "ddt": ddt, "dB": dB, "dC": dC, "dA": dA, "dDskip": dDs, "dh_init": dh}
+    return dict({"dx": dx, "ddt": ddt, "dB": dB, "dC": dC, "dA": dA, "dDskip": dDs, "dh_init": dh},
+                **extra)
 
 
 def train_scan_blocks_bwd(x, dt, B, C, A, Dskip, block_len, h0_blocks, dy, want_dh0_blocks=False,
-                          ws=None):
+                          ws=None, **fusion):
     """Gradients of train_scan_blocks -> dict with dx, ddt, dB, dC, dA, dDskip
-    and dh0_blocks ([batch, T/L+1, D, 16] fp32, or None)."""
+    and dh0_blocks ([batch, T/L+1, D, 16] fp32, or None); with the fusions as
+    in train_scan_bwd, also d_dt_bias and dz."""
     batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip)
     nb = T // block_len + 1
     _check(h0_blocks, "h0_blocks", torch.float32, (batch, nb, D, N))
@@ -349,9 +376,12 @@ def train_scan_blocks_bwd(x, dt, B, C, A, Dskip, block_len, h0_blocks, dy, want_
     s = _shape(batch, D, N, block_len, code)
     if ws is None:
         ws = _workspace(workspace_bytes(batch, D, T, OP_BLOCKS_BWD, block_len, N, x.dtype), x.device)
+    fz = _fusion(x, D, **fusion)
+    gz, extra = _fusion_grads(x, D, fusion)
     rc = load().bdssm_train_scan_blocks_bwd(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A),
                                             _p(Dskip), _p(h0_blocks), _p(dy), _p(dx), _p(ddt),
                                             _p(dB), _p(dC), _p(dA), _p(dDs), _p(dh), _p(ws),
-                                            0 if ws is None else ws.numel(), _stream())
+                                            0 if ws is None else ws.numel(), fz, gz, _stream())
     _raise("bdssm_train_scan_blocks_bwd", rc)
-    return {"dx": dx, "ddt": ddt, "dB": dB, "dC": dC, "dA": dA, "dDskip": dDs, "dh0_blocks": dh}
+    return dict({"dx": dx, "ddt": ddt, "dB": dB, "dC": dC, "dA": dA, "dDskip": dDs,
+                 "dh0_blocks": dh}, **extra)

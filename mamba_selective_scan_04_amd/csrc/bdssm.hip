@@ -34,7 +34,7 @@ using namespace bdssm_dev;
 
 namespace {
 
-constexpr int kVersion = 10300;   // 1.3.0
+constexpr int kVersion = 10400;   // 1.4.0
 
 // 256 CUs x 4 SIMDs x 8 resident waves (the chunk kernel fits in 64 VGPRs)
 constexpr int64_t kFineWaves = 256 * 4 * 8;
@@ -218,9 +218,10 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 //   continuous form with several coarse chunks: agg_q [batch, n_fine, D, 16],
 //     agg_s [batch, n_fine, D], q_in [batch, n_fine, D, 16];
 //   both forms: part_bc [batch, ceil(D/32), T, 32], part_a [batch, nc, D, 16],
+//     part_bias [batch, nc, D] (the dt_bias gradient of the fused backward),
 //     part_d [batch, nc, D]   (nc = coarse chunks of the backward pass).
 struct BwdWorkspace {
-    float *agg_q, *agg_s, *q_in, *part_bc, *part_a, *part_d;
+    float *agg_q, *agg_s, *q_in, *part_bc, *part_a, *part_d, *part_bias;
     size_t bytes;
 };
 
@@ -243,6 +244,7 @@ BwdWorkspace layout_bwd(void *base, int64_t batch, int64_t D, int64_t T, int64_t
     w.part_bc = take((size_t)batch * ceil_div(D, kPairChannels) * T * 32 * sizeof(float));
     w.part_a = take((size_t)batch * nc * D * kStates * sizeof(float));
     w.part_d = take((size_t)batch * nc * D * sizeof(float));
+    w.part_bias = take((size_t)batch * nc * D * sizeof(float));
     w.bytes = off;
     return w;
 }
@@ -606,16 +608,15 @@ void launch_sweep(bool rev, const void *x, const void *dt, const void *B, const 
     });
 }
 
-template <typename Tin>
-void launch_adjoint_chunk(const void *dt, const void *dy, const void *C, const float *A,
-                          const float *dbounds, float *qout, float *sout, int64_t batch, int64_t T,
-                          int64_t D, int64_t L, int64_t Tc, int n_chunks, int c_first, int n_launch,
-                          hipStream_t st) {
-    if (n_launch <= 0) return;
+template <typename Tin, int kDt>
+void launch_adjoint_chunk_k(const void *dt, const void *dy, const void *C, const float *A,
+                            const float *dbounds, float *qout, float *sout, int64_t batch, int64_t T,
+                            int64_t D, int64_t L, int64_t Tc, int n_chunks, int c_first, int n_launch,
+                            const float *dt_bias, const void *z, hipStream_t st) {
 #define BDSSM_ADJ(LL)                                                                              \
-    hipLaunchKernelGGL((adjoint_chunk_kernel<Tin, LL>), grid3(D, n_launch, batch), dim3(kWave), 0, st, \
-                       (const Tin *)dt, (const Tin *)dy, (const Tin *)C, A, dbounds, qout, sout, T,   \
-                       (int)D, Tc, n_chunks, c_first)
+    hipLaunchKernelGGL((adjoint_chunk_kernel<Tin, LL, kDt>), grid3(D, n_launch, batch), dim3(kWave), 0, \
+                       st, (const Tin *)dt, (const Tin *)dy, (const Tin *)C, A, dbounds, qout, sout, T, \
+                       (int)D, Tc, n_chunks, c_first, dt_bias, (const Tin *)z)
     switch (L) {
     case 1: BDSSM_ADJ(1); break;
     case 2: BDSSM_ADJ(2); break;
@@ -626,12 +627,44 @@ void launch_adjoint_chunk(const void *dt, const void *dy, const void *C, const f
 #undef BDSSM_ADJ
 }
 
+// Adjoint aggregates of n_launch fine chunks; the step size and gate of the
+// fused forward when given.
+template <typename Tin>
+void launch_adjoint_chunk(const void *dt, const void *dy, const void *C, const float *A,
+                          const float *dbounds, float *qout, float *sout, int64_t batch, int64_t T,
+                          int64_t D, int64_t L, int64_t Tc, int n_chunks, int c_first, int n_launch,
+                          hipStream_t st, int dt_mode = kDtPlain, const float *dt_bias = nullptr,
+                          const void *z = nullptr) {
+    if (n_launch <= 0) return;
+    switch (dt_mode) {
+    case kDtSoftplus:
+        launch_adjoint_chunk_k<Tin, kDtSoftplus>(dt, dy, C, A, dbounds, qout, sout, batch, T, D, L, Tc,
+                                                 n_chunks, c_first, n_launch, dt_bias, z, st);
+        break;
+    case kDtBias:
+        launch_adjoint_chunk_k<Tin, kDtBias>(dt, dy, C, A, dbounds, qout, sout, batch, T, D, L, Tc,
+                                             n_chunks, c_first, n_launch, dt_bias, z, st);
+        break;
+    default:
+        launch_adjoint_chunk_k<Tin, kDtPlain>(dt, dy, C, A, dbounds, qout, sout, batch, T, D, L, Tc,
+                                              n_chunks, c_first, n_launch, dt_bias, z, st);
+        break;
+    }
+}
+
 struct BwdArgs {
     const void *x, *dt, *B, *C, *dy;
     const float *A, *Dskip, *h_start, *qin, *dbounds;
     int64_t qin_bs, qin_cs;
     void *dx, *ddt;
     float *part_bc, *part_a, *part_d, *dh0;
+    // the fused forward's gradients (fused: any of them in use)
+    bool fused = false;
+    const float *dt_bias = nullptr;
+    int dt_mode = kDtPlain;
+    const void *z = nullptr;
+    void *dz = nullptr;
+    float *part_bias = nullptr;
 };
 
 // The backward's block-local kernel.  bwd_pair_kernel (two states per lane,
@@ -640,7 +673,8 @@ struct BwdArgs {
 // four-state bwd_wave_kernel (segment recomputation, 64 channels per
 // workgroup) is faster (measured on MI355X).  BDSSM_BWD_KERNEL=wave / pair
 // forces one of them (tuning and tests).
-bool bwd_use_wave(int64_t L) {
+bool bwd_use_wave(int64_t L, bool fused = false) {
+    if (fused) return false;                 // only bwd_pair_kernel has the fused variant
     const char *v = getenv("BDSSM_BWD_KERNEL");
     if (v != nullptr && v[0] == 'w') return true;
     if (v != nullptr && v[0] == 'p') return false;
@@ -648,24 +682,31 @@ bool bwd_use_wave(int64_t L) {
 }
 
 // channels per workgroup of the chosen kernel (the dB / dC partial blocks)
-int64_t bwd_block_channels(int64_t L) { return bwd_use_wave(L) ? kWave : kPairChannels; }
+int64_t bwd_block_channels(int64_t L, bool fused = false) {
+    return bwd_use_wave(L, fused) ? kWave : kPairChannels;
+}
 
 // workgroups of the chosen kernel resident at once: bwd_pair_kernel fits
 // three per CU (168 registers, 44 KB LDS), bwd_wave_kernel two
-int64_t bwd_block_capacity(int64_t L) { return bwd_use_wave(L) ? kCoarseGroups : 3 * 256; }
+int64_t bwd_block_capacity(int64_t L, bool fused = false) {
+    return bwd_use_wave(L, fused) ? kCoarseGroups : 3 * 256;
+}
 
 // chunk plans of the two backward forms, for the chosen kernel's geometry
-Plan bwd_plan(int64_t batch, int64_t D, int64_t T, int64_t L) {
-    return make_plan(batch, D, T, kBwdPrepassWeight, bwd_block_channels(L), bwd_block_capacity(L));
+Plan bwd_plan(int64_t batch, int64_t D, int64_t T, int64_t L, bool fused = false) {
+    return make_plan(batch, D, T, kBwdPrepassWeight, bwd_block_channels(L, fused),
+                     bwd_block_capacity(L, fused));
 }
-bool bwd_blocks_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t *tc, int64_t *nc) {
-    return blocks_plan(batch, D, T, L, kStates, tc, nc, bwd_block_channels(L), bwd_block_capacity(L));
+bool bwd_blocks_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t *tc, int64_t *nc,
+                     bool fused = false) {
+    return blocks_plan(batch, D, T, L, kStates, tc, nc, bwd_block_channels(L, fused),
+                       bwd_block_capacity(L, fused));
 }
 
 template <typename Tin, int L, bool kBlockInit>
 void launch_bwd_L(const BwdArgs &a, int64_t batch, int64_t T, int64_t D, int64_t Tc, int nc,
                   hipStream_t st) {
-    if (bwd_use_wave(L)) {
+    if (bwd_use_wave(L, a.fused)) {
         hipLaunchKernelGGL((bwd_wave_kernel<Tin, L, kBlockInit>), grid3(D, nc, batch), dim3(4 * kWave), 0,
                            st, (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
                            (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
@@ -674,11 +715,19 @@ void launch_bwd_L(const BwdArgs &a, int64_t batch, int64_t T, int64_t D, int64_t
         return;
     }
     const dim3 g((unsigned)ceil_div(D, kPairChannels), (unsigned)nc, (unsigned)batch);
-    hipLaunchKernelGGL((bwd_pair_kernel<Tin, L, kBlockInit>), g, dim3(4 * kWave), 0, st,
-                       (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
-                       (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
-                       a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0, T,
-                       (int)D, Tc);
+    const BwdFuse<Tin> fz{a.dt_bias, a.dt_mode, (const Tin *)a.z, (Tin *)a.dz, a.part_bias};
+    if (a.fused)
+        hipLaunchKernelGGL((bwd_pair_kernel<Tin, L, kBlockInit, true>), g, dim3(4 * kWave), 0, st,
+                           (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
+                           (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
+                           a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0,
+                           T, (int)D, Tc, fz);
+    else
+        hipLaunchKernelGGL((bwd_pair_kernel<Tin, L, kBlockInit, false>), g, dim3(4 * kWave), 0, st,
+                           (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
+                           (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
+                           a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0,
+                           T, (int)D, Tc, fz);
 }
 
 template <typename Tin, bool kBlockInit>
@@ -695,12 +744,16 @@ void launch_bwd(int64_t L, const BwdArgs &a, int64_t batch, int64_t T, int64_t D
 
 template <typename Tin>
 void launch_bwd_reduce(const BwdWorkspace &w, void *dB, void *dC, float *dA, float *dDskip,
-                       int64_t batch, int64_t T, int64_t D, int64_t L, int64_t nc, hipStream_t st) {
+                       int64_t batch, int64_t T, int64_t D, int64_t L, int64_t nc, hipStream_t st,
+                       bool fused = false, float *d_bias = nullptr) {
     const int64_t nbc = batch * T * 32;
     hipLaunchKernelGGL((bc_reduce_kernel<Tin>), dim3((unsigned)ceil_div(nbc, 256)), dim3(256), 0, st,
-                       w.part_bc, (Tin *)dB, (Tin *)dC, (int)batch, T, (int)ceil_div(D, bwd_block_channels(L)));
-    hipLaunchKernelGGL(param_reduce_kernel, dim3((unsigned)ceil_div(D * (kStates + 1), 256)), dim3(256),
-                       0, st, w.part_a, w.part_d, dA, dDskip, (int)D, (int)(batch * nc));
+                       w.part_bc, (Tin *)dB, (Tin *)dC, (int)batch, T,
+                       (int)ceil_div(D, bwd_block_channels(L, fused)));
+    const bool nb = fused && d_bias != nullptr;
+    hipLaunchKernelGGL(param_reduce_kernel, dim3((unsigned)ceil_div(D * (kStates + (nb ? 2 : 1)), 256)),
+                       dim3(256), 0, st, w.part_a, w.part_d, dA, dDskip, (int)D, (int)(batch * nc),
+                       nb ? w.part_bias : nullptr, nb ? d_bias : nullptr);
 }
 
 // Forward state only over T tokens from h_init: h_final <- state after T.
@@ -795,19 +848,31 @@ const char *bdssm_status_str(int status) {
 size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T, int op) {
     if (check_shape(shape) != BDSSM_OK || T < 0 || T % shape->block_len != 0) return (size_t)-1;
     if (op < BDSSM_OP_PREFILL || op > BDSSM_OP_BLOCKS_BWD) return (size_t)-1;
-    const int64_t batch = shape->batch, D = shape->d_inner, N = shape->d_state;
+    const int64_t batch = shape->batch, D = shape->d_inner;
     if (batch == 0 || D == 0 || T == 0) return 0;
     if ((op == BDSSM_OP_TRAIN_BWD || op == BDSSM_OP_BLOCKS_BWD) &&
         (!wave_block(shape->block_len) || shape->d_state != kStates))
         return (size_t)-1;
+    // the backward's plan depends on the kernel, which a fusion can change:
+    // size for the larger of the two
     if (op == BDSSM_OP_TRAIN_BWD) {
-        const Plan p = bwd_plan(batch, D, T, shape->block_len);
-        return layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, p.n_coarse > 1).bytes;
+        size_t n = 0;
+        for (int fused = 0; fused < 2; ++fused) {
+            const Plan p = bwd_plan(batch, D, T, shape->block_len, fused != 0);
+            const size_t m = layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, p.n_coarse > 1).bytes;
+            n = m > n ? m : n;
+        }
+        return n;
     }
     if (op == BDSSM_OP_BLOCKS_BWD) {
-        int64_t tc, nc;
-        if (!bwd_blocks_plan(batch, D, T, shape->block_len, &tc, &nc)) return (size_t)-1;
-        return layout_bwd(nullptr, batch, D, T, 1, nc, false).bytes;
+        size_t n = 0;
+        for (int fused = 0; fused < 2; ++fused) {
+            int64_t tc, nc;
+            if (!bwd_blocks_plan(batch, D, T, shape->block_len, &tc, &nc, fused != 0)) return (size_t)-1;
+            const size_t m = layout_bwd(nullptr, batch, D, T, 1, nc, false).bytes;
+            n = m > n ? m : n;
+        }
+        return n;
     }
     Plan p;
     if (op == BDSSM_OP_FULL) p = make_plan(batch, D, T);
@@ -1087,6 +1152,47 @@ bool ws_clear(void *ws, size_t bytes, std::initializer_list<Range> others) {
     return true;
 }
 
+// The fused forward's gradients requested from a backward call: resolves the
+// fusion and checks the extra arguments (alignment; dz and d_dt_bias are
+// outputs, z and dt_bias inputs; separate reverse operands are rejected).
+int resolve_bwd_fusion(const bdssm_fusion *f, bdssm_fusion_grads *g, const bdssm_shape *s,
+                       int64_t T, std::initializer_list<Range> ins, std::initializer_list<Range> outs,
+                       BwdArgs *a) {
+    a->fused = false;
+    if (f != nullptr && f->dt_rev != nullptr) return BDSSM_ERR_SHAPE;
+    const float *bias = f ? f->dt_bias : nullptr;
+    const int mode = (f && f->dt_softplus) ? kDtSoftplus : (bias ? kDtBias : kDtPlain);
+    const void *z = f ? f->z : nullptr;
+    void *dz = g ? g->dz : nullptr;
+    float *dbias = g ? g->d_dt_bias : nullptr;
+    if (z != nullptr && dz == nullptr) return BDSSM_ERR_NULL;
+    if (z == nullptr) dz = nullptr;
+    const void *ps[] = {bias, z, dz, dbias};
+    for (const void *p : ps)
+        if (!aligned16(p)) return BDSSM_ERR_ALIGN;
+    const size_t ntok = (size_t)s->batch * T * s->d_inner * esize(s);
+    const Range fin[] = {{bias, (size_t)s->d_inner * 4}, {z, ntok}};
+    const Range fout[] = {{dz, ntok}, {dbias, (size_t)s->d_inner * 4}};
+    for (const Range &o : fout) {
+        for (const Range &i : ins)
+            if (overlaps(o, i)) return BDSSM_ERR_ALIAS;
+        for (const Range &i : fin)
+            if (overlaps(o, i)) return BDSSM_ERR_ALIAS;
+        for (const Range &o2 : outs)
+            if (overlaps(o, o2)) return BDSSM_ERR_ALIAS;
+    }
+    if (overlaps(fout[0], fout[1])) return BDSSM_ERR_ALIAS;
+    for (const Range &o : outs)
+        for (const Range &i : fin)
+            if (overlaps(o, i)) return BDSSM_ERR_ALIAS;
+    a->fused = mode != kDtPlain || z != nullptr || dbias != nullptr;
+    a->dt_bias = bias;
+    a->dt_mode = mode;
+    a->z = z;
+    a->dz = dz;
+    return BDSSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1095,23 +1201,40 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
                          const void *B, const void *C, const float *A, const float *Dskip,
                          const float *h_bounds, const void *dy, const float *d_bounds, void *dx,
                          void *ddt, void *dB, void *dC, float *dA, float *dDskip, float *dh_init,
-                         void *ws, size_t ws_bytes, void *stream) {
+                         void *ws, size_t ws_bytes, const bdssm_fusion *fusion,
+                         bdssm_fusion_grads *grads, void *stream) {
     const size_t nstate = shape ? (size_t)(shape->batch > 0 ? shape->batch : 0) *
                                       (shape->d_inner > 0 ? shape->d_inner : 0) * kStates * 4 : 0;
     int rc = check_bwd(shape, T, x, dt, B, C, A, Dskip, h_bounds, dy, d_bounds, dx, ddt, dB, dC, dA,
                        dDskip, dh_init, nstate);
     if (rc) return rc;
     const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len;
+    BwdArgs a{x, dt, B, C, dy, A, Dskip, h_bounds, nullptr, d_bounds, 0, 0, dx, ddt,
+              nullptr, nullptr, nullptr, dh_init};
+    {
+        const size_t e = esize(shape);
+        const size_t ntok = (size_t)batch * T * D * e, nbc = (size_t)batch * T * kStates * e;
+        const size_t nbnd = (size_t)batch * (T / L + 1) * D * kStates * 4;
+        rc = resolve_bwd_fusion(fusion, grads, shape, T,
+                                {{x, ntok}, {dt, ntok}, {B, nbc}, {C, nbc}, {dy, ntok}, {h_bounds, nbnd},
+                                 {d_bounds, nbnd}, {A, (size_t)D * kStates * 4}, {Dskip, (size_t)D * 4}},
+                                {{dx, ntok}, {ddt, ntok}, {dB, nbc}, {dC, nbc}, {dA, (size_t)D * kStates * 4},
+                                 {dDskip, (size_t)D * 4}, {dh_init, nstate}, {ws, ws_bytes}},
+                                &a);
+        if (rc) return rc;
+    }
+    float *d_bias = grads ? grads->d_dt_bias : nullptr;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (batch == 0 || D == 0 || T == 0) {
         rc = zero_bwd(D, dA, dDskip, dh_init, batch * D * kStates, st);
+        if (!rc && d_bias && D > 0) rc = copy_or_zero(nullptr, d_bias, D, st);
         if (rc || dh_init == nullptr || d_bounds == nullptr || batch == 0 || D == 0) return rc;
         // T == 0: the only gradient of the start state is its own bound
         return copy_or_zero(d_bounds, dh_init, batch * D * kStates, st);
     }
     if (!aligned16(ws)) return BDSSM_ERR_ALIGN;
-    const Plan p = bwd_plan(batch, D, T, L);
+    const Plan p = bwd_plan(batch, D, T, L, a.fused);
     const bool carry = p.n_coarse > 1;
     const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, carry);
     if (ws == nullptr || ws_bytes < probe.bytes) return BDSSM_ERR_WORKSPACE;
@@ -1126,18 +1249,22 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
         return BDSSM_ERR_ALIAS;
     const BwdWorkspace w = layout_bwd(ws, batch, D, T, p.n_fine, p.n_coarse, carry);
     const int64_t hs = D * kStates;
-    BwdArgs a{x, dt, B, C, dy, A, Dskip, h_bounds, nullptr, d_bounds, 0, 0, dx, ddt,
-              w.part_bc, w.part_a, w.part_d, dh_init};
+    a.part_bc = w.part_bc;
+    a.part_a = w.part_a;
+    a.part_d = w.part_d;
+    a.part_bias = w.part_bias;
     const int64_t Tc = carry ? p.fine_len * p.per_coarse : p.fine_len * p.n_fine;
     if (carry) {
         // adjoint aggregates of the fine chunks right of the first coarse chunk,
         // then the adjoint entering each fine chunk from its right end
         if (shape->dtype == BDSSM_BF16)
             launch_adjoint_chunk<uint16_t>(dt, dy, C, A, d_bounds, w.agg_q, w.agg_s, batch, T, D, L,
-                                           p.fine_len, p.n_fine, p.per_coarse, p.n_fine - p.per_coarse, st);
+                                           p.fine_len, p.n_fine, p.per_coarse, p.n_fine - p.per_coarse, st,
+                                           a.dt_mode, a.dt_bias, a.z);
         else
             launch_adjoint_chunk<float>(dt, dy, C, A, d_bounds, w.agg_q, w.agg_s, batch, T, D, L,
-                                        p.fine_len, p.n_fine, p.per_coarse, p.n_fine - p.per_coarse, st);
+                                        p.fine_len, p.n_fine, p.per_coarse, p.n_fine - p.per_coarse, st,
+                                        a.dt_mode, a.dt_bias, a.z);
         launch_carry(true, w.agg_q, w.agg_s, A, nullptr, w.q_in, nullptr, batch, D, kStates, p.n_fine,
                      p.n_fine, st, p.per_coarse - 1);
         a.qin = w.q_in + (int64_t)(p.per_coarse - 1) * hs;
@@ -1147,10 +1274,10 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
     const int nc = carry ? p.n_coarse : 1;
     if (shape->dtype == BDSSM_BF16) {
         launch_bwd<uint16_t, false>(L, a, batch, T, D, Tc, nc, st);
-        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, nc, st);
+        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, nc, st, a.fused, d_bias);
     } else {
         launch_bwd<float, false>(L, a, batch, T, D, Tc, nc, st);
-        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, nc, st);
+        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, nc, st, a.fused, d_bias);
     }
     return launch_status();
 }
@@ -1159,7 +1286,8 @@ int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void 
                                 const void *B, const void *C, const float *A, const float *Dskip,
                                 const float *h0_blocks, const void *dy, void *dx, void *ddt,
                                 void *dB, void *dC, float *dA, float *dDskip, float *dh0_blocks,
-                                void *ws, size_t ws_bytes, void *stream) {
+                                void *ws, size_t ws_bytes, const bdssm_fusion *fusion,
+                                bdssm_fusion_grads *grads, void *stream) {
     size_t nbnd = 0;
     if (shape && shape->block_len > 0 && T >= 0 && shape->batch > 0 && shape->d_inner > 0)
         nbnd = (size_t)shape->batch * (T / shape->block_len + 1) * shape->d_inner * kStates * 4;
@@ -1167,13 +1295,30 @@ int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void 
                        dDskip, dh0_blocks, nbnd);
     if (rc) return rc;
     const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len;
+    BwdArgs a{x, dt, B, C, dy, A, Dskip, h0_blocks, nullptr, nullptr, 0, 0, dx, ddt,
+              nullptr, nullptr, nullptr, dh0_blocks};
+    {
+        const size_t e = esize(shape);
+        const size_t ntok = (size_t)batch * T * D * e, nbc = (size_t)batch * T * kStates * e;
+        rc = resolve_bwd_fusion(fusion, grads, shape, T,
+                                {{x, ntok}, {dt, ntok}, {B, nbc}, {C, nbc}, {dy, ntok}, {h0_blocks, nbnd},
+                                 {A, (size_t)D * kStates * 4}, {Dskip, (size_t)D * 4}},
+                                {{dx, ntok}, {ddt, ntok}, {dB, nbc}, {dC, nbc}, {dA, (size_t)D * kStates * 4},
+                                 {dDskip, (size_t)D * 4}, {dh0_blocks, nbnd}, {ws, ws_bytes}},
+                                &a);
+        if (rc) return rc;
+    }
+    float *d_bias = grads ? grads->d_dt_bias : nullptr;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    if (batch == 0 || D == 0 || T == 0)
-        return zero_bwd(D, dA, dDskip, dh0_blocks, batch * D * kStates, st);
+    if (batch == 0 || D == 0 || T == 0) {
+        rc = zero_bwd(D, dA, dDskip, dh0_blocks, batch * D * kStates, st);
+        if (!rc && d_bias && D > 0) rc = copy_or_zero(nullptr, d_bias, D, st);
+        return rc;
+    }
     if (!aligned16(ws)) return BDSSM_ERR_ALIGN;
     int64_t tc, nc;
-    if (!bwd_blocks_plan(batch, D, T, L, &tc, &nc)) return BDSSM_ERR_SHAPE;
+    if (!bwd_blocks_plan(batch, D, T, L, &tc, &nc, a.fused)) return BDSSM_ERR_SHAPE;
     const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, 1, nc, false);
     if (ws == nullptr || ws_bytes < probe.bytes) return BDSSM_ERR_WORKSPACE;
     const size_t e = esize(shape);
@@ -1185,14 +1330,16 @@ int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void 
                                     {A, (size_t)D * kStates * 4}, {Dskip, (size_t)D * 4}}))
         return BDSSM_ERR_ALIAS;
     const BwdWorkspace w = layout_bwd(ws, batch, D, T, 1, nc, false);
-    const BwdArgs a{x, dt, B, C, dy, A, Dskip, h0_blocks, nullptr, nullptr, 0, 0, dx, ddt,
-                    w.part_bc, w.part_a, w.part_d, dh0_blocks};
+    a.part_bc = w.part_bc;
+    a.part_a = w.part_a;
+    a.part_d = w.part_d;
+    a.part_bias = w.part_bias;
     if (shape->dtype == BDSSM_BF16) {
         launch_bwd<uint16_t, true>(L, a, batch, T, D, tc, (int)nc, st);
-        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, nc, st);
+        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, nc, st, a.fused, d_bias);
     } else {
         launch_bwd<float, true>(L, a, batch, T, D, tc, (int)nc, st);
-        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, nc, st);
+        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, nc, st, a.fused, d_bias);
     }
     return launch_status();
 }

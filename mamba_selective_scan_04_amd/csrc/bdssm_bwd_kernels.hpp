@@ -45,11 +45,14 @@ namespace bdssm_dev {
 // grid = (ceil(D/64), chunks launched, batch), block = 64; chunk c = c_first +
 // blockIdx.y.  L divides 16 and chunks are whole 16-token groups, so block
 // ends sit at chunk-local rows p with (p + 1) % L == 0 (masks and shifts).
-template <typename Tin, int L>
+// Fusions: dt is formed as step_size<kDt>(dt stream, dt_bias) and, with the
+// gate z (may be null), dy enters as dy silu(z), as in the forward.
+template <typename Tin, int L, int kDt = kDtPlain>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(6))) void adjoint_chunk_kernel(
     const Tin *__restrict__ dt, const Tin *__restrict__ dy, const Tin *__restrict__ Cm,
     const float *__restrict__ A, const float *__restrict__ dbounds, float *__restrict__ qout,
-    float *__restrict__ sout, int64_t T, int D, int64_t Tc, int n_chunks, int c_first)
+    float *__restrict__ sout, int64_t T, int D, int64_t Tc, int n_chunks, int c_first,
+    const float *__restrict__ dt_bias, const Tin *__restrict__ z)
 {
     static_assert(kGroup % L == 0, "block length must divide the token group");
     constexpr int U = 4;
@@ -81,6 +84,9 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(6))) void
     const int64_t first = (int64_t)b * T + t_begin;
     const Rows<Tin> ds(dt + first * D, len, D, d);
     const Rows<Tin> ys(dy + first * D, len, D, d);
+    const bool gate = z != nullptr;
+    const Rows<Tin> zs((gate ? z : dy) + first * D, len, D, d);
+    const float bias = (kDt != kDtPlain && dt_bias != nullptr) ? dt_bias[d] : 0.f;
     const Tin *cs = Cm + first * kStates;
 
     auto consume = [&](const Tin *dr, const Tin *yr, int k0, int count) {
@@ -98,8 +104,9 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(6))) void
                         q[4 * k + 2] += v.z; q[4 * k + 3] += v.w;
                     }
                 }
-                const float dl = widen(dr[i]);
-                const float gy = live ? widen(yr[i]) : 0.f;
+                const float dl = step_size<kDt>(widen(dr[i]), bias);
+                float gy = live ? widen(yr[i]) : 0.f;
+                if (gate) gy *= silu_f(widen(zs.load(p)));
                 S += dl;
                 const Tin *crow = cs + (int64_t)p * kStates;
 #pragma unroll
@@ -542,30 +549,59 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 // rows (shared by the workgroup, each wave loads a quarter) are DMA'd into
 // LDS one group ahead and widened to fp32 in place by the lane that loaded
 // them.  Arguments and the other partial outputs as in bwd_wave_kernel.
+//
+// kFuse (the gradients of the forward's fusions, BwdFuse): the dt rows are
+// turned into the step size of the forward (step_size<dt_mode> with dt_bias)
+// as they are widened; with the gate z (staged as a fourth row stream), dy
+// becomes dy silu(z), the gradient of the ungated output, and the z row holds
+// dy silu'(z).  Pass B also forms y_pre = sum_n C (hf + hr) (a third dt / x
+// transpose quantity; + Dskip x at the flush), and the flush stores
+// dz = dy silu'(z) y_pre.  The dt stream's gradient is the step size's
+// gradient times softplus'(v) = s(v) (s the logistic function), taken from the
+// step size itself as s(v) = 1 - exp(-softplus(v)); its sums over the chunk's
+// tokens go to part_bias [batch, chunks, D] for the gradient of dt_bias.
 // grid = (ceil(D/32), chunks, batch), block = 256.
 constexpr int kPairChannels = 32;     // channels per bwd_pair_kernel workgroup
 
-template <typename Tin, int L, bool kBlockInit>
+template <typename Tin> struct BwdFuse {
+    const float *dt_bias;   // [D] or null
+    int dt_mode;            // kDtPlain / kDtBias / kDtSoftplus
+    const Tin *z;           // gate [batch, T, D] or null
+    Tin *dz;                // [batch, T, D], written when z is given
+    float *part_bias;       // [batch, chunks, D] or null
+};
+
+// The logistic function of v from softplus(v) = sp: 1 - exp(-sp), with the
+// series sp - sp^2/2 + sp^3/6 where the subtraction would cancel (sp < 1/32).
+__device__ __forceinline__ float sigmoid_from_softplus(float sp) {
+    if (sp < 0.03125f) return sp * (1.f - sp * (0.5f - sp * (1.f / 6.f)));
+    return 1.f - fast_exp2(-sp * kLog2e);
+}
+
+template <typename Tin, int L, bool kBlockInit, bool kFuse = false>
 __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) void bwd_pair_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const Tin *__restrict__ Cm, const Tin *__restrict__ dy, const float *__restrict__ A,
     const float *__restrict__ Dskip, const float *__restrict__ h_start, const float *qin,
     int64_t qin_bs, int64_t qin_cs, const float *__restrict__ dbounds, Tin *__restrict__ dx,
     Tin *__restrict__ ddt, float *__restrict__ part_bc, float *__restrict__ part_a,
-    float *__restrict__ part_d, float *__restrict__ dh0, int64_t T, int D, int64_t Tc)
+    float *__restrict__ part_d, float *__restrict__ dh0, int64_t T, int D, int64_t Tc,
+    BwdFuse<Tin> fz)
 {
     constexpr int CW = 8;                     // channels per wave
     constexpr int ES = sizeof(Tin);
     constexpr int G = kGroup;                 // 16 tokens per group
+    constexpr int NSB = kFuse ? 4 : 3;        // row streams: x, dt, dy (, z)
+    constexpr int NQ = kFuse ? 3 : 2;         // transposed per-token sums: dt, x (, y_pre)
     static_assert(G % L == 0, "block length must divide the token group");
     // Double buffers as distinct arrays (A / B), so that the compiler can tell
     // the loads in flight into one buffer from the reads of the other and
-    // does not wait for them: [wave][stream x, dt, dy][token][channel] and
-    // [B, C][token][state]
-    __shared__ __attribute__((aligned(16))) uint32_t xdA[4][3][G][CW], xdB[4][3][G][CW];
+    // does not wait for them: [wave][stream x, dt, dy (, z)][token][channel]
+    // and [B, C][token][state]
+    __shared__ __attribute__((aligned(16))) uint32_t xdA[4][NSB][G][CW], xdB[4][NSB][G][CW];
     __shared__ __attribute__((aligned(16))) uint32_t bcA[2][G][kStates], bcB[2][G][kStates];
     __shared__ __attribute__((aligned(16))) float tb[4][2 * kStates][CW];   // dB / dC transpose, one token
-    __shared__ __attribute__((aligned(16))) float td[4][4][2][CW][CW];      // dt / x transpose, 4 tokens
+    __shared__ __attribute__((aligned(16))) float td[4][4][NQ][CW][CW];     // per-token sums, 4 tokens
     __shared__ __attribute__((aligned(16))) float redA[4][G * 2 * kStates], redB[4][G * 2 * kStates];
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -626,6 +662,11 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
     const bool ld_live = d_w0 + ld_col < D;
     const int ld_ch = ld_live ? d_w0 + ld_col : D - 1;
     const int bc_tok = 4 * w + (lane >> 4), bc_col = lane & 15;
+    const bool gate = kFuse && fz.z != nullptr;
+    const bool sp_mode = kFuse && fz.dt_mode == kDtSoftplus;
+    const float ld_bias = (kFuse && fz.dt_bias != nullptr) ? fz.dt_bias[ld_ch] : 0.f;
+    const Rows<Tin> zs((gate ? fz.z : dy) + first * D, len, D, 0);
+    float bias_acc = 0.f;                     // this lane's share of the dt-stream gradient sum
 
     // dt and dy of tokens past the chunk end and of channels past D are read
     // at an offset beyond the buffer's range, which returns zero: such tokens
@@ -639,6 +680,9 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
             load_to_lds<ES>(xs.rsrc, &xd[w][0][8 * j][0], ld_ch * ES + k * xs.pitch, 0);
             load_to_lds<ES>(ds.rsrc, &xd[w][1][8 * j][0], zoff, 0);
             load_to_lds<ES>(ys.rsrc, &xd[w][2][8 * j][0], zoff, 0);
+            if constexpr (kFuse) {
+                if (gate) load_to_lds<ES>(zs.rsrc, &xd[w][NSB - 1][8 * j][0], zoff, 0);
+            }
         }
         const int kb = (k0 + bc_tok < len) ? k0 + bc_tok : len - 1;
         load_to_lds<ES>(brs, &bc[0][4 * w][0], (kb * kStates + bc_col) * ES, 0);
@@ -650,9 +694,10 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
         __builtin_amdgcn_s_waitcnt(0x0F70);
         if constexpr (ES == 2) {
 #pragma unroll
-            for (int s = 0; s < 3; ++s)
+            for (int s = 0; s < NSB; ++s)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
+                    if (s == 3 && !gate) continue;
                     uint32_t &v = (&xd[w][s][8 * j][0])[lane];
                     v <<= 16;
                 }
@@ -660,6 +705,26 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
             for (int s = 0; s < 2; ++s) {
                 uint32_t &v = (&bc[s][4 * w][0])[lane];
                 v <<= 16;
+            }
+        }
+        if constexpr (kFuse) {
+            // the step size of the forward, and the gate's two factors of dy
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                uint32_t &dv = (&xd[w][1][8 * j][0])[lane];
+                const float raw = __uint_as_float(dv);
+                float dl = raw;
+                if (fz.dt_mode == kDtSoftplus) dl = step_size<kDtSoftplus>(raw, ld_bias);
+                else if (fz.dt_mode == kDtBias) dl = step_size<kDtBias>(raw, ld_bias);
+                dv = __float_as_uint(dl);
+                if (gate) {
+                    uint32_t &yv = (&xd[w][2][8 * j][0])[lane];
+                    uint32_t &zv = (&xd[w][3][8 * j][0])[lane];
+                    const float zf = __uint_as_float(zv), gy = __uint_as_float(yv);
+                    const float sg = __builtin_amdgcn_rcpf(1.f + fast_exp2(-zf * kLog2e));
+                    yv = __float_as_uint(gy * (zf * sg));                         // dy silu(z)
+                    zv = __float_as_uint(gy * (sg * __builtin_fmaf(zf, 1.f - sg, 1.f)));   // dy silu'(z)
+                }
             }
         }
     };
@@ -754,6 +819,22 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
                 vc[j] = gy * (hf_t + hr[j]);          // dC
             }
             if (g == 0) dD_acc = __builtin_fmaf(gy, xv, dD_acc);
+            if constexpr (kFuse) {
+                // y_pre's share of the lane's two states: C (hf + hr) = C dC / gy
+                // is formed from hf_t + hr_t directly (gy may be zero)
+                if (gate) {
+                    float yp = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const float hf_t = (i == G - 1) ? hf[j]
+                                           : (kBlockInit && (i + 1) % L == 0)
+                                                 ? __builtin_fmaf(fast_exp2(dl * a2[j]), hp_s[i][j], dxv * bb[j])
+                                                 : hp_s[i + 1][j];
+                        yp = __builtin_fmaf(cc[j], hf_t + hr[j], yp);
+                    }
+                    td[w][i & 3][2][cl][g] = yp;
+                }
+            }
             if constexpr (kBlockInit) {
                 if (i % L == 0 && dh0 != nullptr && i < nvalid && live)
                     *reinterpret_cast<float2 *>(dh0 + (((int64_t)b * (nbl + 1) + (t_begin + k0 + i) / L) * D + d) * kStates + s0) =
@@ -781,8 +862,30 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
                 const int it = i + o_tok;
                 if (o_live && it < nvalid) {
                     Tin *dst = (o_q ? dxw : dtw) + (int64_t)(k0 + it) * D + d_w0 + o_ch;
-                    if (o_q) tot = __builtin_fmaf(f32(xd[w][2][it][o_ch]), o_dsk, tot);
+                    if (o_q) {
+                        tot = __builtin_fmaf(f32(xd[w][2][it][o_ch]), o_dsk, tot);
+                    } else if constexpr (kFuse) {
+                        // the dt stream's gradient: through softplus when it is used
+                        if (sp_mode) tot *= sigmoid_from_softplus(f32(xd[w][1][it][o_ch]));
+                        bias_acc += tot;
+                    }
                     *dst = narrow<Tin>(tot);
+                }
+                if constexpr (kFuse) {
+                    // dz = dy silu'(z) (y_pre + Dskip x): lanes 0..31 take token
+                    // lane / 8 of the 4 and channel lane % 8
+                    if (gate && lane < 32) {
+                        const int tz = lane >> 3;
+                        const float4 r0 = *reinterpret_cast<const float4 *>(&td[w][tz][2][o_ch][0]);
+                        const float4 r1 = *reinterpret_cast<const float4 *>(&td[w][tz][2][o_ch][4]);
+                        const float yp = ((r0.x + r0.y) + (r0.z + r0.w)) + ((r1.x + r1.y) + (r1.z + r1.w));
+                        const int iz = i + tz;
+                        if (o_live && iz < nvalid) {
+                            const float ypre = __builtin_fmaf(o_dsk, f32(xd[w][0][iz][o_ch]), yp);
+                            fz.dz[first * D + (int64_t)(k0 + iz) * D + d_w0 + o_ch] =
+                                narrow<Tin>(f32(xd[w][3][iz][o_ch]) * ypre);
+                        }
+                    }
                 }
                 asm volatile("" ::: "memory");
             }
@@ -867,6 +970,15 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
         *reinterpret_cast<float2 *>(part_a + (pc * D + d) * kStates + s0) = make_float2(dA_acc[0], dA_acc[1]);
         if (g == 0) part_d[pc * D + d] = dD_acc;
     }
+    if constexpr (kFuse) {
+        // the dt-stream gradient summed over the chunk: the 4 token lanes of
+        // each output channel (lanes ch, ch + 16, ch + 32, ch + 48), in a
+        // fixed order
+        bias_acc += xchg16(bias_acc);
+        bias_acc += xchg32(bias_acc, lane);
+        if (fz.part_bias != nullptr && lane < CW && o_live)
+            fz.part_bias[((int64_t)b * gridDim.y + c) * D + d_w0 + lane] = bias_acc;
+    }
 }
 
 // dB and dC: sum the channel-block partials in order.  One thread per
@@ -887,11 +999,14 @@ __global__ __launch_bounds__(256) void bc_reduce_kernel(const float *__restrict_
     else dC[bt * kStates + j - kStates] = narrow<Tin>(s);
 }
 
-// dA [D,16] and dDskip [D]: sum the (batch, chunk) partials in order.
+// dA [D,16], dDskip [D] and (when part_bias is given) the dt_bias gradient
+// [D]: sum the (batch, chunk) partials in order.
 __global__ __launch_bounds__(256) void param_reduce_kernel(const float *__restrict__ part_a,
                                                            const float *__restrict__ part_d,
                                                            float *__restrict__ dA, float *__restrict__ dDskip,
-                                                           int D, int n_parts)
+                                                           int D, int n_parts,
+                                                           const float *__restrict__ part_bias,
+                                                           float *__restrict__ d_bias)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t na = (int64_t)D * kStates;
@@ -904,6 +1019,11 @@ __global__ __launch_bounds__(256) void param_reduce_kernel(const float *__restri
         float s = 0.f;
         for (int k = 0; k < n_parts; ++k) s += part_d[(int64_t)k * D + dd];
         dDskip[dd] = s;
+    } else if (i < na + 2 * D && part_bias != nullptr && d_bias != nullptr) {
+        const int64_t dd = i - na - D;
+        float s = 0.f;
+        for (int k = 0; k < n_parts; ++k) s += part_bias[(int64_t)k * D + dd];
+        d_bias[dd] = s;
     }
 }
 

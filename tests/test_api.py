@@ -28,7 +28,7 @@ def test_exports_match_header():
 
 
 def test_version_and_status_strings():
-    assert m.version() == 10300
+    assert m.version() == 10400
     for code in range(-7, 1):
         assert m.status_str(code) not in ("", "unknown status")
     assert m.status_str(-99) == "unknown status"
@@ -164,10 +164,12 @@ def test_binding_rejects_cpu_tensors():
 def train_bwd(s, T, x=FAKE, dt=FAKE + 0x1000, Bm=FAKE + 0x2000, C=FAKE + 0x3000, A=FAKE + 0x4000,
               Ds=FAKE + 0x5000, hb=FAKE + 0x6000, dy=FAKE + 0x7000, dbnd=None, dx=FAKE + 0x8000,
               ddt=FAKE + 0x9000, dB=FAKE + 0xA000, dC=FAKE + 0xB000, dA=FAKE + 0xC000,
-              dD=FAKE + 0xD000, dh=None, ws=None, ws_bytes=0):
+              dD=FAKE + 0xD000, dh=None, ws=None, ws_bytes=0, fusion=None, grads=None):
     return lib().bdssm_train_scan_bwd(ctypes.byref(s), T, P(x), P(dt), P(Bm), P(C), P(A), P(Ds),
                                       P(hb), P(dy), P(dbnd), P(dx), P(ddt), P(dB), P(dC), P(dA),
-                                      P(dD), P(dh), P(ws), ws_bytes, None)
+                                      P(dD), P(dh), P(ws), ws_bytes,
+                                      None if fusion is None else ctypes.byref(fusion),
+                                      None if grads is None else ctypes.byref(grads), None)
 
 
 def test_backward_argument_errors():
@@ -190,8 +192,30 @@ def test_backward_argument_errors():
     assert train_bwd(s, 16, ws=FAKE + 0x100000, ws_bytes=need - 1) == -5
     rc = lib().bdssm_train_scan_blocks_bwd(ctypes.byref(s), 16, *[P(FAKE + k * 0x1000) for k in range(6)],
                                            P(None), P(FAKE + 0x7000), *[P(FAKE + k * 0x1000) for k in range(8, 14)],
-                                           P(None), P(None), 0, None)
+                                           P(None), P(None), 0, None, None, None)
     assert rc == -1                                    # h0_blocks required
+
+
+def test_fused_backward_argument_errors():
+    s = shape(D=8)
+    Fz, G = B.Fusion, B.FusionGrads
+    bias, z = FAKE + 0x20000, FAKE + 0x21000
+    assert train_bwd(s, 16, fusion=Fz(None, 0, None, FAKE + 0x22000)) == -2   # no reverse operands
+    assert train_bwd(s, 16, fusion=Fz(None, 0, z)) == -1                      # gate without dz
+    assert train_bwd(s, 16, fusion=Fz(None, 0, z), grads=G(None, None)) == -1
+    assert train_bwd(s, 16, fusion=Fz(None, 0, z), grads=G(MIS, None)) == -4
+    assert train_bwd(s, 16, fusion=Fz(MIS, 1, None)) == -4                    # misaligned bias
+    assert train_bwd(s, 16, fusion=Fz(None, 0, z), grads=G(z, None)) == -7    # dz on top of z
+    assert train_bwd(s, 16, fusion=Fz(None, 0, z), grads=G(FAKE, None)) == -7  # dz on top of x
+    assert train_bwd(s, 16, fusion=Fz(None, 0, z),
+                     grads=G(FAKE + 0x8000, None)) == -7                     # dz on top of dx
+    assert train_bwd(s, 16, fusion=Fz(bias, 1, None),
+                     grads=G(None, FAKE + 0xC000)) == -7                     # d_dt_bias on dA
+    assert train_bwd(s, 16, fusion=Fz(bias, 1, None), grads=G(None, bias)) == -7
+    assert train_bwd(s, 16, fusion=Fz(None, 0, z), grads=G(FAKE + 0x23000, None),
+                     dx=z) == -7                                             # dx on top of z
+    # valid fused arguments reach the workspace check
+    assert train_bwd(s, 16, fusion=Fz(bias, 1, z), grads=G(FAKE + 0x23000, FAKE + 0x24000)) == -5
 
 
 def test_backward_workspace_sizes():
