@@ -687,7 +687,8 @@ int64_t bwd_block_channels(int64_t L, bool fused = false) {
 }
 
 // workgroups of the chosen kernel resident at once: bwd_pair_kernel fits
-// three per CU (168 registers, 44 KB LDS), bwd_wave_kernel two
+// three per CU (168 registers, 44 KB LDS; 48 KB with the fused streams),
+// bwd_wave_kernel two
 int64_t bwd_block_capacity(int64_t L, bool fused = false) {
     return bwd_use_wave(L, fused) ? kCoarseGroups : 3 * 256;
 }

@@ -554,12 +554,16 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 // turned into the step size of the forward (step_size<dt_mode> with dt_bias)
 // as they are widened; with the gate z (staged as a fourth row stream), dy
 // becomes dy silu(z), the gradient of the ungated output, and the z row holds
-// dy silu'(z).  Pass B also forms y_pre = sum_n C (hf + hr) (a third dt / x
-// transpose quantity; + Dskip x at the flush), and the flush stores
-// dz = dy silu'(z) y_pre.  The dt stream's gradient is the step size's
-// gradient times softplus'(v) = s(v) (s the logistic function), taken from the
-// step size itself as s(v) = 1 - exp(-softplus(v)); its sums over the chunk's
-// tokens go to part_bias [batch, chunks, D] for the gradient of dt_bias.
+// dy silu'(z).  Pass B also forms y_pre = sum_n C (hf + hr) + Dskip x of each
+// token (summed over the channel's 8 lanes by DPP) and parks it in the
+// token's x slot, and the flush parks the dt partial total in the dy slot
+// (pass B no longer reads either).  After pass B, when the group's state
+// arrays are dead, an epilogue turns the parked values into the dt stream's
+// gradient (the step size's gradient times softplus'(v) = s(v), s the
+// logistic function, taken from the step size as s(v) = 1 - exp(-softplus(v)))
+// and dz = dy silu'(z) y_pre, with masked buffer stores; the dt-stream
+// gradient's sums over the chunk's tokens go to part_bias [batch, chunks, D]
+// for the gradient of dt_bias.  (Done inside pass B, the same work spills.)
 // grid = (ceil(D/32), chunks, batch), block = 256.
 constexpr int kPairChannels = 32;     // channels per bwd_pair_kernel workgroup
 
@@ -592,7 +596,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
     constexpr int ES = sizeof(Tin);
     constexpr int G = kGroup;                 // 16 tokens per group
     constexpr int NSB = kFuse ? 4 : 3;        // row streams: x, dt, dy (, z)
-    constexpr int NQ = kFuse ? 3 : 2;         // transposed per-token sums: dt, x (, y_pre)
+    constexpr int NQ = 2;                     // transposed per-token sums: dt, x
     static_assert(G % L == 0, "block length must divide the token group");
     // Double buffers as distinct arrays (A / B), so that the compiler can tell
     // the loads in flight into one buffer from the reads of the other and
@@ -667,6 +671,10 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
     const float ld_bias = (kFuse && fz.dt_bias != nullptr) ? fz.dt_bias[ld_ch] : 0.f;
     const Rows<Tin> zs((gate ? fz.z : dy) + first * D, len, D, 0);
     float bias_acc = 0.f;                     // this lane's share of the dt-stream gradient sum
+    const float dsk = kFuse ? Dskip[d] : 0.f;
+    // the fused epilogue's outputs (no gate: an empty range, every store dropped)
+    const Rows<Tin> dts(ddt + first * D, len, D, 0);
+    const Rows<Tin> dzs(gate ? fz.dz + first * D : ddt, gate ? len : 0, D, 0);
 
     // dt and dy of tokens past the chunk end and of channels past D are read
     // at an offset beyond the buffer's range, which returns zero: such tokens
@@ -795,7 +803,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
             const float dxv = dl * xv;
             const float2 bv = bcv(0, i), cv = bcv(1, i);
             const float bb[2] = {bv.x, bv.y}, cc[2] = {cv.x, cv.y};
-            float s1 = 0.f, s2 = 0.f, vb[2], vc[2];
+            float s1 = 0.f, s2 = 0.f, vb[2], vc[2], yp = 0.f;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const float a = fast_exp2(dl * a2[j]);   // formed again: keeps the kernel at 3 waves per SIMD
@@ -817,23 +825,17 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
                                                                       : hp_s[i + 1][j];
                 vb[j] = du * dxv;                     // dB
                 vc[j] = gy * (hf_t + hr[j]);          // dC
+                if constexpr (kFuse) yp = __builtin_fmaf(cc[j], hf_t + hr[j], yp);
             }
             if (g == 0) dD_acc = __builtin_fmaf(gy, xv, dD_acc);
             if constexpr (kFuse) {
-                // y_pre's share of the lane's two states: C (hf + hr) = C dC / gy
-                // is formed from hf_t + hr_t directly (gy may be zero)
-                if (gate) {
-                    float yp = 0.f;
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const float hf_t = (i == G - 1) ? hf[j]
-                                           : (kBlockInit && (i + 1) % L == 0)
-                                                 ? __builtin_fmaf(fast_exp2(dl * a2[j]), hp_s[i][j], dxv * bb[j])
-                                                 : hp_s[i + 1][j];
-                        yp = __builtin_fmaf(cc[j], hf_t + hr[j], yp);
-                    }
-                    td[w][i & 3][2][cl][g] = yp;
-                }
+                // y_pre of the token: the lane's C (hf + hr) summed over the
+                // channel's 8 state pairs (lanes 8 cl .. 8 cl + 7), + Dskip x,
+                // into the token's x slot (pass B is done with it)
+                yp += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(yp), 0xB1, 0xF, 0xF, false));
+                yp += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(yp), 0x4E, 0xF, 0xF, false));
+                yp += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(yp), 0x141, 0xF, 0xF, false));
+                xd[w][0][i][cl] = __float_as_uint(__builtin_fmaf(dsk, xv, yp));
             }
             if constexpr (kBlockInit) {
                 if (i % L == 0 && dh0 != nullptr && i < nvalid && live)
@@ -860,34 +862,44 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
                 const float4 p1 = *reinterpret_cast<const float4 *>(&td[w][o_tok][o_q][o_ch][4]);
                 float tot = ((p0.x + p0.y) + (p0.z + p0.w)) + ((p1.x + p1.y) + (p1.z + p1.w));
                 const int it = i + o_tok;
-                if (o_live && it < nvalid) {
-                    Tin *dst = (o_q ? dxw : dtw) + (int64_t)(k0 + it) * D + d_w0 + o_ch;
-                    if (o_q) {
-                        tot = __builtin_fmaf(f32(xd[w][2][it][o_ch]), o_dsk, tot);
-                    } else if constexpr (kFuse) {
-                        // the dt stream's gradient: through softplus when it is used
-                        if (sp_mode) tot *= sigmoid_from_softplus(f32(xd[w][1][it][o_ch]));
-                        bias_acc += tot;
-                    }
-                    *dst = narrow<Tin>(tot);
-                }
                 if constexpr (kFuse) {
-                    // dz = dy silu'(z) (y_pre + Dskip x): lanes 0..31 take token
-                    // lane / 8 of the 4 and channel lane % 8
-                    if (gate && lane < 32) {
-                        const int tz = lane >> 3;
-                        const float4 r0 = *reinterpret_cast<const float4 *>(&td[w][tz][2][o_ch][0]);
-                        const float4 r1 = *reinterpret_cast<const float4 *>(&td[w][tz][2][o_ch][4]);
-                        const float yp = ((r0.x + r0.y) + (r0.z + r0.w)) + ((r1.x + r1.y) + (r1.z + r1.w));
-                        const int iz = i + tz;
-                        if (o_live && iz < nvalid) {
-                            const float ypre = __builtin_fmaf(o_dsk, f32(xd[w][0][iz][o_ch]), yp);
-                            fz.dz[first * D + (int64_t)(k0 + iz) * D + d_w0 + o_ch] =
-                                narrow<Tin>(f32(xd[w][3][iz][o_ch]) * ypre);
-                        }
+                    // dx is final here; the dt-stream gradient before the
+                    // softplus factor goes to the token's dy slot (read
+                    // first by the dx lanes) for the group's epilogue
+                    const float gyv = f32(xd[w][2][it][o_ch]);
+                    if (o_q) {
+                        tot = __builtin_fmaf(gyv, o_dsk, tot);
+                        if (o_live && it < nvalid) dxw[(int64_t)(k0 + it) * D + d_w0 + o_ch] = narrow<Tin>(tot);
+                    }
+                    asm volatile("" ::: "memory");
+                    if (!o_q) xd[w][2][it][o_ch] = __float_as_uint(tot);
+                } else {
+                    if (o_live && it < nvalid) {
+                        Tin *dst = (o_q ? dxw : dtw) + (int64_t)(k0 + it) * D + d_w0 + o_ch;
+                        if (o_q) tot = __builtin_fmaf(f32(xd[w][2][it][o_ch]), o_dsk, tot);
+                        *dst = narrow<Tin>(tot);
                     }
                 }
                 asm volatile("" ::: "memory");
+            }
+        }
+        if constexpr (kFuse) {
+            // epilogue of the group: lane (tokens l / 8 and l / 8 + 8, channel
+            // l % 8) applies softplus'(v) = s(v) to the dt-stream gradient,
+            // adds it to the bias sum and stores it, and stores
+            // dz = dy silu'(z) y_pre
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int t = (lane >> 3) + 8 * h;
+                const bool ok = o_live && t < nvalid;
+                // stores of dead channels and tokens past the group go to an
+                // offset beyond the buffer's range, which drops them
+                const int32_t off = ok ? (k0 + t) * dts.pitch + (d_w0 + o_ch) * ES : kOutOfRange;
+                float gdt = f32(xd[w][2][t][o_ch]);
+                if (sp_mode) gdt *= sigmoid_from_softplus(f32(xd[w][1][t][o_ch]));
+                bias_acc += ok ? gdt : 0.f;
+                dts.store_at(off, narrow<Tin>(gdt));
+                dzs.store_at(off, narrow<Tin>(f32(xd[w][3][t][o_ch]) * f32(xd[w][0][t][o_ch])));
             }
         }
     };
@@ -974,6 +986,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
         // the dt-stream gradient summed over the chunk: the 4 token lanes of
         // each output channel (lanes ch, ch + 16, ch + 32, ch + 48), in a
         // fixed order
+        bias_acc += xchg8(bias_acc);
         bias_acc += xchg16(bias_acc);
         bias_acc += xchg32(bias_acc, lane);
         if (fz.part_bias != nullptr && lane < CW && o_live)
