@@ -482,7 +482,7 @@ void launch_carry(bool rev, const float *agg_h, const float *agg_s, const float 
                            h_final, (int)batch, (int)D, (int)N, n_chunks, n_agg, c_low);
 }
 
-template <typename Tin, int L, bool kInit, bool kFuse>
+template <typename Tin, int L, bool kInit, int kFuse>
 void launch_bidir_k(dim3 g, const void *x, const void *dt, const void *B, const void *C,
                     const float *A, const float *Dskip, const float *hin, int64_t hin_bs,
                     int64_t hin_cs, void *y, float *bounds, float *hout, int64_t T, int64_t D,
@@ -499,17 +499,22 @@ void launch_bidir_L(const void *x, const void *dt, const void *B, const void *C,
                     float *bounds, float *hout, int64_t batch, int64_t T, int64_t D, int64_t Tc,
                     int n_chunks, const float *h0_blocks, const Fuse &f, hipStream_t st) {
     const dim3 g = grid3(D, n_chunks, batch);
+    // kernel variant: 0 plain, 1 fused step size / gate, 2 also separate
+    // reverse operands
+    const int fv = f.dt_r != nullptr ? 2 : f.any() ? 1 : 0;
+#define BDSSM_BIDIR(INIT, FV)                                                                       \
+    launch_bidir_k<Tin, L, INIT, FV>(g, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, T, D, \
+                                     Tc, h0_blocks, f, st)
     if (h0_blocks != nullptr) {
-        if (f.any())
-            launch_bidir_k<Tin, L, true, true>(g, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, T, D, Tc, h0_blocks, f, st);
-        else
-            launch_bidir_k<Tin, L, true, false>(g, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, T, D, Tc, h0_blocks, f, st);
+        if (fv == 2) BDSSM_BIDIR(true, 2);
+        else if (fv == 1) BDSSM_BIDIR(true, 1);
+        else BDSSM_BIDIR(true, 0);
     } else {
-        if (f.any())
-            launch_bidir_k<Tin, L, false, true>(g, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, T, D, Tc, h0_blocks, f, st);
-        else
-            launch_bidir_k<Tin, L, false, false>(g, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, T, D, Tc, h0_blocks, f, st);
+        if (fv == 2) BDSSM_BIDIR(false, 2);
+        else if (fv == 1) BDSSM_BIDIR(false, 1);
+        else BDSSM_BIDIR(false, 0);
     }
+#undef BDSSM_BIDIR
 }
 
 template <typename Tin, int kN, bool kInit, int kDt>

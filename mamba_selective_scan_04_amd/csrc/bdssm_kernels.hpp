@@ -407,14 +407,16 @@ __global__ __launch_bounds__(256) void carry_kernel(
 // hout (optional): forward state after token T-1 (written by the last chunk;
 // may alias hin when there is a single chunk: each lane reads its own states
 // before it writes them).
-// kFuse (optional layer features, FuseArgs): dt is formed from the dt stream as
+// kFuse (optional layer features, FuseArgs; 1: step size and gate, 2: also
+// separate reverse operands, a variant of its own so that the others do not
+// carry its registers and LDS): dt is formed from the dt stream as
 // step_size<dt_mode> with dt_bias (each lane transforms the 4 dt values it
 // loaded, in LDS, once per token and channel); when z is given the output is
 // multiplied by silu(z) (z rows are loaded with x and dt); when dt_r is given
 // the reverse scan takes its own operands (dt_r, B_r, C_r rows staged beside
 // the forward ones, decays exp2(dt_r A_r') computed in the reverse pass).
 // grid = (ceil(D/64), chunks, batch), block = 256 (4 independent waves).
-template <typename Tin, int L, bool kBlockInit, bool kFuse = false>
+template <typename Tin, int L, bool kBlockInit, int kFuse = 0>
 __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) void bidir_wave_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const Tin *__restrict__ Cm, const float *__restrict__ A, const float *__restrict__ Dskip,
@@ -425,8 +427,9 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
     constexpr int P = 4;                      // states per lane
     constexpr int CW = kWave / P;             // channels per wave (16)
     constexpr int ES = sizeof(Tin);
-    constexpr int NS = kFuse ? 4 : 2;         // token-row streams: x, dt (, z, dt_r)
-    constexpr int NR = kFuse ? 4 : 2;         // per-token rows: B, C (, B_r, C_r)
+    constexpr bool kSep = kFuse == 2;         // separate reverse operands
+    constexpr int NS = kSep ? 4 : kFuse ? 3 : 2;   // token-row streams: x, dt (, z (, dt_r))
+    constexpr int NR = kSep ? 4 : 2;               // per-token rows: B, C (, B_r, C_r)
     static_assert(kGroup % L == 0, "block length must divide the token group");
     // per wave: token rows [stream][4 loads][64], raw B/C rows [row][4 loads][64]
     // (both double buffered: the next group's loads are in flight), and fp32
@@ -484,7 +487,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
     const int ld_tok = lane >> 4, ld_col = lane & 15;
     const int ld_ch = (d_w0 + ld_col < D) ? d_w0 + ld_col : D - 1;
     const bool gate = kFuse && fz.z != nullptr;
-    const bool sep = kFuse && fz.dt_r != nullptr;
+    const bool sep = kSep && fz.dt_r != nullptr;
     const Rows<Tin> zs((gate ? fz.z : x) + first * D, len, D, 0);
     const Rows<Tin> rds((sep ? fz.dt_r : x) + first * D, len, D, 0);
     __amdgpu_buffer_rsrc_t rbrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -492,9 +495,9 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
     __amdgpu_buffer_rsrc_t rcrs = __builtin_amdgcn_make_buffer_rsrc(
         uniform_ptr(const_cast<Tin *>((sep ? fz.C_r : Cm) + first * kStates)), 0, uniform(len * kStates * ES), kRawBufferWord3);
     const float ld_bias = (kFuse && fz.dt_bias != nullptr) ? fz.dt_bias[ld_ch] : 0.f;
-    const float ld_bias_r = (kFuse && sep && fz.dt_bias_r != nullptr) ? fz.dt_bias_r[ld_ch] : 0.f;
+    const float ld_bias_r = (kSep && sep && fz.dt_bias_r != nullptr) ? fz.dt_bias_r[ld_ch] : 0.f;
     float a2r[P] = {0.f, 0.f, 0.f, 0.f};
-    if (sep) {
+    if (kSep && sep) {
         const float4 av = *reinterpret_cast<const float4 *>(fz.A_r + (int64_t)d * kStates + s0);
         a2r[0] = av.x * kLog2e; a2r[1] = av.y * kLog2e; a2r[2] = av.z * kLog2e; a2r[3] = av.w * kLog2e;
     }
@@ -508,8 +511,10 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
             load_to_lds<ES>(ds.rsrc, &xd[w][1][j][0], ld_ch * ES + k * ds.pitch, 0);
             load_to_lds<ES>(brs, &bcr[w][0][j][0], (k * kStates + ld_col) * ES, 0);
             load_to_lds<ES>(crs, &bcr[w][1][j][0], (k * kStates + ld_col) * ES, 0);
-            if constexpr (kFuse) {
+            if constexpr (kFuse != 0) {
                 if (gate) load_to_lds<ES>(zs.rsrc, &xd[w][2][j][0], ld_ch * ES + k * zs.pitch, 0);
+            }
+            if constexpr (kSep) {
                 if (sep) {
                     load_to_lds<ES>(rds.rsrc, &xd[w][3][j][0], ld_ch * ES + k * rds.pitch, 0);
                     load_to_lds<ES>(rbrs, &bcr[w][2][j][0], (k * kStates + ld_col) * ES, 0);
@@ -535,10 +540,12 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 bcf[w][4 * j + ld_tok][which][ld_col] = elem(bcr[w][which][j][lane]);
-        if constexpr (kFuse) {
+        if constexpr (kFuse != 0) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 xd[w][1][j][lane] = __float_as_uint(form_dt(elem(xd[w][1][j][lane]), ld_bias));
+        }
+        if constexpr (kSep) {
             if (sep) {
 #pragma unroll
                 for (int which = 2; which < 4; ++which)
@@ -552,7 +559,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
         }
     };
     // dt as stored in LDS: raw stream bits, or fp32 after the fusion transform
-    auto dt_elem = [&](uint32_t v) -> float { return kFuse ? __uint_as_float(v) : elem(v); };
+    auto dt_elem = [&](uint32_t v) -> float { return kFuse != 0 ? __uint_as_float(v) : elem(v); };
     // quad reduce-scatter helpers (DPP within groups of 4 lanes)
     auto xor2 = [](float v) {
         return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
@@ -655,7 +662,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
                 ya[i] = acc;
                 if ((i & 3) == 0) asm volatile("" ::: "memory");
             }
-        } else if constexpr (kFuse) {
+        } else if constexpr (kSep) {
             // the reverse scan's own operands: dt_r, B_r, C_r, A_r
 #pragma unroll
             for (int i = kGroup - 1; i >= 0; --i) {
@@ -698,7 +705,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
             const int i = 4 * g + q;
             const float xv = elem(xd[w][0][g][q * CW + cl]);
             float tot = __builtin_fmaf(dsk, xv, r4[q]);
-            if constexpr (kFuse) {
+            if constexpr (kFuse != 0) {
                 if (gate) tot *= silu_f(elem(xd[w][2][g][q * CW + cl]));
             }
             if (live && i < nvalid) ylane[(int64_t)(k0 + i) * D] = narrow<Tin>(tot);
