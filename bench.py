@@ -25,7 +25,8 @@ baseline (reverse over the whole sequence, rescanned every denoising step).
 Training workloads (train_87m, train_350m) time the all-block training scan,
 the two-stream form and the full-sequence scan instead.  --crossover sweeps the
 context length from 8K to 64K tokens and prints generation rates of the
-block-restricted and the full-sequence schemes.
+block-restricted and the full-sequence schemes; --model-loop runs the scan
+inside a random-weight stand-in Mamba stack (context only).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--crossover]
 """
@@ -177,6 +178,11 @@ def main():
     ap.add_argument("--crossover", action="store_true",
                     help="sweep the context length (8K..64K, batch 8, d_inner 1536) and report "
                          "block-restricted against full-sequence generation rates")
+    ap.add_argument("--model-loop", action="store_true",
+                    help="stand-in multi-layer denoising loop (random-weight Mamba stack around "
+                         "the fused scan, no attention): cached block-restricted step against the "
+                         "full-sequence rescan, at 8K and 64K context")
+    ap.add_argument("--layers", type=int, default=24, help="--model-loop: layers of the stack")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -191,6 +197,8 @@ def main():
     m.load()   # fails loudly if the HIP library is missing
     if args.crossover:
         return crossover_main(args, m, synth, torch)
+    if args.model_loop:
+        return model_loop_main(args, m, synth, torch)
     wl = dict(synth.WORKLOADS[args.workload])
     if "seq" in wl:
         return train_main(args, wl, m, synth, torch)
@@ -715,6 +723,180 @@ def crossover_main(args, m, synth, torch):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "crossover sweep, contexts 8192..65536", "batch": batch,
                    "d_inner": D, "d_state": NS, "block": L, "denoising_steps": S},
+        "rows": rows,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def model_loop_main(args, m, synth, torch):
+    """A stand-in for the model around the scan: a stack of random-weight
+    Mamba-1 mixer layers (RMSNorm, in-projection to x and the gate z,
+    x-projection to the low-rank dt and B, C, dt-projection, the fused scan
+    with dt = softplus(dt_raw + bias) and the silu(z) gate, out-projection,
+    residual), batch 8, d_model 768, d_inner 1536, 16 states, dt rank 48.  The
+    projections are plain torch GEMMs; there are no attention layers and no
+    short convolution.  Per denoising step of one 16-token block it times
+      cached: the block's 16 tokens through every layer, each layer's scan a
+              block_step from that layer's cache (plus, per block, the commit
+              pass of the clean tokens, reported apart);
+      full:   context + block through every layer, each scan a full_scan (the
+              full-sequence scheme rescans everything every step).
+    The ratio is a model-level analog for a Mamba-only stack; the pages'
+    figures include attention layers and are quoted only as context."""
+    batch, dm, D, R, L, S = 8, 768, 1536, 48, 16, 16
+    nl = args.layers
+    dtype = torch.bfloat16
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    st = torch.cuda.current_stream()
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+
+    def w(shape, fan_in):
+        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) / math.sqrt(fan_in)).to(dtype)
+
+    layers = []
+    for i in range(nl):
+        A, Dskip = synth.params(D, NS, 900 + i, "default", dev)
+        layers.append(dict(norm=torch.ones(dm, device=dev, dtype=dtype), w_x=w((dm, D), dm),
+                           w_z=w((dm, D), dm), w_p=w((D, R + 2 * NS), D), w_dt=w((R, D), R),
+                           dt_bias=torch.full((D,), math.log(math.expm1(0.05)), device=dev),
+                           A=A, Dskip=Dskip, w_out=w((D, dm), D)))
+
+    def mixer_inputs(lay, X):
+        """[batch, T, d_model] -> the scan's x, dt_raw, B, C, z ([batch, T, .])"""
+        b, T = X.shape[0], X.shape[1]
+        h = X.view(-1, dm)
+        h = (h.float() * torch.rsqrt(h.float().pow(2).mean(-1, keepdim=True) + 1e-5)).to(dtype) * lay["norm"]
+        x = torch.mm(h, lay["w_x"])
+        z = torch.mm(h, lay["w_z"])
+        p = torch.mm(x, lay["w_p"])
+        dt = torch.mm(p[:, :R], lay["w_dt"])
+        Bm = p[:, R:R + NS].contiguous()
+        Cm = p[:, R + NS:].contiguous()
+        return (x.view(b, T, D), dt.view(b, T, D), Bm.view(b, T, NS), Cm.view(b, T, NS), z.view(b, T, D))
+
+    def layer_out(lay, X, y):
+        return X + torch.mm(y.view(-1, D), lay["w_out"]).view(X.shape)
+
+    def cached_step(X, caches):
+        for lay, h in zip(layers, caches):
+            x, dt, Bm, Cm, z = mixer_inputs(lay, X)
+            y = m.block_step(h, x, dt, Bm, Cm, lay["A"], lay["Dskip"], dt_bias=lay["dt_bias"],
+                             dt_softplus=True, z=z)
+            X = layer_out(lay, X, y)
+        return X
+
+    def commit_pass(X, caches):
+        for lay, h in zip(layers, caches):
+            x, dt, Bm, Cm, z = mixer_inputs(lay, X)
+            _, y = m.commit(h, x, dt, Bm, Cm, lay["A"], lay["Dskip"], want_y=True,
+                            dt_bias=lay["dt_bias"], dt_softplus=True, z=z)
+            X = layer_out(lay, X, y)
+        return X
+
+    def full_step(X, ws):
+        for lay in layers:
+            x, dt, Bm, Cm, z = mixer_inputs(lay, X)
+            y = m.full_scan(x, dt, Bm, Cm, lay["A"], lay["Dskip"], ws=ws, dt_bias=lay["dt_bias"],
+                            dt_softplus=True, z=z)
+            X = layer_out(lay, X, y)
+        return X
+
+    def prefill_pass(X, caches, ws):
+        for lay, h in zip(layers, caches):
+            x, dt, Bm, Cm, z = mixer_inputs(lay, X)
+            _, y = m.prefill(x, dt, Bm, Cm, lay["A"], lay["Dskip"], L, h_cache=h, want_y=True, ws=ws,
+                             dt_bias=lay["dt_bias"], dt_softplus=True, z=z)
+            X = layer_out(lay, X, y)
+        return X
+
+    def time_calls(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        a.record(st)
+        for _ in range(reps):
+            fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    rows = []
+    for ctx in (8192, 65536):
+        log("[bench] model loop: ctx %d, %d layers" % (ctx, nl))
+        Tf = ctx + L
+        Xc = torch.randn(batch, ctx, dm, generator=g, device=dev, dtype=torch.float32).to(dtype)
+        Xb = torch.randn(batch, L, dm, generator=g, device=dev, dtype=torch.float32).to(dtype)
+        Xf = torch.randn(batch, Tf, dm, generator=g, device=dev, dtype=torch.float32).to(dtype)
+        caches = [torch.zeros(batch, D, NS, dtype=torch.float32, device=dev) for _ in range(nl)]
+        wsp = torch.empty(max(1, m.workspace_bytes(batch, D, ctx, m.OP_PREFILL, L, NS, dtype)),
+                          dtype=torch.uint8, device=dev)
+        wsf = torch.empty(max(1, m.workspace_bytes(batch, D, Tf, m.OP_FULL, 1, NS, dtype)),
+                          dtype=torch.uint8, device=dev)
+        pf_ms = time_calls(lambda: prefill_pass(Xc, caches, wsp), 1)
+        step_ms = time_calls(lambda: cached_step(Xb, caches), 20)
+        # the cached step replayed from a HIP graph (the launches are the same
+        # every step); kept only if every replay, with eager work between
+        # them, reproduces the eager result bit for bit
+        ref = cached_step(Xb, caches).clone()
+        gr = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(st)
+        with torch.cuda.stream(side):
+            cached_step(Xb, caches)
+        st.wait_stream(side)
+        with torch.cuda.graph(gr):
+            out_g = cached_step(Xb, caches)
+        graph_ok = True
+        for _ in range(3):
+            gr.replay()
+            torch.cuda.synchronize()
+            graph_ok = graph_ok and torch.equal(out_g, ref)
+            cached_step(Xb, caches)
+            torch.cuda.synchronize()
+        step_graph_ms = time_calls(gr.replay, 50) if graph_ok else None
+        del gr, out_g
+        ccaches = [c.clone() for c in caches]
+        commit_ms = time_calls(lambda: commit_pass(Xb, ccaches), 5)
+        full_ms = time_calls(lambda: full_step(Xf, wsf), 2)
+        # the scans alone, for the share of the step they take
+        scan_in = mixer_inputs(layers[0], Xb)
+        scan_ms = nl * time_calls(lambda: m.block_step(caches[0], *scan_in[:4], layers[0]["A"], layers[0]["Dskip"],
+                                                       dt_bias=layers[0]["dt_bias"], dt_softplus=True,
+                                                       z=scan_in[4]), 50)
+        full_in = mixer_inputs(layers[0], Xf)
+        full_scan_ms = nl * time_calls(lambda: m.full_scan(*full_in[:4], layers[0]["A"], layers[0]["Dskip"], ws=wsf,
+                                                           dt_bias=layers[0]["dt_bias"], dt_softplus=True,
+                                                           z=full_in[4]), 2)
+        blk_ms = S * step_ms + commit_ms
+        blk_g_ms = None if step_graph_ms is None else S * step_graph_ms + commit_ms
+        rows.append({"ctx": ctx, "layers": nl, "prefill_ms": pf_ms,
+                     "cached_step_ms": step_ms, "cached_step_graph_ms": step_graph_ms,
+                     "graph_replays_match_eager": graph_ok, "commit_pass_ms": commit_ms,
+                     "cached_block_ms": blk_ms, "cached_block_graph_ms": blk_g_ms,
+                     "full_step_ms": full_ms, "full_block_ms": S * full_ms,
+                     "step_ratio": full_ms / step_ms, "block_ratio": S * full_ms / blk_ms,
+                     "block_ratio_graph": None if blk_g_ms is None else S * full_ms / blk_g_ms,
+                     "scan_share_cached": scan_ms / step_ms,
+                     "scan_share_cached_graph": None if step_graph_ms is None else scan_ms / step_graph_ms,
+                     "scan_share_full": full_scan_ms / full_ms,
+                     "generation_tokens_per_s": batch * L / (blk_ms * 1e-3),
+                     "full_generation_tokens_per_s": batch * L / (S * full_ms * 1e-3)})
+        del Xc, Xf, caches, ccaches, wsp, wsf, full_in
+        torch.cuda.empty_cache()
+    r = rows[-1]
+    line = {
+        "metric": "stand-in model loop: denoising-step time, cached block-restricted vs full-sequence rescan",
+        "value": r["block_ratio"], "unit": "x (full-sequence time / block-restricted time per block)",
+        "n_gpus": 1, "steps": S, "warmup": 1, "ms_per_step": r["cached_step_ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random weights)",
+        "config": {"workload": "random-weight Mamba-1 stack, no attention, eager launches "
+                               "(cached step also from a HIP graph)",
+                   "batch": batch, "d_model": dm, "d_inner": D, "d_state": NS, "dt_rank": R,
+                   "layers": nl, "block": L, "denoising_steps": S},
         "rows": rows,
     }
     print(json.dumps(line), flush=True)
