@@ -555,8 +555,8 @@ def train_main(args, wl, m, synth, torch):
     b.record(st)
     torch.cuda.synchronize()
     two_ms = a.elapsed_time(b) / args.steps
-    # the backward runs 16 states, L | 16, and no separate reverse operands
-    if args.reverse_operands or ns != NS or L not in (1, 2, 4, 8, 16):
+    # the backward takes no separate reverse operands
+    if args.reverse_operands:
         line = train_line(args, batch, D, T, L, dtype, nbytes, slots, ms_per_step, ev_ms,
                           blocks_ms, full_ms, two_ms, None, None, None, torch, ns)
         print(json.dumps(line), flush=True)

@@ -34,7 +34,7 @@ using namespace bdssm_dev;
 
 namespace {
 
-constexpr int kVersion = 10400;   // 1.4.0
+constexpr int kVersion = 10500;   // 1.5.0
 
 // 256 CUs x 4 SIMDs x 8 resident waves (the chunk kernel fits in 64 VGPRs)
 constexpr int64_t kFineWaves = 256 * 4 * 8;
@@ -215,9 +215,10 @@ struct Workspace {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Backward workspace (fp32, 256-byte aligned):
-//   continuous form with several coarse chunks: agg_q [batch, n_fine, D, 16],
-//     agg_s [batch, n_fine, D], q_in [batch, n_fine, D, 16];
-//   both forms: part_bc [batch, ceil(D/32), T, 32], part_a [batch, nc, D, 16],
+//   continuous form with several coarse chunks: agg_q [batch, n_fine, D, N],
+//     agg_s [batch, n_fine, D], q_in [batch, n_fine, D, N];
+//   both forms: part_bc [batch, nblk, T, 2N] (nblk = channel blocks of the
+//     block-local kernel), part_a [batch, nc, D, N],
 //     part_bias [batch, nc, D] (the dt_bias gradient of the fused backward),
 //     part_d [batch, nc, D]   (nc = coarse chunks of the backward pass).
 struct BwdWorkspace {
@@ -226,7 +227,7 @@ struct BwdWorkspace {
 };
 
 BwdWorkspace layout_bwd(void *base, int64_t batch, int64_t D, int64_t T, int64_t n_fine,
-                        int64_t nc, bool carry) {
+                        int64_t nc, bool carry, int64_t N, int64_t nblk) {
     BwdWorkspace w{};
     size_t off = 0;
     auto take = [&](size_t n) -> float * {
@@ -235,14 +236,13 @@ BwdWorkspace layout_bwd(void *base, int64_t batch, int64_t D, int64_t T, int64_t
         return r;
     };
     if (carry) {
-        const size_t nh = (size_t)batch * n_fine * D * kStates * sizeof(float);
+        const size_t nh = (size_t)batch * n_fine * D * N * sizeof(float);
         w.agg_q = take(nh);
         w.agg_s = take((size_t)batch * n_fine * D * sizeof(float));
         w.q_in = take(nh);
     }
-    // sized for the smaller channel block of the two backward kernels
-    w.part_bc = take((size_t)batch * ceil_div(D, kPairChannels) * T * 32 * sizeof(float));
-    w.part_a = take((size_t)batch * nc * D * kStates * sizeof(float));
+    w.part_bc = take((size_t)batch * nblk * T * 2 * N * sizeof(float));
+    w.part_a = take((size_t)batch * nc * D * N * sizeof(float));
     w.part_d = take((size_t)batch * nc * D * sizeof(float));
     w.part_bias = take((size_t)batch * nc * D * sizeof(float));
     w.bytes = off;
@@ -698,15 +698,92 @@ int64_t bwd_block_capacity(int64_t L, bool fused = false) {
     return bwd_use_wave(L, fused) ? kCoarseGroups : 3 * 256;
 }
 
-// chunk plans of the two backward forms, for the chosen kernel's geometry
-Plan bwd_plan(int64_t batch, int64_t D, int64_t T, int64_t L, bool fused = false) {
-    return make_plan(batch, D, T, kBwdPrepassWeight, bwd_block_channels(L, fused),
-                     bwd_block_capacity(L, fused));
+// The general backward path (bwd_general_kernel): block lengths outside the
+// 16-token group's divisors and state counts other than 16.
+bool bwd_general(int64_t L, int64_t N) { return !(wave_block(L) && N == kStates); }
+
+// channels per workgroup of the block-local kernel (the dB / dC partial blocks)
+int64_t bwd_channels(int64_t L, int64_t N, bool fused) {
+    return bwd_general(L, N) ? 4 * kWave / N : bwd_block_channels(L, fused);
 }
-bool bwd_blocks_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t *tc, int64_t *nc,
-                     bool fused = false) {
+
+// chunk plans of the two backward forms, for the chosen kernel's geometry.
+// The general path's chunks are whole blocks (its own adjoint pre-pass and
+// the carry join them), as in the forward's general plan.
+bool bwd_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, bool fused, Plan *p) {
+    if (bwd_general(L, N)) return plan_general(batch, D, T, L, p);
+    *p = make_plan(batch, D, T, kBwdPrepassWeight, bwd_block_channels(L, fused),
+                   bwd_block_capacity(L, fused));
+    return true;
+}
+bool bwd_blocks_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, int64_t *tc,
+                     int64_t *nc, bool fused) {
+    if (bwd_general(L, N)) return blocks_plan(batch, D, T, L, N, tc, nc, bwd_channels(L, N, fused), 3 * 256);
     return blocks_plan(batch, D, T, L, kStates, tc, nc, bwd_block_channels(L, fused),
                        bwd_block_capacity(L, fused));
+}
+
+// dynamic LDS of bwd_general_kernel: hf and pr at every 16-token segment start
+size_t bwd_general_lds(int64_t L) { return (size_t)ceil_div(L, kGroup) * 4 * 2 * kWave * sizeof(float); }
+
+template <typename Tin, int kN, bool kBlockInit>
+void launch_bwd_general_k(const BwdArgs &a, int64_t batch, int64_t T, int64_t D, int64_t L, int64_t Tc,
+                          int nc, hipStream_t st) {
+    const dim3 g((unsigned)ceil_div(D, 4 * kWave / kN), (unsigned)nc, (unsigned)batch);
+    const BwdFuse<Tin> fz{a.dt_bias, a.dt_mode, (const Tin *)a.z, (Tin *)a.dz, a.part_bias};
+    const size_t lds = bwd_general_lds(L);
+    if (a.fused)
+        hipLaunchKernelGGL((bwd_general_kernel<Tin, kN, kBlockInit, true>), g, dim3(4 * kWave), lds, st,
+                           (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
+                           (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
+                           a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0,
+                           T, (int)D, (int)L, Tc, fz);
+    else
+        hipLaunchKernelGGL((bwd_general_kernel<Tin, kN, kBlockInit, false>), g, dim3(4 * kWave), lds, st,
+                           (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
+                           (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
+                           a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0,
+                           T, (int)D, (int)L, Tc, fz);
+}
+
+template <typename Tin, bool kBlockInit>
+void launch_bwd_general(int64_t N, const BwdArgs &a, int64_t batch, int64_t T, int64_t D, int64_t L,
+                        int64_t Tc, int nc, hipStream_t st) {
+    with_states(N, [&](auto kn) {
+        launch_bwd_general_k<Tin, decltype(kn)::value, kBlockInit>(a, batch, T, D, L, Tc, nc, st);
+    });
+}
+
+template <typename Tin, int kN, int kDt>
+void launch_adjoint_general_k(const void *dt, const void *dy, const void *C, const float *A,
+                              const float *dbounds, float *qout, float *sout, int64_t batch, int64_t T,
+                              int64_t D, int64_t L, int64_t Tc, int n_chunks, int c_first, int n_launch,
+                              const float *dt_bias, const void *z, hipStream_t st) {
+    hipLaunchKernelGGL((adjoint_general_kernel<Tin, kN, kDt>),
+                       dim3((unsigned)ceil_div(D, kWave), (unsigned)n_launch, (unsigned)batch), dim3(kWave),
+                       0, st, (const Tin *)dt, (const Tin *)dy, (const Tin *)C, A, dbounds, qout, sout, T,
+                       (int)D, (int)L, Tc, n_chunks, c_first, dt_bias, (const Tin *)z);
+}
+
+// chunk-local adjoints of the general path (chunks c_first .. c_first + n_launch - 1)
+template <typename Tin>
+void launch_adjoint_general(int64_t N, const void *dt, const void *dy, const void *C, const float *A,
+                            const float *dbounds, float *qout, float *sout, int64_t batch, int64_t T,
+                            int64_t D, int64_t L, int64_t Tc, int n_chunks, int c_first, int n_launch,
+                            int dt_mode, const float *dt_bias, const void *z, hipStream_t st) {
+    if (n_launch <= 0) return;
+    with_states(N, [&](auto kn) {
+        constexpr int K = decltype(kn)::value;
+        if (dt_mode == kDtSoftplus)
+            launch_adjoint_general_k<Tin, K, kDtSoftplus>(dt, dy, C, A, dbounds, qout, sout, batch, T, D, L, Tc,
+                                                          n_chunks, c_first, n_launch, dt_bias, z, st);
+        else if (dt_mode == kDtBias)
+            launch_adjoint_general_k<Tin, K, kDtBias>(dt, dy, C, A, dbounds, qout, sout, batch, T, D, L, Tc,
+                                                      n_chunks, c_first, n_launch, dt_bias, z, st);
+        else
+            launch_adjoint_general_k<Tin, K, kDtPlain>(dt, dy, C, A, dbounds, qout, sout, batch, T, D, L, Tc,
+                                                       n_chunks, c_first, n_launch, dt_bias, z, st);
+    });
 }
 
 template <typename Tin, int L, bool kBlockInit>
@@ -750,16 +827,16 @@ void launch_bwd(int64_t L, const BwdArgs &a, int64_t batch, int64_t T, int64_t D
 
 template <typename Tin>
 void launch_bwd_reduce(const BwdWorkspace &w, void *dB, void *dC, float *dA, float *dDskip,
-                       int64_t batch, int64_t T, int64_t D, int64_t L, int64_t nc, hipStream_t st,
-                       bool fused = false, float *d_bias = nullptr) {
-    const int64_t nbc = batch * T * 32;
+                       int64_t batch, int64_t T, int64_t D, int64_t L, int64_t N, int64_t nc,
+                       hipStream_t st, bool fused = false, float *d_bias = nullptr) {
+    const int64_t nbc = batch * T * 2 * N;
     hipLaunchKernelGGL((bc_reduce_kernel<Tin>), dim3((unsigned)ceil_div(nbc, 256)), dim3(256), 0, st,
                        w.part_bc, (Tin *)dB, (Tin *)dC, (int)batch, T,
-                       (int)ceil_div(D, bwd_block_channels(L, fused)));
+                       (int)ceil_div(D, bwd_channels(L, N, fused)), (int)N);
     const bool nb = fused && d_bias != nullptr;
-    hipLaunchKernelGGL(param_reduce_kernel, dim3((unsigned)ceil_div(D * (kStates + (nb ? 2 : 1)), 256)),
+    hipLaunchKernelGGL(param_reduce_kernel, dim3((unsigned)ceil_div(D * (N + (nb ? 2 : 1)), 256)),
                        dim3(256), 0, st, w.part_a, w.part_d, dA, dDskip, (int)D, (int)(batch * nc),
-                       nb ? w.part_bias : nullptr, nb ? d_bias : nullptr);
+                       nb ? w.part_bias : nullptr, nb ? d_bias : nullptr, (int)N);
 }
 
 // Forward state only over T tokens from h_init: h_final <- state after T.
@@ -856,16 +933,16 @@ size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T, int op) {
     if (op < BDSSM_OP_PREFILL || op > BDSSM_OP_BLOCKS_BWD) return (size_t)-1;
     const int64_t batch = shape->batch, D = shape->d_inner;
     if (batch == 0 || D == 0 || T == 0) return 0;
-    if ((op == BDSSM_OP_TRAIN_BWD || op == BDSSM_OP_BLOCKS_BWD) &&
-        (!wave_block(shape->block_len) || shape->d_state != kStates))
-        return (size_t)-1;
+    const int64_t N = shape->d_state, L = shape->block_len;
     // the backward's plan depends on the kernel, which a fusion can change:
     // size for the larger of the two
     if (op == BDSSM_OP_TRAIN_BWD) {
         size_t n = 0;
         for (int fused = 0; fused < 2; ++fused) {
-            const Plan p = bwd_plan(batch, D, T, shape->block_len, fused != 0);
-            const size_t m = layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, p.n_coarse > 1).bytes;
+            Plan p;
+            if (!bwd_plan(batch, D, T, L, N, fused != 0, &p)) return (size_t)-1;
+            const size_t m = layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, p.n_coarse > 1, N,
+                                        ceil_div(D, bwd_channels(L, N, fused != 0))).bytes;
             n = m > n ? m : n;
         }
         return n;
@@ -874,8 +951,9 @@ size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T, int op) {
         size_t n = 0;
         for (int fused = 0; fused < 2; ++fused) {
             int64_t tc, nc;
-            if (!bwd_blocks_plan(batch, D, T, shape->block_len, &tc, &nc, fused != 0)) return (size_t)-1;
-            const size_t m = layout_bwd(nullptr, batch, D, T, 1, nc, false).bytes;
+            if (!bwd_blocks_plan(batch, D, T, L, N, &tc, &nc, fused != 0)) return (size_t)-1;
+            const size_t m = layout_bwd(nullptr, batch, D, T, 1, nc, false, N,
+                                        ceil_div(D, bwd_channels(L, N, fused != 0))).bytes;
             n = m > n ? m : n;
         }
         return n;
@@ -1117,11 +1195,11 @@ int check_bwd(const bdssm_shape *shape, int64_t T, const void *x, const void *dt
     int rc = check_shape(shape);
     if (rc) return rc;
     if (T < 0 || T % shape->block_len != 0) return BDSSM_ERR_SHAPE;
-    // the backward kernels keep a block inside one 16-token group and run 16 states
-    if (!wave_block(shape->block_len) || shape->d_state != kStates) return BDSSM_ERR_SHAPE;
+    // the general path's checkpoints cover blocks up to kMaxLdsBlock tokens
+    if (shape->block_len > kMaxLdsBlock) return BDSSM_ERR_SHAPE;
     rc = check_streams(shape, T, x, dt, B, C, true, A, Dskip, true);
     if (rc) return rc;
-    const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len;
+    const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len, N = shape->d_state;
     if (D > 0 && (dA == nullptr || dDskip == nullptr)) return BDSSM_ERR_NULL;
     const bool work = batch > 0 && D > 0 && T > 0;
     if (work && (!h_states || !dy || !dx || !ddt || !dB || !dC)) return BDSSM_ERR_NULL;
@@ -1129,11 +1207,11 @@ int check_bwd(const bdssm_shape *shape, int64_t T, const void *x, const void *dt
     for (const void *p : ps)
         if (p && !aligned16(p)) return BDSSM_ERR_ALIGN;
     const size_t e = esize(shape);
-    const size_t ntok = (size_t)batch * T * D * e, nbc = (size_t)batch * T * kStates * e;
-    const size_t nbnd = (size_t)batch * (T / L + 1) * D * kStates * 4;
+    const size_t ntok = (size_t)batch * T * D * e, nbc = (size_t)batch * T * N * e;
+    const size_t nbnd = (size_t)batch * (T / L + 1) * D * N * 4;
     const Range outs[] = {{dx, ntok}, {ddt, ntok}, {dB, nbc}, {dC, nbc},
-                          {dA, (size_t)D * kStates * 4}, {dDskip, (size_t)D * 4}, {dh, dh_bytes}};
-    const Range ins[] = {{x, ntok}, {dt, ntok}, {B, nbc}, {C, nbc}, {A, (size_t)D * kStates * 4},
+                          {dA, (size_t)D * N * 4}, {dDskip, (size_t)D * 4}, {dh, dh_bytes}};
+    const Range ins[] = {{x, ntok}, {dt, ntok}, {B, nbc}, {C, nbc}, {A, (size_t)D * N * 4},
                          {Dskip, (size_t)D * 4}, {h_states, nbnd}, {dy, ntok}, {dbounds, nbnd}};
     for (const Range &o : outs) {
         for (const Range &i : ins)
@@ -1145,8 +1223,8 @@ int check_bwd(const bdssm_shape *shape, int64_t T, const void *x, const void *dt
 }
 
 // Zero the parameter gradients (and the start-state gradient) of an empty call.
-int zero_bwd(int64_t D, float *dA, float *dDskip, float *dh, int64_t dh_n, hipStream_t st) {
-    int rc = D > 0 ? copy_or_zero(nullptr, dA, D * kStates, st) : BDSSM_OK;
+int zero_bwd(int64_t D, int64_t N, float *dA, float *dDskip, float *dh, int64_t dh_n, hipStream_t st) {
+    int rc = D > 0 ? copy_or_zero(nullptr, dA, D * N, st) : BDSSM_OK;
     if (!rc && D > 0) rc = copy_or_zero(nullptr, dDskip, D, st);
     if (!rc && dh && dh_n > 0) rc = copy_or_zero(nullptr, dh, dh_n, st);
     return rc;
@@ -1210,80 +1288,93 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
                          void *ws, size_t ws_bytes, const bdssm_fusion *fusion,
                          bdssm_fusion_grads *grads, void *stream) {
     const size_t nstate = shape ? (size_t)(shape->batch > 0 ? shape->batch : 0) *
-                                      (shape->d_inner > 0 ? shape->d_inner : 0) * kStates * 4 : 0;
+                                      (shape->d_inner > 0 ? shape->d_inner : 0) *
+                                      (shape->d_state > 0 ? shape->d_state : 0) * 4 : 0;
     int rc = check_bwd(shape, T, x, dt, B, C, A, Dskip, h_bounds, dy, d_bounds, dx, ddt, dB, dC, dA,
                        dDskip, dh_init, nstate);
     if (rc) return rc;
-    const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len;
+    const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len, N = shape->d_state;
     BwdArgs a{x, dt, B, C, dy, A, Dskip, h_bounds, nullptr, d_bounds, 0, 0, dx, ddt,
               nullptr, nullptr, nullptr, dh_init};
-    {
-        const size_t e = esize(shape);
-        const size_t ntok = (size_t)batch * T * D * e, nbc = (size_t)batch * T * kStates * e;
-        const size_t nbnd = (size_t)batch * (T / L + 1) * D * kStates * 4;
-        rc = resolve_bwd_fusion(fusion, grads, shape, T,
-                                {{x, ntok}, {dt, ntok}, {B, nbc}, {C, nbc}, {dy, ntok}, {h_bounds, nbnd},
-                                 {d_bounds, nbnd}, {A, (size_t)D * kStates * 4}, {Dskip, (size_t)D * 4}},
-                                {{dx, ntok}, {ddt, ntok}, {dB, nbc}, {dC, nbc}, {dA, (size_t)D * kStates * 4},
-                                 {dDskip, (size_t)D * 4}, {dh_init, nstate}, {ws, ws_bytes}},
-                                &a);
-        if (rc) return rc;
-    }
+    const size_t e = esize(shape);
+    const size_t ntok = (size_t)batch * T * D * e, nbc = (size_t)batch * T * N * e;
+    const size_t nbnd = (size_t)batch * (T / L + 1) * D * N * 4;
+    const size_t npar = (size_t)D * N * 4;
+    rc = resolve_bwd_fusion(fusion, grads, shape, T,
+                            {{x, ntok}, {dt, ntok}, {B, nbc}, {C, nbc}, {dy, ntok}, {h_bounds, nbnd},
+                             {d_bounds, nbnd}, {A, npar}, {Dskip, (size_t)D * 4}},
+                            {{dx, ntok}, {ddt, ntok}, {dB, nbc}, {dC, nbc}, {dA, npar},
+                             {dDskip, (size_t)D * 4}, {dh_init, nstate}, {ws, ws_bytes}},
+                            &a);
+    if (rc) return rc;
     float *d_bias = grads ? grads->d_dt_bias : nullptr;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (batch == 0 || D == 0 || T == 0) {
-        rc = zero_bwd(D, dA, dDskip, dh_init, batch * D * kStates, st);
+        rc = zero_bwd(D, N, dA, dDskip, dh_init, batch * D * N, st);
         if (!rc && d_bias && D > 0) rc = copy_or_zero(nullptr, d_bias, D, st);
         if (rc || dh_init == nullptr || d_bounds == nullptr || batch == 0 || D == 0) return rc;
         // T == 0: the only gradient of the start state is its own bound
-        return copy_or_zero(d_bounds, dh_init, batch * D * kStates, st);
+        return copy_or_zero(d_bounds, dh_init, batch * D * N, st);
     }
     if (!aligned16(ws)) return BDSSM_ERR_ALIGN;
-    const Plan p = bwd_plan(batch, D, T, L, a.fused);
+    const bool general = bwd_general(L, N);
+    Plan p;
+    if (!bwd_plan(batch, D, T, L, N, a.fused, &p)) return BDSSM_ERR_SHAPE;
     const bool carry = p.n_coarse > 1;
-    const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, carry);
+    const int64_t nblk = ceil_div(D, bwd_channels(L, N, a.fused));
+    const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, carry, N, nblk);
     if (ws == nullptr || ws_bytes < probe.bytes) return BDSSM_ERR_WORKSPACE;
-    const size_t e = esize(shape);
-    const size_t ntok = (size_t)batch * T * D * e, nbc = (size_t)batch * T * kStates * e;
-    const size_t nbnd = (size_t)batch * (T / L + 1) * D * kStates * 4;
     if (!ws_clear(ws, probe.bytes, {{x, ntok}, {dt, ntok}, {B, nbc}, {C, nbc}, {dy, ntok},
                                     {h_bounds, nbnd}, {d_bounds, nbnd}, {dx, ntok}, {ddt, ntok},
-                                    {dB, nbc}, {dC, nbc}, {dA, (size_t)D * kStates * 4},
-                                    {dDskip, (size_t)D * 4}, {dh_init, nstate},
-                                    {A, (size_t)D * kStates * 4}, {Dskip, (size_t)D * 4}}))
+                                    {dB, nbc}, {dC, nbc}, {dA, npar}, {dDskip, (size_t)D * 4},
+                                    {dh_init, nstate}, {A, npar}, {Dskip, (size_t)D * 4}}))
         return BDSSM_ERR_ALIAS;
-    const BwdWorkspace w = layout_bwd(ws, batch, D, T, p.n_fine, p.n_coarse, carry);
-    const int64_t hs = D * kStates;
+    const BwdWorkspace w = layout_bwd(ws, batch, D, T, p.n_fine, p.n_coarse, carry, N, nblk);
+    const int64_t hs = D * N;
     a.part_bc = w.part_bc;
     a.part_a = w.part_a;
     a.part_d = w.part_d;
     a.part_bias = w.part_bias;
     const int64_t Tc = carry ? p.fine_len * p.per_coarse : p.fine_len * p.n_fine;
+    const bool bf = shape->dtype == BDSSM_BF16;
     if (carry) {
         // adjoint aggregates of the fine chunks right of the first coarse chunk,
         // then the adjoint entering each fine chunk from its right end
-        if (shape->dtype == BDSSM_BF16)
+        const int c_first = p.per_coarse, n_launch = p.n_fine - p.per_coarse;
+        if (general) {
+            if (bf)
+                launch_adjoint_general<uint16_t>(N, dt, dy, C, A, d_bounds, w.agg_q, w.agg_s, batch, T, D, L,
+                                                 p.fine_len, p.n_fine, c_first, n_launch, a.dt_mode, a.dt_bias,
+                                                 a.z, st);
+            else
+                launch_adjoint_general<float>(N, dt, dy, C, A, d_bounds, w.agg_q, w.agg_s, batch, T, D, L,
+                                              p.fine_len, p.n_fine, c_first, n_launch, a.dt_mode, a.dt_bias,
+                                              a.z, st);
+        } else if (bf) {
             launch_adjoint_chunk<uint16_t>(dt, dy, C, A, d_bounds, w.agg_q, w.agg_s, batch, T, D, L,
-                                           p.fine_len, p.n_fine, p.per_coarse, p.n_fine - p.per_coarse, st,
-                                           a.dt_mode, a.dt_bias, a.z);
-        else
+                                           p.fine_len, p.n_fine, c_first, n_launch, st, a.dt_mode, a.dt_bias,
+                                           a.z);
+        } else {
             launch_adjoint_chunk<float>(dt, dy, C, A, d_bounds, w.agg_q, w.agg_s, batch, T, D, L,
-                                        p.fine_len, p.n_fine, p.per_coarse, p.n_fine - p.per_coarse, st,
-                                        a.dt_mode, a.dt_bias, a.z);
-        launch_carry(true, w.agg_q, w.agg_s, A, nullptr, w.q_in, nullptr, batch, D, kStates, p.n_fine,
+                                        p.fine_len, p.n_fine, c_first, n_launch, st, a.dt_mode, a.dt_bias,
+                                        a.z);
+        }
+        launch_carry(true, w.agg_q, w.agg_s, A, nullptr, w.q_in, nullptr, batch, D, N, p.n_fine,
                      p.n_fine, st, p.per_coarse - 1);
         a.qin = w.q_in + (int64_t)(p.per_coarse - 1) * hs;
         a.qin_bs = (int64_t)p.n_fine * hs;
         a.qin_cs = (int64_t)p.per_coarse * hs;
     }
     const int nc = carry ? p.n_coarse : 1;
-    if (shape->dtype == BDSSM_BF16) {
-        launch_bwd<uint16_t, false>(L, a, batch, T, D, Tc, nc, st);
-        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, nc, st, a.fused, d_bias);
+    if (bf) {
+        if (general) launch_bwd_general<uint16_t, false>(N, a, batch, T, D, L, Tc, nc, st);
+        else launch_bwd<uint16_t, false>(L, a, batch, T, D, Tc, nc, st);
+        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias);
     } else {
-        launch_bwd<float, false>(L, a, batch, T, D, Tc, nc, st);
-        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, nc, st, a.fused, d_bias);
+        if (general) launch_bwd_general<float, false>(N, a, batch, T, D, L, Tc, nc, st);
+        else launch_bwd<float, false>(L, a, batch, T, D, Tc, nc, st);
+        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias);
     }
     return launch_status();
 }
@@ -1295,57 +1386,58 @@ int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void 
                                 void *ws, size_t ws_bytes, const bdssm_fusion *fusion,
                                 bdssm_fusion_grads *grads, void *stream) {
     size_t nbnd = 0;
-    if (shape && shape->block_len > 0 && T >= 0 && shape->batch > 0 && shape->d_inner > 0)
-        nbnd = (size_t)shape->batch * (T / shape->block_len + 1) * shape->d_inner * kStates * 4;
+    if (shape && shape->block_len > 0 && T >= 0 && shape->batch > 0 && shape->d_inner > 0 &&
+        shape->d_state > 0)
+        nbnd = (size_t)shape->batch * (T / shape->block_len + 1) * shape->d_inner * shape->d_state * 4;
     int rc = check_bwd(shape, T, x, dt, B, C, A, Dskip, h0_blocks, dy, nullptr, dx, ddt, dB, dC, dA,
                        dDskip, dh0_blocks, nbnd);
     if (rc) return rc;
-    const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len;
+    const int64_t batch = shape->batch, D = shape->d_inner, L = shape->block_len, N = shape->d_state;
     BwdArgs a{x, dt, B, C, dy, A, Dskip, h0_blocks, nullptr, nullptr, 0, 0, dx, ddt,
               nullptr, nullptr, nullptr, dh0_blocks};
-    {
-        const size_t e = esize(shape);
-        const size_t ntok = (size_t)batch * T * D * e, nbc = (size_t)batch * T * kStates * e;
-        rc = resolve_bwd_fusion(fusion, grads, shape, T,
-                                {{x, ntok}, {dt, ntok}, {B, nbc}, {C, nbc}, {dy, ntok}, {h0_blocks, nbnd},
-                                 {A, (size_t)D * kStates * 4}, {Dskip, (size_t)D * 4}},
-                                {{dx, ntok}, {ddt, ntok}, {dB, nbc}, {dC, nbc}, {dA, (size_t)D * kStates * 4},
-                                 {dDskip, (size_t)D * 4}, {dh0_blocks, nbnd}, {ws, ws_bytes}},
-                                &a);
-        if (rc) return rc;
-    }
+    const size_t e = esize(shape);
+    const size_t ntok = (size_t)batch * T * D * e, nbc = (size_t)batch * T * N * e;
+    const size_t npar = (size_t)D * N * 4;
+    rc = resolve_bwd_fusion(fusion, grads, shape, T,
+                            {{x, ntok}, {dt, ntok}, {B, nbc}, {C, nbc}, {dy, ntok}, {h0_blocks, nbnd},
+                             {A, npar}, {Dskip, (size_t)D * 4}},
+                            {{dx, ntok}, {ddt, ntok}, {dB, nbc}, {dC, nbc}, {dA, npar},
+                             {dDskip, (size_t)D * 4}, {dh0_blocks, nbnd}, {ws, ws_bytes}},
+                            &a);
+    if (rc) return rc;
     float *d_bias = grads ? grads->d_dt_bias : nullptr;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (batch == 0 || D == 0 || T == 0) {
-        rc = zero_bwd(D, dA, dDskip, dh0_blocks, batch * D * kStates, st);
+        rc = zero_bwd(D, N, dA, dDskip, dh0_blocks, batch * D * N, st);
         if (!rc && d_bias && D > 0) rc = copy_or_zero(nullptr, d_bias, D, st);
         return rc;
     }
     if (!aligned16(ws)) return BDSSM_ERR_ALIGN;
+    const bool general = bwd_general(L, N);
     int64_t tc, nc;
-    if (!bwd_blocks_plan(batch, D, T, L, &tc, &nc, a.fused)) return BDSSM_ERR_SHAPE;
-    const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, 1, nc, false);
+    if (!bwd_blocks_plan(batch, D, T, L, N, &tc, &nc, a.fused)) return BDSSM_ERR_SHAPE;
+    const int64_t nblk = ceil_div(D, bwd_channels(L, N, a.fused));
+    const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, 1, nc, false, N, nblk);
     if (ws == nullptr || ws_bytes < probe.bytes) return BDSSM_ERR_WORKSPACE;
-    const size_t e = esize(shape);
-    const size_t ntok = (size_t)batch * T * D * e, nbc = (size_t)batch * T * kStates * e;
     if (!ws_clear(ws, probe.bytes, {{x, ntok}, {dt, ntok}, {B, nbc}, {C, nbc}, {dy, ntok},
                                     {h0_blocks, nbnd}, {dx, ntok}, {ddt, ntok}, {dB, nbc},
-                                    {dC, nbc}, {dA, (size_t)D * kStates * 4},
-                                    {dDskip, (size_t)D * 4}, {dh0_blocks, nbnd},
-                                    {A, (size_t)D * kStates * 4}, {Dskip, (size_t)D * 4}}))
+                                    {dC, nbc}, {dA, npar}, {dDskip, (size_t)D * 4}, {dh0_blocks, nbnd},
+                                    {A, npar}, {Dskip, (size_t)D * 4}}))
         return BDSSM_ERR_ALIAS;
-    const BwdWorkspace w = layout_bwd(ws, batch, D, T, 1, nc, false);
+    const BwdWorkspace w = layout_bwd(ws, batch, D, T, 1, nc, false, N, nblk);
     a.part_bc = w.part_bc;
     a.part_a = w.part_a;
     a.part_d = w.part_d;
     a.part_bias = w.part_bias;
     if (shape->dtype == BDSSM_BF16) {
-        launch_bwd<uint16_t, true>(L, a, batch, T, D, tc, (int)nc, st);
-        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, nc, st, a.fused, d_bias);
+        if (general) launch_bwd_general<uint16_t, true>(N, a, batch, T, D, L, tc, (int)nc, st);
+        else launch_bwd<uint16_t, true>(L, a, batch, T, D, tc, (int)nc, st);
+        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias);
     } else {
-        launch_bwd<float, true>(L, a, batch, T, D, tc, (int)nc, st);
-        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, nc, st, a.fused, d_bias);
+        if (general) launch_bwd_general<float, true>(N, a, batch, T, D, L, tc, (int)nc, st);
+        else launch_bwd<float, true>(L, a, batch, T, D, tc, (int)nc, st);
+        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias);
     }
     return launch_status();
 }

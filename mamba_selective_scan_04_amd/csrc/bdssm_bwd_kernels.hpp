@@ -994,35 +994,348 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
     }
 }
 
-// dB and dC: sum the channel-block partials in order.  One thread per
-// (batch, token, j), j < 16 -> dB state j, j >= 16 -> dC state j - 16.
-template <typename Tin>
-__global__ __launch_bounds__(256) void bc_reduce_kernel(const float *__restrict__ part_bc, Tin *__restrict__ dB,
-                                                        Tin *__restrict__ dC, int batch, int64_t T, int nblk64)
+// ------------------------------------------------------------------------
+// The general backward: block lengths outside {1, 2, 4, 8, 16} (up to
+// kMaxLdsBlock) and state counts other than 16, the gradients of bwd_pair_kernel.
+
+// Chunk-local adjoint for kN states and any block length L (adjoint_chunk_kernel's
+// job).  Chunks are whole blocks, so the chunk's last row ends a block; block
+// ends are counted from the right end.  grid = (ceil(D/64), chunks launched,
+// batch), block = 64; chunk c = c_first + blockIdx.y.
+template <typename Tin, int kN, int kDt = kDtPlain>
+__global__ __launch_bounds__(kWave) void adjoint_general_kernel(
+    const Tin *__restrict__ dt, const Tin *__restrict__ dy, const Tin *__restrict__ Cm,
+    const float *__restrict__ A, const float *__restrict__ dbounds, float *__restrict__ qout,
+    float *__restrict__ sout, int64_t T, int D, int L, int64_t Tc, int n_chunks, int c_first,
+    const float *__restrict__ dt_bias, const Tin *__restrict__ z)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)batch * T * 32) return;
-    const int j = (int)(i & 31);
-    const int64_t bt = i >> 5;
-    const int64_t b = bt / T, t = bt % T;
-    const float *p = part_bc + (b * nblk64 * T + t) * 32 + j;
-    float s = 0.f;
-    for (int k = 0; k < nblk64; ++k) s += p[(int64_t)k * T * 32];
-    if (j < kStates) dB[bt * kStates + j] = narrow<Tin>(s);
-    else dC[bt * kStates + j - kStates] = narrow<Tin>(s);
+    const int lane = threadIdx.x;
+    const int d_raw = blockIdx.x * kWave + lane;
+    const bool live = d_raw < D;
+    const int d = live ? d_raw : D - 1;
+    const int c = c_first + blockIdx.y;
+    const int b = blockIdx.z;
+    const int64_t t_begin = (int64_t)c * Tc;
+    const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
+    const int len = (int)(t_end - t_begin);
+    const int64_t nbl = T / L;
+    const int64_t blk0 = t_begin / L;
+
+    float a2[kN], q[kN];
+    load_row<kN>(A + (int64_t)d * kN, a2);
+#pragma unroll
+    for (int n = 0; n < kN; ++n) { a2[n] *= kLog2e; q[n] = 0.f; }
+    float S = 0.f;
+    const int64_t first = (int64_t)b * T + t_begin;
+    const Rows<Tin> ds(dt + first * D, len, D, d);
+    const Rows<Tin> ys(dy + first * D, len, D, d);
+    const bool gate = z != nullptr;
+    const Rows<Tin> zs((gate ? z : dy) + first * D, len, D, d);
+    const float bias = (kDt != kDtPlain && dt_bias != nullptr) ? dt_bias[d] : 0.f;
+    const Tin *cs = Cm + first * kN;
+    int kb = 0;                                   // rows walked since the last block end
+    for (int p = len - 1; p >= 0; --p) {
+        if (dbounds != nullptr && kb == 0) {
+            float v[kN];
+            load_row<kN>(dbounds + (((int64_t)b * (nbl + 1) + blk0 + (p + 1) / L) * D + d) * kN, v);
+#pragma unroll
+            for (int n = 0; n < kN; ++n) q[n] += v[n];
+        }
+        const float dl = step_size<kDt>(widen(ds.load(p)), bias);
+        float gy = live ? widen(ys.load(p)) : 0.f;
+        if (gate) gy *= silu_f(widen(zs.load(p)));
+        S += dl;
+        const Tin *crow = cs + (int64_t)p * kN;
+#pragma unroll
+        for (int k = 0; k < kN / 2; ++k) {
+            float c0, c1;
+            load_pair(crow, k, c0, c1);
+            q[2 * k] = fast_exp2(dl * a2[2 * k]) * __builtin_fmaf(gy, c0, q[2 * k]);
+            q[2 * k + 1] = fast_exp2(dl * a2[2 * k + 1]) * __builtin_fmaf(gy, c1, q[2 * k + 1]);
+        }
+        kb = (kb + 1 == L) ? 0 : kb + 1;
+    }
+    if (live) {
+        store_row<kN>(qout + (((int64_t)b * n_chunks + c) * D + d) * kN, q);
+        sout[((int64_t)b * n_chunks + c) * D + d] = S;
+    }
 }
 
-// dA [D,16], dDskip [D] and (when part_bias is given) the dt_bias gradient
+// v summed with the lane v ^ kMask holds (all lanes active)
+template <int kMask> __device__ __forceinline__ float xor_add(float v, int lane) {
+    if constexpr (kMask == 1)
+        return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    else if constexpr (kMask == 2)
+        return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+    else if constexpr (kMask == 4) return v + xchg4(v);
+    else if constexpr (kMask == 8) return v + xchg8(v);
+    else if constexpr (kMask == 16) return v + xchg16(v);
+    else return v + xchg32(v, lane);
+}
+// butterfly sum over the lane-index bits kFrom, 2 kFrom, ... below kTo
+template <int kFrom, int kTo> __device__ __forceinline__ float lane_sum(float v, int lane) {
+    if constexpr (kFrom >= kTo) return v;
+    else return lane_sum<2 * kFrom, kTo>(xor_add<kFrom>(v, lane), lane);
+}
+
+// Block-local backward of the general path, one lane per (channel, state):
+// lane = kN cl + n, CW = 64 / kN channels per wave, 4 waves per workgroup.
+// Each block of the chunk (right to left) is walked twice: left to right for
+// hf and the reverse adjoint gr, keeping both at every 16-token segment start
+// (LDS, dynamic size 2 KB per segment), then segment by segment right to left:
+// the segment's hf before each token and gr are formed again from its
+// checkpoint into registers, and the right-to-left walk runs hr and the
+// forward adjoint with every gradient term, as in bwd_pair_kernel.  The
+// token rows of a segment are staged in LDS (x, dt, dy per wave, B and C
+// shared by the workgroup; widened, the step size and the gate's factors
+// formed once per element).  Sums: over the channel's
+// kN lanes by butterfly (dt, x, and y_pre for the gate), over the wave's
+// channels by butterfly and over the 4 waves in LDS (dB, dC: part_bc
+// [batch, ceil(D / (4 CW)), T, 2 kN]).  Arguments as in bwd_pair_kernel.
+// grid = (ceil(D / (4 CW)), chunks, batch), block = 256.
+template <typename Tin, int kN, bool kBlockInit, bool kFuse>
+__global__ __launch_bounds__(4 * kWave) void bwd_general_kernel(
+    const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
+    const Tin *__restrict__ Cm, const Tin *__restrict__ dy, const float *__restrict__ A,
+    const float *__restrict__ Dskip, const float *__restrict__ h_start, const float *qin,
+    int64_t qin_bs, int64_t qin_cs, const float *__restrict__ dbounds, Tin *__restrict__ dx,
+    Tin *__restrict__ ddt, float *__restrict__ part_bc, float *__restrict__ part_a,
+    float *__restrict__ part_d, float *__restrict__ dh0, int64_t T, int D, int L, int64_t Tc,
+    BwdFuse<Tin> fz)
+{
+    constexpr int CW = kWave / kN;            // channels per wave
+    constexpr int G = 16;                     // segment length
+    constexpr int ES = sizeof(Tin);
+    constexpr int NE = (G * CW + kWave - 1) / kWave;   // token-row elements per lane per stream
+    __shared__ float tx[4][G][CW], tdl[4][G][CW], tgy[4][G][CW], tzv[4][G][CW];
+    __shared__ float tb[G][kN], tc[G][kN];       // B / C rows, shared by the 4 waves
+    __shared__ float red[4][G][2 * kN];
+    extern __shared__ float ck[];             // [segments][4 waves][2][64]: hf, pr at segment starts
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = uniform(threadIdx.x >> 6);
+    const int cl = lane / kN;
+    const int n = lane % kN;
+    const int d_w0 = blockIdx.x * 4 * CW + w * CW;
+    const int d_raw = d_w0 + cl;
+    const bool live = d_raw < D;
+    const int d = live ? d_raw : D - 1;
+    const int c = blockIdx.y;
+    const int b = blockIdx.z;
+    const int64_t t_begin = (int64_t)c * Tc;
+    const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
+    const int len = (int)(t_end - t_begin);
+    const int64_t nbl = T / L;
+    const int nseg = (L + G - 1) / G;
+
+    const float ar = A[(int64_t)d * kN + n];
+    const float a2 = ar * kLog2e;
+    const float dsk = Dskip[d];
+    float q = 0.f;
+    if (!kBlockInit && qin != nullptr && t_end < T)
+        q = qin[(int64_t)b * qin_bs + (int64_t)c * qin_cs + (int64_t)d * kN + n];
+    float dA_acc = 0.f, dD_acc = 0.f, bias_acc = 0.f;
+    auto state_idx = [&](int64_t blk) { return (((int64_t)b * (nbl + 1) + blk) * D + d) * kN + n; };
+    if (kBlockInit && dh0 != nullptr && t_end == T && live) dh0[state_idx(nbl)] = 0.f;
+
+    const int64_t first = (int64_t)b * T + t_begin;
+    const Rows<Tin> xs(x + first * D, len, D, 0);
+    const Rows<Tin> dts(dt + first * D, len, D, 0);
+    const Rows<Tin> ys(dy + first * D, len, D, 0);
+    const bool gate = kFuse && fz.z != nullptr;
+    const Rows<Tin> zs((gate ? fz.z : dy) + first * D, len, D, 0);
+    const Rows<Tin> bs(Bm + first * kN, len, kN, 0);
+    const Rows<Tin> cs(Cm + first * kN, len, kN, 0);
+    const bool sp_mode = kFuse && fz.dt_mode == kDtSoftplus;
+
+    // stage the rows of tokens k0 .. k0 + cnt - 1 (chunk-local) for this wave
+    auto stage = [&](int k0, int cnt) {
+#pragma unroll
+        for (int j = 0; j < NE; ++j) {
+            const int e = lane + kWave * j;
+            if (e < G * CW) {
+                const int i = e / CW, ch = e % CW;
+                const bool ok = i < cnt && d_w0 + ch < D;
+                const int32_t off = ok ? (d_w0 + ch) * ES + (k0 + i) * xs.pitch : kOutOfRange;
+                const float xv = widen(xs.load_at(off));
+                float dl = widen(dts.load_at(off));
+                float gy = widen(ys.load_at(off));
+                float zv = 0.f;
+                if constexpr (kFuse) {
+                    const float bias = (fz.dt_bias != nullptr && ok) ? fz.dt_bias[d_w0 + ch] : 0.f;
+                    if (fz.dt_mode == kDtSoftplus) dl = ok ? step_size<kDtSoftplus>(dl, bias) : 0.f;
+                    else if (fz.dt_mode == kDtBias) dl = ok ? step_size<kDtBias>(dl, bias) : 0.f;
+                    if (gate) {
+                        const float zf = widen(zs.load_at(off));
+                        const float sg = __builtin_amdgcn_rcpf(1.f + fast_exp2(-zf * kLog2e));
+                        zv = gy * (sg * __builtin_fmaf(zf, 1.f - sg, 1.f));     // dy silu'(z)
+                        gy = gy * (zf * sg);                                     // dy silu(z)
+                    }
+                }
+                tx[w][i][ch] = xv;
+                tdl[w][i][ch] = dl;
+                tgy[w][i][ch] = gy;
+                tzv[w][i][ch] = zv;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < (G * kN + 4 * kWave - 1) / (4 * kWave); ++j) {
+            const int e = threadIdx.x + 4 * kWave * j;
+            if (e < G * kN) {
+                const int i = e / kN, col = e % kN;
+                const int32_t off = i < cnt ? col * ES + (k0 + i) * bs.pitch : kOutOfRange;
+                tb[i][col] = widen(bs.load_at(off));
+                tc[i][col] = widen(cs.load_at(off));
+            }
+        }
+        __syncthreads();                              // the shared B / C rows are complete
+    };
+
+    float *pbc = part_bc + ((int64_t)b * gridDim.x + blockIdx.x) * T * (2 * kN);
+    float *ckw = ck + (int64_t)w * 2 * kWave;     // + seg * 4 * 2 * 64
+
+    for (int kb0 = len - L; kb0 >= 0; kb0 -= L) {            // blocks, right to left
+        const int64_t blk = (t_begin + kb0) / L;
+        // pass 1: hf and the reverse adjoint's carried pr = a gr, left to right
+        float hf = h_start[state_idx(blk)];
+        float pr = 0.f;
+        for (int sg = 0; sg < nseg; ++sg) {
+            const int k0 = kb0 + sg * G;
+            const int cnt = (L - sg * G < G) ? L - sg * G : G;
+            ckw[sg * 8 * kWave + n + kN * cl] = hf;
+            ckw[sg * 8 * kWave + kWave + n + kN * cl] = pr;
+            if (sg == nseg - 1) break;                      // the last segment is formed again in pass 2
+            __syncthreads();                                 // every wave is done with the last rows
+            stage(k0, cnt);
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                const float dl = tdl[w][i][cl], xv = tx[w][i][cl], gy = tgy[w][i][cl];
+                const float a = fast_exp2(dl * a2);
+                const float grv = __builtin_fmaf(gy, tc[i][n], pr);
+                hf = __builtin_fmaf(a, hf, dl * xv * tb[i][n]);
+                pr = a * grv;
+            }
+            asm volatile("" ::: "memory");
+        }
+        // pass 2: segments right to left
+        float hr = 0.f;
+        if (kBlockInit) q = 0.f;
+        else if (dbounds != nullptr) q += dbounds[state_idx(blk + 1)];
+        for (int sg = nseg - 1; sg >= 0; --sg) {
+            const int k0 = kb0 + sg * G;
+            const int cnt = (L - sg * G < G) ? L - sg * G : G;
+            __syncthreads();                                 // rows and red of the last segment consumed
+            stage(k0, cnt);
+            float hp[G], gs[G];
+            float h = ckw[sg * 8 * kWave + n + kN * cl];
+            float p2 = ckw[sg * 8 * kWave + kWave + n + kN * cl];
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                const float dl = tdl[w][i][cl], xv = tx[w][i][cl], gy = tgy[w][i][cl];
+                const float a = fast_exp2(dl * a2);
+                hp[i] = h;
+                gs[i] = __builtin_fmaf(gy, tc[i][n], p2);
+                h = __builtin_fmaf(a, h, dl * xv * tb[i][n]);
+                p2 = a * gs[i];
+            }
+            // rows past cnt carry dt = 0, x = dy = 0: their decay is 1 and they
+            // inject nothing, so h after the last row is the state after row cnt - 1
+#pragma unroll
+            for (int i = G - 1; i >= 0; --i) {
+                if (i < cnt) {
+                    const float dl = tdl[w][i][cl], xv = tx[w][i][cl], gy = tgy[w][i][cl];
+                    const float bv = tb[i][n], cv = tc[i][n];
+                    const float a = fast_exp2(dl * a2);
+                    const float u = dl * xv * bv;
+                    const float hr1 = hr;
+                    hr = __builtin_fmaf(a, hr1, u);
+                    const float gf = __builtin_fmaf(gy, cv, q);
+                    const float du = gf + gs[i];
+                    const float da = __builtin_fmaf(gf, hp[i], gs[i] * hr1);
+                    q = a * gf;
+                    const float daa = da * a;
+                    dA_acc = __builtin_fmaf(daa, dl, dA_acc);
+                    // the state after token i (rows past cnt leave it unchanged)
+                    const float hf_t = (i == G - 1) ? h : hp[(i + 1) & (G - 1)];
+                    const float hsum = hf_t + hr;
+                    // sums over the channel's kN lanes
+                    float sdt = lane_sum<1, kN>(__builtin_fmaf(du * bv, xv, daa * ar), lane);
+                    float sx = lane_sum<1, kN>(du * bv * dl, lane);
+                    float yp = 0.f;
+                    if constexpr (kFuse) yp = lane_sum<1, kN>(cv * hsum, lane);
+                    // dB, dC of the token: sums over the wave's channels
+                    const float vb = lane_sum<kN, kWave>(du * dl * xv, lane);
+                    const float vc = lane_sum<kN, kWave>(gy * hsum, lane);
+                    if (cl == 0) {
+                        red[w][i][n] = vb;
+                        red[w][i][kN + n] = vc;
+                    }
+                    const int64_t row = (first + k0 + i) * D + d;
+                    if (n == 0 && live) {
+                        dD_acc = __builtin_fmaf(gy, xv, dD_acc);
+                        dx[row] = narrow<Tin>(__builtin_fmaf(gy, dsk, sx));
+                        if constexpr (kFuse) {
+                            if (sp_mode) sdt *= sigmoid_from_softplus(dl);
+                            bias_acc += sdt;
+                            if (gate) fz.dz[row] = narrow<Tin>(tzv[w][i][cl] * __builtin_fmaf(dsk, xv, yp));
+                        }
+                        ddt[row] = narrow<Tin>(sdt);
+                    }
+                    if (kBlockInit && sg == 0 && i == 0 && dh0 != nullptr && live) dh0[state_idx(blk)] = q;
+                }
+            }
+            __syncthreads();
+            // dB / dC of the segment: the 4 waves' sums in order
+            for (int o = threadIdx.x; o < cnt * 2 * kN; o += 4 * kWave) {
+                const int i = o / (2 * kN), j = o % (2 * kN);
+                pbc[(t_begin + k0 + i) * (2 * kN) + j] = ((red[0][i][j] + red[1][i][j]) + red[2][i][j]) + red[3][i][j];
+            }
+        }
+    }
+    // continuous form: the start state's gradient (chunk 0)
+    if (!kBlockInit && c == 0 && dh0 != nullptr && live)
+        dh0[((int64_t)b * D + d) * kN + n] = q + (dbounds != nullptr ? dbounds[state_idx(0)] : 0.f);
+    if (live) {
+        const int64_t pc = (int64_t)b * gridDim.y + c;
+        part_a[(pc * D + d) * kN + n] = dA_acc;
+        if (n == 0) {
+            part_d[pc * D + d] = dD_acc;
+            if (kFuse && fz.part_bias != nullptr) fz.part_bias[pc * D + d] = bias_acc;
+        }
+    }
+}
+
+// dB and dC: sum the channel-block partials in order.  One thread per
+// (batch, token, j), j < N -> dB state j, j >= N -> dC state j - N.
+template <typename Tin>
+__global__ __launch_bounds__(256) void bc_reduce_kernel(const float *__restrict__ part_bc, Tin *__restrict__ dB,
+                                                        Tin *__restrict__ dC, int batch, int64_t T, int nblk,
+                                                        int N)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int ncol = 2 * N;
+    if (i >= (int64_t)batch * T * ncol) return;
+    const int j = (int)(i % ncol);
+    const int64_t bt = i / ncol;
+    const int64_t b = bt / T, t = bt % T;
+    const float *p = part_bc + (b * nblk * T + t) * ncol + j;
+    float s = 0.f;
+    for (int k = 0; k < nblk; ++k) s += p[(int64_t)k * T * ncol];
+    if (j < N) dB[bt * N + j] = narrow<Tin>(s);
+    else dC[bt * N + j - N] = narrow<Tin>(s);
+}
+
+// dA [D,N], dDskip [D] and (when part_bias is given) the dt_bias gradient
 // [D]: sum the (batch, chunk) partials in order.
 __global__ __launch_bounds__(256) void param_reduce_kernel(const float *__restrict__ part_a,
                                                            const float *__restrict__ part_d,
                                                            float *__restrict__ dA, float *__restrict__ dDskip,
                                                            int D, int n_parts,
                                                            const float *__restrict__ part_bias,
-                                                           float *__restrict__ d_bias)
+                                                           float *__restrict__ d_bias, int N)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t na = (int64_t)D * kStates;
+    const int64_t na = (int64_t)D * N;
     if (i < na) {
         float s = 0.f;
         for (int k = 0; k < n_parts; ++k) s += part_a[(int64_t)k * na + i];

@@ -191,8 +191,9 @@ template <typename Tin> struct Rows {
     }
     __device__ __forceinline__ Tin load(int k) const;
     __device__ __forceinline__ void store(int k, Tin v) const;
-    // store at a byte offset of the lane's own choosing (an offset past the
-    // rows drops the store)
+    // load / store at a byte offset of the lane's own choosing (an offset past
+    // the rows reads zero / drops the store)
+    __device__ __forceinline__ Tin load_at(int32_t off) const;
     __device__ __forceinline__ void store_at(int32_t off, Tin v) const;
 };
 template <> __device__ __forceinline__ uint16_t Rows<uint16_t>::load(int k) const {
@@ -206,6 +207,12 @@ template <> __device__ __forceinline__ void Rows<uint16_t>::store(int k, uint16_
 }
 template <> __device__ __forceinline__ void Rows<float>::store(int k, float v) const {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsrc, lane_off, k * pitch, 0);
+}
+template <> __device__ __forceinline__ uint16_t Rows<uint16_t>::load_at(int32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b16(rsrc, off, 0, 0);
+}
+template <> __device__ __forceinline__ float Rows<float>::load_at(int32_t off) const {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0));
 }
 template <> __device__ __forceinline__ void Rows<uint16_t>::store_at(int32_t off, uint16_t v) const {
     __builtin_amdgcn_raw_buffer_store_b16(v, rsrc, off, 0, 0);

@@ -28,7 +28,7 @@ def test_exports_match_header():
 
 
 def test_version_and_status_strings():
-    assert m.version() == 10400
+    assert m.version() == 10500
     for code in range(-7, 1):
         assert m.status_str(code) not in ("", "unknown status")
     assert m.status_str(-99) == "unknown status"
@@ -133,10 +133,14 @@ def test_workspace_sizes():
     assert m.workspace_bytes(8, 1536, 4096, m.OP_TRAIN, d_state=32) > m.workspace_bytes(8, 1536, 4096, m.OP_TRAIN, d_state=8)
     with pytest.raises(ValueError):
         m.workspace_bytes(1, 64, 512, m.OP_TRAIN, d_state=6)
+    # the backward's general path takes the other state counts and block lengths
+    assert m.workspace_bytes(1, 64, 512, m.OP_TRAIN_BWD, d_state=8) > 0
+    assert m.workspace_bytes(1, 64, 512, m.OP_TRAIN_BWD, block_len=32) > 0
+    assert m.workspace_bytes(2, 64, 512, m.OP_BLOCKS_BWD, block_len=256, d_state=32) > 0
     with pytest.raises(ValueError):
-        m.workspace_bytes(1, 64, 512, m.OP_TRAIN_BWD, d_state=8)
+        m.workspace_bytes(1, 64, 512, m.OP_TRAIN_BWD, block_len=512)
     with pytest.raises(ValueError):
-        m.workspace_bytes(1, 64, 512, m.OP_TRAIN_BWD, block_len=32)
+        m.workspace_bytes(1, 64, 512, m.OP_BLOCKS_BWD, d_state=6)
     # monotone in T
     a = m.workspace_bytes(8, 1536, 4096, m.OP_TRAIN)
     b = m.workspace_bytes(8, 1536, 8192, m.OP_TRAIN)
@@ -174,10 +178,14 @@ def train_bwd(s, T, x=FAKE, dt=FAKE + 0x1000, Bm=FAKE + 0x2000, C=FAKE + 0x3000,
 
 def test_backward_argument_errors():
     s = shape(D=8)
-    assert train_bwd(shape(N=8), 16) == -2             # the backward runs 16 states only
+    assert train_bwd(shape(N=6), 16) == -2             # unsupported state count
     assert train_bwd(s, 24) == -2                      # T % L != 0
-    assert train_bwd(shape(D=8, L=32), 32) == -2       # the backward takes L | 16 only
-    assert train_bwd(shape(D=8, L=3), 48) == -2
+    assert train_bwd(shape(D=8, L=257), 257) == -2     # blocks above 256 tokens
+    # other state counts and block lengths pass the checks (general path) and
+    # stop at the missing workspace
+    assert train_bwd(shape(D=8, N=8), 16) == -5
+    assert train_bwd(shape(D=8, L=32), 32) == -5
+    assert train_bwd(shape(D=8, L=3), 12) == -5
     assert train_bwd(s, 16, hb=None) == -1             # saved block states required
     assert train_bwd(s, 16, dy=None) == -1
     assert train_bwd(s, 16, dA=None) == -1

@@ -3,7 +3,8 @@ one-lane-per-channel kernels instantiated per state count) on every forward
 entry point and the baseline, against the fp64 oracle, element by element:
 block lengths inside and outside {1, 2, 4, 8, 16}, forced multi-chunk plans,
 ragged channel counts, the two-stream form, the fusions and separate reverse
-operands.  The backward entry points take 16 states only and reject others.
+operands.  The backward of these state counts is covered by
+test_parity_bwd_general.py.
 """
 import pytest
 import torch
@@ -118,11 +119,3 @@ def test_fusions_and_reverse_operands(dev, monkeypatch):
     close(bnd, bo, STATE_TOL, "h_bounds")
     close(yf, oracle.full_scan(*oa, **ok), TOL[dtype], "full_scan y")
 
-
-def test_backward_rejects_other_state_counts(dev):
-    batch, T, D, L, n = 1, 32, 64, 16, 8
-    c = Case(batch, T, D, torch.float32, sid=75, n=n)
-    _, bnd = m.train_scan(*c.args(), L, want_bounds=True)
-    dy = synth.normal((batch, T, D), 7501, "cuda")
-    with pytest.raises((m.BdssmError, ValueError)):
-        m.train_scan_bwd(*c.args(), L, bnd, dy)
