@@ -62,7 +62,11 @@
  *     channel that stages one block's forward output in LDS (256 * block_len
  *     bytes).  The pages fix neither size (the workloads here use 16 and 16)
  *     and name a dynamic block size as future work ([ZH] "未来方向").
- *   backward entry points: d_state 16, block_len 1, 2, 4, 8 or 16.
+ *   backward entry points: the same sizes.  d_state 16 with block_len 1, 2,
+ *     4, 8 or 16 runs the register-resident kernels; every other combination
+ *     runs a kernel with one lane per (channel, state) that keeps the forward
+ *     state and the reverse adjoint at every 16-token segment start of a
+ *     block in LDS and forms each segment again (slower, same results).
  */
 #ifndef BDSSM_H
 #define BDSSM_H
@@ -134,7 +138,7 @@ typedef struct {
 typedef struct {
     int64_t batch;     /* >= 0 */
     int64_t d_inner;   /* channels D, >= 0 */
-    int64_t d_state;   /* states N: 4, 8, 16 or 32 (16 for the backward) */
+    int64_t d_state;   /* states N: 4, 8, 16 or 32 */
     int64_t block_len; /* L, the denoising block length */
     int32_t dtype;     /* bdssm_dtype of x, dt, B, C, y */
 } bdssm_shape;
