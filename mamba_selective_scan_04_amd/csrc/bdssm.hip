@@ -517,6 +517,40 @@ void launch_bidir_L(const void *x, const void *dt, const void *B, const void *C,
 #undef BDSSM_BIDIR
 }
 
+// One block from the cache on block_lane_kernel (block_step: kCommit false;
+// commit: true, y optional).  Used for L <= 16 with shared reverse operands.
+template <typename Tin, bool kCommit>
+void launch_block_lane(int64_t N, const void *x, const void *dt, const void *B, const void *C,
+                       const float *A, const float *Dskip, float *h_cache, void *y, int64_t batch,
+                       int64_t D, int64_t L, const Fuse &f, hipStream_t st) {
+    with_states(N, [&](auto kn) {
+        constexpr int K = decltype(kn)::value;
+        const dim3 g((unsigned)ceil_div(D, 4 * kWave / K), (unsigned)batch);
+        if (f.any())
+            hipLaunchKernelGGL((block_lane_kernel<Tin, K, kCommit, true>), g, dim3(4 * kWave), 0, st,
+                               (const Tin *)x, (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip,
+                               h_cache, (Tin *)y, (int)D, (int)L, f.args<Tin>());
+        else
+            hipLaunchKernelGGL((block_lane_kernel<Tin, K, kCommit, false>), g, dim3(4 * kWave), 0, st,
+                               (const Tin *)x, (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip,
+                               h_cache, (Tin *)y, (int)D, (int)L, f.args<Tin>());
+    });
+}
+
+// Whether a single-block call runs block_lane_kernel.  Measured on MI355X
+// (65K context, batch 8, graph replays): the state-only commit takes 4.5 us
+// there against 5.8 us on the one-lane-per-channel chunk kernel, but the block
+// step takes 5.1 us against 4.3 us on bidir_wave_kernel, whose row DMA beats
+// the lane kernel's per-lane loads; so only the state-only commit uses it.
+// BDSSM_BLOCK_KERNEL=lane / wave forces one path (comparison and tests).
+bool block_lane_path(int64_t L, const Fuse &f, bool with_y) {
+    if (L > kGroup || f.dt_r != nullptr) return false;
+    const char *v = getenv("BDSSM_BLOCK_KERNEL");
+    if (v != nullptr && v[0] == 'w') return false;
+    if (v != nullptr && v[0] == 'l') return true;
+    return !with_y;
+}
+
 template <typename Tin, int kN, bool kInit, int kDt>
 void launch_block_bidir_k(dim3 g, int64_t L, const void *x, const void *dt, const void *B,
                           const void *C, const float *A, const float *Dskip, const float *hin,
@@ -1034,10 +1068,16 @@ int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void 
     const Fuse f = resolve_fusion(fusion, true);
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    if (shape->dtype == BDSSM_BF16)
+    if (block_lane_path(L, f, true)) {
+        if (shape->dtype == BDSSM_BF16)
+            launch_block_lane<uint16_t, false>(N, x, dt, B, C, A, Dskip, const_cast<float *>(h_cache), y, batch, D, L, f, st);
+        else
+            launch_block_lane<float, false>(N, x, dt, B, C, A, Dskip, const_cast<float *>(h_cache), y, batch, D, L, f, st);
+    } else if (shape->dtype == BDSSM_BF16) {
         launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, h_cache, D * N, 0, y, nullptr, nullptr, batch, L, D, N, L, 1, st, nullptr, f);
-    else
+    } else {
         launch_bidir<float>(L, x, dt, B, C, A, Dskip, h_cache, D * N, 0, y, nullptr, nullptr, batch, L, D, N, L, 1, st, nullptr, f);
+    }
     return launch_status();
 }
 
@@ -1064,7 +1104,12 @@ int bdssm_commit(const bdssm_shape *shape, float *h_cache, const void *x, const 
     const Fuse f = resolve_fusion(fusion, with_y);
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    if (shape->dtype == BDSSM_BF16) {
+    if (block_lane_path(L, f, with_y)) {
+        if (shape->dtype == BDSSM_BF16)
+            launch_block_lane<uint16_t, true>(N, x, dt, B, C, A, Dskip, h_cache, y, batch, D, L, f, st);
+        else
+            launch_block_lane<float, true>(N, x, dt, B, C, A, Dskip, h_cache, y, batch, D, L, f, st);
+    } else if (shape->dtype == BDSSM_BF16) {
         if (with_y) launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, h_cache, D * N, 0, y, nullptr, h_cache, batch, L, D, N, L, 1, st, nullptr, f);
         else launch_chunk_state<uint16_t>(false, x, dt, B, A, h_cache, h_cache, nullptr, batch, L, D, N, L, 1, 0, 1, st, f);
     } else {

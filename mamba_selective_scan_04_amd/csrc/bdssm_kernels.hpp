@@ -731,6 +731,136 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 }
 
 // ------------------------------------------------------------------------
+// One block from the cache, for the latency-bound single-block calls
+// (block_step, commit; L <= 16, shared operands): one lane per (channel,
+// state), 64 / kN channels per wave, four independent waves per workgroup, so a block
+// spreads over kN times the waves of a one-lane-per-channel layout and each
+// lane runs one state's recurrence.  Every load of the block is issued up
+// front.  The per-channel rows (x, dt, z) are loaded once per element by the
+// channel's lanes in turn, the step size and silu(z) formed there, and shared
+// through LDS; each lane loads its state's B and C.  The lane runs the forward
+// recurrence from the cache and, when y is wanted, the in-block reverse; the
+// per-token outputs are summed over the channel's kN lanes through LDS, plus
+// Dskip x, times silu(z).  kCommit writes the forward state after the block
+// back to h_cache (each lane reads, then writes, its own entry).
+// grid = (ceil(D / (256 / kN)), batch), block = 256.
+template <typename Tin, int kN, bool kCommit, bool kFuse>
+__global__ __launch_bounds__(4 * kWave) void block_lane_kernel(
+    const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
+    const Tin *__restrict__ Cm, const float *__restrict__ A, const float *__restrict__ Dskip,
+    float *h_cache, Tin *__restrict__ y, int D, int L, FuseArgs<Tin> fz)
+{
+    constexpr int CW = kWave / kN;            // channels per wave
+    constexpr int G = kGroup;                 // L <= 16
+    __shared__ float part_s[4][G][kWave];     // per-lane output partials
+    __shared__ float xs_s[4][G][CW], dls_s[4][G][CW], gz_s[4][G][CW];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = uniform(threadIdx.x >> 6);
+    auto &part = part_s[w];
+    auto &xs = xs_s[w];
+    auto &dls = dls_s[w];
+    auto &gz = gz_s[w];
+    const int cl = lane / kN, n = lane % kN;
+    const int d0 = (blockIdx.x * 4 + w) * CW;
+    const int d_raw = d0 + cl;
+    const bool live = d_raw < D;
+    const int d = live ? d_raw : D - 1;
+    const int b = blockIdx.y;
+    const int64_t row0 = (int64_t)b * L;
+    const bool with_y = y != nullptr;
+    const bool gate = kFuse && with_y && fz.z != nullptr;
+    // output lanes: channel lane % CW (CW divides 64)
+    const int c_out = lane % CW;
+    const bool out_live = d0 + c_out < D;
+    const float dsk_out = with_y ? Dskip[out_live ? d0 + c_out : D - 1] : 0.f;   // Dskip may be null without y
+
+    const int64_t hidx = ((int64_t)b * D + d) * kN + n;
+    float h = h_cache[hidx];
+    const float a2 = A[(int64_t)d * kN + n] * kLog2e;
+    const float bias = (kFuse && fz.dt_bias != nullptr) ? fz.dt_bias[d] : 0.f;
+
+    // every load first (one memory round trip): the channel's rows, lane
+    // (cl, n) taking tokens n, n + kN, ..., and the lane's B and C
+    // (rows past L re-read row L - 1: unconditional loads go out back to back)
+    constexpr int NT = (G + kN - 1) / kN;
+    Tin rx[NT], rd[NT], rz[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int t = j * kN + n;
+        const int64_t r = (row0 + (t < L ? t : L - 1)) * D + d;
+        rx[j] = x[r];
+        rd[j] = dt[r];
+        rz[j] = gate ? fz.z[r] : rx[j];
+    }
+    const Tin *crow = with_y ? Cm : Bm;       // C may be null without y
+    Tin rb[G], rc[G];
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+        const int64_t r = (row0 + (t < L ? t : L - 1)) * kN + n;
+        rb[t] = Bm[r];
+        rc[t] = crow[r];
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int t = j * kN + n;
+        if (t < L) {
+            float dv = widen(rd[j]);
+            if constexpr (kFuse) {
+                if (fz.dt_mode == kDtSoftplus) dv = step_size<kDtSoftplus>(dv, bias);
+                else if (fz.dt_mode == kDtBias) dv = step_size<kDtBias>(dv, bias);
+            }
+            xs[t][cl] = widen(rx[j]);
+            dls[t][cl] = dv;
+            if (gate) gz[t][cl] = silu_f(widen(rz[j]));
+        }
+    }
+    float bv[G], cv[G];
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+        if (t < L) {
+            bv[t] = widen(rb[t]);
+            cv[t] = with_y ? widen(rc[t]) : 0.f;
+        }
+    }
+    asm volatile("" ::: "memory");
+    float a[G], u[G], yp[G];
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+        if (t < L) {
+            const float dv = dls[t][cl];
+            a[t] = fast_exp2(dv * a2);
+            u[t] = dv * xs[t][cl] * bv[t];
+            h = __builtin_fmaf(a[t], h, u[t]);
+            yp[t] = cv[t] * h;
+        }
+    }
+    if (kCommit && live) h_cache[hidx] = h;
+    if (!with_y) return;
+    float hr = 0.f;
+#pragma unroll
+    for (int t = G - 1; t >= 0; --t) {
+        if (t < L) {
+            hr = __builtin_fmaf(a[t], hr, u[t]);
+            part[t][lane] = __builtin_fmaf(cv[t], hr, yp[t]);
+        }
+    }
+    asm volatile("" ::: "memory");
+    for (int o = lane; o < L * CW; o += kWave) {
+        const int t = o / CW;
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < kN; k += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(&part[t][c_out * kN + k]);
+            s += (v.x + v.y) + (v.z + v.w);
+        }
+        float tot = __builtin_fmaf(dsk_out, xs[t][c_out], s);
+        if (gate) tot *= gz[t][c_out];
+        if (out_live) y[(row0 + t) * D + d0 + c_out] = narrow<Tin>(tot);
+    }
+}
+
+// ------------------------------------------------------------------------
 // Directional output sweep for the full-sequence baseline: one lane per
 // channel, 16 states.  Forward (kRev = false): from the chunk's incoming
 // forward state, writes yf_t = sum_n C_t h_t to an fp32 buffer.  Reverse:

@@ -304,3 +304,42 @@ def test_train_blocks_with_clean_bounds_matches_continuous(dev):
     yb = m.train_scan_blocks(*c.args(), 16, bnd)
     _sync()
     assert rel_err(to_np(yb), to_np(y)) < TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("kernel", ["lane", "wave"])
+@pytest.mark.parametrize("n,L,D,dtype", [(16, 16, 130, torch.bfloat16), (16, 5, 70, torch.float32),
+                                         (4, 16, 65, torch.bfloat16), (32, 12, 33, torch.float32),
+                                         (8, 1, 200, torch.bfloat16)])
+def test_single_block_kernels(dev, kernel, n, L, D, dtype, monkeypatch):
+    """block_step and commit (with and without y) on either single-block kernel
+    (one lane per (channel, state), or the bidirectional / chunk kernels),
+    with and without the step-size and gate fusions, against the oracle."""
+    from mamba_selective_scan_04_amd import synth
+    monkeypatch.setenv("BDSSM_BLOCK_KERNEL", kernel)
+    batch, P = 2, 4 * L
+    c = Case(batch, P + L, D, dtype, sid=12, a_kind="random", n=n)
+    h, _ = m.prefill(*c.segment(0, P), L)
+    blk = c.segment(P, P + L)
+    ho, _ = oracle.prefill(*c.oracle_args(0, P), L)
+    ob = c.oracle_args(P, P + L)
+    for fused in (False, True):
+        kw, ok = {}, {}
+        if fused:
+            bias = synth.normal((D,), 1201, "cuda", torch.float32, std=0.3)
+            z = synth.normal((batch, L, D), 1202, "cuda", dtype, std=1.5)
+            kw = dict(dt_bias=bias, dt_softplus=True, z=z)
+            ok = dict(dt_bias=to_np(bias), dt_softplus=True, z=synth.to_oracle(z))
+        y = m.block_step(h, *blk, **kw)
+        hc = h.clone()
+        _, yc = m.commit(hc, *blk, want_y=True, **kw)
+        hc2 = h.clone()
+        m.commit(hc2, *blk, **{k: v for k, v in kw.items() if k != "z"})
+        _sync()
+        tol = TOL[dtype]
+        assert rel_err(to_np(y), oracle.block_step(ho, *ob, **ok)) < tol, (fused, "block_step")
+        hco, yco = oracle.commit(ho, *ob, want_y=True, **ok)
+        assert rel_err(to_np(yc), yco) < tol, (fused, "commit y")
+        assert rel_err(to_np(hc), hco) < STATE_TOL, (fused, "commit state")
+        ok2 = {k: v for k, v in ok.items() if k != "z"}
+        hco2, _ = oracle.commit(ho, *ob, **ok2)
+        assert rel_err(to_np(hc2), hco2) < STATE_TOL, (fused, "commit state, no y")
