@@ -113,7 +113,7 @@ static int pick_reverse(rev_operands *r, const void *dt, const void *Bm, const v
     return 0;
 }
 
-int oracle_version(void) { return 4; }
+int oracle_version(void) { return 5; }
 
 /* Threads the OpenMP loop over rows will use (1 without OpenMP). */
 int oracle_num_threads(void)
@@ -608,6 +608,238 @@ int oracle_scan_bwd_ex(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L
             if (dA) for (int64_t i = 0; i < D * N; ++i) dA[i] += p[2 * n_bc + i];
             if (dDskip) for (int64_t i = 0; i < D; ++i) dDskip[i] += p[2 * n_bc + D * N + i];
             if (d_dt_bias) for (int64_t i = 0; i < D; ++i) d_dt_bias[i] += p[2 * n_bc + D * N + D + i];
+        }
+    }
+    free(parts);
+    return fail ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------
+ * The same gradients when the reverse scan has operands of its own (see
+ * rev_operands: dt_r with its own bias and the same softplus setting, B_r,
+ * C_r, A_r).  The two recurrences then share only x:
+ *   hf_t = a_t hf_{t-1} + u_t,      a_t = exp(dt_t A),     u_t = dt_t B_t x_t
+ *   hr_t = ar_t hr_{t+1} + ur_t,    ar_t = exp(dtr_t A_r), ur_t = dtr_t B_r_t x_t
+ *   y_t  = (sum_n C_t hf_t + C_r_t hr_t + Dskip x_t) [silu(z_t)]
+ * Adjoints (g = dy, or dy silu(z) with the gate):
+ *   gf_t = g_t C_t + a_{t+1} gf_{t+1}       (+ dbounds at block ends, as before)
+ *   gr_t = g_t C_r_t + ar_{t-1} gr_{t-1}    (left to right inside each block)
+ * and every term splits by direction:
+ *   forward operands:  ddt  += sum_n gf B x + gf hf_{t-1} a A;  dB += gf dt x;
+ *                      dC += g hf_t;  dA += gf hf_{t-1} a dt
+ *   reverse operands:  ddt_r += sum_n gr B_r x + gr hr_{t+1} ar A_r;
+ *                      dB_r += gr dtr x;  dC_r += g hr_t;  dA_r += gr hr_{t+1} ar dtr
+ *   dx += sum_n gf dt B + gr dtr B_r  (+ g Dskip)
+ * The dt streams' gradients go through softplus'(v) = s(v) of their own v, and
+ * d_dt_bias / d_dt_bias_r sum them.  With the reverse sharing the forward's
+ * operands these are the terms of oracle_scan_bwd_ex, added pairwise.
+ * Arguments as in oracle_scan_bwd_ex plus the reverse operands (dt_r, B_r, C_r
+ * in the stream dtype, A_r [D, N] and dt_bias_r [D] fp64, dt_bias_r may be
+ * NULL) and their gradients (fp64, any may be NULL): ddt_r [batch, T, D],
+ * dB_r, dC_r [batch, T, N], dA_r [D, N], d_dt_bias_r [D].
+ */
+int oracle_scan_bwd_sep(int64_t batch, int64_t T, int64_t D, int64_t N, int64_t L, int dtype,
+                        const void *x, const void *dt, const void *Bm, const void *Cm,
+                        const double *A, const double *Dskip, int blocks, const double *h0,
+                        const double *h0_blocks, const double *dy, const double *dbounds,
+                        const double *dt_bias, int dt_softplus, const void *z,
+                        const void *dt_r, const void *B_r, const void *C_r, const double *A_r,
+                        const double *dt_bias_r,
+                        double *dx, double *ddt, double *dB, double *dC, double *dA,
+                        double *dDskip, double *dh0, double *dh0_blocks, double *dz,
+                        double *d_dt_bias, double *ddt_r, double *dB_r, double *dC_r,
+                        double *dA_r, double *d_dt_bias_r)
+{
+    if (batch < 0 || T < 0 || D < 0 || N < 1 || L < 1 || T % L != 0) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) return -1;
+    if (!A || !Dskip || !A_r) return -1;
+    if (T > 0 && (!x || !dt || !Bm || !Cm || !dy || !dt_r || !B_r || !C_r)) return -1;
+    if (blocks && (h0 || dbounds || (T > 0 && !h0_blocks))) return -1;
+    if (!blocks && (h0_blocks || dh0_blocks)) return -1;
+    const int64_t nb = T / L;
+    const size_t n_tok = (size_t)(batch * T * D), n_bc = (size_t)(batch * T * N);
+    double *outs_tok[] = {dx, ddt, dz, ddt_r};
+    for (int i = 0; i < 4; ++i) if (outs_tok[i]) memset(outs_tok[i], 0, n_tok * sizeof(double));
+    double *outs_bc[] = {dB, dC, dB_r, dC_r};
+    for (int i = 0; i < 4; ++i) if (outs_bc[i]) memset(outs_bc[i], 0, n_bc * sizeof(double));
+    if (dA) memset(dA, 0, (size_t)(D * N) * sizeof(double));
+    if (dA_r) memset(dA_r, 0, (size_t)(D * N) * sizeof(double));
+    if (dDskip) memset(dDskip, 0, (size_t)D * sizeof(double));
+    if (d_dt_bias) memset(d_dt_bias, 0, (size_t)D * sizeof(double));
+    if (d_dt_bias_r) memset(d_dt_bias_r, 0, (size_t)D * sizeof(double));
+    if (dh0) memset(dh0, 0, (size_t)(batch * D * N) * sizeof(double));
+    if (dh0_blocks) memset(dh0_blocks, 0, (size_t)(batch * (nb + 1) * D * N) * sizeof(double));
+    if (batch == 0 || D == 0) return 0;
+
+    int nthr = 1;
+#ifdef _OPENMP
+    nthr = omp_get_max_threads();
+#endif
+    /* per-thread partial sums: dB, dC, dB_r, dC_r, dA, dA_r, dDskip, the two bias sums */
+    const size_t part = 4 * n_bc + 2 * (size_t)(D * N) + 3 * (size_t)D;
+    double *parts = (double *)calloc((size_t)nthr * part, sizeof(double));
+    if (!parts) return -1;
+    int fail = 0;
+
+#pragma omp parallel num_threads(nthr)
+    {
+        int tid = 0;
+#ifdef _OPENMP
+        tid = omp_get_thread_num();
+#endif
+        double *my_dB = parts + (size_t)tid * part;
+        double *my_dC = my_dB + n_bc;
+        double *my_dBr = my_dC + n_bc;
+        double *my_dCr = my_dBr + n_bc;
+        double *my_dA = my_dCr + n_bc;
+        double *my_dAr = my_dA + D * N;
+        double *my_dD = my_dAr + D * N;
+        double *my_dbias = my_dD + D;
+        double *my_dbias_r = my_dbias + D;
+        const size_t tn = (size_t)(T > 0 ? T : 1) * (size_t)N;
+        double *a = (double *)malloc(tn * sizeof(double));      /* a_t[n]        */
+        double *ar = (double *)malloc(tn * sizeof(double));     /* ar_t[n]       */
+        double *hp = (double *)malloc(tn * sizeof(double));     /* hf_{t-1}[n]   */
+        double *rn = (double *)malloc(tn * sizeof(double));     /* hr_{t+1}[n]   */
+        double *gr = (double *)malloc(tn * sizeof(double));     /* gr_t[n]       */
+        double *h = (double *)malloc((size_t)N * sizeof(double));
+        double *q = (double *)malloc((size_t)N * sizeof(double));
+        if (!a || !ar || !hp || !rn || !gr || !h || !q) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(static) collapse(2)
+        for (int64_t b = 0; b < batch; ++b) {
+            for (int64_t d = 0; d < D; ++d) {
+                if (fail) continue;
+                const double bias = dt_bias ? dt_bias[d] : 0.0, bias_r = dt_bias_r ? dt_bias_r[d] : 0.0;
+                /* forward recurrence: its decays and the state before every token */
+                for (int64_t t = 0; t < T; ++t) {
+                    if (t == 0 || (blocks && t % L == 0)) {
+                        for (int64_t n = 0; n < N; ++n) {
+                            if (blocks) h[n] = h0_blocks[((b * (nb + 1) + t / L) * D + d) * N + n];
+                            else h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
+                        }
+                    }
+                    const size_t ix = (size_t)((b * T + t) * D + d);
+                    const size_t ib = (size_t)((b * T + t) * N);
+                    const double dtv = step_size(ld(dt, ix, dtype), bias, dt_softplus);
+                    const double xv = ld(x, ix, dtype);
+                    for (int64_t n = 0; n < N; ++n) {
+                        const double at = exp(dtv * A[d * N + n]);
+                        a[t * N + n] = at;
+                        hp[t * N + n] = h[n];
+                        h[n] = at * h[n] + dtv * ld(Bm, ib + n, dtype) * xv;
+                    }
+                }
+                /* reverse recurrence in each block, on its own operands: the state after every token */
+                for (int64_t k = 0; k < nb; ++k) {
+                    for (int64_t n = 0; n < N; ++n) h[n] = 0.0;
+                    for (int64_t t = k * L + L - 1; t >= k * L; --t) {
+                        const size_t ix = (size_t)((b * T + t) * D + d);
+                        const size_t ib = (size_t)((b * T + t) * N);
+                        const double dtr = step_size(ld(dt_r, ix, dtype), bias_r, dt_softplus);
+                        const double xv = ld(x, ix, dtype);
+                        for (int64_t n = 0; n < N; ++n) {
+                            const double at = exp(dtr * A_r[d * N + n]);
+                            ar[t * N + n] = at;
+                            rn[t * N + n] = h[n];
+                            h[n] = at * h[n] + dtr * ld(B_r, ib + n, dtype) * xv;
+                        }
+                    }
+                }
+                /* adjoint of the reverse recurrence, left to right in each block */
+                for (int64_t k = 0; k < nb; ++k) {
+                    for (int64_t n = 0; n < N; ++n) q[n] = 0.0;
+                    for (int64_t t = k * L; t < k * L + L; ++t) {
+                        const size_t ix = (size_t)((b * T + t) * D + d);
+                        const size_t ib = (size_t)((b * T + t) * N);
+                        const double gy = z ? dy[ix] * silu(ld(z, ix, dtype)) : dy[ix];
+                        for (int64_t n = 0; n < N; ++n) {
+                            const double g = gy * ld(C_r, ib + n, dtype) + q[n];
+                            gr[t * N + n] = g;
+                            q[n] = ar[t * N + n] * g;
+                        }
+                    }
+                }
+                /* adjoint of the forward recurrence, right to left, and every gradient */
+                for (int64_t n = 0; n < N; ++n) q[n] = 0.0;
+                for (int64_t t = T - 1; t >= 0; --t) {
+                    const size_t ix = (size_t)((b * T + t) * D + d);
+                    const size_t ib = (size_t)((b * T + t) * N);
+                    const double v = ld(dt, ix, dtype) + bias, vr = ld(dt_r, ix, dtype) + bias_r;
+                    const double dtv = step_size(ld(dt, ix, dtype), bias, dt_softplus);
+                    const double dtr = step_size(ld(dt_r, ix, dtype), bias_r, dt_softplus);
+                    const double xv = ld(x, ix, dtype);
+                    const double zv = z ? ld(z, ix, dtype) : 0.0;
+                    const double gy = z ? dy[ix] * silu(zv) : dy[ix];
+                    const int block_end = (t + 1) % L == 0;
+                    if (blocks && block_end)
+                        for (int64_t n = 0; n < N; ++n) q[n] = 0.0;
+                    double sdt = 0.0, sdt_r = 0.0, sx = 0.0, ypre = Dskip[d] * xv;
+                    for (int64_t n = 0; n < N; ++n) {
+                        const double bv = ld(Bm, ib + n, dtype), cv = ld(Cm, ib + n, dtype);
+                        const double bvr = ld(B_r, ib + n, dtype), cvr = ld(C_r, ib + n, dtype);
+                        double gf = gy * cv + q[n];
+                        if (!blocks && block_end && dbounds)
+                            gf += dbounds[((b * (nb + 1) + (t + 1) / L) * D + d) * N + n];
+                        const double at = a[t * N + n], atr = ar[t * N + n];
+                        const double g_r = gr[t * N + n];
+                        const double hf_t = at * hp[t * N + n] + dtv * bv * xv;
+                        const double hr_t = atr * rn[t * N + n] + dtr * bvr * xv;
+                        /* forward operands */
+                        const double da = gf * hp[t * N + n];
+                        sdt += gf * bv * xv + da * at * A[d * N + n];
+                        my_dB[ib + n] += gf * dtv * xv;
+                        my_dC[ib + n] += gy * hf_t;
+                        my_dA[d * N + n] += da * at * dtv;
+                        /* reverse operands */
+                        const double da_r = g_r * rn[t * N + n];
+                        sdt_r += g_r * bvr * xv + da_r * atr * A_r[d * N + n];
+                        my_dBr[ib + n] += g_r * dtr * xv;
+                        my_dCr[ib + n] += gy * hr_t;
+                        my_dAr[d * N + n] += da_r * atr * dtr;
+                        sx += gf * dtv * bv + g_r * dtr * bvr;
+                        ypre += cv * hf_t + cvr * hr_t;
+                        q[n] = at * gf;
+                    }
+                    const double draw = dt_softplus ? sdt * sigmoid(v) : sdt;
+                    const double draw_r = dt_softplus ? sdt_r * sigmoid(vr) : sdt_r;
+                    if (ddt) ddt[ix] = draw;
+                    if (ddt_r) ddt_r[ix] = draw_r;
+                    my_dbias[d] += draw;
+                    my_dbias_r[d] += draw_r;
+                    if (dx) dx[ix] = sx + gy * Dskip[d];
+                    my_dD[d] += gy * xv;
+                    if (dz && z) {
+                        const double s = sigmoid(zv);
+                        dz[ix] = dy[ix] * ypre * s * (1.0 + zv * (1.0 - s));
+                    }
+                    if (blocks && t % L == 0 && dh0_blocks)
+                        for (int64_t n = 0; n < N; ++n)
+                            dh0_blocks[((b * (nb + 1) + t / L) * D + d) * N + n] = q[n];
+                }
+                if (!blocks && dh0)
+                    for (int64_t n = 0; n < N; ++n)
+                        dh0[(b * D + d) * N + n] =
+                            q[n] + (dbounds ? dbounds[((b * (nb + 1)) * D + d) * N + n] : 0.0);
+            }
+        }
+        free(a); free(ar); free(hp); free(rn); free(gr); free(h); free(q);
+    }
+    if (!fail) {
+        for (int th = 0; th < nthr; ++th) {
+            const double *p = parts + (size_t)th * part;
+            double *dst[] = {dB, dC, dB_r, dC_r};
+            for (int i = 0; i < 4; ++i)
+                if (dst[i]) for (size_t j = 0; j < n_bc; ++j) dst[i][j] += p[i * n_bc + j];
+            const double *pa = p + 4 * n_bc;
+            if (dA) for (int64_t i = 0; i < D * N; ++i) dA[i] += pa[i];
+            if (dA_r) for (int64_t i = 0; i < D * N; ++i) dA_r[i] += pa[D * N + i];
+            const double *pd = pa + 2 * D * N;
+            if (dDskip) for (int64_t i = 0; i < D; ++i) dDskip[i] += pd[i];
+            if (d_dt_bias) for (int64_t i = 0; i < D; ++i) d_dt_bias[i] += pd[D + i];
+            if (d_dt_bias_r) for (int64_t i = 0; i < D; ++i) d_dt_bias_r[i] += pd[2 * D + i];
         }
     }
     free(parts);

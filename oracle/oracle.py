@@ -56,6 +56,9 @@ def bind(lib):
     lib.oracle_scan_bwd_ex.argtypes = ([I, I, I, I, I, ctypes.c_int] + [P] * 6 + [ctypes.c_int]
                                        + [P] * 5 + [ctypes.c_int] + [P] * 11)
     lib.oracle_scan_bwd_ex.restype = ctypes.c_int
+    lib.oracle_scan_bwd_sep.argtypes = ([I, I, I, I, I, ctypes.c_int] + [P] * 6 + [ctypes.c_int]
+                                        + [P] * 5 + [ctypes.c_int] + [P] * 6 + [P] * 15)
+    lib.oracle_scan_bwd_sep.restype = ctypes.c_int
     return lib
 
 
@@ -223,7 +226,7 @@ def train_blocks(x, dt, B, C, A, Dskip, L, h0_blocks, dt_bias=None, dt_softplus=
 
 
 def scan_bwd(x, dt, B, C, A, Dskip, L, dy, h0=None, h0_blocks=None, dbounds=None, dt_bias=None,
-             dt_softplus=False, z=None):
+             dt_softplus=False, z=None, rev=None):
     """Reverse-mode gradients of the training forms.  Continuous form (the
     gradient of train_scan): forward from h0, optional dbounds = dJ/dh_bounds
     ([batch, T/L+1, D, N]).  Two-stream form (the gradient of train_blocks):
@@ -233,7 +236,9 @@ def scan_bwd(x, dt, B, C, A, Dskip, L, dy, h0=None, h0_blocks=None, dbounds=None
     With the forward's fusions (dt_bias, dt_softplus, z as in scan) ddt is the
     gradient of the dt stream (before bias and softplus), and the dict also
     holds d_dt_bias [D] (when dt_bias is given) and dz [batch, T, D] (when z
-    is given)."""
+    is given).  rev: separate reverse-direction operands {dt, B, C, A[, dt_bias]}
+    as in scan; their gradients come back as ddt_rev, dB_rev, dC_rev, dA_rev
+    (and d_dt_bias_rev when rev has a dt_bias)."""
     x, dt, B, C = _c(x), _c(dt), _c(B), _c(C)
     A = _c(A, np.float64)
     Dskip = _c(Dskip, np.float64)
@@ -266,6 +271,23 @@ def scan_bwd(x, dt, B, C, A, Dskip, L, dy, h0=None, h0_blocks=None, dbounds=None
         out["d_dt_bias"] = np.empty(D)
     if zz is not None:
         out["dz"] = np.empty((batch, T, D))
+    if rev is not None:
+        rv = _reverse(x, B, A, rev)
+        out.update(ddt_rev=np.empty((batch, T, D)), dB_rev=np.empty((batch, T, N)),
+                   dC_rev=np.empty((batch, T, N)), dA_rev=np.empty((D, N)))
+        if rv[4] is not None:
+            out["d_dt_bias_rev"] = np.empty(D)
+        rc = load().oracle_scan_bwd_sep(
+            batch, T, D, N, L, code, _ptr(x), _ptr(dt), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
+            int(blocks), _ptr(h0), _ptr(h0b), _ptr(dy), _ptr(dbounds), _ptr(bias),
+            int(bool(dt_softplus)), _ptr(zz), _ptr(rv[0]), _ptr(rv[1]), _ptr(rv[2]), _ptr(rv[3]),
+            _ptr(rv[4]), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dB"]), _ptr(out["dC"]),
+            _ptr(out["dA"]), _ptr(out["dDskip"]), _ptr(out.get("dh0")), _ptr(out.get("dh0_blocks")),
+            _ptr(out.get("dz")), _ptr(out.get("d_dt_bias")), _ptr(out["ddt_rev"]), _ptr(out["dB_rev"]),
+            _ptr(out["dC_rev"]), _ptr(out["dA_rev"]), _ptr(out.get("d_dt_bias_rev")))
+        if rc != 0:
+            raise ValueError("oracle_scan_bwd_sep rejected its arguments (rc=%d)" % rc)
+        return out
     rc = load().oracle_scan_bwd_ex(batch, T, D, N, L, code, _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
                                    _ptr(A), _ptr(Dskip), int(blocks), _ptr(h0), _ptr(h0b), _ptr(dy),
                                    _ptr(dbounds), _ptr(bias), int(bool(dt_softplus)), _ptr(zz),

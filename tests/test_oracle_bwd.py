@@ -315,3 +315,96 @@ def test_fused_gradients_without_fusion_arguments_are_the_plain_ones():
                         dt_softplus=False, z=None)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+# ---- gradients with separate reverse-direction operands (dt_r, B_r, C_r, A_r and
+# the reverse bias), pinned by central differences of the forward that uses them
+
+def sep_inputs(rng, batch, T, D, N, softplus, fused):
+    p = fused_inputs(rng, batch, T, D, N, softplus, fused, fused)
+    q = rand64(rng, batch, T, D, N)
+    p["dt_r"] = rng.normal(-1.0, 0.8, (batch, T, D)) if softplus else q["dt"]
+    p["B_r"], p["C_r"], p["A_r"] = q["B"], q["C"], q["A"]
+    if fused:
+        p["bias_r"] = rng.normal(0.0, 0.3 if softplus else 0.05, D)
+    return p
+
+
+def sep_rev(p):
+    return dict(dt=p["dt_r"], B=p["B_r"], C=p["C_r"], A=p["A_r"], dt_bias=p.get("bias_r"))
+
+
+SEP_MODES = [("plain", False, False), ("softplus_bias_gate", True, True)]
+SEP_PAIRS = [("dx", "x"), ("ddt", "dt"), ("dB", "B"), ("dC", "C"), ("dA", "A"), ("dDskip", "Dskip"),
+             ("ddt_rev", "dt_r"), ("dB_rev", "B_r"), ("dC_rev", "C_r"), ("dA_rev", "A_r")]
+
+
+@pytest.mark.parametrize("mode,softplus,fused", SEP_MODES)
+def test_separate_reverse_operands_continuous_gradient(mode, softplus, fused):
+    rng = np.random.default_rng(700 + len(mode))
+    batch, T, D, N, L = 2, 8, 3, 4, 4
+    p = sep_inputs(rng, batch, T, D, N, softplus, fused)
+    p["h0"] = rng.standard_normal((batch, D, N))
+    dy = rng.standard_normal((batch, T, D))
+    db = rng.standard_normal((batch, T // L + 1, D, N))
+
+    def J(q):
+        r = oracle.scan(q["x"], q["dt"], q["B"], q["C"], q["A"], q["Dskip"], L, h0=q["h0"], want_y=True,
+                        want_bounds=True, dt_bias=q.get("bias"), dt_softplus=softplus, z=q.get("z"),
+                        rev=sep_rev(q))
+        return float(np.sum(dy * r["y"]) + np.sum(db * r["bounds"]))
+
+    g = oracle.scan_bwd(p["x"], p["dt"], p["B"], p["C"], p["A"], p["Dskip"], L, dy, h0=p["h0"],
+                        dbounds=db, dt_bias=p.get("bias"), dt_softplus=softplus, z=p.get("z"),
+                        rev=sep_rev(p))
+    pairs = SEP_PAIRS + [("dh0", "h0")]
+    if fused:
+        pairs += [("d_dt_bias", "bias"), ("d_dt_bias_rev", "bias_r"), ("dz", "z")]
+    fd = central_differences(p, [pn for _, pn in pairs], J)
+    for gname, pname in pairs:
+        assert rel(g[gname], fd[pname]) < FD_TOL, (mode, gname, rel(g[gname], fd[pname]))
+
+
+@pytest.mark.parametrize("mode,softplus,fused", SEP_MODES)
+def test_separate_reverse_operands_two_stream_gradient(mode, softplus, fused):
+    rng = np.random.default_rng(800 + len(mode))
+    batch, T, D, N, L = 2, 8, 3, 4, 2
+    p = sep_inputs(rng, batch, T, D, N, softplus, fused)
+    p["h0_blocks"] = rng.standard_normal((batch, T // L + 1, D, N))
+    dy = rng.standard_normal((batch, T, D))
+
+    def J(q):
+        y = oracle.train_blocks(q["x"], q["dt"], q["B"], q["C"], q["A"], q["Dskip"], L, q["h0_blocks"],
+                                dt_bias=q.get("bias"), dt_softplus=softplus, z=q.get("z"), rev=sep_rev(q))
+        return float(np.sum(dy * y))
+
+    g = oracle.scan_bwd(p["x"], p["dt"], p["B"], p["C"], p["A"], p["Dskip"], L, dy,
+                        h0_blocks=p["h0_blocks"], dt_bias=p.get("bias"), dt_softplus=softplus,
+                        z=p.get("z"), rev=sep_rev(p))
+    pairs = SEP_PAIRS + [("dh0_blocks", "h0_blocks")]
+    if fused:
+        pairs += [("d_dt_bias", "bias"), ("d_dt_bias_rev", "bias_r"), ("dz", "z")]
+    fd = central_differences(p, [pn for _, pn in pairs], J)
+    for gname, pname in pairs:
+        assert rel(g[gname], fd[pname]) < FD_TOL, (mode, gname, rel(g[gname], fd[pname]))
+
+
+def test_separate_operands_equal_to_the_forwards_split_the_shared_gradients():
+    """With the reverse given the forward's own operands, each shared operand's
+    gradient is the sum of its two direction's parts (the shared routine's
+    result), and the gradients of the rest agree."""
+    rng = np.random.default_rng(900)
+    batch, T, D, N, L = 2, 16, 3, 4, 4
+    p = rand64(rng, batch, T, D, N)
+    dy = rng.standard_normal((batch, T, D))
+    bias = rng.normal(0.0, 0.3, D)
+    dtr = rng.normal(-1.0, 0.8, (batch, T, D))
+    shared = oracle.scan_bwd(p["x"], dtr, p["B"], p["C"], p["A"], p["Dskip"], L, dy, dt_bias=bias,
+                             dt_softplus=True)
+    sep = oracle.scan_bwd(p["x"], dtr, p["B"], p["C"], p["A"], p["Dskip"], L, dy, dt_bias=bias,
+                          dt_softplus=True, rev=dict(dt=dtr, B=p["B"], C=p["C"], A=p["A"], dt_bias=bias))
+    for k, kr in (("ddt", "ddt_rev"), ("dB", "dB_rev"), ("dC", "dC_rev"), ("dA", "dA_rev"),
+                  ("d_dt_bias", "d_dt_bias_rev")):
+        assert rel(sep[k] + sep[kr], shared[k]) < 1e-12, k
+    for k in ("dx", "dDskip", "dh0"):
+        assert rel(sep[k], shared[k]) < 1e-12, k

@@ -69,6 +69,14 @@ MUTANTS_BWD = {
     "bwd_ypre_missing_skip": ("double sdt = 0.0, sx = 0.0, ypre = Dskip[d] * xv;",
                               "double sdt = 0.0, sx = 0.0, ypre = 0.0;"),
     "bwd_dbias_before_softplus": ("my_dbias[d] += draw;", "my_dbias[d] += sdt;"),
+    # gradients with separate reverse operands
+    "sep_reverse_adjoint_uses_forward_C": ("const double g = gy * ld(C_r, ib + n, dtype) + q[n];",
+                                           "const double g = gy * ld(Cm, ib + n, dtype) + q[n];"),
+    "sep_dBr_uses_forward_dt": ("my_dBr[ib + n] += g_r * dtr * xv;", "my_dBr[ib + n] += g_r * dtv * xv;"),
+    "sep_dx_missing_reverse_term": ("sx += gf * dtv * bv + g_r * dtr * bvr;", "sx += gf * dtv * bv;"),
+    "sep_reverse_decay_uses_forward_A": ("const double at = exp(dtr * A_r[d * N + n]);",
+                                         "const double at = exp(dtr * A[d * N + n]);"),
+    "sep_dAr_missing_decay": ("my_dAr[d * N + n] += da_r * atr * dtr;", "my_dAr[d * N + n] += da_r * dtr;"),
 }
 
 MUTANTS_FUSED = {
