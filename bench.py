@@ -555,20 +555,15 @@ def train_main(args, wl, m, synth, torch):
     b.record(st)
     torch.cuda.synchronize()
     two_ms = a.elapsed_time(b) / args.steps
-    # the backward takes no separate reverse operands
-    if args.reverse_operands:
-        line = train_line(args, batch, D, T, L, dtype, nbytes, slots, ms_per_step, ev_ms,
-                          blocks_ms, full_ms, two_ms, None, None, None, torch, ns)
-        print(json.dumps(line), flush=True)
-        return 0
     # backward passes: continuous form (from the saved block states) and the
     # two-stream form; then one whole all-block training step, forward and
     # backward over both streams
     dy = synth.normal((batch, T, D), 1000 * sid + 8, dev, dtype)
-    wsb = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_TRAIN_BWD, L, ns, dtype)),
-                      dtype=torch.uint8, device=dev)
-    wsbb = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_BLOCKS_BWD, L, ns, dtype)),
-                       dtype=torch.uint8, device=dev)
+    sep = args.reverse_operands
+    wsb = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_TRAIN_BWD_REV if sep else m.OP_TRAIN_BWD,
+                                               L, ns, dtype)), dtype=torch.uint8, device=dev)
+    wsbb = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_BLOCKS_BWD_REV if sep else m.OP_BLOCKS_BWD,
+                                                L, ns, dtype)), dtype=torch.uint8, device=dev)
     m.train_scan(x, dt, Bm, Cm, A, Dskip, L, y=y, h_bounds=bnd, ws=ws, **fz)
     m.train_scan_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, ws=wsb, **fz)
     torch.cuda.synchronize()

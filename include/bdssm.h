@@ -97,7 +97,9 @@ typedef enum {
     BDSSM_OP_TRAIN = 1,       /* bdssm_train_scan */
     BDSSM_OP_FULL = 2,        /* bdssm_full_scan */
     BDSSM_OP_TRAIN_BWD = 3,   /* bdssm_train_scan_bwd */
-    BDSSM_OP_BLOCKS_BWD = 4   /* bdssm_train_scan_blocks_bwd */
+    BDSSM_OP_BLOCKS_BWD = 4,  /* bdssm_train_scan_blocks_bwd */
+    BDSSM_OP_TRAIN_BWD_REV = 5,   /* bdssm_train_scan_bwd with separate reverse operands */
+    BDSSM_OP_BLOCKS_BWD_REV = 6   /* bdssm_train_scan_blocks_bwd with separate reverse operands */
 } bdssm_op;
 
 /*
@@ -241,7 +243,11 @@ int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, 
  *   softplus: the step size's gradient times softplus'(v) = 1 / (1 + e^-v)).
  *   With z, dy is the gradient of the gated output y_pre silu(z); the gate's
  *   gradient dz = dy y_pre silu'(z) (y_pre recomputed) goes to grads->dz.
- *   Separate reverse operands (dt_rev) are rejected with BDSSM_ERR_SHAPE.
+ *   With separate reverse operands (dt_rev, B_rev, C_rev, A_rev, dt_bias_rev)
+ *   each gradient term splits by direction: ddt, dB, dC, dA belong to the
+ *   forward operands and grads->ddt_rev, dB_rev, dC_rev, dA_rev (and
+ *   d_dt_bias_rev) to the reverse ones; dx sums both directions.  The
+ *   workspace is then sized by BDSSM_OP_TRAIN_BWD_REV / BDSSM_OP_BLOCKS_BWD_REV.
  * grads: NULL, or the outputs of the fusion's gradients: dz [batch, T, D]
  *   stream dtype (required when fusion->z is given); d_dt_bias NULL or [D] fp32,
  *   the dt stream's gradient summed over batch and tokens (= dJ/d dt_bias).
@@ -249,6 +255,16 @@ int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, 
 typedef struct {
     void *dz;
     float *d_dt_bias;
+    /* With separate reverse operands (fusion->dt_rev): their gradients.
+     * ddt_rev [batch, T, D] and dB_rev, dC_rev [batch, T, N] (stream dtype)
+     * and dA_rev [D, N] fp32 are required; d_dt_bias_rev [D] fp32 or NULL.
+     * ddt_rev is the gradient of the dt_rev stream (through dt_bias_rev and
+     * softplus as in the forward). */
+    void *ddt_rev;
+    void *dB_rev;
+    void *dC_rev;
+    float *dA_rev;
+    float *d_dt_bias_rev;
 } bdssm_fusion_grads;
 
 int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,

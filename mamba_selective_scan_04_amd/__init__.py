@@ -10,5 +10,6 @@ from .bdssm import (  # noqa: F401
     BdssmError, load, version, status_str, workspace_bytes,
     prefill, block_step, commit, train_scan, train_scan_blocks, full_scan,
     train_scan_bwd, train_scan_blocks_bwd,
-    OP_PREFILL, OP_TRAIN, OP_FULL, OP_TRAIN_BWD, OP_BLOCKS_BWD, F32, BF16, LIB_PATH, EXPORTS,
+    OP_PREFILL, OP_TRAIN, OP_FULL, OP_TRAIN_BWD, OP_BLOCKS_BWD, OP_TRAIN_BWD_REV, OP_BLOCKS_BWD_REV,
+    F32, BF16, LIB_PATH, EXPORTS,
 )

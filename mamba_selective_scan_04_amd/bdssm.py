@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(HERE, "libbdssm.so")
 F32 = 0
 BF16 = 1
 OP_PREFILL, OP_TRAIN, OP_FULL, OP_TRAIN_BWD, OP_BLOCKS_BWD = 0, 1, 2, 3, 4
+OP_TRAIN_BWD_REV, OP_BLOCKS_BWD_REV = 5, 6      # the backward with separate reverse operands
 EXPORTS = ("bdssm_prefill", "bdssm_block_step", "bdssm_commit", "bdssm_train_scan",
            "bdssm_train_scan_blocks", "bdssm_full_scan", "bdssm_train_scan_bwd",
            "bdssm_train_scan_blocks_bwd", "bdssm_workspace_bytes", "bdssm_status_str",
@@ -54,7 +55,9 @@ class Fusion(ctypes.Structure):
 
 
 class FusionGrads(ctypes.Structure):
-    _fields_ = [("dz", ctypes.c_void_p), ("d_dt_bias", ctypes.c_void_p)]
+    _fields_ = [("dz", ctypes.c_void_p), ("d_dt_bias", ctypes.c_void_p), ("ddt_rev", ctypes.c_void_p),
+                ("dB_rev", ctypes.c_void_p), ("dC_rev", ctypes.c_void_p), ("dA_rev", ctypes.c_void_p),
+                ("d_dt_bias_rev", ctypes.c_void_p)]
 
 
 _lib = None
@@ -319,16 +322,27 @@ def _grad_outputs(x, D, N):
 
 def _fusion_grads(x, D, fusion):
     """Outputs of the fused forward's gradients: dz when z is given, d_dt_bias
-    when dt_bias is -> (ctypes pointer or None, dict of the tensors)."""
+    when dt_bias is, and with separate reverse operands (rev) ddt_rev, dB_rev,
+    dC_rev, dA_rev (and d_dt_bias_rev when rev has a dt_bias)
+    -> (ctypes pointer or None, dict of the tensors)."""
     out = {}
     if fusion.get("z") is not None:
         out["dz"] = torch.empty_like(x)
     if fusion.get("dt_bias") is not None:
         out["d_dt_bias"] = torch.empty(D, dtype=torch.float32, device=x.device)
+    rev = fusion.get("rev")
+    if rev is not None:
+        out["ddt_rev"] = torch.empty_like(x)
+        out["dB_rev"] = torch.empty_like(rev["B"])
+        out["dC_rev"] = torch.empty_like(rev["C"])
+        out["dA_rev"] = torch.empty_like(rev["A"])
+        if rev.get("dt_bias") is not None:
+            out["d_dt_bias_rev"] = torch.empty(D, dtype=torch.float32, device=x.device)
     if not out:
         return None, out
     ptr = lambda t: None if t is None else t.data_ptr()
-    g = FusionGrads(ptr(out.get("dz")), ptr(out.get("d_dt_bias")))
+    g = FusionGrads(*[ptr(out.get(k)) for k in ("dz", "d_dt_bias", "ddt_rev", "dB_rev", "dC_rev",
+                                                 "dA_rev", "d_dt_bias_rev")])
     return ctypes.pointer(g), out
 
 
@@ -337,9 +351,10 @@ def train_scan_bwd(x, dt, B, C, A, Dskip, block_len, h_bounds, dy, d_bounds=None
     """Gradients of train_scan given dy (and dJ/dh_bounds) -> dict with dx, ddt,
     dB, dC (stream dtype), dA, dDskip (fp32) and dh_init (fp32 or None).
     h_bounds: the block states train_scan returned for the same inputs.
-    fusion: the forward's dt_bias / dt_softplus / z; ddt is then the gradient
-    of the raw dt stream, and the dict gains d_dt_bias (fp32 [D], with a bias)
-    and dz (with a gate)."""
+    fusion: the forward's dt_bias / dt_softplus / z / rev; ddt is then the
+    gradient of the raw dt stream, and the dict gains d_dt_bias (fp32 [D], with
+    a bias), dz (with a gate) and, with separate reverse operands, ddt_rev,
+    dB_rev, dC_rev, dA_rev (and d_dt_bias_rev)."""
     batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip)
     nb = T // block_len + 1
     _check(h_bounds, "h_bounds", torch.float32, (batch, nb, D, N))
@@ -349,7 +364,8 @@ def train_scan_bwd(x, dt, B, C, A, Dskip, block_len, h_bounds, dy, d_bounds=None
     dh = torch.empty(batch, D, N, dtype=torch.float32, device=x.device) if want_dh_init else None
     s = _shape(batch, D, N, block_len, code)
     if ws is None:
-        ws = _workspace(workspace_bytes(batch, D, T, OP_TRAIN_BWD, block_len, N, x.dtype), x.device)
+        op = OP_TRAIN_BWD_REV if fusion.get("rev") is not None else OP_TRAIN_BWD
+        ws = _workspace(workspace_bytes(batch, D, T, op, block_len, N, x.dtype), x.device)
     fz = _fusion(x, D, **fusion)
     gz, extra = _fusion_grads(x, D, fusion)
     rc = load().bdssm_train_scan_bwd(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A),
@@ -375,7 +391,8 @@ def train_scan_blocks_bwd(x, dt, B, C, A, Dskip, block_len, h0_blocks, dy, want_
           if want_dh0_blocks else None)
     s = _shape(batch, D, N, block_len, code)
     if ws is None:
-        ws = _workspace(workspace_bytes(batch, D, T, OP_BLOCKS_BWD, block_len, N, x.dtype), x.device)
+        op = OP_BLOCKS_BWD_REV if fusion.get("rev") is not None else OP_BLOCKS_BWD
+        ws = _workspace(workspace_bytes(batch, D, T, op, block_len, N, x.dtype), x.device)
     fz = _fusion(x, D, **fusion)
     gz, extra = _fusion_grads(x, D, fusion)
     rc = load().bdssm_train_scan_blocks_bwd(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A),

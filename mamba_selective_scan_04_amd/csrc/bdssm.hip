@@ -34,7 +34,7 @@ using namespace bdssm_dev;
 
 namespace {
 
-constexpr int kVersion = 10500;   // 1.5.0
+constexpr int kVersion = 10600;   // 1.6.0
 
 // 256 CUs x 4 SIMDs x 8 resident waves (the chunk kernel fits in 64 VGPRs)
 constexpr int64_t kFineWaves = 256 * 4 * 8;
@@ -220,14 +220,16 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 //   both forms: part_bc [batch, nblk, T, 2N] (nblk = channel blocks of the
 //     block-local kernel), part_a [batch, nc, D, N],
 //     part_bias [batch, nc, D] (the dt_bias gradient of the fused backward),
-//     part_d [batch, nc, D]   (nc = coarse chunks of the backward pass).
+//     part_d [batch, nc, D]   (nc = coarse chunks of the backward pass);
+//   separate reverse operands: part_bc_r, part_a_r, part_bias_r (sizes as above).
 struct BwdWorkspace {
     float *agg_q, *agg_s, *q_in, *part_bc, *part_a, *part_d, *part_bias;
+    float *part_bc_r, *part_a_r, *part_bias_r;    // separate reverse operands only
     size_t bytes;
 };
 
 BwdWorkspace layout_bwd(void *base, int64_t batch, int64_t D, int64_t T, int64_t n_fine,
-                        int64_t nc, bool carry, int64_t N, int64_t nblk) {
+                        int64_t nc, bool carry, int64_t N, int64_t nblk, bool sep = false) {
     BwdWorkspace w{};
     size_t off = 0;
     auto take = [&](size_t n) -> float * {
@@ -245,6 +247,11 @@ BwdWorkspace layout_bwd(void *base, int64_t batch, int64_t D, int64_t T, int64_t
     w.part_a = take((size_t)batch * nc * D * N * sizeof(float));
     w.part_d = take((size_t)batch * nc * D * sizeof(float));
     w.part_bias = take((size_t)batch * nc * D * sizeof(float));
+    if (sep) {
+        w.part_bc_r = take((size_t)batch * nblk * T * 2 * N * sizeof(float));
+        w.part_a_r = take((size_t)batch * nc * D * N * sizeof(float));
+        w.part_bias_r = take((size_t)batch * nc * D * sizeof(float));
+    }
     w.bytes = off;
     return w;
 }
@@ -704,6 +711,12 @@ struct BwdArgs {
     const void *z = nullptr;
     void *dz = nullptr;
     float *part_bias = nullptr;
+    // separate reverse operands (sep), their gradients and partials
+    bool sep = false;
+    const void *dt_r = nullptr, *B_r = nullptr, *C_r = nullptr;
+    const float *A_r = nullptr, *dt_bias_r = nullptr;
+    void *ddt_r = nullptr;
+    float *part_bc_r = nullptr, *part_a_r = nullptr, *part_bias_r = nullptr;
 };
 
 // The backward's block-local kernel.  bwd_pair_kernel (two states per lane,
@@ -734,50 +747,57 @@ int64_t bwd_block_capacity(int64_t L, bool fused = false) {
 
 // The general backward path (bwd_general_kernel): block lengths outside the
 // 16-token group's divisors and state counts other than 16.
-bool bwd_general(int64_t L, int64_t N) { return !(wave_block(L) && N == kStates); }
+// Separate reverse operands always take it (bwd_general_kernel<..., 2>).
+bool bwd_general(int64_t L, int64_t N, bool sep = false) { return sep || !(wave_block(L) && N == kStates); }
 
 // channels per workgroup of the block-local kernel (the dB / dC partial blocks)
-int64_t bwd_channels(int64_t L, int64_t N, bool fused) {
-    return bwd_general(L, N) ? 4 * kWave / N : bwd_block_channels(L, fused);
+int64_t bwd_channels(int64_t L, int64_t N, bool fused, bool sep = false) {
+    if (sep) return bwd_general_waves<2>() * kWave / N;
+    return bwd_general(L, N) ? bwd_general_waves<0>() * kWave / N : bwd_block_channels(L, fused);
 }
 
 // chunk plans of the two backward forms, for the chosen kernel's geometry.
 // The general path's chunks are whole blocks (its own adjoint pre-pass and
 // the carry join them), as in the forward's general plan.
-bool bwd_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, bool fused, Plan *p) {
-    if (bwd_general(L, N)) return plan_general(batch, D, T, L, p);
+bool bwd_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, bool fused, Plan *p,
+              bool sep = false) {
+    if (bwd_general(L, N, sep)) return plan_general(batch, D, T, L, p);
     *p = make_plan(batch, D, T, kBwdPrepassWeight, bwd_block_channels(L, fused),
                    bwd_block_capacity(L, fused));
     return true;
 }
 bool bwd_blocks_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, int64_t *tc,
-                     int64_t *nc, bool fused) {
-    if (bwd_general(L, N)) return blocks_plan(batch, D, T, L, N, tc, nc, bwd_channels(L, N, fused), 3 * 256);
+                     int64_t *nc, bool fused, bool sep = false) {
+    if (bwd_general(L, N, sep))
+        return blocks_plan(batch, D, T, L, N, tc, nc, bwd_channels(L, N, fused, sep), 3 * 256);
     return blocks_plan(batch, D, T, L, kStates, tc, nc, bwd_block_channels(L, fused),
                        bwd_block_capacity(L, fused));
 }
 
 // dynamic LDS of bwd_general_kernel: hf and pr at every 16-token segment start
-size_t bwd_general_lds(int64_t L) { return (size_t)ceil_div(L, kGroup) * 4 * 2 * kWave * sizeof(float); }
+size_t bwd_general_lds(int64_t L, int nw) { return (size_t)ceil_div(L, kGroup) * nw * 2 * kWave * sizeof(float); }
+
+template <typename Tin, int kN, bool kBlockInit, int kF>
+void launch_bwd_general_v(const BwdArgs &a, int64_t batch, int64_t T, int64_t D, int64_t L, int64_t Tc,
+                          int nc, hipStream_t st) {
+    constexpr int NW = bwd_general_waves<kF>();
+    const dim3 g((unsigned)ceil_div(D, NW * kWave / kN), (unsigned)nc, (unsigned)batch);
+    const BwdFuse<Tin> fz{a.dt_bias, a.dt_mode, (const Tin *)a.z, (Tin *)a.dz, a.part_bias,
+                          (const Tin *)a.dt_r, (const Tin *)a.B_r, (const Tin *)a.C_r, a.A_r, a.dt_bias_r,
+                          (Tin *)a.ddt_r, a.part_bc_r, a.part_a_r, a.part_bias_r};
+    hipLaunchKernelGGL((bwd_general_kernel<Tin, kN, kBlockInit, kF>), g, dim3(NW * kWave),
+                       bwd_general_lds(L, NW), st, (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B,
+                       (const Tin *)a.C, (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs,
+                       a.qin_cs, a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0,
+                       T, (int)D, (int)L, Tc, fz);
+}
 
 template <typename Tin, int kN, bool kBlockInit>
 void launch_bwd_general_k(const BwdArgs &a, int64_t batch, int64_t T, int64_t D, int64_t L, int64_t Tc,
                           int nc, hipStream_t st) {
-    const dim3 g((unsigned)ceil_div(D, 4 * kWave / kN), (unsigned)nc, (unsigned)batch);
-    const BwdFuse<Tin> fz{a.dt_bias, a.dt_mode, (const Tin *)a.z, (Tin *)a.dz, a.part_bias};
-    const size_t lds = bwd_general_lds(L);
-    if (a.fused)
-        hipLaunchKernelGGL((bwd_general_kernel<Tin, kN, kBlockInit, true>), g, dim3(4 * kWave), lds, st,
-                           (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
-                           (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
-                           a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0,
-                           T, (int)D, (int)L, Tc, fz);
-    else
-        hipLaunchKernelGGL((bwd_general_kernel<Tin, kN, kBlockInit, false>), g, dim3(4 * kWave), lds, st,
-                           (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
-                           (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
-                           a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0,
-                           T, (int)D, (int)L, Tc, fz);
+    if (a.sep) launch_bwd_general_v<Tin, kN, kBlockInit, 2>(a, batch, T, D, L, Tc, nc, st);
+    else if (a.fused) launch_bwd_general_v<Tin, kN, kBlockInit, 1>(a, batch, T, D, L, Tc, nc, st);
+    else launch_bwd_general_v<Tin, kN, kBlockInit, 0>(a, batch, T, D, L, Tc, nc, st);
 }
 
 template <typename Tin, bool kBlockInit>
@@ -862,15 +882,26 @@ void launch_bwd(int64_t L, const BwdArgs &a, int64_t batch, int64_t T, int64_t D
 template <typename Tin>
 void launch_bwd_reduce(const BwdWorkspace &w, void *dB, void *dC, float *dA, float *dDskip,
                        int64_t batch, int64_t T, int64_t D, int64_t L, int64_t N, int64_t nc,
-                       hipStream_t st, bool fused = false, float *d_bias = nullptr) {
+                       hipStream_t st, bool fused = false, float *d_bias = nullptr,
+                       const bdssm_fusion_grads *gr = nullptr) {
+    const bool sep = gr != nullptr;
     const int64_t nbc = batch * T * 2 * N;
+    const int nblk = (int)ceil_div(D, bwd_channels(L, N, fused, sep));
     hipLaunchKernelGGL((bc_reduce_kernel<Tin>), dim3((unsigned)ceil_div(nbc, 256)), dim3(256), 0, st,
-                       w.part_bc, (Tin *)dB, (Tin *)dC, (int)batch, T,
-                       (int)ceil_div(D, bwd_channels(L, N, fused)), (int)N);
+                       w.part_bc, (Tin *)dB, (Tin *)dC, (int)batch, T, nblk, (int)N);
     const bool nb = fused && d_bias != nullptr;
     hipLaunchKernelGGL(param_reduce_kernel, dim3((unsigned)ceil_div(D * (N + (nb ? 2 : 1)), 256)),
                        dim3(256), 0, st, w.part_a, w.part_d, dA, dDskip, (int)D, (int)(batch * nc),
                        nb ? w.part_bias : nullptr, nb ? d_bias : nullptr, (int)N);
+    if (sep) {
+        // the reverse operands' dB_r, dC_r, dA_r (and their bias gradient)
+        hipLaunchKernelGGL((bc_reduce_kernel<Tin>), dim3((unsigned)ceil_div(nbc, 256)), dim3(256), 0, st,
+                           w.part_bc_r, (Tin *)gr->dB_rev, (Tin *)gr->dC_rev, (int)batch, T, nblk, (int)N);
+        const bool nbr = gr->d_dt_bias_rev != nullptr;
+        hipLaunchKernelGGL(param_reduce_kernel, dim3((unsigned)ceil_div(D * (N + 2), 256)), dim3(256), 0, st,
+                           w.part_a_r, nullptr, gr->dA_rev, nullptr, (int)D, (int)(batch * nc),
+                           nbr ? w.part_bias_r : nullptr, nbr ? gr->d_dt_bias_rev : nullptr, (int)N);
+    }
 }
 
 // Forward state only over T tokens from h_init: h_final <- state after T.
@@ -964,30 +995,32 @@ const char *bdssm_status_str(int status) {
 
 size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T, int op) {
     if (check_shape(shape) != BDSSM_OK || T < 0 || T % shape->block_len != 0) return (size_t)-1;
-    if (op < BDSSM_OP_PREFILL || op > BDSSM_OP_BLOCKS_BWD) return (size_t)-1;
+    if (op < BDSSM_OP_PREFILL || op > BDSSM_OP_BLOCKS_BWD_REV) return (size_t)-1;
     const int64_t batch = shape->batch, D = shape->d_inner;
     if (batch == 0 || D == 0 || T == 0) return 0;
     const int64_t N = shape->d_state, L = shape->block_len;
     // the backward's plan depends on the kernel, which a fusion can change:
     // size for the larger of the two
-    if (op == BDSSM_OP_TRAIN_BWD) {
+    if (op == BDSSM_OP_TRAIN_BWD || op == BDSSM_OP_TRAIN_BWD_REV) {
+        const bool sep = op == BDSSM_OP_TRAIN_BWD_REV;
         size_t n = 0;
-        for (int fused = 0; fused < 2; ++fused) {
+        for (int fused = sep ? 1 : 0; fused < 2; ++fused) {
             Plan p;
-            if (!bwd_plan(batch, D, T, L, N, fused != 0, &p)) return (size_t)-1;
+            if (!bwd_plan(batch, D, T, L, N, fused != 0, &p, sep)) return (size_t)-1;
             const size_t m = layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, p.n_coarse > 1, N,
-                                        ceil_div(D, bwd_channels(L, N, fused != 0))).bytes;
+                                        ceil_div(D, bwd_channels(L, N, fused != 0, sep)), sep).bytes;
             n = m > n ? m : n;
         }
         return n;
     }
-    if (op == BDSSM_OP_BLOCKS_BWD) {
+    if (op == BDSSM_OP_BLOCKS_BWD || op == BDSSM_OP_BLOCKS_BWD_REV) {
+        const bool sep = op == BDSSM_OP_BLOCKS_BWD_REV;
         size_t n = 0;
-        for (int fused = 0; fused < 2; ++fused) {
+        for (int fused = sep ? 1 : 0; fused < 2; ++fused) {
             int64_t tc, nc;
-            if (!bwd_blocks_plan(batch, D, T, L, N, &tc, &nc, fused != 0)) return (size_t)-1;
+            if (!bwd_blocks_plan(batch, D, T, L, N, &tc, &nc, fused != 0, sep)) return (size_t)-1;
             const size_t m = layout_bwd(nullptr, batch, D, T, 1, nc, false, N,
-                                        ceil_div(D, bwd_channels(L, N, fused != 0))).bytes;
+                                        ceil_div(D, bwd_channels(L, N, fused != 0, sep)), sep).bytes;
             n = m > n ? m : n;
         }
         return n;
@@ -1267,6 +1300,13 @@ int check_bwd(const bdssm_shape *shape, int64_t T, const void *x, const void *dt
     return BDSSM_OK;
 }
 
+// Zero the reverse operands' parameter gradients of an empty call.
+int zero_bwd_rev(const bdssm_fusion_grads *g, int64_t D, int64_t N, hipStream_t st) {
+    int rc = copy_or_zero(nullptr, g->dA_rev, D * N, st);
+    if (!rc && g->d_dt_bias_rev) rc = copy_or_zero(nullptr, g->d_dt_bias_rev, D, st);
+    return rc;
+}
+
 // Zero the parameter gradients (and the start-state gradient) of an empty call.
 int zero_bwd(int64_t D, int64_t N, float *dA, float *dDskip, float *dh, int64_t dh_n, hipStream_t st) {
     int rc = D > 0 ? copy_or_zero(nullptr, dA, D * N, st) : BDSSM_OK;
@@ -1288,9 +1328,11 @@ int resolve_bwd_fusion(const bdssm_fusion *f, bdssm_fusion_grads *g, const bdssm
                        int64_t T, std::initializer_list<Range> ins, std::initializer_list<Range> outs,
                        BwdArgs *a) {
     a->fused = false;
-    if (f != nullptr && f->dt_rev != nullptr) return BDSSM_ERR_SHAPE;
+    a->sep = false;
     const float *bias = f ? f->dt_bias : nullptr;
-    const int mode = (f && f->dt_softplus) ? kDtSoftplus : (bias ? kDtBias : kDtPlain);
+    // a reverse bias alone also selects the bias form (the forward's bias is then zero)
+    const bool rbias = f && f->dt_rev != nullptr && f->dt_bias_rev != nullptr;
+    const int mode = (f && f->dt_softplus) ? kDtSoftplus : ((bias || rbias) ? kDtBias : kDtPlain);
     const void *z = f ? f->z : nullptr;
     void *dz = g ? g->dz : nullptr;
     float *dbias = g ? g->d_dt_bias : nullptr;
@@ -1319,6 +1361,50 @@ int resolve_bwd_fusion(const bdssm_fusion *f, bdssm_fusion_grads *g, const bdssm
     a->dt_mode = mode;
     a->z = z;
     a->dz = dz;
+    if (f == nullptr || f->dt_rev == nullptr) return BDSSM_OK;
+    // separate reverse operands: their inputs and the gradients they need
+    if (f->B_rev == nullptr || f->C_rev == nullptr || f->A_rev == nullptr) return BDSSM_ERR_NULL;
+    if (g == nullptr || g->ddt_rev == nullptr || g->dB_rev == nullptr || g->dC_rev == nullptr ||
+        g->dA_rev == nullptr)
+        return BDSSM_ERR_NULL;
+    const size_t nbc = (size_t)s->batch * T * s->d_state * esize(s);
+    const size_t npar = (size_t)s->d_inner * s->d_state * 4;
+    const void *pr[] = {f->dt_rev, f->B_rev, f->C_rev, f->A_rev, f->dt_bias_rev, g->ddt_rev, g->dB_rev,
+                        g->dC_rev, g->dA_rev, g->d_dt_bias_rev};
+    for (const void *p : pr)
+        if (!aligned16(p)) return BDSSM_ERR_ALIGN;
+    const Range rin[] = {{f->dt_rev, ntok}, {f->B_rev, nbc}, {f->C_rev, nbc}, {f->A_rev, npar},
+                         {f->dt_bias_rev, (size_t)s->d_inner * 4}};
+    const Range rout[] = {{g->ddt_rev, ntok}, {g->dB_rev, nbc}, {g->dC_rev, nbc}, {g->dA_rev, npar},
+                          {g->d_dt_bias_rev, (size_t)s->d_inner * 4}};
+    for (const Range &o : rout) {
+        for (const Range &i : ins)
+            if (overlaps(o, i)) return BDSSM_ERR_ALIAS;
+        for (const Range &i : fin)
+            if (overlaps(o, i)) return BDSSM_ERR_ALIAS;
+        for (const Range &i : rin)
+            if (overlaps(o, i)) return BDSSM_ERR_ALIAS;
+        for (const Range &o2 : outs)
+            if (overlaps(o, o2)) return BDSSM_ERR_ALIAS;
+        for (const Range &o2 : fout)
+            if (overlaps(o, o2)) return BDSSM_ERR_ALIAS;
+        for (const Range &o2 : rout)
+            if (&o2 != &o && overlaps(o, o2)) return BDSSM_ERR_ALIAS;
+    }
+    for (const Range &i : rin) {
+        for (const Range &o : outs)
+            if (overlaps(o, i)) return BDSSM_ERR_ALIAS;
+        for (const Range &o : fout)
+            if (overlaps(o, i)) return BDSSM_ERR_ALIAS;
+    }
+    a->sep = true;
+    a->fused = true;
+    a->dt_r = f->dt_rev;
+    a->B_r = f->B_rev;
+    a->C_r = f->C_rev;
+    a->A_r = f->A_rev;
+    a->dt_bias_r = f->dt_bias_rev;
+    a->ddt_r = g->ddt_rev;
     return BDSSM_OK;
 }
 
@@ -1358,29 +1444,33 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
     if (batch == 0 || D == 0 || T == 0) {
         rc = zero_bwd(D, N, dA, dDskip, dh_init, batch * D * N, st);
         if (!rc && d_bias && D > 0) rc = copy_or_zero(nullptr, d_bias, D, st);
+        if (!rc && a.sep && D > 0) rc = zero_bwd_rev(grads, D, N, st);
         if (rc || dh_init == nullptr || d_bounds == nullptr || batch == 0 || D == 0) return rc;
         // T == 0: the only gradient of the start state is its own bound
         return copy_or_zero(d_bounds, dh_init, batch * D * N, st);
     }
     if (!aligned16(ws)) return BDSSM_ERR_ALIGN;
-    const bool general = bwd_general(L, N);
+    const bool general = bwd_general(L, N, a.sep);
     Plan p;
-    if (!bwd_plan(batch, D, T, L, N, a.fused, &p)) return BDSSM_ERR_SHAPE;
+    if (!bwd_plan(batch, D, T, L, N, a.fused, &p, a.sep)) return BDSSM_ERR_SHAPE;
     const bool carry = p.n_coarse > 1;
-    const int64_t nblk = ceil_div(D, bwd_channels(L, N, a.fused));
-    const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, carry, N, nblk);
+    const int64_t nblk = ceil_div(D, bwd_channels(L, N, a.fused, a.sep));
+    const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, carry, N, nblk, a.sep);
     if (ws == nullptr || ws_bytes < probe.bytes) return BDSSM_ERR_WORKSPACE;
     if (!ws_clear(ws, probe.bytes, {{x, ntok}, {dt, ntok}, {B, nbc}, {C, nbc}, {dy, ntok},
                                     {h_bounds, nbnd}, {d_bounds, nbnd}, {dx, ntok}, {ddt, ntok},
                                     {dB, nbc}, {dC, nbc}, {dA, npar}, {dDskip, (size_t)D * 4},
                                     {dh_init, nstate}, {A, npar}, {Dskip, (size_t)D * 4}}))
         return BDSSM_ERR_ALIAS;
-    const BwdWorkspace w = layout_bwd(ws, batch, D, T, p.n_fine, p.n_coarse, carry, N, nblk);
+    const BwdWorkspace w = layout_bwd(ws, batch, D, T, p.n_fine, p.n_coarse, carry, N, nblk, a.sep);
     const int64_t hs = D * N;
     a.part_bc = w.part_bc;
     a.part_a = w.part_a;
     a.part_d = w.part_d;
     a.part_bias = w.part_bias;
+    a.part_bc_r = w.part_bc_r;
+    a.part_a_r = w.part_a_r;
+    a.part_bias_r = w.part_bias_r;
     const int64_t Tc = carry ? p.fine_len * p.per_coarse : p.fine_len * p.n_fine;
     const bool bf = shape->dtype == BDSSM_BF16;
     if (carry) {
@@ -1415,11 +1505,13 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
     if (bf) {
         if (general) launch_bwd_general<uint16_t, false>(N, a, batch, T, D, L, Tc, nc, st);
         else launch_bwd<uint16_t, false>(L, a, batch, T, D, Tc, nc, st);
-        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias);
+        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias,
+                                    a.sep ? grads : nullptr);
     } else {
         if (general) launch_bwd_general<float, false>(N, a, batch, T, D, L, Tc, nc, st);
         else launch_bwd<float, false>(L, a, batch, T, D, Tc, nc, st);
-        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias);
+        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias,
+                                 a.sep ? grads : nullptr);
     }
     return launch_status();
 }
@@ -1456,33 +1548,39 @@ int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void 
     if (batch == 0 || D == 0 || T == 0) {
         rc = zero_bwd(D, N, dA, dDskip, dh0_blocks, batch * D * N, st);
         if (!rc && d_bias && D > 0) rc = copy_or_zero(nullptr, d_bias, D, st);
+        if (!rc && a.sep && D > 0) rc = zero_bwd_rev(grads, D, N, st);
         return rc;
     }
     if (!aligned16(ws)) return BDSSM_ERR_ALIGN;
-    const bool general = bwd_general(L, N);
+    const bool general = bwd_general(L, N, a.sep);
     int64_t tc, nc;
-    if (!bwd_blocks_plan(batch, D, T, L, N, &tc, &nc, a.fused)) return BDSSM_ERR_SHAPE;
-    const int64_t nblk = ceil_div(D, bwd_channels(L, N, a.fused));
-    const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, 1, nc, false, N, nblk);
+    if (!bwd_blocks_plan(batch, D, T, L, N, &tc, &nc, a.fused, a.sep)) return BDSSM_ERR_SHAPE;
+    const int64_t nblk = ceil_div(D, bwd_channels(L, N, a.fused, a.sep));
+    const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, 1, nc, false, N, nblk, a.sep);
     if (ws == nullptr || ws_bytes < probe.bytes) return BDSSM_ERR_WORKSPACE;
     if (!ws_clear(ws, probe.bytes, {{x, ntok}, {dt, ntok}, {B, nbc}, {C, nbc}, {dy, ntok},
                                     {h0_blocks, nbnd}, {dx, ntok}, {ddt, ntok}, {dB, nbc},
                                     {dC, nbc}, {dA, npar}, {dDskip, (size_t)D * 4}, {dh0_blocks, nbnd},
                                     {A, npar}, {Dskip, (size_t)D * 4}}))
         return BDSSM_ERR_ALIAS;
-    const BwdWorkspace w = layout_bwd(ws, batch, D, T, 1, nc, false, N, nblk);
+    const BwdWorkspace w = layout_bwd(ws, batch, D, T, 1, nc, false, N, nblk, a.sep);
     a.part_bc = w.part_bc;
     a.part_a = w.part_a;
     a.part_d = w.part_d;
     a.part_bias = w.part_bias;
+    a.part_bc_r = w.part_bc_r;
+    a.part_a_r = w.part_a_r;
+    a.part_bias_r = w.part_bias_r;
     if (shape->dtype == BDSSM_BF16) {
         if (general) launch_bwd_general<uint16_t, true>(N, a, batch, T, D, L, tc, (int)nc, st);
         else launch_bwd<uint16_t, true>(L, a, batch, T, D, tc, (int)nc, st);
-        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias);
+        launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias,
+                                    a.sep ? grads : nullptr);
     } else {
         if (general) launch_bwd_general<float, true>(N, a, batch, T, D, L, tc, (int)nc, st);
         else launch_bwd<float, true>(L, a, batch, T, D, tc, (int)nc, st);
-        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias);
+        launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias,
+                                 a.sep ? grads : nullptr);
     }
     return launch_status();
 }

@@ -573,6 +573,12 @@ template <typename Tin> struct BwdFuse {
     const Tin *z;           // gate [batch, T, D] or null
     Tin *dz;                // [batch, T, D], written when z is given
     float *part_bias;       // [batch, chunks, D] or null
+    // separate reverse-direction operands (bwd_general_kernel<..., 2> only):
+    // inputs, the reverse dt stream's gradient and the reverse partials
+    const Tin *dt_r, *B_r, *C_r;
+    const float *A_r, *dt_bias_r;
+    Tin *ddt_r;
+    float *part_bc_r, *part_a_r, *part_bias_r;
 };
 
 // The logistic function of v from softplus(v) = sp: 1 - exp(-sp), with the
@@ -1079,22 +1085,29 @@ template <int kFrom, int kTo> __device__ __forceinline__ float lane_sum(float v,
 }
 
 // Block-local backward of the general path, one lane per (channel, state):
-// lane = kN cl + n, CW = 64 / kN channels per wave, 4 waves per workgroup.
+// lane = kN cl + n, CW = 64 / kN channels per wave, NW waves per workgroup.
 // Each block of the chunk (right to left) is walked twice: left to right for
 // hf and the reverse adjoint gr, keeping both at every 16-token segment start
-// (LDS, dynamic size 2 KB per segment), then segment by segment right to left:
-// the segment's hf before each token and gr are formed again from its
+// (LDS, dynamic size NW / 2 KB per segment), then segment by segment right to
+// left: the segment's hf before each token and gr are formed again from its
 // checkpoint into registers, and the right-to-left walk runs hr and the
 // forward adjoint with every gradient term, as in bwd_pair_kernel.  The
 // token rows of a segment are staged in LDS (x, dt, dy per wave, B and C
 // shared by the workgroup; widened, the step size and the gate's factors
-// formed once per element).  Sums: over the channel's
-// kN lanes by butterfly (dt, x, and y_pre for the gate), over the wave's
-// channels by butterfly and over the 4 waves in LDS (dB, dC: part_bc
-// [batch, ceil(D / (4 CW)), T, 2 kN]).  Arguments as in bwd_pair_kernel.
-// grid = (ceil(D / (4 CW)), chunks, batch), block = 256.
-template <typename Tin, int kN, bool kBlockInit, bool kFuse>
-__global__ __launch_bounds__(4 * kWave) void bwd_general_kernel(
+// formed once per element).  Sums: over the channel's kN lanes by butterfly
+// (dt, x, and y_pre for the gate), over the wave's channels by butterfly and
+// over the NW waves in LDS (dB, dC: part_bc [batch, ceil(D / (NW CW)), T,
+// 2 kN]).  Arguments as in bwd_pair_kernel.
+// kFuse: 0 plain, 1 the fusions (BwdFuse), 2 the fusions and separate reverse
+// operands: the reverse recurrence and its adjoint run on dt_r (own bias),
+// B_r, C_r, A_r, and every gradient term splits by direction (the reverse
+// operands' gradients go to ddt_r and the _r partials); two waves per
+// workgroup keep its LDS below 64 KB at kN = 32 and L = 256.
+// grid = (ceil(D / (NW CW)), chunks, batch), block = 64 NW.
+template <int kFuse> constexpr int bwd_general_waves() { return kFuse == 2 ? 2 : 4; }
+
+template <typename Tin, int kN, bool kBlockInit, int kFuse>
+__global__ __launch_bounds__(bwd_general_waves<kFuse>() * kWave) void bwd_general_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const Tin *__restrict__ Cm, const Tin *__restrict__ dy, const float *__restrict__ A,
     const float *__restrict__ Dskip, const float *__restrict__ h_start, const float *qin,
@@ -1103,20 +1116,23 @@ __global__ __launch_bounds__(4 * kWave) void bwd_general_kernel(
     float *__restrict__ part_d, float *__restrict__ dh0, int64_t T, int D, int L, int64_t Tc,
     BwdFuse<Tin> fz)
 {
+    constexpr int NW = bwd_general_waves<kFuse>();
+    constexpr bool kSep = kFuse == 2;
+    constexpr int NR = kSep ? 2 : 1;          // B / C row sets: forward (, reverse)
     constexpr int CW = kWave / kN;            // channels per wave
     constexpr int G = 16;                     // segment length
     constexpr int ES = sizeof(Tin);
     constexpr int NE = (G * CW + kWave - 1) / kWave;   // token-row elements per lane per stream
-    __shared__ float tx[4][G][CW], tdl[4][G][CW], tgy[4][G][CW], tzv[4][G][CW];
-    __shared__ float tb[G][kN], tc[G][kN];       // B / C rows, shared by the 4 waves
-    __shared__ float red[4][G][2 * kN];
-    extern __shared__ float ck[];             // [segments][4 waves][2][64]: hf, pr at segment starts
+    __shared__ float tx[NW][G][CW], tdl[NW][G][CW], tgy[NW][G][CW], tzv[NW][G][CW], tdr[NW][kSep ? G : 1][CW];
+    __shared__ float tb[NR][G][kN], tc[NR][G][kN];   // B / C rows, shared by the waves
+    __shared__ float red[NR][NW][G][2 * kN];
+    extern __shared__ float ck[];             // [segments][NW waves][2][64]: hf, pr at segment starts
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform(threadIdx.x >> 6);
     const int cl = lane / kN;
     const int n = lane % kN;
-    const int d_w0 = blockIdx.x * 4 * CW + w * CW;
+    const int d_w0 = blockIdx.x * NW * CW + w * CW;
     const int d_raw = d_w0 + cl;
     const bool live = d_raw < D;
     const int d = live ? d_raw : D - 1;
@@ -1130,11 +1146,13 @@ __global__ __launch_bounds__(4 * kWave) void bwd_general_kernel(
 
     const float ar = A[(int64_t)d * kN + n];
     const float a2 = ar * kLog2e;
+    const float arr = kSep ? fz.A_r[(int64_t)d * kN + n] : 0.f;
+    const float a2r = arr * kLog2e;
     const float dsk = Dskip[d];
     float q = 0.f;
     if (!kBlockInit && qin != nullptr && t_end < T)
         q = qin[(int64_t)b * qin_bs + (int64_t)c * qin_cs + (int64_t)d * kN + n];
-    float dA_acc = 0.f, dD_acc = 0.f, bias_acc = 0.f;
+    float dA_acc = 0.f, dD_acc = 0.f, bias_acc = 0.f, dAr_acc = 0.f, bias_r_acc = 0.f;
     auto state_idx = [&](int64_t blk) { return (((int64_t)b * (nbl + 1) + blk) * D + d) * kN + n; };
     if (kBlockInit && dh0 != nullptr && t_end == T && live) dh0[state_idx(nbl)] = 0.f;
 
@@ -1142,13 +1160,23 @@ __global__ __launch_bounds__(4 * kWave) void bwd_general_kernel(
     const Rows<Tin> xs(x + first * D, len, D, 0);
     const Rows<Tin> dts(dt + first * D, len, D, 0);
     const Rows<Tin> ys(dy + first * D, len, D, 0);
-    const bool gate = kFuse && fz.z != nullptr;
+    const bool gate = kFuse != 0 && fz.z != nullptr;
     const Rows<Tin> zs((gate ? fz.z : dy) + first * D, len, D, 0);
+    const Rows<Tin> drs((kSep ? fz.dt_r : dt) + first * D, len, D, 0);
     const Rows<Tin> bs(Bm + first * kN, len, kN, 0);
     const Rows<Tin> cs(Cm + first * kN, len, kN, 0);
-    const bool sp_mode = kFuse && fz.dt_mode == kDtSoftplus;
+    const Rows<Tin> brs((kSep ? fz.B_r : Bm) + first * kN, len, kN, 0);
+    const Rows<Tin> crs((kSep ? fz.C_r : Cm) + first * kN, len, kN, 0);
+    const bool sp_mode = kFuse != 0 && fz.dt_mode == kDtSoftplus;
+    auto step_of = [&](float raw, float bias, bool ok) -> float {
+        if constexpr (kFuse != 0) {
+            if (fz.dt_mode == kDtSoftplus) return ok ? step_size<kDtSoftplus>(raw, bias) : 0.f;
+            if (fz.dt_mode == kDtBias) return ok ? step_size<kDtBias>(raw, bias) : 0.f;
+        }
+        return raw;
+    };
 
-    // stage the rows of tokens k0 .. k0 + cnt - 1 (chunk-local) for this wave
+    // stage the rows of tokens k0 .. k0 + cnt - 1 (chunk-local)
     auto stage = [&](int k0, int cnt) {
 #pragma unroll
         for (int j = 0; j < NE; ++j) {
@@ -1161,16 +1189,18 @@ __global__ __launch_bounds__(4 * kWave) void bwd_general_kernel(
                 float dl = widen(dts.load_at(off));
                 float gy = widen(ys.load_at(off));
                 float zv = 0.f;
-                if constexpr (kFuse) {
-                    const float bias = (fz.dt_bias != nullptr && ok) ? fz.dt_bias[d_w0 + ch] : 0.f;
-                    if (fz.dt_mode == kDtSoftplus) dl = ok ? step_size<kDtSoftplus>(dl, bias) : 0.f;
-                    else if (fz.dt_mode == kDtBias) dl = ok ? step_size<kDtBias>(dl, bias) : 0.f;
+                if constexpr (kFuse != 0) {
+                    dl = step_of(dl, (fz.dt_bias != nullptr && ok) ? fz.dt_bias[d_w0 + ch] : 0.f, ok);
                     if (gate) {
                         const float zf = widen(zs.load_at(off));
                         const float sg = __builtin_amdgcn_rcpf(1.f + fast_exp2(-zf * kLog2e));
                         zv = gy * (sg * __builtin_fmaf(zf, 1.f - sg, 1.f));     // dy silu'(z)
                         gy = gy * (zf * sg);                                     // dy silu(z)
                     }
+                }
+                if constexpr (kSep) {
+                    tdr[w][i][ch] = step_of(widen(drs.load_at(off)),
+                                            (fz.dt_bias_r != nullptr && ok) ? fz.dt_bias_r[d_w0 + ch] : 0.f, ok);
                 }
                 tx[w][i][ch] = xv;
                 tdl[w][i][ch] = dl;
@@ -1179,31 +1209,38 @@ __global__ __launch_bounds__(4 * kWave) void bwd_general_kernel(
             }
         }
 #pragma unroll
-        for (int j = 0; j < (G * kN + 4 * kWave - 1) / (4 * kWave); ++j) {
-            const int e = threadIdx.x + 4 * kWave * j;
+        for (int j = 0; j < (G * kN + NW * kWave - 1) / (NW * kWave); ++j) {
+            const int e = threadIdx.x + NW * kWave * j;
             if (e < G * kN) {
                 const int i = e / kN, col = e % kN;
                 const int32_t off = i < cnt ? col * ES + (k0 + i) * bs.pitch : kOutOfRange;
-                tb[i][col] = widen(bs.load_at(off));
-                tc[i][col] = widen(cs.load_at(off));
+                tb[0][i][col] = widen(bs.load_at(off));
+                tc[0][i][col] = widen(cs.load_at(off));
+                if constexpr (kSep) {
+                    tb[NR - 1][i][col] = widen(brs.load_at(off));
+                    tc[NR - 1][i][col] = widen(crs.load_at(off));
+                }
             }
         }
         __syncthreads();                              // the shared B / C rows are complete
     };
+    // the reverse recurrence's step and rows (the forward's without kSep)
+    auto rdl = [&](int i) { return kSep ? tdr[w][i & (kSep ? G - 1 : 0)][cl] : tdl[w][i][cl]; };
 
     float *pbc = part_bc + ((int64_t)b * gridDim.x + blockIdx.x) * T * (2 * kN);
-    float *ckw = ck + (int64_t)w * 2 * kWave;     // + seg * 4 * 2 * 64
+    float *pbcr = kSep ? fz.part_bc_r + ((int64_t)b * gridDim.x + blockIdx.x) * T * (2 * kN) : nullptr;
+    float *ckw = ck + (int64_t)w * 2 * kWave;     // + seg * NW * 2 * 64
 
     for (int kb0 = len - L; kb0 >= 0; kb0 -= L) {            // blocks, right to left
         const int64_t blk = (t_begin + kb0) / L;
-        // pass 1: hf and the reverse adjoint's carried pr = a gr, left to right
+        // pass 1: hf and the reverse adjoint's carried pr = a_r gr, left to right
         float hf = h_start[state_idx(blk)];
         float pr = 0.f;
         for (int sg = 0; sg < nseg; ++sg) {
             const int k0 = kb0 + sg * G;
             const int cnt = (L - sg * G < G) ? L - sg * G : G;
-            ckw[sg * 8 * kWave + n + kN * cl] = hf;
-            ckw[sg * 8 * kWave + kWave + n + kN * cl] = pr;
+            ckw[sg * NW * 2 * kWave + lane] = hf;
+            ckw[sg * NW * 2 * kWave + kWave + lane] = pr;
             if (sg == nseg - 1) break;                      // the last segment is formed again in pass 2
             __syncthreads();                                 // every wave is done with the last rows
             stage(k0, cnt);
@@ -1211,9 +1248,10 @@ __global__ __launch_bounds__(4 * kWave) void bwd_general_kernel(
             for (int i = 0; i < G; ++i) {
                 const float dl = tdl[w][i][cl], xv = tx[w][i][cl], gy = tgy[w][i][cl];
                 const float a = fast_exp2(dl * a2);
-                const float grv = __builtin_fmaf(gy, tc[i][n], pr);
-                hf = __builtin_fmaf(a, hf, dl * xv * tb[i][n]);
-                pr = a * grv;
+                const float a_r = kSep ? fast_exp2(rdl(i) * a2r) : a;
+                const float grv = __builtin_fmaf(gy, tc[NR - 1][i][n], pr);
+                hf = __builtin_fmaf(a, hf, dl * xv * tb[0][i][n]);
+                pr = a_r * grv;
             }
             asm volatile("" ::: "memory");
         }
@@ -1227,16 +1265,17 @@ __global__ __launch_bounds__(4 * kWave) void bwd_general_kernel(
             __syncthreads();                                 // rows and red of the last segment consumed
             stage(k0, cnt);
             float hp[G], gs[G];
-            float h = ckw[sg * 8 * kWave + n + kN * cl];
-            float p2 = ckw[sg * 8 * kWave + kWave + n + kN * cl];
+            float h = ckw[sg * NW * 2 * kWave + lane];
+            float p2 = ckw[sg * NW * 2 * kWave + kWave + lane];
 #pragma unroll
             for (int i = 0; i < G; ++i) {
                 const float dl = tdl[w][i][cl], xv = tx[w][i][cl], gy = tgy[w][i][cl];
                 const float a = fast_exp2(dl * a2);
+                const float a_r = kSep ? fast_exp2(rdl(i) * a2r) : a;
                 hp[i] = h;
-                gs[i] = __builtin_fmaf(gy, tc[i][n], p2);
-                h = __builtin_fmaf(a, h, dl * xv * tb[i][n]);
-                p2 = a * gs[i];
+                gs[i] = __builtin_fmaf(gy, tc[NR - 1][i][n], p2);
+                h = __builtin_fmaf(a, h, dl * xv * tb[0][i][n]);
+                p2 = a_r * gs[i];
             }
             // rows past cnt carry dt = 0, x = dy = 0: their decay is 1 and they
             // inject nothing, so h after the last row is the state after row cnt - 1
@@ -1244,40 +1283,79 @@ __global__ __launch_bounds__(4 * kWave) void bwd_general_kernel(
             for (int i = G - 1; i >= 0; --i) {
                 if (i < cnt) {
                     const float dl = tdl[w][i][cl], xv = tx[w][i][cl], gy = tgy[w][i][cl];
-                    const float bv = tb[i][n], cv = tc[i][n];
+                    const float bv = tb[0][i][n], cv = tc[0][i][n];
                     const float a = fast_exp2(dl * a2);
-                    const float u = dl * xv * bv;
-                    const float hr1 = hr;
-                    hr = __builtin_fmaf(a, hr1, u);
-                    const float gf = __builtin_fmaf(gy, cv, q);
-                    const float du = gf + gs[i];
-                    const float da = __builtin_fmaf(gf, hp[i], gs[i] * hr1);
-                    q = a * gf;
-                    const float daa = da * a;
-                    dA_acc = __builtin_fmaf(daa, dl, dA_acc);
                     // the state after token i (rows past cnt leave it unchanged)
                     const float hf_t = (i == G - 1) ? h : hp[(i + 1) & (G - 1)];
-                    const float hsum = hf_t + hr;
+                    const float gf = __builtin_fmaf(gy, cv, q);
+                    float sdt_l, sx_l, yp_l, vb_l, vc_l, sdtr_l = 0.f, vbr_l = 0.f, vcr_l = 0.f;
+                    if constexpr (kSep) {
+                        const float dlr = rdl(i), bvr = tb[NR - 1][i][n], cvr = tc[NR - 1][i][n];
+                        const float a_r = fast_exp2(dlr * a2r);
+                        const float hr1 = hr;
+                        hr = __builtin_fmaf(a_r, hr1, dlr * xv * bvr);
+                        const float daa = gf * hp[i] * a;               // forward operands
+                        dA_acc = __builtin_fmaf(daa, dl, dA_acc);
+                        sdt_l = __builtin_fmaf(gf * bv, xv, daa * ar);
+                        vb_l = gf * dl * xv;
+                        vc_l = gy * hf_t;
+                        const float daar = gs[i] * hr1 * a_r;           // reverse operands
+                        dAr_acc = __builtin_fmaf(daar, dlr, dAr_acc);
+                        sdtr_l = __builtin_fmaf(gs[i] * bvr, xv, daar * arr);
+                        vbr_l = gs[i] * dlr * xv;
+                        vcr_l = gy * hr;
+                        sx_l = __builtin_fmaf(gf * bv, dl, gs[i] * bvr * dlr);
+                        yp_l = __builtin_fmaf(cv, hf_t, cvr * hr);
+                    } else {
+                        const float u = dl * xv * bv;
+                        const float hr1 = hr;
+                        hr = __builtin_fmaf(a, hr1, u);
+                        const float du = gf + gs[i];
+                        const float daa = __builtin_fmaf(gf, hp[i], gs[i] * hr1) * a;
+                        dA_acc = __builtin_fmaf(daa, dl, dA_acc);
+                        const float hsum = hf_t + hr;
+                        sdt_l = __builtin_fmaf(du * bv, xv, daa * ar);
+                        sx_l = du * bv * dl;
+                        yp_l = cv * hsum;
+                        vb_l = du * dl * xv;
+                        vc_l = gy * hsum;
+                    }
+                    q = a * gf;
                     // sums over the channel's kN lanes
-                    float sdt = lane_sum<1, kN>(__builtin_fmaf(du * bv, xv, daa * ar), lane);
-                    float sx = lane_sum<1, kN>(du * bv * dl, lane);
+                    float sdt = lane_sum<1, kN>(sdt_l, lane);
+                    const float sx = lane_sum<1, kN>(sx_l, lane);
                     float yp = 0.f;
-                    if constexpr (kFuse) yp = lane_sum<1, kN>(cv * hsum, lane);
+                    if constexpr (kFuse != 0) yp = lane_sum<1, kN>(yp_l, lane);
+                    float sdtr = 0.f;
+                    if constexpr (kSep) sdtr = lane_sum<1, kN>(sdtr_l, lane);
                     // dB, dC of the token: sums over the wave's channels
-                    const float vb = lane_sum<kN, kWave>(du * dl * xv, lane);
-                    const float vc = lane_sum<kN, kWave>(gy * hsum, lane);
+                    const float vb = lane_sum<kN, kWave>(vb_l, lane);
+                    const float vc = lane_sum<kN, kWave>(vc_l, lane);
                     if (cl == 0) {
-                        red[w][i][n] = vb;
-                        red[w][i][kN + n] = vc;
+                        red[0][w][i][n] = vb;
+                        red[0][w][i][kN + n] = vc;
+                    }
+                    if constexpr (kSep) {
+                        const float vbr = lane_sum<kN, kWave>(vbr_l, lane);
+                        const float vcr = lane_sum<kN, kWave>(vcr_l, lane);
+                        if (cl == 0) {
+                            red[NR - 1][w][i][n] = vbr;
+                            red[NR - 1][w][i][kN + n] = vcr;
+                        }
                     }
                     const int64_t row = (first + k0 + i) * D + d;
                     if (n == 0 && live) {
                         dD_acc = __builtin_fmaf(gy, xv, dD_acc);
                         dx[row] = narrow<Tin>(__builtin_fmaf(gy, dsk, sx));
-                        if constexpr (kFuse) {
+                        if constexpr (kFuse != 0) {
                             if (sp_mode) sdt *= sigmoid_from_softplus(dl);
                             bias_acc += sdt;
                             if (gate) fz.dz[row] = narrow<Tin>(tzv[w][i][cl] * __builtin_fmaf(dsk, xv, yp));
+                        }
+                        if constexpr (kSep) {
+                            if (sp_mode) sdtr *= sigmoid_from_softplus(rdl(i));
+                            bias_r_acc += sdtr;
+                            fz.ddt_r[row] = narrow<Tin>(sdtr);
                         }
                         ddt[row] = narrow<Tin>(sdt);
                     }
@@ -1285,10 +1363,16 @@ __global__ __launch_bounds__(4 * kWave) void bwd_general_kernel(
                 }
             }
             __syncthreads();
-            // dB / dC of the segment: the 4 waves' sums in order
-            for (int o = threadIdx.x; o < cnt * 2 * kN; o += 4 * kWave) {
+            // dB / dC of the segment: the waves' sums in order
+            for (int o = threadIdx.x; o < cnt * 2 * kN; o += NW * kWave) {
                 const int i = o / (2 * kN), j = o % (2 * kN);
-                pbc[(t_begin + k0 + i) * (2 * kN) + j] = ((red[0][i][j] + red[1][i][j]) + red[2][i][j]) + red[3][i][j];
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    float sum = red[r][0][i][j];
+#pragma unroll
+                    for (int v = 1; v < NW; ++v) sum += red[r][v][i][j];
+                    (r == 0 ? pbc : pbcr)[(t_begin + k0 + i) * (2 * kN) + j] = sum;
+                }
             }
         }
     }
@@ -1298,9 +1382,11 @@ __global__ __launch_bounds__(4 * kWave) void bwd_general_kernel(
     if (live) {
         const int64_t pc = (int64_t)b * gridDim.y + c;
         part_a[(pc * D + d) * kN + n] = dA_acc;
+        if constexpr (kSep) fz.part_a_r[(pc * D + d) * kN + n] = dAr_acc;
         if (n == 0) {
             part_d[pc * D + d] = dD_acc;
-            if (kFuse && fz.part_bias != nullptr) fz.part_bias[pc * D + d] = bias_acc;
+            if (kFuse != 0 && fz.part_bias != nullptr) fz.part_bias[pc * D + d] = bias_acc;
+            if (kSep && fz.part_bias_r != nullptr) fz.part_bias_r[pc * D + d] = bias_r_acc;
         }
     }
 }
@@ -1325,8 +1411,8 @@ __global__ __launch_bounds__(256) void bc_reduce_kernel(const float *__restrict_
     else dC[bt * N + j - N] = narrow<Tin>(s);
 }
 
-// dA [D,N], dDskip [D] and (when part_bias is given) the dt_bias gradient
-// [D]: sum the (batch, chunk) partials in order.
+// dA [D,N], dDskip [D] (when part_d is given) and (when part_bias is given)
+// the dt_bias gradient [D]: sum the (batch, chunk) partials in order.
 __global__ __launch_bounds__(256) void param_reduce_kernel(const float *__restrict__ part_a,
                                                            const float *__restrict__ part_d,
                                                            float *__restrict__ dA, float *__restrict__ dDskip,
@@ -1341,6 +1427,7 @@ __global__ __launch_bounds__(256) void param_reduce_kernel(const float *__restri
         for (int k = 0; k < n_parts; ++k) s += part_a[(int64_t)k * na + i];
         dA[i] = s;
     } else if (i < na + D) {
+        if (part_d == nullptr || dDskip == nullptr) return;
         const int64_t dd = i - na;
         float s = 0.f;
         for (int k = 0; k < n_parts; ++k) s += part_d[(int64_t)k * D + dd];

@@ -28,7 +28,7 @@ def test_exports_match_header():
 
 
 def test_version_and_status_strings():
-    assert m.version() == 10500
+    assert m.version() == 10600
     for code in range(-7, 1):
         assert m.status_str(code) not in ("", "unknown status")
     assert m.status_str(-99) == "unknown status"
@@ -137,6 +137,11 @@ def test_workspace_sizes():
     assert m.workspace_bytes(1, 64, 512, m.OP_TRAIN_BWD, d_state=8) > 0
     assert m.workspace_bytes(1, 64, 512, m.OP_TRAIN_BWD, block_len=32) > 0
     assert m.workspace_bytes(2, 64, 512, m.OP_BLOCKS_BWD, block_len=256, d_state=32) > 0
+    # separate reverse operands: their own partials on top
+    assert m.workspace_bytes(8, 1536, 4096, m.OP_TRAIN_BWD_REV) > m.workspace_bytes(8, 1536, 4096, m.OP_TRAIN_BWD)
+    assert m.workspace_bytes(2, 64, 512, m.OP_BLOCKS_BWD_REV, block_len=32) > 0
+    with pytest.raises(ValueError):
+        m.workspace_bytes(1, 64, 512, 7)
     with pytest.raises(ValueError):
         m.workspace_bytes(1, 64, 512, m.OP_TRAIN_BWD, block_len=512)
     with pytest.raises(ValueError):
@@ -208,7 +213,17 @@ def test_fused_backward_argument_errors():
     s = shape(D=8)
     Fz, G = B.Fusion, B.FusionGrads
     bias, z = FAKE + 0x20000, FAKE + 0x21000
-    assert train_bwd(s, 16, fusion=Fz(None, 0, None, FAKE + 0x22000)) == -2   # no reverse operands
+    # separate reverse operands need B_rev, C_rev, A_rev and their gradient outputs
+    assert train_bwd(s, 16, fusion=Fz(None, 0, None, FAKE + 0x22000)) == -1
+    rv = Fz(None, 0, None, FAKE + 0x22000, FAKE + 0x25000, FAKE + 0x26000, FAKE + 0x27000)
+    assert train_bwd(s, 16, fusion=rv) == -1
+    assert train_bwd(s, 16, fusion=rv, grads=G(None, None, FAKE + 0x28000, FAKE + 0x29000)) == -1
+    full = G(None, None, FAKE + 0x28000, FAKE + 0x29000, FAKE + 0x2A000, FAKE + 0x2B000)
+    assert train_bwd(s, 16, fusion=rv, grads=full) == -5                     # reaches the workspace
+    assert train_bwd(s, 16, fusion=rv, grads=G(None, None, FAKE + 0x28000, FAKE + 0x29000, FAKE + 0x2A000,
+                                               FAKE + 0x25000)) == -7        # dA_rev on top of B_rev
+    assert train_bwd(s, 16, fusion=rv, grads=G(None, None, FAKE, FAKE + 0x29000, FAKE + 0x2A000,
+                                               FAKE + 0x2B000)) == -7        # ddt_rev on top of x
     assert train_bwd(s, 16, fusion=Fz(None, 0, z)) == -1                      # gate without dz
     assert train_bwd(s, 16, fusion=Fz(None, 0, z), grads=G(None, None)) == -1
     assert train_bwd(s, 16, fusion=Fz(None, 0, z), grads=G(MIS, None)) == -4

@@ -161,12 +161,3 @@ def test_fused_bwd_empty_sequence(dev):
     assert g["dz"].shape == (batch, 0, D)
     assert torch.equal(g["dh_init"], db[:, 0])
 
-
-def test_backward_rejects_separate_reverse_operands(dev):
-    batch, T, D, L = 1, 32, 64, 16
-    c = Case(batch, T, D, torch.float32, sid=56)
-    rev = dict(dt=c.dev["dt"].clone(), B=c.dev["B"].clone(), C=c.dev["C"].clone(), A=c.dev["A"].clone())
-    _, bnd = m.train_scan(*c.args(), L, want_bounds=True, rev=rev)
-    dy = seeded((batch, T, D), 5601)
-    with pytest.raises(m.BdssmError):
-        m.train_scan_bwd(*c.args(), L, bnd, dy, rev=rev)
