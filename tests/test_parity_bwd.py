@@ -212,3 +212,49 @@ def test_both_backward_kernels(dev, kernel, L, monkeypatch):
     rb = oracle.scan_bwd(*c.oracle_args(), L, to_np(dy), h0_blocks=to_np(h0b))
     check(gb, rb, GRADS, TOL[torch.bfloat16], kernel + " blocks")
     check(gb, rb, PARAM_GRADS + ("dh0_blocks",), STATE_TOL, kernel + " blocks")
+
+
+def test_training_step_graph_replays_match_eager(dev, monkeypatch):
+    """The whole all-block training step (both forms, forward and backward,
+    caller workspaces) captured in one HIP graph: every replay, with eager
+    work in between, reproduces the eager gradients bit for bit (the library
+    records no memset nodes and allocates nothing)."""
+    monkeypatch.setenv("BDSSM_CHUNK", "64")
+    batch, T, D, L = 2, 512, 96, 16
+    c = Case(batch, T, D, torch.bfloat16, sid=40, a_kind="random")
+    dy = seeded((batch, T, D), 4001, torch.bfloat16)
+    y = torch.empty_like(c.dev["x"])
+    bnd = torch.empty(batch, T // L + 1, D, N, device="cuda")
+    ws = torch.empty(max(1, m.workspace_bytes(batch, D, T, m.OP_TRAIN, L, N, torch.bfloat16)),
+                     dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(m.workspace_bytes(batch, D, T, m.OP_TRAIN_BWD, L, N, torch.bfloat16),
+                      dtype=torch.uint8, device="cuda")
+    wsbb = torch.empty(m.workspace_bytes(batch, D, T, m.OP_BLOCKS_BWD, L, N, torch.bfloat16),
+                       dtype=torch.uint8, device="cuda")
+
+    def step():
+        m.train_scan(*c.args(), L, y=y, h_bounds=bnd, ws=ws)
+        gn = m.train_scan_blocks_bwd(*c.args(), L, bnd, dy, want_dh0_blocks=True, ws=wsbb)
+        gc = m.train_scan_bwd(*c.args(), L, bnd, dy, d_bounds=gn["dh0_blocks"], want_dh_init=True, ws=wsb)
+        return gn, gc
+
+    ref_n, ref_c = step()
+    torch.cuda.synchronize()
+    ref = {("n", k): v.clone() for k, v in ref_n.items() if v is not None}
+    ref.update({("c", k): v.clone() for k, v in ref_c.items() if v is not None})
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out_n, out_c = step()
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for (form, k), v in ref.items():
+            got = (out_n if form == "n" else out_c)[k]
+            assert torch.equal(got, v), (form, k)
+        step()                                     # eager work between the replays
+        torch.cuda.synchronize()
