@@ -186,7 +186,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         return 2
 
