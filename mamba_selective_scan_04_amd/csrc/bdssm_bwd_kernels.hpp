@@ -1084,6 +1084,31 @@ template <int kFrom, int kTo> __device__ __forceinline__ float lane_sum(float v,
     else return lane_sum<2 * kFrom, kTo>(xor_add<kFrom>(v, lane), lane);
 }
 
+// The sum over each aligned group of kN lanes, in every lane of the group,
+// with DPP alone for kN <= 16 (no LDS-pipe swizzles): quad exchanges, then
+// half-row mirror (kN = 8) or row rotations by 4 and 8 (kN = 16: after the
+// quad sums, rotating a 16-lane row by 4 and then 8 adds up its four quads).
+template <int kN> __device__ __forceinline__ float group_sum(float v, int lane) {
+    auto dpp = [](float x, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, false));
+    };
+    using Q1 = std::integral_constant<int, 0xB1>;     // quad_perm [1,0,3,2]
+    using Q2 = std::integral_constant<int, 0x4E>;     // quad_perm [2,3,0,1]
+    using HM = std::integral_constant<int, 0x141>;    // row_half_mirror
+    using R4 = std::integral_constant<int, 0x124>;    // row_ror:4
+    using R8 = std::integral_constant<int, 0x128>;    // row_ror:8
+    v += dpp(v, Q1{});
+    if constexpr (kN >= 4) v += dpp(v, Q2{});
+    if constexpr (kN == 8) v += dpp(v, HM{});
+    if constexpr (kN >= 16) {
+        v += dpp(v, R4{});
+        v += dpp(v, R8{});
+    }
+    if constexpr (kN >= 32) v += xchg16(v);
+    (void)lane;
+    return v;
+}
+
 // Block-local backward of the general path, one lane per (channel, state):
 // lane = kN cl + n, CW = 64 / kN channels per wave, NW waves per workgroup.
 // Each block of the chunk (right to left) is walked twice: left to right for
@@ -1322,12 +1347,12 @@ __global__ __launch_bounds__(bwd_general_waves<kFuse>() * kWave) void bwd_genera
                     }
                     q = a * gf;
                     // sums over the channel's kN lanes
-                    float sdt = lane_sum<1, kN>(sdt_l, lane);
-                    const float sx = lane_sum<1, kN>(sx_l, lane);
+                    float sdt = group_sum<kN>(sdt_l, lane);
+                    const float sx = group_sum<kN>(sx_l, lane);
                     float yp = 0.f;
-                    if constexpr (kFuse != 0) yp = lane_sum<1, kN>(yp_l, lane);
+                    if constexpr (kFuse != 0) yp = group_sum<kN>(yp_l, lane);
                     float sdtr = 0.f;
-                    if constexpr (kSep) sdtr = lane_sum<1, kN>(sdtr_l, lane);
+                    if constexpr (kSep) sdtr = group_sum<kN>(sdtr_l, lane);
                     // dB, dC of the token: sums over the wave's channels
                     const float vb = lane_sum<kN, kWave>(vb_l, lane);
                     const float vc = lane_sum<kN, kWave>(vc_l, lane);
