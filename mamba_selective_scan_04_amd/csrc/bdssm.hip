@@ -221,15 +221,25 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 //     block-local kernel), part_a [batch, nc, D, N],
 //     part_bias [batch, nc, D] (the dt_bias gradient of the fused backward),
 //     part_d [batch, nc, D]   (nc = coarse chunks of the backward pass);
-//   separate reverse operands: part_bc_r, part_a_r, part_bias_r (sizes as above).
+//   separate reverse operands: part_bc_r, part_a_r, part_bias_r (sizes as above);
+//   long blocks (L a multiple of 16 above 16, 16 states): gstate
+//     [batch, ceil(T/16), 2, D, 16] (group_state_kernel).
 struct BwdWorkspace {
     float *agg_q, *agg_s, *q_in, *part_bc, *part_a, *part_d, *part_bias;
     float *part_bc_r, *part_a_r, *part_bias_r;    // separate reverse operands only
+    float *gstate;                                // long blocks only
     size_t bytes;
 };
 
+// block lengths that bwd_pair_kernel<..., 0, ...> takes: multiples of the
+// 16-token group above it, 16 states, shared operands
+bool long_block(int64_t L, int64_t N, bool sep = false) {
+    return !sep && N == kStates && L > kGroup && L % kGroup == 0;
+}
+
 BwdWorkspace layout_bwd(void *base, int64_t batch, int64_t D, int64_t T, int64_t n_fine,
-                        int64_t nc, bool carry, int64_t N, int64_t nblk, bool sep = false) {
+                        int64_t nc, bool carry, int64_t N, int64_t nblk, bool sep = false,
+                        int64_t L = 0) {
     BwdWorkspace w{};
     size_t off = 0;
     auto take = [&](size_t n) -> float * {
@@ -252,6 +262,7 @@ BwdWorkspace layout_bwd(void *base, int64_t batch, int64_t D, int64_t T, int64_t
         w.part_a_r = take((size_t)batch * nc * D * N * sizeof(float));
         w.part_bias_r = take((size_t)batch * nc * D * sizeof(float));
     }
+    if (long_block(L, N, sep)) w.gstate = take((size_t)batch * ceil_div(T, kGroup) * 2 * D * kStates * sizeof(float));
     w.bytes = off;
     return w;
 }
@@ -745,14 +756,26 @@ int64_t bwd_block_capacity(int64_t L, bool fused = false) {
     return bwd_use_wave(L, fused) ? kCoarseGroups : 3 * 256;
 }
 
+// Long blocks (multiples of 16 above 16 at 16 states) take bwd_pair_kernel
+// with group states from group_state_kernel; BDSSM_BWD_KERNEL=general sends
+// them to bwd_general_kernel instead (tests).
+bool bwd_long(int64_t L, int64_t N, bool sep = false) {
+    if (!long_block(L, N, sep)) return false;
+    const char *v = getenv("BDSSM_BWD_KERNEL");
+    return !(v != nullptr && v[0] == 'g');
+}
+
 // The general backward path (bwd_general_kernel): block lengths outside the
-// 16-token group's divisors and state counts other than 16.
+// 16-token group's divisors and its multiples, and state counts other than 16.
 // Separate reverse operands always take it (bwd_general_kernel<..., 2>).
-bool bwd_general(int64_t L, int64_t N, bool sep = false) { return sep || !(wave_block(L) && N == kStates); }
+bool bwd_general(int64_t L, int64_t N, bool sep = false) {
+    return sep || (!(wave_block(L) && N == kStates) && !bwd_long(L, N));
+}
 
 // channels per workgroup of the block-local kernel (the dB / dC partial blocks)
 int64_t bwd_channels(int64_t L, int64_t N, bool fused, bool sep = false) {
     if (sep) return bwd_general_waves<2>() * kWave / N;
+    if (bwd_long(L, N)) return kPairChannels;
     return bwd_general(L, N) ? bwd_general_waves<0>() * kWave / N : bwd_block_channels(L, fused);
 }
 
@@ -761,14 +784,14 @@ int64_t bwd_channels(int64_t L, int64_t N, bool fused, bool sep = false) {
 // the carry join them), as in the forward's general plan.
 bool bwd_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, bool fused, Plan *p,
               bool sep = false) {
-    if (bwd_general(L, N, sep)) return plan_general(batch, D, T, L, p);
+    if (bwd_general(L, N, sep) || bwd_long(L, N, sep)) return plan_general(batch, D, T, L, p);
     *p = make_plan(batch, D, T, kBwdPrepassWeight, bwd_block_channels(L, fused),
                    bwd_block_capacity(L, fused));
     return true;
 }
 bool bwd_blocks_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, int64_t *tc,
                      int64_t *nc, bool fused, bool sep = false) {
-    if (bwd_general(L, N, sep))
+    if (bwd_general(L, N, sep) || bwd_long(L, N, sep))
         return blocks_plan(batch, D, T, L, N, tc, nc, bwd_channels(L, N, fused, sep), 3 * 256);
     return blocks_plan(batch, D, T, L, kStates, tc, nc, bwd_block_channels(L, fused),
                        bwd_block_capacity(L, fused));
@@ -858,13 +881,13 @@ void launch_bwd_L(const BwdArgs &a, int64_t batch, int64_t T, int64_t D, int64_t
                            (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
                            (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
                            a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0,
-                           T, (int)D, Tc, fz);
+                           T, (int)D, Tc, fz, (const float *)nullptr, 0);
     else
         hipLaunchKernelGGL((bwd_pair_kernel<Tin, L, kBlockInit, false>), g, dim3(4 * kWave), 0, st,
                            (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
                            (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
                            a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0,
-                           T, (int)D, Tc, fz);
+                           T, (int)D, Tc, fz, (const float *)nullptr, 0);
 }
 
 template <typename Tin, bool kBlockInit>
@@ -877,6 +900,41 @@ void launch_bwd(int64_t L, const BwdArgs &a, int64_t batch, int64_t T, int64_t D
     case 8: launch_bwd_L<Tin, 8, kBlockInit>(a, batch, T, D, Tc, nc, st); break;
     default: launch_bwd_L<Tin, 16, kBlockInit>(a, batch, T, D, Tc, nc, st); break;
     }
+}
+
+template <typename Tin, int kDt>
+void launch_group_state_k(const BwdArgs &a, float *gstate, int64_t batch, int64_t T, int64_t D, int64_t L,
+                          hipStream_t st) {
+    const int64_t nbt = ceil_div(T, L);
+    hipLaunchKernelGGL((group_state_kernel<Tin, kDt>),
+                       dim3((unsigned)ceil_div(D, kWave), (unsigned)(nbt < 65535 ? nbt : 65535), (unsigned)batch),
+                       dim3(kWave), 0, st, (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B,
+                       (const Tin *)a.C, (const Tin *)a.dy, a.A, a.h_start, gstate, T, (int)D, (int)L,
+                       a.dt_bias, (const Tin *)a.z);
+}
+
+// long blocks: the group states, then bwd_pair_kernel over groups that
+// continue a block (chunks are whole blocks)
+template <typename Tin, bool kBlockInit>
+void launch_bwd_long(const BwdArgs &a, float *gstate, int64_t batch, int64_t T, int64_t D, int64_t L,
+                     int64_t Tc, int nc, hipStream_t st) {
+    if (a.dt_mode == kDtSoftplus) launch_group_state_k<Tin, kDtSoftplus>(a, gstate, batch, T, D, L, st);
+    else if (a.dt_mode == kDtBias) launch_group_state_k<Tin, kDtBias>(a, gstate, batch, T, D, L, st);
+    else launch_group_state_k<Tin, kDtPlain>(a, gstate, batch, T, D, L, st);
+    const dim3 g((unsigned)ceil_div(D, kPairChannels), (unsigned)nc, (unsigned)batch);
+    const BwdFuse<Tin> fz{a.dt_bias, a.dt_mode, (const Tin *)a.z, (Tin *)a.dz, a.part_bias};
+    if (a.fused)
+        hipLaunchKernelGGL((bwd_pair_kernel<Tin, 0, kBlockInit, true>), g, dim3(4 * kWave), 0, st,
+                           (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
+                           (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
+                           a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0,
+                           T, (int)D, Tc, fz, (const float *)gstate, (int)L);
+    else
+        hipLaunchKernelGGL((bwd_pair_kernel<Tin, 0, kBlockInit, false>), g, dim3(4 * kWave), 0, st,
+                           (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
+                           (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
+                           a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0,
+                           T, (int)D, Tc, fz, (const float *)gstate, (int)L);
 }
 
 template <typename Tin>
@@ -1008,7 +1066,7 @@ size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T, int op) {
             Plan p;
             if (!bwd_plan(batch, D, T, L, N, fused != 0, &p, sep)) return (size_t)-1;
             const size_t m = layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, p.n_coarse > 1, N,
-                                        ceil_div(D, bwd_channels(L, N, fused != 0, sep)), sep).bytes;
+                                        ceil_div(D, bwd_channels(L, N, fused != 0, sep)), sep, L).bytes;
             n = m > n ? m : n;
         }
         return n;
@@ -1020,7 +1078,7 @@ size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T, int op) {
             int64_t tc, nc;
             if (!bwd_blocks_plan(batch, D, T, L, N, &tc, &nc, fused != 0, sep)) return (size_t)-1;
             const size_t m = layout_bwd(nullptr, batch, D, T, 1, nc, false, N,
-                                        ceil_div(D, bwd_channels(L, N, fused != 0, sep)), sep).bytes;
+                                        ceil_div(D, bwd_channels(L, N, fused != 0, sep)), sep, L).bytes;
             n = m > n ? m : n;
         }
         return n;
@@ -1450,19 +1508,19 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
         return copy_or_zero(d_bounds, dh_init, batch * D * N, st);
     }
     if (!aligned16(ws)) return BDSSM_ERR_ALIGN;
-    const bool general = bwd_general(L, N, a.sep);
+    const bool general = bwd_general(L, N, a.sep), lng = bwd_long(L, N, a.sep);
     Plan p;
     if (!bwd_plan(batch, D, T, L, N, a.fused, &p, a.sep)) return BDSSM_ERR_SHAPE;
     const bool carry = p.n_coarse > 1;
     const int64_t nblk = ceil_div(D, bwd_channels(L, N, a.fused, a.sep));
-    const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, carry, N, nblk, a.sep);
+    const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, p.n_fine, p.n_coarse, carry, N, nblk, a.sep, L);
     if (ws == nullptr || ws_bytes < probe.bytes) return BDSSM_ERR_WORKSPACE;
     if (!ws_clear(ws, probe.bytes, {{x, ntok}, {dt, ntok}, {B, nbc}, {C, nbc}, {dy, ntok},
                                     {h_bounds, nbnd}, {d_bounds, nbnd}, {dx, ntok}, {ddt, ntok},
                                     {dB, nbc}, {dC, nbc}, {dA, npar}, {dDskip, (size_t)D * 4},
                                     {dh_init, nstate}, {A, npar}, {Dskip, (size_t)D * 4}}))
         return BDSSM_ERR_ALIAS;
-    const BwdWorkspace w = layout_bwd(ws, batch, D, T, p.n_fine, p.n_coarse, carry, N, nblk, a.sep);
+    const BwdWorkspace w = layout_bwd(ws, batch, D, T, p.n_fine, p.n_coarse, carry, N, nblk, a.sep, L);
     const int64_t hs = D * N;
     a.part_bc = w.part_bc;
     a.part_a = w.part_a;
@@ -1477,7 +1535,7 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
         // adjoint aggregates of the fine chunks right of the first coarse chunk,
         // then the adjoint entering each fine chunk from its right end
         const int c_first = p.per_coarse, n_launch = p.n_fine - p.per_coarse;
-        if (general) {
+        if (general || lng) {
             if (bf)
                 launch_adjoint_general<uint16_t>(N, dt, dy, C, A, d_bounds, w.agg_q, w.agg_s, batch, T, D, L,
                                                  p.fine_len, p.n_fine, c_first, n_launch, a.dt_mode, a.dt_bias,
@@ -1504,11 +1562,13 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
     const int nc = carry ? p.n_coarse : 1;
     if (bf) {
         if (general) launch_bwd_general<uint16_t, false>(N, a, batch, T, D, L, Tc, nc, st);
+        else if (lng) launch_bwd_long<uint16_t, false>(a, w.gstate, batch, T, D, L, Tc, nc, st);
         else launch_bwd<uint16_t, false>(L, a, batch, T, D, Tc, nc, st);
         launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias,
                                     a.sep ? grads : nullptr);
     } else {
         if (general) launch_bwd_general<float, false>(N, a, batch, T, D, L, Tc, nc, st);
+        else if (lng) launch_bwd_long<float, false>(a, w.gstate, batch, T, D, L, Tc, nc, st);
         else launch_bwd<float, false>(L, a, batch, T, D, Tc, nc, st);
         launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias,
                                  a.sep ? grads : nullptr);
@@ -1552,18 +1612,18 @@ int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void 
         return rc;
     }
     if (!aligned16(ws)) return BDSSM_ERR_ALIGN;
-    const bool general = bwd_general(L, N, a.sep);
+    const bool general = bwd_general(L, N, a.sep), lng = bwd_long(L, N, a.sep);
     int64_t tc, nc;
     if (!bwd_blocks_plan(batch, D, T, L, N, &tc, &nc, a.fused, a.sep)) return BDSSM_ERR_SHAPE;
     const int64_t nblk = ceil_div(D, bwd_channels(L, N, a.fused, a.sep));
-    const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, 1, nc, false, N, nblk, a.sep);
+    const BwdWorkspace probe = layout_bwd(nullptr, batch, D, T, 1, nc, false, N, nblk, a.sep, L);
     if (ws == nullptr || ws_bytes < probe.bytes) return BDSSM_ERR_WORKSPACE;
     if (!ws_clear(ws, probe.bytes, {{x, ntok}, {dt, ntok}, {B, nbc}, {C, nbc}, {dy, ntok},
                                     {h0_blocks, nbnd}, {dx, ntok}, {ddt, ntok}, {dB, nbc},
                                     {dC, nbc}, {dA, npar}, {dDskip, (size_t)D * 4}, {dh0_blocks, nbnd},
                                     {A, npar}, {Dskip, (size_t)D * 4}}))
         return BDSSM_ERR_ALIAS;
-    const BwdWorkspace w = layout_bwd(ws, batch, D, T, 1, nc, false, N, nblk, a.sep);
+    const BwdWorkspace w = layout_bwd(ws, batch, D, T, 1, nc, false, N, nblk, a.sep, L);
     a.part_bc = w.part_bc;
     a.part_a = w.part_a;
     a.part_d = w.part_d;
@@ -1573,11 +1633,13 @@ int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void 
     a.part_bias_r = w.part_bias_r;
     if (shape->dtype == BDSSM_BF16) {
         if (general) launch_bwd_general<uint16_t, true>(N, a, batch, T, D, L, tc, (int)nc, st);
+        else if (lng) launch_bwd_long<uint16_t, true>(a, w.gstate, batch, T, D, L, tc, (int)nc, st);
         else launch_bwd<uint16_t, true>(L, a, batch, T, D, tc, (int)nc, st);
         launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias,
                                     a.sep ? grads : nullptr);
     } else {
         if (general) launch_bwd_general<float, true>(N, a, batch, T, D, L, tc, (int)nc, st);
+        else if (lng) launch_bwd_long<float, true>(a, w.gstate, batch, T, D, L, tc, (int)nc, st);
         else launch_bwd<float, true>(L, a, batch, T, D, tc, (int)nc, st);
         launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias,
                                  a.sep ? grads : nullptr);

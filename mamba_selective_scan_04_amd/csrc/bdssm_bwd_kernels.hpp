@@ -596,14 +596,19 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
     int64_t qin_bs, int64_t qin_cs, const float *__restrict__ dbounds, Tin *__restrict__ dx,
     Tin *__restrict__ ddt, float *__restrict__ part_bc, float *__restrict__ part_a,
     float *__restrict__ part_d, float *__restrict__ dh0, int64_t T, int D, int64_t Tc,
-    BwdFuse<Tin> fz)
+    BwdFuse<Tin> fz, const float *__restrict__ gstate, int Lr)
 {
     constexpr int CW = 8;                     // channels per wave
     constexpr int ES = sizeof(Tin);
     constexpr int G = kGroup;                 // 16 tokens per group
     constexpr int NSB = kFuse ? 4 : 3;        // row streams: x, dt, dy (, z)
     constexpr int NQ = 2;                     // transposed per-token sums: dt, x
-    static_assert(G % L == 0, "block length must divide the token group");
+    // L = 0: blocks of Lr tokens, a multiple of 16 above 16, spanning several
+    // groups; gstate holds the forward state and the reverse adjoint's carry
+    // at every group start ([batch, T/16, 2, D, 16], group_state_kernel)
+    constexpr bool kLong = L == 0;
+    constexpr int LB = kLong ? G : L;         // block length as seen inside one group
+    static_assert(kLong || G % L == 0, "block length must divide the token group");
     // Double buffers as distinct arrays (A / B), so that the compiler can tell
     // the loads in flight into one buffer from the reads of the other and
     // does not wait for them: [wave][stream x, dt, dy (, z)][token][channel]
@@ -628,7 +633,8 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
     const int64_t t_begin = (int64_t)c * Tc;
     const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
     const int len = (int)(t_end - t_begin);
-    const int64_t nbl = T / L;
+    const int Lb = kLong ? Lr : L;            // block length
+    const int64_t nbl = T / Lb;
 
     float a2[2], ar[2], q[2];
     {
@@ -748,7 +754,10 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
     Tin *dxw = dx + first * D;
     Tin *dtw = ddt + first * D;
 
-    constexpr int NB = G / L;                 // blocks per group
+    constexpr int NB = G / LB;                // blocks per group (1 for kLong)
+    constexpr int NH = kLong ? 2 : (kBlockInit ? NB : 1);   // group-start values
+    constexpr int ND = kLong ? 1 : (kBlockInit ? 1 : NB);   // d_bounds entries
+    float hrc[2] = {0.f, 0.f};                // kLong: the reverse state carried between groups
     // hst: forward state at the group start (two-stream form: at each block
     // start of the group); dbd: dbounds at each block end of the group
     // (continuous form; zero past the chunk end or without dbounds)
@@ -765,11 +774,18 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
         // pass A: forward state and reverse adjoint, left to right
         float hp_s[G][2], gr_s[G][2];
         float hf[2] = {hst[0].x, hst[0].y}, pr[2] = {0.f, 0.f};
+        if constexpr (kLong) {
+            pr[0] = hst[NH - 1].x; pr[1] = hst[NH - 1].y;
+        }
+        // kLong: whether this group starts / ends a block (uniform; chunks
+        // are whole blocks, so the chunk's end ends one)
+        const bool gsb = !kLong || k0 % Lb == 0;
+        const bool geb = !kLong || (k0 + G) % Lb == 0 || k0 + G >= len;
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            if (i % L == 0 && i != 0) {
+            if (i % LB == 0 && i != 0) {
                 if constexpr (kBlockInit) {
-                    hf[0] = hst[i / L].x; hf[1] = hst[i / L].y;
+                    hf[0] = hst[i / LB].x; hf[1] = hst[i / LB].y;
                 }
                 pr[0] = pr[1] = 0.f;
             }
@@ -795,14 +811,17 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
         asm volatile("" ::: "memory");
         // pass B: reverse state and forward adjoint, right to left
         float hr[2] = {0.f, 0.f};
+        if constexpr (kLong) {
+            hr[0] = hrc[0]; hr[1] = hrc[1];
+        }
 #pragma unroll
         for (int i = G - 1; i >= 0; --i) {
-            if ((i + 1) % L == 0) {
+            if ((i + 1) % LB == 0 && geb) {
                 hr[0] = hr[1] = 0.f;
                 if constexpr (kBlockInit) {
                     q[0] = q[1] = 0.f;
                 } else {
-                    q[0] += dbd[i / L].x; q[1] += dbd[i / L].y;
+                    q[0] += dbd[i / LB].x; q[1] += dbd[i / LB].y;
                 }
             }
             const float xv = xval(i), dl = dval(i), gy = yval(i);
@@ -827,7 +846,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
                 // forward state after token i: kept as the state before token
                 // i + 1, except where the two-stream form restarts a block
                 const float hf_t = (i == G - 1) ? hf[j]
-                                   : (kBlockInit && (i + 1) % L == 0) ? __builtin_fmaf(a, hp_s[i][j], u)
+                                   : (kBlockInit && (i + 1) % LB == 0) ? __builtin_fmaf(a, hp_s[i][j], u)
                                                                       : hp_s[i + 1][j];
                 vb[j] = du * dxv;                     // dB
                 vc[j] = gy * (hf_t + hr[j]);          // dC
@@ -844,9 +863,11 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
                 xd[w][0][i][cl] = __float_as_uint(__builtin_fmaf(dsk, xv, yp));
             }
             if constexpr (kBlockInit) {
-                if (i % L == 0 && dh0 != nullptr && i < nvalid && live)
-                    *reinterpret_cast<float2 *>(dh0 + (((int64_t)b * (nbl + 1) + (t_begin + k0 + i) / L) * D + d) * kStates + s0) =
+                if (i % LB == 0 && gsb && dh0 != nullptr && i < nvalid && live) {
+                    const int64_t blk = kLong ? t_begin / Lb + k0 / Lb : (t_begin + k0 + i) / LB;
+                    *reinterpret_cast<float2 *>(dh0 + (((int64_t)b * (nbl + 1) + blk) * D + d) * kStates + s0) =
                         make_float2(q[0], q[1]);
+                }
             }
             // dB / dC of the token: sum over the wave's 8 channels
             tb[w][s0][cl] = vb[0];
@@ -889,6 +910,9 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
                 asm volatile("" ::: "memory");
             }
         }
+        if constexpr (kLong) {
+            hrc[0] = hr[0]; hrc[1] = hr[1];
+        }
         if constexpr (kFuse) {
             // epilogue of the group: lane (tokens l / 8 and l / 8 + 8, channel
             // l % 8) applies softplus'(v) = s(v) to the dt-stream gradient,
@@ -915,10 +939,30 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
     // the wait for the rows at the end of the previous group covers them (the
     // vector-memory counter is in order: a wait for them placed after a later
     // DMA would wait for the DMA as well).
-    float2 hstn[kBlockInit ? NB : 1], dbdn[kBlockInit ? 1 : NB];
+    float2 hstn[NH], dbdn[ND];
     auto load_group = [&](int k0n) {
         const int nv = (len - k0n < G) ? len - k0n : G;
-        if constexpr (kBlockInit) {
+        if constexpr (kLong) {
+            // a block's first group starts from the block state and a zero
+            // reverse adjoint, the others from the group-state pre-pass
+            if (k0n % Lb == 0) {
+                hstn[0] = state_at(h_start, t_begin / Lb + k0n / Lb);
+                hstn[1] = make_float2(0.f, 0.f);
+            } else {
+                const int64_t ng = (T + G - 1) / G;
+                const float *gs = gstate + ((((int64_t)b * ng + (t_begin + k0n) / G) * 2) * D + d) * kStates + s0;
+                hstn[0] = *reinterpret_cast<const float2 *>(gs);
+                const float2 v = *reinterpret_cast<const float2 *>(gs + (int64_t)D * kStates);
+                // a dead channel carries no adjoint (its step size need not be
+                // zero under the softplus transform, so it would reach dB)
+                hstn[1] = live ? v : make_float2(0.f, 0.f);
+            }
+            dbdn[0] = make_float2(0.f, 0.f);
+            if (!kBlockInit && dbounds != nullptr && (k0n + G) % Lb == 0 && k0n + G <= len) {
+                const float2 v = state_at(dbounds, t_begin / Lb + (k0n + G) / Lb);
+                if (live) dbdn[0] = v;
+            }
+        } else if constexpr (kBlockInit) {
 #pragma unroll
             for (int k = 0; k < NB; ++k) {
                 const int ib = k * L < nv ? k * L : 0;
@@ -943,11 +987,11 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
     // added in a fixed order
     auto step = [&](auto &xd, auto &bc, auto &red, auto &xdn, auto &bcn, int k0) {
         const bool more = k0 > 0;
-        float2 hst[kBlockInit ? NB : 1], dbd[kBlockInit ? 1 : NB];
+        float2 hst[NH], dbd[ND];
 #pragma unroll
-        for (int k = 0; k < (kBlockInit ? NB : 1); ++k) hst[k] = hstn[k];
+        for (int k = 0; k < NH; ++k) hst[k] = hstn[k];
 #pragma unroll
-        for (int k = 0; k < (kBlockInit ? 1 : NB); ++k) dbd[k] = dbdn[k];
+        for (int k = 0; k < ND; ++k) dbd[k] = dbdn[k];
         if (more) {
             load_group(k0 - G);
             issue(xdn, bcn, k0 - G);
@@ -1064,6 +1108,77 @@ __global__ __launch_bounds__(kWave) void adjoint_general_kernel(
     if (live) {
         store_row<kN>(qout + (((int64_t)b * n_chunks + c) * D + d) * kN, q);
         sout[((int64_t)b * n_chunks + c) * D + d] = S;
+    }
+}
+
+// Group states for bwd_pair_kernel's long blocks (block lengths that are
+// multiples of 16 above 16, 16 states): the forward state and the reverse
+// adjoint's carry (a * gr, the adjoint of the in-block reverse recurrence,
+// which runs left to right from zero at the block start) at every 16-token
+// group start that lies inside a block, not at its start, into gstate
+// [batch, ceil(T/16), 2, D, 16] (entries at block starts are not written).
+// Walks each block from its start state up to its last group start, with the
+// pair kernel's pass-A recurrences.  One lane per channel, the 16 states in
+// registers; grid = (ceil(D/64), min(blocks, 65535), batch), block = 64.
+template <typename Tin, int kDt>
+__global__ __launch_bounds__(kWave) void group_state_kernel(
+    const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
+    const Tin *__restrict__ Cm, const Tin *__restrict__ dy, const float *__restrict__ A,
+    const float *__restrict__ h_start, float *__restrict__ gstate, int64_t T, int D, int L,
+    const float *__restrict__ dt_bias, const Tin *__restrict__ z)
+{
+    constexpr int G = kGroup;
+    const int lane = threadIdx.x;
+    const int d_raw = blockIdx.x * kWave + lane;
+    const bool live = d_raw < D;
+    const int d = live ? d_raw : D - 1;
+    const int b = blockIdx.z;
+    const int64_t nbl = T / L, nbt = (T + L - 1) / L, ng = (T + G - 1) / G;
+    float a2[kStates];
+    load_row<kStates>(A + (int64_t)d * kStates, a2);
+#pragma unroll
+    for (int n = 0; n < kStates; ++n) a2[n] *= kLog2e;
+    const bool gate = z != nullptr;
+    const float bias = (kDt != kDtPlain && dt_bias != nullptr) ? dt_bias[d] : 0.f;
+    const int64_t row0 = (int64_t)b * T;
+    for (int64_t blk = blockIdx.y; blk < nbt; blk += gridDim.y) {
+        const int64_t t0 = blk * L;
+        const int64_t pend = (t0 + L < T) ? t0 + L : T;
+        if (t0 + G >= pend) continue;                  // one group: nothing to hand over
+        float hf[kStates], pr[kStates];
+        load_row<kStates>(h_start + (((int64_t)b * (nbl + 1) + blk) * D + d) * kStates, hf);
+#pragma unroll
+        for (int n = 0; n < kStates; ++n) pr[n] = 0.f;
+        for (int64_t gs = t0; gs + G < pend; gs += G) {
+            for (int i = 0; i < G; ++i) {
+                const int64_t r = row0 + gs + i;
+                const float dl = step_size<kDt>(widen(dt[r * D + d]), bias);
+                const float dxv = dl * widen(x[r * D + d]);
+                float gy = widen(dy[r * D + d]);
+                if (gate) gy *= silu_f(widen(z[r * D + d]));
+                const Tin *brow = Bm + r * kStates, *crow = Cm + r * kStates;
+#pragma unroll
+                for (int k = 0; k < kStates / 2; ++k) {
+                    float b0, b1, c0, c1;
+                    load_pair(brow, k, b0, b1);
+                    load_pair(crow, k, c0, c1);
+                    const float bb[2] = {b0, b1}, cc[2] = {c0, c1};
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int n = 2 * k + j;
+                        const float a = fast_exp2(dl * a2[n]);
+                        const float gr = __builtin_fmaf(gy, cc[j], pr[n]);
+                        hf[n] = __builtin_fmaf(a, hf[n], dxv * bb[j]);
+                        pr[n] = a * gr;
+                    }
+                }
+            }
+            if (live) {
+                float *o = gstate + ((((int64_t)b * ng + (gs + G) / G) * 2) * D + d) * kStates;
+                store_row<kStates>(o, hf);
+                store_row<kStates>(o + (int64_t)D * kStates, pr);
+            }
+        }
     }
 }
 

@@ -7,6 +7,9 @@ than one 16-token segment and blocks that end inside one, and the fusions.
 
 The oracle receives the same input values as the GPU (read back from the
 device tensors); dy, d_bounds and the two-stream block starts are seeded.
+Block lengths that are multiples of 16 at 16 states normally take the pair
+kernel with group states (tests/test_parity_bwd_long.py); here
+BDSSM_BWD_KERNEL=general keeps them on the general kernel.
 """
 import pytest
 import torch
@@ -84,14 +87,16 @@ CASES = [  # (N, L, T, D, dtype)
 def test_general_backward(dev, N, L, T, D, dtype, monkeypatch):
     """Several chunks (the adjoint pre-pass and the carry), both forms."""
     monkeypatch.setenv("BDSSM_CHUNK", "64")
+    monkeypatch.setenv("BDSSM_BWD_KERNEL", "general")
     sid = 60 + CASES.index((N, L, T, D, dtype))
     c = Case(2, T, D, dtype, sid=sid, a_kind="random", n=N)
     both_forms(c, L, sid, label="N=%d L=%d" % (N, L))
 
 
 @pytest.mark.parametrize("N,L", [(16, 32), (8, 16), (4, 100)])
-def test_general_backward_single_chunk_long_memory(dev, N, L):
+def test_general_backward_single_chunk_long_memory(dev, N, L, monkeypatch):
     """One chunk per row (no carry), slowly decaying states."""
+    monkeypatch.setenv("BDSSM_BWD_KERNEL", "general")
     T, D = 4 * L if L > 16 else 128, 64
     c = Case(2, T, D, torch.float32, sid=80 + N + L, a_kind="long", n=N)
     both_forms(c, L, 80 + N + L, label="N=%d L=%d long" % (N, L))
