@@ -187,21 +187,23 @@ def test_two_stream_backward_87m_sampled(dev):
         assert rel_err(got, r0[k]) < TOL_BF16, (k, worst(got, r0[k]))
 
 
-@pytest.mark.parametrize("variant", ["fused", "block32"])
+@pytest.mark.parametrize("variant", ["fused", "block32", "block32-fused"])
 def test_training_backward_87m_variants_sampled(dev, variant):
     """The backward at the 87M training shape in the configurations the
-    benchmark's --fused and --block-len 32 runs time: the fused backward
-    (raw dt through bias and softplus, silu gate) and the general path.
+    benchmark's --fused, --block-len 32 and --block-len 32 --fused runs time:
+    the fused backward (raw dt through bias and softplus, silu gate) and the
+    long-block path (group states, then the pair kernel).
     Sampled channels over every batch row; dB, dC on batch row 0."""
     wl = synth.WORKLOADS["train_87m"]
     batch, D, T, sid = wl["batch"], wl["d_inner"], wl["seq"], wl["sid"]
-    L = 32 if variant == "block32" else wl["block"]
+    L = 32 if variant.startswith("block32") else wl["block"]
+    fused = variant.endswith("fused")
     print("[fullsize] train_87m backward (%s): batch %d, D %d, T %d, L %d" % (variant, batch, D, T, L),
           flush=True)
     x, dt, Bm, Cm = synth.stream(batch, T, D, N, sid, 0, torch.bfloat16, dev)
     A, Dskip = synth.params(D, N, sid, "default", dev)
     kw = {}
-    if variant == "fused":
+    if fused:
         dt = synth.normal((batch, T, D), 1000 * sid + 70, dev, torch.bfloat16, mean=-1.0, std=0.5)
         kw = dict(dt_bias=synth.normal((D,), 1000 * sid + 72, dev, torch.float32, std=0.3),
                   dt_softplus=True, z=synth.normal((batch, T, D), 1000 * sid + 73, dev, torch.bfloat16))
@@ -215,20 +217,20 @@ def test_training_backward_87m_variants_sampled(dev, variant):
     idx = torch.as_tensor(ch, device=dev)
 
     def okw(sel, rows):
-        if variant != "fused":
+        if not fused:
             return {}
         return dict(dt_bias=to_np(kw["dt_bias"][sel]), dt_softplus=True, z=ora(rows(kw["z"])))
 
     r = oracle.scan_bwd(ora(gather(x, ch)), ora(gather(dt, ch)), ora(Bm), ora(Cm), ora(A[idx]),
                         ora(Dskip[idx]), L, to_np(gather(dy, ch)), dbounds=to_np(db[:, :, idx]),
                         **okw(idx, lambda t: gather(t, ch)))
-    streams = ("dx", "ddt") + (("dz",) if variant == "fused" else ())
+    streams = ("dx", "ddt") + (("dz",) if fused else ())
     for k in streams:
         got = to_np(gather(g[k], ch))
         assert rel_err(got, r[k]) < TOL_BF16, (k, worst(got, r[k]))
     params = [("dA", to_np(g["dA"][idx])), ("dDskip", to_np(g["dDskip"][idx])),
               ("dh0", to_np(g["dh_init"][:, idx]))]
-    if variant == "fused":
+    if fused:
         params.append(("d_dt_bias", to_np(g["d_dt_bias"][idx])))
     for k, got in params:
         assert rel_err(got, r[k]) < STATE_TOL, (k, worst(got, r[k]))
