@@ -569,17 +569,30 @@ bool block_lane_path(int64_t L, const Fuse &f, bool with_y) {
     return !with_y;
 }
 
+// Segment length of block_bidir_kernel for block length L and N states: small
+// enough that the staged outputs (256 bytes per token) do not limit the
+// workgroups per CU below what the registers allow (16 waves per CU at
+// N <= 16: 32 tokens; 8 at N = 32: 64), no smaller, since every segment
+// boundary adds state-only reverse work (measured on MI355X at the 87M
+// training shape).  BDSSM_SEG overrides (tuning, tests).
+int block_seg(int64_t L, int64_t N) {
+    const int64_t forced = env_int("BDSSM_SEG", 0);
+    const int64_t s = forced > 0 ? forced : (N >= 32 ? 64 : 32);
+    return (int)(L < s ? L : s);
+}
+
 template <typename Tin, int kN, bool kInit, int kDt>
 void launch_block_bidir_k(dim3 g, int64_t L, const void *x, const void *dt, const void *B,
                           const void *C, const float *A, const float *Dskip, const float *hin,
                           int64_t hin_bs, int64_t hin_cs, void *y, float *bounds, float *hout,
                           int64_t T, int64_t D, int64_t Tc, const float *h0_blocks, const Fuse &f,
                           hipStream_t st) {
-    const size_t lds = (size_t)L * kWave * sizeof(float);
+    const int seg = block_seg(L, kN);
+    const size_t lds = (size_t)seg * kWave * sizeof(float);
     hipLaunchKernelGGL((block_bidir_kernel<Tin, kN, kInit, kDt>), g, dim3(kWave), lds, st,
                        (const Tin *)x, (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip,
                        hin, hin_bs, hin_cs, (Tin *)y, bounds, hout, T, (int)D, (int)L, Tc,
-                       h0_blocks, f.args<Tin>());
+                       h0_blocks, f.args<Tin>(), seg);
 }
 
 // Bidirectional pass with block_bidir_kernel (any L <= kMaxLdsBlock; Tc a

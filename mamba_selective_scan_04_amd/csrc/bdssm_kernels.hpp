@@ -977,25 +977,33 @@ __global__ __launch_bounds__(kWave) void sweep_output_kernel(
 //     to yf_t and storing y (times silu(z_t) when the gate is given).
 // The second walk forms its decays again: a block may be longer than the
 // registers can hold, and the rows it re-reads are the block's own, still in
-// L2.  LDS holds one fp32 value per token and channel of a block: 256 * L
-// bytes of dynamic shared memory.
+// L2.  LDS holds one fp32 value per token and channel of a block (of a
+// segment, for blocks longer than seg): 256 * min(L, seg) bytes of dynamic
+// shared memory.
 // Chunks are whole numbers of blocks (Tc % L == 0).  hin, bounds, hout and the
 // fusions as in bidir_wave_kernel (states are [.., kN] instead of [.., 16]);
 // with separate reverse operands the reverse walk reads dt_r (with dt_bias_r,
 // same transform), B_r, C_r and A_r.
 // grid = (ceil(D/64), chunks, batch), block = 64.
 constexpr int kMaxLdsBlock = 256;
+// Blocks longer than seg tokens are finished in segments of seg tokens (the
+// LDS then holds one segment's outputs, 256 seg bytes: 8 KB at seg = 32
+// rather than 64 KB for a whole 256-token block, which let only two
+// workgroups share a CU): the reverse state entering a
+// segment from the right is formed again by a state-only reverse walk from
+// the block's end (an exp and two FMAs per state and token, no C, no output),
+// which adds (L / seg - 1) / 2 state-only walks of the block.
 
 template <typename Tin, int kN, bool kBlockInit, int kDt>
-__global__ __launch_bounds__(kWave) void block_bidir_kernel(
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kN <= 16 ? 4 : 1))) void block_bidir_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const Tin *__restrict__ Cm, const float *__restrict__ A, const float *__restrict__ Dskip,
     const float *hin, int64_t hin_bs, int64_t hin_cs, Tin *__restrict__ y,
     float *__restrict__ bounds, float *hout, int64_t T, int D, int L, int64_t Tc,
-    const float *__restrict__ h0_blocks, FuseArgs<Tin> fz)
+    const float *__restrict__ h0_blocks, FuseArgs<Tin> fz, int seg)
 {
     static_assert(kN % 2 == 0, "B and C rows are read in pairs");
-    extern __shared__ float yf_lds[];             // [L][64]
+    extern __shared__ float yf_lds[];             // [min(L, seg)][64]
     constexpr int U = 4;                          // tokens per pipeline stage
     const int lane = threadIdx.x;
     const int d_raw = blockIdx.x * kWave + lane;
@@ -1051,6 +1059,19 @@ __global__ __launch_bounds__(kWave) void block_bidir_kernel(
         }
         yf_lds[r * kWave + lane] = acc0 + acc1;
     };
+    // one token of the reverse walk that only carries the state (a segment
+    // right of the one being finished)
+    auto rev_state_tok = [&](int p, float xv, float dl) {
+        const float dx = dl * xv;
+        const Tin *brow = rbs + (int64_t)p * kN;
+#pragma unroll
+        for (int q = 0; q < kN / 2; ++q) {
+            float b0, b1;
+            load_pair(brow, q, b0, b1);
+            hr[2 * q] = __builtin_fmaf(fast_exp2(dl * a2r[2 * q]), hr[2 * q], dx * b0);
+            hr[2 * q + 1] = __builtin_fmaf(fast_exp2(dl * a2r[2 * q + 1]), hr[2 * q + 1], dx * b1);
+        }
+    };
     // one token of the reverse walk
     auto rev_tok = [&](int p, int r, float xv, float dl, float zv) {
         const float dx = dl * xv;
@@ -1070,21 +1091,24 @@ __global__ __launch_bounds__(kWave) void block_bidir_kernel(
         if (gate) tot *= silu_f(zv);
         if (live) ys.store(p, narrow<Tin>(tot));
     };
-    // walk the block starting at chunk row k0, forward or reverse; the rows of
-    // the next U tokens are loaded before the arithmetic of the current U
-    auto walk = [&](auto rev_tag, int k0) {
-        constexpr bool R = decltype(rev_tag)::value;
+    // walk rows k0 .. k0 + n - 1 of the chunk, forward (mode 0) or reverse
+    // (mode 1: with the output, LDS row p - r0; mode 2: the state alone); the
+    // rows of the next U tokens are loaded before the arithmetic of the
+    // current U
+    auto walk = [&](auto mode_tag, int k0, int n, int r0) {
+        constexpr int M = decltype(mode_tag)::value;
+        constexpr bool R = M != 0;
         const Rows<Tin> &dsrc = R ? rds : ds;
-        const int nst = (L + U - 1) / U;
-        auto pos = [&](int k) { return R ? k0 + L - 1 - k : k0 + k; };
+        const int nst = (n + U - 1) / U;
+        auto pos = [&](int k) { return R ? k0 + n - 1 - k : k0 + k; };
         auto stage = [&](int s, Tin *xo, Tin *dout, Tin *zo) {
 #pragma unroll
             for (int i = 0; i < U; ++i) {
-                const int k = (s * U + i < L) ? s * U + i : L - 1;
+                const int k = (s * U + i < n) ? s * U + i : n - 1;
                 const int p = pos(k);
                 xo[i] = xs.load(p);
                 dout[i] = dsrc.load(p);
-                zo[i] = (R && gate) ? zs.load(p) : xo[i];
+                zo[i] = (M == 1 && gate) ? zs.load(p) : xo[i];
             }
         };
         Tin xr[U], dr[U], zr[U];
@@ -1095,12 +1119,14 @@ __global__ __launch_bounds__(kWave) void block_bidir_kernel(
 #pragma unroll
             for (int i = 0; i < U; ++i) {
                 const int k = s * U + i;
-                if (k < L) {
+                if (k < n) {
                     const int p = pos(k);
-                    if constexpr (R)
-                        rev_tok(p, p - k0, widen(xr[i]), step_size<kDt>(widen(dr[i]), bias_r), widen(zr[i]));
+                    if constexpr (M == 2)
+                        rev_state_tok(p, widen(xr[i]), step_size<kDt>(widen(dr[i]), bias_r));
+                    else if constexpr (M == 1)
+                        rev_tok(p, p - r0, widen(xr[i]), step_size<kDt>(widen(dr[i]), bias_r), widen(zr[i]));
                     else
-                        fwd_tok(p, p - k0, widen(xr[i]), step_size<kDt>(widen(dr[i]), bias));
+                        fwd_tok(p, p - r0, widen(xr[i]), step_size<kDt>(widen(dr[i]), bias));
                 }
             }
 #pragma unroll
@@ -1115,10 +1141,18 @@ __global__ __launch_bounds__(kWave) void block_bidir_kernel(
         } else if (bounds != nullptr && live) {
             store_row<kN>(bounds + (((int64_t)b * (nbl + 1) + blk) * D + d) * kN, h);
         }
-        walk(std::false_type{}, k0);
+        // segments of at most seg tokens, left to right: the forward walk
+        // stages the segment's outputs; the reverse state entering it from the
+        // right is formed again from the block's end (state only), then the
+        // reverse walk over the segment finishes y
+        for (int s0 = 0; s0 < L; s0 += seg) {
+            const int sl = (L - s0 < seg) ? L - s0 : seg;
+            walk(std::integral_constant<int, 0>{}, k0 + s0, sl, k0 + s0);
 #pragma unroll
-        for (int n = 0; n < kN; ++n) hr[n] = 0.f;
-        walk(std::true_type{}, k0);
+            for (int n = 0; n < kN; ++n) hr[n] = 0.f;
+            if (s0 + sl < L) walk(std::integral_constant<int, 2>{}, k0 + s0 + sl, L - s0 - sl, 0);
+            walk(std::integral_constant<int, 1>{}, k0 + s0, sl, k0 + s0);
+        }
     }
     if (t_end == T && live) {
         if (!kBlockInit && bounds != nullptr)

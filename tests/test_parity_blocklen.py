@@ -1,5 +1,6 @@
 """GPU parity of the block lengths outside {1, 2, 4, 8, 16} (block_bidir_kernel:
-one lane per channel, each block's forward output staged in LDS) on every
+one lane per channel, each block's forward output staged in LDS, blocks
+longer than 64 tokens finished in 64-token segments) on every
 forward entry point, against the fp64 oracle, element by element: lengths
 that are not powers of two, multiples of 16, the largest supported (256),
 ragged channel counts, forced multi-chunk plans (chunks rounded up to whole
@@ -206,3 +207,52 @@ def test_reverse_bias_without_forward_bias(dev, L, monkeypatch):
     close(y, oracle.train_scan(*oa, L, rev=ro)[0], TOL[dtype], "train_scan y")
     close(yb, oracle.train_blocks(*oa, L, to_np(h0b), rev=ro), TOL[dtype], "two-stream y")
     close(yf, oracle.full_scan(*oa, rev=ro), TOL[dtype], "full_scan y")
+
+
+QUAD = [  # (L, N, dtype, variant)
+    (128, 16, torch.bfloat16, "plain"),
+    (128, 8, torch.float32, "plain"),
+    (96, 32, torch.bfloat16, "plain"),
+    (128, 4, torch.float32, "plain"),
+    (128, 16, torch.bfloat16, "fused"),
+    (128, 16, torch.float32, "rev"),
+    (24, 16, torch.bfloat16, "plain"),
+]
+
+
+@pytest.mark.parametrize("seg", ["0", "64", "24"])
+@pytest.mark.parametrize("L,N_,dtype,variant", QUAD)
+def test_long_block_forward_segments(dev, seg, L, N_, dtype, variant, monkeypatch):
+    """block_bidir_kernel's segments (the reverse state entering each segment
+    formed again from the block's end) on both training forms: the default
+    length (32 tokens, 64 at N = 32), 64-token segments (L = 96: a 32-token
+    last segment) and 24-token ones (L = 128:
+    five and a ragged 8-token last one; L = 24: one), several chunks, 70
+    channels, 4 to 32 states, the fusions and separate reverse operands."""
+    monkeypatch.setenv("BDSSM_CHUNK", "64")
+    monkeypatch.setenv("BDSSM_SEG", seg)
+    batch, T, D = 2, {128: 512, 96: 384, 24: 480}[L], 70
+    sid = 400 + QUAD.index((L, N_, dtype, variant))
+    c = Case(batch, T, D, dtype, sid=sid, a_kind="random", n=N_)
+    kw, ok = {}, {}
+    if variant == "fused":
+        c.dev["dt"] = synth.normal((batch, T, D), 1000 * sid + 1, "cpu", torch.float32, mean=-1.0,
+                                   std=0.5).to(dtype).to("cuda").contiguous()
+        bias = synth.normal((D,), 1000 * sid + 2, "cuda", torch.float32, std=0.3)
+        z = synth.normal((batch, T, D), 1000 * sid + 3, "cuda", dtype, std=2.0)
+        kw = dict(dt_bias=bias, dt_softplus=True, z=z)
+        ok = dict(dt_bias=to_np(bias), dt_softplus=True, z=synth.to_oracle(z))
+    elif variant == "rev":
+        rev = _rev_operands(batch, T, D, dtype, sid, with_bias=False)
+        kw, ok = dict(rev=rev), dict(rev=_rev_oracle(rev))
+    y, bnd = m.train_scan(*c.args(), L, want_bounds=True, **kw)
+    h0b = synth.normal((batch, T // L + 1, D, N_), 1000 * sid + 4, "cuda")
+    yb = m.train_scan_blocks(*c.args(), L, h0b, **kw)
+    torch.cuda.synchronize()
+    oa = c.oracle_args()
+    yo, bo = oracle.train_scan(*oa, L, want_bounds=True, **ok)
+    ybo = oracle.train_blocks(*oa, L, to_np(h0b), **ok)
+    label = "seg %s L=%d N=%d %s" % (seg, L, N_, variant)
+    close(y, yo, TOL[dtype], label + " y")
+    close(bnd, bo, STATE_TOL, label + " h_bounds")
+    close(yb, ybo, TOL[dtype], label + " two-stream y")
