@@ -961,7 +961,7 @@ void launch_bwd_reduce(const BwdWorkspace &w, void *dB, void *dC, float *dA, flo
     hipLaunchKernelGGL((bc_reduce_kernel<Tin>), dim3((unsigned)ceil_div(nbc, 256)), dim3(256), 0, st,
                        w.part_bc, (Tin *)dB, (Tin *)dC, (int)batch, T, nblk, (int)N);
     const bool nb = fused && d_bias != nullptr;
-    hipLaunchKernelGGL(param_reduce_kernel, dim3((unsigned)ceil_div(D * (N + (nb ? 2 : 1)), 256)),
+    hipLaunchKernelGGL(param_reduce_kernel, dim3((unsigned)ceil_div(D * (N + (nb ? 2 : 1)), kWave)),
                        dim3(256), 0, st, w.part_a, w.part_d, dA, dDskip, (int)D, (int)(batch * nc),
                        nb ? w.part_bias : nullptr, nb ? d_bias : nullptr, (int)N);
     if (sep) {
@@ -969,7 +969,7 @@ void launch_bwd_reduce(const BwdWorkspace &w, void *dB, void *dC, float *dA, flo
         hipLaunchKernelGGL((bc_reduce_kernel<Tin>), dim3((unsigned)ceil_div(nbc, 256)), dim3(256), 0, st,
                            w.part_bc_r, (Tin *)gr->dB_rev, (Tin *)gr->dC_rev, (int)batch, T, nblk, (int)N);
         const bool nbr = gr->d_dt_bias_rev != nullptr;
-        hipLaunchKernelGGL(param_reduce_kernel, dim3((unsigned)ceil_div(D * (N + 2), 256)), dim3(256), 0, st,
+        hipLaunchKernelGGL(param_reduce_kernel, dim3((unsigned)ceil_div(D * (N + 2), kWave)), dim3(256), 0, st,
                            w.part_a_r, nullptr, gr->dA_rev, nullptr, (int)D, (int)(batch * nc),
                            nbr ? w.part_bias_r : nullptr, nbr ? gr->d_dt_bias_rev : nullptr, (int)N);
     }

@@ -1084,26 +1084,49 @@ __global__ __launch_bounds__(kWave) void adjoint_general_kernel(
     const float bias = (kDt != kDtPlain && dt_bias != nullptr) ? dt_bias[d] : 0.f;
     const Tin *cs = Cm + first * kN;
     int kb = 0;                                   // rows walked since the last block end
-    for (int p = len - 1; p >= 0; --p) {
-        if (dbounds != nullptr && kb == 0) {
-            float v[kN];
-            load_row<kN>(dbounds + (((int64_t)b * (nbl + 1) + blk0 + (p + 1) / L) * D + d) * kN, v);
+    // rows in stages of U tokens from the right; the next stage's dt, dy (and
+    // z) are loaded before the current stage's arithmetic
+    constexpr int U = 4;
+    auto stage = [&](int p0, Tin *dr, Tin *yr, Tin *zr) {
 #pragma unroll
-            for (int n = 0; n < kN; ++n) q[n] += v[n];
+        for (int u = 0; u < U; ++u) {
+            const int p = (p0 - u >= 0) ? p0 - u : 0;
+            dr[u] = ds.load(p);
+            yr[u] = ys.load(p);
+            zr[u] = gate ? zs.load(p) : yr[u];
         }
-        const float dl = step_size<kDt>(widen(ds.load(p)), bias);
-        float gy = live ? widen(ys.load(p)) : 0.f;
-        if (gate) gy *= silu_f(widen(zs.load(p)));
-        S += dl;
-        const Tin *crow = cs + (int64_t)p * kN;
+    };
+    Tin dc[U], yc[U], zc[U];
+    stage(len - 1, dc, yc, zc);
+    for (int p0 = len - 1; p0 >= 0; p0 -= U) {
+        Tin dn[U], yn[U], zn[U];
+        if (p0 - U >= 0) stage(p0 - U, dn, yn, zn);
 #pragma unroll
-        for (int k = 0; k < kN / 2; ++k) {
-            float c0, c1;
-            load_pair(crow, k, c0, c1);
-            q[2 * k] = fast_exp2(dl * a2[2 * k]) * __builtin_fmaf(gy, c0, q[2 * k]);
-            q[2 * k + 1] = fast_exp2(dl * a2[2 * k + 1]) * __builtin_fmaf(gy, c1, q[2 * k + 1]);
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 - u;
+            if (p < 0) break;
+            if (dbounds != nullptr && kb == 0) {
+                float v[kN];
+                load_row<kN>(dbounds + (((int64_t)b * (nbl + 1) + blk0 + (p + 1) / L) * D + d) * kN, v);
+#pragma unroll
+                for (int n = 0; n < kN; ++n) q[n] += v[n];
+            }
+            const float dl = step_size<kDt>(widen(dc[u]), bias);
+            float gy = live ? widen(yc[u]) : 0.f;
+            if (gate) gy *= silu_f(widen(zc[u]));
+            S += dl;
+            const Tin *crow = cs + (int64_t)p * kN;
+#pragma unroll
+            for (int k = 0; k < kN / 2; ++k) {
+                float c0, c1;
+                load_pair(crow, k, c0, c1);
+                q[2 * k] = fast_exp2(dl * a2[2 * k]) * __builtin_fmaf(gy, c0, q[2 * k]);
+                q[2 * k + 1] = fast_exp2(dl * a2[2 * k + 1]) * __builtin_fmaf(gy, c1, q[2 * k + 1]);
+            }
+            kb = (kb + 1 == L) ? 0 : kb + 1;
         }
-        kb = (kb + 1 == L) ? 0 : kb + 1;
+#pragma unroll
+        for (int u = 0; u < U; ++u) { dc[u] = dn[u]; yc[u] = yn[u]; zc[u] = zn[u]; }
     }
     if (live) {
         store_row<kN>(qout + (((int64_t)b * n_chunks + c) * D + d) * kN, q);
@@ -1149,29 +1172,53 @@ __global__ __launch_bounds__(kWave) void group_state_kernel(
         load_row<kStates>(h_start + (((int64_t)b * (nbl + 1) + blk) * D + d) * kStates, hf);
 #pragma unroll
         for (int n = 0; n < kStates; ++n) pr[n] = 0.f;
+        // rows in stages of U tokens; the next stage's x, dt, dy (and z) are
+        // loaded before the current stage's arithmetic
+        constexpr int U = 4;
+        auto stage = [&](int64_t r0, Tin *xr, Tin *dr, Tin *yr, Tin *zr) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t o = (r0 + u) * D + d;
+                xr[u] = x[o];
+                dr[u] = dt[o];
+                yr[u] = dy[o];
+                zr[u] = gate ? z[o] : yr[u];
+            }
+        };
+        Tin xc[U], dc[U], yc[U], zc[U];
+        stage(row0 + t0, xc, dc, yc, zc);
         for (int64_t gs = t0; gs + G < pend; gs += G) {
-            for (int i = 0; i < G; ++i) {
-                const int64_t r = row0 + gs + i;
-                const float dl = step_size<kDt>(widen(dt[r * D + d]), bias);
-                const float dxv = dl * widen(x[r * D + d]);
-                float gy = widen(dy[r * D + d]);
-                if (gate) gy *= silu_f(widen(z[r * D + d]));
-                const Tin *brow = Bm + r * kStates, *crow = Cm + r * kStates;
+            for (int i0 = 0; i0 < G; i0 += U) {
+                Tin xn[U], dn[U], yn[U], zn[U];
+                // the last stage before the block's final group has no successor
+                const bool more = i0 + U < G || gs + 2 * G < pend;
+                if (more) stage(row0 + gs + i0 + U, xn, dn, yn, zn);
 #pragma unroll
-                for (int k = 0; k < kStates / 2; ++k) {
-                    float b0, b1, c0, c1;
-                    load_pair(brow, k, b0, b1);
-                    load_pair(crow, k, c0, c1);
-                    const float bb[2] = {b0, b1}, cc[2] = {c0, c1};
+                for (int u = 0; u < U; ++u) {
+                    const int64_t r = row0 + gs + i0 + u;
+                    const float dl = step_size<kDt>(widen(dc[u]), bias);
+                    const float dxv = dl * widen(xc[u]);
+                    float gy = widen(yc[u]);
+                    if (gate) gy *= silu_f(widen(zc[u]));
+                    const Tin *brow = Bm + r * kStates, *crow = Cm + r * kStates;
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int n = 2 * k + j;
-                        const float a = fast_exp2(dl * a2[n]);
-                        const float gr = __builtin_fmaf(gy, cc[j], pr[n]);
-                        hf[n] = __builtin_fmaf(a, hf[n], dxv * bb[j]);
-                        pr[n] = a * gr;
+                    for (int k = 0; k < kStates / 2; ++k) {
+                        float b0, b1, c0, c1;
+                        load_pair(brow, k, b0, b1);
+                        load_pair(crow, k, c0, c1);
+                        const float bb[2] = {b0, b1}, cc[2] = {c0, c1};
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const int n = 2 * k + j;
+                            const float a = fast_exp2(dl * a2[n]);
+                            const float gr = __builtin_fmaf(gy, cc[j], pr[n]);
+                            hf[n] = __builtin_fmaf(a, hf[n], dxv * bb[j]);
+                            pr[n] = a * gr;
+                        }
                     }
                 }
+#pragma unroll
+                for (int u = 0; u < U; ++u) { xc[u] = xn[u]; dc[u] = dn[u]; yc[u] = yn[u]; zc[u] = zn[u]; }
             }
             if (live) {
                 float *o = gstate + ((((int64_t)b * ng + (gs + G) / G) * 2) * D + d) * kStates;
@@ -1552,7 +1599,11 @@ __global__ __launch_bounds__(256) void bc_reduce_kernel(const float *__restrict_
 }
 
 // dA [D,N], dDskip [D] (when part_d is given) and (when part_bias is given)
-// the dt_bias gradient [D]: sum the (batch, chunk) partials in order.
+// the dt_bias gradient [D]: sums of the (batch, chunk) partials.  A workgroup
+// covers 64 outputs; its four waves sum interleaved quarters of the partials
+// (k = w, w + 4, ...; eight loads in flight per lane), and wave 0 adds the four
+// in a fixed order, so the result does not depend on timing.
+// grid = ceil((D N + 2 D) / 64) (or D N + D without the bias), block = 256.
 __global__ __launch_bounds__(256) void param_reduce_kernel(const float *__restrict__ part_a,
                                                            const float *__restrict__ part_d,
                                                            float *__restrict__ dA, float *__restrict__ dDskip,
@@ -1560,24 +1611,38 @@ __global__ __launch_bounds__(256) void param_reduce_kernel(const float *__restri
                                                            const float *__restrict__ part_bias,
                                                            float *__restrict__ d_bias, int N)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    __shared__ float acc[4][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x >> 6;
+    const int64_t i = (int64_t)blockIdx.x * kWave + lane;
     const int64_t na = (int64_t)D * N;
+    // which array this output sums, its stride between partials and its index
+    const float *src = nullptr;
+    float *dst = nullptr;
+    int64_t stride = 0, j = 0;
     if (i < na) {
-        float s = 0.f;
-        for (int k = 0; k < n_parts; ++k) s += part_a[(int64_t)k * na + i];
-        dA[i] = s;
+        src = part_a; dst = dA; stride = na; j = i;
     } else if (i < na + D) {
-        if (part_d == nullptr || dDskip == nullptr) return;
-        const int64_t dd = i - na;
-        float s = 0.f;
-        for (int k = 0; k < n_parts; ++k) s += part_d[(int64_t)k * D + dd];
-        dDskip[dd] = s;
-    } else if (i < na + 2 * D && part_bias != nullptr && d_bias != nullptr) {
-        const int64_t dd = i - na - D;
-        float s = 0.f;
-        for (int k = 0; k < n_parts; ++k) s += part_bias[(int64_t)k * D + dd];
-        d_bias[dd] = s;
+        if (part_d != nullptr && dDskip != nullptr) { src = part_d; dst = dDskip; stride = D; j = i - na; }
+    } else if (i < na + 2 * D) {
+        if (part_bias != nullptr && d_bias != nullptr) { src = part_bias; dst = d_bias; stride = D; j = i - na - D; }
     }
+    float s = 0.f;
+    if (src != nullptr) {
+        constexpr int kU = 8;
+        int k = w;
+        for (; k + 4 * (kU - 1) < n_parts; k += 4 * kU) {
+            float v[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) v[u] = src[(int64_t)(k + 4 * u) * stride + j];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) s += v[u];
+        }
+        for (; k < n_parts; k += 4) s += src[(int64_t)k * stride + j];
+    }
+    acc[w][lane] = s;
+    __syncthreads();
+    if (w == 0 && dst != nullptr) dst[j] = ((acc[0][lane] + acc[1][lane]) + acc[2][lane]) + acc[3][lane];
 }
 
 }  // namespace bdssm_dev
