@@ -1292,9 +1292,12 @@ template <int kN> __device__ __forceinline__ float group_sum(float v, int lane) 
 // workgroup keep its LDS below 64 KB at kN = 32 and L = 256.
 // grid = (ceil(D / (NW CW)), chunks, batch), block = 64 NW.
 template <int kFuse> constexpr int bwd_general_waves() { return kFuse == 2 ? 2 : 4; }
+// At 32 states the registers are held to 128 (four waves per SIMD; some
+// spills): measured 17% faster at the 87M shape.  At 4 and 8 states the same
+// bound spills the token loop and is slower, so they keep three.
 
 template <typename Tin, int kN, bool kBlockInit, int kFuse>
-__global__ __launch_bounds__(bwd_general_waves<kFuse>() * kWave) void bwd_general_kernel(
+__global__ __launch_bounds__(bwd_general_waves<kFuse>() * kWave) __attribute__((amdgpu_waves_per_eu(kN == 32 ? 4 : 1))) void bwd_general_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const Tin *__restrict__ Cm, const Tin *__restrict__ dy, const float *__restrict__ A,
     const float *__restrict__ Dskip, const float *__restrict__ h_start, const float *qin,
