@@ -1084,49 +1084,26 @@ __global__ __launch_bounds__(kWave) void adjoint_general_kernel(
     const float bias = (kDt != kDtPlain && dt_bias != nullptr) ? dt_bias[d] : 0.f;
     const Tin *cs = Cm + first * kN;
     int kb = 0;                                   // rows walked since the last block end
-    // rows in stages of U tokens from the right; the next stage's dt, dy (and
-    // z) are loaded before the current stage's arithmetic
-    constexpr int U = 4;
-    auto stage = [&](int p0, Tin *dr, Tin *yr, Tin *zr) {
+    for (int p = len - 1; p >= 0; --p) {
+        if (dbounds != nullptr && kb == 0) {
+            float v[kN];
+            load_row<kN>(dbounds + (((int64_t)b * (nbl + 1) + blk0 + (p + 1) / L) * D + d) * kN, v);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int p = (p0 - u >= 0) ? p0 - u : 0;
-            dr[u] = ds.load(p);
-            yr[u] = ys.load(p);
-            zr[u] = gate ? zs.load(p) : yr[u];
+            for (int n = 0; n < kN; ++n) q[n] += v[n];
         }
-    };
-    Tin dc[U], yc[U], zc[U];
-    stage(len - 1, dc, yc, zc);
-    for (int p0 = len - 1; p0 >= 0; p0 -= U) {
-        Tin dn[U], yn[U], zn[U];
-        if (p0 - U >= 0) stage(p0 - U, dn, yn, zn);
+        const float dl = step_size<kDt>(widen(ds.load(p)), bias);
+        float gy = live ? widen(ys.load(p)) : 0.f;
+        if (gate) gy *= silu_f(widen(zs.load(p)));
+        S += dl;
+        const Tin *crow = cs + (int64_t)p * kN;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int p = p0 - u;
-            if (p < 0) break;
-            if (dbounds != nullptr && kb == 0) {
-                float v[kN];
-                load_row<kN>(dbounds + (((int64_t)b * (nbl + 1) + blk0 + (p + 1) / L) * D + d) * kN, v);
-#pragma unroll
-                for (int n = 0; n < kN; ++n) q[n] += v[n];
-            }
-            const float dl = step_size<kDt>(widen(dc[u]), bias);
-            float gy = live ? widen(yc[u]) : 0.f;
-            if (gate) gy *= silu_f(widen(zc[u]));
-            S += dl;
-            const Tin *crow = cs + (int64_t)p * kN;
-#pragma unroll
-            for (int k = 0; k < kN / 2; ++k) {
-                float c0, c1;
-                load_pair(crow, k, c0, c1);
-                q[2 * k] = fast_exp2(dl * a2[2 * k]) * __builtin_fmaf(gy, c0, q[2 * k]);
-                q[2 * k + 1] = fast_exp2(dl * a2[2 * k + 1]) * __builtin_fmaf(gy, c1, q[2 * k + 1]);
-            }
-            kb = (kb + 1 == L) ? 0 : kb + 1;
+        for (int k = 0; k < kN / 2; ++k) {
+            float c0, c1;
+            load_pair(crow, k, c0, c1);
+            q[2 * k] = fast_exp2(dl * a2[2 * k]) * __builtin_fmaf(gy, c0, q[2 * k]);
+            q[2 * k + 1] = fast_exp2(dl * a2[2 * k + 1]) * __builtin_fmaf(gy, c1, q[2 * k + 1]);
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) { dc[u] = dn[u]; yc[u] = yn[u]; zc[u] = zn[u]; }
+        kb = (kb + 1 == L) ? 0 : kb + 1;
     }
     if (live) {
         store_row<kN>(qout + (((int64_t)b * n_chunks + c) * D + d) * kN, q);
@@ -1172,53 +1149,29 @@ __global__ __launch_bounds__(kWave) void group_state_kernel(
         load_row<kStates>(h_start + (((int64_t)b * (nbl + 1) + blk) * D + d) * kStates, hf);
 #pragma unroll
         for (int n = 0; n < kStates; ++n) pr[n] = 0.f;
-        // rows in stages of U tokens; the next stage's x, dt, dy (and z) are
-        // loaded before the current stage's arithmetic
-        constexpr int U = 4;
-        auto stage = [&](int64_t r0, Tin *xr, Tin *dr, Tin *yr, Tin *zr) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t o = (r0 + u) * D + d;
-                xr[u] = x[o];
-                dr[u] = dt[o];
-                yr[u] = dy[o];
-                zr[u] = gate ? z[o] : yr[u];
-            }
-        };
-        Tin xc[U], dc[U], yc[U], zc[U];
-        stage(row0 + t0, xc, dc, yc, zc);
         for (int64_t gs = t0; gs + G < pend; gs += G) {
-            for (int i0 = 0; i0 < G; i0 += U) {
-                Tin xn[U], dn[U], yn[U], zn[U];
-                // the last stage before the block's final group has no successor
-                const bool more = i0 + U < G || gs + 2 * G < pend;
-                if (more) stage(row0 + gs + i0 + U, xn, dn, yn, zn);
+            for (int i = 0; i < G; ++i) {
+                const int64_t r = row0 + gs + i;
+                const float dl = step_size<kDt>(widen(dt[r * D + d]), bias);
+                const float dxv = dl * widen(x[r * D + d]);
+                float gy = widen(dy[r * D + d]);
+                if (gate) gy *= silu_f(widen(z[r * D + d]));
+                const Tin *brow = Bm + r * kStates, *crow = Cm + r * kStates;
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int64_t r = row0 + gs + i0 + u;
-                    const float dl = step_size<kDt>(widen(dc[u]), bias);
-                    const float dxv = dl * widen(xc[u]);
-                    float gy = widen(yc[u]);
-                    if (gate) gy *= silu_f(widen(zc[u]));
-                    const Tin *brow = Bm + r * kStates, *crow = Cm + r * kStates;
+                for (int k = 0; k < kStates / 2; ++k) {
+                    float b0, b1, c0, c1;
+                    load_pair(brow, k, b0, b1);
+                    load_pair(crow, k, c0, c1);
+                    const float bb[2] = {b0, b1}, cc[2] = {c0, c1};
 #pragma unroll
-                    for (int k = 0; k < kStates / 2; ++k) {
-                        float b0, b1, c0, c1;
-                        load_pair(brow, k, b0, b1);
-                        load_pair(crow, k, c0, c1);
-                        const float bb[2] = {b0, b1}, cc[2] = {c0, c1};
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) {
-                            const int n = 2 * k + j;
-                            const float a = fast_exp2(dl * a2[n]);
-                            const float gr = __builtin_fmaf(gy, cc[j], pr[n]);
-                            hf[n] = __builtin_fmaf(a, hf[n], dxv * bb[j]);
-                            pr[n] = a * gr;
-                        }
+                    for (int j = 0; j < 2; ++j) {
+                        const int n = 2 * k + j;
+                        const float a = fast_exp2(dl * a2[n]);
+                        const float gr = __builtin_fmaf(gy, cc[j], pr[n]);
+                        hf[n] = __builtin_fmaf(a, hf[n], dxv * bb[j]);
+                        pr[n] = a * gr;
                     }
                 }
-#pragma unroll
-                for (int u = 0; u < U; ++u) { xc[u] = xn[u]; dc[u] = dn[u]; yc[u] = yn[u]; zc[u] = zn[u]; }
             }
             if (live) {
                 float *o = gstate + ((((int64_t)b * ng + (gs + G) / G) * 2) * D + d) * kStates;
