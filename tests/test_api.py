@@ -250,6 +250,22 @@ def test_backward_workspace_sizes():
     assert m.workspace_bytes(1, 64, 0, m.OP_TRAIN_BWD) == 0
 
 
+@pytest.mark.parametrize("op", ["OP_TRAIN_BWD", "OP_BLOCKS_BWD"])
+def test_long_block_backward_workspace(op, monkeypatch):
+    """Block lengths that are multiples of 16 above 16 (16 states) add the
+    group states [batch, T/16, 2, D, 16] fp32 to the backward's workspace,
+    also when BDSSM_BWD_KERNEL=general routes them elsewhere (so that a size
+    queried under one setting serves the other)."""
+    batch, D, T = 2, 256, 1024
+    gstate = batch * (T // 16) * 2 * D * 16 * 4
+    op = getattr(m, op)
+    n32 = m.workspace_bytes(batch, D, T, op, block_len=32)
+    assert n32 >= gstate
+    monkeypatch.setenv("BDSSM_BWD_KERNEL", "general")
+    assert m.workspace_bytes(batch, D, T, op, block_len=32) >= gstate
+    assert m.workspace_bytes(batch, D, T, op, block_len=64) >= gstate
+
+
 def test_fusion_argument_errors():
     f = B.Fusion(MIS, 1, None)                         # misaligned bias
     s = shape()
