@@ -550,6 +550,13 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 // LDS one group ahead and widened to fp32 in place by the lane that loaded
 // them.  Arguments and the other partial outputs as in bwd_wave_kernel.
 //
+// L = 0 (long blocks: Lr tokens, a multiple of 16 above 16): a block spans
+// several groups.  Groups are still walked right to left, so hr and the
+// forward adjoint carry from a group into the one on its left and restart
+// only where a block ends; the forward state and the reverse adjoint's carry
+// at a group start inside a block come from group_state_kernel (gstate), at a
+// block start from the block state and zero.  Chunks are whole blocks.
+//
 // kFuse (the gradients of the forward's fusions, BwdFuse): the dt rows are
 // turned into the step size of the forward (step_size<dt_mode> with dt_bias)
 // as they are widened; with the gate z (staged as a fourth row stream), dy
