@@ -958,7 +958,7 @@ void launch_bwd_reduce(const BwdWorkspace &w, void *dB, void *dC, float *dA, flo
     const bool sep = gr != nullptr;
     const int64_t nbc = batch * T * 2 * N;
     const int nblk = (int)ceil_div(D, bwd_channels(L, N, fused, sep));
-    hipLaunchKernelGGL((bc_reduce_kernel<Tin>), dim3((unsigned)ceil_div(nbc, 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL((bc_reduce_kernel<Tin>), dim3((unsigned)ceil_div(nbc / 4, 256)), dim3(256), 0, st,
                        w.part_bc, (Tin *)dB, (Tin *)dC, (int)batch, T, nblk, (int)N);
     const bool nb = fused && d_bias != nullptr;
     hipLaunchKernelGGL(param_reduce_kernel, dim3((unsigned)ceil_div(D * (N + (nb ? 2 : 1)), kWave)),
@@ -966,7 +966,7 @@ void launch_bwd_reduce(const BwdWorkspace &w, void *dB, void *dC, float *dA, flo
                        nb ? w.part_bias : nullptr, nb ? d_bias : nullptr, (int)N);
     if (sep) {
         // the reverse operands' dB_r, dC_r, dA_r (and their bias gradient)
-        hipLaunchKernelGGL((bc_reduce_kernel<Tin>), dim3((unsigned)ceil_div(nbc, 256)), dim3(256), 0, st,
+        hipLaunchKernelGGL((bc_reduce_kernel<Tin>), dim3((unsigned)ceil_div(nbc / 4, 256)), dim3(256), 0, st,
                            w.part_bc_r, (Tin *)gr->dB_rev, (Tin *)gr->dC_rev, (int)batch, T, nblk, (int)N);
         const bool nbr = gr->d_dt_bias_rev != nullptr;
         hipLaunchKernelGGL(param_reduce_kernel, dim3((unsigned)ceil_div(D * (N + 2), kWave)), dim3(256), 0, st,

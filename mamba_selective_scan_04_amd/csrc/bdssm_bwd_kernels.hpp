@@ -1541,24 +1541,43 @@ __global__ __launch_bounds__(bwd_general_waves<kFuse>() * kWave) __attribute__((
     }
 }
 
-// dB and dC: sum the channel-block partials in order.  One thread per
-// (batch, token, j), j < N -> dB state j, j >= N -> dC state j - N.
+// dB and dC: sum the channel-block partials in order.  One thread per four
+// consecutive columns of one (batch, token) row (16-byte loads; 2N is a
+// multiple of 4), j < N -> dB states j .. j + 3, else dC states j - N ..;
+// eight channel blocks' loads in flight, each column summed over the blocks
+// in increasing order.  grid = ceil(batch T 2N / 4 / 256), block = 256.
 template <typename Tin>
 __global__ __launch_bounds__(256) void bc_reduce_kernel(const float *__restrict__ part_bc, Tin *__restrict__ dB,
                                                         Tin *__restrict__ dC, int batch, int64_t T, int nblk,
                                                         int N)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     const int ncol = 2 * N;
     if (i >= (int64_t)batch * T * ncol) return;
     const int j = (int)(i % ncol);
     const int64_t bt = i / ncol;
     const int64_t b = bt / T, t = bt % T;
-    const float *p = part_bc + (b * nblk * T + t) * ncol + j;
-    float s = 0.f;
-    for (int k = 0; k < nblk; ++k) s += p[(int64_t)k * T * ncol];
-    if (j < N) dB[bt * N + j] = narrow<Tin>(s);
-    else dC[bt * N + j - N] = narrow<Tin>(s);
+    const float4 *p = reinterpret_cast<const float4 *>(part_bc + (b * nblk * T + t) * ncol + j);
+    const int64_t stride = T * ncol / 4;          // one channel block, in float4
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    constexpr int kU = 8;
+    int k = 0;
+    for (; k + kU <= nblk; k += kU) {
+        float4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) v[u] = p[(int64_t)(k + u) * stride];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) { s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w; }
+    }
+    for (; k < nblk; ++k) {
+        const float4 v = p[(int64_t)k * stride];
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    Tin *o = (j < N) ? dB + bt * N + j : dC + bt * N + j - N;
+    o[0] = narrow<Tin>(s.x);
+    o[1] = narrow<Tin>(s.y);
+    o[2] = narrow<Tin>(s.z);
+    o[3] = narrow<Tin>(s.w);
 }
 
 // dA [D,N], dDskip [D] (when part_d is given) and (when part_bias is given)
