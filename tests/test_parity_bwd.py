@@ -214,13 +214,15 @@ def test_both_backward_kernels(dev, kernel, L, monkeypatch):
     check(gb, rb, PARAM_GRADS + ("dh0_blocks",), STATE_TOL, kernel + " blocks")
 
 
-def test_training_step_graph_replays_match_eager(dev, monkeypatch):
+@pytest.mark.parametrize("L", [16, 32, 64])
+def test_training_step_graph_replays_match_eager(dev, L, monkeypatch):
     """The whole all-block training step (both forms, forward and backward,
     caller workspaces) captured in one HIP graph: every replay, with eager
     work in between, reproduces the eager gradients bit for bit (the library
-    records no memset nodes and allocates nothing)."""
+    records no memset nodes and allocates nothing).  L = 32 and 64 run the
+    long-block kernels (segmented forward, group states, pair backward)."""
     monkeypatch.setenv("BDSSM_CHUNK", "64")
-    batch, T, D, L = 2, 512, 96, 16
+    batch, T, D = 2, 512, 96
     c = Case(batch, T, D, torch.bfloat16, sid=40, a_kind="random")
     dy = seeded((batch, T, D), 4001, torch.bfloat16)
     y = torch.empty_like(c.dev["x"])
