@@ -253,9 +253,11 @@ def test_backward_workspace_sizes():
 @pytest.mark.parametrize("op", ["OP_TRAIN_BWD", "OP_BLOCKS_BWD"])
 def test_long_block_backward_workspace(op, monkeypatch):
     """Block lengths that are multiples of 16 above 16 (16 states) add the
-    group states [batch, T/16, 2, D, 16] fp32 to the backward's workspace,
-    also when BDSSM_BWD_KERNEL=general routes them elsewhere (so that a size
-    queried under one setting serves the other)."""
+    group states [batch, T/16, 2, D, 16] fp32 to the backward's workspace; the
+    query reserves them also when BDSSM_BWD_KERNEL=general routes these
+    lengths to the general kernel (whose other arrays differ in size: a call
+    under another setting than the query's is refused when its workspace is
+    too small)."""
     batch, D, T = 2, 256, 1024
     gstate = batch * (T // 16) * 2 * D * 16 * 4
     op = getattr(m, op)
