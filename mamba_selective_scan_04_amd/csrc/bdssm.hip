@@ -595,14 +595,50 @@ void launch_block_bidir_k(dim3 g, int64_t L, const void *x, const void *dt, cons
                        h0_blocks, f.args<Tin>(), seg);
 }
 
+// A single block per batch row (T == L, one chunk, no block states) above 32
+// tokens at up to 16 states: block_split_kernel spreads the block's tokens
+// over up to 8 waves (at 8 x 1536 channels: 35 / 50 / 89 us at L = 64 / 128 /
+// 256 against 65 / 165 / 469 us on block_bidir_kernel; at L = 32 the latter
+// is slightly faster).  BDSSM_SPLIT=0 keeps block_bidir_kernel (tests).
+bool use_split(int64_t L, int64_t N, int64_t T, int n_chunks, const float *bounds, const float *h0_blocks) {
+    if (N > 16 || L <= 2 * kGroup || T != L || n_chunks != 1 || bounds != nullptr || h0_blocks != nullptr) return false;
+    const char *v = getenv("BDSSM_SPLIT");
+    return !(v != nullptr && v[0] == '0');
+}
+
+template <typename Tin, int kN>
+void launch_block_split(int64_t L, const void *x, const void *dt, const void *B, const void *C,
+                        const float *A, const float *Dskip, const float *hin, int64_t hin_bs, void *y,
+                        float *hout, int64_t batch, int64_t D, const Fuse &f, hipStream_t st) {
+    if constexpr (kN <= 16) {
+        const int nw = (int)(ceil_div(L, kGroup) < 8 ? ceil_div(L, kGroup) : 8);   // segments <= kSplitSeg
+        const size_t lds = (size_t)nw * (kN + 1) * kWave * sizeof(float);
+        const dim3 g((unsigned)ceil_div(D, kWave), 1u, (unsigned)batch);
+#define BDSSM_SPLIT_K(KDT)                                                                                   \
+    hipLaunchKernelGGL((block_split_kernel<Tin, kN, KDT>), g, dim3(nw * kWave), lds, st, (const Tin *)x,    \
+                       (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip, hin, hin_bs, (Tin *)y, hout, \
+                       (int)D, (int)L, f.args<Tin>())
+        switch (f.dt_mode) {
+        case kDtSoftplus: BDSSM_SPLIT_K(kDtSoftplus); break;
+        case kDtBias: BDSSM_SPLIT_K(kDtBias); break;
+        default: BDSSM_SPLIT_K(kDtPlain); break;
+        }
+#undef BDSSM_SPLIT_K
+    }
+}
+
 // Bidirectional pass with block_bidir_kernel (any L <= kMaxLdsBlock; Tc a
-// multiple of L).
+// multiple of L), or block_split_kernel for a single block per row.
 template <typename Tin, int kN>
 void launch_block_bidir(int64_t L, const void *x, const void *dt, const void *B, const void *C,
                         const float *A, const float *Dskip, const float *hin, int64_t hin_bs,
                         int64_t hin_cs, void *y, float *bounds, float *hout, int64_t batch,
                         int64_t T, int64_t D, int64_t Tc, int n_chunks, const float *h0_blocks,
                         const Fuse &f, hipStream_t st) {
+    if (use_split(L, kN, T, n_chunks, bounds, h0_blocks)) {
+        launch_block_split<Tin, kN>(L, x, dt, B, C, A, Dskip, hin, hin_bs, y, hout, batch, D, f, st);
+        return;
+    }
     const dim3 g = grid3(D, n_chunks, batch);
 #define BDSSM_BLOCK(INIT, KDT)                                                                       \
     launch_block_bidir_k<Tin, kN, INIT, KDT>(g, L, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, \

@@ -1161,6 +1161,181 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kN <= 16 
     }
 }
 
+// One block per batch row (the block step, the commit with outputs), block
+// lengths above 16, up to 16 states: block_bidir_kernel would walk the whole
+// block in one wave per 64 channels (batch * D / 64 waves in all).  Here the
+// block's tokens are split over the NW waves of the workgroup (segments of
+// ceil(L / NW) <= kSplitSeg tokens), all on the same 64 channels (lane =
+// channel):
+//   1. each wave walks its segment forward from a zero state, state only, and
+//      leaves the local state and the sum of its step sizes in LDS (the decay
+//      over a segment is exp2(A' sum dt)); each wave combines hin with the
+//      segments left of it into the state entering its segment;
+//   2. the same in reverse: local states from zero at the segment's right
+//      end, combined over the segments right of it (zero at the block's end);
+//   3. each wave walks its segment forward, keeping sum_n C hf per token in
+//      registers, then in reverse, adding sum_n C hr + Dskip x (times
+//      silu(z)) and storing y; the last wave stores the final forward state
+//      in hout.
+// hout may alias hin (commit): every wave reads hin before the barriers that
+// precede the store.  Fusions and separate reverse operands as in
+// block_bidir_kernel.  LDS: NW (kN + 1) 256 bytes (one direction at a time).
+// grid = (ceil(D/64), 1, batch), block = 64 NW (NW <= 8).
+constexpr int kSplitSeg = 32;
+
+template <typename Tin, int kN, int kDt>
+__global__ __launch_bounds__(8 * kWave) void block_split_kernel(
+    const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
+    const Tin *__restrict__ Cm, const float *__restrict__ A, const float *__restrict__ Dskip,
+    const float *hin, int64_t hin_bs, Tin *__restrict__ y, float *hout, int D, int L,
+    FuseArgs<Tin> fz)
+{
+    static_assert(kN % 2 == 0 && kN <= 16, "B and C rows are read in pairs; registers");
+    extern __shared__ float lds_split[];          // [NW][kN + 1][64]
+    const int NW = blockDim.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const int d_raw = blockIdx.x * kWave + lane;
+    const bool live = d_raw < D;
+    const int d = live ? d_raw : D - 1;
+    const int b = blockIdx.z;
+    const int SL = (L + NW - 1) / NW;
+    const int s0 = (w * SL < L) ? w * SL : L;
+    const int ns = ((s0 + SL < L) ? s0 + SL : L) - s0;       // tokens of this segment (uniform)
+    auto slot = [&](int k, int n) -> float & { return lds_split[((size_t)k * (kN + 1) + n) * kWave + lane]; };
+
+    const bool gate = fz.z != nullptr;
+    const bool sep = fz.dt_r != nullptr;
+    float a2[kN], a2r[kN], h[kN], hr[kN];
+    load_row<kN>(A + (int64_t)d * kN, a2);
+    load_row<kN>((sep ? fz.A_r : A) + (int64_t)d * kN, a2r);
+#pragma unroll
+    for (int n = 0; n < kN; ++n) { a2[n] *= kLog2e; a2r[n] *= kLog2e; }
+    const float dsk = Dskip[d];
+    const float bias = (kDt != kDtPlain && fz.dt_bias != nullptr) ? fz.dt_bias[d] : 0.f;
+    const float bias_r = sep ? ((kDt != kDtPlain && fz.dt_bias_r != nullptr) ? fz.dt_bias_r[d] : 0.f) : bias;
+    const int64_t first = (int64_t)b * L;
+    const Rows<Tin> xs(x + first * D, L, D, d);
+    const Rows<Tin> ds(dt + first * D, L, D, d);
+    const Rows<Tin> rds((sep ? fz.dt_r : dt) + first * D, L, D, d);
+    const Rows<Tin> zs((gate ? fz.z : x) + first * D, L, D, d);
+    const Rows<Tin> ys(y + first * D, L, D, d);
+    const Tin *bs = Bm + first * kN, *cs = Cm + first * kN;
+    const Tin *rbs = (sep ? fz.B_r : Bm) + first * kN, *rcs = (sep ? fz.C_r : Cm) + first * kN;
+
+    // one state-only token: st <- exp2(dl a) st + dl x B
+    auto state_tok = [&](float *st, const float *aa, const Tin *brow, float dl, float xv) {
+        const float dx = dl * xv;
+#pragma unroll
+        for (int q = 0; q < kN / 2; ++q) {
+            float b0, b1;
+            load_pair(brow, q, b0, b1);
+            st[2 * q] = __builtin_fmaf(fast_exp2(dl * aa[2 * q]), st[2 * q], dx * b0);
+            st[2 * q + 1] = __builtin_fmaf(fast_exp2(dl * aa[2 * q + 1]), st[2 * q + 1], dx * b1);
+        }
+    };
+
+    // 1. forward: local state of the segment, then the state entering it
+    {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) h[n] = 0.f;
+        float S = 0.f;
+        for (int i = 0; i < ns; ++i) {
+            const int p = s0 + i;
+            const float dl = step_size<kDt>(widen(ds.load(p)), bias);
+            S += dl;
+            state_tok(h, a2, bs + (int64_t)p * kN, dl, widen(xs.load(p)));
+        }
+#pragma unroll
+        for (int n = 0; n < kN; ++n) slot(w, n) = h[n];
+        slot(w, kN) = S;
+    }
+    __syncthreads();
+    if (hin != nullptr) {
+        load_row<kN>(hin + (int64_t)b * hin_bs + (int64_t)d * kN, h);
+    } else {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) h[n] = 0.f;
+    }
+    for (int k = 0; k < w; ++k) {
+        const float S = slot(k, kN);
+#pragma unroll
+        for (int n = 0; n < kN; ++n) h[n] = __builtin_fmaf(fast_exp2(S * a2[n]), h[n], slot(k, n));
+    }
+    __syncthreads();          // the slots are reused; every read of hin precedes the store to hout
+    // 2. reverse: local state of the segment, then the state entering it from the right
+    {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) hr[n] = 0.f;
+        float S = 0.f;
+        for (int i = ns - 1; i >= 0; --i) {
+            const int p = s0 + i;
+            const float dl = step_size<kDt>(widen(rds.load(p)), bias_r);
+            S += dl;
+            state_tok(hr, a2r, rbs + (int64_t)p * kN, dl, widen(xs.load(p)));
+        }
+#pragma unroll
+        for (int n = 0; n < kN; ++n) slot(w, n) = hr[n];
+        slot(w, kN) = S;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < kN; ++n) hr[n] = 0.f;
+    for (int k = NW - 1; k > w; --k) {
+        const float S = slot(k, kN);
+#pragma unroll
+        for (int n = 0; n < kN; ++n) hr[n] = __builtin_fmaf(fast_exp2(S * a2r[n]), hr[n], slot(k, n));
+    }
+    // 3. the outputs of the segment
+    float yf[kSplitSeg];
+#pragma unroll
+    for (int i = 0; i < kSplitSeg; ++i) {
+        if (i < ns) {
+            const int p = s0 + i;
+            const float dl = step_size<kDt>(widen(ds.load(p)), bias);
+            const float dx = dl * widen(xs.load(p));
+            const Tin *brow = bs + (int64_t)p * kN, *crow = cs + (int64_t)p * kN;
+            float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+            for (int q = 0; q < kN / 2; ++q) {
+                float b0, b1, c0, c1;
+                load_pair(brow, q, b0, b1);
+                load_pair(crow, q, c0, c1);
+                h[2 * q] = __builtin_fmaf(fast_exp2(dl * a2[2 * q]), h[2 * q], dx * b0);
+                h[2 * q + 1] = __builtin_fmaf(fast_exp2(dl * a2[2 * q + 1]), h[2 * q + 1], dx * b1);
+                acc0 = __builtin_fmaf(c0, h[2 * q], acc0);
+                acc1 = __builtin_fmaf(c1, h[2 * q + 1], acc1);
+            }
+            yf[i] = acc0 + acc1;
+        }
+    }
+    if (w == NW - 1 && hout != nullptr && live) store_row<kN>(hout + ((int64_t)b * D + d) * kN, h);
+#pragma unroll
+    for (int i = kSplitSeg - 1; i >= 0; --i) {
+        if (i < ns) {
+            const int p = s0 + i;
+            const float xv = widen(xs.load(p));
+            const float dl = step_size<kDt>(widen(rds.load(p)), bias_r);
+            const float dx = dl * xv;
+            const Tin *brow = rbs + (int64_t)p * kN, *crow = rcs + (int64_t)p * kN;
+            float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+            for (int q = 0; q < kN / 2; ++q) {
+                float b0, b1, c0, c1;
+                load_pair(brow, q, b0, b1);
+                load_pair(crow, q, c0, c1);
+                hr[2 * q] = __builtin_fmaf(fast_exp2(dl * a2r[2 * q]), hr[2 * q], dx * b0);
+                hr[2 * q + 1] = __builtin_fmaf(fast_exp2(dl * a2r[2 * q + 1]), hr[2 * q + 1], dx * b1);
+                acc0 = __builtin_fmaf(c0, hr[2 * q], acc0);
+                acc1 = __builtin_fmaf(c1, hr[2 * q + 1], acc1);
+            }
+            float tot = __builtin_fmaf(dsk, xv, yf[i] + (acc0 + acc1));
+            if (gate) tot *= silu_f(widen(zs.load(p)));
+            if (live) ys.store(p, narrow<Tin>(tot));
+        }
+    }
+}
+
 // dst[i] = src[i], or 0 when src is null.  A kernel rather than a memset or
 // memcpy node so that callers may capture the entry points in a HIP graph.
 __global__ __launch_bounds__(256) void copy_or_zero_kernel(const float *src, float *dst, int64_t n)

@@ -256,3 +256,50 @@ def test_long_block_forward_segments(dev, seg, L, N_, dtype, variant, monkeypatc
     close(y, yo, TOL[dtype], label + " y")
     close(bnd, bo, STATE_TOL, label + " h_bounds")
     close(yb, ybo, TOL[dtype], label + " two-stream y")
+
+
+SPLIT = [  # (L, N, dtype, variant)
+    (32, 16, torch.bfloat16, "plain"),
+    (100, 8, torch.float32, "fused"),
+    (256, 16, torch.bfloat16, "rev"),
+    (48, 4, torch.float32, "plain"),
+    (17, 16, torch.float32, "fused"),
+]
+
+
+@pytest.mark.parametrize("split", ["1", "0"])
+@pytest.mark.parametrize("L,N_,dtype,variant", SPLIT)
+def test_single_block_long(dev, split, L, N_, dtype, variant, monkeypatch):
+    """The block step and the commit with outputs on one block longer than 16
+    tokens: above 32 tokens block_split_kernel (the block's tokens over up to
+    8 waves, segment states combined in LDS; the commit's cache read and
+    written in place), else and when forced off block_bidir_kernel; 4 to 16
+    states, 130 channels, the fusions and separate reverse operands, against
+    the oracle from a seeded cache."""
+    monkeypatch.setenv("BDSSM_SPLIT", split)
+    batch, D = 2, 130
+    sid = 420 + SPLIT.index((L, N_, dtype, variant))
+    c = Case(batch, L, D, dtype, sid=sid, a_kind="random", n=N_)
+    kw, ok = {}, {}
+    if variant == "fused":
+        c.dev["dt"] = synth.normal((batch, L, D), 1000 * sid + 1, "cpu", torch.float32, mean=-1.0,
+                                   std=0.5).to(dtype).to("cuda").contiguous()
+        bias = synth.normal((D,), 1000 * sid + 2, "cuda", torch.float32, std=0.3)
+        z = synth.normal((batch, L, D), 1000 * sid + 3, "cuda", dtype, std=2.0)
+        kw = dict(dt_bias=bias, dt_softplus=True, z=z)
+        ok = dict(dt_bias=to_np(bias), dt_softplus=True, z=synth.to_oracle(z))
+    elif variant == "rev":
+        rev = _rev_operands(batch, L, D, dtype, sid, with_bias=False)
+        kw, ok = dict(rev=rev), dict(rev=_rev_oracle(rev))
+    h = synth.normal((batch, D, N_), 1000 * sid + 5, "cuda", std=0.5)
+    ys = m.block_step(h, *c.args()[:6], **kw)
+    hc = h.clone()
+    _, yc = m.commit(hc, *c.args()[:6], want_y=True, **kw)
+    torch.cuda.synchronize()
+    oa = c.oracle_args()
+    ho = to_np(h)
+    label = "split %s L=%d N=%d %s" % (split, L, N_, variant)
+    close(ys, oracle.block_step(ho, *oa[:6], **ok), TOL[dtype], label + " block_step y")
+    hco, yco = oracle.commit(ho, *oa[:6], want_y=True, **ok)
+    close(yc, yco, TOL[dtype], label + " commit y")
+    close(hc, hco, STATE_TOL, label + " commit state")
