@@ -1,22 +1,33 @@
-"""Build step of the HIP library: compiles csrc/bdssm.hip for gfx950 into
-libbdssm.so next to this file (in-tree, so it travels with the source tree).
+"""Build step of the HIP library: compiles the sources under csrc/ for gfx950
+and links libbdssm.so next to this file (in-tree, so it travels with the
+source tree).
 
-    python -m mamba_selective_scan_04_amd.build
+    python -m mamba_selective_scan_04_amd.build            # everything
+    python -m mamba_selective_scan_04_amd.build --changed  # only objects older than their sources
+
+The kernel launchers live in launch_*.hip; each is compiled twice, once per
+stream type (-DBDSSM_TIN=float and -DBDSSM_TIN=uint16_t, the bf16 bits), so
+that the template instantiations spread over parallel compiler processes.
+bdssm.hip holds the C ABI and the launch plans.  Objects go to _build/.
 """
+import concurrent.futures
 import os
 import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "bdssm.hip")
-DEPS = [SRC, os.path.join(HERE, "csrc", "bdssm_kernels.hpp"), os.path.join(HERE, "csrc", "bdssm_bwd_kernels.hpp"),
-        os.path.join(ROOT, "include", "bdssm.h")]
+CSRC = os.path.join(HERE, "csrc")
+BUILD_DIR = os.path.join(HERE, "_build")
+HEADERS = [os.path.join(CSRC, h) for h in ("bdssm_kernels.hpp", "bdssm_bwd_kernels.hpp", "bdssm_launch.hpp")] + [
+    os.path.join(ROOT, "include", "bdssm.h")]
+LAUNCH_UNITS = ("launch_chunk", "launch_bidir", "launch_block", "launch_bwd", "launch_bwd_general")
+STREAM_TYPES = (("f32", "float"), ("bf16", "uint16_t"))
 LIB = os.path.join(HERE, "libbdssm.so")
 ARCH = os.environ.get("BDSSM_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "--offload-arch=" + ARCH, "-fPIC", "-shared",
+    "-O3", "-std=c++17", "--offload-arch=" + ARCH, "-fPIC",
     # keep the compiler from forming packed fp32 instructions (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
@@ -29,30 +40,77 @@ def hipcc():
     return p if os.path.exists(p) else "hipcc"
 
 
+def units():
+    """(source, object, extra flags) of every translation unit."""
+    out = [(os.path.join(CSRC, "bdssm.hip"), os.path.join(BUILD_DIR, "bdssm.o"), [])]
+    for u in LAUNCH_UNITS:
+        for tag, ctype in STREAM_TYPES:
+            out.append((os.path.join(CSRC, u + ".hip"), os.path.join(BUILD_DIR, "%s.%s.o" % (u, tag)),
+                        ["-DBDSSM_TIN=" + ctype]))
+    return out
+
+
+def sources():
+    return sorted({s for s, _, _ in units()}) + HEADERS
+
+
 def up_to_date():
-    return os.path.exists(LIB) and all(os.path.getmtime(LIB) >= os.path.getmtime(d) for d in DEPS)
+    return os.path.exists(LIB) and all(os.path.getmtime(LIB) >= os.path.getmtime(d) for d in sources())
 
 
-def build(verbose=False):
-    """Always compiles (the build check must exercise the compiler)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include"), "-o", tmp, SRC]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+def _clean(out):
     # the host pass does not know the packed-fp32 feature and says so; drop that line
-    out = "\n".join(l for l in r.stdout.splitlines() if "not a recognized feature" not in l)
+    return "\n".join(l for l in out.splitlines() if "not a recognized feature" not in l)
+
+
+def _compile(src, obj, extra):
+    tmp = obj + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + HIPCC_FLAGS + extra + ["-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c", "-o", tmp, src]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = _clean(r.stdout)
     if r.returncode != 0:
         if os.path.exists(tmp):
             os.remove(tmp)
-        raise RuntimeError("hipcc failed (%d):\n%s" % (r.returncode, out))
-    if out.strip() and verbose:
-        print(out)
+        raise RuntimeError("hipcc failed (%d) on %s:\n%s\n%s" % (r.returncode, os.path.basename(obj), " ".join(cmd), out))
+    os.replace(tmp, obj)
+    return out
+
+
+def build(verbose=False, changed_only=False, jobs=None):
+    """Compiles every translation unit (all of them unless changed_only, which
+    skips objects newer than their source and every header) and links the
+    library."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    todo = []
+    for src, obj, extra in units():
+        if changed_only and os.path.exists(obj):
+            t = os.path.getmtime(obj)
+            if all(os.path.getmtime(d) <= t for d in [src] + HEADERS):
+                continue
+        todo.append((src, obj, extra))
+    jobs = jobs or min(len(todo) or 1, os.cpu_count() or 4, 12)
+    if verbose:
+        print("compiling %d of %d translation units with %d jobs" % (len(todo), len(units()), jobs), flush=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        futs = {ex.submit(_compile, *t): t for t in todo}
+        for fu in concurrent.futures.as_completed(futs):
+            out = fu.result()
+            if verbose:
+                print("  built", os.path.basename(futs[fu][1]), flush=True)
+                if out.strip():
+                    print(out)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + [o for _, o, _ in units()]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        if os.path.exists(tmp):
+            os.remove(tmp)
+        raise RuntimeError("link failed (%d):\n%s" % (r.returncode, _clean(r.stdout)))
     os.replace(tmp, LIB)
     return LIB
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, changed_only="--changed" in sys.argv[1:])
     print("built", LIB)
     sys.exit(0)

@@ -1,6 +1,6 @@
 // bdssm_bwd_kernels.hpp -- gfx950 kernels of the backward pass (reverse-mode
-// gradients) of the all-block training forms.  Device code only; launch
-// policy and the C ABI are in bdssm.hip.
+// gradients) of the all-block training forms.  Device code only; the launch
+// plans and the C ABI are in bdssm.hip, the launchers in launch_bwd*.hip.
 //
 // Page cited: gist.science German page on arXiv 2607.02805, "Technische
 // Zusammenfassung" > "Methodik" [DE-M]: the all-block objective lets the
@@ -1586,7 +1586,7 @@ __global__ __launch_bounds__(256) void bc_reduce_kernel(const float *__restrict_
 // (k = w, w + 4, ...; eight loads in flight per lane), and wave 0 adds the four
 // in a fixed order, so the result does not depend on timing.
 // grid = ceil((D N + 2 D) / 64) (or D N + D without the bias), block = 256.
-__global__ __launch_bounds__(256) void param_reduce_kernel(const float *__restrict__ part_a,
+static __global__ __attribute__((unused)) __launch_bounds__(256) void param_reduce_kernel(const float *__restrict__ part_a,
                                                            const float *__restrict__ part_d,
                                                            float *__restrict__ dA, float *__restrict__ dDskip,
                                                            int D, int n_parts,

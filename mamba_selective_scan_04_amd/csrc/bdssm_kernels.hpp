@@ -1,6 +1,6 @@
 // bdssm_kernels.hpp -- gfx950 (CDNA4, wave64) kernels of the block-restricted
-// bidirectional selective scan.  Device code only; the launch policy and the
-// C ABI are in bdssm.hip.
+// bidirectional selective scan.  Device code only; the launch plans and the
+// C ABI are in bdssm.hip, the launchers in launch_*.hip.
 //
 // Pages cited (arXiv 2607.02805, "Training Hybrid Block Diffusion Language
 // Models with Partial Bidirectionality"):
@@ -1338,7 +1338,7 @@ __global__ __launch_bounds__(8 * kWave) void block_split_kernel(
 
 // dst[i] = src[i], or 0 when src is null.  A kernel rather than a memset or
 // memcpy node so that callers may capture the entry points in a HIP graph.
-__global__ __launch_bounds__(256) void copy_or_zero_kernel(const float *src, float *dst, int64_t n)
+static __global__ __attribute__((unused)) __launch_bounds__(256) void copy_or_zero_kernel(const float *src, float *dst, int64_t n)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) dst[i] = src != nullptr ? src[i] : 0.f;

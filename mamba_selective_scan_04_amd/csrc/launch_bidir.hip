@@ -1,0 +1,76 @@
+// launch_bidir.hip -- launchers of the register-resident bidirectional wave kernel
+// (bidir_wave_kernel: block lengths 1, 2, 4, 8, 16 at 16 states).
+// Compiled once per stream type (BDSSM_TIN = float, or uint16_t for bf16).
+#include "bdssm_launch.hpp"
+
+#ifndef BDSSM_TIN
+#error "compiled once per stream type: -DBDSSM_TIN=float or -DBDSSM_TIN=uint16_t"
+#endif
+
+namespace bdssm_host {
+
+template <typename Tin, int L, bool kInit, int kFuse>
+void launch_bidir_k(dim3 g, const void *x, const void *dt, const void *B, const void *C,
+                    const float *A, const float *Dskip, const float *hin, int64_t hin_bs,
+                    int64_t hin_cs, void *y, float *bounds, float *hout, int64_t T, int64_t D,
+                    int64_t Tc, const float *h0_blocks, const Fuse &f, hipStream_t st) {
+    hipLaunchKernelGGL((bidir_wave_kernel<Tin, L, kInit, kFuse>), g, dim3(4 * kWave), 0, st,
+                       (const Tin *)x, (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip,
+                       hin, hin_bs, hin_cs, (Tin *)y, bounds, hout, T, (int)D, Tc, h0_blocks,
+                       f.args<Tin>());
+}
+
+template <typename Tin, int L>
+void launch_bidir_L(const void *x, const void *dt, const void *B, const void *C, const float *A,
+                    const float *Dskip, const float *hin, int64_t hin_bs, int64_t hin_cs, void *y,
+                    float *bounds, float *hout, int64_t batch, int64_t T, int64_t D, int64_t Tc,
+                    int n_chunks, const float *h0_blocks, const Fuse &f, hipStream_t st) {
+    const dim3 g = grid3(D, n_chunks, batch);
+    // kernel variant: 0 plain, 1 fused step size / gate, 2 also separate
+    // reverse operands
+    const int fv = f.dt_r != nullptr ? 2 : f.any() ? 1 : 0;
+#define BDSSM_BIDIR(INIT, FV)                                                                       \
+    launch_bidir_k<Tin, L, INIT, FV>(g, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, T, D, \
+                                     Tc, h0_blocks, f, st)
+    if (h0_blocks != nullptr) {
+        if (fv == 2) BDSSM_BIDIR(true, 2);
+        else if (fv == 1) BDSSM_BIDIR(true, 1);
+        else BDSSM_BIDIR(true, 0);
+    } else {
+        if (fv == 2) BDSSM_BIDIR(false, 2);
+        else if (fv == 1) BDSSM_BIDIR(false, 1);
+        else BDSSM_BIDIR(false, 0);
+    }
+#undef BDSSM_BIDIR
+}
+
+// The bidirectional pass: the wave kernels for N = 16 and L | 16, else
+// block_bidir_kernel (Tc then a multiple of L).
+template <typename Tin>
+void launch_bidir(int64_t L, const void *x, const void *dt, const void *B, const void *C,
+                  const float *A, const float *Dskip, const float *hin, int64_t hin_bs,
+                  int64_t hin_cs, void *y, float *bounds, float *hout, int64_t batch, int64_t T,
+                  int64_t D, int64_t N, int64_t Tc, int n_chunks, hipStream_t st,
+                  const float *h0_blocks, const Fuse &f) {
+    if (!wave_path(L, N)) {
+        launch_block_bidir_any<Tin>(N, L, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout,
+                                    batch, T, D, Tc, n_chunks, h0_blocks, f, st);
+        return;
+    }
+    switch (L) {
+    case 1: launch_bidir_L<Tin, 1>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
+    case 2: launch_bidir_L<Tin, 2>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
+    case 4: launch_bidir_L<Tin, 4>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
+    case 8: launch_bidir_L<Tin, 8>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
+    default: launch_bidir_L<Tin, 16>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
+    }
+}
+
+// ------------------------------------------------ explicit instantiations
+
+template void launch_bidir<BDSSM_TIN>(int64_t, const void *, const void *, const void *, const void *,
+                                    const float *, const float *, const float *, int64_t, int64_t, void *,
+                                    float *, float *, int64_t, int64_t, int64_t, int64_t, int64_t, int,
+                                    hipStream_t, const float *, const Fuse &);
+
+}  // namespace bdssm_host

@@ -23,7 +23,9 @@ import os
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = [os.path.join(HERE, "csrc", "bdssm_kernels.hpp"), os.path.join(HERE, "csrc", "bdssm.hip")]
+# every kernel and launch source: a change to any of them marks a summary stale
+KERNEL_SOURCES = sorted(os.path.join(HERE, "csrc", f) for f in os.listdir(os.path.join(HERE, "csrc"))
+                        if f.endswith((".hip", ".hpp")))
 COPY_BYTES = 1 << 30
 
 
