@@ -35,7 +35,7 @@ void launch_block_lane(int64_t N, const void *x, const void *dt, const void *B, 
 // N <= 16: 32 tokens; 8 at N = 32: 64), no smaller, since every segment
 // boundary adds state-only reverse work (measured on MI355X at the 87M
 // training shape).  BDSSM_SEG overrides (tuning, tests).
-int block_seg(int64_t L, int64_t N) {
+static int block_seg(int64_t L, int64_t N) {
     const int64_t forced = env_int("BDSSM_SEG", 0);
     const int64_t s = forced > 0 ? forced : (N >= 32 ? 64 : 32);
     return (int)(L < s ? L : s);
@@ -60,7 +60,7 @@ void launch_block_bidir_k(dim3 g, int64_t L, const void *x, const void *dt, cons
 // over up to 8 waves (at 8 x 1536 channels: 35 / 50 / 89 us at L = 64 / 128 /
 // 256 against 65 / 165 / 469 us on block_bidir_kernel; at L = 32 the latter
 // is slightly faster).  BDSSM_SPLIT=0 keeps block_bidir_kernel (tests).
-bool use_split(int64_t L, int64_t N, int64_t T, int n_chunks, const float *bounds, const float *h0_blocks) {
+static bool use_split(int64_t L, int64_t N, int64_t T, int n_chunks, const float *bounds, const float *h0_blocks) {
     if (N > 16 || L <= 2 * kGroup || T != L || n_chunks != 1 || bounds != nullptr || h0_blocks != nullptr) return false;
     const char *v = getenv("BDSSM_SPLIT");
     return !(v != nullptr && v[0] == '0');
