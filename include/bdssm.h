@@ -163,6 +163,30 @@ int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const 
                   const bdssm_fusion *fusion, void *stream);
 
 /*
+ * bdssm_prefill for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, checks and results as bdssm_prefill, without ws / ws_bytes:
+ * the workspace comes from a scratch array that the library holds on each
+ * device it runs on, BDSSM_SCRATCH_BYTES long, for the life of the process.
+ * The call allocates nothing.
+ *   Limit: returns BDSSM_ERR_WORKSPACE, and enqueues nothing, when
+ *   bdssm_workspace_bytes(shape, t_ctx, BDSSM_OP_PREFILL) exceeds
+ *   BDSSM_SCRATCH_BYTES (every plan at d_state <= 16 fits, for any context
+ *   length; at d_state 32 only batch * t_ctx * d_inner up to about 4.6e6).
+ *   Concurrency: every call on one device shares that device's array; calls
+ *   that overlap in time on one device (several streams or threads) race and
+ *   must be serialised by the caller.  Nothing in the array needs to be
+ *   cleared between calls.
+ *   The first call on a device looks up the array's address there (no
+ *   allocation); a failure of that lookup returns BDSSM_ERR_HIP.
+ */
+#define BDSSM_SCRATCH_BYTES ((size_t)72 << 20)
+int bdssm_prefill_noalloc(const bdssm_shape *shape, int64_t t_ctx, const void *x, const void *dt,
+                          const void *B, const void *C, const float *A, const float *Dskip,
+                          const float *h_init, float *h_cache, void *y, const bdssm_fusion *fusion,
+                          void *stream);
+
+/*
  * One denoising step on the active block (exactly L tokens) [ABS], [DE-M]:
  * forward from the cache plus the reverse confined to the block.
  *   h_cache [batch,D,N] in, read only.

@@ -2,6 +2,7 @@
 
 Names and semantics follow include/bdssm.h:
   prefill(x, dt, B, C, A, Dskip, block_len, h_init=None, h_cache=None, y=None, want_y=False)
+  prefill_noalloc(x, dt, B, C, A, Dskip, block_len, h_init=None, h_cache=None, y=None, want_y=False)
   block_step(h_cache, x, dt, B, C, A, Dskip, y=None)
   commit(h_cache, x, dt, B, C, A, Dskip, want_y=False, y=None)
   train_scan(x, dt, B, C, A, Dskip, block_len, h_init=None, want_bounds=False, y=None, h_bounds=None)
@@ -29,7 +30,8 @@ F32 = 0
 BF16 = 1
 OP_PREFILL, OP_TRAIN, OP_FULL, OP_TRAIN_BWD, OP_BLOCKS_BWD = 0, 1, 2, 3, 4
 OP_TRAIN_BWD_REV, OP_BLOCKS_BWD_REV = 5, 6      # the backward with separate reverse operands
-EXPORTS = ("bdssm_prefill", "bdssm_block_step", "bdssm_commit", "bdssm_train_scan",
+SCRATCH_BYTES = 72 << 20    # BDSSM_SCRATCH_BYTES: the scratch array of bdssm_prefill_noalloc
+EXPORTS = ("bdssm_prefill", "bdssm_prefill_noalloc", "bdssm_block_step", "bdssm_commit", "bdssm_train_scan",
            "bdssm_train_scan_blocks", "bdssm_full_scan", "bdssm_train_scan_bwd",
            "bdssm_train_scan_blocks_bwd", "bdssm_workspace_bytes", "bdssm_status_str",
            "bdssm_version")
@@ -76,6 +78,7 @@ def load():
     Z = ctypes.c_size_t
     F = ctypes.POINTER(Fusion)
     lib.bdssm_prefill.argtypes = [S, I, P, P, P, P, P, P, P, P, P, P, Z, F, P]
+    lib.bdssm_prefill_noalloc.argtypes = [S, I, P, P, P, P, P, P, P, P, P, F, P]
     lib.bdssm_block_step.argtypes = [S, P, P, P, P, P, P, P, P, F, P]
     lib.bdssm_commit.argtypes = [S, P, P, P, P, P, P, P, P, F, P]
     lib.bdssm_train_scan.argtypes = [S, I, P, P, P, P, P, P, P, P, P, P, Z, F, P]
@@ -84,7 +87,7 @@ def load():
     G = ctypes.POINTER(FusionGrads)
     lib.bdssm_train_scan_bwd.argtypes = [S, I] + [P] * 17 + [Z, F, G, P]
     lib.bdssm_train_scan_blocks_bwd.argtypes = [S, I] + [P] * 16 + [Z, F, G, P]
-    for f in ("bdssm_prefill", "bdssm_block_step", "bdssm_commit", "bdssm_train_scan",
+    for f in ("bdssm_prefill", "bdssm_prefill_noalloc", "bdssm_block_step", "bdssm_commit", "bdssm_train_scan",
               "bdssm_train_scan_blocks", "bdssm_full_scan", "bdssm_train_scan_bwd",
               "bdssm_train_scan_blocks_bwd", "bdssm_version"):
         getattr(lib, f).restype = ctypes.c_int
@@ -221,6 +224,29 @@ def prefill(x, dt, B, C, A, Dskip, block_len, h_init=None, h_cache=None, y=None,
                               _p(h_init), _p(h_cache), _p(y), _p(ws),
                               0 if ws is None else ws.numel(), fz, _stream())
     _raise("bdssm_prefill", rc)
+    return h_cache, y
+
+
+def prefill_noalloc(x, dt, B, C, A, Dskip, block_len, h_init=None, h_cache=None, y=None,
+                    want_y=False, **fusion):
+    """prefill without a workspace argument: the library's own scratch array
+    serves as the workspace (calls on one device must not overlap in time).
+    Allocates nothing itself when h_cache (and y, if wanted) are passed in.
+    -> (h_cache, y or None)."""
+    batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip, need_c=want_y or y is not None)
+    want_y = want_y or y is not None
+    _check(h_init, "h_init", torch.float32, (batch, D, N))
+    if h_cache is None:
+        h_cache = torch.empty(batch, D, N, dtype=torch.float32, device=x.device)
+    _check(h_cache, "h_cache", torch.float32, (batch, D, N))
+    if want_y and y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", x.dtype, (batch, T, D))
+    s = _shape(batch, D, N, block_len, code)
+    fz = _fusion(x, D, **fusion)
+    rc = load().bdssm_prefill_noalloc(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A), _p(Dskip),
+                                      _p(h_init), _p(h_cache), _p(y), fz, _stream())
+    _raise("bdssm_prefill_noalloc", rc)
     return h_cache, y
 
 

@@ -21,7 +21,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <initializer_list>
+#include <mutex>
 #include <type_traits>
 
 #include "bdssm.h"
@@ -224,6 +226,112 @@ void run_full(const bdssm_shape *s, int64_t T, const void *x, const void *dt, co
     launch_sweep<Tin>(true, x, rdt, rB, rC, rA, Dskip, w.hr_in, w.yf, y, batch, T, D, N, p.fine_len, nf, st, fr);
 }
 
+// ---------------------------------------------------------------- prefill
+//
+// What bdssm_prefill and bdssm_prefill_noalloc share: the argument checks,
+// the plan with the workspace it needs, and the launches.  They differ only
+// in where the workspace comes from (the caller's buffer, or the library's
+// scratch array).
+
+struct PrefillPlan {
+    Fuse f;
+    Plan p{};
+    size_t ws_bytes = 0;   // workspace the plan needs (0: none)
+    bool empty = false;    // no rows: nothing to enqueue
+};
+
+// Argument checks in the order of the C ABI's contract (ws / ws_bytes: the
+// caller's workspace, or nullptr / 0), then the plan.
+int prefill_prepare(const bdssm_shape *shape, int64_t t_ctx, const void *x, const void *dt,
+                    const void *B, const void *C, const float *A, const float *Dskip,
+                    const float *h_init, float *h_cache, void *y, void *ws, size_t ws_bytes,
+                    const bdssm_fusion *fusion, PrefillPlan *out) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (t_ctx < 0 || t_ctx % shape->block_len != 0) return BDSSM_ERR_SHAPE;
+    const bool with_y = y != nullptr;
+    rc = check_streams(shape, t_ctx, x, dt, B, C, with_y, A, Dskip, with_y);
+    if (rc) return rc;
+    const int64_t batch = shape->batch, D = shape->d_inner, N = shape->d_state;
+    if (batch == 0 || D == 0) { out->empty = true; return BDSSM_OK; }
+    if (h_cache == nullptr) return BDSSM_ERR_NULL;
+    if (!aligned16(h_cache) || !aligned16(h_init) || !aligned16(y) || !aligned16(ws))
+        return BDSSM_ERR_ALIGN;
+    const size_t nstate = (size_t)batch * D * N * 4;
+    const size_t ny = (size_t)batch * t_ctx * D * esize(shape);
+    rc = check_alias(shape, t_ctx, x, dt, B, C, A, Dskip, nullptr,
+                     {Range{h_cache, nstate}, Range{y, ny}});
+    if (rc) return rc;
+    if (h_init && h_init != h_cache && overlaps({h_init, nstate}, {h_cache, nstate}))
+        return BDSSM_ERR_ALIAS;
+    if (h_init && overlaps({h_init, nstate}, {y, ny})) return BDSSM_ERR_ALIAS;
+    rc = check_fusion(fusion, shape, t_ctx, with_y, {Range{h_cache, nstate}, Range{y, ny}, Range{ws, ws_bytes}});
+    if (rc) return rc;
+    out->f = resolve_fusion(fusion, with_y);
+    if (t_ctx == 0) return BDSSM_OK;
+    if (!plan_for(batch, D, t_ctx, shape->block_len, N, &out->p)) return BDSSM_ERR_SHAPE;
+    out->ws_bytes = layout_ws(nullptr, batch, D, N, t_ctx, out->p, BDSSM_OP_PREFILL).bytes;
+    return BDSSM_OK;
+}
+
+int prefill_launch(const bdssm_shape *shape, int64_t t_ctx, const void *x, const void *dt, const void *B,
+                   const void *C, const float *A, const float *Dskip, const float *h_init, float *h_cache,
+                   void *y, void *ws, const PrefillPlan &pp, hipStream_t st) {
+    const int64_t batch = shape->batch, D = shape->d_inner, N = shape->d_state;
+    if (t_ctx == 0) return copy_or_zero(h_init, h_cache, batch * D * N, st);
+    const Workspace w = layout_ws(ws, batch, D, N, t_ctx, pp.p, BDSSM_OP_PREFILL);
+    const bool with_y = y != nullptr;
+    (void)hipGetLastError();
+    if (shape->dtype == BDSSM_BF16) {
+        if (with_y) run_bidirectional<uint16_t>(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, y, nullptr, h_cache, w, pp.p, st, pp.f);
+        else run_state_only<uint16_t>(shape, t_ctx, x, dt, B, A, h_init, h_cache, w, pp.p, st, pp.f);
+    } else {
+        if (with_y) run_bidirectional<float>(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, y, nullptr, h_cache, w, pp.p, st, pp.f);
+        else run_state_only<float>(shape, t_ctx, x, dt, B, A, h_init, h_cache, w, pp.p, st, pp.f);
+    }
+    return launch_status();
+}
+
+// ------------------------------------------------ the allocation-free scratch
+//
+// bdssm_prefill_noalloc takes its workspace from this array instead of a
+// caller's buffer.  Each device the library runs on holds its own copy for
+// the life of the process.  Its address is looked up once per device, with
+// that device current, on the first call there; host code uses only that
+// address (the array's name in host code is not a device address).  Every
+// call on one device shares the array: calls that overlap in time on one
+// device (different streams, or threads) race.  Nothing in it needs to start
+// at zero: every workspace array of the prefill is written before it is read.
+constexpr size_t kScratchBytes = BDSSM_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's scratch address (looked up on the first call there).
+int scratch_ptr(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return BDSSM_ERR_HIP;
+    }
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+                (void)hipGetLastError();
+                return BDSSM_ERR_HIP;
+            }
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return BDSSM_OK;
+}
+
 }  // namespace
 
 // ====================================================================== ABI
@@ -288,50 +396,38 @@ int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const 
                   const void *B, const void *C, const float *A, const float *Dskip,
                   const float *h_init, float *h_cache, void *y, void *ws, size_t ws_bytes,
                   const bdssm_fusion *fusion, void *stream) {
-    int rc = check_shape(shape);
-    if (rc) return rc;
-    if (t_ctx < 0 || t_ctx % shape->block_len != 0) return BDSSM_ERR_SHAPE;
-    const bool with_y = y != nullptr;
-    rc = check_streams(shape, t_ctx, x, dt, B, C, with_y, A, Dskip, with_y);
-    if (rc) return rc;
-    const int64_t batch = shape->batch, D = shape->d_inner, N = shape->d_state;
-    if (batch == 0 || D == 0) return BDSSM_OK;
-    if (h_cache == nullptr) return BDSSM_ERR_NULL;
-    if (!aligned16(h_cache) || !aligned16(h_init) || !aligned16(y) || !aligned16(ws))
-        return BDSSM_ERR_ALIGN;
-    const size_t nstate = (size_t)batch * D * N * 4;
-    const size_t ny = (size_t)batch * t_ctx * D * esize(shape);
-    rc = check_alias(shape, t_ctx, x, dt, B, C, A, Dskip, nullptr,
-                     {Range{h_cache, nstate}, Range{y, ny}});
-    if (rc) return rc;
-    if (h_init && h_init != h_cache && overlaps({h_init, nstate}, {h_cache, nstate}))
-        return BDSSM_ERR_ALIAS;
-    if (h_init && overlaps({h_init, nstate}, {y, ny})) return BDSSM_ERR_ALIAS;
-    rc = check_fusion(fusion, shape, t_ctx, with_y, {Range{h_cache, nstate}, Range{y, ny}, Range{ws, ws_bytes}});
-    if (rc) return rc;
-    const Fuse f = resolve_fusion(fusion, with_y);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (t_ctx == 0) return copy_or_zero(h_init, h_cache, batch * D * N, st);
-    Plan p;
-    if (!plan_for(batch, D, t_ctx, shape->block_len, N, &p)) return BDSSM_ERR_SHAPE;
-    const Workspace probe = layout_ws(nullptr, batch, D, N, t_ctx, p, BDSSM_OP_PREFILL);
-    if (probe.bytes > 0 && (ws == nullptr || ws_bytes < probe.bytes)) return BDSSM_ERR_WORKSPACE;
-    if (probe.bytes > 0) {
-        rc = check_alias(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, {Range{ws, probe.bytes}});
+    PrefillPlan pp;
+    int rc = prefill_prepare(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, h_cache, y, ws, ws_bytes, fusion,
+                             &pp);
+    if (rc || pp.empty) return rc;
+    if (pp.ws_bytes > 0) {
+        if (ws == nullptr || ws_bytes < pp.ws_bytes) return BDSSM_ERR_WORKSPACE;
+        rc = check_alias(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, {Range{ws, pp.ws_bytes}});
         if (rc) return rc;
-        if (overlaps({ws, probe.bytes}, {y, ny}) || overlaps({ws, probe.bytes}, {h_cache, nstate}))
+        const size_t nstate = (size_t)shape->batch * shape->d_inner * shape->d_state * 4;
+        const size_t ny = (size_t)shape->batch * t_ctx * shape->d_inner * esize(shape);
+        if (overlaps({ws, pp.ws_bytes}, {y, ny}) || overlaps({ws, pp.ws_bytes}, {h_cache, nstate}))
             return BDSSM_ERR_ALIAS;
     }
-    const Workspace w = layout_ws(ws, batch, D, N, t_ctx, p, BDSSM_OP_PREFILL);
-    (void)hipGetLastError();
-    if (shape->dtype == BDSSM_BF16) {
-        if (with_y) run_bidirectional<uint16_t>(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, y, nullptr, h_cache, w, p, st, f);
-        else run_state_only<uint16_t>(shape, t_ctx, x, dt, B, A, h_init, h_cache, w, p, st, f);
-    } else {
-        if (with_y) run_bidirectional<float>(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, y, nullptr, h_cache, w, p, st, f);
-        else run_state_only<float>(shape, t_ctx, x, dt, B, A, h_init, h_cache, w, p, st, f);
+    return prefill_launch(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, h_cache, y, ws, pp,
+                          static_cast<hipStream_t>(stream));
+}
+
+int bdssm_prefill_noalloc(const bdssm_shape *shape, int64_t t_ctx, const void *x, const void *dt,
+                          const void *B, const void *C, const float *A, const float *Dskip,
+                          const float *h_init, float *h_cache, void *y, const bdssm_fusion *fusion,
+                          void *stream) {
+    PrefillPlan pp;
+    int rc = prefill_prepare(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, h_cache, y, nullptr, 0, fusion, &pp);
+    if (rc || pp.empty) return rc;
+    if (pp.ws_bytes > kScratchBytes) return BDSSM_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (pp.ws_bytes > 0) {
+        rc = scratch_ptr(&ws);
+        if (rc) return rc;
     }
-    return launch_status();
+    return prefill_launch(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, h_cache, y, ws, pp,
+                          static_cast<hipStream_t>(stream));
 }
 
 int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void *x,
