@@ -10,6 +10,8 @@ Names and semantics follow include/bdssm.h:
   full_scan(x, dt, B, C, A, Dskip, y=None)
   train_scan_bwd(x, dt, B, C, A, Dskip, block_len, h_bounds, dy, d_bounds=None, want_dh_init=False)
   train_scan_blocks_bwd(x, dt, B, C, A, Dskip, block_len, h0_blocks, dy, want_dh0_blocks=False)
+  bind_block_step(...), bind_commit(...): the call checked and marshalled once, for
+      repeated eager launches (BoundCall)
 The six forward functions also take the optional layer features as keyword
 arguments: dt_bias ([D] fp32), dt_softplus (bool), z (gate, like y), and rev
 (separate reverse-direction operands: dict with dt, B, C, A, optional dt_bias).
@@ -120,17 +122,18 @@ def _p(t):
 
 
 def _check(t, name, dtype=None, shape=None):
+    # the cheapest torch accessors: this runs for every tensor of every call
     if t is None:
         return
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError("%s must be on the GPU (got %s)" % (name, t.device))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
-    if dtype is not None and t.dtype != dtype:
+    if dtype is not None and t.dtype is not dtype:
         raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != shape:
         raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
 
 
@@ -334,6 +337,49 @@ def full_scan(x, dt, B, C, A, Dskip, y=None, ws=None, **fusion):
                                 _p(y), _p(ws), 0 if ws is None else ws.numel(), fz, _stream())
     _raise("bdssm_full_scan", rc)
     return y
+
+
+class BoundCall:
+    """One library call with its arguments checked and marshalled once.
+    Calling the object enqueues the same call again, on the stream that was
+    current when it was bound, with the same tensors (which it keeps alive):
+    the per-call host cost is the ctypes call and the launch alone.  The
+    tensors' contents may change between calls; their storage must not."""
+    __slots__ = ("_fn", "_args", "_name", "_keep")
+
+    def __init__(self, fn, name, args, keep):
+        self._fn, self._name, self._args, self._keep = fn, name, tuple(args), keep
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _raise(self._name, rc)
+
+
+def bind_block_step(h_cache, x, dt, B, C, A, Dskip, y, **fusion):
+    """block_step(h_cache, x, dt, B, C, A, Dskip, y=y, **fusion) as a BoundCall."""
+    batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip)
+    _check(h_cache, "h_cache", torch.float32, (batch, D, N))
+    _check(y, "y", x.dtype, (batch, T, D))
+    s = _shape(batch, D, N, T, code)
+    fz = _fusion(x, D, **fusion)
+    args = (ctypes.byref(s), _p(h_cache), _p(x), _p(dt), _p(B), _p(C), _p(A), _p(Dskip), _p(y), fz,
+            _stream())
+    return BoundCall(load().bdssm_block_step, "bdssm_block_step", args,
+                     (s, fz, h_cache, x, dt, B, C, A, Dskip, y, fusion))
+
+
+def bind_commit(h_cache, x, dt, B, C, A, Dskip, y=None, **fusion):
+    """commit(h_cache, x, dt, B, C, A, Dskip, y=y, **fusion) as a BoundCall."""
+    batch, T, D, N, code = _streams(x, dt, B, C, A, Dskip, need_c=y is not None)
+    _check(h_cache, "h_cache", torch.float32, (batch, D, N))
+    _check(y, "y", x.dtype, (batch, T, D))
+    s = _shape(batch, D, N, T, code)
+    fz = _fusion(x, D, **fusion)
+    args = (ctypes.byref(s), _p(h_cache), _p(x), _p(dt), _p(B), _p(C), _p(A), _p(Dskip), _p(y), fz,
+            _stream())
+    return BoundCall(load().bdssm_commit, "bdssm_commit", args,
+                     (s, fz, h_cache, x, dt, B, C, A, Dskip, y, fusion))
 
 
 def _grad_outputs(x, D, N):

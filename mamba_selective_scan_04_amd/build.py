@@ -9,6 +9,8 @@ The kernel launchers live in launch_*.hip; each is compiled twice, once per
 stream type (-DBDSSM_TIN=float and -DBDSSM_TIN=uint16_t, the bf16 bits), so
 that the template instantiations spread over parallel compiler processes.
 bdssm.hip holds the C ABI and the launch plans.  Objects go to _build/.
+libbdssm_probe.so (csrc/roof_probe.hip) holds the benchmark's
+microbenchmarks; it is not part of the scan library.
 """
 import concurrent.futures
 import os
@@ -24,6 +26,9 @@ HEADERS = [os.path.join(CSRC, h) for h in ("bdssm_kernels.hpp", "bdssm_bwd_kerne
 LAUNCH_UNITS = ("launch_chunk", "launch_bidir", "launch_block", "launch_bwd", "launch_bwd_general")
 STREAM_TYPES = (("f32", "float"), ("bf16", "uint16_t"))
 LIB = os.path.join(HERE, "libbdssm.so")
+PROBE_LIB = os.path.join(HERE, "libbdssm_probe.so")
+PROBE_SRC = os.path.join(CSRC, "roof_probe.hip")
+PROBE_OBJ = os.path.join(BUILD_DIR, "roof_probe.o")
 ARCH = os.environ.get("BDSSM_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -51,7 +56,7 @@ def units():
 
 
 def sources():
-    return sorted({s for s, _, _ in units()}) + HEADERS
+    return sorted({s for s, _, _ in units()}) + HEADERS + [PROBE_SRC]
 
 
 def up_to_date():
@@ -82,7 +87,7 @@ def build(verbose=False, changed_only=False, jobs=None):
     library."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     todo = []
-    for src, obj, extra in units():
+    for src, obj, extra in units() + [(PROBE_SRC, PROBE_OBJ, [])]:
         if changed_only and os.path.exists(obj):
             t = os.path.getmtime(obj)
             if all(os.path.getmtime(d) <= t for d in [src] + HEADERS):
@@ -90,7 +95,8 @@ def build(verbose=False, changed_only=False, jobs=None):
         todo.append((src, obj, extra))
     jobs = jobs or min(len(todo) or 1, os.cpu_count() or 4, 12)
     if verbose:
-        print("compiling %d of %d translation units with %d jobs" % (len(todo), len(units()), jobs), flush=True)
+        print("compiling %d of %d translation units with %d jobs" % (len(todo), len(units()) + 1, jobs),
+              flush=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         futs = {ex.submit(_compile, *t): t for t in todo}
         for fu in concurrent.futures.as_completed(futs):
@@ -99,15 +105,20 @@ def build(verbose=False, changed_only=False, jobs=None):
                 print("  built", os.path.basename(futs[fu][1]), flush=True)
                 if out.strip():
                     print(out)
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + [o for _, o, _ in units()]
+    _link(LIB, [o for _, o, _ in units()])
+    _link(PROBE_LIB, [PROBE_OBJ])
+    return LIB
+
+
+def _link(lib, objs):
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         if os.path.exists(tmp):
             os.remove(tmp)
-        raise RuntimeError("link failed (%d):\n%s" % (r.returncode, _clean(r.stdout)))
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError("link of %s failed (%d):\n%s" % (os.path.basename(lib), r.returncode, _clean(r.stdout)))
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

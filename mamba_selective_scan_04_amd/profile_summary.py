@@ -12,29 +12,88 @@ profiles/.
       scaled to bytes by what the same counter reads for a plain device copy of
       known size (the 1 GiB copyBuffer launches of bench.py --copy-calibration)
 
+  python -m mamba_selective_scan_04_amd.profile_summary hash [family]
+      the source hash of a kernel family (prefill, bidir, backward) or of
+      every source
+
 Only this library's kernels (bdssm_dev::) and the calibration copy are listed.
-The summary starts with the source hash of the kernels so a stale profile can
-be recognised.
+A summary starts with the source hash of the kernel family it measures, so
+that a stale profile can be recognised: the hash covers the shared device
+helpers, the family's kernels and their launch and plan code, and nothing
+else, so that work on one family leaves the others' profiles valid.
 """
 import collections
 import csv
 import hashlib
 import os
+import re
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# every kernel and launch source: a change to any of them marks a summary stale
-KERNEL_SOURCES = sorted(os.path.join(HERE, "csrc", f) for f in os.listdir(os.path.join(HERE, "csrc"))
-                        if f.endswith((".hip", ".hpp")))
+CSRC = os.path.join(HERE, "csrc")
+KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                        if f.endswith((".hip", ".hpp")) and not f.startswith("roof_probe"))
 COPY_BYTES = 1 << 30
+# the definitions each profiled family depends on (kernels, launchers, plans)
+FAMILIES = {
+    "prefill": ("chunk_state_kernel", "carry_kernel", "make_plan", "plan_for", "launch_chunk_state_k",
+                "launch_chunk_state", "launch_carry", "run_state_only", "layout_ws"),
+    "bidir": ("chunk_state_kernel", "carry_kernel", "bidir_wave_kernel", "block_lane_kernel", "make_plan",
+              "blocks_plan", "plan_for", "launch_chunk_state_k", "launch_chunk_state", "launch_carry",
+              "launch_bidir_k", "launch_bidir_L", "launch_bidir", "launch_block_lane", "block_lane_path",
+              "run_bidirectional", "layout_ws"),
+}
 
 
-def source_hash():
+def _definitions(text, name):
+    """The text of every definition of `name` in a source: from its template
+    line (if any) to the first closing brace in column 0."""
+    lines = text.split("\n")
+    out = []
+    i = 0
+    while i < len(lines):
+        l = lines[i]
+        if l[:1] not in ("", " ", "/", "#", "}") and re.search(r"\b%s\(" % re.escape(name), l):
+            j = i
+            while j < len(lines) and not lines[j].rstrip().endswith(("{", ";")):
+                j += 1
+            if j < len(lines) and lines[j].rstrip().endswith("{"):
+                k0 = i - 1 if i > 0 and lines[i - 1].startswith("template") else i
+                k = j
+                while k < len(lines) and lines[k] != "}":
+                    k += 1
+                out.append("\n".join(lines[k0:k + 1]))
+                i = k
+        i += 1
+    return out
+
+
+def source_hash(family=None):
+    """Hash of every kernel and launch source (family None), or of one
+    family's definitions plus the shared device helpers (the kernel header up
+    to its first kernel)."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+    if family is None:
+        for p in KERNEL_SOURCES:
+            with open(p, "rb") as f:
+                h.update(f.read())
+        return h.hexdigest()[:16]
+    texts = [open(p).read() for p in KERNEL_SOURCES]
+    kern = open(os.path.join(CSRC, "bdssm_kernels.hpp")).read()
+    h.update(kern[:kern.index("__global__")].encode())
+    for name in FAMILIES[family]:
+        found = [d for t in texts for d in _definitions(t, name)]
+        if not found:
+            raise KeyError("no definition of %s in the sources" % name)
+        for d in found:
+            h.update(d.encode())
     return h.hexdigest()[:16]
+
+
+def hash_line(family):
+    if family is None:
+        return "kernel source hash: %s" % source_hash()
+    return "kernel source hash (%s): %s" % (family, source_hash(family))
 
 
 def short(name):
@@ -46,7 +105,7 @@ def keep(name):
     return "bdssm_dev::" in name or "copyBuffer" in name
 
 
-def trace(path):
+def trace(path, family=None):
     groups = collections.defaultdict(list)
     for r in csv.DictReader(open(path)):
         if not keep(r["Kernel_Name"]):
@@ -54,7 +113,7 @@ def trace(path):
         grid = (int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]))
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         groups[(short(r["Kernel_Name"]), grid)].append(dur)
-    out = ["kernel source hash: %s" % source_hash(), "",
+    out = [hash_line(family), "",
            "| kernel | grid (threads x,y,z) | calls | avg us | min us | max us |",
            "|---|---|---:|---:|---:|---:|"]
     for (k, g), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
@@ -72,7 +131,7 @@ def _counters(path):
     return groups
 
 
-def pmc(fetch_path, write_path):
+def pmc(fetch_path, write_path, family=None):
     f = _counters(fetch_path)
     w = _counters(write_path)
     # the calibration copies are the copyBuffer launch group that writes the most
@@ -85,7 +144,7 @@ def pmc(fetch_path, write_path):
         raise SystemExit("no calibration copy in the counter files (run bench.py --copy-calibration)")
     sf = COPY_BYTES / (sum(cf) / len(cf) * 1024)
     sw = COPY_BYTES / (sum(cw) / len(cw) * 1024)
-    out = ["kernel source hash: %s" % source_hash(), "",
+    out = [hash_line(family), "",
            "calibration: a 1 GiB device copy reads FETCH_SIZE %.0f KiB and WRITE_SIZE %.0f KiB per "
            "dispatch, so bytes = FETCH_SIZE x 1024 x %.4f and WRITE_SIZE x 1024 x %.4f"
            % (sum(cf) / len(cf), sum(cw) / len(cw), sf, sw), "",
@@ -108,7 +167,7 @@ VALU_LANES = 1024 * 16   # 256 CUs x 4 SIMDs x 16 lanes: lane issue slots per cl
 NOMINAL_GHZ = 2.4
 
 
-def valu(path):
+def valu(path, family=None):
     """Per kernel launch group: duration, the clock the dies ran at
     (GRBM_GUI_ACTIVE / N_XCC / duration), VALU instructions issued (a v_exp
     counts twice, as it occupies the SIMD for twice the cycles), the lane issue
@@ -124,7 +183,7 @@ def valu(path):
     groups = collections.defaultdict(list)
     for (disp, name, grid, us), c in rows.items():
         groups[(name, grid)].append((us, c))
-    out = ["kernel source hash: %s" % source_hash(), "",
+    out = [hash_line(family), "",
            "| kernel | grid (threads) | dispatches | avg us | clock GHz | VALU instr (v_exp x2) | "
            "lane slots / s | of 2.4 GHz peak | of peak at measured clock | VALUBusy % |",
            "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
@@ -146,14 +205,19 @@ def valu(path):
 
 
 def main(argv):
+    fam = None
+    if "--family" in argv:
+        i = argv.index("--family")
+        fam = argv[i + 1]
+        argv = argv[:i] + argv[i + 2:]
     if len(argv) >= 2 and argv[0] == "trace":
-        print(trace(argv[1]))
+        print(trace(argv[1], fam))
     elif len(argv) >= 3 and argv[0] == "pmc":
-        print(pmc(argv[1], argv[2]))
+        print(pmc(argv[1], argv[2], fam))
     elif len(argv) >= 2 and argv[0] == "valu":
-        print(valu(argv[1]))
+        print(valu(argv[1], fam))
     elif len(argv) >= 1 and argv[0] == "hash":
-        print(source_hash())
+        print(source_hash(argv[1] if len(argv) > 1 else None))
     else:
         print(__doc__)
         return 2

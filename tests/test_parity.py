@@ -343,3 +343,35 @@ def test_single_block_kernels(dev, kernel, n, L, D, dtype, monkeypatch):
         ok2 = {k: v for k, v in ok.items() if k != "z"}
         hco2, _ = oracle.commit(ho, *ob, **ok2)
         assert rel_err(to_np(hc2), hco2) < STATE_TOL, (fused, "commit state, no y")
+
+
+def test_bound_calls_match_plain_calls(dev):
+    """BoundCall (checked and marshalled once, launched many times) enqueues
+    the same work as the plain binding call: block_step and commit, plain and
+    fused, bit for bit, also after the inputs' contents change."""
+    from mamba_selective_scan_04_amd import synth
+    batch, L, D, P = 4, 16, 200, 64
+    c = Case(batch, P + L, D, torch.bfloat16, sid=24, a_kind="random")
+    h, _ = m.prefill(*c.segment(0, P), L)
+    blk = c.segment(P, P + L)
+    bias = synth.normal((D,), 2401, "cuda", torch.float32, std=0.3)
+    z = synth.normal((batch, L, D), 2402, "cuda", torch.bfloat16)
+    for kw in ({}, dict(dt_bias=bias, dt_softplus=True, z=z)):
+        y_ref = m.block_step(h, *blk, **kw)
+        y = torch.empty_like(y_ref)
+        call = m.bind_block_step(h, *blk, y, **kw)
+        call()
+        _sync()
+        assert torch.equal(y, y_ref)
+        blk[0].mul_(-0.5)                       # new contents, same storage
+        y_ref = m.block_step(h, *blk, **kw)
+        call()
+        _sync()
+        assert torch.equal(y, y_ref)
+        ckw = {k: v for k, v in kw.items() if k != "z"}
+        h_ref = h.clone()
+        m.commit(h_ref, *blk, **ckw)
+        hb = h.clone()
+        m.bind_commit(hb, *blk, **ckw)()
+        _sync()
+        assert torch.equal(hb, h_ref)
