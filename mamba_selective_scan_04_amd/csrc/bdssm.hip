@@ -61,6 +61,13 @@ int check_shape(const bdssm_shape *s) {
 
 size_t esize(const bdssm_shape *s) { return s->dtype == BDSSM_BF16 ? 2 : 4; }
 
+// The single-block kernels address one block's rows of a stream with 32-bit
+// buffer offsets (L rows of D elements); 4 bytes per element covers both
+// dtypes, as in the chunk plans.
+bool block_rows_fit(const bdssm_shape *s) {
+    return s->block_len * s->d_inner * 4 < ((int64_t)1 << 31);
+}
+
 // Shared checks of the per-token streams of one call covering T tokens.
 int check_streams(const bdssm_shape *s, int64_t T, const void *x, const void *dt, const void *B,
                   const void *C, bool need_c, const float *A, const float *Dskip, bool need_dskip) {
@@ -438,6 +445,7 @@ int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void 
     const int64_t L = shape->block_len;
     rc = check_streams(shape, L, x, dt, B, C, true, A, Dskip, true);
     if (rc) return rc;
+    if (!block_rows_fit(shape)) return BDSSM_ERR_SHAPE;
     const int64_t batch = shape->batch, D = shape->d_inner, N = shape->d_state;
     if (batch == 0 || D == 0) return BDSSM_OK;
     if (h_cache == nullptr || y == nullptr) return BDSSM_ERR_NULL;
@@ -472,6 +480,7 @@ int bdssm_commit(const bdssm_shape *shape, float *h_cache, const void *x, const 
     const bool with_y = y != nullptr;
     rc = check_streams(shape, L, x, dt, B, C, with_y, A, Dskip, with_y);
     if (rc) return rc;
+    if (!block_rows_fit(shape)) return BDSSM_ERR_SHAPE;
     const int64_t batch = shape->batch, D = shape->d_inner, N = shape->d_state;
     if (batch == 0 || D == 0) return BDSSM_OK;
     if (h_cache == nullptr) return BDSSM_ERR_NULL;

@@ -22,16 +22,25 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
-def build(force=True):
-    """Compile the C oracle into oracle/liboracle.so with gcc + OpenMP."""
-    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
-        return _LIB
-    tmp = _LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-o", tmp, _SRC, "-lm"]
+# the sanitizer build (address + undefined behaviour, host code only): a
+# process that loads it needs the ASan runtime preloaded (LD_PRELOAD)
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=all"]
+
+
+def build(force=True, sanitize=False, out=None):
+    """Compile the C oracle into oracle/liboracle.so (or `out`) with gcc +
+    OpenMP; sanitize=True builds with AddressSanitizer and UBSan."""
+    lib = out or _LIB
+    if not force and os.path.exists(lib) and os.path.getmtime(lib) >= os.path.getmtime(_SRC):
+        return lib
+    tmp = lib + ".tmp%d" % os.getpid()
+    opt = SANITIZE_FLAGS if sanitize else ["-O2"]
+    cmd = ["gcc"] + opt + ["-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+                           "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def bind(lib):
@@ -63,11 +72,16 @@ def bind(lib):
 
 
 def load():
+    """The oracle library: oracle/liboracle.so (built if missing or stale), or
+    the build named by BDSSM_ORACLE_LIB (e.g. the sanitizer build)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        _lib = bind(ctypes.CDLL(_LIB))
+        path = os.environ.get("BDSSM_ORACLE_LIB")
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+        _lib = bind(ctypes.CDLL(path))
     return _lib
 
 

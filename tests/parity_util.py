@@ -84,4 +84,28 @@ def worst(got, ref):
     e = np.abs(g - r) / den
     i = np.unravel_index(int(np.argmax(e)), e.shape)
     return dict(index=tuple(int(v) for v in i), got=float(g[i]), ref=float(r[i]),
-                floor=float(rms), err=float(e[i]), normwise=float(np.max(np.abs(g - r)) / np.max(np.abs(r))))
+                floor=float(rms), err=float(e[i]), normwise=float(np.max(np.abs(g - r)) / np.max(np.abs(r))),
+                q13=rel_err_q13(g, r))
+
+
+def rel_err_q13(got, ref):
+    """The same metric with the floor at 0.01 rms(r) (reported beside the
+    bars in failure messages; the bars apply to rel_err)."""
+    g = np.asarray(got, np.float64)
+    r = np.asarray(ref, np.float64)
+    if r.size == 0:
+        return 0.0
+    rms = np.sqrt(np.mean(r * r))
+    return float(np.max(np.abs(g - r) / np.maximum(np.abs(r), 0.01 * rms + 1e-300)))
+
+
+def bf16_within_ulp(got, ref):
+    """Fraction of bf16 outputs within one bf16 rounding of the oracle's value:
+    |g - bf16(r)| <= |bf16(r)| 2^-7 (bf16(r): the fp64 value rounded to fp32,
+    then to bf16 by torch's round-to-nearest-even)."""
+    r = torch.from_numpy(np.ascontiguousarray(np.asarray(ref, np.float64))).float().to(torch.bfloat16).float()
+    r = r.numpy().astype(np.float64)
+    g = np.asarray(got, np.float64)
+    if r.size == 0:
+        return 1.0
+    return float(np.mean(np.abs(g - r) <= np.abs(r) * 2.0 ** -7 + 1e-30))

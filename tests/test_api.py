@@ -280,3 +280,20 @@ def test_fusion_argument_errors():
                                 P(FAKE + 0x3000), P(FAKE + 0x4000), P(FAKE + 0x5000),
                                 P(FAKE + 0x6000), P(FAKE + 0x7000), ctypes.byref(f), None)
     assert rc == -7
+
+
+def test_single_block_rows_beyond_32bit_offsets():
+    """block_step and commit address one block's rows with 32-bit buffer
+    offsets: L x d_inner x 4 bytes at or above 2^31 is rejected (here 256 x
+    2^21 x 4 = 2^31) before any HIP call.  With one channel fewer the call
+    passes that check and stops at the next host check (a NULL cache or
+    output), so nothing is ever launched."""
+    far = [(k + 1) << 33 for k in range(8)]
+    for D, want in ((1 << 21, -2), ((1 << 21) - 1, -1)):
+        s = shape(batch=1, D=D, L=256, dtype=B.F32)
+        rc = lib().bdssm_block_step(ctypes.byref(s), None, P(far[1]), P(far[2]), P(far[3]), P(far[4]),
+                                    P(far[5]), P(far[6]), None, None, None)
+        assert rc == want, (D, rc)
+        rc = lib().bdssm_commit(ctypes.byref(s), None, P(far[1]), P(far[2]), P(far[3]), P(far[4]),
+                                P(far[5]), P(far[6]), None, None, None)
+        assert rc == want, (D, rc)

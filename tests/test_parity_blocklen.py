@@ -264,6 +264,9 @@ SPLIT = [  # (L, N, dtype, variant)
     (256, 16, torch.bfloat16, "rev"),
     (48, 4, torch.float32, "plain"),
     (17, 16, torch.float32, "fused"),
+    (64, 16, torch.bfloat16, "bias"),      # dt + bias without softplus
+    (200, 16, torch.float32, "revbias"),   # reverse operands with their own bias, no forward bias
+    (64, 8, torch.bfloat16, "revbias"),
 ]
 
 
@@ -288,8 +291,14 @@ def test_single_block_long(dev, split, L, N_, dtype, variant, monkeypatch):
         z = synth.normal((batch, L, D), 1000 * sid + 3, "cuda", dtype, std=2.0)
         kw = dict(dt_bias=bias, dt_softplus=True, z=z)
         ok = dict(dt_bias=to_np(bias), dt_softplus=True, z=synth.to_oracle(z))
-    elif variant == "rev":
-        rev = _rev_operands(batch, L, D, dtype, sid, with_bias=False)
+    elif variant == "bias":
+        bias = synth.normal((D,), 1000 * sid + 2, "cuda", torch.float32, std=0.05)
+        kw, ok = dict(dt_bias=bias), dict(dt_bias=to_np(bias))
+    elif variant in ("rev", "revbias"):
+        rev = _rev_operands(batch, L, D, dtype, sid, with_bias=variant == "revbias")
+        if N_ != N:
+            rev["B"], rev["C"] = rev["B"][..., :N_].contiguous(), rev["C"][..., :N_].contiguous()
+            rev["A"] = rev["A"][:, :N_].contiguous()
         kw, ok = dict(rev=rev), dict(rev=_rev_oracle(rev))
     h = synth.normal((batch, D, N_), 1000 * sid + 5, "cuda", std=0.5)
     ys = m.block_step(h, *c.args()[:6], **kw)

@@ -12,11 +12,19 @@ import torch
 import mamba_selective_scan_04_amd as m
 import oracle
 from mamba_selective_scan_04_amd import synth
-from parity_util import N, STATE_TOL, TOL, rel_err, to_np, worst
+from parity_util import N, STATE_TOL, TOL, bf16_within_ulp, rel_err, to_np, worst
 
 pytestmark = pytest.mark.gpu
 
 TOL_BF16 = TOL[torch.bfloat16]
+ULP_FRAC = 0.999          # bf16 outputs within one bf16 rounding of the oracle's value
+
+
+def check_y(got, ref, what=""):
+    """A bf16 output against the oracle: the 2e-2 bar and the one-ulp share."""
+    assert rel_err(got, ref) < TOL_BF16, (what, worst(got, ref))
+    frac = bf16_within_ulp(got, ref)
+    assert frac >= ULP_FRAC, (what, frac, worst(got, ref))
 
 
 def sample_channels(D, k, seed):
@@ -36,7 +44,7 @@ def ora(t):
 
 
 @pytest.mark.parametrize("name", ["infer_8k_b8", "infer_65k_b1", "infer_65k_b8", "infer_262k_b1",
-                                  "infer_262k_b16"])
+                                  "infer_262k_b4", "infer_262k_b16"])
 def test_inference_workload_sampled(dev, name):
     wl = synth.WORKLOADS[name]
     batch, D, ctx, L, sid = wl["batch"], wl["d_inner"], wl["ctx"], wl["block"], wl["sid"]
@@ -63,7 +71,7 @@ def test_inference_workload_sampled(dev, name):
     for s, yg in ((s0, y0), (s15, y15)):
         yo = oracle.block_step(ho, ora(gather(s[0], ch)), ora(gather(s[1], ch)), ora(s[2]), ora(s[3]), Ah, Dh)
         got = to_np(gather(yg, ch))
-        assert rel_err(got, yo) < TOL_BF16, worst(got, yo)
+        check_y(got, yo, "block_step y")
     ho2, _ = oracle.commit(ho, ora(gather(c0[0], ch)), ora(gather(c0[1], ch)), ora(c0[2]), ora(c0[3]), Ah, Dh)
     got_h2 = to_np(h[:, torch.as_tensor(ch, device=dev)])
     assert rel_err(got_h2, ho2) < STATE_TOL, worst(got_h2, ho2)
@@ -85,12 +93,12 @@ def test_training_workload_sampled(dev, name):
     args = (ora(gather(x, ch)), ora(gather(dt, ch)), ora(Bm), ora(Cm), ora(A[idx]), ora(Dskip[idx]))
     r = oracle.scan(*args, L, want_y=True, want_bounds=True)
     got = to_np(gather(y, ch))
-    assert rel_err(got, r["y"]) < TOL_BF16, worst(got, r["y"])
+    check_y(got, r["y"], "train_scan y")
     gb = to_np(bnd[:, :, idx])
     assert rel_err(gb, r["bounds"]) < STATE_TOL, worst(gb, r["bounds"])
     yfo = oracle.full_scan(*args)
     gf = to_np(gather(yfull, ch))
-    assert rel_err(gf, yfo) < TOL_BF16, worst(gf, yfo)
+    check_y(gf, yfo, "full_scan y")
 
 
 def test_baseline_full_scan_65k_sampled(dev):
@@ -107,7 +115,7 @@ def test_baseline_full_scan_65k_sampled(dev):
     yo = oracle.full_scan(ora(gather(x, ch)), ora(gather(dt, ch)), ora(Bm), ora(Cm),
                           ora(A[idx]), ora(Dskip[idx]))
     got = to_np(gather(y, ch))
-    assert rel_err(got, yo) < TOL_BF16, worst(got, yo)
+    check_y(got, yo, "full_scan y")
 
 
 def test_train_blocks_87m_sampled(dev):
@@ -124,7 +132,7 @@ def test_train_blocks_87m_sampled(dev):
     yo = oracle.train_blocks(ora(gather(x, ch)), ora(gather(dt, ch)), ora(Bm), ora(Cm), ora(A[idx]),
                              ora(Dskip[idx]), L, to_np(h0b[:, :, idx]))
     got = to_np(gather(y, ch))
-    assert rel_err(got, yo) < TOL_BF16, worst(got, yo)
+    check_y(got, yo, "train_scan_blocks y")
 
 
 @pytest.mark.parametrize("name", ["train_87m", "train_350m"])
