@@ -26,7 +26,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libbdssm.so")
+# BDSSM_LIBRARY: load another build of the library (comparisons of builds)
+LIB_PATH = os.environ.get("BDSSM_LIBRARY") or os.path.join(HERE, "libbdssm.so")
 
 F32 = 0
 BF16 = 1

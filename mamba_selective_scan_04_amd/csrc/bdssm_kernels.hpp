@@ -52,6 +52,15 @@ __device__ __forceinline__ float widen(uint16_t v) {
     return __uint_as_float(static_cast<uint32_t>(v) << 16);   // bf16 -> fp32 is exact
 }
 
+// A stream element held across loop iterations: bf16 bits zero-extended to 32
+// bits.  Carried as 16-bit values, pairs of them get packed into one register
+// (v_perm), and the pack waits for both loads as soon as they are issued,
+// which undoes a software prefetch.
+template <typename Tin> struct Staged { using type = Tin; };
+template <> struct Staged<uint16_t> { using type = uint32_t; };
+__device__ __forceinline__ float widen_staged(float v) { return v; }
+__device__ __forceinline__ float widen_staged(uint32_t v) { return __uint_as_float(v << 16); }
+
 template <typename Tin> __device__ __forceinline__ Tin narrow(float v);
 template <> __device__ __forceinline__ float narrow<float>(float v) { return v; }
 template <> __device__ __forceinline__ uint16_t narrow<uint16_t>(float v) {
@@ -232,20 +241,23 @@ template <> __device__ __forceinline__ void Rows<float>::store_at(int32_t off, f
 //     instantiation so profiles tell the two uses apart).
 // kRev scans the chunk from its last token to its first (the reverse
 // direction of the full-sequence baseline).
-// Tokens stream through a 6-deep register pipeline: the loads of the next 6
-// tokens are issued before the arithmetic of the current 6 (6 keeps the bf16
-// kernel within 64 VGPRs, i.e. 8 waves per SIMD).
+// Tokens stream through a register pipeline of 5-token stages: the loads of
+// the next stage are issued before the arithmetic of the current one.
 // grid = (ceil(D/64), chunks launched, batch), block = 64.
 // hout / sout are indexed by chunk id c = c_first + blockIdx.y over n_chunks.
 // kDt: how dt is formed from the dt stream (kDtPlain / kDtBias / kDtSoftplus,
 // with the per-channel dt_bias, which may be null).
+// Resident waves per SIMD the chunk scan is built for (the launch plans size
+// their fine chunks to exactly one round of them): 7 leaves 72 VGPRs, room for
+// two stages of 5 tokens without spills.
+constexpr int kChunkWaves = 7;
 template <typename Tin, bool kRev, bool kDirect, int kDt = kDtPlain, int kN = kStates>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kN > 16 ? 4 : 8))) void chunk_state_kernel(
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kN > 16 ? 4 : kChunkWaves))) void chunk_state_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const float *__restrict__ A, const float *h0, float *hout, float *__restrict__ sout,
     int64_t T, int D, int64_t Tc, int n_chunks, int c_first, const float *__restrict__ dt_bias)
 {
-    constexpr int U = 6;                      // tokens per pipeline stage
+    constexpr int U = 5;                      // tokens per pipeline stage
     const int lane = threadIdx.x;
     const int d_raw = blockIdx.x * kWave + lane;
     const bool live = d_raw < D;
@@ -275,12 +287,22 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kN > 16 ?
     // step k of the sweep visits row pos(k) of the chunk
     auto pos = [&](int k) -> int { return kRev ? len - 1 - k : k; };
 
-    auto consume = [&](const Tin *xr, const Tin *dr, int k0, int count) {
+    // Tokens stream through registers in stages of U: a stage's x and dt are
+    // loaded one stage ahead into one of two buffers used in turn (the loop is
+    // unrolled by two, so no copy between iterations forces an early wait),
+    // held as 32-bit values (Staged).  Measured on MI355X at 65,536 tokens x 8
+    // x 1536 channels (prefill): 1.735 ms with 5-token stages at 7 waves per
+    // SIMD; 1.75 ms with 4 or 6 tokens at 8, 7 or 6 waves; 1.80 ms with 8
+    // tokens at 5 waves; 1.89 ms with one 6-token buffer copied forward each
+    // stage (the copy and a 16-bit packing of the staged values waited for
+    // the loads at once); 1.95 ms with the rows staged in LDS by DMA.
+    using St = typename Staged<Tin>::type;
+    auto consume = [&](const St *xr, const St *dr, int k0, int count) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             if (i < count) {
-                const float dl = step_size<kDt>(widen(dr[i]), bias);
-                const float dx = dl * widen(xr[i]);
+                const float dl = step_size<kDt>(widen_staged(dr[i]), bias);
+                const float dx = dl * widen_staged(xr[i]);
                 S += dl;
                 const Tin *brow = bs + (int64_t)pos(k0 + i) * kN;
 #pragma unroll
@@ -293,7 +315,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kN > 16 ?
             }
         }
     };
-    auto load_stage = [&](int k0, int count, Tin *xo, Tin *dout) {
+    // count < U: the rows past the chunk re-read its last row
+    auto load_stage = [&](int k0, int count, St *xo, St *dout) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             const int k = pos(k0 + (i < count ? i : count - 1));
@@ -302,21 +325,23 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kN > 16 ?
         }
     };
 
+    // full stages in the loop (a constant token count, so no per-token
+    // branches), the partial one after it
     const int n_full = len / U;
     const int rem = len - n_full * U;
-    Tin xr[U], dr[U];
-    if (n_full > 0) load_stage(0, U, xr, dr);
-    for (int g = 0; g < n_full; ++g) {
-        // issue the next stage's loads before this stage's arithmetic
-        Tin xn[U], dn[U];
-        if (g + 1 < n_full) load_stage((g + 1) * U, U, xn, dn);
-        consume(xr, dr, g * U, U);
-#pragma unroll
-        for (int i = 0; i < U; ++i) { xr[i] = xn[i]; dr[i] = dn[i]; }
+    St xa[U], da[U], xb[U], db[U];
+    if (n_full > 0) load_stage(0, U, xa, da);
+    int g = 0;
+    for (; g + 1 < n_full; g += 2) {
+        load_stage((g + 1) * U, U, xb, db);
+        consume(xa, da, g * U, U);
+        if (g + 2 < n_full) load_stage((g + 2) * U, U, xa, da);
+        consume(xb, db, (g + 1) * U, U);
     }
+    if (g < n_full) consume(xa, da, g * U, U);       // an odd number of full stages: the last is in xa
     if (rem > 0) {
-        load_stage(n_full * U, rem, xr, dr);
-        consume(xr, dr, n_full * U, rem);
+        load_stage(n_full * U, rem, xb, db);
+        consume(xb, db, n_full * U, rem);
     }
     if (live) {
         store_row<kN>(hout + (((int64_t)b * n_chunks + c) * D + d) * kN, h);
@@ -876,7 +901,7 @@ __global__ __launch_bounds__(kWave) void sweep_output_kernel(
     int64_t T, int D, int64_t Tc, int n_chunks, const float *__restrict__ dt_bias,
     const Tin *__restrict__ z)
 {
-    constexpr int U = 4;                      // tokens per pipeline stage
+    constexpr int U = 6;                      // tokens per pipeline stage
     const int lane = threadIdx.x;
     const int d_raw = blockIdx.x * kWave + lane;
     const bool live = d_raw < D;

@@ -19,8 +19,8 @@ namespace bdssm_host {
 
 using namespace bdssm_dev;
 
-// 256 CUs x 4 SIMDs x 8 resident waves (the chunk kernel fits in 64 VGPRs)
-constexpr int64_t kFineWaves = 256 * 4 * 8;
+// 256 CUs x 4 SIMDs x the chunk kernel's resident waves per SIMD
+constexpr int64_t kFineWaves = 256 * 4 * kChunkWaves;
 // workgroups of the bidirectional kernel resident at once (two 4-wave
 // workgroups per CU at its register use)
 constexpr int64_t kCoarseGroups = 512;
@@ -33,7 +33,7 @@ constexpr double kBwdPrepassWeight = 0.2;
 // so a launch has batch * ceil(D/64) waves per chunk; long sequences are cut
 // into chunks until the chip is full.
 //   fine chunks  (one wave per 64 channels, 16 states per lane): at most
-//                kFineWaves waves, the number resident at once (8 per SIMD),
+//                kFineWaves waves, the number resident at once (kChunkWaves per SIMD),
 //                so the launch runs in a single round with no tail.
 //   coarse chunks (bidirectional pass, 4 independent waves per 64
 //                channels): count chosen by a small cost model (below) against
