@@ -160,9 +160,10 @@ def committed_traffic(workload, batch, D):
 
 
 def committed_clock(workload):
-    """(clock GHz, VALUBusy %, kernel average us) of the prefill's chunk scan
-    from the committed VALU counter summary for this workload, or None if there
-    is none or the kernels have changed since it was taken."""
+    """Clock and issue figures of the prefill's chunk scan from the committed VALU
+    counter summary for this workload, or None if there is none or the kernels
+    have changed since it was taken. Every figure comes from that one counter
+    run: its clock, VALUBusy, kernel average and issue fraction at its clock."""
     from mamba_selective_scan_04_amd import profile_summary
     path = os.path.join(ROOT, "profiles", "prefill_%s_valu_counters.md" % workload.replace("infer_", ""))
     if not os.path.exists(path):
@@ -176,12 +177,14 @@ def committed_clock(workload):
         if len(cells) != 10 or not re.fullmatch(r"chunk_state_kernel<\w+, false, false, 0, 16>", cells[0]):
             continue
         try:
-            grid, us, ghz, busy = int(cells[1]), float(cells[3]), float(cells[4]), float(cells[9])
+            grid, us, ghz, frac, busy = (int(cells[1]), float(cells[3]), float(cells[4]), float(cells[8]),
+                                         float(cells[9]))
         except ValueError:
             continue
         if best is None or grid > best[0]:
-            best = (grid, ghz, busy, us)
-    return None if best is None else best[1:]
+            best = (grid, {"clock_GHz": ghz, "valu_busy_pct": busy, "kernel_us": us,
+                           "slot_frac_at_its_clock": frac})
+    return None if best is None else best[1]
 
 
 # ------------------------------------------------------------ microbenchmarks
@@ -957,14 +960,15 @@ def inference_line(args, r, probes, configs):
                      "issue",
         "launch_ms": e_ms,
         "frac_of_probed_fma_rate": pf_slots / (e_ms * 1e-3) / (probes["fma_T_per_s"] * 1e12),
+        "frac_of_probed_scan_mix": pf["tokens_per_s"] * r["d_inner"] * NS / (probes["scan_mix_T_elements_per_s"] * 1e12),
         "frac_hbm_of_probed_read": pf["GBs"] / probes["hbm_read_GBs"],
     }
     clk = None if fused else committed_clock(args.workload)
     if clk is not None:
-        roofline["clock_GHz_measured"] = clk[0]
-        roofline["valu_busy_pct"] = clk[1]
-        roofline["counter_run_kernel_us"] = clk[2]
-        roofline["frac_at_measured_clock"] = pf["slot_frac"] * 2.4 / clk[0]
+        roofline["counter_run"] = dict(clk, note=(
+            "the chunk scan alone, from the committed VALU counter pass (a profiled run, own clock); "
+            "slot_frac_at_its_clock above 1 means the SIMDs overlapped part of each v_exp_f32's second "
+            "issue cycle with other waves' VALU work, so the 2-slot exp model is a conservative roof"))
     line = {
         "metric": "block-step scan GB/s & % HBM peak at 65K/262K ctx; prefill tokens/s",
         "value": r["step"]["GBs"],
