@@ -164,6 +164,18 @@ __device__ __forceinline__ float xchg16(float v) {       // ds_swizzle bit mode:
 __device__ __forceinline__ float xchg32(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(v)));
 }
+// Two-value folds with the gfx950 lane swaps (VALU instructions, no LDS pipe):
+// fold32(a, b) is a[l] + a[l + 32] in lanes l < 32 and b[l - 32] + b[l] in lanes
+// l >= 32; fold16(a, b) is, per 16-lane row r, the sum of rows r and r ^ 1 of a
+// in the even rows and of b in the odd rows.
+__device__ __forceinline__ float fold32(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float fold16(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // ------------------------------------------------------------------------
 // Backward of the bidirectional pass over one coarse chunk.  Same lane layout
@@ -535,16 +547,19 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 //     state, gr reset at block starts; keeps a_t, hf_{t-1}, gr_t per token;
 //   pass B (right to left): hr (reset at block ends), gf (q carried across
 //     groups; + dbounds or reset at block ends), every gradient term.
-// Reductions go through small per-wave LDS transposes instead of cross-lane
-// butterflies:
-//   * dB / dC: per token the lane's 4 values go to tb[value][channel]; lane
-//     pairs then read one value's 8 channels (one 16-byte read each half) and
-//     add; the wave's sums meet the other waves' in red (one barrier per
-//     group) and are added in a fixed order into part_bc [batch, ceil(D/32),
-//     T, 32], reduced over channel blocks by bc_reduce_kernel;
-//   * dt and x: per token the lane's two partial sums go to td[token][q]
-//     [channel][pair]; every 4 tokens each lane sums one (token, q, channel)
-//     over the 8 state pairs and stores it.
+// Reductions stay in registers (VALU lane exchanges, no LDS round trip):
+//   * dB / dC: per token the lane's 4 values are summed over the wave's 8
+//     channels by two 32-lane folds (permlane32 swaps), one 16-lane fold
+//     (permlane16 swap) and a DPP row rotation, which leave lane l with value
+//     kind l / 16 of state pair l % 8; the wave's sums meet the other waves'
+//     in red (one barrier per group) and are added in a fixed order into
+//     part_bc [batch, ceil(D/32), T, 32], reduced over channel blocks by
+//     bc_reduce_kernel;
+//   * dt and x: per token the lane's two partial sums are summed over the
+//     channel's 8 state pairs by a DPP half-row mirror exchange (dt kept in
+//     lanes g < 4, x in g >= 4) and two quad exchanges; each lane keeps one
+//     token of every 4, so that after 4 tokens the 64 lanes hold (token, dt
+//     or x, channel) and store them together.
 // Staging: x / dt / dy rows of the wave's 8 channels and the group's B / C
 // rows (shared by the workgroup, each wave loads a quarter) are DMA'd into
 // LDS one group ahead and widened to fp32 in place by the lane that loaded
@@ -609,7 +624,6 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
     constexpr int ES = sizeof(Tin);
     constexpr int G = kGroup;                 // 16 tokens per group
     constexpr int NSB = kFuse ? 4 : 3;        // row streams: x, dt, dy (, z)
-    constexpr int NQ = 2;                     // transposed per-token sums: dt, x
     // L = 0: blocks of Lr tokens, a multiple of 16 above 16, spanning several
     // groups; gstate holds the forward state and the reverse adjoint's carry
     // at every group start ([batch, T/16, 2, D, 16], group_state_kernel)
@@ -622,8 +636,6 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
     // and [B, C][token][state]
     __shared__ __attribute__((aligned(16))) uint32_t xdA[4][NSB][G][CW], xdB[4][NSB][G][CW];
     __shared__ __attribute__((aligned(16))) uint32_t bcA[2][G][kStates], bcB[2][G][kStates];
-    __shared__ __attribute__((aligned(16))) float tb[4][2 * kStates][CW];   // dB / dC transpose, one token
-    __shared__ __attribute__((aligned(16))) float td[4][4][NQ][CW][CW];     // per-token sums, 4 tokens
     __shared__ __attribute__((aligned(16))) float redA[4][G * 2 * kStates], redB[4][G * 2 * kStates];
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -664,11 +676,18 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
         *reinterpret_cast<float2 *>(dh0 + (((int64_t)b * (nbl + 1) + nbl) * D + d) * kStates + s0) =
             make_float2(0.f, 0.f);
 
-    // output lane of the dt / x transpose: token l / 16 of a 4-token segment,
-    // quantity (l / 8) % 2 (0: dt, 1: x), channel l % 8
-    const int o_tok = lane >> 4, o_q = (lane >> 3) & 1, o_ch = lane & 7;
+    // after the per-token channel sums: lane l holds dB / dC value kind l / 16
+    // (dB of state 2g, dB of 2g + 1, dC of 2g, dC of 2g + 1) of state pair
+    // g = l % 8, i.e. entry bc_idx of the token's 32 (dB by state, then dC)
+    const int bc_idx = ((lane >> 5) << 4) + s0 + ((lane >> 4) & 1);
+    // the dt / x sums of a 4-token segment: lane l holds token 4s + l % 4 of
+    // quantity (l / 4) % 2 (0: dt, 1: x) of its own channel cl
+    const int o_tok = lane & 3, o_q = (lane >> 2) & 1;
+    // Dskip dy enters the x sum once per channel, in lane g == 4
+    const float dskg = (g == 4) ? Dskip[d] : 0.f;
+    // the fused epilogue's lanes: tokens l / 8 and l / 8 + 8, channel l % 8
+    const int o_ch = lane & 7;
     const bool o_live = d_w0 + o_ch < D;
-    const float o_dsk = Dskip[o_live ? d_w0 + o_ch : D - 1];
 
     const int64_t first = (int64_t)b * T + t_begin;
     const Rows<Tin> xs(x + first * D, len, D, 0);
@@ -821,6 +840,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
         if constexpr (kLong) {
             hr[0] = hrc[0]; hr[1] = hrc[1];
         }
+        float tsum = 0.f;                     // this lane's token of the current 4-token segment
 #pragma unroll
         for (int i = G - 1; i >= 0; --i) {
             if ((i + 1) % LB == 0 && geb) {
@@ -859,7 +879,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
                 vc[j] = gy * (hf_t + hr[j]);          // dC
                 if constexpr (kFuse) yp = __builtin_fmaf(cc[j], hf_t + hr[j], yp);
             }
-            if (g == 0) dD_acc = __builtin_fmaf(gy, xv, dD_acc);
+            dD_acc = __builtin_fmaf(gy, xv, dD_acc);   // every lane; lane g == 0's total is stored
             if constexpr (kFuse) {
                 // y_pre of the token: the lane's C (hf + hr) summed over the
                 // channel's 8 state pairs (lanes 8 cl .. 8 cl + 7), + Dskip x,
@@ -876,45 +896,45 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
                         make_float2(q[0], q[1]);
                 }
             }
-            // dB / dC of the token: sum over the wave's 8 channels
-            tb[w][s0][cl] = vb[0];
-            tb[w][s0 + 1][cl] = vb[1];
-            tb[w][kStates + s0][cl] = vc[0];
-            tb[w][kStates + s0 + 1][cl] = vc[1];
+            // dB / dC of the token summed over the wave's 8 channels (lanes
+            // g, g + 8, ..., g + 56): the 32-lane folds add channel c + 4 to c,
+            // the 16-lane fold channel c + 2, the row rotation by 8 channel
+            // c + 1; the sums meet the other waves' in red
             {
-                const float4 h4 = *reinterpret_cast<const float4 *>(&tb[w][lane >> 1][4 * (lane & 1)]);
-                float sum = (h4.x + h4.y) + (h4.z + h4.w);
-                sum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sum), 0xB1, 0xF, 0xF, false));
-                if ((lane & 1) == 0) red[w][i * 2 * kStates + (lane >> 1)] = sum;
+                const float f0 = fold32(vb[0], vc[0]);
+                const float f1 = fold32(vb[1], vc[1]);
+                float sum = fold16(f0, f1);
+                sum += xchg8(sum);
+                if ((lane & 8) == 0) red[w][i * 2 * kStates + bc_idx] = sum;
             }
-            // dt and x partials of the token: sum over the channel's 8 pairs,
-            // flushed every 4 tokens
-            td[w][i & 3][0][cl][g] = __builtin_fmaf(xv, s1, s2);
-            td[w][i & 3][1][cl][g] = dl * s1;
+            // dt and x partials of the token summed over the channel's 8 state
+            // pairs: the half-row mirror exchange leaves the dt sum's pairs in
+            // lanes g < 4 and the x sum's in lanes g >= 4, two quad exchanges
+            // complete them; lane g keeps token i where g % 4 == i % 4
+            {
+                const float pa = __builtin_fmaf(xv, s1, s2);
+                const float pb = __builtin_fmaf(dskg, gy, dl * s1);
+                float v = o_q ? pb : pa;
+                const float snd = o_q ? pa : pb;
+                v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(snd), 0x141, 0xF, 0xF, false));
+                v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+                v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+                if (o_tok == (i & 3)) tsum = v;
+            }
             if ((i & 3) == 0) {
-                const float4 p0 = *reinterpret_cast<const float4 *>(&td[w][o_tok][o_q][o_ch][0]);
-                const float4 p1 = *reinterpret_cast<const float4 *>(&td[w][o_tok][o_q][o_ch][4]);
-                float tot = ((p0.x + p0.y) + (p0.z + p0.w)) + ((p1.x + p1.y) + (p1.z + p1.w));
                 const int it = i + o_tok;
                 if constexpr (kFuse) {
                     // dx is final here; the dt-stream gradient before the
-                    // softplus factor goes to the token's dy slot (read
-                    // first by the dx lanes) for the group's epilogue
-                    const float gyv = f32(xd[w][2][it][o_ch]);
+                    // softplus factor goes to the token's dy slot for the
+                    // group's epilogue
                     if (o_q) {
-                        tot = __builtin_fmaf(gyv, o_dsk, tot);
-                        if (o_live && it < nvalid) dxw[(int64_t)(k0 + it) * D + d_w0 + o_ch] = narrow<Tin>(tot);
+                        if (live && it < nvalid) dxw[(int64_t)(k0 + it) * D + d] = narrow<Tin>(tsum);
+                    } else {
+                        xd[w][2][it][cl] = __float_as_uint(tsum);
                     }
-                    asm volatile("" ::: "memory");
-                    if (!o_q) xd[w][2][it][o_ch] = __float_as_uint(tot);
                 } else {
-                    if (o_live && it < nvalid) {
-                        Tin *dst = (o_q ? dxw : dtw) + (int64_t)(k0 + it) * D + d_w0 + o_ch;
-                        if (o_q) tot = __builtin_fmaf(f32(xd[w][2][it][o_ch]), o_dsk, tot);
-                        *dst = narrow<Tin>(tot);
-                    }
+                    if (live && it < nvalid) (o_q ? dxw : dtw)[(int64_t)(k0 + it) * D + d] = narrow<Tin>(tsum);
                 }
-                asm volatile("" ::: "memory");
             }
         }
         if constexpr (kLong) {
