@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(6))) void
 
 // Cross-lane exchanges used by the channel reduction (partner = lane ^ mask).
 __device__ __forceinline__ float xchg8(float v) {        // DPP row_ror:8 == lane ^ 8 in a row of 16
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+    return dpp_perm<kDppRor8>(v);
 }
 __device__ __forceinline__ float xchg4(float v) {        // ds_swizzle bit mode: xor_mask 4
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (4 << 10) | 0x1F));
@@ -317,15 +317,16 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
                 bcf[w][4 * j + ld_tok][which][ld_col] = elem(bcr[w][which][j][lane]);
     };
     auto xor2 = [](float v) {
-        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+        return dpp_perm<kDppXor2>(v);
     };
     auto xor1 = [](float v) {
-        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+        return dpp_perm<kDppXor1>(v);
     };
     const bool hi2 = (g & 2) != 0, hi1 = (g & 1) != 0;
     const bool b2 = (lane & 4) != 0, b3 = (lane & 8) != 0, b4 = (lane & 16) != 0, b5 = (lane & 32) != 0;
-    // slot of this lane's reduced dB / dC value within a token's 32
-    const int red_slot = (b3 ? kStates : 0) + s0 + (b2 ? 2 : 0) + (b4 ? 1 : 0);
+    // slot of this lane's reduced dB / dC value within a token's 32: dB (b5
+    // clear) or dC, state 4g + 2 b4 + b3
+    const int red_slot = (b5 ? kStates : 0) + s0 + (b4 ? 2 : 0) + (b3 ? 1 : 0);
     const int nblk64 = gridDim.x;
     float *pbc = part_bc + ((int64_t)b * nblk64 + blockIdx.x) * T * 32;
     Tin *dxl = dx + first * D + d;
@@ -447,28 +448,17 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
                 }
                 {
                     // reduce the token's 8 values (dB, dC x 4 states) over the
-                    // wave's 16 channels: reduce-scatter over lanes ^ 8, ^ 4, ^ 16,
-                    // then a plain sum over lanes ^ 32 (both halves hold it)
-                    float r4[4];
+                    // wave's 16 channels: reduce-scatter over lane bit 5 (dB /
+                    // dC) and bit 4 (states j, j + 2) by lane-swap folds, over
+                    // bit 3 (states j, j + 1) by a row rotation, then a plain
+                    // sum over bit 2 (both lanes hold it)
+                    float f4[4];
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const float keep = b3 ? tokv[m + 4] : tokv[m];
-                        const float send = b3 ? tokv[m] : tokv[m + 4];
-                        r4[m] = keep + xchg8(send);
-                    }
-                    float r2[2];
-#pragma unroll
-                    for (int m = 0; m < 2; ++m) {
-                        const float keep = b2 ? r4[m + 2] : r4[m];
-                        const float send = b2 ? r4[m] : r4[m + 2];
-                        r2[m] = keep + xchg4(send);
-                    }
-                    const float keep = b4 ? r2[1] : r2[0];
-                    const float send = b4 ? r2[0] : r2[1];
-                    float r1 = keep + xchg16(send);
-                    r1 += xchg32(r1, lane);
-                    // slot: dB (b3 = 0) or dC (b3 = 1), state 4g + 2 b2 + b4
-                    if (!b5) red[w][i * 2 * kStates + red_slot] = r1;
+                    for (int m = 0; m < 4; ++m) f4[m] = fold32(tokv[m], tokv[m + 4]);
+                    const float e0 = fold16(f4[0], f4[2]), e1 = fold16(f4[1], f4[3]);
+                    float r1 = (b3 ? e1 : e0) + xchg8(b3 ? e0 : e1);
+                    r1 += xchg4(r1);
+                    if (!b2) red[w][i * 2 * kStates + red_slot] = r1;
                 }
             }
             // ddt and dx of the segment: quad reduce-scatter over the channel's
@@ -550,9 +540,10 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 // Reductions stay in registers (VALU lane exchanges, no LDS round trip):
 //   * dB / dC: per token the lane's 4 values are summed over the wave's 8
 //     channels by two 32-lane folds (permlane32 swaps), one 16-lane fold
-//     (permlane16 swap) and a DPP row rotation, which leave lane l with value
-//     kind l / 16 of state pair l % 8; the wave's sums meet the other waves'
-//     in red (one barrier per group) and are added in a fixed order into
+//     (permlane16 swap) and a DPP row rotation over a token pair, which leave
+//     lane l with value kind l / 16 of state pair l % 8 of one of the two
+//     tokens; the wave's sums meet the other waves' in red (one barrier per
+//     group) and are added in a fixed order into
 //     part_bc [batch, ceil(D/32), T, 32], reduced over channel blocks by
 //     bc_reduce_kernel;
 //   * dt and x: per token the lane's two partial sums are summed over the
@@ -680,6 +671,9 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
     // (dB of state 2g, dB of 2g + 1, dC of 2g, dC of 2g + 1) of state pair
     // g = l % 8, i.e. entry bc_idx of the token's 32 (dB by state, then dC)
     const int bc_idx = ((lane >> 5) << 4) + s0 + ((lane >> 4) & 1);
+    // a token pair's sums: lanes with bit 3 clear hold token i + 1, the others token i
+    const bool b3 = (lane & 8) != 0;
+    const int red_lane = (b3 ? 0 : 2 * kStates) + bc_idx;
     // the dt / x sums of a 4-token segment: lane l holds token 4s + l % 4 of
     // quantity (l / 4) % 2 (0: dt, 1: x) of its own channel cl
     const int o_tok = lane & 3, o_q = (lane >> 2) & 1;
@@ -841,6 +835,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
             hr[0] = hrc[0]; hr[1] = hrc[1];
         }
         float tsum = 0.f;                     // this lane's token of the current 4-token segment
+        float s16_next = 0.f;                 // the 16-lane fold of token i + 1 (i even)
 #pragma unroll
         for (int i = G - 1; i >= 0; --i) {
             if ((i + 1) % LB == 0 && geb) {
@@ -884,9 +879,9 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
                 // y_pre of the token: the lane's C (hf + hr) summed over the
                 // channel's 8 state pairs (lanes 8 cl .. 8 cl + 7), + Dskip x,
                 // into the token's x slot (pass B is done with it)
-                yp += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(yp), 0xB1, 0xF, 0xF, false));
-                yp += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(yp), 0x4E, 0xF, 0xF, false));
-                yp += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(yp), 0x141, 0xF, 0xF, false));
+                yp += dpp_perm<kDppXor1>(yp);
+                yp += dpp_perm<kDppXor2>(yp);
+                yp += dpp_perm<kDppHalfMirror>(yp);
                 xd[w][0][i][cl] = __float_as_uint(__builtin_fmaf(dsk, xv, yp));
             }
             if constexpr (kBlockInit) {
@@ -898,14 +893,23 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
             }
             // dB / dC of the token summed over the wave's 8 channels (lanes
             // g, g + 8, ..., g + 56): the 32-lane folds add channel c + 4 to c,
-            // the 16-lane fold channel c + 2, the row rotation by 8 channel
-            // c + 1; the sums meet the other waves' in red
+            // the 16-lane fold channel c + 2; the last step (channel c + 1, a
+            // row rotation by 8) takes two tokens at once, lanes with bit 3
+            // clear keeping token i + 1 and the others token i, so that all
+            // 64 lanes store a distinct sum; the sums meet the other waves'
+            // in red
             {
                 const float f0 = fold32(vb[0], vc[0]);
                 const float f1 = fold32(vb[1], vc[1]);
-                float sum = fold16(f0, f1);
-                sum += xchg8(sum);
-                if ((lane & 8) == 0) red[w][i * 2 * kStates + bc_idx] = sum;
+                const float s16 = fold16(f0, f1);
+                if (i & 1) {
+                    s16_next = s16;
+                } else {
+                    float keep = b3 ? s16 : s16_next;
+                    const float snd = b3 ? s16_next : s16;
+                    keep += xchg8(snd);
+                    red[w][i * 2 * kStates + red_lane] = keep;
+                }
             }
             // dt and x partials of the token summed over the channel's 8 state
             // pairs: the half-row mirror exchange leaves the dt sum's pairs in
@@ -916,9 +920,9 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
                 const float pb = __builtin_fmaf(dskg, gy, dl * s1);
                 float v = o_q ? pb : pa;
                 const float snd = o_q ? pa : pb;
-                v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(snd), 0x141, 0xF, 0xF, false));
-                v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-                v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+                v += dpp_perm<kDppHalfMirror>(snd);
+                v += dpp_perm<kDppXor1>(v);
+                v += dpp_perm<kDppXor2>(v);
                 if (o_tok == (i & 3)) tsum = v;
             }
             if ((i & 3) == 0) {
@@ -1212,18 +1216,27 @@ __global__ __launch_bounds__(kWave) void group_state_kernel(
 // v summed with the lane v ^ kMask holds (all lanes active)
 template <int kMask> __device__ __forceinline__ float xor_add(float v, int lane) {
     if constexpr (kMask == 1)
-        return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+        return v + dpp_perm<kDppXor1>(v);
     else if constexpr (kMask == 2)
-        return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+        return v + dpp_perm<kDppXor2>(v);
     else if constexpr (kMask == 4) return v + xchg4(v);
     else if constexpr (kMask == 8) return v + xchg8(v);
-    else if constexpr (kMask == 16) return v + xchg16(v);
-    else return v + xchg32(v, lane);
+    else if constexpr (kMask == 16) return fold16(v, v);
+    else return fold32(v, v);
 }
 // butterfly sum over the lane-index bits kFrom, 2 kFrom, ... below kTo
 template <int kFrom, int kTo> __device__ __forceinline__ float lane_sum(float v, int lane) {
-    if constexpr (kFrom >= kTo) return v;
-    else return lane_sum<2 * kFrom, kTo>(xor_add<kFrom>(v, lane), lane);
+    if constexpr (kFrom >= kTo) {
+        return v;
+    } else if constexpr (kFrom == 4 && kTo >= 16) {
+        // bits 2 and 3 together: row rotations by 4 and 8 add up the four
+        // lanes of a 16-lane row that agree in bits 0 and 1
+        v += dpp_perm<kDppRor4>(v);
+        v += dpp_perm<kDppRor8>(v);
+        return lane_sum<16, kTo>(v, lane);
+    } else {
+        return lane_sum<2 * kFrom, kTo>(xor_add<kFrom>(v, lane), lane);
+    }
 }
 
 // The sum over each aligned group of kN lanes, in every lane of the group,
@@ -1231,22 +1244,14 @@ template <int kFrom, int kTo> __device__ __forceinline__ float lane_sum(float v,
 // half-row mirror (kN = 8) or row rotations by 4 and 8 (kN = 16: after the
 // quad sums, rotating a 16-lane row by 4 and then 8 adds up its four quads).
 template <int kN> __device__ __forceinline__ float group_sum(float v, int lane) {
-    auto dpp = [](float x, auto ctrl) {
-        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, false));
-    };
-    using Q1 = std::integral_constant<int, 0xB1>;     // quad_perm [1,0,3,2]
-    using Q2 = std::integral_constant<int, 0x4E>;     // quad_perm [2,3,0,1]
-    using HM = std::integral_constant<int, 0x141>;    // row_half_mirror
-    using R4 = std::integral_constant<int, 0x124>;    // row_ror:4
-    using R8 = std::integral_constant<int, 0x128>;    // row_ror:8
-    v += dpp(v, Q1{});
-    if constexpr (kN >= 4) v += dpp(v, Q2{});
-    if constexpr (kN == 8) v += dpp(v, HM{});
+    v += dpp_perm<kDppXor1>(v);
+    if constexpr (kN >= 4) v += dpp_perm<kDppXor2>(v);
+    if constexpr (kN == 8) v += dpp_perm<kDppHalfMirror>(v);
     if constexpr (kN >= 16) {
-        v += dpp(v, R4{});
-        v += dpp(v, R8{});
+        v += dpp_perm<kDppRor4>(v);
+        v += dpp_perm<kDppRor8>(v);
     }
-    if constexpr (kN >= 32) v += xchg16(v);
+    if constexpr (kN >= 32) v = fold16(v, v);
     (void)lane;
     return v;
 }

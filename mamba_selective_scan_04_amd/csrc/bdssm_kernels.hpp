@@ -70,6 +70,19 @@ template <> __device__ __forceinline__ uint16_t narrow<uint16_t>(float v) {
 
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 
+// A full lane permutation by DPP (every lane reads a valid source lane: quad
+// permutations, row rotations, row mirrors).  Written with a zero old value and
+// bound_ctrl so that the compiler folds the move into the instruction that
+// consumes it (v_add_f32_dpp and the like).
+template <int kCtrl> __device__ __forceinline__ float dpp_perm(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppHalfMirror = 0x141;   // row_half_mirror: lane ^ 7 within 8
+constexpr int kDppRor4 = 0x124;         // row_ror:4
+constexpr int kDppRor8 = 0x128;         // row_ror:8: lane ^ 8 within a row of 16
+
 // ------------------------------------------------- optional Mamba-1 fusions
 // The step size may arrive raw: dt = dt_raw + bias (kDtBias), optionally
 // through softplus (kDtSoftplus); the output may be gated by silu(z).
@@ -594,10 +607,10 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
     auto dt_elem = [&](uint32_t v) -> float { return kFuse != 0 ? __uint_as_float(v) : elem(v); };
     // quad reduce-scatter helpers (DPP within groups of 4 lanes)
     auto xor2 = [](float v) {
-        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+        return dpp_perm<kDppXor2>(v);
     };
     auto xor1 = [](float v) {
-        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+        return dpp_perm<kDppXor1>(v);
     };
     Tin *ylane = y + first * D + d;
     const bool hi2 = (g & 2) != 0, hi1 = (g & 1) != 0;
