@@ -578,7 +578,6 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 // gradient's sums over the chunk's tokens go to part_bias [batch, chunks, D]
 // for the gradient of dt_bias.  (Done inside pass B, the same work spills.)
 // grid = (ceil(D/32), chunks, batch), block = 256.
-constexpr int kPairChannels = 32;     // channels per bwd_pair_kernel workgroup
 
 template <typename Tin> struct BwdFuse {
     const float *dt_bias;   // [D] or null
@@ -821,9 +820,12 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
                 hf[j] = __builtin_fmaf(a, hf[j], dxv * bb[j]);
                 pr[j] = a * gr_j;
             }
-            // 4-token batches: keeps the compiler from reading all 16 tokens'
-            // rows ahead (register pressure)
-            if ((i & 3) == 3) asm volatile("" ::: "memory");
+            // 4-token batches: the batch's arithmetic completes before the
+            // next batch's rows are read (register pressure)
+            if ((i & 3) == 3)
+                asm volatile("" : "+v"(hf[0]), "+v"(hf[1]), "+v"(pr[0]), "+v"(pr[1]), "+v"(gr_s[i][0]),
+                             "+v"(gr_s[i][1]), "+v"(gr_s[i - 1][0]), "+v"(gr_s[i - 1][1]), "+v"(gr_s[i - 2][0]),
+                             "+v"(gr_s[i - 2][1]), "+v"(gr_s[i - 3][0]), "+v"(gr_s[i - 3][1]) :: "memory");
         }
 
         // read the token rows again in pass B rather than keeping pass A's
@@ -926,6 +928,8 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
                 if (o_tok == (i & 3)) tsum = v;
             }
             if ((i & 3) == 0) {
+                asm volatile("" : "+v"(hr[0]), "+v"(hr[1]), "+v"(q[0]), "+v"(q[1]), "+v"(dA_acc[0]),
+                             "+v"(dA_acc[1]), "+v"(tsum), "+v"(dD_acc) :: "memory");
                 const int it = i + o_tok;
                 if constexpr (kFuse) {
                     // dx is final here; the dt-stream gradient before the

@@ -769,6 +769,287 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 }
 
 // ------------------------------------------------------------------------
+// Bidirectional kernel, two states per lane (the shared-operand passes: plain
+// and with the step-size / gate fusions): lane = 8 * channel + state pair
+// (states 2g, 2g + 1), 8 channels per wave, 4 waves (32 channels) per
+// workgroup.  A 16-token group's decays then take 32 registers per lane
+// instead of 64, and the kernel runs more waves per SIMD than
+// bidir_wave_kernel, whose four-state lanes wait on latency at two.
+// Per group, staged as in bwd_pair_kernel (the x / dt (/ z) rows of the
+// wave's 8 channels DMA'd into the wave's LDS slice, the group's B / C rows
+// shared by the workgroup, each wave loading a quarter; one group ahead,
+// widened in place by the lane that loaded them; one barrier per group):
+//   forward, left to right: a = exp2(dt A'), hf = a hf + dt x B, the lane's
+//     output partial C . hf over its two states; the decays and dt x of the
+//     group stay in registers;
+//   reverse, right to left, reset where a block ends: hr = a hr + dt x B,
+//     partial += C . hr;
+//   output: the 16 tokens' partials are summed over the channel's 8 lanes by
+//     a reduce-scatter (DPP half-row mirror, then the two quad exchanges),
+//     after which lane g holds tokens 2g and 2g + 1 of its channel; + Dskip x,
+//     times silu(z) with the gate, stored through buffer stores whose
+//     out-of-range offsets drop dead channels and tokens past the chunk.
+// dt of tokens past the chunk end and of channels past D reads zero (an
+// out-of-range DMA offset; after the step-size transform it is set to zero
+// again): such tokens decay by 1 and inject nothing.
+// Arguments as in bidir_wave_kernel; separate reverse operands run
+// bidir_wave_kernel<..., 2>.
+// grid = (ceil(D/32), chunks, batch), block = 256.
+constexpr int kPairChannels = 32;     // channels per workgroup of the two-state kernels
+
+template <typename Tin, int L, bool kBlockInit, int kFuse = 0>
+__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 1 ? 2 : 4))) void bidir_pair_kernel(
+    const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
+    const Tin *__restrict__ Cm, const float *__restrict__ A, const float *__restrict__ Dskip,
+    const float *hin, int64_t hin_bs, int64_t hin_cs,
+    Tin *__restrict__ y, float *__restrict__ bounds, float *hout,
+    int64_t T, int D, int64_t Tc, const float *__restrict__ h0_blocks, FuseArgs<Tin> fz)
+{
+    static_assert(kFuse == 0 || kFuse == 1, "separate reverse operands run bidir_wave_kernel");
+    static_assert(kGroup % L == 0, "block length must divide the token group");
+    constexpr int CW = 8;                     // channels per wave
+    constexpr int ES = sizeof(Tin);
+    constexpr int G = kGroup;                 // 16 tokens per group
+    constexpr int NS = kFuse ? 3 : 2;         // row streams: x, dt (, z)
+    // double buffers as distinct arrays (the loads in flight into one are told
+    // apart from the reads of the other): [wave][stream][token][channel] and
+    // [B, C][token][state]
+    __shared__ __attribute__((aligned(16))) uint32_t xdA[4][NS][G][CW], xdB[4][NS][G][CW];
+    __shared__ __attribute__((aligned(16))) uint32_t bcA[2][G][kStates], bcB[2][G][kStates];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = uniform(threadIdx.x >> 6);
+    const int cl = lane >> 3;                 // channel within the wave
+    const int g = lane & 7;                   // state pair
+    const int s0 = 2 * g;
+    const int d_w0 = blockIdx.x * kPairChannels + w * CW;
+    const int d_raw = d_w0 + cl;
+    const bool live = d_raw < D;
+    const int d = live ? d_raw : D - 1;
+    const int c = blockIdx.y;
+    const int b = blockIdx.z;
+    const int64_t t_begin = (int64_t)c * Tc;
+    const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
+    const int len = (int)(t_end - t_begin);
+    const int64_t nbl = T / L;
+
+    float a2[2], hf[2] = {0.f, 0.f};
+    {
+        const float2 av = *reinterpret_cast<const float2 *>(A + (int64_t)d * kStates + s0);
+        a2[0] = av.x * kLog2e; a2[1] = av.y * kLog2e;
+        if (hin != nullptr) {
+            const float2 hv = *reinterpret_cast<const float2 *>(
+                hin + (int64_t)b * hin_bs + (int64_t)c * hin_cs + (int64_t)d * kStates + s0);
+            hf[0] = hv.x; hf[1] = hv.y;
+        }
+    }
+    const float dsk = Dskip[d];
+    auto store_state = [&](float *dst) {
+        *reinterpret_cast<float2 *>(dst + s0) = make_float2(hf[0], hf[1]);
+    };
+    if (bounds != nullptr && c == 0 && live)
+        store_state(bounds + ((int64_t)b * (nbl + 1) * D + d) * kStates);
+
+    const int64_t first = (int64_t)b * T + t_begin;
+    const Rows<Tin> xs(x + first * D, len, D, 0);
+    const Rows<Tin> ds(dt + first * D, len, D, 0);
+    const Rows<Tin> ys(y + first * D, len, D, 0);
+    __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(const_cast<Tin *>(Bm + first * kStates)), 0, uniform(len * kStates * ES), kRawBufferWord3);
+    __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(const_cast<Tin *>(Cm + first * kStates)), 0, uniform(len * kStates * ES), kRawBufferWord3);
+    // DMA lanes: x / dt (/ z) load j covers tokens 8j .. 8j+7 (lane: token
+    // l / 8, channel l % 8); B / C: wave w loads tokens 4w .. 4w+3 (lane:
+    // token l / 16, state l % 16)
+    const int ld_tok = lane >> 3, ld_col = lane & 7;
+    const bool ld_live = d_w0 + ld_col < D;
+    const int ld_ch = ld_live ? d_w0 + ld_col : D - 1;
+    const int bc_tok = 4 * w + (lane >> 4), bc_col = lane & 15;
+    const bool gate = kFuse && fz.z != nullptr;
+    const float ld_bias = (kFuse && fz.dt_bias != nullptr) ? fz.dt_bias[ld_ch] : 0.f;
+    const Rows<Tin> zs((gate ? fz.z : x) + first * D, len, D, 0);
+
+    auto issue = [&](auto &xd, auto &bc, int k0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int kr = k0 + 8 * j + ld_tok;
+            const int k = kr < len ? kr : len - 1;
+            const int zoff = (kr < len && ld_live) ? ld_ch * ES + k * ds.pitch : kOutOfRange;
+            load_to_lds<ES>(xs.rsrc, &xd[w][0][8 * j][0], ld_ch * ES + k * xs.pitch, 0);
+            load_to_lds<ES>(ds.rsrc, &xd[w][1][8 * j][0], zoff, 0);
+            if constexpr (kFuse) {
+                if (gate) load_to_lds<ES>(zs.rsrc, &xd[w][2][8 * j][0], zoff, 0);
+            }
+        }
+        const int kb = (k0 + bc_tok < len) ? k0 + bc_tok : len - 1;
+        load_to_lds<ES>(brs, &bc[0][4 * w][0], (kb * kStates + bc_col) * ES, 0);
+        load_to_lds<ES>(crs, &bc[1][4 * w][0], (kb * kStates + bc_col) * ES, 0);
+    };
+    // after this wave's own loads have landed, widen the dwords this lane
+    // loaded to fp32 in place; with the fusions, form the step size (zero
+    // again past the chunk end) and silu(z)
+    auto widen = [&](auto &xd, auto &bc, int k0) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        if constexpr (ES == 2) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    if (s == 2 && !gate) continue;
+                    uint32_t &v = (&xd[w][s][8 * j][0])[lane];
+                    v <<= 16;
+                }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                uint32_t &v = (&bc[s][4 * w][0])[lane];
+                v <<= 16;
+            }
+        }
+        if constexpr (kFuse) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                uint32_t &dv = (&xd[w][1][8 * j][0])[lane];
+                const float raw = __uint_as_float(dv);
+                float dl = raw;
+                if (fz.dt_mode == kDtSoftplus) dl = step_size<kDtSoftplus>(raw, ld_bias);
+                else if (fz.dt_mode == kDtBias) dl = step_size<kDtBias>(raw, ld_bias);
+                dv = __float_as_uint(k0 + 8 * j + ld_tok < len ? dl : 0.f);
+                if (gate) {
+                    uint32_t &zv = (&xd[w][2][8 * j][0])[lane];
+                    zv = __float_as_uint(silu_f(__uint_as_float(zv)));
+                }
+            }
+        }
+    };
+    auto f32 = [](uint32_t v) { return __uint_as_float(v); };
+    auto bcv = [&](auto &bc, int which, int i) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(&bc[which][i][s0]);
+        return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
+    };
+
+    // two-stream form: the block start states of a group, loaded one group
+    // ahead with its rows for L >= 4 (at most 4 blocks per group)
+    constexpr int NB = kBlockInit ? G / L : 1;
+    constexpr bool kAhead = kBlockInit && L >= 4;
+    float2 hbn[NB];
+    auto load_hb = [&](int k0n) {
+        if constexpr (kBlockInit) {
+            const int nv = (len - k0n < G) ? len - k0n : G;
+#pragma unroll
+            for (int q = 0; q < NB; ++q) {
+                const int i = q * L < nv ? q * L : 0;
+                const int64_t blk = (t_begin + k0n + i) / L;
+                hbn[q] = *reinterpret_cast<const float2 *>(
+                    h0_blocks + (((int64_t)b * (nbl + 1) + blk) * D + d) * kStates + s0);
+            }
+        }
+    };
+    const bool hb2 = (g & 4) != 0, hb1 = (g & 2) != 0, hb0 = (g & 1) != 0;
+
+    auto group = [&](auto &xd, auto &bc, int k0, const float2 *hb) {
+        const int nvalid = (len - k0 < G) ? len - k0 : G;   // uniform
+        float dA[G][2], dxs[G], ya[G];
+        // forward, left to right
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            if constexpr (kBlockInit) {
+                if (i % L == 0) { hf[0] = hb[i / L].x; hf[1] = hb[i / L].y; }
+            }
+            const float dl = f32(xd[w][1][i][cl]);
+            const float dxv = dl * f32(xd[w][0][i][cl]);
+            const float2 bv = bcv(bc, 0, i), cv = bcv(bc, 1, i);
+            dxs[i] = dxv;
+            const float a0 = fast_exp2(dl * a2[0]), a1 = fast_exp2(dl * a2[1]);
+            dA[i][0] = a0; dA[i][1] = a1;
+            hf[0] = __builtin_fmaf(a0, hf[0], dxv * bv.x);
+            hf[1] = __builtin_fmaf(a1, hf[1], dxv * bv.y);
+            ya[i] = __builtin_fmaf(cv.y, hf[1], cv.x * hf[0]);
+            if ((i + 1) % L == 0 && bounds != nullptr && i < nvalid && live) {
+                const int64_t kb = (t_begin + k0 + i + 1) / L;
+                store_state(bounds + (((int64_t)b * (nbl + 1) + kb) * D + d) * kStates);
+            }
+            if ((i & 3) == 3) {
+                // 4-token batches: the batch's arithmetic completes before the
+                // next batch's LDS reads are issued (register pressure)
+                asm volatile("" : "+v"(hf[0]), "+v"(hf[1]), "+v"(ya[i]), "+v"(ya[i - 1]), "+v"(ya[i - 2]),
+                             "+v"(ya[i - 3]) :: "memory");
+            }
+        }
+        // reverse, right to left, from zero at every block end
+        float hr[2] = {0.f, 0.f};
+#pragma unroll
+        for (int i = G - 1; i >= 0; --i) {
+            if ((i + 1) % L == 0) { hr[0] = hr[1] = 0.f; }
+            const float2 bv = bcv(bc, 0, i), cv = bcv(bc, 1, i);
+            hr[0] = __builtin_fmaf(dA[i][0], hr[0], dxs[i] * bv.x);
+            hr[1] = __builtin_fmaf(dA[i][1], hr[1], dxs[i] * bv.y);
+            ya[i] = __builtin_fmaf(cv.y, hr[1], __builtin_fmaf(cv.x, hr[0], ya[i]));
+            if ((i & 3) == 0) {
+                asm volatile("" : "+v"(hr[0]), "+v"(hr[1]), "+v"(ya[i]), "+v"(ya[i + 1]), "+v"(ya[i + 2]),
+                             "+v"(ya[i + 3]) :: "memory");
+            }
+        }
+        // the channel's sum over its 8 lanes: lane g keeps tokens 8 (g / 4)
+        // .. + 7 after the mirror exchange (partner 7 - g), 4 of them after
+        // the exchange with g ^ 2, tokens 2g and 2g + 1 after the one with
+        // g ^ 1
+        float r8[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float keep = hb2 ? ya[k + 8] : ya[k];
+            const float send = hb2 ? ya[k] : ya[k + 8];
+            r8[k] = keep + dpp_perm<kDppHalfMirror>(send);
+        }
+        float r4[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float keep = hb1 ? r8[k + 4] : r8[k];
+            const float send = hb1 ? r8[k] : r8[k + 4];
+            r4[k] = keep + dpp_perm<kDppXor2>(send);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const float keep = hb0 ? r4[k + 2] : r4[k];
+            const float send = hb0 ? r4[k] : r4[k + 2];
+            const int t = 2 * g + k;
+            float tot = __builtin_fmaf(dsk, f32(xd[w][0][t][cl]), keep + dpp_perm<kDppXor1>(send));
+            if constexpr (kFuse) {
+                if (gate) tot *= f32(xd[w][2][t][cl]);
+            }
+            const int32_t off = (live && t < nvalid) ? (k0 + t) * ys.pitch + d * ES : kOutOfRange;
+            ys.store_at(off, narrow<Tin>(tot));
+        }
+    };
+
+    // one group: the next group's loads go out first, then this group's
+    // passes, then the next group's widening; the barrier keeps every wave's
+    // reads of this group's B / C rows ahead of the loads that overwrite them
+    auto step = [&](auto &xd, auto &bc, auto &xdn, auto &bcn, int k0) {
+        const bool more = k0 + G < len;
+        float2 hb[NB];
+        if constexpr (kBlockInit && !kAhead) load_hb(k0);
+#pragma unroll
+        for (int q = 0; q < NB; ++q) hb[q] = hbn[q];
+        if (more) {
+            if constexpr (kAhead) load_hb(k0 + G);
+            issue(xdn, bcn, k0 + G);
+        }
+        group(xd, bc, k0, hb);
+        if (more) widen(xdn, bcn, k0 + G);
+        __syncthreads();
+    };
+    if constexpr (kAhead) load_hb(0);
+    issue(xdA, bcA, 0);
+    widen(xdA, bcA, 0);
+    __syncthreads();
+    for (int k0 = 0; k0 < len; k0 += 2 * G) {
+        step(xdA, bcA, xdB, bcB, k0);
+        if (k0 + G < len) step(xdB, bcB, xdA, bcA, k0 + G);
+    }
+    if (hout != nullptr && t_end == T && live) store_state(hout + ((int64_t)b * D + d) * kStates);
+}
+
+// ------------------------------------------------------------------------
 // One block from the cache, for the latency-bound single-block calls
 // (block_step, commit; L <= 16, shared operands): one lane per (channel,
 // state), 64 / kN channels per wave, four independent waves per workgroup, so a block

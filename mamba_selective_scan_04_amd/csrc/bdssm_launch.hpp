@@ -67,7 +67,7 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // many of its workgroups are resident at once (the forward wave kernel: 64,
 // 512; bwd_pair_kernel: 32, 768).
 inline Plan make_plan(int64_t batch, int64_t D, int64_t T, double prepass_weight = 0.45,
-               int64_t coarse_ch = kWave, int64_t coarse_cap = kCoarseGroups) {
+               int64_t coarse_ch = kWave, int64_t coarse_cap = kCoarseGroups, bool one_round = false) {
     Plan p{};
     const int64_t groups = batch * ceil_div(D, kWave);          // fine pass: one wave per 64 channels
     const int64_t cgroups = batch * ceil_div(D, coarse_ch);     // coarse pass workgroups per chunk
@@ -104,6 +104,15 @@ inline Plan make_plan(int64_t batch, int64_t D, int64_t T, double prepass_weight
         const double est = rounds / cand + prepass_weight * (double)(cand - 1) / cand * (double)cgroups / coarse_groups;
         if (est < best - 1e-9) { best = est; nc = cand; }
     }
+    // one_round: the most coarse chunks whose workgroups are all resident at
+    // once (a pass that keeps its SIMDs busy at three of its four resident
+    // workgroups per CU loses more to a partly filled second round than it
+    // gains from the extra ones)
+    if (one_round && cgroups <= coarse_groups) {
+        nc = coarse_groups / cgroups;
+        if (nc > 32) nc = 32;
+        if (nc > nf) nc = nf;
+    }
     const int64_t forced_nc = env_int("BDSSM_COARSE_CHUNKS", 0);
     if (forced_nc > 0) nc = forced_nc < nf ? forced_nc : nf;
     int64_t per = ceil_div(nf, nc);
@@ -127,6 +136,17 @@ inline bool supported_states(int64_t N) { return N == 4 || N == 8 || N == 16 || 
 
 // Whether a bidirectional pass runs the register-resident wave kernels.
 inline bool wave_path(int64_t L, int64_t N) { return N == kStates && wave_block(L); }
+
+// The register-resident bidirectional pass with shared operands runs
+// bidir_pair_kernel (two states per lane); BDSSM_BIDIR_KERNEL=wave keeps it on
+// bidir_wave_kernel (four states per lane; tests).  Separate reverse operands
+// always take bidir_wave_kernel<..., 2>.
+inline bool pair_bidir() {
+    const char *v = getenv("BDSSM_BIDIR_KERNEL");
+    return !(v != nullptr && v[0] == 'w');
+}
+// workgroups of bidir_pair_kernel resident at once (four per CU)
+constexpr int64_t kPairGroups = 4 * 256;
 
 // f(std::integral_constant<int, N>) for a supported state count N.
 template <typename F> void with_states(int64_t N, F &&f) {
@@ -183,7 +203,10 @@ inline bool plan_general(int64_t batch, int64_t D, int64_t T, int64_t L, Plan *o
 
 // The plan of the forward entry points for block length L, N states.
 inline bool plan_for(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, Plan *out) {
-    if (wave_path(L, N)) { *out = make_plan(batch, D, T); return true; }
+    if (wave_path(L, N)) {
+        *out = make_plan(batch, D, T, 0.45, kPairChannels, kPairGroups, true);
+        return true;
+    }
     return plan_general(batch, D, T, L, out);
 }
 

@@ -1,5 +1,6 @@
-// launch_bidir.hip -- launchers of the register-resident bidirectional wave kernel
-// (bidir_wave_kernel: block lengths 1, 2, 4, 8, 16 at 16 states).
+// launch_bidir.hip -- launchers of the register-resident bidirectional kernels
+// (bidir_pair_kernel, and bidir_wave_kernel for separate reverse operands:
+// block lengths 1, 2, 4, 8, 16 at 16 states).
 // Compiled once per stream type (BDSSM_TIN = float, or uint16_t for bf16).
 #include "bdssm_launch.hpp"
 
@@ -20,15 +21,41 @@ void launch_bidir_k(dim3 g, const void *x, const void *dt, const void *B, const 
                        f.args<Tin>());
 }
 
+template <typename Tin, int L, bool kInit, int kFuse>
+void launch_pair_k(dim3 g, const void *x, const void *dt, const void *B, const void *C,
+                   const float *A, const float *Dskip, const float *hin, int64_t hin_bs,
+                   int64_t hin_cs, void *y, float *bounds, float *hout, int64_t T, int64_t D,
+                   int64_t Tc, const float *h0_blocks, const Fuse &f, hipStream_t st) {
+    hipLaunchKernelGGL((bidir_pair_kernel<Tin, L, kInit, kFuse>), g, dim3(4 * kWave), 0, st,
+                       (const Tin *)x, (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip,
+                       hin, hin_bs, hin_cs, (Tin *)y, bounds, hout, T, (int)D, Tc, h0_blocks,
+                       f.args<Tin>());
+}
+
 template <typename Tin, int L>
 void launch_bidir_L(const void *x, const void *dt, const void *B, const void *C, const float *A,
                     const float *Dskip, const float *hin, int64_t hin_bs, int64_t hin_cs, void *y,
                     float *bounds, float *hout, int64_t batch, int64_t T, int64_t D, int64_t Tc,
                     int n_chunks, const float *h0_blocks, const Fuse &f, hipStream_t st) {
-    const dim3 g = grid3(D, n_chunks, batch);
     // kernel variant: 0 plain, 1 fused step size / gate, 2 also separate
     // reverse operands
     const int fv = f.dt_r != nullptr ? 2 : f.any() ? 1 : 0;
+    if (fv != 2 && pair_bidir()) {
+        const dim3 gp((unsigned)ceil_div(D, kPairChannels), (unsigned)n_chunks, (unsigned)batch);
+#define BDSSM_PAIR(INIT, FV)                                                                         \
+    launch_pair_k<Tin, L, INIT, FV>(gp, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, T, D, \
+                                    Tc, h0_blocks, f, st)
+        if (h0_blocks != nullptr) {
+            if (fv == 1) BDSSM_PAIR(true, 1);
+            else BDSSM_PAIR(true, 0);
+        } else {
+            if (fv == 1) BDSSM_PAIR(false, 1);
+            else BDSSM_PAIR(false, 0);
+        }
+#undef BDSSM_PAIR
+        return;
+    }
+    const dim3 g = grid3(D, n_chunks, batch);
 #define BDSSM_BIDIR(INIT, FV)                                                                       \
     launch_bidir_k<Tin, L, INIT, FV>(g, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, T, D, \
                                      Tc, h0_blocks, f, st)

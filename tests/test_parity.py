@@ -64,11 +64,19 @@ def test_tiny_fp32_workload(dev):
 
 # ----------------------------------------------------- medium bf16, ragged, chunked
 
+# the bidirectional pass on bidir_pair_kernel (two states per lane, the
+# default) and on bidir_wave_kernel (four states per lane)
+BIDIR = ["pair", "wave"]
+
+
+@pytest.mark.parametrize("bidir", BIDIR)
 @pytest.mark.parametrize("a_kind", ["default", "random", "long"])
-def test_bf16_medium_all_forms(dev, a_kind, monkeypatch):
-    """batch 2, 200 channels (three full 64-lane tiles and a ragged one),
-    2048 tokens; chunk length forced to 128 so every chunked path runs."""
+def test_bf16_medium_all_forms(dev, a_kind, bidir, monkeypatch):
+    """batch 2, 200 channels (three full 64-lane tiles and a ragged one; six
+    full 32-channel tiles and a ragged one), 2048 tokens; chunk length forced
+    to 128 so every chunked path runs."""
     monkeypatch.setenv("BDSSM_CHUNK", "128")
+    monkeypatch.setenv("BDSSM_BIDIR_KERNEL", bidir)
     c = Case(2, 2048, 200, torch.bfloat16, sid=8, a_kind=a_kind)
     L = 16
     tol = TOL[torch.bfloat16]
@@ -108,10 +116,12 @@ def test_fp32_zero_A_and_initial_state(dev, monkeypatch):
     assert rel_err(to_np(yt), r["y"]) < TOL[torch.float32]
 
 
+@pytest.mark.parametrize("bidir", BIDIR)
 @pytest.mark.parametrize("L,T", [(1, 37), (2, 50), (4, 36), (8, 40), (8, 8), (16, 48)])
-def test_block_lengths_and_ragged_groups(dev, L, T):
+def test_block_lengths_and_ragged_groups(dev, L, T, bidir, monkeypatch):
     """Every supported block length, with sequence lengths that leave the last
     16-token group partly filled."""
+    monkeypatch.setenv("BDSSM_BIDIR_KERNEL", bidir)
     c = Case(1, T, 70, torch.float32, sid=10, a_kind="random")
     yt, bnd = m.train_scan(*c.args(), L, want_bounds=True)
     blk = c.segment(T - L, T)
@@ -282,11 +292,14 @@ def test_graph_replay_matches_eager(dev):
 
 # ---------------------------------------------------- two-stream training form
 
+@pytest.mark.parametrize("bidir", BIDIR)
 @pytest.mark.parametrize("L,T,D,dtype", [(16, 512, 130, torch.bfloat16), (8, 200, 70, torch.float32),
-                                         (4, 36, 64, torch.float32), (1, 37, 65, torch.float32)])
-def test_train_blocks_against_oracle(dev, L, T, D, dtype):
+                                         (4, 36, 64, torch.float32), (1, 37, 65, torch.float32),
+                                         (2, 50, 33, torch.bfloat16)])
+def test_train_blocks_against_oracle(dev, L, T, D, dtype, bidir, monkeypatch):
     """Every block from its own (seeded, synthetic) start state."""
     from mamba_selective_scan_04_amd import synth
+    monkeypatch.setenv("BDSSM_BIDIR_KERNEL", bidir)
     c = Case(2, T, D, dtype, sid=18, a_kind="random")
     h0b = synth.normal((2, T // L + 1, D, N), 1000 * 18 + 7).to(dev)
     y = m.train_scan_blocks(*c.args(), L, h0b)

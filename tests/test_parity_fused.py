@@ -61,10 +61,17 @@ def sub(kw, t0, t1):
 MODES = ["softplus_bias", "softplus", "bias"]
 
 
+# the bidirectional pass on bidir_pair_kernel (two states per lane, the
+# default) and on bidir_wave_kernel (four states per lane)
+BIDIR = ["pair", "wave"]
+
+
+@pytest.mark.parametrize("bidir", BIDIR)
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("mode", MODES)
-def test_fused_training_and_baseline_forms(dev, dtype, mode, monkeypatch):
+def test_fused_training_and_baseline_forms(dev, dtype, mode, bidir, monkeypatch):
     monkeypatch.setenv("BDSSM_CHUNK", "64")
+    monkeypatch.setenv("BDSSM_BIDIR_KERNEL", bidir)
     batch, T, D, L = 2, 512, 130, 16
     c, kw = fused_case(batch, T, D, dtype, 51, mode)
     y, bnd = m.train_scan(*c.args(), L, want_bounds=True, **kw)
@@ -84,11 +91,13 @@ def test_fused_training_and_baseline_forms(dev, dtype, mode, monkeypatch):
     assert rel_err(to_np(yfull), yfo) < tol, worst(to_np(yfull), yfo)
 
 
+@pytest.mark.parametrize("bidir", BIDIR)
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("mode", MODES)
-def test_fused_inference_cycle(dev, dtype, mode, monkeypatch):
+def test_fused_inference_cycle(dev, dtype, mode, bidir, monkeypatch):
     """prefill (state only and with y), block step, commit (with and without y)."""
     monkeypatch.setenv("BDSSM_CHUNK", "64")
+    monkeypatch.setenv("BDSSM_BIDIR_KERNEL", bidir)
     batch, D, L, P = 2, 200, 16, 480
     T = P + 2 * L
     c, kw = fused_case(batch, T, D, dtype, 52, mode)
