@@ -770,35 +770,57 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 
 // ------------------------------------------------------------------------
 // Bidirectional kernel, two states per lane (the shared-operand passes: plain
-// and with the step-size / gate fusions): lane = 8 * channel + state pair
-// (states 2g, 2g + 1), 8 channels per wave, 4 waves (32 channels) per
-// workgroup.  A 16-token group's decays then take 32 registers per lane
-// instead of 64, and the kernel runs more waves per SIMD than
+// and with the step-size / gate fusions), for kN = 4, 8, 16 or 32 states:
+// lane = P * channel + state pair (states 2g, 2g + 1), P = kN / 2 lanes per
+// channel, CW = 64 / P channels per wave, 4 waves (4 CW channels) per
+// workgroup.  A 16-token group's decays then take 32 registers per lane at
+// any state count, and the kernel runs more waves per SIMD than
 // bidir_wave_kernel, whose four-state lanes wait on latency at two.
 // Per group, staged as in bwd_pair_kernel (the x / dt (/ z) rows of the
-// wave's 8 channels DMA'd into the wave's LDS slice, the group's B / C rows
-// shared by the workgroup, each wave loading a quarter; one group ahead,
-// widened in place by the lane that loaded them; one barrier per group):
+// wave's CW channels DMA'd into the wave's LDS slice, the group's B / C rows
+// shared by the workgroup, their loads spread over the waves; one group
+// ahead, widened in place by the lane that loaded them; one barrier per
+// group):
 //   forward, left to right: a = exp2(dt A'), hf = a hf + dt x B, the lane's
 //     output partial C . hf over its two states; the decays and dt x of the
 //     group stay in registers;
 //   reverse, right to left, reset where a block ends: hr = a hr + dt x B,
 //     partial += C . hr;
-//   output: the 16 tokens' partials are summed over the channel's 8 lanes by
-//     a reduce-scatter (DPP half-row mirror, then the two quad exchanges),
-//     after which lane g holds tokens 2g and 2g + 1 of its channel; + Dskip x,
-//     times silu(z) with the gate, stored through buffer stores whose
-//     out-of-range offsets drop dead channels and tokens past the chunk.
+//   output: the 16 tokens' partials are summed over the channel's P lanes by
+//     a reduce-scatter over the lane bits of g, from the top bit down (row
+//     rotation by 8 for bit 3, half-row mirror for bit 2, the quad exchanges
+//     for bits 1 and 0), after which lane g holds tokens 16 g / P .. of its
+//     channel; + Dskip x, times silu(z) with the gate, stored through buffer
+//     stores whose out-of-range offsets drop dead channels and tokens past the
+//     chunk.
 // dt of tokens past the chunk end and of channels past D reads zero (an
 // out-of-range DMA offset; after the step-size transform it is set to zero
 // again): such tokens decay by 1 and inject nothing.
-// Arguments as in bidir_wave_kernel; separate reverse operands run
-// bidir_wave_kernel<..., 2>.
-// grid = (ceil(D/32), chunks, batch), block = 256.
-constexpr int kPairChannels = 32;     // channels per workgroup of the two-state kernels
+// Arguments as in bidir_wave_kernel, with states [.., kN]; separate reverse
+// operands run bidir_wave_kernel<..., 2> (16 states) or block_bidir_kernel.
+// grid = (ceil(D / (4 CW)), chunks, batch), block = 256.
+template <int kN> constexpr int pair_channels() { return 4 * (2 * kWave / kN); }
+constexpr int kPairChannels = pair_channels<kStates>();   // 32: the 16-state two-state kernels
 
-template <typename Tin, int L, bool kBlockInit, int kFuse = 0>
-__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 1 ? 2 : 4))) void bidir_pair_kernel(
+// One step of the output reduce-scatter: lanes whose bit kBit of g is set
+// keep the upper half of the values, the others the lower half, each adding
+// its partner's (the lane that differs in bit kBit; below bit 3 a DPP
+// pattern that flips it within the same aligned group).
+template <int kBit, int kV>
+__device__ __forceinline__ void pair_scatter(const float (&in)[2 * kV], float (&out)[kV], bool hi) {
+#pragma unroll
+    for (int k = 0; k < kV; ++k) {
+        const float keep = hi ? in[k + kV] : in[k];
+        const float send = hi ? in[k] : in[k + kV];
+        if constexpr (kBit == 3) out[k] = keep + dpp_perm<kDppRor8>(send);
+        else if constexpr (kBit == 2) out[k] = keep + dpp_perm<kDppHalfMirror>(send);
+        else if constexpr (kBit == 1) out[k] = keep + dpp_perm<kDppXor2>(send);
+        else out[k] = keep + dpp_perm<kDppXor1>(send);
+    }
+}
+
+template <typename Tin, int kN, int L, bool kBlockInit, int kFuse = 0>
+__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 1 ? 2 : kN == 4 ? 3 : 4))) void bidir_pair_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const Tin *__restrict__ Cm, const float *__restrict__ A, const float *__restrict__ Dskip,
     const float *hin, int64_t hin_bs, int64_t hin_cs,
@@ -807,22 +829,28 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
 {
     static_assert(kFuse == 0 || kFuse == 1, "separate reverse operands run bidir_wave_kernel");
     static_assert(kGroup % L == 0, "block length must divide the token group");
-    constexpr int CW = 8;                     // channels per wave
+    static_assert(kN == 4 || kN == 8 || kN == 16 || kN == 32, "state counts 4, 8, 16, 32");
+    constexpr int P = kN / 2;                 // lanes per channel
+    constexpr int CW = kWave / P;             // channels per wave
     constexpr int ES = sizeof(Tin);
     constexpr int G = kGroup;                 // 16 tokens per group
     constexpr int NS = kFuse ? 3 : 2;         // row streams: x, dt (, z)
+    constexpr int XL = G * CW / kWave;        // x / dt loads per group and stream (P tokens each)
+    constexpr int BL = G * kN / kWave;        // B / C loads per group and stream (64 / kN tokens each)
+    constexpr int BT = kWave / kN;            // tokens per B / C load
+    constexpr int NV = G / P;                 // output tokens per lane
     // double buffers as distinct arrays (the loads in flight into one are told
     // apart from the reads of the other): [wave][stream][token][channel] and
     // [B, C][token][state]
     __shared__ __attribute__((aligned(16))) uint32_t xdA[4][NS][G][CW], xdB[4][NS][G][CW];
-    __shared__ __attribute__((aligned(16))) uint32_t bcA[2][G][kStates], bcB[2][G][kStates];
+    __shared__ __attribute__((aligned(16))) uint32_t bcA[2][G][kN], bcB[2][G][kN];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform(threadIdx.x >> 6);
-    const int cl = lane >> 3;                 // channel within the wave
-    const int g = lane & 7;                   // state pair
+    const int cl = lane / P;                  // channel within the wave
+    const int g = lane % P;                   // state pair
     const int s0 = 2 * g;
-    const int d_w0 = blockIdx.x * kPairChannels + w * CW;
+    const int d_w0 = blockIdx.x * (4 * CW) + w * CW;
     const int d_raw = d_w0 + cl;
     const bool live = d_raw < D;
     const int d = live ? d_raw : D - 1;
@@ -835,11 +863,11 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
 
     float a2[2], hf[2] = {0.f, 0.f};
     {
-        const float2 av = *reinterpret_cast<const float2 *>(A + (int64_t)d * kStates + s0);
+        const float2 av = *reinterpret_cast<const float2 *>(A + (int64_t)d * kN + s0);
         a2[0] = av.x * kLog2e; a2[1] = av.y * kLog2e;
         if (hin != nullptr) {
             const float2 hv = *reinterpret_cast<const float2 *>(
-                hin + (int64_t)b * hin_bs + (int64_t)c * hin_cs + (int64_t)d * kStates + s0);
+                hin + (int64_t)b * hin_bs + (int64_t)c * hin_cs + (int64_t)d * kN + s0);
             hf[0] = hv.x; hf[1] = hv.y;
         }
     }
@@ -848,42 +876,48 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
         *reinterpret_cast<float2 *>(dst + s0) = make_float2(hf[0], hf[1]);
     };
     if (bounds != nullptr && c == 0 && live)
-        store_state(bounds + ((int64_t)b * (nbl + 1) * D + d) * kStates);
+        store_state(bounds + ((int64_t)b * (nbl + 1) * D + d) * kN);
 
     const int64_t first = (int64_t)b * T + t_begin;
     const Rows<Tin> xs(x + first * D, len, D, 0);
     const Rows<Tin> ds(dt + first * D, len, D, 0);
     const Rows<Tin> ys(y + first * D, len, D, 0);
     __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(const_cast<Tin *>(Bm + first * kStates)), 0, uniform(len * kStates * ES), kRawBufferWord3);
+        uniform_ptr(const_cast<Tin *>(Bm + first * kN)), 0, uniform(len * kN * ES), kRawBufferWord3);
     __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(const_cast<Tin *>(Cm + first * kStates)), 0, uniform(len * kStates * ES), kRawBufferWord3);
-    // DMA lanes: x / dt (/ z) load j covers tokens 8j .. 8j+7 (lane: token
-    // l / 8, channel l % 8); B / C: wave w loads tokens 4w .. 4w+3 (lane:
-    // token l / 16, state l % 16)
-    const int ld_tok = lane >> 3, ld_col = lane & 7;
+        uniform_ptr(const_cast<Tin *>(Cm + first * kN)), 0, uniform(len * kN * ES), kRawBufferWord3);
+    // DMA lanes: x / dt (/ z) load j covers tokens P j .. P j + P - 1 (lane:
+    // token l / CW, channel l % CW); B / C load j (taken by wave j % 4) covers
+    // tokens BT j .. (lane: token l / kN, state l % kN)
+    const int ld_tok = lane / CW, ld_col = lane % CW;
     const bool ld_live = d_w0 + ld_col < D;
     const int ld_ch = ld_live ? d_w0 + ld_col : D - 1;
-    const int bc_tok = 4 * w + (lane >> 4), bc_col = lane & 15;
+    const int bc_tok = lane / kN, bc_col = lane % kN;
     const bool gate = kFuse && fz.z != nullptr;
     const float ld_bias = (kFuse && fz.dt_bias != nullptr) ? fz.dt_bias[ld_ch] : 0.f;
     const Rows<Tin> zs((gate ? fz.z : x) + first * D, len, D, 0);
 
     auto issue = [&](auto &xd, auto &bc, int k0) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int kr = k0 + 8 * j + ld_tok;
+        for (int j = 0; j < XL; ++j) {
+            const int kr = k0 + P * j + ld_tok;
             const int k = kr < len ? kr : len - 1;
             const int zoff = (kr < len && ld_live) ? ld_ch * ES + k * ds.pitch : kOutOfRange;
-            load_to_lds<ES>(xs.rsrc, &xd[w][0][8 * j][0], ld_ch * ES + k * xs.pitch, 0);
-            load_to_lds<ES>(ds.rsrc, &xd[w][1][8 * j][0], zoff, 0);
+            load_to_lds<ES>(xs.rsrc, &xd[w][0][P * j][0], ld_ch * ES + k * xs.pitch, 0);
+            load_to_lds<ES>(ds.rsrc, &xd[w][1][P * j][0], zoff, 0);
             if constexpr (kFuse) {
-                if (gate) load_to_lds<ES>(zs.rsrc, &xd[w][2][8 * j][0], zoff, 0);
+                if (gate) load_to_lds<ES>(zs.rsrc, &xd[w][2][P * j][0], zoff, 0);
             }
         }
-        const int kb = (k0 + bc_tok < len) ? k0 + bc_tok : len - 1;
-        load_to_lds<ES>(brs, &bc[0][4 * w][0], (kb * kStates + bc_col) * ES, 0);
-        load_to_lds<ES>(crs, &bc[1][4 * w][0], (kb * kStates + bc_col) * ES, 0);
+#pragma unroll
+        for (int j = 0; j < BL; j += 4) {
+            if (j + w < BL) {
+                const int kt = k0 + BT * (j + w) + bc_tok;
+                const int kb = kt < len ? kt : len - 1;
+                load_to_lds<ES>(brs, &bc[0][BT * (j + w)][0], (kb * kN + bc_col) * ES, 0);
+                load_to_lds<ES>(crs, &bc[1][BT * (j + w)][0], (kb * kN + bc_col) * ES, 0);
+            }
+        }
     };
     // after this wave's own loads have landed, widen the dwords this lane
     // loaded to fp32 in place; with the fusions, form the step size (zero
@@ -894,28 +928,33 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
 #pragma unroll
             for (int s = 0; s < NS; ++s)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
+                for (int j = 0; j < XL; ++j) {
                     if (s == 2 && !gate) continue;
-                    uint32_t &v = (&xd[w][s][8 * j][0])[lane];
+                    uint32_t &v = (&xd[w][s][P * j][0])[lane];
                     v <<= 16;
                 }
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                uint32_t &v = (&bc[s][4 * w][0])[lane];
-                v <<= 16;
+            for (int j = 0; j < BL; j += 4) {
+                if (j + w < BL) {
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        uint32_t &v = (&bc[s][BT * (j + w)][0])[lane];
+                        v <<= 16;
+                    }
+                }
             }
         }
         if constexpr (kFuse) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                uint32_t &dv = (&xd[w][1][8 * j][0])[lane];
+            for (int j = 0; j < XL; ++j) {
+                uint32_t &dv = (&xd[w][1][P * j][0])[lane];
                 const float raw = __uint_as_float(dv);
                 float dl = raw;
                 if (fz.dt_mode == kDtSoftplus) dl = step_size<kDtSoftplus>(raw, ld_bias);
                 else if (fz.dt_mode == kDtBias) dl = step_size<kDtBias>(raw, ld_bias);
-                dv = __float_as_uint(k0 + 8 * j + ld_tok < len ? dl : 0.f);
+                dv = __float_as_uint(k0 + P * j + ld_tok < len ? dl : 0.f);
                 if (gate) {
-                    uint32_t &zv = (&xd[w][2][8 * j][0])[lane];
+                    uint32_t &zv = (&xd[w][2][P * j][0])[lane];
                     zv = __float_as_uint(silu_f(__uint_as_float(zv)));
                 }
             }
@@ -940,11 +979,10 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
                 const int i = q * L < nv ? q * L : 0;
                 const int64_t blk = (t_begin + k0n + i) / L;
                 hbn[q] = *reinterpret_cast<const float2 *>(
-                    h0_blocks + (((int64_t)b * (nbl + 1) + blk) * D + d) * kStates + s0);
+                    h0_blocks + (((int64_t)b * (nbl + 1) + blk) * D + d) * kN + s0);
             }
         }
     };
-    const bool hb2 = (g & 4) != 0, hb1 = (g & 2) != 0, hb0 = (g & 1) != 0;
 
     auto group = [&](auto &xd, auto &bc, int k0, const float2 *hb) {
         const int nvalid = (len - k0 < G) ? len - k0 : G;   // uniform
@@ -966,7 +1004,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
             ya[i] = __builtin_fmaf(cv.y, hf[1], cv.x * hf[0]);
             if ((i + 1) % L == 0 && bounds != nullptr && i < nvalid && live) {
                 const int64_t kb = (t_begin + k0 + i + 1) / L;
-                store_state(bounds + (((int64_t)b * (nbl + 1) + kb) * D + d) * kStates);
+                store_state(bounds + (((int64_t)b * (nbl + 1) + kb) * D + d) * kN);
             }
             if ((i & 3) == 3) {
                 // 4-token batches: the batch's arithmetic completes before the
@@ -989,30 +1027,31 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
                              "+v"(ya[i + 3]) :: "memory");
             }
         }
-        // the channel's sum over its 8 lanes: lane g keeps tokens 8 (g / 4)
-        // .. + 7 after the mirror exchange (partner 7 - g), 4 of them after
-        // the exchange with g ^ 2, tokens 2g and 2g + 1 after the one with
-        // g ^ 1
-        float r8[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float keep = hb2 ? ya[k + 8] : ya[k];
-            const float send = hb2 ? ya[k] : ya[k + 8];
-            r8[k] = keep + dpp_perm<kDppHalfMirror>(send);
+        // the channel's sum over its P lanes, from the top bit of g down: lane
+        // g ends with tokens NV g .. NV g + NV - 1
+        float r[NV];
+        if constexpr (P == 16) {
+            float r8[8], r4[4], r2[2];
+            pair_scatter<3, 8>(ya, r8, (g & 8) != 0);
+            pair_scatter<2, 4>(r8, r4, (g & 4) != 0);
+            pair_scatter<1, 2>(r4, r2, (g & 2) != 0);
+            pair_scatter<0, 1>(r2, r, (g & 1) != 0);
+        } else if constexpr (P == 8) {
+            float r8[8], r4[4];
+            pair_scatter<2, 8>(ya, r8, (g & 4) != 0);
+            pair_scatter<1, 4>(r8, r4, (g & 2) != 0);
+            pair_scatter<0, 2>(r4, r, (g & 1) != 0);
+        } else if constexpr (P == 4) {
+            float r8[8];
+            pair_scatter<1, 8>(ya, r8, (g & 2) != 0);
+            pair_scatter<0, 4>(r8, r, (g & 1) != 0);
+        } else {
+            pair_scatter<0, 8>(ya, r, (g & 1) != 0);
         }
-        float r4[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float keep = hb1 ? r8[k + 4] : r8[k];
-            const float send = hb1 ? r8[k] : r8[k + 4];
-            r4[k] = keep + dpp_perm<kDppXor2>(send);
-        }
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const float keep = hb0 ? r4[k + 2] : r4[k];
-            const float send = hb0 ? r4[k] : r4[k + 2];
-            const int t = 2 * g + k;
-            float tot = __builtin_fmaf(dsk, f32(xd[w][0][t][cl]), keep + dpp_perm<kDppXor1>(send));
+        for (int k = 0; k < NV; ++k) {
+            const int t = NV * g + k;
+            float tot = __builtin_fmaf(dsk, f32(xd[w][0][t][cl]), r[k]);
             if constexpr (kFuse) {
                 if (gate) tot *= f32(xd[w][2][t][cl]);
             }
@@ -1046,7 +1085,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
         step(xdA, bcA, xdB, bcB, k0);
         if (k0 + G < len) step(xdB, bcB, xdA, bcA, k0 + G);
     }
-    if (hout != nullptr && t_end == T && live) store_state(hout + ((int64_t)b * D + d) * kStates);
+    if (hout != nullptr && t_end == T && live) store_state(hout + ((int64_t)b * D + d) * kN);
 }
 
 // ------------------------------------------------------------------------

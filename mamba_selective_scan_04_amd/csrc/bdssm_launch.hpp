@@ -147,6 +147,11 @@ inline bool pair_bidir() {
 }
 // workgroups of bidir_pair_kernel resident at once (four per CU)
 constexpr int64_t kPairGroups = 4 * 256;
+// Whether a bidirectional pass with shared operands can run bidir_pair_kernel
+// (block lengths dividing the 16-token group, any supported state count), and
+// its channels per workgroup (4 waves x 64 lanes / (N / 2) lanes per channel).
+inline bool pair_path(int64_t L, int64_t N) { return wave_block(L) && supported_states(N); }
+inline int64_t pair_channels_of(int64_t N) { return 8 * kWave / N; }
 
 // f(std::integral_constant<int, N>) for a supported state count N.
 template <typename F> void with_states(int64_t N, F &&f) {
@@ -165,7 +170,7 @@ template <typename F> void with_states(int64_t N, F &&f) {
 // blocks (one wave per 64 channels there, so four times the chunks).
 inline bool blocks_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, int64_t *tc_out,
                  int64_t *nc_out, int64_t coarse_ch = kWave, int64_t coarse_cap = kCoarseGroups) {
-    const bool wave = wave_path(L, N);
+    const bool wave = pair_path(L, N);
     const int64_t unit = wave ? kGroup : L;
     const int64_t groups = batch * ceil_div(D, coarse_ch);
     const int64_t nunits = ceil_div(T, unit);
@@ -203,8 +208,8 @@ inline bool plan_general(int64_t batch, int64_t D, int64_t T, int64_t L, Plan *o
 
 // The plan of the forward entry points for block length L, N states.
 inline bool plan_for(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, Plan *out) {
-    if (wave_path(L, N)) {
-        *out = make_plan(batch, D, T, 0.45, kPairChannels, kPairGroups, true);
+    if (pair_path(L, N)) {
+        *out = make_plan(batch, D, T, 0.45, pair_channels_of(N), kPairGroups, true);
         return true;
     }
     return plan_general(batch, D, T, L, out);

@@ -1,6 +1,6 @@
 // launch_bidir.hip -- launchers of the register-resident bidirectional kernels
-// (bidir_pair_kernel, and bidir_wave_kernel for separate reverse operands:
-// block lengths 1, 2, 4, 8, 16 at 16 states).
+// (bidir_pair_kernel: block lengths 1, 2, 4, 8, 16 at 4, 8, 16 or 32 states;
+// bidir_wave_kernel for separate reverse operands at 16 states).
 // Compiled once per stream type (BDSSM_TIN = float, or uint16_t for bf16).
 #include "bdssm_launch.hpp"
 
@@ -21,41 +21,62 @@ void launch_bidir_k(dim3 g, const void *x, const void *dt, const void *B, const 
                        f.args<Tin>());
 }
 
-template <typename Tin, int L, bool kInit, int kFuse>
+template <typename Tin, int kN, int L, bool kInit, int kFuse>
 void launch_pair_k(dim3 g, const void *x, const void *dt, const void *B, const void *C,
                    const float *A, const float *Dskip, const float *hin, int64_t hin_bs,
                    int64_t hin_cs, void *y, float *bounds, float *hout, int64_t T, int64_t D,
                    int64_t Tc, const float *h0_blocks, const Fuse &f, hipStream_t st) {
-    hipLaunchKernelGGL((bidir_pair_kernel<Tin, L, kInit, kFuse>), g, dim3(4 * kWave), 0, st,
+    hipLaunchKernelGGL((bidir_pair_kernel<Tin, kN, L, kInit, kFuse>), g, dim3(4 * kWave), 0, st,
                        (const Tin *)x, (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip,
                        hin, hin_bs, hin_cs, (Tin *)y, bounds, hout, T, (int)D, Tc, h0_blocks,
                        f.args<Tin>());
 }
 
+// bidir_pair_kernel at kN states and block length L (shared operands)
+template <typename Tin, int kN, int L>
+void launch_pair_L(const void *x, const void *dt, const void *B, const void *C, const float *A,
+                   const float *Dskip, const float *hin, int64_t hin_bs, int64_t hin_cs, void *y,
+                   float *bounds, float *hout, int64_t batch, int64_t T, int64_t D, int64_t Tc,
+                   int n_chunks, const float *h0_blocks, const Fuse &f, hipStream_t st) {
+    const dim3 g((unsigned)ceil_div(D, pair_channels<kN>()), (unsigned)n_chunks, (unsigned)batch);
+    const bool fused = f.any();
+#define BDSSM_PAIR(INIT, FV)                                                                         \
+    launch_pair_k<Tin, kN, L, INIT, FV>(g, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, T, D, \
+                                        Tc, h0_blocks, f, st)
+    if (h0_blocks != nullptr) {
+        if (fused) BDSSM_PAIR(true, 1);
+        else BDSSM_PAIR(true, 0);
+    } else {
+        if (fused) BDSSM_PAIR(false, 1);
+        else BDSSM_PAIR(false, 0);
+    }
+#undef BDSSM_PAIR
+}
+
+template <typename Tin, int kN>
+void launch_pair(int64_t L, const void *x, const void *dt, const void *B, const void *C, const float *A,
+                 const float *Dskip, const float *hin, int64_t hin_bs, int64_t hin_cs, void *y,
+                 float *bounds, float *hout, int64_t batch, int64_t T, int64_t D, int64_t Tc,
+                 int n_chunks, const float *h0_blocks, const Fuse &f, hipStream_t st) {
+    switch (L) {
+    case 1: launch_pair_L<Tin, kN, 1>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
+    case 2: launch_pair_L<Tin, kN, 2>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
+    case 4: launch_pair_L<Tin, kN, 4>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
+    case 8: launch_pair_L<Tin, kN, 8>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
+    default: launch_pair_L<Tin, kN, 16>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
+    }
+}
+
+// bidir_wave_kernel (16 states): separate reverse operands, or forced
 template <typename Tin, int L>
 void launch_bidir_L(const void *x, const void *dt, const void *B, const void *C, const float *A,
                     const float *Dskip, const float *hin, int64_t hin_bs, int64_t hin_cs, void *y,
                     float *bounds, float *hout, int64_t batch, int64_t T, int64_t D, int64_t Tc,
                     int n_chunks, const float *h0_blocks, const Fuse &f, hipStream_t st) {
+    const dim3 g = grid3(D, n_chunks, batch);
     // kernel variant: 0 plain, 1 fused step size / gate, 2 also separate
     // reverse operands
     const int fv = f.dt_r != nullptr ? 2 : f.any() ? 1 : 0;
-    if (fv != 2 && pair_bidir()) {
-        const dim3 gp((unsigned)ceil_div(D, kPairChannels), (unsigned)n_chunks, (unsigned)batch);
-#define BDSSM_PAIR(INIT, FV)                                                                         \
-    launch_pair_k<Tin, L, INIT, FV>(gp, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, T, D, \
-                                    Tc, h0_blocks, f, st)
-        if (h0_blocks != nullptr) {
-            if (fv == 1) BDSSM_PAIR(true, 1);
-            else BDSSM_PAIR(true, 0);
-        } else {
-            if (fv == 1) BDSSM_PAIR(false, 1);
-            else BDSSM_PAIR(false, 0);
-        }
-#undef BDSSM_PAIR
-        return;
-    }
-    const dim3 g = grid3(D, n_chunks, batch);
 #define BDSSM_BIDIR(INIT, FV)                                                                       \
     launch_bidir_k<Tin, L, INIT, FV>(g, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, T, D, \
                                      Tc, h0_blocks, f, st)
@@ -71,14 +92,24 @@ void launch_bidir_L(const void *x, const void *dt, const void *B, const void *C,
 #undef BDSSM_BIDIR
 }
 
-// The bidirectional pass: the wave kernels for N = 16 and L | 16, else
-// block_bidir_kernel (Tc then a multiple of L).
+// The bidirectional pass: for L | 16, bidir_pair_kernel at any supported
+// state count (shared operands), bidir_wave_kernel for separate reverse
+// operands at 16 states; everything else on block_bidir_kernel (Tc then a
+// multiple of L).
 template <typename Tin>
 void launch_bidir(int64_t L, const void *x, const void *dt, const void *B, const void *C,
                   const float *A, const float *Dskip, const float *hin, int64_t hin_bs,
                   int64_t hin_cs, void *y, float *bounds, float *hout, int64_t batch, int64_t T,
                   int64_t D, int64_t N, int64_t Tc, int n_chunks, hipStream_t st,
                   const float *h0_blocks, const Fuse &f) {
+    const bool sep = f.dt_r != nullptr;
+    if (pair_path(L, N) && !sep && pair_bidir()) {
+        with_states(N, [&](auto n) {
+            launch_pair<Tin, decltype(n)::value>(L, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout,
+                                                 batch, T, D, Tc, n_chunks, h0_blocks, f, st);
+        });
+        return;
+    }
     if (!wave_path(L, N)) {
         launch_block_bidir_any<Tin>(N, L, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout,
                                     batch, T, D, Tc, n_chunks, h0_blocks, f, st);
