@@ -837,7 +837,7 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
         // adjoint aggregates of the fine chunks right of the first coarse chunk,
         // then the adjoint entering each fine chunk from its right end
         const int c_first = p.per_coarse, n_launch = p.n_fine - p.per_coarse;
-        if (general || lng) {
+        if (general || lng || N != kStates) {
             if (bf)
                 launch_adjoint_general<uint16_t>(N, dt, dy, C, A, d_bounds, w.agg_q, w.agg_s, batch, T, D, L,
                                                  p.fine_len, p.n_fine, c_first, n_launch, a.dt_mode, a.dt_bias,
@@ -865,13 +865,13 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
     if (bf) {
         if (general) launch_bwd_general<uint16_t, false>(N, a, batch, T, D, L, Tc, nc, st);
         else if (lng) launch_bwd_long<uint16_t, false>(a, w.gstate, batch, T, D, L, Tc, nc, st);
-        else launch_bwd<uint16_t, false>(L, a, batch, T, D, Tc, nc, st);
+        else launch_bwd<uint16_t, false>(L, N, a, batch, T, D, Tc, nc, st);
         launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias,
                                     a.sep ? grads : nullptr);
     } else {
         if (general) launch_bwd_general<float, false>(N, a, batch, T, D, L, Tc, nc, st);
         else if (lng) launch_bwd_long<float, false>(a, w.gstate, batch, T, D, L, Tc, nc, st);
-        else launch_bwd<float, false>(L, a, batch, T, D, Tc, nc, st);
+        else launch_bwd<float, false>(L, N, a, batch, T, D, Tc, nc, st);
         launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias,
                                  a.sep ? grads : nullptr);
     }
@@ -936,13 +936,13 @@ int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void 
     if (shape->dtype == BDSSM_BF16) {
         if (general) launch_bwd_general<uint16_t, true>(N, a, batch, T, D, L, tc, (int)nc, st);
         else if (lng) launch_bwd_long<uint16_t, true>(a, w.gstate, batch, T, D, L, tc, (int)nc, st);
-        else launch_bwd<uint16_t, true>(L, a, batch, T, D, tc, (int)nc, st);
+        else launch_bwd<uint16_t, true>(L, N, a, batch, T, D, tc, (int)nc, st);
         launch_bwd_reduce<uint16_t>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias,
                                     a.sep ? grads : nullptr);
     } else {
         if (general) launch_bwd_general<float, true>(N, a, batch, T, D, L, tc, (int)nc, st);
         else if (lng) launch_bwd_long<float, true>(a, w.gstate, batch, T, D, L, tc, (int)nc, st);
-        else launch_bwd<float, true>(L, a, batch, T, D, tc, (int)nc, st);
+        else launch_bwd<float, true>(L, N, a, batch, T, D, tc, (int)nc, st);
         launch_bwd_reduce<float>(w, dB, dC, dA, dDskip, batch, T, D, L, N, nc, st, a.fused, d_bias,
                                  a.sep ? grads : nullptr);
     }

@@ -528,33 +528,35 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 
 // ------------------------------------------------------------------------
 // Backward of the bidirectional pass over one coarse chunk, two states per
-// lane: lane = 8 * channel + state pair (states 2g, 2g+1), 8 channels per
-// wave, 4 waves per workgroup (32 channels).  With two states per lane the
-// decays, the forward states before each token and the reverse adjoints of a
-// whole 16-token group fit in 96 VGPRs, so the forward quantities are formed
-// once per token (no recomputation):
+// lane, for kN = 4, 8, 16 or 32 states: lane = P * channel + state pair
+// (states 2g, 2g+1), P = kN / 2 lanes per channel, CW = 64 / P channels per
+// wave, 4 waves per workgroup (4 CW channels: 32 at 16 states).  With two
+// states per lane the forward states before each token and the reverse
+// adjoints of a whole 16-token group fit in 64 VGPRs at any state count, so
+// the forward quantities are formed once per token (no recomputation):
 //   pass A (left to right over the group): hf from the group's block start
-//     state, gr reset at block starts; keeps a_t, hf_{t-1}, gr_t per token;
+//     state, gr reset at block starts; keeps hf_{t-1}, gr_t per token;
 //   pass B (right to left): hr (reset at block ends), gf (q carried across
 //     groups; + dbounds or reset at block ends), every gradient term.
 // Reductions stay in registers (VALU lane exchanges, no LDS round trip):
-//   * dB / dC: per token the lane's 4 values are summed over the wave's 8
-//     channels by two 32-lane folds (permlane32 swaps), one 16-lane fold
-//     (permlane16 swap) and a DPP row rotation over a token pair, which leave
-//     lane l with value kind l / 16 of state pair l % 8 of one of the two
-//     tokens; the wave's sums meet the other waves' in red (one barrier per
-//     group) and are added in a fixed order into
-//     part_bc [batch, ceil(D/32), T, 32], reduced over channel blocks by
-//     bc_reduce_kernel;
+//   * dB / dC: per token the lane's 4 values are summed over the wave's CW
+//     channels by two 32-lane folds (permlane32 swaps) and one 16-lane fold
+//     (permlane16 swap), which leave lane l with dB or dC (bit 5) of state
+//     2g + (bit 4); the channel bits below bit 4 (none at 32 states) are
+//     summed by a DPP row rotation over a token pair (16 states) or by row
+//     rotations and quad exchanges with one lane of each duplicate storing;
+//     the wave's sums meet the other waves' in red (one barrier per group) and
+//     are added in a fixed order into part_bc [batch, ceil(D/(4 CW)), T, 2 kN],
+//     reduced over channel blocks by bc_reduce_kernel;
 //   * dt and x: per token the lane's two partial sums are summed over the
-//     channel's 8 state pairs by a DPP half-row mirror exchange (dt kept in
-//     lanes g < 4, x in g >= 4) and two quad exchanges; each lane keeps one
-//     token of every 4, so that after 4 tokens the 64 lanes hold (token, dt
-//     or x, channel) and store them together.
-// Staging: x / dt / dy rows of the wave's 8 channels and the group's B / C
-// rows (shared by the workgroup, each wave loads a quarter) are DMA'd into
-// LDS one group ahead and widened to fp32 in place by the lane that loaded
-// them.  Arguments and the other partial outputs as in bwd_wave_kernel.
+//     channel's P state pairs by an exchange over the top bit of g (dt kept
+//     in lanes g < P/2, x in the others) and exchanges over the lower bits;
+//     each lane keeps one token of every P/2, so that after P/2 tokens the
+//     64 lanes hold (token, dt or x, channel) and store them together.
+// Staging: x / dt / dy rows of the wave's CW channels and the group's B / C
+// rows (shared by the workgroup, their loads spread over the waves) are DMA'd
+// into LDS one group ahead and widened to fp32 in place by the lane that
+// loaded them.  Arguments and the other partial outputs as in bwd_wave_kernel.
 //
 // L = 0 (long blocks: Lr tokens, a multiple of 16 above 16): a block spans
 // several groups.  Groups are still walked right to left, so hr and the
@@ -568,7 +570,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 // as they are widened; with the gate z (staged as a fourth row stream), dy
 // becomes dy silu(z), the gradient of the ungated output, and the z row holds
 // dy silu'(z).  Pass B also forms y_pre = sum_n C (hf + hr) + Dskip x of each
-// token (summed over the channel's 8 lanes by DPP) and parks it in the
+// token (summed over the channel's P lanes by DPP) and parks it in the
 // token's x slot, and the flush parks the dt partial total in the dy slot
 // (pass B no longer reads either).  After pass B, when the group's state
 // arrays are dead, an epilogue turns the parked values into the dt stream's
@@ -577,7 +579,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 // and dz = dy silu'(z) y_pre, with masked buffer stores; the dt-stream
 // gradient's sums over the chunk's tokens go to part_bias [batch, chunks, D]
 // for the gradient of dt_bias.  (Done inside pass B, the same work spills.)
-// grid = (ceil(D/32), chunks, batch), block = 256.
+// grid = (ceil(D/(4 CW)), chunks, batch), block = 256.
 
 template <typename Tin> struct BwdFuse {
     const float *dt_bias;   // [D] or null
@@ -600,8 +602,8 @@ __device__ __forceinline__ float sigmoid_from_softplus(float sp) {
     return 1.f - fast_exp2(-sp * kLog2e);
 }
 
-template <typename Tin, int L, bool kBlockInit, bool kFuse = false>
-__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) void bwd_pair_kernel(
+template <typename Tin, int kN, int L, bool kBlockInit, bool kFuse = false>
+__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(kN == 4 ? 2 : 3))) void bwd_pair_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const Tin *__restrict__ Cm, const Tin *__restrict__ dy, const float *__restrict__ A,
     const float *__restrict__ Dskip, const float *__restrict__ h_start, const float *qin,
@@ -610,14 +612,22 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
     float *__restrict__ part_d, float *__restrict__ dh0, int64_t T, int D, int64_t Tc,
     BwdFuse<Tin> fz, const float *__restrict__ gstate, int Lr)
 {
-    constexpr int CW = 8;                     // channels per wave
+    static_assert(kN == 4 || kN == 8 || kN == 16 || kN == 32, "state counts 4, 8, 16, 32");
+    constexpr int P = kN / 2;                 // lanes per channel
+    constexpr int CW = kWave / P;             // channels per wave
     constexpr int ES = sizeof(Tin);
     constexpr int G = kGroup;                 // 16 tokens per group
+    constexpr int XL = G * CW / kWave;        // x / dt / dy loads per group and stream (P tokens each)
+    constexpr int BL = G * kN / kWave;        // B / C loads per group and stream (BT tokens each)
+    constexpr int BT = kWave / kN;
+    constexpr int TK = P / 2;                 // tokens per dt / x flush
+    constexpr int EV = CW / 4;                // the fused epilogue's values per lane
     constexpr int NSB = kFuse ? 4 : 3;        // row streams: x, dt, dy (, z)
     // L = 0: blocks of Lr tokens, a multiple of 16 above 16, spanning several
     // groups; gstate holds the forward state and the reverse adjoint's carry
     // at every group start ([batch, T/16, 2, D, 16], group_state_kernel)
     constexpr bool kLong = L == 0;
+    static_assert(!kLong || kN == kStates, "long blocks at 16 states");
     constexpr int LB = kLong ? G : L;         // block length as seen inside one group
     static_assert(kLong || G % L == 0, "block length must divide the token group");
     // Double buffers as distinct arrays (A / B), so that the compiler can tell
@@ -625,15 +635,15 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
     // does not wait for them: [wave][stream x, dt, dy (, z)][token][channel]
     // and [B, C][token][state]
     __shared__ __attribute__((aligned(16))) uint32_t xdA[4][NSB][G][CW], xdB[4][NSB][G][CW];
-    __shared__ __attribute__((aligned(16))) uint32_t bcA[2][G][kStates], bcB[2][G][kStates];
-    __shared__ __attribute__((aligned(16))) float redA[4][G * 2 * kStates], redB[4][G * 2 * kStates];
+    __shared__ __attribute__((aligned(16))) uint32_t bcA[2][G][kN], bcB[2][G][kN];
+    __shared__ __attribute__((aligned(16))) float redA[4][G * 2 * kN], redB[4][G * 2 * kN];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform(threadIdx.x >> 6);
-    const int cl = lane >> 3;                 // channel within the wave
-    const int g = lane & 7;                   // state pair
+    const int cl = lane / P;                  // channel within the wave
+    const int g = lane % P;                   // state pair
     const int s0 = 2 * g;
-    const int d_w0 = blockIdx.x * kPairChannels + w * CW;
+    const int d_w0 = blockIdx.x * (4 * CW) + w * CW;
     const int d_raw = d_w0 + cl;
     const bool live = d_raw < D;
     const int d = live ? d_raw : D - 1;
@@ -647,39 +657,43 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
 
     float a2[2], ar[2], q[2];
     {
-        const float2 av = *reinterpret_cast<const float2 *>(A + (int64_t)d * kStates + s0);
+        const float2 av = *reinterpret_cast<const float2 *>(A + (int64_t)d * kN + s0);
         ar[0] = av.x; ar[1] = av.y;
         a2[0] = av.x * kLog2e; a2[1] = av.y * kLog2e;
         q[0] = q[1] = 0.f;
         if (!kBlockInit && qin != nullptr && t_end < T && live) {
             const float2 v = *reinterpret_cast<const float2 *>(
-                qin + (int64_t)b * qin_bs + (int64_t)c * qin_cs + (int64_t)d * kStates + s0);
+                qin + (int64_t)b * qin_bs + (int64_t)c * qin_cs + (int64_t)d * kN + s0);
             q[0] = v.x; q[1] = v.y;
         }
     }
     float dA_acc[2] = {0.f, 0.f};
     float dD_acc = 0.f;
     auto state_at = [&](const float *base, int64_t blk) -> float2 {
-        return *reinterpret_cast<const float2 *>(base + (((int64_t)b * (nbl + 1) + blk) * D + d) * kStates + s0);
+        return *reinterpret_cast<const float2 *>(base + (((int64_t)b * (nbl + 1) + blk) * D + d) * kN + s0);
     };
     if (kBlockInit && dh0 != nullptr && t_end == T && live)
-        *reinterpret_cast<float2 *>(dh0 + (((int64_t)b * (nbl + 1) + nbl) * D + d) * kStates + s0) =
+        *reinterpret_cast<float2 *>(dh0 + (((int64_t)b * (nbl + 1) + nbl) * D + d) * kN + s0) =
             make_float2(0.f, 0.f);
 
-    // after the per-token channel sums: lane l holds dB / dC value kind l / 16
-    // (dB of state 2g, dB of 2g + 1, dC of 2g, dC of 2g + 1) of state pair
-    // g = l % 8, i.e. entry bc_idx of the token's 32 (dB by state, then dC)
-    const int bc_idx = ((lane >> 5) << 4) + s0 + ((lane >> 4) & 1);
-    // a token pair's sums: lanes with bit 3 clear hold token i + 1, the others token i
+    // after the per-token channel sums: lane l holds dB (bit 5 clear) or dC of
+    // state 2g + (bit 4) of its state pair g, i.e. entry bc_idx of the
+    // token's 2 kN (dB by state, then dC)
+    const int bc_idx = ((lane >> 5) ? kN : 0) + s0 + ((lane >> 4) & 1);
+    // 16 states: a token pair's sums, lanes with bit 3 clear holding token
+    // i + 1 and the others token i
     const bool b3 = (lane & 8) != 0;
-    const int red_lane = (b3 ? 0 : 2 * kStates) + bc_idx;
-    // the dt / x sums of a 4-token segment: lane l holds token 4s + l % 4 of
-    // quantity (l / 4) % 2 (0: dt, 1: x) of its own channel cl
-    const int o_tok = lane & 3, o_q = (lane >> 2) & 1;
-    // Dskip dy enters the x sum once per channel, in lane g == 4
-    const float dskg = (g == 4) ? Dskip[d] : 0.f;
-    // the fused epilogue's lanes: tokens l / 8 and l / 8 + 8, channel l % 8
-    const int o_ch = lane & 7;
+    const int red_lane = (P == 8 && !b3 ? 2 * kN : 0) + bc_idx;
+    // below 16 states the sums end duplicated over the lane bits 1 .. 3 below
+    // the channel bits that the folds leave; one lane of each writes them
+    constexpr int kDupMask = P == 4 ? 12 : P == 2 ? 14 : 0;
+    // the dt / x sums of a TK-token segment: lane l holds token TK s + g % TK
+    // of quantity g / TK (0: dt, 1: x) of its own channel cl
+    const int o_tok = g % TK, o_q = g / TK;
+    // Dskip dy enters the x sum once per channel, in lane g == 0
+    const float dskg = (g == 0) ? Dskip[d] : 0.f;
+    // the fused epilogue's lanes: tokens l / CW + P h (h < EV), channel l % CW
+    const int o_ch = lane % CW;
     const bool o_live = d_w0 + o_ch < D;
 
     const int64_t first = (int64_t)b * T + t_begin;
@@ -687,16 +701,16 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
     const Rows<Tin> ds(dt + first * D, len, D, 0);
     const Rows<Tin> ys(dy + first * D, len, D, 0);
     __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(const_cast<Tin *>(Bm + first * kStates)), 0, uniform(len * kStates * ES), kRawBufferWord3);
+        uniform_ptr(const_cast<Tin *>(Bm + first * kN)), 0, uniform(len * kN * ES), kRawBufferWord3);
     __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(const_cast<Tin *>(Cm + first * kStates)), 0, uniform(len * kStates * ES), kRawBufferWord3);
-    // DMA lanes: x / dt / dy load j covers tokens 8j .. 8j+7 (lane: token l / 8,
-    // channel l % 8); B / C: wave w loads tokens 4w .. 4w+3 (lane: token l / 16,
-    // state l % 16)
-    const int ld_tok = lane >> 3, ld_col = lane & 7;
+        uniform_ptr(const_cast<Tin *>(Cm + first * kN)), 0, uniform(len * kN * ES), kRawBufferWord3);
+    // DMA lanes: x / dt / dy load j covers tokens P j .. P j + P - 1 (lane:
+    // token l / CW, channel l % CW); B / C load j (taken by wave j % 4) covers
+    // tokens BT j .. (lane: token l / kN, state l % kN)
+    const int ld_tok = lane / CW, ld_col = lane % CW;
     const bool ld_live = d_w0 + ld_col < D;
     const int ld_ch = ld_live ? d_w0 + ld_col : D - 1;
-    const int bc_tok = 4 * w + (lane >> 4), bc_col = lane & 15;
+    const int bc_tok = lane / kN, bc_col = lane % kN;
     const bool gate = kFuse && fz.z != nullptr;
     const bool sp_mode = kFuse && fz.dt_mode == kDtSoftplus;
     const float ld_bias = (kFuse && fz.dt_bias != nullptr) ? fz.dt_bias[ld_ch] : 0.f;
@@ -712,20 +726,26 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
     // decay by 1 and inject nothing, and dead channels form no gradient terms
     auto issue = [&](auto &xd, auto &bc, int k0) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int kr = k0 + 8 * j + ld_tok;
+        for (int j = 0; j < XL; ++j) {
+            const int kr = k0 + P * j + ld_tok;
             const int k = kr < len ? kr : len - 1;
             const int zoff = (kr < len && ld_live) ? ld_ch * ES + k * ds.pitch : kOutOfRange;
-            load_to_lds<ES>(xs.rsrc, &xd[w][0][8 * j][0], ld_ch * ES + k * xs.pitch, 0);
-            load_to_lds<ES>(ds.rsrc, &xd[w][1][8 * j][0], zoff, 0);
-            load_to_lds<ES>(ys.rsrc, &xd[w][2][8 * j][0], zoff, 0);
+            load_to_lds<ES>(xs.rsrc, &xd[w][0][P * j][0], ld_ch * ES + k * xs.pitch, 0);
+            load_to_lds<ES>(ds.rsrc, &xd[w][1][P * j][0], zoff, 0);
+            load_to_lds<ES>(ys.rsrc, &xd[w][2][P * j][0], zoff, 0);
             if constexpr (kFuse) {
-                if (gate) load_to_lds<ES>(zs.rsrc, &xd[w][NSB - 1][8 * j][0], zoff, 0);
+                if (gate) load_to_lds<ES>(zs.rsrc, &xd[w][NSB - 1][P * j][0], zoff, 0);
             }
         }
-        const int kb = (k0 + bc_tok < len) ? k0 + bc_tok : len - 1;
-        load_to_lds<ES>(brs, &bc[0][4 * w][0], (kb * kStates + bc_col) * ES, 0);
-        load_to_lds<ES>(crs, &bc[1][4 * w][0], (kb * kStates + bc_col) * ES, 0);
+#pragma unroll
+        for (int j = 0; j < BL; j += 4) {
+            if (BL % 4 == 0 || j + w < BL) {
+                const int kt = k0 + BT * (j + w) + bc_tok;
+                const int kb = kt < len ? kt : len - 1;
+                load_to_lds<ES>(brs, &bc[0][BT * (j + w)][0], (kb * kN + bc_col) * ES, 0);
+                load_to_lds<ES>(crs, &bc[1][BT * (j + w)][0], (kb * kN + bc_col) * ES, 0);
+            }
+        }
     };
     // after this wave's own loads have landed, widen the dwords this lane
     // loaded to fp32 in place (bf16 only)
@@ -735,30 +755,35 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
 #pragma unroll
             for (int s = 0; s < NSB; ++s)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
+                for (int j = 0; j < XL; ++j) {
                     if (s == 3 && !gate) continue;
-                    uint32_t &v = (&xd[w][s][8 * j][0])[lane];
+                    uint32_t &v = (&xd[w][s][P * j][0])[lane];
                     v <<= 16;
                 }
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                uint32_t &v = (&bc[s][4 * w][0])[lane];
-                v <<= 16;
+            for (int j = 0; j < BL; j += 4) {
+                if (BL % 4 == 0 || j + w < BL) {
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        uint32_t &v = (&bc[s][BT * (j + w)][0])[lane];
+                        v <<= 16;
+                    }
+                }
             }
         }
         if constexpr (kFuse) {
             // the step size of the forward, and the gate's two factors of dy
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                uint32_t &dv = (&xd[w][1][8 * j][0])[lane];
+            for (int j = 0; j < XL; ++j) {
+                uint32_t &dv = (&xd[w][1][P * j][0])[lane];
                 const float raw = __uint_as_float(dv);
                 float dl = raw;
                 if (fz.dt_mode == kDtSoftplus) dl = step_size<kDtSoftplus>(raw, ld_bias);
                 else if (fz.dt_mode == kDtBias) dl = step_size<kDtBias>(raw, ld_bias);
                 dv = __float_as_uint(dl);
                 if (gate) {
-                    uint32_t &yv = (&xd[w][2][8 * j][0])[lane];
-                    uint32_t &zv = (&xd[w][3][8 * j][0])[lane];
+                    uint32_t &yv = (&xd[w][2][P * j][0])[lane];
+                    uint32_t &zv = (&xd[w][3][P * j][0])[lane];
                     const float zf = __uint_as_float(zv), gy = __uint_as_float(yv);
                     const float sg = __builtin_amdgcn_rcpf(1.f + fast_exp2(-zf * kLog2e));
                     yv = __float_as_uint(gy * (zf * sg));                         // dy silu(z)
@@ -769,7 +794,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
     };
     auto f32 = [](uint32_t v) { return __uint_as_float(v); };
 
-    float *pbc = part_bc + ((int64_t)b * gridDim.x + blockIdx.x) * T * 32;
+    float *pbc = part_bc + ((int64_t)b * gridDim.x + blockIdx.x) * T * (2 * kN);
     Tin *dxw = dx + first * D;
     Tin *dtw = ddt + first * D;
 
@@ -879,57 +904,80 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
             dD_acc = __builtin_fmaf(gy, xv, dD_acc);   // every lane; lane g == 0's total is stored
             if constexpr (kFuse) {
                 // y_pre of the token: the lane's C (hf + hr) summed over the
-                // channel's 8 state pairs (lanes 8 cl .. 8 cl + 7), + Dskip x,
-                // into the token's x slot (pass B is done with it)
+                // channel's P state pairs (quad exchanges, then the half-row
+                // mirror or the row rotations by 4 and 8), + Dskip x, into the
+                // token's x slot (pass B is done with it)
                 yp += dpp_perm<kDppXor1>(yp);
-                yp += dpp_perm<kDppXor2>(yp);
-                yp += dpp_perm<kDppHalfMirror>(yp);
+                if constexpr (P >= 4) yp += dpp_perm<kDppXor2>(yp);
+                if constexpr (P == 8) yp += dpp_perm<kDppHalfMirror>(yp);
+                if constexpr (P == 16) {
+                    yp += dpp_perm<kDppRor4>(yp);
+                    yp += dpp_perm<kDppRor8>(yp);
+                }
                 xd[w][0][i][cl] = __float_as_uint(__builtin_fmaf(dsk, xv, yp));
             }
             if constexpr (kBlockInit) {
                 if (i % LB == 0 && gsb && dh0 != nullptr && i < nvalid && live) {
                     const int64_t blk = kLong ? t_begin / Lb + k0 / Lb : (t_begin + k0 + i) / LB;
-                    *reinterpret_cast<float2 *>(dh0 + (((int64_t)b * (nbl + 1) + blk) * D + d) * kStates + s0) =
+                    *reinterpret_cast<float2 *>(dh0 + (((int64_t)b * (nbl + 1) + blk) * D + d) * kN + s0) =
                         make_float2(q[0], q[1]);
                 }
             }
-            // dB / dC of the token summed over the wave's 8 channels (lanes
-            // g, g + 8, ..., g + 56): the 32-lane folds add channel c + 4 to c,
-            // the 16-lane fold channel c + 2; the last step (channel c + 1, a
-            // row rotation by 8) takes two tokens at once, lanes with bit 3
-            // clear keeping token i + 1 and the others token i, so that all
-            // 64 lanes store a distinct sum; the sums meet the other waves'
-            // in red
+            // dB / dC of the token summed over the wave's CW channels (lanes
+            // g, g + P, ...): the 32-lane folds sum lane bit 5, the 16-lane
+            // fold bit 4, which completes the sum at 32 states.  At 16 states
+            // the last channel bit (3, a row rotation by 8) takes two tokens
+            // at once, lanes with bit 3 clear keeping token i + 1 and the
+            // others token i, so that all 64 lanes store a distinct sum;
+            // below, the channel bits left (3 and 2, and 1) are summed by row
+            // rotations (and a quad exchange) and one lane of each duplicate
+            // stores.  The sums meet the other waves' in red.
             {
                 const float f0 = fold32(vb[0], vc[0]);
                 const float f1 = fold32(vb[1], vc[1]);
-                const float s16 = fold16(f0, f1);
-                if (i & 1) {
-                    s16_next = s16;
+                float s16 = fold16(f0, f1);
+                if constexpr (P == 16) {
+                    red[w][i * 2 * kN + red_lane] = s16;
+                } else if constexpr (P == 8) {
+                    if (i & 1) {
+                        s16_next = s16;
+                    } else {
+                        float keep = b3 ? s16 : s16_next;
+                        const float snd = b3 ? s16_next : s16;
+                        keep += xchg8(snd);
+                        red[w][i * 2 * kN + red_lane] = keep;
+                    }
                 } else {
-                    float keep = b3 ? s16 : s16_next;
-                    const float snd = b3 ? s16_next : s16;
-                    keep += xchg8(snd);
-                    red[w][i * 2 * kStates + red_lane] = keep;
+                    if constexpr (P == 2) s16 += dpp_perm<kDppXor2>(s16);
+                    s16 += dpp_perm<kDppRor4>(s16);
+                    s16 += dpp_perm<kDppRor8>(s16);
+                    if ((lane & kDupMask) == 0) red[w][i * 2 * kN + red_lane] = s16;
                 }
             }
-            // dt and x partials of the token summed over the channel's 8 state
-            // pairs: the half-row mirror exchange leaves the dt sum's pairs in
-            // lanes g < 4 and the x sum's in lanes g >= 4, two quad exchanges
-            // complete them; lane g keeps token i where g % 4 == i % 4
+            // dt and x partials of the token summed over the channel's P state
+            // pairs: an exchange over the top bit of g (row rotation by 8,
+            // half-row mirror, or a quad exchange) leaves the dt sum's pairs in
+            // lanes g < TK and the x sum's in lanes g >= TK, exchanges over
+            // the lower bits complete them; lane g keeps token i where
+            // g % TK == i % TK
             {
                 const float pa = __builtin_fmaf(xv, s1, s2);
                 const float pb = __builtin_fmaf(dskg, gy, dl * s1);
                 float v = o_q ? pb : pa;
                 const float snd = o_q ? pa : pb;
-                v += dpp_perm<kDppHalfMirror>(snd);
-                v += dpp_perm<kDppXor1>(v);
-                v += dpp_perm<kDppXor2>(v);
-                if (o_tok == (i & 3)) tsum = v;
+                if constexpr (P == 16) v += dpp_perm<kDppRor8>(snd);
+                else if constexpr (P == 8) v += dpp_perm<kDppHalfMirror>(snd);
+                else if constexpr (P == 4) v += dpp_perm<kDppXor2>(snd);
+                else v += dpp_perm<kDppXor1>(snd);
+                if constexpr (P >= 4) v += dpp_perm<kDppXor1>(v);
+                if constexpr (P >= 8) v += dpp_perm<kDppXor2>(v);
+                if constexpr (P == 16) v += dpp_perm<kDppHalfMirror>(v);
+                if (o_tok == i % TK) tsum = v;
             }
-            if ((i & 3) == 0) {
+            if ((i & 3) == 0)
                 asm volatile("" : "+v"(hr[0]), "+v"(hr[1]), "+v"(q[0]), "+v"(q[1]), "+v"(dA_acc[0]),
                              "+v"(dA_acc[1]), "+v"(tsum), "+v"(dD_acc) :: "memory");
+            if (i % TK == 0) {
                 const int it = i + o_tok;
                 if constexpr (kFuse) {
                     // dx is final here; the dt-stream gradient before the
@@ -949,13 +997,12 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
             hrc[0] = hr[0]; hrc[1] = hr[1];
         }
         if constexpr (kFuse) {
-            // epilogue of the group: lane (tokens l / 8 and l / 8 + 8, channel
-            // l % 8) applies softplus'(v) = s(v) to the dt-stream gradient,
-            // adds it to the bias sum and stores it, and stores
-            // dz = dy silu'(z) y_pre
+            // epilogue of the group: lane (tokens l / CW + P h, channel l % CW)
+            // applies softplus'(v) = s(v) to the dt-stream gradient, adds it
+            // to the bias sum and stores it, and stores dz = dy silu'(z) y_pre
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int t = (lane >> 3) + 8 * h;
+            for (int h = 0; h < EV; ++h) {
+                const int t = lane / CW + P * h;
                 const bool ok = o_live && t < nvalid;
                 // stores of dead channels and tokens past the group go to an
                 // offset beyond the buffer's range, which drops them
@@ -1035,11 +1082,14 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
         if (more) widen(xdn, bcn);
         __syncthreads();
         const int nvalid = (len - k0 < G) ? len - k0 : G;
+        constexpr int NR = G * 2 * kN;        // the group's sums, NR / 256 or fewer per thread
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int o = threadIdx.x + h * 256;
-            const float v = ((red[0][o] + red[1][o]) + red[2][o]) + red[3][o];
-            if ((o >> 5) < nvalid) pbc[(t_begin + k0) * 32 + o] = v;
+        for (int h = 0; h < (NR + 4 * kWave - 1) / (4 * kWave); ++h) {
+            const int o = threadIdx.x + h * 4 * kWave;
+            if (NR % (4 * kWave) == 0 || o < NR) {
+                const float v = ((red[0][o] + red[1][o]) + red[2][o]) + red[3][o];
+                if (o / (2 * kN) < nvalid) pbc[(t_begin + k0) * (2 * kN) + o] = v;
+            }
         }
     };
     const int k_last = ((len - 1) / G) * G;
@@ -1059,21 +1109,26 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
             const float2 e = state_at(dbounds, 0);
             v0 += e.x; v1 += e.y;
         }
-        *reinterpret_cast<float2 *>(dh0 + ((int64_t)b * D + d) * kStates + s0) = make_float2(v0, v1);
+        *reinterpret_cast<float2 *>(dh0 + ((int64_t)b * D + d) * kN + s0) = make_float2(v0, v1);
     }
     // dA and dDskip partials of this (batch, chunk)
     if (live) {
         const int64_t pc = (int64_t)b * gridDim.y + c;
-        *reinterpret_cast<float2 *>(part_a + (pc * D + d) * kStates + s0) = make_float2(dA_acc[0], dA_acc[1]);
+        *reinterpret_cast<float2 *>(part_a + (pc * D + d) * kN + s0) = make_float2(dA_acc[0], dA_acc[1]);
         if (g == 0) part_d[pc * D + d] = dD_acc;
     }
     if constexpr (kFuse) {
-        // the dt-stream gradient summed over the chunk: the 4 token lanes of
-        // each output channel (lanes ch, ch + 16, ch + 32, ch + 48), in a
-        // fixed order
-        bias_acc += xchg8(bias_acc);
-        bias_acc += xchg16(bias_acc);
-        bias_acc += xchg32(bias_acc, lane);
+        // the dt-stream gradient summed over the chunk: the token lanes of
+        // each output channel (lanes ch, ch + CW, ...: the lane bits from
+        // log2 CW up), in a fixed order
+        if constexpr (CW <= 4) {
+            bias_acc += dpp_perm<kDppRor4>(bias_acc);
+            bias_acc += dpp_perm<kDppRor8>(bias_acc);
+        } else if constexpr (CW == 8) {
+            bias_acc += xchg8(bias_acc);
+        }
+        if constexpr (CW <= 16) bias_acc = fold16(bias_acc, bias_acc);
+        bias_acc = fold32(bias_acc, bias_acc);
         if (fz.part_bias != nullptr && lane < CW && o_live)
             fz.part_bias[((int64_t)b * gridDim.y + c) * D + d_w0 + lane] = bias_acc;
     }

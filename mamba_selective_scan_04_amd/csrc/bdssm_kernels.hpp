@@ -911,7 +911,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
         }
 #pragma unroll
         for (int j = 0; j < BL; j += 4) {
-            if (j + w < BL) {
+            if (BL % 4 == 0 || j + w < BL) {
                 const int kt = k0 + BT * (j + w) + bc_tok;
                 const int kb = kt < len ? kt : len - 1;
                 load_to_lds<ES>(brs, &bc[0][BT * (j + w)][0], (kb * kN + bc_col) * ES, 0);
@@ -935,7 +935,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
                 }
 #pragma unroll
             for (int j = 0; j < BL; j += 4) {
-                if (j + w < BL) {
+                if (BL % 4 == 0 || j + w < BL) {
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
                         uint32_t &v = (&bc[s][BT * (j + w)][0])[lane];

@@ -386,14 +386,21 @@ struct BwdArgs {
     float *part_bc_r = nullptr, *part_a_r = nullptr, *part_bias_r = nullptr;
 };
 
-// The backward's block-local kernel.  bwd_pair_kernel (two states per lane,
-// the whole 16-token group held in registers, 32 channels per workgroup) is
-// the faster for L = 8 and 16; for L <= 4 its per-block loads spill and the
+// BDSSM_BWD_KERNEL=general keeps every backward on bwd_general_kernel (tests).
+inline bool bwd_force_general() {
+    const char *v = getenv("BDSSM_BWD_KERNEL");
+    return v != nullptr && v[0] == 'g';
+}
+
+// The backward's block-local kernel for L | 16.  bwd_pair_kernel (two states
+// per lane, the whole 16-token group held in registers, 512 / N channels per
+// workgroup) takes every supported state count; at 16 states and L <= 4 the
 // four-state bwd_wave_kernel (segment recomputation, 64 channels per
-// workgroup) is faster (measured on MI355X).  BDSSM_BWD_KERNEL=wave / pair
-// forces one of them (tuning and tests).
-inline bool bwd_use_wave(int64_t L, bool fused = false) {
-    if (fused) return false;                 // only bwd_pair_kernel has the fused variant
+// workgroup) is faster, since the pair kernel's per-block loads spill there
+// (measured on MI355X).  BDSSM_BWD_KERNEL=wave / pair forces one of them at
+// 16 states (tuning and tests).
+inline bool bwd_use_wave(int64_t L, bool fused = false, int64_t N = kStates) {
+    if (fused || N != kStates) return false;   // only bwd_pair_kernel has the fused variant and N != 16
     const char *v = getenv("BDSSM_BWD_KERNEL");
     if (v != nullptr && v[0] == 'w') return true;
     if (v != nullptr && v[0] == 'p') return false;
@@ -401,38 +408,36 @@ inline bool bwd_use_wave(int64_t L, bool fused = false) {
 }
 
 // channels per workgroup of the chosen kernel (the dB / dC partial blocks)
-inline int64_t bwd_block_channels(int64_t L, bool fused = false) {
-    return bwd_use_wave(L, fused) ? kWave : kPairChannels;
+inline int64_t bwd_block_channels(int64_t L, bool fused = false, int64_t N = kStates) {
+    return bwd_use_wave(L, fused, N) ? kWave : pair_channels_of(N);
 }
 
 // workgroups of the chosen kernel resident at once: bwd_pair_kernel fits
-// three per CU (168 registers, 44 KB LDS; 48 KB with the fused streams),
-// bwd_wave_kernel two
-inline int64_t bwd_block_capacity(int64_t L, bool fused = false) {
-    return bwd_use_wave(L, fused) ? kCoarseGroups : 3 * 256;
+// three per CU (148-168 registers, 32-48 KB LDS at 16 states), bwd_wave_kernel
+// two
+inline int64_t bwd_block_capacity(int64_t L, bool fused = false, int64_t N = kStates) {
+    return bwd_use_wave(L, fused, N) ? kCoarseGroups : 3 * 256;
 }
 
 // Long blocks (multiples of 16 above 16 at 16 states) take bwd_pair_kernel
-// with group states from group_state_kernel; BDSSM_BWD_KERNEL=general sends
-// them to bwd_general_kernel instead (tests).
+// with group states from group_state_kernel.
 inline bool bwd_long(int64_t L, int64_t N, bool sep = false) {
-    if (!long_block(L, N, sep)) return false;
-    const char *v = getenv("BDSSM_BWD_KERNEL");
-    return !(v != nullptr && v[0] == 'g');
+    return long_block(L, N, sep) && !bwd_force_general();
 }
 
 // The general backward path (bwd_general_kernel): block lengths outside the
-// 16-token group's divisors and its multiples, and state counts other than 16.
-// Separate reverse operands always take it (bwd_general_kernel<..., 2>).
+// 16-token group's divisors and its multiples, and multiples of 16 at state
+// counts other than 16.  Separate reverse operands always take it
+// (bwd_general_kernel<..., 2>).
 inline bool bwd_general(int64_t L, int64_t N, bool sep = false) {
-    return sep || (!(wave_block(L) && N == kStates) && !bwd_long(L, N));
+    return sep || bwd_force_general() || (!(wave_block(L) && supported_states(N)) && !bwd_long(L, N));
 }
 
 // channels per workgroup of the block-local kernel (the dB / dC partial blocks)
 inline int64_t bwd_channels(int64_t L, int64_t N, bool fused, bool sep = false) {
     if (sep) return bwd_general_waves<2>() * kWave / N;
     if (bwd_long(L, N)) return kPairChannels;
-    return bwd_general(L, N) ? bwd_general_waves<0>() * kWave / N : bwd_block_channels(L, fused);
+    return bwd_general(L, N) ? bwd_general_waves<0>() * kWave / N : bwd_block_channels(L, fused, N);
 }
 
 // chunk plans of the two backward forms, for the chosen kernel's geometry.
@@ -441,16 +446,16 @@ inline int64_t bwd_channels(int64_t L, int64_t N, bool fused, bool sep = false) 
 inline bool bwd_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, bool fused, Plan *p,
               bool sep = false) {
     if (bwd_general(L, N, sep) || bwd_long(L, N, sep)) return plan_general(batch, D, T, L, p);
-    *p = make_plan(batch, D, T, kBwdPrepassWeight, bwd_block_channels(L, fused),
-                   bwd_block_capacity(L, fused));
+    *p = make_plan(batch, D, T, kBwdPrepassWeight, bwd_block_channels(L, fused, N),
+                   bwd_block_capacity(L, fused, N));
     return true;
 }
 inline bool bwd_blocks_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, int64_t *tc,
                      int64_t *nc, bool fused, bool sep = false) {
     if (bwd_general(L, N, sep) || bwd_long(L, N, sep))
         return blocks_plan(batch, D, T, L, N, tc, nc, bwd_channels(L, N, fused, sep), 3 * 256);
-    return blocks_plan(batch, D, T, L, kStates, tc, nc, bwd_block_channels(L, fused),
-                       bwd_block_capacity(L, fused));
+    return blocks_plan(batch, D, T, L, N, tc, nc, bwd_block_channels(L, fused, N),
+                       bwd_block_capacity(L, fused, N));
 }
 
 // dynamic LDS of bwd_general_kernel: hf and pr at every 16-token segment start
@@ -512,9 +517,9 @@ void launch_adjoint_chunk(const void *dt, const void *dy, const void *C, const f
                           hipStream_t st, int dt_mode = kDtPlain, const float *dt_bias = nullptr,
                           const void *z = nullptr);
 
-// The block-local backward kernels (L | 16, 16 states).        launch_bwd.hip
+// The block-local backward kernels (L | 16, N states).         launch_bwd.hip
 template <typename Tin, bool kBlockInit>
-void launch_bwd(int64_t L, const BwdArgs &a, int64_t batch, int64_t T, int64_t D, int64_t Tc,
+void launch_bwd(int64_t L, int64_t N, const BwdArgs &a, int64_t batch, int64_t T, int64_t D, int64_t Tc,
                 int nc, hipStream_t st);
 
 // Long blocks: group states, then bwd_pair_kernel.            launch_bwd.hip

@@ -54,43 +54,53 @@ void launch_adjoint_chunk(const void *dt, const void *dy, const void *C, const f
     }
 }
 
-template <typename Tin, int L, bool kBlockInit>
+template <typename Tin, int kN, int L, bool kBlockInit>
 void launch_bwd_L(const BwdArgs &a, int64_t batch, int64_t T, int64_t D, int64_t Tc, int nc,
                   hipStream_t st) {
-    if (bwd_use_wave(L, a.fused)) {
-        hipLaunchKernelGGL((bwd_wave_kernel<Tin, L, kBlockInit>), grid3(D, nc, batch), dim3(4 * kWave), 0,
-                           st, (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
-                           (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
-                           a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0, T,
-                           (int)D, Tc);
-        return;
+    if constexpr (kN == kStates) {
+        if (bwd_use_wave(L, a.fused, kN)) {
+            hipLaunchKernelGGL((bwd_wave_kernel<Tin, L, kBlockInit>), grid3(D, nc, batch), dim3(4 * kWave), 0,
+                               st, (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
+                               (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
+                               a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0, T,
+                               (int)D, Tc);
+            return;
+        }
     }
-    const dim3 g((unsigned)ceil_div(D, kPairChannels), (unsigned)nc, (unsigned)batch);
+    const dim3 g((unsigned)ceil_div(D, pair_channels<kN>()), (unsigned)nc, (unsigned)batch);
     const BwdFuse<Tin> fz{a.dt_bias, a.dt_mode, (const Tin *)a.z, (Tin *)a.dz, a.part_bias};
     if (a.fused)
-        hipLaunchKernelGGL((bwd_pair_kernel<Tin, L, kBlockInit, true>), g, dim3(4 * kWave), 0, st,
+        hipLaunchKernelGGL((bwd_pair_kernel<Tin, kN, L, kBlockInit, true>), g, dim3(4 * kWave), 0, st,
                            (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
                            (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
                            a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0,
                            T, (int)D, Tc, fz, (const float *)nullptr, 0);
     else
-        hipLaunchKernelGGL((bwd_pair_kernel<Tin, L, kBlockInit, false>), g, dim3(4 * kWave), 0, st,
+        hipLaunchKernelGGL((bwd_pair_kernel<Tin, kN, L, kBlockInit, false>), g, dim3(4 * kWave), 0, st,
                            (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
                            (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
                            a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0,
                            T, (int)D, Tc, fz, (const float *)nullptr, 0);
 }
 
-template <typename Tin, bool kBlockInit>
-void launch_bwd(int64_t L, const BwdArgs &a, int64_t batch, int64_t T, int64_t D, int64_t Tc,
-                int nc, hipStream_t st) {
+template <typename Tin, int kN, bool kBlockInit>
+void launch_bwd_n(int64_t L, const BwdArgs &a, int64_t batch, int64_t T, int64_t D, int64_t Tc, int nc,
+                  hipStream_t st) {
     switch (L) {
-    case 1: launch_bwd_L<Tin, 1, kBlockInit>(a, batch, T, D, Tc, nc, st); break;
-    case 2: launch_bwd_L<Tin, 2, kBlockInit>(a, batch, T, D, Tc, nc, st); break;
-    case 4: launch_bwd_L<Tin, 4, kBlockInit>(a, batch, T, D, Tc, nc, st); break;
-    case 8: launch_bwd_L<Tin, 8, kBlockInit>(a, batch, T, D, Tc, nc, st); break;
-    default: launch_bwd_L<Tin, 16, kBlockInit>(a, batch, T, D, Tc, nc, st); break;
+    case 1: launch_bwd_L<Tin, kN, 1, kBlockInit>(a, batch, T, D, Tc, nc, st); break;
+    case 2: launch_bwd_L<Tin, kN, 2, kBlockInit>(a, batch, T, D, Tc, nc, st); break;
+    case 4: launch_bwd_L<Tin, kN, 4, kBlockInit>(a, batch, T, D, Tc, nc, st); break;
+    case 8: launch_bwd_L<Tin, kN, 8, kBlockInit>(a, batch, T, D, Tc, nc, st); break;
+    default: launch_bwd_L<Tin, kN, 16, kBlockInit>(a, batch, T, D, Tc, nc, st); break;
     }
+}
+
+template <typename Tin, bool kBlockInit>
+void launch_bwd(int64_t L, int64_t N, const BwdArgs &a, int64_t batch, int64_t T, int64_t D, int64_t Tc,
+                int nc, hipStream_t st) {
+    with_states(N, [&](auto n) {
+        launch_bwd_n<Tin, decltype(n)::value, kBlockInit>(L, a, batch, T, D, Tc, nc, st);
+    });
 }
 
 template <typename Tin, int kDt>
@@ -115,13 +125,13 @@ void launch_bwd_long(const BwdArgs &a, float *gstate, int64_t batch, int64_t T, 
     const dim3 g((unsigned)ceil_div(D, kPairChannels), (unsigned)nc, (unsigned)batch);
     const BwdFuse<Tin> fz{a.dt_bias, a.dt_mode, (const Tin *)a.z, (Tin *)a.dz, a.part_bias};
     if (a.fused)
-        hipLaunchKernelGGL((bwd_pair_kernel<Tin, 0, kBlockInit, true>), g, dim3(4 * kWave), 0, st,
+        hipLaunchKernelGGL((bwd_pair_kernel<Tin, kStates, 0, kBlockInit, true>), g, dim3(4 * kWave), 0, st,
                            (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
                            (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
                            a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0,
                            T, (int)D, Tc, fz, (const float *)gstate, (int)L);
     else
-        hipLaunchKernelGGL((bwd_pair_kernel<Tin, 0, kBlockInit, false>), g, dim3(4 * kWave), 0, st,
+        hipLaunchKernelGGL((bwd_pair_kernel<Tin, kStates, 0, kBlockInit, false>), g, dim3(4 * kWave), 0, st,
                            (const Tin *)a.x, (const Tin *)a.dt, (const Tin *)a.B, (const Tin *)a.C,
                            (const Tin *)a.dy, a.A, a.Dskip, a.h_start, a.qin, a.qin_bs, a.qin_cs,
                            a.dbounds, (Tin *)a.dx, (Tin *)a.ddt, a.part_bc, a.part_a, a.part_d, a.dh0,
@@ -159,10 +169,10 @@ template void launch_adjoint_chunk<BDSSM_TIN>(const void *, const void *, const 
                                             const float *, float *, float *, int64_t, int64_t, int64_t,
                                             int64_t, int64_t, int, int, int, hipStream_t, int, const float *,
                                             const void *);
-template void launch_bwd<BDSSM_TIN, false>(int64_t, const BwdArgs &, int64_t, int64_t, int64_t, int64_t, int,
-                                        hipStream_t);
-template void launch_bwd<BDSSM_TIN, true>(int64_t, const BwdArgs &, int64_t, int64_t, int64_t, int64_t, int,
-                                       hipStream_t);
+template void launch_bwd<BDSSM_TIN, false>(int64_t, int64_t, const BwdArgs &, int64_t, int64_t, int64_t, int64_t,
+                                        int, hipStream_t);
+template void launch_bwd<BDSSM_TIN, true>(int64_t, int64_t, const BwdArgs &, int64_t, int64_t, int64_t, int64_t,
+                                       int, hipStream_t);
 template void launch_bwd_long<BDSSM_TIN, false>(const BwdArgs &, float *, int64_t, int64_t, int64_t, int64_t,
                                              int64_t, int, hipStream_t);
 template void launch_bwd_long<BDSSM_TIN, true>(const BwdArgs &, float *, int64_t, int64_t, int64_t, int64_t,

@@ -142,3 +142,40 @@ def test_general_backward_empty_sequence(dev):
     torch.cuda.synchronize()
     assert torch.count_nonzero(g["dA"]) == 0 and g["dA"].shape == (64, N)
     assert torch.equal(g["dh_init"], db[:, 0])
+
+
+PAIR_CASES = [  # (N, L, T, D, dtype): the pair kernel at other state counts
+    (4, 16, 256, 130, torch.bfloat16),
+    (8, 16, 336, 70, torch.float32),
+    (32, 16, 192, 40, torch.bfloat16),
+    (32, 4, 200, 33, torch.float32),
+    (8, 2, 100, 65, torch.bfloat16),
+    (4, 1, 37, 130, torch.float32),
+]
+
+
+@pytest.mark.parametrize("N,L,T,D,dtype", PAIR_CASES)
+def test_pair_backward_state_counts(dev, N, L, T, D, dtype, monkeypatch):
+    """bwd_pair_kernel at 4, 8 and 32 states (the default for block lengths
+    dividing 16): several chunks, ragged channel tiles and last groups, both
+    forms."""
+    monkeypatch.setenv("BDSSM_CHUNK", "64")
+    monkeypatch.setenv("BDSSM_COARSE_CHUNKS", "3")
+    sid = 80 + PAIR_CASES.index((N, L, T, D, dtype))
+    c = Case(2, T, D, dtype, sid=sid, a_kind="random", n=N)
+    both_forms(c, L, sid, label="pair N=%d L=%d" % (N, L))
+
+
+@pytest.mark.parametrize("N", [4, 8, 32])
+def test_pair_backward_state_counts_fused(dev, N, monkeypatch):
+    """The fused pair kernel (softplus with bias, gate) at 4, 8 and 32 states."""
+    monkeypatch.setenv("BDSSM_CHUNK", "64")
+    batch, T, D, L = 2, 200, 70, 8
+    c = Case(batch, T, D, torch.bfloat16, sid=90 + N, a_kind="random", n=N)
+    c.dev["dt"] = synth.normal((batch, T, D), 1000 * (90 + N) + 11, "cpu", torch.float32, mean=-1.0,
+                               std=0.8).to(torch.bfloat16).to("cuda").contiguous()
+    bias = seeded((D,), 1000 * (90 + N) + 12, std=0.3)
+    z = seeded((batch, T, D), 1000 * (90 + N) + 13, torch.bfloat16, std=1.5)
+    kw = dict(dt_softplus=True, dt_bias=bias, z=z)
+    ok = dict(dt_softplus=True, dt_bias=to_np(bias), z=synth.to_oracle(z))
+    both_forms(c, L, 90 + N, kw, ok, label="pair fused N=%d" % N)
