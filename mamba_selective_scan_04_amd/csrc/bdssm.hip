@@ -573,8 +573,9 @@ int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, 
     if (rc) return rc;
     const Fuse f = resolve_fusion(fusion, true);
     int64_t tc, nc;
-    const bool pair = pair_path(L, N);
-    if (!blocks_plan(batch, D, T, L, N, &tc, &nc, pair ? pair_channels_of(N) : kWave, pair ? kPairGroups : kCoarseGroups))
+    const bool pair = pair_path(L, N) || (pair_long(L, N) && pair_bidir());
+    if (!blocks_plan(batch, D, T, L, N, &tc, &nc, pair ? pair_channels_of(N) : kWave,
+                     pair ? (pair_path(L, N) ? kPairGroups : pair_long_capacity(L, N)) : kCoarseGroups))
         return BDSSM_ERR_SHAPE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();

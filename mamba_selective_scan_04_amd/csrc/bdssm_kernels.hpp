@@ -796,10 +796,23 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 // dt of tokens past the chunk end and of channels past D reads zero (an
 // out-of-range DMA offset; after the step-size transform it is set to zero
 // again): such tokens decay by 1 and inject nothing.
-// Arguments as in bidir_wave_kernel, with states [.., kN]; separate reverse
-// operands run bidir_wave_kernel<..., 2> (16 states) or block_bidir_kernel.
+// L = 0 (long blocks: Lr tokens, a multiple of 16 from 32 to kLongMax; chunks
+// are whole blocks): each block's groups are first walked right to left with
+// the reverse recurrence alone (groups kb - 1 .. 1, kb = Lr / 16), keeping the
+// reverse state entering each group from its right in LDS; then the groups run
+// left to right as above, each reverse pass starting from its saved state.
+// The walk reads the group's rows a second time and costs about half the
+// forward pass's issue slots per element, over (kb - 1) / kb of the tokens.
+// Arguments as in bidir_wave_kernel, with states [.., kN] and the block length
+// Lr (L = 0 only); separate reverse operands run bidir_wave_kernel<..., 2>
+// (16 states) or block_bidir_kernel.
 // grid = (ceil(D / (4 CW)), chunks, batch), block = 256.
 template <int kN> constexpr int pair_channels() { return 4 * (2 * kWave / kN); }
+// The longest block the two-state forward takes (multiples of 16 from 32):
+// its right-to-left walk keeps Lr / 16 - 1 reverse states per lane in LDS.
+constexpr int kLongMax = 256;
+// dynamic LDS of bidir_pair_kernel's long-block mode
+inline size_t pair_long_lds(int64_t Lr) { return (size_t)4 * (Lr / kGroup - 1) * kWave * 2 * sizeof(float); }
 constexpr int kPairChannels = pair_channels<kStates>();   // 32: the 16-state two-state kernels
 
 // One step of the output reduce-scatter: lanes whose bit kBit of g is set
@@ -825,10 +838,12 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
     const Tin *__restrict__ Cm, const float *__restrict__ A, const float *__restrict__ Dskip,
     const float *hin, int64_t hin_bs, int64_t hin_cs,
     Tin *__restrict__ y, float *__restrict__ bounds, float *hout,
-    int64_t T, int D, int64_t Tc, const float *__restrict__ h0_blocks, FuseArgs<Tin> fz)
+    int64_t T, int D, int64_t Tc, const float *__restrict__ h0_blocks, FuseArgs<Tin> fz, int Lr)
 {
     static_assert(kFuse == 0 || kFuse == 1, "separate reverse operands run bidir_wave_kernel");
-    static_assert(kGroup % L == 0, "block length must divide the token group");
+    // L = 0: blocks of Lr tokens (a multiple of 16 from 32 to kLongMax)
+    constexpr bool kLong = L == 0;
+    static_assert(kLong || kGroup % L == 0, "block length must divide the token group");
     static_assert(kN == 4 || kN == 8 || kN == 16 || kN == 32, "state counts 4, 8, 16, 32");
     constexpr int P = kN / 2;                 // lanes per channel
     constexpr int CW = kWave / P;             // channels per wave
@@ -839,11 +854,16 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
     constexpr int BL = G * kN / kWave;        // B / C loads per group and stream (64 / kN tokens each)
     constexpr int BT = kWave / kN;            // tokens per B / C load
     constexpr int NV = G / P;                 // output tokens per lane
+    constexpr int LB = kLong ? G : L;         // block length as seen inside one group
     // double buffers as distinct arrays (the loads in flight into one are told
     // apart from the reads of the other): [wave][stream][token][channel] and
     // [B, C][token][state]
     __shared__ __attribute__((aligned(16))) uint32_t xdA[4][NS][G][CW], xdB[4][NS][G][CW];
     __shared__ __attribute__((aligned(16))) uint32_t bcA[2][G][kN], bcB[2][G][kN];
+    // long blocks: the reverse state entering each group of the block from
+    // its right, formed by the block's right-to-left state walk (per lane),
+    // [wave][Lr / 16 - 1][lane] in dynamic LDS
+    extern __shared__ float2 rsv[];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform(threadIdx.x >> 6);
@@ -859,7 +879,8 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
     const int64_t t_begin = (int64_t)c * Tc;
     const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
     const int len = (int)(t_end - t_begin);
-    const int64_t nbl = T / L;
+    const int Lb = kLong ? Lr : L;            // block length
+    const int64_t nbl = T / Lb;
 
     float a2[2], hf[2] = {0.f, 0.f};
     {
@@ -968,30 +989,33 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
 
     // two-stream form: the block start states of a group, loaded one group
     // ahead with its rows for L >= 4 (at most 4 blocks per group)
-    constexpr int NB = kBlockInit ? G / L : 1;
-    constexpr bool kAhead = kBlockInit && L >= 4;
+    constexpr int NB = kBlockInit ? G / LB : 1;
+    constexpr bool kAhead = kBlockInit && (kLong || L >= 4);
     float2 hbn[NB];
     auto load_hb = [&](int k0n) {
         if constexpr (kBlockInit) {
             const int nv = (len - k0n < G) ? len - k0n : G;
 #pragma unroll
             for (int q = 0; q < NB; ++q) {
-                const int i = q * L < nv ? q * L : 0;
-                const int64_t blk = (t_begin + k0n + i) / L;
+                const int i = q * LB < nv ? q * LB : 0;
+                const int64_t blk = (t_begin + k0n + i) / Lb;
                 hbn[q] = *reinterpret_cast<const float2 *>(
                     h0_blocks + (((int64_t)b * (nbl + 1) + blk) * D + d) * kN + s0);
             }
         }
     };
 
-    auto group = [&](auto &xd, auto &bc, int k0, const float2 *hb) {
+    // long blocks: gsb / geb, whether the group starts / ends its block, and
+    // hri, the reverse state entering it from the right
+    auto group = [&](auto &xd, auto &bc, int k0, const float2 *hb, float2 hri = make_float2(0.f, 0.f),
+                     bool gsb = true, bool geb = true) {
         const int nvalid = (len - k0 < G) ? len - k0 : G;   // uniform
         float dA[G][2], dxs[G], ya[G];
         // forward, left to right
 #pragma unroll
         for (int i = 0; i < G; ++i) {
             if constexpr (kBlockInit) {
-                if (i % L == 0) { hf[0] = hb[i / L].x; hf[1] = hb[i / L].y; }
+                if (i % LB == 0 && gsb) { hf[0] = hb[i / LB].x; hf[1] = hb[i / LB].y; }
             }
             const float dl = f32(xd[w][1][i][cl]);
             const float dxv = dl * f32(xd[w][0][i][cl]);
@@ -1002,8 +1026,8 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
             hf[0] = __builtin_fmaf(a0, hf[0], dxv * bv.x);
             hf[1] = __builtin_fmaf(a1, hf[1], dxv * bv.y);
             ya[i] = __builtin_fmaf(cv.y, hf[1], cv.x * hf[0]);
-            if ((i + 1) % L == 0 && bounds != nullptr && i < nvalid && live) {
-                const int64_t kb = (t_begin + k0 + i + 1) / L;
+            if ((i + 1) % LB == 0 && geb && bounds != nullptr && i < nvalid && live) {
+                const int64_t kb = (t_begin + k0 + i + 1) / Lb;
                 store_state(bounds + (((int64_t)b * (nbl + 1) + kb) * D + d) * kN);
             }
             if ((i & 3) == 3) {
@@ -1013,11 +1037,12 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
                              "+v"(ya[i - 3]) :: "memory");
             }
         }
-        // reverse, right to left, from zero at every block end
-        float hr[2] = {0.f, 0.f};
+        // reverse, right to left, from zero at every block end (long blocks:
+        // from the state entering the group from its right)
+        float hr[2] = {hri.x, hri.y};
 #pragma unroll
         for (int i = G - 1; i >= 0; --i) {
-            if ((i + 1) % L == 0) { hr[0] = hr[1] = 0.f; }
+            if (!kLong && (i + 1) % LB == 0) { hr[0] = hr[1] = 0.f; }
             const float2 bv = bcv(bc, 0, i), cv = bcv(bc, 1, i);
             hr[0] = __builtin_fmaf(dA[i][0], hr[0], dxs[i] * bv.x);
             hr[1] = __builtin_fmaf(dA[i][1], hr[1], dxs[i] * bv.y);
@@ -1077,13 +1102,75 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
         if (more) widen(xdn, bcn, k0 + G);
         __syncthreads();
     };
-    if constexpr (kAhead) load_hb(0);
-    issue(xdA, bcA, 0);
-    widen(xdA, bcA, 0);
-    __syncthreads();
-    for (int k0 = 0; k0 < len; k0 += 2 * G) {
-        step(xdA, bcA, xdB, bcB, k0);
-        if (k0 + G < len) step(xdB, bcB, xdA, bcA, k0 + G);
+    if constexpr (kLong) {
+        // Long blocks (chunks are whole blocks): per block of kb groups, a
+        // right-to-left state walk over groups kb - 1 .. 1 leaves the reverse
+        // state entering each group from its right in rsv; then the groups
+        // run left to right as above, each reverse pass starting from its
+        // saved state (zero in the block's last group).  Schedule entry s of
+        // block s / (2 kb - 1): walk steps first, then the groups in order.
+        const int kb = Lr / G;
+        const int per = 2 * kb - 1;
+        const int nsched = (len / Lr) * per;
+        auto sched_k0 = [&](int s) {
+            const int r = s % per;
+            return (s / per) * Lr + (r < kb - 1 ? kb - 1 - r : r - (kb - 1)) * G;
+        };
+        float2 hrw = make_float2(0.f, 0.f);   // the walk's state
+        // the walk over one group, right to left
+        auto walk = [&](auto &xd, auto &bc) {
+#pragma unroll
+            for (int i = G - 1; i >= 0; --i) {
+                const float dl = f32(xd[w][1][i][cl]);
+                const float dxv = dl * f32(xd[w][0][i][cl]);
+                const float2 bv = bcv(bc, 0, i);
+                hrw.x = __builtin_fmaf(fast_exp2(dl * a2[0]), hrw.x, dxv * bv.x);
+                hrw.y = __builtin_fmaf(fast_exp2(dl * a2[1]), hrw.y, dxv * bv.y);
+                if ((i & 3) == 0) asm volatile("" : "+v"(hrw.x), "+v"(hrw.y) :: "memory");
+            }
+        };
+        auto lstep = [&](auto &xd, auto &bc, auto &xdn, auto &bcn, int s) {
+            const bool more = s + 1 < nsched;
+            const int k0 = sched_k0(s), r = s % per;
+            float2 hb[NB];
+#pragma unroll
+            for (int q = 0; q < NB; ++q) hb[q] = hbn[q];
+            if (more) {
+                if constexpr (kAhead) load_hb(sched_k0(s + 1));
+                issue(xdn, bcn, sched_k0(s + 1));
+            }
+            if (r < kb - 1) {
+                const int j = kb - 1 - r;             // walk over group j
+                if (j == kb - 1) hrw = make_float2(0.f, 0.f);
+                walk(xd, bc);
+                rsv[(w * (kb - 1) + j - 1) * kWave + lane] = hrw;
+            } else {
+                const int j = r - (kb - 1);
+                group(xd, bc, k0, hb, j == kb - 1 ? make_float2(0.f, 0.f) : rsv[(w * (kb - 1) + j) * kWave + lane],
+                      j == 0, j == kb - 1);
+            }
+            if (more) widen(xdn, bcn, sched_k0(s + 1));
+            __syncthreads();
+        };
+        if (nsched > 0) {
+            if constexpr (kAhead) load_hb(sched_k0(0));
+            issue(xdA, bcA, sched_k0(0));
+            widen(xdA, bcA, sched_k0(0));
+            __syncthreads();
+        }
+        for (int s = 0; s < nsched; s += 2) {
+            lstep(xdA, bcA, xdB, bcB, s);
+            if (s + 1 < nsched) lstep(xdB, bcB, xdA, bcA, s + 1);
+        }
+    } else {
+        if constexpr (kAhead) load_hb(0);
+        issue(xdA, bcA, 0);
+        widen(xdA, bcA, 0);
+        __syncthreads();
+        for (int k0 = 0; k0 < len; k0 += 2 * G) {
+            step(xdA, bcA, xdB, bcB, k0);
+            if (k0 + G < len) step(xdB, bcB, xdA, bcA, k0 + G);
+        }
     }
     if (hout != nullptr && t_end == T && live) store_state(hout + ((int64_t)b * D + d) * kN);
 }

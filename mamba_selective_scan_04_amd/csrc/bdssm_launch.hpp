@@ -151,6 +151,11 @@ constexpr int64_t kPairGroups = 4 * 256;
 // (block lengths dividing the 16-token group, any supported state count), and
 // its channels per workgroup (4 waves x 64 lanes / (N / 2) lanes per channel).
 inline bool pair_path(int64_t L, int64_t N) { return wave_block(L) && supported_states(N); }
+// Long blocks in bidir_pair_kernel (L = 0 mode, chunks of whole blocks):
+// multiples of 16 from 32 to kLongMax, any supported state count.
+inline bool pair_long(int64_t L, int64_t N) {
+    return L > kGroup && L <= kLongMax && L % kGroup == 0 && supported_states(N);
+}
 inline int64_t pair_channels_of(int64_t N) { return 8 * kWave / N; }
 
 // f(std::integral_constant<int, N>) for a supported state count N.
@@ -170,8 +175,8 @@ template <typename F> void with_states(int64_t N, F &&f) {
 // blocks (one wave per 64 channels there, so four times the chunks).
 inline bool blocks_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, int64_t *tc_out,
                  int64_t *nc_out, int64_t coarse_ch = kWave, int64_t coarse_cap = kCoarseGroups) {
-    const bool wave = pair_path(L, N);
-    const int64_t unit = wave ? kGroup : L;
+    const bool wave = pair_path(L, N) || (pair_long(L, N) && coarse_ch == pair_channels_of(N));
+    const int64_t unit = pair_path(L, N) ? kGroup : L;
     const int64_t groups = batch * ceil_div(D, coarse_ch);
     const int64_t nunits = ceil_div(T, unit);
     int64_t nc = ceil_div((wave ? 4 : 16) * coarse_cap, groups);
@@ -206,12 +211,46 @@ inline bool plan_general(int64_t batch, int64_t D, int64_t T, int64_t L, Plan *o
     return true;
 }
 
+// The long-block pair plan: the pair kernel's coarse chunk count (one round
+// of resident workgroups), every fine chunk a whole number of blocks, so that
+// the coarse chunks are too.  Returns false if the chunking does not fit the
+// grid or the 32-bit offsets.
+inline int64_t pair_long_capacity(int64_t L, int64_t N) {
+    // workgroups per CU by LDS: the rows (x, dt, z double-buffered per wave;
+    // B, C double-buffered) and the walk's saved states, at most four
+    const int64_t lds = 1536 * (8 * kWave / N / 4) + 256 * N + (int64_t)pair_long_lds(L);
+    int64_t per_cu = (160 * 1024) / lds;
+    if (per_cu > 4) per_cu = 4;
+    if (per_cu < 1) per_cu = 1;
+    return per_cu * 256;
+}
+inline bool plan_long(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, Plan *out) {
+    const Plan base = make_plan(batch, D, T, 0.45, pair_channels_of(N), pair_long_capacity(L, N), true);
+    if (T == 0) { *out = base; return true; }
+    const int64_t max_tok = ((((int64_t)1 << 31) - 1) / (D * 4)) / L * L;
+    int64_t fl = ceil_div(base.fine_len, L) * L;
+    if (fl > max_tok) fl = max_tok;
+    if (fl < L) return false;
+    const int64_t nf = ceil_div(T, fl);
+    int64_t per = ceil_div(nf, base.n_coarse);
+    if (per * fl > max_tok) per = max_tok / fl;
+    if (per < 1) per = 1;
+    const int64_t nc = ceil_div(nf, per);
+    if (nf > 65535 || nc > 65535) return false;
+    out->fine_len = fl;
+    out->n_fine = (int)nf;
+    out->per_coarse = (int)per;
+    out->n_coarse = (int)nc;
+    return true;
+}
+
 // The plan of the forward entry points for block length L, N states.
 inline bool plan_for(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, Plan *out) {
     if (pair_path(L, N)) {
         *out = make_plan(batch, D, T, 0.45, pair_channels_of(N), kPairGroups, true);
         return true;
     }
+    if (pair_long(L, N) && pair_bidir()) return plan_long(batch, D, T, L, N, out);
     return plan_general(batch, D, T, L, out);
 }
 

@@ -1,6 +1,7 @@
 // launch_bidir.hip -- launchers of the register-resident bidirectional kernels
-// (bidir_pair_kernel: block lengths 1, 2, 4, 8, 16 at 4, 8, 16 or 32 states;
-// bidir_wave_kernel for separate reverse operands at 16 states).
+// (bidir_pair_kernel: block lengths 1, 2, 4, 8, 16 and multiples of 16 up to
+// 256 at 4, 8, 16 or 32 states; bidir_wave_kernel for separate reverse
+// operands at 16 states).
 // Compiled once per stream type (BDSSM_TIN = float, or uint16_t for bf16).
 #include "bdssm_launch.hpp"
 
@@ -25,24 +26,26 @@ template <typename Tin, int kN, int L, bool kInit, int kFuse>
 void launch_pair_k(dim3 g, const void *x, const void *dt, const void *B, const void *C,
                    const float *A, const float *Dskip, const float *hin, int64_t hin_bs,
                    int64_t hin_cs, void *y, float *bounds, float *hout, int64_t T, int64_t D,
-                   int64_t Tc, const float *h0_blocks, const Fuse &f, hipStream_t st) {
-    hipLaunchKernelGGL((bidir_pair_kernel<Tin, kN, L, kInit, kFuse>), g, dim3(4 * kWave), 0, st,
+                   int64_t Tc, const float *h0_blocks, const Fuse &f, hipStream_t st, int64_t Lr) {
+    hipLaunchKernelGGL((bidir_pair_kernel<Tin, kN, L, kInit, kFuse>), g, dim3(4 * kWave),
+                       L == 0 ? pair_long_lds(Lr) : 0, st,
                        (const Tin *)x, (const Tin *)dt, (const Tin *)B, (const Tin *)C, A, Dskip,
                        hin, hin_bs, hin_cs, (Tin *)y, bounds, hout, T, (int)D, Tc, h0_blocks,
-                       f.args<Tin>());
+                       f.args<Tin>(), (int)Lr);
 }
 
-// bidir_pair_kernel at kN states and block length L (shared operands)
+// bidir_pair_kernel at kN states and block length L (shared operands; L = 0:
+// long blocks of Lr tokens)
 template <typename Tin, int kN, int L>
 void launch_pair_L(const void *x, const void *dt, const void *B, const void *C, const float *A,
                    const float *Dskip, const float *hin, int64_t hin_bs, int64_t hin_cs, void *y,
                    float *bounds, float *hout, int64_t batch, int64_t T, int64_t D, int64_t Tc,
-                   int n_chunks, const float *h0_blocks, const Fuse &f, hipStream_t st) {
+                   int n_chunks, const float *h0_blocks, const Fuse &f, hipStream_t st, int64_t Lr = 0) {
     const dim3 g((unsigned)ceil_div(D, pair_channels<kN>()), (unsigned)n_chunks, (unsigned)batch);
     const bool fused = f.any();
 #define BDSSM_PAIR(INIT, FV)                                                                         \
     launch_pair_k<Tin, kN, L, INIT, FV>(g, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, T, D, \
-                                        Tc, h0_blocks, f, st)
+                                        Tc, h0_blocks, f, st, Lr)
     if (h0_blocks != nullptr) {
         if (fused) BDSSM_PAIR(true, 1);
         else BDSSM_PAIR(true, 0);
@@ -58,6 +61,11 @@ void launch_pair(int64_t L, const void *x, const void *dt, const void *B, const 
                  const float *Dskip, const float *hin, int64_t hin_bs, int64_t hin_cs, void *y,
                  float *bounds, float *hout, int64_t batch, int64_t T, int64_t D, int64_t Tc,
                  int n_chunks, const float *h0_blocks, const Fuse &f, hipStream_t st) {
+    if (L > kGroup) {
+        launch_pair_L<Tin, kN, 0>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc,
+                                  n_chunks, h0_blocks, f, st, L);
+        return;
+    }
     switch (L) {
     case 1: launch_pair_L<Tin, kN, 1>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
     case 2: launch_pair_L<Tin, kN, 2>(x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout, batch, T, D, Tc, n_chunks, h0_blocks, f, st); break;
@@ -92,10 +100,11 @@ void launch_bidir_L(const void *x, const void *dt, const void *B, const void *C,
 #undef BDSSM_BIDIR
 }
 
-// The bidirectional pass: for L | 16, bidir_pair_kernel at any supported
-// state count (shared operands), bidir_wave_kernel for separate reverse
-// operands at 16 states; everything else on block_bidir_kernel (Tc then a
-// multiple of L).
+// The bidirectional pass: for L | 16 and for multiples of 16 up to 256
+// (chunks of whole blocks, several blocks per row), bidir_pair_kernel at any
+// supported state count (shared operands); bidir_wave_kernel for separate
+// reverse operands at 16 states and L | 16; everything else on
+// block_bidir_kernel or block_split_kernel (Tc then a multiple of L).
 template <typename Tin>
 void launch_bidir(int64_t L, const void *x, const void *dt, const void *B, const void *C,
                   const float *A, const float *Dskip, const float *hin, int64_t hin_bs,
@@ -103,7 +112,10 @@ void launch_bidir(int64_t L, const void *x, const void *dt, const void *B, const
                   int64_t D, int64_t N, int64_t Tc, int n_chunks, hipStream_t st,
                   const float *h0_blocks, const Fuse &f) {
     const bool sep = f.dt_r != nullptr;
-    if (pair_path(L, N) && !sep && pair_bidir()) {
+    // long blocks: one block per row (block step, commit) stays on
+    // block_split_kernel / block_bidir_kernel, whose waves share the block
+    const bool lng = pair_long(L, N) && !(n_chunks == 1 && T == L);
+    if ((pair_path(L, N) || lng) && !sep && pair_bidir()) {
         with_states(N, [&](auto n) {
             launch_pair<Tin, decltype(n)::value>(L, x, dt, B, C, A, Dskip, hin, hin_bs, hin_cs, y, bounds, hout,
                                                  batch, T, D, Tc, n_chunks, h0_blocks, f, st);

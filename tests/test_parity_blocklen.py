@@ -231,6 +231,9 @@ def test_long_block_forward_segments(dev, seg, L, N_, dtype, variant, monkeypatc
     channels, 4 to 32 states, the fusions and separate reverse operands."""
     monkeypatch.setenv("BDSSM_CHUNK", "64")
     monkeypatch.setenv("BDSSM_SEG", seg)
+    # multiples of 16 take bidir_pair_kernel by default: keep them on
+    # block_bidir_kernel here
+    monkeypatch.setenv("BDSSM_BIDIR_KERNEL", "wave")
     batch, T, D = 2, {128: 512, 96: 384, 24: 480}[L], 70
     sid = 400 + QUAD.index((L, N_, dtype, variant))
     c = Case(batch, T, D, dtype, sid=sid, a_kind="random", n=N_)
@@ -312,3 +315,49 @@ def test_single_block_long(dev, split, L, N_, dtype, variant, monkeypatch):
     hco, yco = oracle.commit(ho, *oa[:6], want_y=True, **ok)
     close(yc, yco, TOL[dtype], label + " commit y")
     close(hc, hco, STATE_TOL, label + " commit state")
+
+
+PAIR_LONG = [  # (L, N, T, D, dtype, variant): bidir_pair_kernel's long-block mode
+    (32, 16, 512, 70, torch.bfloat16, "plain"),
+    (48, 16, 480, 33, torch.float32, "plain"),
+    (256, 16, 768, 96, torch.bfloat16, "plain"),
+    (128, 32, 512, 40, torch.float32, "plain"),
+    (64, 8, 512, 130, torch.bfloat16, "plain"),
+    (96, 4, 384, 200, torch.float32, "plain"),
+    (64, 16, 512, 70, torch.bfloat16, "fused"),
+    (32, 32, 256, 24, torch.bfloat16, "fused"),
+]
+
+
+@pytest.mark.parametrize("L,N_,T,D,dtype,variant", PAIR_LONG)
+def test_pair_long_blocks(dev, L, N_, T, D, dtype, variant, monkeypatch):
+    """Blocks longer than one 16-token group in the two-state forward (each
+    block's right-to-left state walk, then its groups left to right): both
+    training forms with several chunks, the prefill with y, ragged channel
+    tiles, 4 to 32 states and the fusions, against the oracle."""
+    monkeypatch.setenv("BDSSM_CHUNK", "64")
+    batch = 2
+    sid = 420 + PAIR_LONG.index((L, N_, T, D, dtype, variant))
+    c = Case(batch, T, D, dtype, sid=sid, a_kind="random", n=N_)
+    kw, ok = {}, {}
+    if variant == "fused":
+        c.dev["dt"] = synth.normal((batch, T, D), 1000 * sid + 1, "cpu", torch.float32, mean=-1.0,
+                                   std=0.5).to(dtype).to("cuda").contiguous()
+        bias = synth.normal((D,), 1000 * sid + 2, "cuda", torch.float32, std=0.3)
+        z = synth.normal((batch, T, D), 1000 * sid + 3, "cuda", dtype, std=2.0)
+        kw = dict(dt_bias=bias, dt_softplus=True, z=z)
+        ok = dict(dt_bias=to_np(bias), dt_softplus=True, z=synth.to_oracle(z))
+    y, bnd = m.train_scan(*c.args(), L, want_bounds=True, **kw)
+    h0b = synth.normal((batch, T // L + 1, D, N_), 1000 * sid + 4, "cuda")
+    yb = m.train_scan_blocks(*c.args(), L, h0b, **kw)
+    h, yp = m.prefill(*c.args(), L, want_y=True, **kw)
+    torch.cuda.synchronize()
+    oa = c.oracle_args()
+    yo, bo = oracle.train_scan(*oa, L, want_bounds=True, **ok)
+    ybo = oracle.train_blocks(*oa, L, to_np(h0b), **ok)
+    label = "pair long L=%d N=%d %s" % (L, N_, variant)
+    close(y, yo, TOL[dtype], label + " y")
+    close(bnd, bo, STATE_TOL, label + " h_bounds")
+    close(yb, ybo, TOL[dtype], label + " two-stream y")
+    close(yp, yo, TOL[dtype], label + " prefill y")
+    close(h, bo[:, -1], STATE_TOL, label + " prefill state")
