@@ -248,3 +248,44 @@ def test_training_backward_87m_variants_sampled(dev, variant):
     for k in ("dB", "dC"):
         got = to_np(g[k][:1])
         assert rel_err(got, r0[k]) < TOL_BF16, (k, worst(got, r0[k]))
+
+
+@pytest.mark.parametrize("variant", ["dstate32", "block64", "block256"])
+def test_training_87m_two_state_paths_sampled(dev, variant):
+    """The two-state kernels' other configurations at the 87M training shape:
+    d_state 32 (16 lanes per channel; forward and backward) and long blocks
+    (the forward's right-to-left state walk at L = 64 and 256; continuous and
+    two-stream forms).  Sampled channels over every batch row."""
+    wl = synth.WORKLOADS["train_87m"]
+    batch, D, T, sid = wl["batch"], wl["d_inner"], wl["seq"], wl["sid"]
+    n = 32 if variant == "dstate32" else N
+    L = {"dstate32": wl["block"], "block64": 64, "block256": 256}[variant]
+    print("[fullsize] train_87m (%s): batch %d, D %d, T %d, L %d, N %d" % (variant, batch, D, T, L, n),
+          flush=True)
+    x, dt, Bm, Cm = synth.stream(batch, T, D, n, sid, 0, torch.bfloat16, dev)
+    A, Dskip = synth.params(D, n, sid, "default", dev)
+    y, bnd = m.train_scan(x, dt, Bm, Cm, A, Dskip, L, want_bounds=True)
+    h0b = synth.normal((batch, T // L + 1, D, n), 1000 * sid + 77, dev)
+    yb = m.train_scan_blocks(x, dt, Bm, Cm, A, Dskip, L, h0b)
+    torch.cuda.synchronize()
+    ch = sample_channels(D, 8, 53)
+    idx = torch.as_tensor(ch, device=dev)
+    args = (ora(gather(x, ch)), ora(gather(dt, ch)), ora(Bm), ora(Cm), ora(A[idx]), ora(Dskip[idx]))
+    r = oracle.scan(*args, L, want_y=True, want_bounds=True)
+    check_y(to_np(gather(y, ch)), r["y"], "train_scan y")
+    gb = to_np(bnd[:, :, idx])
+    assert rel_err(gb, r["bounds"]) < STATE_TOL, worst(gb, r["bounds"])
+    ybo = oracle.train_blocks(*args, L, to_np(h0b[:, :, idx]))
+    check_y(to_np(gather(yb, ch)), ybo, "train_scan_blocks y")
+    if variant != "dstate32":
+        return
+    dy = synth.normal((batch, T, D), 1000 * sid + 78, dev, torch.bfloat16)
+    g = m.train_scan_bwd(x, dt, Bm, Cm, A, Dskip, L, bnd, dy, want_dh_init=True)
+    torch.cuda.synchronize()
+    rb = oracle.scan_bwd(*args, L, to_np(gather(dy, ch)))
+    for k in ("dx", "ddt"):
+        got = to_np(gather(g[k], ch))
+        assert rel_err(got, rb[k]) < TOL_BF16, (k, worst(got, rb[k]))
+    for k, got in (("dA", to_np(g["dA"][idx])), ("dDskip", to_np(g["dDskip"][idx])),
+                   ("dh0", to_np(g["dh_init"][:, idx]))):
+        assert rel_err(got, rb[k]) < STATE_TOL, (k, worst(got, rb[k]))
