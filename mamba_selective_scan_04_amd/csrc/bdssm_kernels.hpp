@@ -773,18 +773,19 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 // and with the step-size / gate fusions), for kN = 4, 8, 16 or 32 states:
 // lane = P * channel + state pair (states 2g, 2g + 1), P = kN / 2 lanes per
 // channel, CW = 64 / P channels per wave, 4 waves (4 CW channels) per
-// workgroup.  A 16-token group's decays then take 32 registers per lane at
-// any state count, and the kernel runs more waves per SIMD than
-// bidir_wave_kernel, whose four-state lanes wait on latency at two.
+// workgroup.  A 16-token group's decays and injections then take 64
+// registers per lane at any state count, and the kernel runs three waves per
+// SIMD, where bidir_wave_kernel's four-state lanes wait on latency at two.
 // Per group, staged as in bwd_pair_kernel (the x / dt (/ z) rows of the
 // wave's CW channels DMA'd into the wave's LDS slice, the group's B / C rows
 // shared by the workgroup, their loads spread over the waves; one group
 // ahead, widened in place by the lane that loaded them; one barrier per
 // group):
-//   forward, left to right: a = exp2(dt A'), hf = a hf + dt x B, the lane's
-//     output partial C . hf over its two states; the decays and dt x of the
-//     group stay in registers;
-//   reverse, right to left, reset where a block ends: hr = a hr + dt x B,
+//   forward, left to right: a = exp2(dt A'), u = dt x B, hf = a hf + u, the
+//     lane's output partial C . hf over its two states; the group's decays
+//     and injections stay in registers (64 per lane), so the reverse pass
+//     forms neither again;
+//   reverse, right to left, reset where a block ends: hr = a hr + u,
 //     partial += C . hr;
 //   output: the 16 tokens' partials are summed over the channel's P lanes by
 //     a reduce-scatter over the lane bits of g, from the top bit down (row
@@ -833,7 +834,7 @@ __device__ __forceinline__ void pair_scatter(const float (&in)[2 * kV], float (&
 }
 
 template <typename Tin, int kN, int L, bool kBlockInit, int kFuse = 0>
-__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 1 ? 2 : kN == 4 ? 3 : 4))) void bidir_pair_kernel(
+__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 1 ? 2 : 3))) void bidir_pair_kernel(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const Tin *__restrict__ Cm, const float *__restrict__ A, const float *__restrict__ Dskip,
     const float *hin, int64_t hin_bs, int64_t hin_cs,
@@ -1010,7 +1011,10 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
     auto group = [&](auto &xd, auto &bc, int k0, const float2 *hb, float2 hri = make_float2(0.f, 0.f),
                      bool gsb = true, bool geb = true) {
         const int nvalid = (len - k0 < G) ? len - k0 : G;   // uniform
-        float dA[G][2], dxs[G], ya[G];
+        // injections kept per state (at 4 states dt x per token: the
+        // registers of the wider x / dt staging leave no room for more)
+        constexpr int KU = kN == 4 ? 1 : 2;
+        float dA[G][2], us[G][KU], ya[G];
         // forward, left to right
 #pragma unroll
         for (int i = 0; i < G; ++i) {
@@ -1020,11 +1024,17 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
             const float dl = f32(xd[w][1][i][cl]);
             const float dxv = dl * f32(xd[w][0][i][cl]);
             const float2 bv = bcv(bc, 0, i), cv = bcv(bc, 1, i);
-            dxs[i] = dxv;
             const float a0 = fast_exp2(dl * a2[0]), a1 = fast_exp2(dl * a2[1]);
             dA[i][0] = a0; dA[i][1] = a1;
-            hf[0] = __builtin_fmaf(a0, hf[0], dxv * bv.x);
-            hf[1] = __builtin_fmaf(a1, hf[1], dxv * bv.y);
+            const float u0 = dxv * bv.x, u1 = dxv * bv.y;
+            if constexpr (KU == 2) {
+                us[i][0] = u0;
+                us[i][KU - 1] = u1;
+            } else {
+                us[i][0] = dxv;
+            }
+            hf[0] = __builtin_fmaf(a0, hf[0], u0);
+            hf[1] = __builtin_fmaf(a1, hf[1], u1);
             ya[i] = __builtin_fmaf(cv.y, hf[1], cv.x * hf[0]);
             if ((i + 1) % LB == 0 && geb && bounds != nullptr && i < nvalid && live) {
                 const int64_t kb = (t_begin + k0 + i + 1) / Lb;
@@ -1043,9 +1053,15 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
 #pragma unroll
         for (int i = G - 1; i >= 0; --i) {
             if (!kLong && (i + 1) % LB == 0) { hr[0] = hr[1] = 0.f; }
-            const float2 bv = bcv(bc, 0, i), cv = bcv(bc, 1, i);
-            hr[0] = __builtin_fmaf(dA[i][0], hr[0], dxs[i] * bv.x);
-            hr[1] = __builtin_fmaf(dA[i][1], hr[1], dxs[i] * bv.y);
+            const float2 cv = bcv(bc, 1, i);
+            float u0 = us[i][0], u1 = us[i][KU - 1];
+            if constexpr (KU == 1) {
+                const float2 bv = bcv(bc, 0, i);
+                u0 *= bv.x;
+                u1 *= bv.y;
+            }
+            hr[0] = __builtin_fmaf(dA[i][0], hr[0], u0);
+            hr[1] = __builtin_fmaf(dA[i][1], hr[1], u1);
             ya[i] = __builtin_fmaf(cv.y, hr[1], __builtin_fmaf(cv.x, hr[0], ya[i]));
             if ((i & 3) == 0) {
                 asm volatile("" : "+v"(hr[0]), "+v"(hr[1]), "+v"(ya[i]), "+v"(ya[i + 1]), "+v"(ya[i + 2]),

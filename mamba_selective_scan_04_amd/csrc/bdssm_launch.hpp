@@ -145,8 +145,9 @@ inline bool pair_bidir() {
     const char *v = getenv("BDSSM_BIDIR_KERNEL");
     return !(v != nullptr && v[0] == 'w');
 }
-// workgroups of bidir_pair_kernel resident at once (four per CU)
-constexpr int64_t kPairGroups = 4 * 256;
+// workgroups of bidir_pair_kernel resident at once (three per CU: its
+// registers)
+constexpr int64_t kPairGroups = 3 * 256;
 // Whether a bidirectional pass with shared operands can run bidir_pair_kernel
 // (block lengths dividing the 16-token group, any supported state count), and
 // its channels per workgroup (4 waves x 64 lanes / (N / 2) lanes per channel).
@@ -217,10 +218,11 @@ inline bool plan_general(int64_t batch, int64_t D, int64_t T, int64_t L, Plan *o
 // grid or the 32-bit offsets.
 inline int64_t pair_long_capacity(int64_t L, int64_t N) {
     // workgroups per CU by LDS: the rows (x, dt, z double-buffered per wave;
-    // B, C double-buffered) and the walk's saved states, at most four
+    // B, C double-buffered) and the walk's saved states, at most three (the
+    // registers)
     const int64_t lds = 1536 * (8 * kWave / N / 4) + 256 * N + (int64_t)pair_long_lds(L);
     int64_t per_cu = (160 * 1024) / lds;
-    if (per_cu > 4) per_cu = 4;
+    if (per_cu > 3) per_cu = 3;
     if (per_cu < 1) per_cu = 1;
     return per_cu * 256;
 }
