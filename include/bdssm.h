@@ -44,8 +44,18 @@
  * nothing; entry points that need scratch take a caller-supplied workspace
  * sized by bdssm_workspace_bytes().  There is no global mutable state, so
  * calls on different streams are independent as long as they do not share
- * output or workspace buffers.  Work is enqueued on `stream` (a hipStream_t;
- * NULL = the null stream) and returns without waiting.
+ * output or workspace buffers.  Work is enqueued on `stream` (NULL = the null
+ * stream) and returns without waiting.
+ *
+ * Entry points.  bdssm_prefill, bdssm_block_step, bdssm_commit,
+ * bdssm_train_scan and bdssm_full_scan take the scan's operands alone, and
+ * bdssm_workspace_bytes(shape, T) sizes a workspace that serves any of them
+ * at length T.  Each of the five has an _ex form with one more argument
+ * before the stream, a pointer to a bdssm_fusion or NULL (the plain call), and
+ * bdssm_workspace_bytes_op sizes the workspace of one entry point exactly,
+ * the backward ones included.  The two-stream training form, the backward
+ * entry points and the allocation-free prefill take the fusion argument
+ * directly.
  *
  * Errors.  Every entry point returns an int status (bdssm_status).  Argument
  * checks run on the host before any HIP call, so a rejected call enqueues
@@ -57,22 +67,31 @@
  * Limits of this version: T % block_len == 0; x, dt, B, C, z, the reverse
  * operands and y share one dtype.
  *   forward entry points: d_state 4, 8, 16 or 32 and block_len 1 to 256.
- *     d_state 16 with block_len 1, 2, 4, 8 or 16 runs the register-resident
- *     kernels; every other combination runs a kernel with one lane per
- *     channel that stages one block's forward output in LDS (256 * block_len
- *     bytes).  The pages fix neither size (the workloads here use 16 and 16)
- *     and name a dynamic block size as future work ([ZH] "未来方向").
- *   backward entry points: the same sizes.  d_state 16 with block_len 1, 2,
- *     4, 8 or 16 runs the register-resident kernels; every other combination
- *     runs a kernel with one lane per (channel, state) that keeps the forward
- *     state and the reverse adjoint at every 16-token segment start of a
- *     block in LDS and forms each segment again (slower, same results).
+ *     block_len 1, 2, 4, 8, 16, and the multiples of 16 from 32 to 256, run
+ *     register-resident kernels with two states per lane (the multiples of
+ *     16 walk each block's 16-token groups from the right first, for the
+ *     reverse state entering each group); every other block length runs a
+ *     kernel with one lane per channel that stages one block's forward
+ *     output in LDS (256 * block_len bytes).  With separate reverse
+ *     operands, d_state 16 with block_len 1, 2, 4, 8 or 16 runs a
+ *     register-resident kernel with four states per lane and every other
+ *     combination the one-lane kernel.  The pages fix neither size
+ *     (the workloads here use 16 and 16) and name a dynamic block size as
+ *     future work ([ZH] "未来方向").
+ *   backward entry points: the same sizes.  block_len 1, 2, 4, 8 or 16 at
+ *     any of the state counts, and the multiples of 16 at d_state 16, run
+ *     the register-resident kernel with two states per lane; every other
+ *     combination (and separate reverse operands) runs a kernel with one
+ *     lane per (channel, state) that keeps the forward state and the reverse
+ *     adjoint at every 16-token segment start of a block in LDS and forms
+ *     each segment again (slower, same results).
  */
 #ifndef BDSSM_H
 #define BDSSM_H
 
 #include <stddef.h>
 #include <stdint.h>
+#include <hip/hip_runtime_api.h>   /* hipStream_t (define __HIP_PLATFORM_AMD__ when not built by hipcc) */
 
 #ifdef __cplusplus
 extern "C" {
@@ -91,7 +110,7 @@ typedef enum {
 
 typedef enum { BDSSM_F32 = 0, BDSSM_BF16 = 1 } bdssm_dtype;
 
-/* Which entry point a workspace is sized for. */
+/* Which entry point a workspace is sized for (bdssm_workspace_bytes_op). */
 typedef enum {
     BDSSM_OP_PREFILL = 0,     /* bdssm_prefill */
     BDSSM_OP_TRAIN = 1,       /* bdssm_train_scan */
@@ -154,13 +173,17 @@ typedef struct {
  *   y       NULL (state only), or [batch,t_ctx,D] out: the clean-stream output,
  *           forward plus reverse within each L-block, i.e. what committing the
  *           blocks one at a time with y would emit.  C may be NULL iff y is.
- *   ws      workspace of ws_bytes >= bdssm_workspace_bytes(shape, t_ctx,
- *           BDSSM_OP_PREFILL).
+ *   ws      workspace of ws_bytes >= bdssm_workspace_bytes_op(shape, t_ctx,
+ *           BDSSM_OP_PREFILL) (bdssm_workspace_bytes(shape, t_ctx) is enough).
  */
 int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const void *dt,
                   const void *B, const void *C, const float *A, const float *Dskip,
                   const float *h_init, float *h_cache, void *y, void *ws, size_t ws_bytes,
-                  const bdssm_fusion *fusion, void *stream);
+                  hipStream_t stream);
+int bdssm_prefill_ex(const bdssm_shape *shape, int64_t t_ctx, const void *x, const void *dt,
+                     const void *B, const void *C, const float *A, const float *Dskip,
+                     const float *h_init, float *h_cache, void *y, void *ws, size_t ws_bytes,
+                     const bdssm_fusion *fusion, hipStream_t stream);
 
 /*
  * bdssm_prefill for callers that cannot allocate device memory: code under
@@ -170,7 +193,7 @@ int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const 
  * device it runs on, BDSSM_SCRATCH_BYTES long, for the life of the process.
  * The call allocates nothing.
  *   Limit: returns BDSSM_ERR_WORKSPACE, and enqueues nothing, when
- *   bdssm_workspace_bytes(shape, t_ctx, BDSSM_OP_PREFILL) exceeds
+ *   bdssm_workspace_bytes_op(shape, t_ctx, BDSSM_OP_PREFILL) exceeds
  *   BDSSM_SCRATCH_BYTES (every plan at d_state <= 16 fits, for any context
  *   length; at d_state 32 only batch * t_ctx * d_inner up to about 4.6e6).
  *   Concurrency: every call on one device shares that device's array; calls
@@ -184,7 +207,7 @@ int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const 
 int bdssm_prefill_noalloc(const bdssm_shape *shape, int64_t t_ctx, const void *x, const void *dt,
                           const void *B, const void *C, const float *A, const float *Dskip,
                           const float *h_init, float *h_cache, void *y, const bdssm_fusion *fusion,
-                          void *stream);
+                          hipStream_t stream);
 
 /*
  * One denoising step on the active block (exactly L tokens) [ABS], [DE-M]:
@@ -194,7 +217,10 @@ int bdssm_prefill_noalloc(const bdssm_shape *shape, int64_t t_ctx, const void *x
  */
 int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void *x,
                      const void *dt, const void *B, const void *C, const float *A,
-                     const float *Dskip, void *y, const bdssm_fusion *fusion, void *stream);
+                     const float *Dskip, void *y, hipStream_t stream);
+int bdssm_block_step_ex(const bdssm_shape *shape, const float *h_cache, const void *x,
+                        const void *dt, const void *B, const void *C, const float *A,
+                        const float *Dskip, void *y, const bdssm_fusion *fusion, hipStream_t stream);
 
 /*
  * Commit a finished block (its final clean inputs, L tokens) [DE-M]: the
@@ -205,7 +231,10 @@ int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void 
  */
 int bdssm_commit(const bdssm_shape *shape, float *h_cache, const void *x, const void *dt,
                  const void *B, const void *C, const float *A, const float *Dskip, void *y,
-                 const bdssm_fusion *fusion, void *stream);
+                 hipStream_t stream);
+int bdssm_commit_ex(const bdssm_shape *shape, float *h_cache, const void *x, const void *dt,
+                    const void *B, const void *C, const float *A, const float *Dskip, void *y,
+                    const bdssm_fusion *fusion, hipStream_t stream);
 
 /*
  * All-block training form over T tokens [DE-M]: the forward scan runs over
@@ -214,12 +243,17 @@ int bdssm_commit(const bdssm_shape *shape, float *h_cache, const void *x, const 
  *   y        [batch,T,D] out.
  *   h_bounds NULL, or [batch,T/L+1,D,N] out: the forward state before token 0
  *            and after every L-th token (the per-block prefix caches).
- *   ws       ws_bytes >= bdssm_workspace_bytes(shape, T, BDSSM_OP_TRAIN).
+ *   ws       ws_bytes >= bdssm_workspace_bytes_op(shape, T, BDSSM_OP_TRAIN)
+ *            (bdssm_workspace_bytes(shape, T) is enough).
  */
 int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
                      const void *B, const void *C, const float *A, const float *Dskip,
                      const float *h_init, void *y, float *h_bounds, void *ws, size_t ws_bytes,
-                     const bdssm_fusion *fusion, void *stream);
+                     hipStream_t stream);
+int bdssm_train_scan_ex(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
+                        const void *B, const void *C, const float *A, const float *Dskip,
+                        const float *h_init, void *y, float *h_bounds, void *ws, size_t ws_bytes,
+                        const bdssm_fusion *fusion, hipStream_t stream);
 
 /*
  * Two-stream all-block training form, noisy stream [DE-M]: downstream block
@@ -238,7 +272,7 @@ int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const v
 int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
                             const void *B, const void *C, const float *A, const float *Dskip,
                             const float *h0_blocks, void *y, const bdssm_fusion *fusion,
-                            void *stream);
+                            hipStream_t stream);
 
 /*
  * Backward of bdssm_train_scan (reverse-mode gradients).  The all-block
@@ -259,7 +293,7 @@ int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, 
  *   dx, ddt  [batch, T, D] stream dtype;   dB, dC [batch, T, N] stream dtype;
  *   dA [D, N] fp32 (summed over batch and tokens);  dDskip [D] fp32;
  *   dh_init  NULL, or [batch, D, N] fp32: dJ/dh_init.
- *   ws       ws_bytes >= bdssm_workspace_bytes(shape, T, BDSSM_OP_TRAIN_BWD).
+ *   ws       ws_bytes >= bdssm_workspace_bytes_op(shape, T, BDSSM_OP_TRAIN_BWD).
  * Sums over channels (dB, dC), batch and tokens (dA, dDskip) are taken in a
  * fixed order: results are bitwise reproducible for a given shape.
  * fusion: the same bdssm_fusion as the forward call, or NULL.  With dt_bias /
@@ -296,7 +330,7 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
                          const float *h_bounds, const void *dy, const float *d_bounds, void *dx,
                          void *ddt, void *dB, void *dC, float *dA, float *dDskip, float *dh_init,
                          void *ws, size_t ws_bytes, const bdssm_fusion *fusion,
-                         bdssm_fusion_grads *grads, void *stream);
+                         bdssm_fusion_grads *grads, hipStream_t stream);
 
 /*
  * Backward of bdssm_train_scan_blocks (the noisy stream of the two-stream
@@ -307,14 +341,14 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
  *             forward call.
  *   dy, dx, ddt, dB, dC, dA, dDskip, fusion, grads as in bdssm_train_scan_bwd.
  *   dh0_blocks NULL, or [batch, T/L+1, D, N] fp32 out (entry T/L is zero).
- *   ws        ws_bytes >= bdssm_workspace_bytes(shape, T, BDSSM_OP_BLOCKS_BWD).
+ *   ws        ws_bytes >= bdssm_workspace_bytes_op(shape, T, BDSSM_OP_BLOCKS_BWD).
  */
 int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
                                 const void *B, const void *C, const float *A, const float *Dskip,
                                 const float *h0_blocks, const void *dy, void *dx, void *ddt,
                                 void *dB, void *dC, float *dA, float *dDskip, float *dh0_blocks,
                                 void *ws, size_t ws_bytes, const bdssm_fusion *fusion,
-                                bdssm_fusion_grads *grads, void *stream);
+                                bdssm_fusion_grads *grads, hipStream_t stream);
 
 /*
  * Baseline: the full-sequence bidirectional scan of the earlier diffusion
@@ -322,15 +356,24 @@ int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void 
  * single block of length T (reverse over the whole sequence), forward from
  * zero.  block_len is ignored.
  *   y   [batch,T,D] out.
- *   ws  ws_bytes >= bdssm_workspace_bytes(shape, T, BDSSM_OP_FULL).
+ *   ws  ws_bytes >= bdssm_workspace_bytes_op(shape, T, BDSSM_OP_FULL)
+ *       (bdssm_workspace_bytes(shape, T) is enough).
  */
 int bdssm_full_scan(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
                     const void *B, const void *C, const float *A, const float *Dskip, void *y,
-                    void *ws, size_t ws_bytes, const bdssm_fusion *fusion, void *stream);
+                    void *ws, size_t ws_bytes, hipStream_t stream);
+int bdssm_full_scan_ex(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
+                       const void *B, const void *C, const float *A, const float *Dskip, void *y,
+                       void *ws, size_t ws_bytes, const bdssm_fusion *fusion, hipStream_t stream);
 
-/* Workspace bytes the given entry point needs at sequence length T (0 if none;
- * (size_t)-1 if the shape is invalid). */
-size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T, int op);
+/* Workspace bytes that serve bdssm_prefill, bdssm_train_scan and
+ * bdssm_full_scan (and their _ex forms) at sequence length T: the largest of
+ * the three (0 if none needs one; (size_t)-1 if the shape is invalid). */
+size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T);
+
+/* Workspace bytes the entry point op (bdssm_op) needs at sequence length T (0
+ * if none; (size_t)-1 if the shape or op is invalid). */
+size_t bdssm_workspace_bytes_op(const bdssm_shape *shape, int64_t T, int op);
 
 /* Static, human-readable text for a status code. */
 const char *bdssm_status_str(int status);

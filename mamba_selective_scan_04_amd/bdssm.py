@@ -34,10 +34,13 @@ BF16 = 1
 OP_PREFILL, OP_TRAIN, OP_FULL, OP_TRAIN_BWD, OP_BLOCKS_BWD = 0, 1, 2, 3, 4
 OP_TRAIN_BWD_REV, OP_BLOCKS_BWD_REV = 5, 6      # the backward with separate reverse operands
 SCRATCH_BYTES = 72 << 20    # BDSSM_SCRATCH_BYTES: the scratch array of bdssm_prefill_noalloc
-EXPORTS = ("bdssm_prefill", "bdssm_prefill_noalloc", "bdssm_block_step", "bdssm_commit", "bdssm_train_scan",
-           "bdssm_train_scan_blocks", "bdssm_full_scan", "bdssm_train_scan_bwd",
-           "bdssm_train_scan_blocks_bwd", "bdssm_workspace_bytes", "bdssm_status_str",
-           "bdssm_version")
+# the five entry points of the scan, each also in an _ex form that takes the
+# fusions (the binding calls the plain form when no fusion is asked for)
+PLAIN = ("bdssm_prefill", "bdssm_block_step", "bdssm_commit", "bdssm_train_scan", "bdssm_full_scan")
+EXPORTS = PLAIN + tuple(f + "_ex" for f in PLAIN) + (
+    "bdssm_prefill_noalloc", "bdssm_train_scan_blocks", "bdssm_train_scan_bwd",
+    "bdssm_train_scan_blocks_bwd", "bdssm_workspace_bytes", "bdssm_workspace_bytes_op",
+    "bdssm_status_str", "bdssm_version")
 
 
 class BdssmError(RuntimeError):
@@ -80,22 +83,24 @@ def load():
     P, I, S = ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(Shape)
     Z = ctypes.c_size_t
     F = ctypes.POINTER(Fusion)
-    lib.bdssm_prefill.argtypes = [S, I, P, P, P, P, P, P, P, P, P, P, Z, F, P]
+    lib.bdssm_prefill.argtypes = [S, I, P, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.bdssm_block_step.argtypes = [S, P, P, P, P, P, P, P, P, P]
+    lib.bdssm_commit.argtypes = [S, P, P, P, P, P, P, P, P, P]
+    lib.bdssm_train_scan.argtypes = [S, I, P, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.bdssm_full_scan.argtypes = [S, I, P, P, P, P, P, P, P, P, Z, P]
+    for f in PLAIN:   # the _ex forms: the fusion before the stream
+        getattr(lib, f + "_ex").argtypes = getattr(lib, f).argtypes[:-1] + [F, P]
     lib.bdssm_prefill_noalloc.argtypes = [S, I, P, P, P, P, P, P, P, P, P, F, P]
-    lib.bdssm_block_step.argtypes = [S, P, P, P, P, P, P, P, P, F, P]
-    lib.bdssm_commit.argtypes = [S, P, P, P, P, P, P, P, P, F, P]
-    lib.bdssm_train_scan.argtypes = [S, I, P, P, P, P, P, P, P, P, P, P, Z, F, P]
-    lib.bdssm_full_scan.argtypes = [S, I, P, P, P, P, P, P, P, P, Z, F, P]
     lib.bdssm_train_scan_blocks.argtypes = [S, I, P, P, P, P, P, P, P, P, F, P]
     G = ctypes.POINTER(FusionGrads)
     lib.bdssm_train_scan_bwd.argtypes = [S, I] + [P] * 17 + [Z, F, G, P]
     lib.bdssm_train_scan_blocks_bwd.argtypes = [S, I] + [P] * 16 + [Z, F, G, P]
-    for f in ("bdssm_prefill", "bdssm_prefill_noalloc", "bdssm_block_step", "bdssm_commit", "bdssm_train_scan",
-              "bdssm_train_scan_blocks", "bdssm_full_scan", "bdssm_train_scan_bwd",
-              "bdssm_train_scan_blocks_bwd", "bdssm_version"):
+    for f in EXPORTS:
         getattr(lib, f).restype = ctypes.c_int
-    lib.bdssm_workspace_bytes.argtypes = [S, I, ctypes.c_int]
+    lib.bdssm_workspace_bytes.argtypes = [S, I]
     lib.bdssm_workspace_bytes.restype = ctypes.c_size_t
+    lib.bdssm_workspace_bytes_op.argtypes = [S, I, ctypes.c_int]
+    lib.bdssm_workspace_bytes_op.restype = ctypes.c_size_t
     lib.bdssm_status_str.argtypes = [ctypes.c_int]
     lib.bdssm_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -151,6 +156,21 @@ def _raise(fn, rc):
         raise BdssmError(fn, rc, status_str(rc))
 
 
+def _form(name, fz, args):
+    """(function, its name, full arguments) of one of the five scan entry
+    points: the plain form without a fusion, the _ex form with one."""
+    if fz is None:
+        return getattr(load(), name), name, tuple(args) + (_stream(),)
+    return getattr(load(), name + "_ex"), name + "_ex", tuple(args) + (fz, _stream())
+
+
+def _call(name, fz, *args):
+    fn, fname, full = _form(name, fz, args)
+    rc = fn(*full)
+    _raise(fname, rc)
+    return rc
+
+
 def _streams(x, dt, B, C, A, Dskip, need_c=True):
     if x.dim() != 3:
         raise ValueError("x must be [batch, T, D]")
@@ -194,9 +214,14 @@ def _fusion(x, D, dt_bias=None, dt_softplus=False, z=None, rev=None):
     return ctypes.pointer(f)
 
 
-def workspace_bytes(batch, d_inner, T, op, block_len=16, d_state=16, dtype=torch.bfloat16):
+def workspace_bytes(batch, d_inner, T, op=None, block_len=16, d_state=16, dtype=torch.bfloat16):
+    """Workspace bytes of the entry point op (OP_*) at length T; op None: a
+    workspace that serves prefill, train_scan and full_scan."""
     s = _shape(batch, d_inner, d_state, block_len, BF16 if dtype == torch.bfloat16 else F32)
-    n = load().bdssm_workspace_bytes(ctypes.byref(s), T, op)
+    if op is None:
+        n = load().bdssm_workspace_bytes(ctypes.byref(s), T)
+    else:
+        n = load().bdssm_workspace_bytes_op(ctypes.byref(s), T, op)
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid shape for workspace query")
     return n
@@ -224,10 +249,8 @@ def prefill(x, dt, B, C, A, Dskip, block_len, h_init=None, h_cache=None, y=None,
     if ws is None:
         ws = _workspace(workspace_bytes(batch, D, T, OP_PREFILL, block_len, N, x.dtype), x.device)
     fz = _fusion(x, D, **fusion)
-    rc = load().bdssm_prefill(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A), _p(Dskip),
-                              _p(h_init), _p(h_cache), _p(y), _p(ws),
-                              0 if ws is None else ws.numel(), fz, _stream())
-    _raise("bdssm_prefill", rc)
+    _call("bdssm_prefill", fz, ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A), _p(Dskip),
+               _p(h_init), _p(h_cache), _p(y), _p(ws), 0 if ws is None else ws.numel())
     return h_cache, y
 
 
@@ -263,9 +286,8 @@ def block_step(h_cache, x, dt, B, C, A, Dskip, y=None, **fusion):
     _check(y, "y", x.dtype, (batch, T, D))
     s = _shape(batch, D, N, T, code)
     fz = _fusion(x, D, **fusion)
-    rc = load().bdssm_block_step(ctypes.byref(s), _p(h_cache), _p(x), _p(dt), _p(B), _p(C), _p(A),
-                                 _p(Dskip), _p(y), fz, _stream())
-    _raise("bdssm_block_step", rc)
+    _call("bdssm_block_step", fz, ctypes.byref(s), _p(h_cache), _p(x), _p(dt), _p(B), _p(C), _p(A),
+          _p(Dskip), _p(y))
     return y
 
 
@@ -279,9 +301,8 @@ def commit(h_cache, x, dt, B, C, A, Dskip, want_y=False, y=None, **fusion):
     _check(y, "y", x.dtype, (batch, T, D))
     s = _shape(batch, D, N, T, code)
     fz = _fusion(x, D, **fusion)
-    rc = load().bdssm_commit(ctypes.byref(s), _p(h_cache), _p(x), _p(dt), _p(B), _p(C), _p(A),
-                             _p(Dskip), _p(y), fz, _stream())
-    _raise("bdssm_commit", rc)
+    _call("bdssm_commit", fz, ctypes.byref(s), _p(h_cache), _p(x), _p(dt), _p(B), _p(C), _p(A),
+          _p(Dskip), _p(y))
     return h_cache, y
 
 
@@ -301,10 +322,8 @@ def train_scan(x, dt, B, C, A, Dskip, block_len, h_init=None, want_bounds=False,
     if ws is None:
         ws = _workspace(workspace_bytes(batch, D, T, OP_TRAIN, block_len, N, x.dtype), x.device)
     fz = _fusion(x, D, **fusion)
-    rc = load().bdssm_train_scan(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A),
-                                 _p(Dskip), _p(h_init), _p(y), _p(h_bounds), _p(ws),
-                                 0 if ws is None else ws.numel(), fz, _stream())
-    _raise("bdssm_train_scan", rc)
+    _call("bdssm_train_scan", fz, ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A),
+          _p(Dskip), _p(h_init), _p(y), _p(h_bounds), _p(ws), 0 if ws is None else ws.numel())
     return y, h_bounds
 
 
@@ -334,9 +353,8 @@ def full_scan(x, dt, B, C, A, Dskip, y=None, ws=None, **fusion):
     if ws is None:
         ws = _workspace(workspace_bytes(batch, D, T, OP_FULL, 1, N, x.dtype), x.device)
     fz = _fusion(x, D, **fusion)
-    rc = load().bdssm_full_scan(ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A), _p(Dskip),
-                                _p(y), _p(ws), 0 if ws is None else ws.numel(), fz, _stream())
-    _raise("bdssm_full_scan", rc)
+    _call("bdssm_full_scan", fz, ctypes.byref(s), T, _p(x), _p(dt), _p(B), _p(C), _p(A), _p(Dskip),
+          _p(y), _p(ws), 0 if ws is None else ws.numel())
     return y
 
 
@@ -364,10 +382,9 @@ def bind_block_step(h_cache, x, dt, B, C, A, Dskip, y, **fusion):
     _check(y, "y", x.dtype, (batch, T, D))
     s = _shape(batch, D, N, T, code)
     fz = _fusion(x, D, **fusion)
-    args = (ctypes.byref(s), _p(h_cache), _p(x), _p(dt), _p(B), _p(C), _p(A), _p(Dskip), _p(y), fz,
-            _stream())
-    return BoundCall(load().bdssm_block_step, "bdssm_block_step", args,
-                     (s, fz, h_cache, x, dt, B, C, A, Dskip, y, fusion))
+    args = (ctypes.byref(s), _p(h_cache), _p(x), _p(dt), _p(B), _p(C), _p(A), _p(Dskip), _p(y))
+    fn, name, args = _form("bdssm_block_step", fz, args)
+    return BoundCall(fn, name, args, (s, fz, h_cache, x, dt, B, C, A, Dskip, y, fusion))
 
 
 def bind_commit(h_cache, x, dt, B, C, A, Dskip, y=None, **fusion):
@@ -377,10 +394,9 @@ def bind_commit(h_cache, x, dt, B, C, A, Dskip, y=None, **fusion):
     _check(y, "y", x.dtype, (batch, T, D))
     s = _shape(batch, D, N, T, code)
     fz = _fusion(x, D, **fusion)
-    args = (ctypes.byref(s), _p(h_cache), _p(x), _p(dt), _p(B), _p(C), _p(A), _p(Dskip), _p(y), fz,
-            _stream())
-    return BoundCall(load().bdssm_commit, "bdssm_commit", args,
-                     (s, fz, h_cache, x, dt, B, C, A, Dskip, y, fusion))
+    args = (ctypes.byref(s), _p(h_cache), _p(x), _p(dt), _p(B), _p(C), _p(A), _p(Dskip), _p(y))
+    fn, name, args = _form("bdssm_commit", fz, args)
+    return BoundCall(fn, name, args, (s, fz, h_cache, x, dt, B, C, A, Dskip, y, fusion))
 
 
 def _grad_outputs(x, D, N):

@@ -33,7 +33,7 @@ using namespace bdssm_host;
 
 namespace {
 
-constexpr int kVersion = 10600;   // 1.6.0
+constexpr int kVersion = 10700;   // 1.7.0
 
 // ---------------------------------------------------------------- checking
 
@@ -361,7 +361,7 @@ const char *bdssm_status_str(int status) {
     }
 }
 
-size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T, int op) {
+size_t bdssm_workspace_bytes_op(const bdssm_shape *shape, int64_t T, int op) {
     if (check_shape(shape) != BDSSM_OK || T < 0 || T % shape->block_len != 0) return (size_t)-1;
     if (op < BDSSM_OP_PREFILL || op > BDSSM_OP_BLOCKS_BWD_REV) return (size_t)-1;
     const int64_t batch = shape->batch, D = shape->d_inner;
@@ -399,10 +399,20 @@ size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T, int op) {
     return layout_ws(nullptr, batch, D, shape->d_state, T, p, op).bytes;
 }
 
-int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const void *dt,
+size_t bdssm_workspace_bytes(const bdssm_shape *shape, int64_t T) {
+    size_t n = 0;
+    for (int op : {BDSSM_OP_PREFILL, BDSSM_OP_TRAIN, BDSSM_OP_FULL}) {
+        const size_t m = bdssm_workspace_bytes_op(shape, T, op);
+        if (m == (size_t)-1) return m;
+        n = m > n ? m : n;
+    }
+    return n;
+}
+
+int bdssm_prefill_ex(const bdssm_shape *shape, int64_t t_ctx, const void *x, const void *dt,
                   const void *B, const void *C, const float *A, const float *Dskip,
                   const float *h_init, float *h_cache, void *y, void *ws, size_t ws_bytes,
-                  const bdssm_fusion *fusion, void *stream) {
+                  const bdssm_fusion *fusion, hipStream_t stream) {
     PrefillPlan pp;
     int rc = prefill_prepare(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, h_cache, y, ws, ws_bytes, fusion,
                              &pp);
@@ -417,13 +427,13 @@ int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const 
             return BDSSM_ERR_ALIAS;
     }
     return prefill_launch(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, h_cache, y, ws, pp,
-                          static_cast<hipStream_t>(stream));
+                          stream);
 }
 
 int bdssm_prefill_noalloc(const bdssm_shape *shape, int64_t t_ctx, const void *x, const void *dt,
                           const void *B, const void *C, const float *A, const float *Dskip,
                           const float *h_init, float *h_cache, void *y, const bdssm_fusion *fusion,
-                          void *stream) {
+                          hipStream_t stream) {
     PrefillPlan pp;
     int rc = prefill_prepare(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, h_cache, y, nullptr, 0, fusion, &pp);
     if (rc || pp.empty) return rc;
@@ -434,12 +444,12 @@ int bdssm_prefill_noalloc(const bdssm_shape *shape, int64_t t_ctx, const void *x
         if (rc) return rc;
     }
     return prefill_launch(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, h_cache, y, ws, pp,
-                          static_cast<hipStream_t>(stream));
+                          stream);
 }
 
-int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void *x,
+int bdssm_block_step_ex(const bdssm_shape *shape, const float *h_cache, const void *x,
                      const void *dt, const void *B, const void *C, const float *A,
-                     const float *Dskip, void *y, const bdssm_fusion *fusion, void *stream) {
+                     const float *Dskip, void *y, const bdssm_fusion *fusion, hipStream_t stream) {
     int rc = check_shape(shape);
     if (rc) return rc;
     const int64_t L = shape->block_len;
@@ -456,7 +466,7 @@ int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void 
     rc = check_fusion(fusion, shape, L, true, {Range{y, (size_t)batch * L * D * esize(shape)}});
     if (rc) return rc;
     const Fuse f = resolve_fusion(fusion, true);
-    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipStream_t st = stream;
     (void)hipGetLastError();
     if (block_lane_path(L, f, true)) {
         if (shape->dtype == BDSSM_BF16)
@@ -471,9 +481,9 @@ int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void 
     return launch_status();
 }
 
-int bdssm_commit(const bdssm_shape *shape, float *h_cache, const void *x, const void *dt,
+int bdssm_commit_ex(const bdssm_shape *shape, float *h_cache, const void *x, const void *dt,
                  const void *B, const void *C, const float *A, const float *Dskip, void *y,
-                 const bdssm_fusion *fusion, void *stream) {
+                 const bdssm_fusion *fusion, hipStream_t stream) {
     int rc = check_shape(shape);
     if (rc) return rc;
     const int64_t L = shape->block_len;
@@ -493,7 +503,7 @@ int bdssm_commit(const bdssm_shape *shape, float *h_cache, const void *x, const 
                                                  Range{y, (size_t)batch * L * D * esize(shape)}});
     if (rc) return rc;
     const Fuse f = resolve_fusion(fusion, with_y);
-    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipStream_t st = stream;
     (void)hipGetLastError();
     if (block_lane_path(L, f, with_y)) {
         if (shape->dtype == BDSSM_BF16)
@@ -510,10 +520,10 @@ int bdssm_commit(const bdssm_shape *shape, float *h_cache, const void *x, const 
     return launch_status();
 }
 
-int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
+int bdssm_train_scan_ex(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
                      const void *B, const void *C, const float *A, const float *Dskip,
                      const float *h_init, void *y, float *h_bounds, void *ws, size_t ws_bytes,
-                     const bdssm_fusion *fusion, void *stream) {
+                     const bdssm_fusion *fusion, hipStream_t stream) {
     int rc = check_shape(shape);
     if (rc) return rc;
     if (T < 0 || T % shape->block_len != 0) return BDSSM_ERR_SHAPE;
@@ -536,7 +546,7 @@ int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const v
                                                Range{h_bounds, nbnd}, Range{T > 0 ? ws : nullptr, probe.bytes}});
     if (rc) return rc;
     const Fuse f = resolve_fusion(fusion, true);
-    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipStream_t st = stream;
     if (T == 0) {
         if (h_bounds == nullptr) return BDSSM_OK;
         return copy_or_zero(h_init, h_bounds, batch * D * N, st);
@@ -554,7 +564,7 @@ int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const v
 int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
                             const void *B, const void *C, const float *A, const float *Dskip,
                             const float *h0_blocks, void *y, const bdssm_fusion *fusion,
-                            void *stream) {
+                            hipStream_t stream) {
     int rc = check_shape(shape);
     if (rc) return rc;
     if (T < 0 || T % shape->block_len != 0) return BDSSM_ERR_SHAPE;
@@ -577,7 +587,7 @@ int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, 
     if (!blocks_plan(batch, D, T, L, N, &tc, &nc, pair ? pair_channels_of(N) : kWave,
                      pair ? (pair_path(L, N) ? kPairGroups : pair_long_capacity(L, N)) : kCoarseGroups))
         return BDSSM_ERR_SHAPE;
-    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipStream_t st = stream;
     (void)hipGetLastError();
     if (shape->dtype == BDSSM_BF16)
         launch_bidir<uint16_t>(L, x, dt, B, C, A, Dskip, nullptr, 0, 0, y, nullptr, nullptr, batch, T, D, N, tc, (int)nc, st, h0_blocks, f);
@@ -586,9 +596,9 @@ int bdssm_train_scan_blocks(const bdssm_shape *shape, int64_t T, const void *x, 
     return launch_status();
 }
 
-int bdssm_full_scan(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
+int bdssm_full_scan_ex(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
                     const void *B, const void *C, const float *A, const float *Dskip, void *y,
-                    void *ws, size_t ws_bytes, const bdssm_fusion *fusion, void *stream) {
+                    void *ws, size_t ws_bytes, const bdssm_fusion *fusion, hipStream_t stream) {
     if (shape == nullptr) return BDSSM_ERR_NULL;
     // the block length does not apply; validate the rest with L = 1
     bdssm_shape s1 = *shape;
@@ -612,11 +622,46 @@ int bdssm_full_scan(const bdssm_shape *shape, int64_t T, const void *x, const vo
     if (rc) return rc;
     const Fuse f = resolve_fusion(fusion, true);
     const Workspace w = layout_ws(ws, batch, D, s1.d_state, T, p, BDSSM_OP_FULL);
-    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipStream_t st = stream;
     (void)hipGetLastError();
     if (s1.dtype == BDSSM_BF16) run_full<uint16_t>(&s1, T, x, dt, B, C, A, Dskip, y, w, p, st, f);
     else run_full<float>(&s1, T, x, dt, B, C, A, Dskip, y, w, p, st, f);
     return launch_status();
+}
+
+// The five entry points without the fusions: the same calls with fusion NULL.
+int bdssm_prefill(const bdssm_shape *shape, int64_t t_ctx, const void *x, const void *dt,
+                  const void *B, const void *C, const float *A, const float *Dskip,
+                  const float *h_init, float *h_cache, void *y, void *ws, size_t ws_bytes,
+                  hipStream_t stream) {
+    return bdssm_prefill_ex(shape, t_ctx, x, dt, B, C, A, Dskip, h_init, h_cache, y, ws, ws_bytes, nullptr,
+                            stream);
+}
+
+int bdssm_block_step(const bdssm_shape *shape, const float *h_cache, const void *x, const void *dt,
+                     const void *B, const void *C, const float *A, const float *Dskip, void *y,
+                     hipStream_t stream) {
+    return bdssm_block_step_ex(shape, h_cache, x, dt, B, C, A, Dskip, y, nullptr, stream);
+}
+
+int bdssm_commit(const bdssm_shape *shape, float *h_cache, const void *x, const void *dt,
+                 const void *B, const void *C, const float *A, const float *Dskip, void *y,
+                 hipStream_t stream) {
+    return bdssm_commit_ex(shape, h_cache, x, dt, B, C, A, Dskip, y, nullptr, stream);
+}
+
+int bdssm_train_scan(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
+                     const void *B, const void *C, const float *A, const float *Dskip,
+                     const float *h_init, void *y, float *h_bounds, void *ws, size_t ws_bytes,
+                     hipStream_t stream) {
+    return bdssm_train_scan_ex(shape, T, x, dt, B, C, A, Dskip, h_init, y, h_bounds, ws, ws_bytes, nullptr,
+                               stream);
+}
+
+int bdssm_full_scan(const bdssm_shape *shape, int64_t T, const void *x, const void *dt,
+                    const void *B, const void *C, const float *A, const float *Dskip, void *y,
+                    void *ws, size_t ws_bytes, hipStream_t stream) {
+    return bdssm_full_scan_ex(shape, T, x, dt, B, C, A, Dskip, y, ws, ws_bytes, nullptr, stream);
 }
 
 }  // extern "C"
@@ -778,7 +823,7 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
                          const float *h_bounds, const void *dy, const float *d_bounds, void *dx,
                          void *ddt, void *dB, void *dC, float *dA, float *dDskip, float *dh_init,
                          void *ws, size_t ws_bytes, const bdssm_fusion *fusion,
-                         bdssm_fusion_grads *grads, void *stream) {
+                         bdssm_fusion_grads *grads, hipStream_t stream) {
     const size_t nstate = shape ? (size_t)(shape->batch > 0 ? shape->batch : 0) *
                                       (shape->d_inner > 0 ? shape->d_inner : 0) *
                                       (shape->d_state > 0 ? shape->d_state : 0) * 4 : 0;
@@ -800,7 +845,7 @@ int bdssm_train_scan_bwd(const bdssm_shape *shape, int64_t T, const void *x, con
                             &a);
     if (rc) return rc;
     float *d_bias = grads ? grads->d_dt_bias : nullptr;
-    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipStream_t st = stream;
     (void)hipGetLastError();
     if (batch == 0 || D == 0 || T == 0) {
         rc = zero_bwd(D, N, dA, dDskip, dh_init, batch * D * N, st);
@@ -884,7 +929,7 @@ int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void 
                                 const float *h0_blocks, const void *dy, void *dx, void *ddt,
                                 void *dB, void *dC, float *dA, float *dDskip, float *dh0_blocks,
                                 void *ws, size_t ws_bytes, const bdssm_fusion *fusion,
-                                bdssm_fusion_grads *grads, void *stream) {
+                                bdssm_fusion_grads *grads, hipStream_t stream) {
     size_t nbnd = 0;
     if (shape && shape->block_len > 0 && T >= 0 && shape->batch > 0 && shape->d_inner > 0 &&
         shape->d_state > 0)
@@ -906,7 +951,7 @@ int bdssm_train_scan_blocks_bwd(const bdssm_shape *shape, int64_t T, const void 
                             &a);
     if (rc) return rc;
     float *d_bias = grads ? grads->d_dt_bias : nullptr;
-    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipStream_t st = stream;
     (void)hipGetLastError();
     if (batch == 0 || D == 0 || T == 0) {
         rc = zero_bwd(D, N, dA, dDskip, dh0_blocks, batch * D * N, st);

@@ -28,7 +28,7 @@ def test_exports_match_header():
 
 
 def test_version_and_status_strings():
-    assert m.version() == 10600
+    assert m.version() == 10700
     for code in range(-7, 1):
         assert m.status_str(code) not in ("", "unknown status")
     assert m.status_str(-99) == "unknown status"
@@ -53,7 +53,7 @@ def P(v):
 def prefill(s, T, x=FAKE, dt=FAKE + 0x1000, Bm=FAKE + 0x2000, C=FAKE + 0x3000, A=FAKE + 0x4000,
             Ds=FAKE + 0x5000, h_init=None, h_cache=FAKE + 0x6000, y=None, ws=None, ws_bytes=0):
     return lib().bdssm_prefill(ctypes.byref(s), T, P(x), P(dt), P(Bm), P(C), P(A), P(Ds),
-                               P(h_init), P(h_cache), P(y), P(ws), ws_bytes, None, None)
+                               P(h_init), P(h_cache), P(y), P(ws), ws_bytes, None)
 
 
 def test_shape_errors():
@@ -73,7 +73,8 @@ def test_dtype_error():
 
 
 def test_null_errors():
-    assert lib().bdssm_prefill(None, 16, *([None] * 10), 0, None, None) == -1
+    assert lib().bdssm_prefill(None, 16, *([None] * 10), 0, None) == -1
+    assert lib().bdssm_prefill_ex(None, 16, *([None] * 10), 0, None, None) == -1
     assert prefill(shape(), 16, x=None) == -1
     assert prefill(shape(), 16, h_cache=None) == -1
     # y requested without C
@@ -104,7 +105,7 @@ def test_alias_error():
     s = shape()
     rc = lib().bdssm_block_step(ctypes.byref(s), P(FAKE), P(FAKE + 0x1000), P(FAKE + 0x2000),
                                 P(FAKE + 0x3000), P(FAKE + 0x4000), P(FAKE + 0x5000),
-                                P(FAKE + 0x6000), P(FAKE), None, None)
+                                P(FAKE + 0x6000), P(FAKE), None)
     assert rc == -7
 
 
@@ -113,7 +114,8 @@ def test_empty_calls_are_noops():
     assert prefill(shape(batch=0), 16, x=None, dt=None, Bm=None, C=None, h_cache=None) == 0
     assert prefill(shape(D=0), 16, x=None, dt=None, Bm=None, C=None, h_cache=None) == 0
     s = shape(batch=0)
-    assert lib().bdssm_full_scan(ctypes.byref(s), 0, *([None] * 8), 0, None, None) == 0
+    assert lib().bdssm_full_scan(ctypes.byref(s), 0, *([None] * 8), 0, None) == 0
+    assert lib().bdssm_full_scan_ex(ctypes.byref(s), 0, *([None] * 8), 0, None, None) == 0
 
 
 def test_workspace_sizes():
@@ -271,14 +273,14 @@ def test_long_block_backward_workspace(op, monkeypatch):
 def test_fusion_argument_errors():
     f = B.Fusion(MIS, 1, None)                         # misaligned bias
     s = shape()
-    rc = lib().bdssm_block_step(ctypes.byref(s), P(FAKE), P(FAKE + 0x1000), P(FAKE + 0x2000),
-                                P(FAKE + 0x3000), P(FAKE + 0x4000), P(FAKE + 0x5000),
-                                P(FAKE + 0x6000), P(FAKE + 0x7000), ctypes.byref(f), None)
+    rc = lib().bdssm_block_step_ex(ctypes.byref(s), P(FAKE), P(FAKE + 0x1000), P(FAKE + 0x2000),
+                                   P(FAKE + 0x3000), P(FAKE + 0x4000), P(FAKE + 0x5000),
+                                   P(FAKE + 0x6000), P(FAKE + 0x7000), ctypes.byref(f), None)
     assert rc == -4
     f = B.Fusion(None, 1, FAKE + 0x7000)               # gate on top of y
-    rc = lib().bdssm_block_step(ctypes.byref(s), P(FAKE), P(FAKE + 0x1000), P(FAKE + 0x2000),
-                                P(FAKE + 0x3000), P(FAKE + 0x4000), P(FAKE + 0x5000),
-                                P(FAKE + 0x6000), P(FAKE + 0x7000), ctypes.byref(f), None)
+    rc = lib().bdssm_block_step_ex(ctypes.byref(s), P(FAKE), P(FAKE + 0x1000), P(FAKE + 0x2000),
+                                   P(FAKE + 0x3000), P(FAKE + 0x4000), P(FAKE + 0x5000),
+                                   P(FAKE + 0x6000), P(FAKE + 0x7000), ctypes.byref(f), None)
     assert rc == -7
 
 
@@ -292,8 +294,8 @@ def test_single_block_rows_beyond_32bit_offsets():
     for D, want in ((1 << 21, -2), ((1 << 21) - 1, -1)):
         s = shape(batch=1, D=D, L=256, dtype=B.F32)
         rc = lib().bdssm_block_step(ctypes.byref(s), None, P(far[1]), P(far[2]), P(far[3]), P(far[4]),
-                                    P(far[5]), P(far[6]), None, None, None)
+                                    P(far[5]), P(far[6]), None, None)
         assert rc == want, (D, rc)
         rc = lib().bdssm_commit(ctypes.byref(s), None, P(far[1]), P(far[2]), P(far[3]), P(far[4]),
-                                P(far[5]), P(far[6]), None, None, None)
+                                P(far[5]), P(far[6]), None, None)
         assert rc == want, (D, rc)
