@@ -533,11 +533,15 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 // wave, 4 waves per workgroup (4 CW channels: 32 at 16 states).  With two
 // states per lane the forward states before each token and the reverse
 // adjoints of a whole 16-token group fit in 64 VGPRs at any state count, so
-// the forward quantities are formed once per token (no recomputation):
+// the forward state and the reverse adjoint are formed once per token (no
+// segment recomputation):
 //   pass A (left to right over the group): hf from the group's block start
-//     state, gr reset at block starts; keeps hf_{t-1}, gr_t per token;
+//     state, gr reset at block starts; keeps hf_{t-1}, gr_t per token, and
+//     the decays of the group's last KA tokens (up to 12: what the registers
+//     left over hold without spilling);
 //   pass B (right to left): hr (reset at block ends), gf (q carried across
-//     groups; + dbounds or reset at block ends), every gradient term.
+//     groups; + dbounds or reset at block ends), every gradient term; the
+//     decays of the other tokens and the injections are formed again.
 // Reductions stay in registers (VALU lane exchanges, no LDS round trip):
 //   * dB / dC: per token the lane's 4 values are summed over the wave's CW
 //     channels by two 32-lane folds (permlane32 swaps) and one 16-lane fold
@@ -623,6 +627,14 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(kN ==
     constexpr int TK = P / 2;                 // tokens per dt / x flush
     constexpr int EV = CW / 4;                // the fused epilogue's values per lane
     constexpr int NSB = kFuse ? 4 : 3;        // row streams: x, dt, dy (, z)
+    // decays kept from pass A for pass B, per group: as many tokens as the
+    // registers hold without spilling at three waves per SIMD (two at 4
+    // states); the others are formed again in pass B
+    constexpr int KA = kFuse ? 0
+                       : kN == 4 ? 12
+                       : (L == 1 || L == 2) ? 0
+                       : kN == 8 ? (L == 16 ? 8 : 0)
+                       : (L == 0 || L == 4) ? 8 : 12;
     // L = 0: blocks of Lr tokens, a multiple of 16 above 16, spanning several
     // groups; gstate holds the forward state and the reverse adjoint's carry
     // at every group start ([batch, T/16, 2, D, 16], group_state_kernel)
@@ -817,6 +829,10 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(kN ==
 
         // pass A: forward state and reverse adjoint, left to right
         float hp_s[G][2], gr_s[G][2];
+        // the decays of the group's last KA tokens, kept for pass B (which
+        // takes those tokens first, so their registers free early); the rest
+        // pass B forms again
+        float a_s[KA > 0 ? KA : 1][2];
         float hf[2] = {hst[0].x, hst[0].y}, pr[2] = {0.f, 0.f};
         if constexpr (kLong) {
             pr[0] = hst[NH - 1].x; pr[1] = hst[NH - 1].y;
@@ -839,6 +855,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(kN ==
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const float a = fast_exp2(dl * a2[j]);
+                if (i >= G - KA) a_s[i - (G - KA)][j] = a;
                 const float gr_j = __builtin_fmaf(gy, cc[j], pr[j]);
                 hp_s[i][j] = hf[j];
                 gr_s[i][j] = gr_j;
@@ -880,7 +897,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(kN ==
             float s1 = 0.f, s2 = 0.f, vb[2], vc[2], yp = 0.f;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const float a = fast_exp2(dl * a2[j]);   // formed again: keeps the kernel at 3 waves per SIMD
+                const float a = (i >= G - KA) ? a_s[i - (G - KA)][j] : fast_exp2(dl * a2[j]);
                 const float u = dxv * bb[j];
                 const float hr1 = hr[j];
                 hr[j] = __builtin_fmaf(a, hr1, u);
