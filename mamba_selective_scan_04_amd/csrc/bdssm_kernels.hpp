@@ -780,7 +780,9 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 // wave's CW channels DMA'd into the wave's LDS slice, the group's B / C rows
 // shared by the workgroup, their loads spread over the waves; one group
 // ahead, widened in place by the lane that loaded them; one barrier per
-// group):
+// group; at 16 and 32 states with blocks of at most 16 tokens, two groups
+// per barrier with the next two groups' rows in flight, so that the loads
+// have two groups' work to land in):
 //   forward, left to right: a = exp2(dt A'), u = dt x B, hf = a hf + u, the
 //     lane's output partial C . hf over its two states; the group's decays
 //     and injections stay in registers (64 per lane), so the reverse pass
@@ -993,23 +995,24 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
     constexpr int NB = kBlockInit ? G / LB : 1;
     constexpr bool kAhead = kBlockInit && (kLong || L >= 4);
     float2 hbn[NB];
-    auto load_hb = [&](int k0n) {
+    auto load_hb_into = [&](float2 (&dst)[NB], int k0n) {
         if constexpr (kBlockInit) {
             const int nv = (len - k0n < G) ? len - k0n : G;
 #pragma unroll
             for (int q = 0; q < NB; ++q) {
                 const int i = q * LB < nv ? q * LB : 0;
                 const int64_t blk = (t_begin + k0n + i) / Lb;
-                hbn[q] = *reinterpret_cast<const float2 *>(
+                dst[q] = *reinterpret_cast<const float2 *>(
                     h0_blocks + (((int64_t)b * (nbl + 1) + blk) * D + d) * kN + s0);
             }
         }
     };
+    auto load_hb = [&](int k0n) { load_hb_into(hbn, k0n); };
 
     // long blocks: gsb / geb, whether the group starts / ends its block, and
     // hri, the reverse state entering it from the right
     auto group = [&](auto &xd, auto &bc, int k0, const float2 *hb, float2 hri = make_float2(0.f, 0.f),
-                     bool gsb = true, bool geb = true) {
+                     bool gsb = true, bool geb = true) __attribute__((always_inline)) {
         const int nvalid = (len - k0 < G) ? len - k0 : G;   // uniform
         // injections kept per state (at 4 states dt x per token: the
         // registers of the wider x / dt staging leave no room for more)
@@ -1177,6 +1180,53 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
         for (int s = 0; s < nsched; s += 2) {
             lstep(xdA, bcA, xdB, bcB, s);
             if (s + 1 < nsched) lstep(xdB, bcB, xdA, bcA, s + 1);
+        }
+    } else if constexpr (kN >= 16) {
+        // two groups per barrier, the next two groups' rows loading meanwhile
+        // (four row buffers)
+        __shared__ __attribute__((aligned(16))) uint32_t xdC[4][NS][G][CW], xdD[4][NS][G][CW];
+        __shared__ __attribute__((aligned(16))) uint32_t bcC[2][G][kN], bcD[2][G][kN];
+        float2 hbn2[NB];
+        auto macro = [&](auto &x0, auto &b0, auto &x1, auto &b1, auto &n0, auto &nb0, auto &n1, auto &nb1,
+                         int k0) {
+            const bool has1 = k0 + G < len;
+            const bool more0 = k0 + 2 * G < len, more1 = k0 + 3 * G < len;
+            float2 hA[NB], hB[NB];
+            if constexpr (kBlockInit && !kAhead) load_hb_into(hA, k0);
+#pragma unroll
+            for (int q = 0; q < NB; ++q) {
+                if constexpr (kAhead) hA[q] = hbn[q];
+                hB[q] = hbn2[q];
+            }
+            if (more0) {
+                if constexpr (kAhead) load_hb_into(hbn, k0 + 2 * G);
+                issue(n0, nb0, k0 + 2 * G);
+            }
+            if (more1) {
+                if constexpr (kAhead) load_hb_into(hbn2, k0 + 3 * G);
+                issue(n1, nb1, k0 + 3 * G);
+            }
+            group(x0, b0, k0, hA);
+            if (has1) {
+                if constexpr (kBlockInit && !kAhead) load_hb_into(hB, k0 + G);
+                group(x1, b1, k0 + G, hB);
+            }
+            if (more0) widen(n0, nb0, k0 + 2 * G);
+            if (more1) widen(n1, nb1, k0 + 3 * G);
+            __syncthreads();
+        };
+        if constexpr (kAhead) {
+            load_hb_into(hbn, 0);
+            if (G < len) load_hb_into(hbn2, G);
+        }
+        issue(xdA, bcA, 0);
+        if (G < len) issue(xdB, bcB, G);
+        widen(xdA, bcA, 0);
+        if (G < len) widen(xdB, bcB, G);
+        __syncthreads();
+        for (int k0 = 0; k0 < len; k0 += 4 * G) {
+            macro(xdA, bcA, xdB, bcB, xdC, bcC, xdD, bcD, k0);
+            if (k0 + 2 * G < len) macro(xdC, bcC, xdD, bcD, xdA, bcA, xdB, bcB, k0 + 2 * G);
         }
     } else {
         if constexpr (kAhead) load_hb(0);
