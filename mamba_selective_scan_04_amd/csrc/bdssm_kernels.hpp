@@ -780,9 +780,10 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 // wave's CW channels DMA'd into the wave's LDS slice, the group's B / C rows
 // shared by the workgroup, their loads spread over the waves; one group
 // ahead, widened in place by the lane that loaded them; one barrier per
-// group; at 16 and 32 states with blocks of at most 16 tokens, two groups
-// per barrier with the next two groups' rows in flight, so that the loads
-// have two groups' work to land in):
+// group; at 16 and 32 states with blocks of at most 16 tokens (except the
+// two-stream form at L = 4), two groups per barrier with the next two
+// groups' rows in flight, so that the loads have two groups' work to land
+// in):
 //   forward, left to right: a = exp2(dt A'), u = dt x B, hf = a hf + u, the
 //     lane's output partial C . hf over its two states; the group's decays
 //     and injections stay in registers (64 per lane), so the reverse pass
@@ -1181,9 +1182,10 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
             lstep(xdA, bcA, xdB, bcB, s);
             if (s + 1 < nsched) lstep(xdB, bcB, xdA, bcA, s + 1);
         }
-    } else if constexpr (kN >= 16) {
+    } else if constexpr (kN >= 16 && !(kBlockInit && L == 4)) {
         // two groups per barrier, the next two groups' rows loading meanwhile
-        // (four row buffers)
+        // (four row buffers; not for the two-stream form at L = 4, whose
+        // second group's four block start states would spill)
         __shared__ __attribute__((aligned(16))) uint32_t xdC[4][NS][G][CW], xdD[4][NS][G][CW];
         __shared__ __attribute__((aligned(16))) uint32_t bcC[2][G][kN], bcD[2][G][kN];
         float2 hbn2[NB];
