@@ -11,9 +11,15 @@ that the template instantiations spread over parallel compiler processes.
 bdssm.hip holds the C ABI and the launch plans.  Objects go to _build/.
 libbdssm_probe.so (csrc/roof_probe.hip) holds the benchmark's
 microbenchmarks; it is not part of the scan library.
+
+The compiler's resource report of every kernel (registers, spills, scratch,
+LDS, waves per SIMD) goes to _build/<object>.resources.tsv, one line per
+kernel; tests/test_resources.py checks the hot kernels' lines (no spills,
+the occupancy their design assumes).
 """
 import concurrent.futures
 import os
+import re
 import subprocess
 import sys
 
@@ -36,6 +42,8 @@ HIPCC_FLAGS = [
     # keep the compiler from forming packed fp32 instructions (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
+    # per-kernel register / LDS / occupancy report (collected by _resources)
+    "-Rpass-analysis=kernel-resource-usage",
 ]
 
 
@@ -64,8 +72,33 @@ def up_to_date():
 
 
 def _clean(out):
-    # the host pass does not know the packed-fp32 feature and says so; drop that line
-    return "\n".join(l for l in out.splitlines() if "not a recognized feature" not in l)
+    # the host pass does not know the packed-fp32 feature and says so; drop
+    # that line, and the resource remarks (kept in the .resources.tsv files)
+    return "\n".join(l for l in out.splitlines()
+                     if "not a recognized feature" not in l and "remark:" not in l)
+
+
+RESOURCE_FIELDS = (("VGPRs", "vgprs"), ("AGPRs", "agprs"), ("VGPRs Spill", "vgpr_spill"),
+                   ("ScratchSize [bytes/lane]", "scratch"), ("Occupancy [waves/SIMD]", "waves"),
+                   ("LDS Size [bytes/block]", "lds"))
+
+
+def _resources(out):
+    """The kernel-resource-usage remarks of one compiler run -> tsv text:
+    kernel (mangled), then the RESOURCE_FIELDS values."""
+    rows, cur = [], None
+    for line in out.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = {"name": m.group(1)}
+            rows.append(cur)
+            continue
+        m = re.search(r"remark:\s+([^:\[]+(?:\[[^\]]*\])?): (-?\d+)", line)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = m.group(2)
+    head = "kernel\t" + "\t".join(k for _, k in RESOURCE_FIELDS)
+    return "\n".join([head] + ["\t".join([r["name"]] + [r.get(f, "") for f, _ in RESOURCE_FIELDS])
+                               for r in rows if r["name"].startswith("_Z")]) + "\n"
 
 
 def _compile(src, obj, extra):
@@ -77,6 +110,8 @@ def _compile(src, obj, extra):
         if os.path.exists(tmp):
             os.remove(tmp)
         raise RuntimeError("hipcc failed (%d) on %s:\n%s\n%s" % (r.returncode, os.path.basename(obj), " ".join(cmd), out))
+    with open(obj + ".resources.tsv", "w") as f:
+        f.write(_resources(r.stdout))
     os.replace(tmp, obj)
     return out
 
