@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(6))) void
     const float *__restrict__ dt_bias, const Tin *__restrict__ z)
 {
     static_assert(kGroup % L == 0, "block length must divide the token group");
-    constexpr int U = 4;
+    constexpr int U = 4;                      // tokens per pipeline stage
     const int lane = threadIdx.x;
     const int d_raw = blockIdx.x * kWave + lane;
     const bool live = d_raw < D;
@@ -89,7 +89,13 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(6))) void
     const float bias = (kDt != kDtPlain && dt_bias != nullptr) ? dt_bias[d] : 0.f;
     const Tin *cs = Cm + first * kStates;
 
-    auto consume = [&](const Tin *dr, const Tin *yr, int k0, int count) {
+    // Tokens stream through registers in stages of U as in chunk_state_kernel:
+    // a stage's dt and dy are loaded one stage ahead into one of two buffers
+    // used in turn (the loop unrolled by two, so no copy between iterations
+    // forces an early wait), held as 32-bit values; the gate z is read where
+    // it is used.
+    using St = typename Staged<Tin>::type;
+    auto consume = [&](const St *dr, const St *yr, int k0, int count) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             if (i < count) {
@@ -104,8 +110,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(6))) void
                         q[4 * k + 2] += v.z; q[4 * k + 3] += v.w;
                     }
                 }
-                const float dl = step_size<kDt>(widen(dr[i]), bias);
-                float gy = live ? widen(yr[i]) : 0.f;
+                const float dl = step_size<kDt>(widen_staged(dr[i]), bias);
+                float gy = live ? widen_staged(yr[i]) : 0.f;
                 if (gate) gy *= silu_f(widen(zs.load(p)));
                 S += dl;
                 const Tin *crow = cs + (int64_t)p * kStates;
@@ -119,7 +125,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(6))) void
             }
         }
     };
-    auto load_stage = [&](int k0, int count, Tin *dout, Tin *yo) {
+    // count < U: the rows past the stage re-read its last row
+    auto load_stage = [&](int k0, int count, St *dout, St *yo) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             const int p = len - 1 - (k0 + (i < count ? i : count - 1));
@@ -129,18 +136,19 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(6))) void
     };
     const int n_full = len / U;
     const int rem = len - n_full * U;
-    Tin dr[U], yr[U];
-    if (n_full > 0) load_stage(0, U, dr, yr);
-    for (int g = 0; g < n_full; ++g) {
-        Tin dn[U], yn[U];
-        if (g + 1 < n_full) load_stage((g + 1) * U, U, dn, yn);
-        consume(dr, yr, g * U, U);
-#pragma unroll
-        for (int i = 0; i < U; ++i) { dr[i] = dn[i]; yr[i] = yn[i]; }
+    St da[U], ya[U], db[U], yb[U];
+    if (n_full > 0) load_stage(0, U, da, ya);
+    int g = 0;
+    for (; g + 1 < n_full; g += 2) {
+        load_stage((g + 1) * U, U, db, yb);
+        consume(da, ya, g * U, U);
+        if (g + 2 < n_full) load_stage((g + 2) * U, U, da, ya);
+        consume(db, yb, (g + 1) * U, U);
     }
+    if (g < n_full) consume(da, ya, g * U, U);       // an odd number of full stages: the last is in da
     if (rem > 0) {
-        load_stage(n_full * U, rem, dr, yr);
-        consume(dr, yr, n_full * U, rem);
+        load_stage(n_full * U, rem, db, yb);
+        consume(db, yb, n_full * U, rem);
     }
     if (live) {
         float4 *o = reinterpret_cast<float4 *>(qout + (((int64_t)b * n_chunks + c) * D + d) * kStates);
