@@ -308,6 +308,30 @@ def test_train_blocks_against_oracle(dev, L, T, D, dtype, bidir, monkeypatch):
     assert rel_err(to_np(y), yo) < TOL[dtype], worst(to_np(y), yo)
 
 
+@pytest.mark.parametrize("n", [16, 32])
+@pytest.mark.parametrize("L", [8, 16])
+@pytest.mark.parametrize("T", [16, 17, 33, 48, 64, 80, 101])
+def test_pair_group_pairs_and_ragged_tails(dev, T, L, n):
+    """bidir_pair_kernel runs two 16-token groups per barrier at 16 and 32
+    states: sequences of 1 to 7 groups (an odd last group, a partial last
+    group, an even count), both training forms, against the oracle."""
+    from mamba_selective_scan_04_amd import synth
+    if T % L:
+        T = (T // L + 1) * L
+    sid = 60 + T + L + n
+    c = Case(2, T, 40, torch.float32, sid=sid, a_kind="random", n=n)
+    h0 = synth.normal((2, 40, n), 1000 * sid + 5).to(dev)
+    y, bnd = m.train_scan(*c.args(), L, h_init=h0, want_bounds=True)
+    h0b = synth.normal((2, T // L + 1, 40, n), 1000 * sid + 7).to(dev)
+    yb = m.train_scan_blocks(*c.args(), L, h0b)
+    _sync()
+    yo, bo = oracle.train_scan(*c.oracle_args(), L, h_init=to_np(h0), want_bounds=True)
+    assert rel_err(to_np(y), yo) < TOL[torch.float32], worst(to_np(y), yo)
+    assert rel_err(to_np(bnd), bo) < STATE_TOL
+    ybo = oracle.train_blocks(*c.oracle_args(), L, to_np(h0b))
+    assert rel_err(to_np(yb), ybo) < TOL[torch.float32], worst(to_np(yb), ybo)
+
+
 def test_train_blocks_with_clean_bounds_matches_continuous(dev):
     """Passing the stream's own boundary states (from train_scan) reproduces
     train_scan's output: the noisy-stream form equals the clean form when the
