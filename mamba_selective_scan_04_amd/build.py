@@ -43,7 +43,7 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
     # per-kernel register / LDS / occupancy report (collected by _resources)
-    "-Rpass-analysis=kernel-resource-usage",
+    "-Rpass-analysis=kernel-resource-usage", "-fno-caret-diagnostics",
 ]
 
 
@@ -74,8 +74,18 @@ def up_to_date():
 def _clean(out):
     # the host pass does not know the packed-fp32 feature and says so; drop
     # that line, and the resource remarks (kept in the .resources.tsv files)
-    return "\n".join(l for l in out.splitlines()
-                     if "not a recognized feature" not in l and "remark:" not in l)
+    # with the include chains that introduce them
+    keep, chain = [], []
+    for l in out.splitlines():
+        if l.startswith("In file included from"):
+            chain.append(l)
+            continue
+        if "remark:" in l or "not a recognized feature" in l:
+            chain = []
+            continue
+        keep += chain + [l]
+        chain = []
+    return "\n".join(keep + chain)
 
 
 RESOURCE_FIELDS = (("VGPRs", "vgprs"), ("AGPRs", "agprs"), ("VGPRs Spill", "vgpr_spill"),

@@ -1198,27 +1198,62 @@ __global__ __launch_bounds__(kWave) void adjoint_general_kernel(
     const Rows<Tin> zs((gate ? z : dy) + first * D, len, D, d);
     const float bias = (kDt != kDtPlain && dt_bias != nullptr) ? dt_bias[d] : 0.f;
     const Tin *cs = Cm + first * kN;
+    // Tokens stream through registers in stages of U as in adjoint_chunk_kernel
+    // (two named 32-bit buffers, the loop unrolled by two).
+    constexpr int U = 4;
+    using St = typename Staged<Tin>::type;
     int kb = 0;                                   // rows walked since the last block end
-    for (int p = len - 1; p >= 0; --p) {
-        if (dbounds != nullptr && kb == 0) {
-            float v[kN];
-            load_row<kN>(dbounds + (((int64_t)b * (nbl + 1) + blk0 + (p + 1) / L) * D + d) * kN, v);
+    auto consume = [&](const St *dr, const St *yr, int k0, int count) {
 #pragma unroll
-            for (int n = 0; n < kN; ++n) q[n] += v[n];
-        }
-        const float dl = step_size<kDt>(widen(ds.load(p)), bias);
-        float gy = live ? widen(ys.load(p)) : 0.f;
-        if (gate) gy *= silu_f(widen(zs.load(p)));
-        S += dl;
-        const Tin *crow = cs + (int64_t)p * kN;
+        for (int i = 0; i < U; ++i) {
+            if (i < count) {
+                const int p = len - 1 - (k0 + i);        // row within the chunk
+                if (dbounds != nullptr && kb == 0) {
+                    float v[kN];
+                    load_row<kN>(dbounds + (((int64_t)b * (nbl + 1) + blk0 + (p + 1) / L) * D + d) * kN, v);
 #pragma unroll
-        for (int k = 0; k < kN / 2; ++k) {
-            float c0, c1;
-            load_pair(crow, k, c0, c1);
-            q[2 * k] = fast_exp2(dl * a2[2 * k]) * __builtin_fmaf(gy, c0, q[2 * k]);
-            q[2 * k + 1] = fast_exp2(dl * a2[2 * k + 1]) * __builtin_fmaf(gy, c1, q[2 * k + 1]);
+                    for (int n = 0; n < kN; ++n) q[n] += v[n];
+                }
+                const float dl = step_size<kDt>(widen_staged(dr[i]), bias);
+                float gy = live ? widen_staged(yr[i]) : 0.f;
+                if (gate) gy *= silu_f(widen(zs.load(p)));
+                S += dl;
+                const Tin *crow = cs + (int64_t)p * kN;
+#pragma unroll
+                for (int k = 0; k < kN / 2; ++k) {
+                    float c0, c1;
+                    load_pair(crow, k, c0, c1);
+                    q[2 * k] = fast_exp2(dl * a2[2 * k]) * __builtin_fmaf(gy, c0, q[2 * k]);
+                    q[2 * k + 1] = fast_exp2(dl * a2[2 * k + 1]) * __builtin_fmaf(gy, c1, q[2 * k + 1]);
+                }
+                kb = (kb + 1 == L) ? 0 : kb + 1;
+            }
         }
-        kb = (kb + 1 == L) ? 0 : kb + 1;
+    };
+    // count < U: the rows past the stage re-read its last row
+    auto load_stage = [&](int k0, int count, St *dout, St *yo) {
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int p = len - 1 - (k0 + (i < count ? i : count - 1));
+            dout[i] = ds.load(p);
+            yo[i] = ys.load(p);
+        }
+    };
+    const int n_full = len / U;
+    const int rem = len - n_full * U;
+    St da[U], ya[U], db[U], yb[U];
+    if (n_full > 0) load_stage(0, U, da, ya);
+    int g = 0;
+    for (; g + 1 < n_full; g += 2) {
+        load_stage((g + 1) * U, U, db, yb);
+        consume(da, ya, g * U, U);
+        if (g + 2 < n_full) load_stage((g + 2) * U, U, da, ya);
+        consume(db, yb, (g + 1) * U, U);
+    }
+    if (g < n_full) consume(da, ya, g * U, U);       // an odd number of full stages: the last is in da
+    if (rem > 0) {
+        load_stage(n_full * U, rem, db, yb);
+        consume(db, yb, n_full * U, rem);
     }
     if (live) {
         store_row<kN>(qout + (((int64_t)b * n_chunks + c) * D + d) * kN, q);
@@ -1243,6 +1278,8 @@ __global__ __launch_bounds__(kWave) void group_state_kernel(
     const float *__restrict__ dt_bias, const Tin *__restrict__ z)
 {
     constexpr int G = kGroup;
+    constexpr int U = 4;                      // tokens per pipeline stage (divides G)
+    using St = typename Staged<Tin>::type;
     const int lane = threadIdx.x;
     const int d_raw = blockIdx.x * kWave + lane;
     const bool live = d_raw < D;
@@ -1264,36 +1301,67 @@ __global__ __launch_bounds__(kWave) void group_state_kernel(
         load_row<kStates>(h_start + (((int64_t)b * (nbl + 1) + blk) * D + d) * kStates, hf);
 #pragma unroll
         for (int n = 0; n < kStates; ++n) pr[n] = 0.f;
-        for (int64_t gs = t0; gs + G < pend; gs += G) {
-            for (int i = 0; i < G; ++i) {
-                const int64_t r = row0 + gs + i;
-                const float dl = step_size<kDt>(widen(dt[r * D + d]), bias);
-                const float dxv = dl * widen(x[r * D + d]);
-                float gy = widen(dy[r * D + d]);
-                if (gate) gy *= silu_f(widen(z[r * D + d]));
-                const Tin *brow = Bm + r * kStates, *crow = Cm + r * kStates;
+        // the tokens before the block's last group (a multiple of 16), through
+        // a register pipeline of U-token stages (two named 32-bit buffers, the
+        // loop unrolled by two, as in chunk_state_kernel)
+        const int nwalk = (int)(((pend - t0 - 1) / G) * G);
+        const int64_t first = row0 + t0;
+        const Rows<Tin> xs(x + first * D, nwalk, D, d);
+        const Rows<Tin> ds(dt + first * D, nwalk, D, d);
+        const Rows<Tin> ys(dy + first * D, nwalk, D, d);
+        const Rows<Tin> zs((gate ? z : dy) + first * D, nwalk, D, d);
+        const Tin *bs = Bm + first * kStates, *cs = Cm + first * kStates;
+        auto consume = [&](const St *xr, const St *dr, const St *yr, int k0) {
 #pragma unroll
-                for (int k = 0; k < kStates / 2; ++k) {
+            for (int i = 0; i < U; ++i) {
+                const int k = k0 + i;
+                const float dl = step_size<kDt>(widen_staged(dr[i]), bias);
+                const float dxv = dl * widen_staged(xr[i]);
+                float gy = widen_staged(yr[i]);
+                if (gate) gy *= silu_f(widen(zs.load(k)));
+                const Tin *brow = bs + (int64_t)k * kStates, *crow = cs + (int64_t)k * kStates;
+#pragma unroll
+                for (int q = 0; q < kStates / 2; ++q) {
                     float b0, b1, c0, c1;
-                    load_pair(brow, k, b0, b1);
-                    load_pair(crow, k, c0, c1);
+                    load_pair(brow, q, b0, b1);
+                    load_pair(crow, q, c0, c1);
                     const float bb[2] = {b0, b1}, cc[2] = {c0, c1};
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        const int n = 2 * k + j;
+                        const int n = 2 * q + j;
                         const float a = fast_exp2(dl * a2[n]);
                         const float gr = __builtin_fmaf(gy, cc[j], pr[n]);
                         hf[n] = __builtin_fmaf(a, hf[n], dxv * bb[j]);
                         pr[n] = a * gr;
                     }
                 }
+                // after each group: the state at the next group's start
+                if ((k + 1) % G == 0 && live) {
+                    float *o = gstate + ((((int64_t)b * ng + (t0 + k + 1) / G) * 2) * D + d) * kStates;
+                    store_row<kStates>(o, hf);
+                    store_row<kStates>(o + (int64_t)D * kStates, pr);
+                }
             }
-            if (live) {
-                float *o = gstate + ((((int64_t)b * ng + (gs + G) / G) * 2) * D + d) * kStates;
-                store_row<kStates>(o, hf);
-                store_row<kStates>(o + (int64_t)D * kStates, pr);
+        };
+        auto load_stage = [&](int k0, St *xo, St *dout, St *yo) {
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                xo[i] = xs.load(k0 + i);
+                dout[i] = ds.load(k0 + i);
+                yo[i] = ys.load(k0 + i);
             }
+        };
+        const int nst = nwalk / U;                 // G is a multiple of U: whole stages
+        St xa[U], da[U], ya[U], xb[U], db[U], yb[U];
+        load_stage(0, xa, da, ya);
+        int g = 0;
+        for (; g + 1 < nst; g += 2) {
+            load_stage((g + 1) * U, xb, db, yb);
+            consume(xa, da, ya, g * U);
+            if (g + 2 < nst) load_stage((g + 2) * U, xa, da, ya);
+            consume(xb, db, yb, (g + 1) * U);
         }
+        if (g < nst) consume(xa, da, ya, g * U);
     }
 }
 
