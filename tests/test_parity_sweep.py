@@ -1,0 +1,137 @@
+"""A seeded sweep over the configuration space: 40 small problems drawn with a
+fixed generator (state count 4 / 8 / 16 / 32; block length 1 to 96; ragged
+channel counts and sequence lengths; fp32 and bf16; no fusion, a step-size
+bias, or softplus with the silu gate), each run through every entry point
+(prefill, block step, commit, both training forms and their gradients) and
+compared element by element with the fp64 oracle on the same inputs.  Each
+problem lands on whichever kernels its sizes select, so the sweep crosses
+the kernel-choice boundaries that the targeted tests cover one by one."""
+import numpy as np
+import pytest
+import torch
+
+import mamba_selective_scan_04_amd as m
+import oracle
+from mamba_selective_scan_04_amd import synth
+from parity_util import Case, STATE_TOL, TOL, rel_err, to_np, worst
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw(count=40, seed=2026):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        n = int(rng.choice([4, 8, 16, 32]))
+        L = int(rng.choice([1, 2, 4, 8, 16, 16, 16, 32, 48, 64, 96]))
+        k = int(rng.integers(1, max(2, 420 // L) + 1))
+        T = L * k
+        D = int(rng.choice([1, 7, 33, 64, 100, 130, 200]))
+        batch = int(rng.integers(1, 4))
+        dtype = "bf16" if rng.random() < 0.5 else "f32"
+        fusion = str(rng.choice(["none", "none", "bias", "softplus_gate"]))
+        out.append((i, n, L, T, D, batch, dtype, fusion))
+    return out
+
+
+CASES = _draw()
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "i%d-n%d-L%d-T%d-D%d-b%d-%s-%s" % c)
+def test_sweep_all_entry_points(dev, case):
+    i, n, L, T, D, batch, dts, fusion = case
+    dtype = torch.bfloat16 if dts == "bf16" else torch.float32
+    sid = 700 + i
+    c = Case(batch, T, D, dtype, sid=sid, a_kind="random", n=n)
+    kw, ok = {}, {}
+    if fusion != "none":
+        # the dt stream holds raw pre-activations (softplus) or small offsets
+        # around the step size (bias alone)
+        if fusion == "softplus_gate":
+            c.dev["dt"] = synth.normal((batch, T, D), 1000 * sid + 1, "cpu", torch.float32, mean=-1.0,
+                                       std=0.5).to(dtype).to("cuda").contiguous()
+        bias = synth.normal((D,), 1000 * sid + 2, "cuda", torch.float32,
+                            std=0.3 if fusion == "softplus_gate" else 0.02)
+        if fusion == "bias":
+            bias = bias.abs()             # the step size dt + bias stays positive
+        kw, ok = dict(dt_bias=bias), dict(dt_bias=to_np(bias))
+        if fusion == "softplus_gate":
+            z = synth.normal((batch, T, D), 1000 * sid + 3, "cuda", dtype, std=2.0)
+            kw.update(dt_softplus=True, z=z)
+            ok.update(dt_softplus=True, z=synth.to_oracle(z))
+    tol = TOL[dtype]
+    oa = c.oracle_args()
+    label = "case %s" % (case,)
+
+    def near(got, ref, bar, what):
+        g = to_np(got)
+        assert g.shape == np.shape(ref), (label, what, g.shape, np.shape(ref))
+        e = rel_err(g, ref)
+        assert e < bar, (label, what, e, worst(g, ref))
+
+    # continuous training form from a seeded start state, with block states
+    h0 = synth.normal((batch, D, n), 1000 * sid + 5).to(dev)
+    y, bnd = m.train_scan(*c.args(), L, h_init=h0, want_bounds=True, **kw)
+    # two-stream form from seeded block starts
+    h0b = synth.normal((batch, T // L + 1, D, n), 1000 * sid + 7).to(dev)
+    yb = m.train_scan_blocks(*c.args(), L, h0b, **kw)
+    # inference: prefill of all but the last block, then a block step and the
+    # commit of the last block
+    P = T - L
+    hc = None
+    if P > 0:
+        hc, _ = m.prefill(*c.segment(0, P), L, h_init=h0, **({k: v for k, v in kw.items() if k != "z"}))
+    else:
+        hc = h0.clone()
+    seg = c.segment(P, T)
+    kb = dict(kw)
+    if "z" in kb:
+        kb["z"] = kb["z"][:, P:T].contiguous()
+    ys = m.block_step(hc, *seg, **kb)
+    hcc = hc.clone()
+    _, yc = m.commit(hcc, *seg, want_y=True, **kb)
+    # gradients of both forms
+    dy = synth.normal((batch, T, D), 1000 * sid + 9, "cpu", torch.float32).to(dtype).to(dev).contiguous()
+    dbnd = synth.normal((batch, T // L + 1, D, n), 1000 * sid + 11).to(dev)
+    g = m.train_scan_bwd(*c.args(), L, bnd, dy, d_bounds=dbnd, want_dh_init=True, **kw)
+    gb = m.train_scan_blocks_bwd(*c.args(), L, h0b, dy, want_dh0_blocks=True, **kw)
+    torch.cuda.synchronize()
+
+    yo, bo = oracle.train_scan(*oa, L, h_init=to_np(h0), want_bounds=True, **ok)
+    near(y, yo, tol, "train_scan y")
+    near(bnd, bo, STATE_TOL, "h_bounds")
+    near(yb, oracle.train_blocks(*oa, L, to_np(h0b), **ok), tol, "train_scan_blocks y")
+    okp = {k: v for k, v in ok.items() if k != "z"}
+    if P > 0:
+        ho, _ = oracle.prefill(*c.oracle_args(0, P), L, h_init=to_np(h0), **okp)
+    else:
+        ho = to_np(h0)
+    near(hc, ho, STATE_TOL, "prefill state")
+    ob = c.oracle_args(P, T)
+    okb = dict(ok)
+    if "z" in okb:
+        okb["z"] = okb["z"][:, P:T]
+    hc_np = to_np(hc)         # the block calls start from the GPU's cache (checked above)
+    near(ys, oracle.block_step(hc_np, *ob, **okb), tol, "block_step y")
+    hco, yco = oracle.commit(hc_np, *ob, want_y=True, **okb)
+    near(yc, yco, tol, "commit y")
+    near(hcc, hco, STATE_TOL, "commit state")
+
+    r = oracle.scan_bwd(*oa, L, to_np(dy), h0=to_np(h0), dbounds=to_np(dbnd), **ok)
+    for k in ("dx", "ddt", "dB", "dC"):
+        near(g[k], r[k], tol, "train_scan_bwd " + k)
+    for k in ("dA", "dDskip"):
+        near(g[k], r[k], STATE_TOL, "train_scan_bwd " + k)
+    near(g["dh_init"], r["dh0"], STATE_TOL, "train_scan_bwd dh_init")
+    rb = oracle.scan_bwd(*oa, L, to_np(dy), h0_blocks=to_np(h0b), **ok)
+    for k in ("dx", "ddt", "dB", "dC"):
+        near(gb[k], rb[k], tol, "train_scan_blocks_bwd " + k)
+    for k in ("dA", "dDskip"):
+        near(gb[k], rb[k], STATE_TOL, "train_scan_blocks_bwd " + k)
+    near(gb["dh0_blocks"], rb["dh0_blocks"], STATE_TOL, "train_scan_blocks_bwd dh0_blocks")
+    if "d_dt_bias" in r:
+        near(g["d_dt_bias"], r["d_dt_bias"], STATE_TOL, "d_dt_bias")
+        near(gb["d_dt_bias"], rb["d_dt_bias"], STATE_TOL, "blocks d_dt_bias")
+    if "dz" in r:
+        near(g["dz"], r["dz"], tol, "dz")
+        near(gb["dz"], rb["dz"], tol, "blocks dz")
