@@ -894,13 +894,6 @@ def main():
     if args.model_loop:
         return model_loop_main(args, m, synth, torch)
     wl = dict(synth.WORKLOADS[args.workload])
-    if "seq" in wl:
-        r = run_training(args.workload, args, m, synth, torch, args.steps, args.warmup)
-        print(json.dumps(train_line(args, r, torch)), flush=True)
-        return 0
-    if args.block_len or args.d_state:
-        print("--block-len / --d-state apply to the training workloads", file=sys.stderr)
-        return 2
     if args.copy_calibration:
         # a plain copy of known size: 1 GiB read + 1 GiB written per launch
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
@@ -910,6 +903,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log("[bench] copy calibration: 3 x 1 GiB device copies")
+    if "seq" in wl:
+        r = run_training(args.workload, args, m, synth, torch, args.steps, args.warmup)
+        print(json.dumps(train_line(args, r, torch)), flush=True)
+        return 0
+    if args.block_len or args.d_state:
+        print("--block-len / --d-state apply to the training workloads", file=sys.stderr)
+        return 2
 
     head = run_inference(args.workload, args, m, synth, torch, probe, args.steps, args.warmup,
                          cpu_rows_baseline=True)

@@ -663,12 +663,13 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(kN ==
     const int cl = lane / P;                  // channel within the wave
     const int g = lane % P;                   // state pair
     const int s0 = 2 * g;
-    const int d_w0 = blockIdx.x * (4 * CW) + w * CW;
+    const BlockPos pos = xcd_paired_block();   // (channel tile, chunk, batch row)
+    const int d_w0 = pos.tile * (4 * CW) + w * CW;
     const int d_raw = d_w0 + cl;
     const bool live = d_raw < D;
     const int d = live ? d_raw : D - 1;
-    const int c = blockIdx.y;
-    const int b = blockIdx.z;
+    const int c = pos.c;
+    const int b = pos.b;
     const int64_t t_begin = (int64_t)c * Tc;
     const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
     const int len = (int)(t_end - t_begin);
@@ -814,7 +815,7 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(kN ==
     };
     auto f32 = [](uint32_t v) { return __uint_as_float(v); };
 
-    float *pbc = part_bc + ((int64_t)b * gridDim.x + blockIdx.x) * T * (2 * kN);
+    float *pbc = part_bc + ((int64_t)b * gridDim.x + pos.tile) * T * (2 * kN);
     Tin *dxw = dx + first * D;
     Tin *dtw = ddt + first * D;
 

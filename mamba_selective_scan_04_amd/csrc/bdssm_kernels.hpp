@@ -812,6 +812,40 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
 // (16 states) or block_bidir_kernel.
 // grid = (ceil(D / (4 CW)), chunks, batch), block = 256.
 template <int kN> constexpr int pair_channels() { return 4 * (2 * kWave / kN); }
+
+// Workgroup -> (channel tile, chunk, batch row) for the two-state kernels,
+// whose 16-state tile is 32 channels, 64 bytes of each bf16 stream row.  The
+// hardware hands workgroups to the 8 XCDs in turn (linear id mod 8), each
+// with its own L2, and a 128-byte line spans two tiles: mapped in order, the
+// two tiles of a line run on different XCDs and the line is fetched from HBM
+// twice.  Within every run of 16 linear ids this pairs tiles 2j and 2j + 1 on
+// one XCD, dispatched 8 apart (ids 16q + i and 16q + 8 + i take tiles 16q +
+// 2i and 16q + 2i + 1); an incomplete last run keeps the plain order.
+struct BlockPos {
+    int tile, c, b;
+};
+// The remapped id differs from the linear one by less than 16, so with at
+// least 16 tiles per row it moves the tile by that much and carries into the
+// chunk and batch indices at most once (no integer division); narrower grids
+// keep the plain order, and so do single-chunk launches (the latency-bound
+// block step and commit, whose 16 rows per workgroup gain nothing from the
+// shared lines: 3.9 us plain against 4.0-4.1 us paired at 65K b8).
+__device__ __forceinline__ BlockPos xcd_paired_block() {
+    const int nx = gridDim.x, ny = gridDim.y;
+    int t = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
+    const int lin = t + nx * (c + ny * b);
+    if (nx >= 16 && ny > 1 && (lin | 15) < nx * ny * (int)gridDim.z) {
+        t += (((lin & 7) << 1) | ((lin >> 3) & 1)) - (lin & 15);
+        if (t >= nx) {
+            t -= nx;
+            if (++c == ny) { c = 0; ++b; }
+        } else if (t < 0) {
+            t += nx;
+            if (--c < 0) { c = ny - 1; --b; }
+        }
+    }
+    return BlockPos{t, c, b};
+}
 // The longest block the two-state forward takes (multiples of 16 from 32):
 // its right-to-left walk keeps Lr / 16 - 1 reverse states per lane in LDS.
 constexpr int kLongMax = 256;
@@ -874,12 +908,13 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(L == 
     const int cl = lane / P;                  // channel within the wave
     const int g = lane % P;                   // state pair
     const int s0 = 2 * g;
-    const int d_w0 = blockIdx.x * (4 * CW) + w * CW;
+    const BlockPos pos = xcd_paired_block();
+    const int d_w0 = pos.tile * (4 * CW) + w * CW;
     const int d_raw = d_w0 + cl;
     const bool live = d_raw < D;
     const int d = live ? d_raw : D - 1;
-    const int c = blockIdx.y;
-    const int b = blockIdx.z;
+    const int c = pos.c;
+    const int b = pos.b;
     const int64_t t_begin = (int64_t)c * Tc;
     const int64_t t_end = (t_begin + Tc < T) ? t_begin + Tc : T;
     const int len = (int)(t_end - t_begin);
