@@ -154,6 +154,27 @@ void launch_carry(bool rev, const float *agg_h, const float *agg_s, const float 
                   const float *h_init, float *h_in, float *h_final, int64_t batch, int64_t D,
                   int64_t N, int n_chunks, int n_agg, hipStream_t st, int c_low) {
     const int64_t total = batch * D * N;
+    // long chunk sequences (more than 64 fold steps; at fewer the one-thread
+    // walk measured as fast): one wave per segment of about 12 fold steps, at
+    // most 16 segments (batches of 16 loads per lane measured slower).
+    // BDSSM_CARRY=serial keeps the one-thread walk, BDSSM_CARRY=tree takes
+    // the segments from 2 steps on (tests)
+    const int64_t K = rev ? n_chunks - 1 - c_low : n_agg;
+    const char *cv = getenv("BDSSM_CARRY");
+    const char mode = cv != nullptr ? cv[0] : 0;
+    int64_t W = mode == 's' ? 1 : (K > 64 || (mode == 't' && K > 1)) ? ceil_div(K, 12) : 1;
+    if (W < 2 && mode == 't' && K > 1) W = 2;
+    if (W > 16) W = 16;
+    if (W >= 2 && ceil_div(total, kWave) * kWave * W < ((int64_t)1 << 31)) {
+        const dim3 gt((unsigned)ceil_div(total, kWave));
+        if (rev)
+            hipLaunchKernelGGL((carry_tree_kernel<true>), gt, dim3((unsigned)(kWave * W)), 0, st, agg_h, agg_s, A,
+                               h_init, h_in, h_final, (int)batch, (int)D, (int)N, n_chunks, n_agg, c_low);
+        else
+            hipLaunchKernelGGL((carry_tree_kernel<false>), gt, dim3((unsigned)(kWave * W)), 0, st, agg_h, agg_s,
+                               A, h_init, h_in, h_final, (int)batch, (int)D, (int)N, n_chunks, n_agg, c_low);
+        return;
+    }
     const dim3 g((unsigned)ceil_div(total, 256));
     if (rev)
         hipLaunchKernelGGL((carry_kernel<true>), g, dim3(256), 0, st, agg_h, agg_s, A, h_init, h_in,

@@ -421,6 +421,100 @@ __global__ __launch_bounds__(256) void carry_kernel(
     }
 }
 
+// The same carry with the chunk sequence cut into W segments, one wave per
+// segment (W = blockDim.x / 64, at most 16; lanes: 64 consecutive (b, d, n)).  Each wave
+// folds its segment from zero into an affine map (S = sum of the step-size
+// sums, H = the segment's state from zero); the maps of the waves before it,
+// through LDS, give the state entering its segment; with h_in requested the
+// wave walks its segment again from that state and writes the states
+// entering its chunks (the reloads hit the cache).  Same outputs as
+// carry_kernel; only the rounding order differs (a segment's decay is
+// exp2(A' S) of the summed S, not the product of its chunks' decays).
+// k counts fold steps: chunk k forward, chunk n_chunks - 1 - k reverse; K =
+// n_agg forward, n_chunks - 1 - c_low reverse.
+template <bool kRev>
+__global__ __launch_bounds__(1024) void carry_tree_kernel(
+    const float *__restrict__ agg_h, const float *__restrict__ agg_s, const float *__restrict__ A,
+    const float *h_init, float *__restrict__ h_in, float *h_final,
+    int batch, int D, int n_states, int n_chunks, int n_agg, int c_low)
+{
+    __shared__ float seg_h[16][kWave], seg_s[16][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int W = uniform((int)(blockDim.x >> 6));
+    const int w = uniform((int)(threadIdx.x >> 6));
+    const int64_t total = (int64_t)batch * D * n_states;
+    const int64_t i_raw = (int64_t)blockIdx.x * kWave + lane;
+    const bool live = i_raw < total;
+    const int64_t i = live ? i_raw : total - 1;
+    const int n = (int)(i % n_states);
+    const int64_t bd = i / n_states;
+    const int d = (int)(bd % D);
+    const int64_t b = bd / D;
+    const float a2 = A[(int64_t)d * n_states + n] * kLog2e;
+    const int64_t cs = (int64_t)D * n_states;
+    const int64_t base_h = b * n_chunks * cs + (int64_t)d * n_states + n;
+    const int64_t base_s = b * n_chunks * (int64_t)D + d;
+    const int K = kRev ? n_chunks - 1 - c_low : n_agg;
+    const int k0 = (int)((int64_t)K * w / W), k1 = (int)((int64_t)K * (w + 1) / W);
+    auto chunk = [&](int k) { return kRev ? n_chunks - 1 - k : k; };
+
+    // the segment from zero: 8 chunks' loads and decays ahead of their FMAs
+    float h = 0.f, S = 0.f;
+    int k = k0;
+    for (; k + 8 <= k1; k += 8) {
+        float s[8], l[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            s[j] = agg_s[base_s + (int64_t)chunk(k + j) * D];
+            l[j] = agg_h[base_h + chunk(k + j) * cs];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            h = __builtin_fmaf(fast_exp2(a2 * s[j]), h, l[j]);
+            S += s[j];
+        }
+    }
+    for (; k < k1; ++k) {
+        const float s = agg_s[base_s + (int64_t)chunk(k) * D];
+        h = __builtin_fmaf(fast_exp2(a2 * s), h, agg_h[base_h + chunk(k) * cs]);
+        S += s;
+    }
+    seg_h[w][lane] = h;
+    seg_s[w][lane] = S;
+    __syncthreads();
+    // the state entering this wave's segment
+    float hin = (!kRev && h_init != nullptr) ? h_init[i] : 0.f;
+    for (int j = 0; j < w; ++j) hin = __builtin_fmaf(fast_exp2(a2 * seg_s[j][lane]), hin, seg_h[j][lane]);
+    float fin = __builtin_fmaf(fast_exp2(a2 * S), hin, h);
+    if (h_in != nullptr) {
+        float hh = hin;
+        int kk = k0;
+        for (; kk + 8 <= k1; kk += 8) {
+            float s[8], l[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                s[j] = agg_s[base_s + (int64_t)chunk(kk + j) * D];
+                l[j] = agg_h[base_h + chunk(kk + j) * cs];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (live) h_in[base_h + chunk(kk + j) * cs] = hh;
+                hh = __builtin_fmaf(fast_exp2(a2 * s[j]), hh, l[j]);
+            }
+        }
+        for (; kk < k1; ++kk) {
+            if (live) h_in[base_h + chunk(kk) * cs] = hh;
+            const float s = agg_s[base_s + (int64_t)chunk(kk) * D];
+            hh = __builtin_fmaf(fast_exp2(a2 * s), hh, agg_h[base_h + chunk(kk) * cs]);
+        }
+        fin = hh;
+    }
+    if (w == W - 1 && live) {
+        if (h_in != nullptr && (kRev || K < n_chunks)) h_in[base_h + chunk(K) * cs] = fin;
+        if (h_final != nullptr) h_final[i] = fin;
+    }
+}
+
 // ------------------------------------------------------------------------
 // Bidirectional kernel: forward scan from the chunk's incoming state, reverse
 // scan restricted to each L-token block, fused output.

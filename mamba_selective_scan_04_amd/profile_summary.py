@@ -35,20 +35,20 @@ KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                         if f.endswith((".hip", ".hpp")) and not f.startswith("roof_probe"))
 COPY_BYTES = 1 << 30
 # the definitions each profiled family depends on (kernels, launchers, plans)
-_BIDIR = ("chunk_state_kernel", "carry_kernel", "bidir_pair_kernel", "pair_scatter", "bidir_wave_kernel",
+_BIDIR = ("chunk_state_kernel", "carry_kernel", "carry_tree_kernel", "bidir_pair_kernel", "pair_scatter", "bidir_wave_kernel",
           "block_lane_kernel", "make_plan", "plan_long", "pair_long_capacity", "blocks_plan", "plan_for",
           "pair_path", "pair_long", "pair_bidir", "launch_chunk_state_k", "launch_chunk_state", "launch_carry",
           "launch_pair_k", "launch_pair_L", "launch_pair", "launch_bidir_k", "launch_bidir_L", "launch_bidir",
           "launch_block_lane", "block_lane_path", "run_bidirectional", "layout_ws")
 _BACKWARD = ("bwd_pair_kernel", "bwd_wave_kernel", "adjoint_chunk_kernel", "adjoint_general_kernel",
-             "group_state_kernel", "bwd_general_kernel", "carry_kernel", "bc_reduce_kernel", "param_reduce_kernel",
+             "group_state_kernel", "bwd_general_kernel", "carry_kernel", "carry_tree_kernel", "bc_reduce_kernel", "param_reduce_kernel",
              "fold16", "fold32", "make_plan", "blocks_plan", "plan_general", "bwd_plan", "bwd_blocks_plan",
              "bwd_use_wave", "bwd_general", "bwd_long", "bwd_channels", "bwd_block_channels",
              "bwd_block_capacity", "layout_bwd", "launch_bwd_L", "launch_bwd_n", "launch_bwd", "launch_bwd_long",
              "launch_bwd_reduce", "launch_adjoint_chunk_k", "launch_adjoint_chunk", "launch_adjoint_general",
              "launch_bwd_general")
 FAMILIES = {
-    "prefill": ("chunk_state_kernel", "carry_kernel", "make_plan", "plan_for", "launch_chunk_state_k",
+    "prefill": ("chunk_state_kernel", "carry_kernel", "carry_tree_kernel", "make_plan", "plan_for", "launch_chunk_state_k",
                 "launch_chunk_state", "launch_carry", "run_state_only", "layout_ws"),
     "bidir": _BIDIR,
     "backward": _BACKWARD,
