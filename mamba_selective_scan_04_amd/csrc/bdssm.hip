@@ -235,19 +235,29 @@ void run_full(const bdssm_shape *s, int64_t T, const void *x, const void *dt, co
               const Plan &p, hipStream_t st, const Fuse &f = Fuse()) {
     const int64_t batch = s->batch, D = s->d_inner, N = s->d_state;
     const int nf = p.n_fine;
-    // forward: aggregates of chunks 0..nf-2, incoming states of all chunks
-    launch_chunk_state<Tin>(false, x, dt, B, A, nullptr, w.agg_h, w.agg_s, batch, T, D, N,
-                            p.fine_len, nf, 0, nf - 1, st, f);
-    launch_carry(false, w.agg_h, w.agg_s, A, nullptr, w.h_in, nullptr, batch, D, N, nf, nf - 1, st);
-    // reverse (with its own operands when given): aggregates of chunks
-    // 1..nf-1 (scanned right to left), incoming states
     const bool sep = f.dt_r != nullptr;
     const void *rdt = sep ? f.dt_r : dt, *rB = sep ? f.B_r : B, *rC = sep ? f.C_r : C;
     const float *rA = sep ? f.A_r : A;
     const Fuse fr = f.reverse();
-    launch_chunk_state<Tin>(true, x, rdt, rB, rA, nullptr, w.ragg_h, w.ragg_s, batch, T, D, N,
-                            p.fine_len, nf, 1, nf - 1, st, fr);
-    launch_carry(true, w.ragg_h, w.ragg_s, rA, nullptr, w.hr_in, nullptr, batch, D, N, nf, nf, st);
+    // shared operands: both directions' aggregates of every chunk in one
+    // forward pass (BDSSM_FULL_AGG=separate: one pass per direction)
+    const char *fa = getenv("BDSSM_FULL_AGG");
+    if (!sep && !(fa != nullptr && fa[0] == 's')) {
+        if (nf > 1)
+            launch_chunk_both<Tin>(x, dt, B, A, w.agg_h, w.agg_s, w.ragg_h, batch, T, D, N, p.fine_len, nf, st, f);
+        launch_carry(false, w.agg_h, w.agg_s, A, nullptr, w.h_in, nullptr, batch, D, N, nf, nf - 1, st);
+        launch_carry(true, w.ragg_h, w.agg_s, A, nullptr, w.hr_in, nullptr, batch, D, N, nf, nf, st);
+    } else {
+        // forward: aggregates of chunks 0..nf-2, incoming states of all chunks
+        launch_chunk_state<Tin>(false, x, dt, B, A, nullptr, w.agg_h, w.agg_s, batch, T, D, N,
+                                p.fine_len, nf, 0, nf - 1, st, f);
+        launch_carry(false, w.agg_h, w.agg_s, A, nullptr, w.h_in, nullptr, batch, D, N, nf, nf - 1, st);
+        // reverse (with its own operands when given): aggregates of chunks
+        // 1..nf-1 (scanned right to left), incoming states
+        launch_chunk_state<Tin>(true, x, rdt, rB, rA, nullptr, w.ragg_h, w.ragg_s, batch, T, D, N,
+                                p.fine_len, nf, 1, nf - 1, st, fr);
+        launch_carry(true, w.ragg_h, w.ragg_s, rA, nullptr, w.hr_in, nullptr, batch, D, N, nf, nf, st);
+    }
     Fuse ff = f;
     ff.z = nullptr;             // the gate multiplies the final output only
     launch_sweep<Tin>(false, x, dt, B, C, A, Dskip, w.h_in, w.yf, y, batch, T, D, N, p.fine_len, nf, st, ff);

@@ -263,13 +263,23 @@ template <> __device__ __forceinline__ void Rows<float>::store_at(int32_t off, f
 // Resident waves per SIMD the chunk scan is built for (the launch plans size
 // their fine chunks to exactly one round of them): 7 leaves 72 VGPRs, room for
 // two stages of 5 tokens without spills.
+//
+// kBoth (chunk_both_kernel, forward only): the same left-to-right pass also
+// forms the chunk's reverse aggregate, the reverse-direction state at the
+// chunk's first token from zero after its last,  r = sum_s P_s u_s  with
+// P_s the product of the decays of the chunk's tokens before s (P = 1 at the
+// first token; r += P u, then P *= dA), into rout; it shares the decays and
+// injections of the forward recurrence (7 issue slots per state and token
+// instead of 5 + 5 for two passes), and S serves both carries.
 constexpr int kChunkWaves = 7;
-template <typename Tin, bool kRev, bool kDirect, int kDt = kDtPlain, int kN = kStates>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kN > 16 ? 4 : kChunkWaves))) void chunk_state_kernel(
+template <typename Tin, bool kRev, bool kDirect, int kDt, int kN, bool kBoth>
+__device__ __forceinline__ void chunk_scan_body(
     const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
     const float *__restrict__ A, const float *h0, float *hout, float *__restrict__ sout,
-    int64_t T, int D, int64_t Tc, int n_chunks, int c_first, const float *__restrict__ dt_bias)
+    int64_t T, int D, int64_t Tc, int n_chunks, int c_first, const float *__restrict__ dt_bias,
+    float *__restrict__ rout)
 {
+    static_assert(!kBoth || (!kRev && !kDirect), "the two-direction aggregates scan forward from zero");
     constexpr int U = 5;                      // tokens per pipeline stage
     const int lane = threadIdx.x;
     const int d_raw = blockIdx.x * kWave + lane;
@@ -292,6 +302,12 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kN > 16 ?
         for (int n = 0; n < kN; ++n) h[n] = 0.f;
     }
     float S = 0.f;
+    // kBoth: the reverse aggregate and the running decay product
+    float r[kBoth ? kN : 1], P[kBoth ? kN : 1];
+    if constexpr (kBoth) {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) { r[n] = 0.f; P[n] = 1.f; }
+    }
     const float bias = (kDt != kDtPlain && dt_bias != nullptr) ? dt_bias[d] : 0.f;
     const int64_t first = (int64_t)b * T + t_begin;           // first row of the chunk
     const Rows<Tin> xs(x + first * D, len, D, d);
@@ -322,8 +338,16 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kN > 16 ?
                 for (int q = 0; q < kN / 2; ++q) {
                     float b0, b1;
                     load_pair(brow, q, b0, b1);
-                    h[2 * q] = __builtin_fmaf(fast_exp2(dl * a2[2 * q]), h[2 * q], dx * b0);
-                    h[2 * q + 1] = __builtin_fmaf(fast_exp2(dl * a2[2 * q + 1]), h[2 * q + 1], dx * b1);
+                    const float e0 = fast_exp2(dl * a2[2 * q]), e1 = fast_exp2(dl * a2[2 * q + 1]);
+                    const float u0 = dx * b0, u1 = dx * b1;
+                    h[2 * q] = __builtin_fmaf(e0, h[2 * q], u0);
+                    h[2 * q + 1] = __builtin_fmaf(e1, h[2 * q + 1], u1);
+                    if constexpr (kBoth) {
+                        r[2 * q] = __builtin_fmaf(P[2 * q], u0, r[2 * q]);
+                        r[2 * q + 1] = __builtin_fmaf(P[2 * q + 1], u1, r[2 * q + 1]);
+                        P[2 * q] *= e0;
+                        P[2 * q + 1] *= e1;
+                    }
                 }
             }
         }
@@ -359,7 +383,33 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kN > 16 ?
     if (live) {
         store_row<kN>(hout + (((int64_t)b * n_chunks + c) * D + d) * kN, h);
         if (!kDirect && sout != nullptr) sout[((int64_t)b * n_chunks + c) * D + d] = S;
+        if constexpr (kBoth) store_row<kN>(rout + (((int64_t)b * n_chunks + c) * D + d) * kN, r);
     }
+}
+
+template <typename Tin, bool kRev, bool kDirect, int kDt = kDtPlain, int kN = kStates>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kN > 16 ? 4 : kChunkWaves))) void chunk_state_kernel(
+    const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
+    const float *__restrict__ A, const float *h0, float *hout, float *__restrict__ sout,
+    int64_t T, int D, int64_t Tc, int n_chunks, int c_first, const float *__restrict__ dt_bias)
+{
+    chunk_scan_body<Tin, kRev, kDirect, kDt, kN, false>(x, dt, Bm, A, h0, hout, sout, T, D, Tc, n_chunks,
+                                                         c_first, dt_bias, nullptr);
+}
+
+// Forward and reverse aggregates of every chunk in one forward pass (the
+// full-sequence baseline with shared operands): hout / sout as for
+// chunk_state_kernel, rout the reverse aggregates [batch, n_chunks, D, kN].
+// Three state arrays and the decay rows fill the registers: four waves per
+// SIMD at 16 states (five spilled).
+template <typename Tin, int kDt = kDtPlain, int kN = kStates>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kN > 16 ? 2 : 4))) void chunk_both_kernel(
+    const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ Bm,
+    const float *__restrict__ A, float *hout, float *__restrict__ sout, float *__restrict__ rout,
+    int64_t T, int D, int64_t Tc, int n_chunks, const float *__restrict__ dt_bias)
+{
+    chunk_scan_body<Tin, false, false, kDt, kN, true>(x, dt, Bm, A, nullptr, hout, sout, T, D, Tc, n_chunks, 0,
+                                                       dt_bias, rout);
 }
 
 // Carry across chunks: one thread per (b, d, n) (n < n_states), sequential

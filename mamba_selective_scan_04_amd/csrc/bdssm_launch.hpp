@@ -513,6 +513,13 @@ void launch_chunk_state(bool rev, const void *x, const void *dt, const void *B, 
                         int64_t D, int64_t N, int64_t Tc, int n_chunks, int c_first, int n_launch,
                         hipStream_t st, const Fuse &f = Fuse());
 
+// Forward and reverse chunk aggregates in one pass (the baseline with shared
+// operands; sout serves both carries).                      launch_chunk.hip
+template <typename Tin>
+void launch_chunk_both(const void *x, const void *dt, const void *B, const float *A, float *hout, float *sout,
+                       float *rout, int64_t batch, int64_t T, int64_t D, int64_t N, int64_t Tc, int n_chunks,
+                       hipStream_t st, const Fuse &f = Fuse());
+
 // The baseline's output sweeps.                               launch_chunk.hip
 template <typename Tin>
 void launch_sweep(bool rev, const void *x, const void *dt, const void *B, const void *C,

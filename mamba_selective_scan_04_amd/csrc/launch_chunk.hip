@@ -53,6 +53,29 @@ void launch_chunk_state(bool rev, const void *x, const void *dt, const void *B, 
     });
 }
 
+// Forward and reverse aggregates of all n_chunks chunks in one pass
+// (chunk_both_kernel; shared operands).
+template <typename Tin>
+void launch_chunk_both(const void *x, const void *dt, const void *B, const float *A, float *hout, float *sout,
+                       float *rout, int64_t batch, int64_t T, int64_t D, int64_t N, int64_t Tc, int n_chunks,
+                       hipStream_t st, const Fuse &f) {
+    if (n_chunks <= 0) return;
+    const dim3 g = grid3(D, n_chunks, batch);
+    const Tin *xp = (const Tin *)x, *dp = (const Tin *)dt, *bp = (const Tin *)B;
+    with_states(N, [&](auto kn) {
+        constexpr int kN = decltype(kn)::value;
+#define BDSSM_BOTH(KDT)                                                                                 \
+        hipLaunchKernelGGL((chunk_both_kernel<Tin, KDT, kN>), g, dim3(kWave), 0, st, xp, dp, bp, A, hout, sout, \
+                           rout, T, (int)D, Tc, n_chunks, f.dt_bias)
+        switch (f.dt_mode) {
+        case kDtSoftplus: BDSSM_BOTH(kDtSoftplus); break;
+        case kDtBias: BDSSM_BOTH(kDtBias); break;
+        default: BDSSM_BOTH(kDtPlain); break;
+        }
+#undef BDSSM_BOTH
+    });
+}
+
 template <typename Tin, bool kRev, int kN>
 void launch_sweep_k(dim3 g, const void *x, const void *dt, const void *B, const void *C,
                     const float *A, const float *Dskip, const float *hin, float *yf, void *y,
@@ -88,6 +111,9 @@ void launch_sweep(bool rev, const void *x, const void *dt, const void *B, const 
 template void launch_chunk_state<BDSSM_TIN>(bool, const void *, const void *, const void *, const float *,
                                           const float *, float *, float *, int64_t, int64_t, int64_t,
                                           int64_t, int64_t, int, int, int, hipStream_t, const Fuse &);
+template void launch_chunk_both<BDSSM_TIN>(const void *, const void *, const void *, const float *, float *,
+                                         float *, float *, int64_t, int64_t, int64_t, int64_t, int64_t, int,
+                                         hipStream_t, const Fuse &);
 template void launch_sweep<BDSSM_TIN>(bool, const void *, const void *, const void *, const void *, const float *,
                                     const float *, const float *, float *, void *, int64_t, int64_t, int64_t,
                                     int64_t, int64_t, int, hipStream_t, const Fuse &);

@@ -35,7 +35,7 @@ KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                         if f.endswith((".hip", ".hpp")) and not f.startswith("roof_probe"))
 COPY_BYTES = 1 << 30
 # the definitions each profiled family depends on (kernels, launchers, plans)
-_BIDIR = ("chunk_state_kernel", "carry_kernel", "carry_tree_kernel", "bidir_pair_kernel", "pair_scatter", "bidir_wave_kernel",
+_BIDIR = ("chunk_scan_body", "chunk_state_kernel", "carry_kernel", "carry_tree_kernel", "bidir_pair_kernel", "pair_scatter", "bidir_wave_kernel",
           "block_lane_kernel", "make_plan", "plan_long", "pair_long_capacity", "blocks_plan", "plan_for",
           "pair_path", "pair_long", "pair_bidir", "launch_chunk_state_k", "launch_chunk_state", "launch_carry",
           "launch_pair_k", "launch_pair_L", "launch_pair", "launch_bidir_k", "launch_bidir_L", "launch_bidir",
@@ -48,12 +48,13 @@ _BACKWARD = ("bwd_pair_kernel", "bwd_wave_kernel", "adjoint_chunk_kernel", "adjo
              "launch_bwd_reduce", "launch_adjoint_chunk_k", "launch_adjoint_chunk", "launch_adjoint_general",
              "launch_bwd_general")
 FAMILIES = {
-    "prefill": ("chunk_state_kernel", "carry_kernel", "carry_tree_kernel", "make_plan", "plan_for", "launch_chunk_state_k",
+    "prefill": ("chunk_scan_body", "chunk_state_kernel", "carry_kernel", "carry_tree_kernel", "make_plan", "plan_for", "launch_chunk_state_k",
                 "launch_chunk_state", "launch_carry", "run_state_only", "layout_ws"),
     "bidir": _BIDIR,
     "backward": _BACKWARD,
     # the training step: the forward passes, the backward and the baseline's sweeps
-    "train": tuple(dict.fromkeys(_BIDIR + _BACKWARD + ("sweep_output_kernel", "run_full"))),
+    "train": tuple(dict.fromkeys(_BIDIR + _BACKWARD + ("sweep_output_kernel", "chunk_both_kernel", "launch_chunk_both",
+                                                        "run_full"))),
 }
 
 
