@@ -426,7 +426,7 @@ size_t bdssm_workspace_bytes_op(const bdssm_shape *shape, int64_t T, int op) {
     }
     Plan p;
     if (op == BDSSM_OP_FULL) p = make_plan(batch, D, T);
-    else if (!plan_for(batch, D, T, shape->block_len, shape->d_state, &p)) return (size_t)-1;
+    else if (!plan_for(batch, D, T, shape->block_len, shape->d_state, &p, op == BDSSM_OP_TRAIN)) return (size_t)-1;
     return layout_ws(nullptr, batch, D, shape->d_state, T, p, op).bytes;
 }
 
@@ -567,7 +567,7 @@ int bdssm_train_scan_ex(const bdssm_shape *shape, int64_t T, const void *x, cons
         return BDSSM_ERR_ALIGN;
     const size_t nbnd = (size_t)batch * (T / L + 1) * D * N * 4;
     Plan p;
-    if (!plan_for(batch, D, T, L, N, &p)) return BDSSM_ERR_SHAPE;
+    if (!plan_for(batch, D, T, L, N, &p, true)) return BDSSM_ERR_SHAPE;
     const Workspace probe = layout_ws(nullptr, batch, D, N, T, p, BDSSM_OP_TRAIN);
     rc = check_alias(shape, T, x, dt, B, C, A, Dskip, h_init,
                      {Range{y, (size_t)batch * T * D * esize(shape)}, Range{h_bounds, nbnd},

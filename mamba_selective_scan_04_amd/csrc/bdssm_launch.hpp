@@ -66,8 +66,12 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // coarse_ch / coarse_cap: channels per workgroup of the coarse pass and how
 // many of its workgroups are resident at once (the forward wave kernel: 64,
 // 512; bwd_pair_kernel: 32, 768).
+// fill_prepass (the training forms): with several coarse chunks the pre-pass
+// covers only (nc - 1) / nc of the fine chunks, so the fine chunks are cut
+// shorter until the pre-pass alone fills one round of resident waves.
 inline Plan make_plan(int64_t batch, int64_t D, int64_t T, double prepass_weight = 0.45,
-               int64_t coarse_ch = kWave, int64_t coarse_cap = kCoarseGroups, bool one_round = false) {
+               int64_t coarse_ch = kWave, int64_t coarse_cap = kCoarseGroups, bool one_round = false,
+               bool fill_prepass = false) {
     Plan p{};
     const int64_t groups = batch * ceil_div(D, kWave);          // fine pass: one wave per 64 channels
     const int64_t cgroups = batch * ceil_div(D, coarse_ch);     // coarse pass workgroups per chunk
@@ -115,6 +119,19 @@ inline Plan make_plan(int64_t batch, int64_t D, int64_t T, double prepass_weight
     }
     const int64_t forced_nc = env_int("BDSSM_COARSE_CHUNKS", 0);
     if (forced_nc > 0) nc = forced_nc < nf ? forced_nc : nf;
+    // BDSSM_FILL_PREPASS=0 keeps the inference plan's fine chunks (tests)
+    const char *fp = getenv("BDSSM_FILL_PREPASS");
+    if (fill_prepass && nc > 1 && forced == 0 && !(fp != nullptr && fp[0] == '0')) {
+        int64_t nf2 = ceil_div(fine_waves * nc, (nc - 1) * groups);
+        if (nf2 > ngroups16) nf2 = ngroups16;
+        if (nf2 > nf) {
+            const int64_t fl2 = ceil_div(ngroups16, nf2) * kGroup;
+            if (ceil_div(T, fl2) <= 65535) {
+                fl = fl2;
+                nf = ceil_div(T, fl);
+            }
+        }
+    }
     int64_t per = ceil_div(nf, nc);
     if (per * fl > max_tok) per = max_tok / fl;
     nc = ceil_div(nf, per);
@@ -247,9 +264,9 @@ inline bool plan_long(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N,
 }
 
 // The plan of the forward entry points for block length L, N states.
-inline bool plan_for(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, Plan *out) {
+inline bool plan_for(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, Plan *out, bool train = false) {
     if (pair_path(L, N)) {
-        *out = make_plan(batch, D, T, 0.45, pair_channels_of(N), kPairGroups, true);
+        *out = make_plan(batch, D, T, 0.45, pair_channels_of(N), kPairGroups, true, train);
         return true;
     }
     if (pair_long(L, N) && pair_bidir()) return plan_long(batch, D, T, L, N, out);
@@ -488,7 +505,7 @@ inline bool bwd_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, 
               bool sep = false) {
     if (bwd_general(L, N, sep) || bwd_long(L, N, sep)) return plan_general(batch, D, T, L, p);
     *p = make_plan(batch, D, T, kBwdPrepassWeight, bwd_block_channels(L, fused, N),
-                   bwd_block_capacity(L, fused, N));
+                   bwd_block_capacity(L, fused, N), false, true);
     return true;
 }
 inline bool bwd_blocks_plan(int64_t batch, int64_t D, int64_t T, int64_t L, int64_t N, int64_t *tc,
