@@ -66,3 +66,23 @@ def test_prefill_chunk_scan_does_not_spill():
     assert len(got) == 3 * 2
     bad = [(g, s, w, v) for g, s, w, v in got if s != 0 or w < 7]
     assert not bad, bad
+
+
+BOTH = re.compile(r"17chunk_both_kernelI([tf])Li(\d)ELi(\d+)E")
+TREE = re.compile(r"17carry_tree_kernelILb([01])E")
+
+
+def test_baseline_aggregate_pass_does_not_spill():
+    # both directions' chunk aggregates in one pass: every stream type, step
+    # size form and state count without spills, four waves per SIMD at 16
+    # states (five spilled)
+    got = matching(BOTH, lambda g: True)
+    assert len(got) == 2 * 3 * 4
+    bad = [(g, s, w, v) for g, s, w, v in got if s != 0 or (g[2] == "16" and w < 4)]
+    assert not bad, bad
+
+
+def test_segmented_carry_does_not_spill():
+    got = matching(TREE, lambda g: True)
+    assert len(got) == 2
+    assert all(s == 0 for _, s, _, _ in got), got
