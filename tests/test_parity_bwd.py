@@ -260,3 +260,35 @@ def test_training_step_graph_replays_match_eager(dev, L, monkeypatch):
             assert torch.equal(got, v), (form, k)
         step()                                     # eager work between the replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("fill", ["1", "0"])
+def test_training_plans_default_chunks(dev, fill, monkeypatch):
+    """Default plans (nothing forced) at a shape where the training plans
+    cut the fine chunks shorter than the inference plan's (batch 4, 1536
+    channels, 2048 tokens: 128 chunks of 16 tokens instead of 64 of 32, four
+    coarse chunks): train_scan with its block states and train_scan_bwd with
+    d_bounds against the oracle, with the shorter chunks and without them
+    (BDSSM_FILL_PREPASS=0)."""
+    monkeypatch.setenv("BDSSM_FILL_PREPASS", fill)
+    batch, T, D, L = 4, 2048, 1536, 16
+    c = Case(batch, T, D, torch.bfloat16, sid=3900, a_kind="random", device=dev, gen_device=dev)
+    dy = synth.normal((batch, T, D), 3901, dev, torch.bfloat16)
+    db = synth.normal((batch, T // L + 1, D, N), 3902, dev, torch.float32)
+    y, bnd = m.train_scan(*c.args(), L, want_bounds=True)
+    g = m.train_scan_bwd(*c.args(), L, bnd, dy, d_bounds=db, want_dh_init=True)
+    torch.cuda.synchronize()
+    ch = list(range(0, D, 97)) + [D - 1]
+    oa = c.oracle_args(chans=ch)
+    idx = torch.as_tensor(ch, device=dev)
+    sel = lambda t: to_np(t.index_select(2, idx))
+    r = oracle.scan(*oa, L, want_y=True, want_bounds=True)
+    assert rel_err(sel(y), r["y"]) < TOL[torch.bfloat16], worst(sel(y), r["y"])
+    assert rel_err(sel(bnd), r["bounds"]) < STATE_TOL, worst(sel(bnd), r["bounds"])
+    rb = oracle.scan_bwd(*oa, L, sel(dy), dbounds=sel(db))
+    for k in ("dx", "ddt"):
+        assert rel_err(sel(g[k]), rb[k]) < TOL[torch.bfloat16], (k, worst(sel(g[k]), rb[k]))
+    ga = to_np(g["dA"].index_select(0, idx))
+    assert rel_err(ga, rb["dA"]) < STATE_TOL, worst(ga, rb["dA"])
+    gh = to_np(g["dh_init"].index_select(1, idx))
+    assert rel_err(gh, rb["dh0"]) < STATE_TOL, worst(gh, rb["dh0"])
