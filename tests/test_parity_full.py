@@ -69,3 +69,22 @@ def test_full_scan_fused_step_size(dev, mode, monkeypatch):
     for form in FORMS:
         assert rel_err(out[form], ref) < TOL[torch.float32], (form, worst(out[form], ref))
     assert rel_err(out["both"], out["separate"]) < 1e-5
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("a_kind", ["zero", "steep"])
+def test_full_scan_decay_extremes(dev, form, a_kind, monkeypatch):
+    """A = 0 (every decay exactly 1: the decay product stays 1 and the
+    reverse aggregate is the plain sum of the chunk's injections) and a
+    steep A (-1000 (n + 1): decays underflow to zero within a token, so the
+    running product does too)."""
+    monkeypatch.setenv("BDSSM_CHUNK", "48")
+    monkeypatch.setenv("BDSSM_FULL_AGG", form)
+    c = Case(2, 960, 72, torch.float32, sid=97, a_kind="zero" if a_kind == "zero" else "default")
+    if a_kind == "steep":
+        c.dev["A"] = (c.dev["A"] * 1000.0).contiguous()
+    y = m.full_scan(*c.args())
+    torch.cuda.synchronize()
+    ref = oracle.full_scan(*c.oracle_args())
+    g = to_np(y)
+    assert rel_err(g, ref) < TOL[torch.float32], worst(g, ref)
