@@ -71,8 +71,12 @@ class Case:
                 synth.to_oracle(d["C"][:, t0:t1]), synth.to_oracle(A), synth.to_oracle(Ds))
 
     def segment(self, t0, t1):
+        """Tokens [t0, t1) as fresh contiguous copies (at batch 1 the slice is
+        already contiguous, and a view would start at an offset that need not
+        meet the library's 16-byte base alignment)."""
         d = self.dev
-        return tuple(d[k][:, t0:t1].contiguous() for k in ("x", "dt", "B", "C")) + (d["A"], d["Dskip"])
+        return tuple(d[k][:, t0:t1].clone(memory_format=torch.contiguous_format) for k in ("x", "dt", "B", "C")) + (
+            d["A"], d["Dskip"])
 
 
 def worst(got, ref):

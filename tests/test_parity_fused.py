@@ -54,7 +54,7 @@ def oracle_kw(kw, t0=None, t1=None):
 
 def sub(kw, t0, t1):
     out = dict(kw)
-    out["z"] = kw["z"][:, t0:t1].contiguous()
+    out["z"] = kw["z"][:, t0:t1].clone(memory_format=torch.contiguous_format)
     return out
 
 
@@ -180,7 +180,7 @@ def rev_oracle(rev, t0=None, t1=None):
 def rev_sub(rev, t0, t1):
     out = dict(rev)
     for k in ("dt", "B", "C"):
-        out[k] = rev[k][:, t0:t1].contiguous()
+        out[k] = rev[k][:, t0:t1].clone(memory_format=torch.contiguous_format)
     return out
 
 

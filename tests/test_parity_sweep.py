@@ -86,7 +86,7 @@ def test_sweep_all_entry_points(dev, case):
     seg = c.segment(P, T)
     kb = dict(kw)
     if "z" in kb:
-        kb["z"] = kb["z"][:, P:T].contiguous()
+        kb["z"] = kb["z"][:, P:T].clone(memory_format=torch.contiguous_format)
     ys = m.block_step(hc, *seg, **kb)
     hcc = hc.clone()
     _, yc = m.commit(hcc, *seg, want_y=True, **kb)
