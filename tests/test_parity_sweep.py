@@ -135,3 +135,41 @@ def test_sweep_all_entry_points(dev, case):
     if "dz" in r:
         near(g["dz"], r["dz"], tol, "dz")
         near(gb["dz"], rb["dz"], tol, "blocks dz")
+
+
+def _draw_env(count=30, seed=2027):
+    """Problems of the same space with the plan and kernel switches drawn
+    too: forced fine chunks (hundreds of chunks at small sizes), the carry's
+    two forms, forced coarse chunk counts, the training plans' pre-pass
+    chunking on or off, and the baseline's two aggregate forms."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for j, case in enumerate(_draw(count, seed + 1)):
+        env = {}
+        if rng.random() < 0.6:
+            env["BDSSM_CHUNK"] = str(int(rng.choice([16, 32, 48, 64])))
+        if rng.random() < 0.5:
+            env["BDSSM_CARRY"] = str(rng.choice(["tree", "serial"]))
+        if rng.random() < 0.3:
+            env["BDSSM_COARSE_CHUNKS"] = str(int(rng.integers(2, 6)))
+        if rng.random() < 0.3:
+            env["BDSSM_FILL_PREPASS"] = "0"
+        env["BDSSM_FULL_AGG"] = str(rng.choice(["both", "separate"]))
+        out.append(((1000 + j,) + case[1:], env))
+    return out
+
+
+@pytest.mark.parametrize("case,env", _draw_env(),
+                         ids=lambda v: "i%d-n%d-L%d-T%d-D%d-b%d-%s-%s" % v if isinstance(v, tuple) else
+                         "-".join("%s=%s" % (k[6:].lower(), x) for k, x in sorted(v.items())))
+def test_sweep_with_plan_switches(dev, case, env, monkeypatch):
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    test_sweep_all_entry_points(dev, case)
+    i, n, L, T, D, batch, dts, _ = case
+    dtype = torch.bfloat16 if dts == "bf16" else torch.float32
+    c = Case(batch, T, D, dtype, sid=700 + i, a_kind="random", n=n)
+    y = m.full_scan(*c.args())
+    torch.cuda.synchronize()
+    ref = oracle.full_scan(*c.oracle_args())
+    assert rel_err(to_np(y), ref) < TOL[dtype], ("full_scan", case, env, worst(to_np(y), ref))
