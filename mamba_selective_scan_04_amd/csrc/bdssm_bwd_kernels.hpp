@@ -637,8 +637,10 @@ __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(kN ==
     constexpr int NSB = kFuse ? 4 : 3;        // row streams: x, dt, dy (, z)
     // decays kept from pass A for pass B, per group: as many tokens as the
     // registers hold without spilling at three waves per SIMD (two at 4
-    // states); the others are formed again in pass B
-    constexpr int KA = kFuse ? 0
+    // states); the others are formed again in pass B.  With the fusions only
+    // the two-stream form at 16 states and L = 16 has room (4 tokens; the
+    // continuous form spilled at 4, the two-stream form at 8)
+    constexpr int KA = kFuse ? ((kN == 16 && L == 16 && kBlockInit) ? 4 : 0)
                        : kN == 4 ? 12
                        : (L == 1 || L == 2) ? 0
                        : kN == 8 ? (L == 16 ? 8 : 0)
